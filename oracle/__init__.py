@@ -1,0 +1,10 @@
+"""CPU oracle of the routed MoE SwiGLU layer (test infrastructure only).
+
+Only tests, the smoke check and the bench's CPU-baseline leg may import this
+package.  The product library never does.
+"""
+from .moe_oracle import (  # noqa: F401
+    capacity, dequantize, expert_ffn, forward, fp8_e4m3fn_decode, permute,
+    router_logits, routing_certificate, routing_weights, silu, softmax_rows,
+    topk_select,
+)

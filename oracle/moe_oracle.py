@@ -1,0 +1,266 @@
+"""CPU oracle for the routed Mixture-of-Experts SwiGLU feed-forward layer (forward pass).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's CPU
+baseline may import this module.  It shares no code with the HIP library and
+imports nothing from it; both sides only receive the same seeded inputs.
+
+The oracle is plain, slow and obviously correct: numpy in fp64, Python loops
+over tokens and assignments, numpy's fp64 matrix product as the only library
+step.  Inputs are the already-rounded tensors the GPU receives (fp32 values,
+bf16 values widened exactly to fp32, or fp8 e4m3fn byte codes plus fp32 scale
+factors); they are widened exactly to fp64 here.
+
+Sources (page titles; sections named on each page):
+  [MIX]  "MoE Model Architectures", Mixtral 8x7B: "Sparse MoE Block" and
+         "Expert FFN" -- router gate, softmax over experts, top-k, divide the
+         top-k weights by their sum, per-expert SwiGLU w2(silu(w1 x) * w3 x),
+         experts with no tokens skipped, weighted outputs summed per token.
+  [DSK]  same page, DeepSeek-V3: "DeepSeekMoE Architecture" (shared experts
+         always computed with weight 1 and added to the routed output) and
+         "Auxiliary-Loss-Free Load Balancing" (per-expert bias inside the
+         router's linear map).
+  [SWT]  same page, Switch Transformers "Top-1 Routing" (capacity: an expert
+         takes at most `expert_capacity` tokens, overflow tokens are dropped).
+  [MINI] "Faster writing: run only the chosen experts; uncap the large
+         profile" (#3): only chosen experts need computing; capacity_factor 0
+         means uncapped; the dropped-routing share is reported.
+  [BUG]  "Current Bug: CuTeDSLMoERunner produces wrong output", root-cause
+         section: expert_offsets over the permuted rows, the inclusive form
+         [4, 8, 8] and the leading-zero form [0, 4, 8, 8] for counts [4, 4, 0].
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes of the repository):
+  * router logit = fp32 rounding (RNE) of the fp64 sum x.W_g (+ bias), so a
+    GPU that accumulates in fp64 selects the same experts (certificate below);
+  * equal probabilities are ordered by the lower expert index;
+  * capacity C = max(1, ceil(cf * T * k / E)) with cf the fp32 capacity
+    factor; priority is assignment order a = t*k + j; dropped assignments add
+    nothing and the remaining weights are not renormalised again;
+  * the shared expert has weight 1, is not counted in k and has no capacity.
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Optional, Sequence
+
+import numpy as np
+
+U64 = 2.0 ** -53          # unit roundoff of fp64
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------
+# fp8 e4m3fn codes -> values (OCP 8-bit floating point format, "fn" variant:
+# 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no infinities,
+# exponent 1111 with mantissa 111 is NaN, exponent 0000 is subnormal).
+# ----------------------------------------------------------------------------
+def fp8_e4m3fn_decode(codes) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    exp = (c >> 3) & 0xF
+    man = (c & 0x7).astype(np.float64)
+    normal = (1.0 + man / 8.0) * np.exp2(exp.astype(np.float64) - 7.0)
+    sub = (man / 8.0) * 2.0 ** -6
+    val = sign * np.where(exp == 0, sub, normal)
+    return np.where((exp == 15) & ((c & 7) == 7), np.nan, val)
+
+
+def dequantize(codes, scale, channel_axis: int) -> np.ndarray:
+    """Per-output-channel scaled fp8 weight: w[..., c] = value(q[..., c]) * s[c]."""
+    v = fp8_e4m3fn_decode(codes)
+    shape = [1] * v.ndim
+    shape[channel_axis] = -1
+    return v * _f64(scale).reshape(shape)
+
+
+# ----------------------------------------------------------------------------
+# Router  ([MIX] gate; [DSK] router bias)
+# ----------------------------------------------------------------------------
+def router_logits(x, W_g, bias=None) -> np.ndarray:
+    """logits[t, e] = fp32( sum_i x[t, i] * W_g[i, e] (+ bias[e]) ), fp64 sum."""
+    s = _f64(x) @ _f64(W_g)
+    if bias is not None:
+        s = s + _f64(bias)[None, :]
+    return s.astype(np.float32)
+
+
+def softmax_rows(logits32) -> np.ndarray:
+    """Softmax over the experts of each token, fp64 ([MIX] softmax over dim 1)."""
+    l = _f64(logits32)
+    p = np.empty_like(l)
+    for t in range(l.shape[0]):
+        m = max(l[t])
+        e = np.array([math.exp(v - m) for v in l[t]])
+        p[t] = e / math.fsum(e)
+    return p
+
+
+def topk_select(probs, k: int) -> np.ndarray:
+    """Per token, the k experts of largest probability, largest first; equal
+    probabilities ordered by the lower expert index ([MIX] topk)."""
+    T, E = probs.shape
+    idx = np.empty((T, k), dtype=np.int32)
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-probs[t, e], e))
+        idx[t] = order[:k]
+    return idx
+
+
+def routing_weights(probs, idx, renormalize: bool) -> np.ndarray:
+    """Top-k probabilities, divided by their sum when renormalising ([MIX]
+    'Normalize top-2 weights to sum to 1'; [DSK] same step)."""
+    T, k = idx.shape
+    w = np.empty((T, k), dtype=np.float64)
+    for t in range(T):
+        sel = [probs[t, e] for e in idx[t]]
+        den = math.fsum(sel) if renormalize else 1.0
+        w[t] = [v / den for v in sel]
+    return w
+
+
+# ----------------------------------------------------------------------------
+# Capacity and token-to-expert permutation ([SWT] capacity, [MINI] cf 0 =
+# uncapped, [MIX] per-expert gather order, [BUG] expert_offsets)
+# ----------------------------------------------------------------------------
+def capacity(T: int, k: int, E: int, capacity_factor) -> Optional[int]:
+    cf = float(np.float32(capacity_factor))
+    if not cf > 0.0:
+        return None
+    return max(1, math.ceil(cf * T * k / E))
+
+
+def permute(idx, E: int, cap: Optional[int]) -> dict:
+    """Group assignments a = t*k + j by expert, keeping ascending a inside an
+    expert (the order in which the per-expert loop of [MIX] finds them), and
+    drop an assignment once its expert already holds `cap` earlier ones.
+
+    counts[e]        kept assignments of expert e
+    offsets[E + 1]   exclusive prefix of counts with a leading 0 ([BUG] form)
+    sorted_assign    kept assignment ids, expert-major, ascending a inside
+    inv_perm[a]      position of a in sorted_assign, or -1 when dropped
+    n_dropped        number of dropped assignments
+    """
+    T, k = idx.shape
+    flat = [int(v) for v in np.asarray(idx).reshape(-1)]
+    buckets = [[] for _ in range(E)]
+    dropped = 0
+    for a, e in enumerate(flat):
+        if cap is None or len(buckets[e]) < cap:
+            buckets[e].append(a)
+        else:
+            dropped += 1
+    counts = np.array([len(b) for b in buckets], dtype=np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    sorted_assign = np.array([a for b in buckets for a in b], dtype=np.int32)
+    inv_perm = np.full(T * k, -1, dtype=np.int32)
+    for pos, a in enumerate(sorted_assign):
+        inv_perm[a] = pos
+    return dict(counts=counts, offsets=offsets, sorted_assign=sorted_assign,
+                inv_perm=inv_perm, n_dropped=dropped)
+
+
+# ----------------------------------------------------------------------------
+# Expert FFN ([MIX] "Expert FFN": w2(silu(w1 x) * w3 x), no biases).  Weights
+# are stored input-major: W_gate = w1 and W_up = w3 as [d, f], W_down = w2 as
+# [f, d], so a row vector x maps to x @ W.
+# ----------------------------------------------------------------------------
+def silu(z) -> np.ndarray:
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(X, W_gate, W_up, W_down) -> np.ndarray:
+    X = _f64(X)
+    G = X @ _f64(W_gate)
+    U = X @ _f64(W_up)
+    H = silu(G) * U
+    return H @ _f64(W_down)
+
+
+# ----------------------------------------------------------------------------
+# Whole layer
+# ----------------------------------------------------------------------------
+ExpertFn = Callable[[int], Sequence[np.ndarray]]
+
+
+def forward(x, W_g, bias, k: int, renormalize: bool, capacity_factor,
+            expert: ExpertFn, E: int, shared: Optional[Sequence[np.ndarray]] = None,
+            tokens: Optional[Sequence[int]] = None) -> dict:
+    """Routed MoE SwiGLU layer.
+
+    expert(e) returns (W_gate[d,f], W_up[d,f], W_down[f,d]) of expert e as
+    arrays widened to fp64 by the caller's choice (fp8 callers pass the
+    dequantized values).  `shared` is the shared expert's triple or None.
+    Routing and permutation are computed for every token; the expert FFN and
+    the weighted sum only for `tokens` (all when None), so large layers can be
+    checked on a sample.  out rows follow the order of `tokens`.
+    """
+    x = _f64(x)
+    T = x.shape[0]
+    logits = router_logits(x, W_g, bias)
+    probs = softmax_rows(logits)
+    idx = topk_select(probs, k)
+    w = routing_weights(probs, idx, renormalize)
+    cap = capacity(T, k, E, capacity_factor)
+    perm = permute(idx, E, cap)
+
+    toks = list(range(T)) if tokens is None else [int(t) for t in tokens]
+    want = set(toks)
+    y_assign = {}                       # a -> expert output row (fp64)
+    offs, sa = perm["offsets"], perm["sorted_assign"]
+    for e in range(E):
+        rows = [int(a) for a in sa[offs[e]:offs[e + 1]] if int(a) // k in want]
+        if not rows:                    # experts without tokens do no work ([MIX])
+            continue
+        Y = expert_ffn(x[[a // k for a in rows]], *expert(e))
+        for a, y in zip(rows, Y):
+            y_assign[a] = y
+
+    out = np.zeros((len(toks), x.shape[1]), dtype=np.float64)
+    for r, t in enumerate(toks):
+        acc = np.zeros(x.shape[1], dtype=np.float64)
+        for j in range(k):              # weighted sum in slot order
+            a = t * k + j
+            if perm["inv_perm"][a] >= 0:
+                acc = acc + w[t, j] * y_assign[a]
+        out[r] = acc
+    if shared is not None:              # [DSK]: shared output + routed output
+        out = out + expert_ffn(x[toks], *shared)
+    return dict(logits=logits, probs=probs, topk_idx=idx, topk_w=w, capacity=cap,
+                out=out, tokens=np.array(toks, dtype=np.int64), **perm)
+
+
+# ----------------------------------------------------------------------------
+# Routing certificate: the selection and slot order are the same for every
+# fp64 summation order when adjacent fp64 logit sums among the top k+1 are
+# separated by more than both sums' worst-case error plus two fp32 ulps.
+# ----------------------------------------------------------------------------
+def routing_certificate(x, W_g, bias, k: int) -> dict:
+    x, W = _f64(x), _f64(W_g)
+    T, d = x.shape
+    E = W.shape[1]
+    s = x @ W
+    if bias is not None:
+        s = s + _f64(bias)[None, :]
+    gamma = (d + 1) * U64 / (1.0 - (d + 1) * U64)
+    bound = gamma * (np.abs(x) @ np.abs(W))
+    if bias is not None:
+        bound = bound + gamma * np.abs(_f64(bias))[None, :]
+    ok = np.ones(T, dtype=bool)
+    margin = np.full(T, np.inf)
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-s[t, e], e))[:min(k + 1, E)]
+        for a, b in zip(order[:-1], order[1:]):
+            ulp = float(np.spacing(np.float32(max(abs(s[t, a]), abs(s[t, b])))))
+            need = 2.0 * (bound[t, a] + bound[t, b]) + 2.0 * ulp
+            gap = s[t, a] - s[t, b]
+            margin[t] = min(margin[t], gap - need)
+            if not gap > need:
+                ok[t] = False
+    return dict(ok=ok, margin=margin)

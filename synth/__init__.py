@@ -1,0 +1,179 @@
+"""Seeded synthetic inputs for the routed MoE SwiGLU feed-forward layer.
+
+This module only draws random tensors and stores them in the types the layer
+consumes (fp32, bf16, or OCP fp8 e4m3fn codes with per-output-channel fp32
+scale factors).  It holds none of the layer's arithmetic: the CPU oracle (fed
+by the tests) and the HIP library both receive exactly the tensors returned
+here, so the two sides never share code beyond this input recipe.
+
+Recipe (every tensor has its own seed derived from the config seed, the tensor
+name and the expert id, so one expert can be regenerated on its own):
+  x        ~ N(0, 1)     drawn in fp32, then stored in the activation dtype
+  W_g      ~ N(0, 0.02)  router weight [d, E], activation dtype
+  experts  ~ N(0, 0.02)  W_gate/W_up [E, d, f], W_down [E, f, d]
+  bias     optional per-expert router bias, b[e] = -s * ln(e + 1) (Zipf rank
+           weights in log space), fp32
+  fp8      per output channel c: s[c] = max|w[:, c]| / 448, q = RNE(w / s)
+           as float8_e4m3fn (the largest finite e4m3fn value is 448).
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+FP8_MAX = 448.0
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    name: str
+    T: int
+    d: int
+    E: int
+    k: int
+    f: int
+    act: str = "bf16"          # activation / router dtype: "f32" | "bf16"
+    wdt: str = "bf16"          # expert weight dtype: "f32" | "bf16" | "fp8"
+    renormalize: bool = True
+    capacity_factor: float = 0.0   # 0 => uncapped
+    shared: bool = False       # one always-on shared expert (same f)
+    bias: str = "none"         # "none" | "zipf"
+    zipf_s: float = 1.1
+    seed: int = 0
+    x_std: float = 1.0
+    w_std: float = 0.02
+
+    def with_(self, **kw) -> "MoEConfig":
+        return dataclasses.replace(self, **kw)
+
+    @property
+    def n_assign(self) -> int:
+        return self.T * self.k
+
+
+# The five workloads (sizes from the pages' model shapes: Mixtral 8x7B
+# hidden 4096 / intermediate 14336 / 8 experts / top-2; a fine-grained
+# DeepSeek-style layer with shared expert; an fp8 layer with capacity).
+CONFIGS = {
+    "tiny_f32": MoEConfig("tiny_f32", T=64, d=256, E=8, k=2, f=512, act="f32", wdt="f32"),
+    "mixtral_decode": MoEConfig("mixtral_decode", T=1, d=4096, E=8, k=2, f=14336),
+    "mixtral_decode_b8": MoEConfig("mixtral_decode_b8", T=8, d=4096, E=8, k=2, f=14336),
+    "mixtral_prefill": MoEConfig("mixtral_prefill", T=4096, d=4096, E=8, k=2, f=14336),
+    "fine_grained": MoEConfig("fine_grained", T=2048, d=7168, E=256, k=8, f=2048,
+                              shared=True, bias="zipf"),
+    "fp8_capacity": MoEConfig("fp8_capacity", T=512, d=2048, E=128, k=8, f=768,
+                              wdt="fp8", capacity_factor=1.25),
+    "fp8_capacity_decode": MoEConfig("fp8_capacity_decode", T=1, d=2048, E=128, k=8, f=768,
+                                     wdt="fp8", capacity_factor=1.25),
+}
+
+
+def tensor_seed(seed: int, name: str, expert: int = -1) -> int:
+    h = hashlib.sha256(f"{seed}/{name}/{expert}".encode()).digest()
+    return int.from_bytes(h[:8], "little") & ((1 << 63) - 1)
+
+
+def _normal(shape, std, seed, device) -> torch.Tensor:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t
+
+
+def _store(t32: torch.Tensor, dt: str) -> torch.Tensor:
+    if dt == "f32":
+        return t32
+    if dt == "bf16":
+        return t32.to(torch.bfloat16)
+    raise ValueError(dt)
+
+
+def quantize_fp8_per_channel(w32: torch.Tensor, channel_dim: int):
+    """w32 fp32 -> (q float8_e4m3fn, s fp32 per channel along channel_dim)."""
+    red = [i for i in range(w32.dim()) if i != channel_dim]
+    amax = w32.abs().amax(dim=red)
+    s = torch.clamp(amax, min=1e-30) / FP8_MAX
+    shape = [1] * w32.dim()
+    shape[channel_dim] = -1
+    q = torch.clamp(w32 / s.view(shape), -FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
+    return q, s.to(torch.float32)
+
+
+def _expert_mats(cfg: MoEConfig, tag: str, e: int, device):
+    wg = _normal((cfg.d, cfg.f), cfg.w_std, tensor_seed(cfg.seed, tag + "gate", e), device)
+    wu = _normal((cfg.d, cfg.f), cfg.w_std, tensor_seed(cfg.seed, tag + "up", e), device)
+    wd = _normal((cfg.f, cfg.d), cfg.w_std, tensor_seed(cfg.seed, tag + "down", e), device)
+    return wg, wu, wd
+
+
+def router_bias(cfg: MoEConfig, device="cpu") -> Optional[torch.Tensor]:
+    if cfg.bias == "none":
+        return None
+    if cfg.bias == "zipf":
+        r = torch.arange(cfg.E, dtype=torch.float64)
+        return (-cfg.zipf_s * torch.log1p(r)).to(torch.float32).to(device)
+    raise ValueError(cfg.bias)
+
+
+def make_inputs(cfg: MoEConfig, device="cpu") -> dict:
+    """All tensors of one layer call, on `device` (contiguous, row-major).
+
+    keys: x [T,d]; W_g [d,E]; bias [E] | None; W_gate, W_up [E,d,f];
+    W_down [E,f,d]; s_gate, s_up [E,f], s_down [E,d] (fp8 only, else None);
+    Ws_gate, Ws_up [d,f], Ws_down [f,d] (+ ss_gate, ss_up, ss_down for fp8)
+    when cfg.shared, else None.
+    """
+    dev = torch.device(device)
+    out = {"cfg": cfg}
+    out["x"] = _store(_normal((cfg.T, cfg.d), cfg.x_std, tensor_seed(cfg.seed, "x"), dev), cfg.act)
+    out["W_g"] = _store(_normal((cfg.d, cfg.E), cfg.w_std, tensor_seed(cfg.seed, "router"), dev), cfg.act)
+    out["bias"] = router_bias(cfg, dev)
+
+    def alloc(shape):
+        dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[cfg.wdt]
+        return torch.empty(shape, dtype=dt, device=dev)
+
+    E, d, f = cfg.E, cfg.d, cfg.f
+    Wg, Wu, Wd = alloc((E, d, f)), alloc((E, d, f)), alloc((E, f, d))
+    fp8 = cfg.wdt == "fp8"
+    if fp8:
+        sg = torch.empty((E, f), dtype=torch.float32, device=dev)
+        su = torch.empty((E, f), dtype=torch.float32, device=dev)
+        sd = torch.empty((E, d), dtype=torch.float32, device=dev)
+    for e in range(E):
+        wg, wu, wd = _expert_mats(cfg, "", e, dev)
+        if fp8:
+            Wg[e], sg[e] = quantize_fp8_per_channel(wg, 1)
+            Wu[e], su[e] = quantize_fp8_per_channel(wu, 1)
+            Wd[e], sd[e] = quantize_fp8_per_channel(wd, 1)
+        else:
+            Wg[e], Wu[e], Wd[e] = _store(wg, cfg.wdt), _store(wu, cfg.wdt), _store(wd, cfg.wdt)
+        del wg, wu, wd
+    out.update(W_gate=Wg, W_up=Wu, W_down=Wd)
+    out.update(s_gate=sg if fp8 else None, s_up=su if fp8 else None, s_down=sd if fp8 else None)
+
+    out.update(Ws_gate=None, Ws_up=None, Ws_down=None, ss_gate=None, ss_up=None, ss_down=None)
+    if cfg.shared:
+        wg, wu, wd = _expert_mats(cfg, "shared_", 0, dev)
+        if fp8:
+            out["Ws_gate"], out["ss_gate"] = quantize_fp8_per_channel(wg, 1)
+            out["Ws_up"], out["ss_up"] = quantize_fp8_per_channel(wu, 1)
+            out["Ws_down"], out["ss_down"] = quantize_fp8_per_channel(wd, 1)
+        else:
+            out["Ws_gate"], out["Ws_up"], out["Ws_down"] = (
+                _store(wg, cfg.wdt), _store(wu, cfg.wdt), _store(wd, cfg.wdt))
+    return out
+
+
+def weight_bytes_per_expert(cfg: MoEConfig) -> int:
+    es = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.wdt]
+    b = 3 * cfg.d * cfg.f * es
+    if cfg.wdt == "fp8":
+        b += (2 * cfg.f + cfg.d) * 4
+    return b

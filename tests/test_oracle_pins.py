@@ -1,0 +1,361 @@
+"""Pins of the CPU oracle to facts outside itself (no GPU needed).
+
+Each test checks the oracle against something the oracle does not compute the
+same way: a value printed on the pages (tests/golden), a library routine
+(torch / scipy), a closed form, an invariant of the method, or brute force on
+tiny inputs.  A plausible slip in the oracle (a dropped term, a wrong sign or
+index, a transposed operand, a wrong tie rule) fails at least one of them.
+"""
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+RNG = np.random.default_rng(1234)
+
+
+def bf16_values(shape, std, rng=RNG):
+    """Random values exactly representable in bf16 (as float64)."""
+    t = torch.from_numpy(rng.normal(0.0, std, size=shape).astype(np.float32))
+    return t.to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def read_golden(golden_dir, name):
+    rows = {}
+    with open(os.path.join(golden_dir, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            rows[key] = [int(v) for v in vals]
+    return rows
+
+
+# --------------------------------------------------------------------------
+# Permutation / expert_offsets
+# --------------------------------------------------------------------------
+def test_offsets_worked_example_from_pages(golden_dir):
+    g = read_golden(golden_dir, "expert_offsets_worked_example.txt")
+    E = g["E"][0]
+    # four tokens, each choosing experts 0 and 1 -> counts [4, 4, 0]
+    idx = np.array([[0, 1]] * 4, dtype=np.int32)
+    p = oracle.permute(idx, E, None)
+    assert p["counts"].tolist() == g["counts"]
+    assert p["offsets"].tolist() == g["offsets_leading_zero"]
+    assert p["offsets"][1:].tolist() == g["offsets_inclusive"]
+    rows0 = list(range(p["offsets"][0], p["offsets"][1]))
+    rows1 = list(range(p["offsets"][1], p["offsets"][2]))
+    assert rows0 == g["rows_expert0"] and rows1 == g["rows_expert1"]
+    assert p["offsets"][2] == p["offsets"][3]          # empty expert 2
+    # expert 0's rows hold the slot-0 assignments in token order
+    assert [int(a) for a in p["sorted_assign"][:4]] == [0, 2, 4, 6]
+    assert p["n_dropped"] == 0
+
+
+def _brute_permute(flat, E, cap):
+    n = len(flat)
+    rank = [sum(1 for b in range(a) if flat[b] == flat[a]) for a in range(n)]
+    kept = [cap is None or rank[a] < cap for a in range(n)]
+    order = sorted((a for a in range(n) if kept[a]), key=lambda a: (flat[a], a))
+    counts = [sum(1 for a in range(n) if kept[a] and flat[a] == e) for e in range(E)]
+    return order, counts, n - sum(kept)
+
+
+@pytest.mark.parametrize("T,k,E,cap", [(7, 2, 5, None), (13, 3, 4, 4), (1, 4, 8, 1),
+                                        (20, 1, 3, 2), (0, 2, 4, None), (9, 4, 4, None)])
+def test_permute_brute_force(T, k, E, cap):
+    rng = np.random.default_rng(T * 100 + k)
+    idx = np.array([rng.permutation(E)[:k] for _ in range(T)], dtype=np.int32).reshape(T, k)
+    p = oracle.permute(idx, E, cap)
+    order, counts, nd = _brute_permute(idx.reshape(-1).tolist(), E, cap)
+    assert p["sorted_assign"].tolist() == order
+    assert p["counts"].tolist() == counts
+    assert p["n_dropped"] == nd
+    assert p["offsets"].tolist() == [0] + list(np.cumsum(counts))
+    # inverse permutation
+    for pos, a in enumerate(order):
+        assert p["inv_perm"][a] == pos
+    assert int((p["inv_perm"] < 0).sum()) == nd
+    assert p["offsets"][-1] == T * k - nd
+
+
+def test_capacity_special_cases():
+    assert oracle.capacity(512, 8, 128, 1.25) == 40
+    assert oracle.capacity(1, 8, 128, 1.25) == 1
+    assert oracle.capacity(100, 2, 8, 0.0) is None
+    # every token on expert 0: the first C assignments in token order are kept
+    T, k, E = 10, 1, 4
+    idx = np.zeros((T, k), dtype=np.int32)
+    C = oracle.capacity(T, k, E, 1.0)           # ceil(10/4) = 3
+    assert C == 3
+    p = oracle.permute(idx, E, C)
+    assert p["sorted_assign"].tolist() == [0, 1, 2]
+    assert p["n_dropped"] == 7
+    assert p["inv_perm"].tolist() == [0, 1, 2] + [-1] * 7
+    # one token: its k experts are distinct, nothing can be dropped
+    idx1 = np.array([[3, 1, 2, 0]], dtype=np.int32)
+    p1 = oracle.permute(idx1, 4, oracle.capacity(1, 4, 4, 1.25))
+    assert p1["n_dropped"] == 0 and p1["sorted_assign"].tolist() == [3, 1, 2, 0]
+
+
+# --------------------------------------------------------------------------
+# Router logits, softmax, top-k, weights
+# --------------------------------------------------------------------------
+def test_router_logits_exact_rounding():
+    T, d, E = 5, 24, 7
+    x = bf16_values((T, d), 1.0)
+    W = bf16_values((d, E), 0.02)
+    b = np.float32(RNG.normal(size=E)).astype(np.float64)
+    got = oracle.router_logits(x, W, b)
+    assert got.dtype == np.float32 and got.shape == (T, E)
+    for t in range(T):
+        for e in range(E):
+            exact = sum(Fraction(x[t, i]) * Fraction(W[i, e]) for i in range(d)) + Fraction(b[e])
+            # bf16 products of this spread sum exactly in fp64, so one rounding to fp32 remains
+            assert Fraction(float(exact)) == exact
+            assert got[t, e] == np.float32(float(exact))
+
+
+def test_softmax_matches_scipy_and_topk_weights():
+    from scipy.special import softmax
+    l = np.float32(RNG.normal(size=(9, 6)) * 3)
+    p = oracle.softmax_rows(l)
+    np.testing.assert_allclose(p, softmax(l.astype(np.float64), axis=1), rtol=1e-14, atol=0)
+    for k in (1, 2, 6):
+        idx = oracle.topk_select(p, k)
+        w_on = oracle.routing_weights(p, idx, True)
+        w_off = oracle.routing_weights(p, idx, False)
+        np.testing.assert_allclose(w_on.sum(1), 1.0, rtol=0, atol=1e-15)
+        np.testing.assert_array_equal(w_off, np.take_along_axis(p, idx.astype(np.int64), 1))
+        if k == 1:
+            assert np.all(w_on == 1.0)             # top-1 (Switch) weight is exactly 1
+        if k == 6:
+            np.testing.assert_allclose(w_on, w_off, rtol=1e-14)
+
+
+def test_softmax_closed_forms():
+    l = np.array([[0.5, 0.5, -np.inf]], dtype=np.float32)
+    p = oracle.softmax_rows(l)
+    assert p[0, 0] == p[0, 1] == 0.5 and p[0, 2] == 0.0
+    l2 = np.array([[np.float32(2.0), np.float32(2.0) - np.float32(math.log(3.0))]], dtype=np.float32)
+    p2 = oracle.softmax_rows(l2)
+    r = math.exp(float(l2[0, 0]) - float(l2[0, 1]))
+    np.testing.assert_allclose(p2[0], [r / (1 + r), 1 / (1 + r)], rtol=1e-15)
+    np.testing.assert_allclose(p2[0], [0.75, 0.25], rtol=1e-7)
+
+
+def _brute_topk(l, k):
+    E = len(l)
+    fr = [Fraction(float(v)) for v in l]
+    best = None
+    for sub in itertools.combinations(range(E), k):
+        key = (sum(fr[e] for e in sub), tuple(-e for e in sub))
+        if best is None or key > best[0]:
+            best = (key, sub)
+    return set(best[1])
+
+
+@pytest.mark.parametrize("trial", range(40))
+def test_topk_brute_force_with_ties(trial):
+    rng = np.random.default_rng(trial)
+    E = int(rng.integers(1, 9))
+    k = int(rng.integers(1, E + 1))
+    # few distinct values so ties are common
+    l = np.float32(rng.integers(-3, 3, size=E) * 0.25 + (0 if trial % 2 else rng.normal(size=E)))
+    p = oracle.softmax_rows(l[None, :])
+    idx = oracle.topk_select(p, k)[0].tolist()
+    assert set(idx) == _brute_topk(l, k)
+    for a, b in zip(idx[:-1], idx[1:]):            # slots: larger first, ties lower index first
+        assert l[a] > l[b] or (l[a] == l[b] and a < b)
+
+
+# --------------------------------------------------------------------------
+# fp8 e4m3fn decoding vs torch's float8_e4m3fn type
+# --------------------------------------------------------------------------
+def test_fp8_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.fp8_e4m3fn_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    m = ~np.isnan(ref)
+    assert np.array_equal(got[m], ref[m])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+
+
+def test_dequantize_channel_axis():
+    q = torch.tensor([[1.0, 2.0, -0.5], [4.0, 0.25, 448.0]]).to(torch.float8_e4m3fn)
+    s = np.array([0.5, 2.0, 1.0 / 448.0], dtype=np.float32)
+    w = oracle.dequantize(q.view(torch.uint8).numpy(), s, 1)
+    np.testing.assert_array_equal(w, q.to(torch.float64).numpy() * s.astype(np.float64)[None, :])
+
+
+# --------------------------------------------------------------------------
+# Expert FFN and the whole layer
+# --------------------------------------------------------------------------
+def torch_dense_swiglu(x, wg, wu, wd):
+    X = torch.from_numpy(np.asarray(x, np.float64))
+    G = X @ torch.from_numpy(np.asarray(wg, np.float64))
+    U = X @ torch.from_numpy(np.asarray(wu, np.float64))
+    return (torch.nn.functional.silu(G) * U) @ torch.from_numpy(np.asarray(wd, np.float64))
+
+
+def test_silu_against_torch_and_identity():
+    z = np.linspace(-40, 40, 1001)
+    ref = torch.nn.functional.silu(torch.from_numpy(z)).numpy()
+    np.testing.assert_allclose(oracle.silu(z), ref, rtol=1e-15, atol=1e-300)
+    np.testing.assert_allclose(oracle.silu(z) - oracle.silu(-z), z, rtol=1e-14, atol=1e-14)
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+
+
+def _layer(T, d, E, k, f, shared=False, seed=0):
+    rng = np.random.default_rng(seed)
+    x = bf16_values((T, d), 1.0, rng)
+    Wg = bf16_values((d, E), 0.3, rng)
+    ex = [(bf16_values((d, f), 0.2, rng), bf16_values((d, f), 0.2, rng),
+           bf16_values((f, d), 0.2, rng)) for _ in range(E)]
+    sh = (bf16_values((d, f), 0.2, rng), bf16_values((d, f), 0.2, rng),
+          bf16_values((f, d), 0.2, rng)) if shared else None
+    return x, Wg, ex, sh
+
+
+def test_single_expert_top1_is_dense_swiglu():
+    T, d, f = 13, 24, 40                        # d != f catches a transposed operand
+    x, Wg, ex, _ = _layer(T, d, 1, 1, f)
+    r = oracle.forward(x, Wg, None, 1, True, 0.0, lambda e: ex[e], 1)
+    assert np.all(r["topk_w"] == 1.0)
+    ref = torch_dense_swiglu(x, *ex[0]).numpy()
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+def test_gather_chosen_equals_all_experts(renorm):
+    T, d, E, k, f = 17, 16, 6, 2, 24
+    x, Wg, ex, _ = _layer(T, d, E, k, f, seed=3)
+    r = oracle.forward(x, Wg, None, k, renorm, 0.0, lambda e: ex[e], E)
+    full = np.zeros((T, E))
+    for t in range(T):
+        for j in range(k):
+            full[t, r["topk_idx"][t, j]] = r["topk_w"][t, j]
+    # every expert on every token, weighted by 0 where not chosen
+    all_out = sum(full[:, e:e + 1] * torch_dense_swiglu(x, *ex[e]).numpy() for e in range(E))
+    np.testing.assert_allclose(r["out"], all_out, rtol=1e-12, atol=1e-12)
+
+
+def test_expert_permutation_invariance():
+    T, d, E, k, f = 11, 16, 7, 3, 20
+    x, Wg, ex, _ = _layer(T, d, E, k, f, seed=5)
+    bias = np.float32(np.random.default_rng(9).normal(size=E))
+    cert = oracle.routing_certificate(x, Wg, bias, k)
+    assert cert["ok"].all()
+    r0 = oracle.forward(x, Wg, bias, k, True, 0.0, lambda e: ex[e], E)
+    pi = np.random.default_rng(11).permutation(E)
+    r1 = oracle.forward(x, Wg[:, pi], bias[pi], k, True, 0.0, lambda e: ex[pi[e]], E)
+    np.testing.assert_array_equal(pi[r1["topk_idx"]], r0["topk_idx"])
+    np.testing.assert_allclose(r1["topk_w"], r0["topk_w"], rtol=1e-15)
+    np.testing.assert_allclose(r1["out"], r0["out"], rtol=1e-13, atol=1e-13)
+
+
+def test_shared_expert_is_additive():
+    T, d, E, k, f = 9, 16, 5, 2, 24
+    x, Wg, ex, sh = _layer(T, d, E, k, f, shared=True, seed=7)
+    a = oracle.forward(x, Wg, None, k, True, 0.0, lambda e: ex[e], E, shared=sh)
+    b = oracle.forward(x, Wg, None, k, True, 0.0, lambda e: ex[e], E, shared=None)
+    np.testing.assert_allclose(a["out"] - b["out"], torch_dense_swiglu(x, *sh).numpy(),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_token_sample_matches_full_layer():
+    T, d, E, k, f = 21, 16, 6, 2, 24
+    x, Wg, ex, sh = _layer(T, d, E, k, f, shared=True, seed=8)
+    full = oracle.forward(x, Wg, None, k, True, 1.0, lambda e: ex[e], E, shared=sh)
+    toks = [20, 3, 0, 11]
+    part = oracle.forward(x, Wg, None, k, True, 1.0, lambda e: ex[e], E, shared=sh, tokens=toks)
+    np.testing.assert_allclose(part["out"], full["out"][toks], rtol=1e-13, atol=1e-15)
+    for key in ("topk_idx", "sorted_assign", "inv_perm", "offsets"):
+        np.testing.assert_array_equal(part[key], full[key])
+
+
+def _fsum_layer(x, Wg, ex, k, renorm, cap, shared):
+    """Pure-Python brute force with exactly rounded sums (math.fsum)."""
+    T, d = x.shape
+    E = Wg.shape[1]
+    f = ex[0][0].shape[1]
+
+    def ffn(v, wg, wu, wd):
+        g = [math.fsum(v[i] * wg[i, c] for i in range(d)) for c in range(f)]
+        u = [math.fsum(v[i] * wu[i, c] for i in range(d)) for c in range(f)]
+        h = [g[c] / (1.0 + math.exp(-g[c])) * u[c] for c in range(f)]
+        return [math.fsum(h[c] * wd[c, o] for c in range(f)) for o in range(d)]
+
+    seen = [0] * E
+    out = []
+    for t in range(T):
+        lg = [float(np.float32(math.fsum(x[t, i] * Wg[i, e] for i in range(d)))) for e in range(E)]
+        m = max(lg)
+        ex_ = [math.exp(v - m) for v in lg]
+        z = math.fsum(ex_)
+        pr = [v / z for v in ex_]
+        chosen = sorted(range(E), key=lambda e: (-pr[e], e))[:k]
+        den = math.fsum(pr[e] for e in chosen) if renorm else 1.0
+        acc = [0.0] * d
+        for e in chosen:
+            keep = cap is None or seen[e] < cap
+            seen[e] += 1
+            if keep:
+                y = ffn(x[t], *ex[e])
+                acc = [acc[o] + pr[e] / den * y[o] for o in range(d)]
+        if shared is not None:
+            y = ffn(x[t], *shared)
+            acc = [acc[o] + y[o] for o in range(d)]
+        out.append(acc)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("renorm,cf,shared", [(True, 0.0, False), (False, 0.0, True), (True, 1.0, False)])
+def test_brute_force_tiny_layer(renorm, cf, shared):
+    T, d, E, k, f = 6, 8, 4, 2, 16
+    x, Wg, ex, sh = _layer(T, d, E, k, f, shared=shared, seed=21)
+    cap = oracle.capacity(T, k, E, cf)
+    r = oracle.forward(x, Wg, None, k, renorm, cf, lambda e: ex[e], E, shared=sh)
+    if cf > 0:
+        assert cap == 3
+    ref = _fsum_layer(x, Wg, ex, k, renorm, cap, sh)
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_tiny_config_subset_brute_force():
+    """The tiny fp32 workload's own inputs, first tokens, checked by brute force."""
+    cfg = synth.CONFIGS["tiny_f32"].with_(T=3, d=32, f=16)
+    inp = synth.make_inputs(cfg)
+    x = inp["x"].double().numpy()
+    Wg = inp["W_g"].double().numpy()
+    ex = [(inp["W_gate"][e].double().numpy(), inp["W_up"][e].double().numpy(),
+           inp["W_down"][e].double().numpy()) for e in range(cfg.E)]
+    r = oracle.forward(x, Wg, None, cfg.k, True, 0.0, lambda e: ex[e], cfg.E)
+    ref = _fsum_layer(x, Wg, ex, cfg.k, True, None, None)
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-15)
+
+
+def test_certificate_flags_near_ties():
+    x = np.array([[1.0, 1.0]])
+    W = np.array([[0.5, 0.5, 0.1], [0.25, 0.25, 0.0]])    # experts 0 and 1 tie exactly
+    c = oracle.routing_certificate(x, W, None, 2)
+    assert not c["ok"][0]
+    W2 = np.array([[0.5, 0.25, 0.1], [0.25, 0.25, 0.0]])
+    assert oracle.routing_certificate(x, W2, None, 2)["ok"][0]
+
+
+def test_workload_shapes_match_pages(golden_dir):
+    rows = read_golden(golden_dir, "mixtral_shapes.txt")
+    for name in ("mixtral_decode", "mixtral_decode_b8", "mixtral_prefill"):
+        c = synth.CONFIGS[name]
+        assert (c.d, c.f, c.E, c.k) == (rows["hidden_size"][0], rows["intermediate_size"][0],
+                                        rows["num_local_experts"][0], rows["num_experts_per_tok"][0])
