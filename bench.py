@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Throughput of the routed MoE SwiGLU layer forward on one MI355X.
+
+One step = one whole layer call (router -> top-k -> dispatch -> expert SwiGLU
+FFN -> weighted combine) on seeded synthetic inputs already resident in HBM.
+The default workload is the Mixtral-shaped single-token decode (T=1, d=4096,
+E=8, top-2, f=14336, bf16).  Expert weights rotate over several copies so that
+every step streams them from HBM, not from the 256 MB last-level cache.
+
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (timed
+live with HIP events on the layer's stream around every launch of it), and
+the CPU oracle timed on a bounded sample on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0        # dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3
+LLC_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="mixtral_decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain device copy of known size (for HBM counter scaling)")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on its own stream)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+
+def algorithmic_work(cfg, counts, touched):
+    """Bytes and flops the layer must move/do for this routing (per call)."""
+    import synth
+    es = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.wdt]
+    ae = 4 if cfg.act == "f32" else 2
+    wexp = synth.weight_bytes_per_expert(cfg)
+    n_exp = touched + (1 if cfg.shared else 0)
+    bytes_total = cfg.T * cfg.d * ae + cfg.d * cfg.E * ae + n_exp * wexp + cfg.T * cfg.d * ae
+    rows = int(sum(counts)) + (cfg.T if cfg.shared else 0)
+    flops = 2 * cfg.T * cfg.d * cfg.E + 6 * rows * cfg.d * cfg.f
+    return bytes_total, flops, n_exp * wexp, es
+
+
+def cpu_baseline(cfg, inp, budget_s=12.0, max_calls=64):
+    """The CPU oracle, as it stands, on single-token (decode) or small-batch calls."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    import torch
+    to64 = lambda t: t.detach().to(torch.float64).cpu().numpy()
+    x = to64(inp["x"])
+    W_g = to64(inp["W_g"])
+    bias = None if inp["bias"] is None else to64(inp["bias"])
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            if cfg.wdt == "fp8":
+                cd = lambda t: t.contiguous().view(torch.uint8).cpu().numpy()
+                cache[e] = (oracle.dequantize(cd(inp["W_gate"][e]), inp["s_gate"][e].cpu().numpy(), 1),
+                            oracle.dequantize(cd(inp["W_up"][e]), inp["s_up"][e].cpu().numpy(), 1),
+                            oracle.dequantize(cd(inp["W_down"][e]), inp["s_down"][e].cpu().numpy(), 1))
+            else:
+                cache[e] = (to64(inp["W_gate"][e]), to64(inp["W_up"][e]), to64(inp["W_down"][e]))
+        return cache[e]
+
+    shared = None
+    if cfg.shared:
+        shared = (to64(inp["Ws_gate"]), to64(inp["Ws_up"]), to64(inp["Ws_down"]))
+    tb = min(cfg.T, 8)             # tokens per oracle call
+    call = lambda t0: oracle.forward(x[t0:t0 + tb], W_g, bias, cfg.k, cfg.renormalize,
+                                     np.float32(cfg.capacity_factor), expert, cfg.E, shared=shared)
+    call(0)                        # untimed: widen the touched experts' weights once
+    n = 0
+    t_start = time.perf_counter()
+    while n < max_calls and (time.perf_counter() - t_start) < budget_s:
+        call((n * tb) % max(1, cfg.T - tb + 1))
+        n += 1
+    dt = time.perf_counter() - t_start
+    return {"value": n * tb / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} oracle layer calls of {tb} token(s) each of the {cfg.name} workload "
+                      f"(routing over all E experts, fp64 SwiGLU of the chosen experts), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported on this build "
+              "(the layer shards by tokens or experts; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    from sparse_mixture_experts_12_amd import _lib as ops
+
+    cfg = synth.CONFIGS[args.workload]
+    decode = cfg.T <= 8 and cfg.act == "bf16"
+    steps = args.steps if args.steps is not None else (200 if decode else 20)
+    warmup = args.warmup if args.warmup is not None else (10 if decode else 3)
+    print(f"[bench] workload={cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} f={cfg.f} "
+          f"act={cfg.act} w={cfg.wdt} steps={steps} warmup={warmup}", file=sys.stderr, flush=True)
+
+    inp = synth.make_inputs(cfg, "cuda")
+    wbytes = synth.weight_bytes_per_expert(cfg) * (cfg.E + (1 if cfg.shared else 0))
+    n_copies = max(1, min(8, math.ceil(2 * LLC_BYTES / max(1, wbytes)) + 1)) if wbytes < 4 * LLC_BYTES else 1
+    if decode:
+        n_copies = max(n_copies, 2)
+    copies = [inp]
+    for _ in range(n_copies - 1):
+        c = dict(inp)
+        for key in ("W_gate", "W_up", "W_down", "Ws_gate", "Ws_up", "Ws_down"):
+            if inp.get(key) is not None:
+                c[key] = inp[key].clone()
+        copies.append(c)
+    wstructs = [ops.weights_struct(c) for c in copies]
+    desc = ops.desc_from_cfg(cfg)
+    ws = ops.alloc_workspace(desc)
+    dt = torch.float32 if cfg.act == "f32" else torch.bfloat16
+    out = torch.empty((cfg.T, cfg.d), dtype=dt, device="cuda")
+    counts = torch.zeros(cfg.E, dtype=torch.int32, device="cuda")
+    nd = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    # routing facts for the algorithmic work (one untimed call with stats)
+    st0 = ops.Stats(d_n_dropped=nd.data_ptr(), d_counts=counts.data_ptr())
+    path = ops.forward(desc, inp["x"], wstructs[0], out, ws, stats=st0)
+    torch.cuda.synchronize()
+    cnt = counts.cpu().numpy()
+    touched = int((cnt > 0).sum())
+    n_dropped = int(nd.cpu()[0])
+
+    hev = HipEvents()
+    ev_b = [hev.create() for _ in range(steps)]
+    ev_e = [hev.create() for _ in range(steps)]
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        ops.forward(desc, inp["x"], wstructs[i % n_copies], out, ws)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    stats = [ops.Stats(ev_begin=ev_b[i].value, ev_end=ev_e[i].value) for i in range(steps)]
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        ops.forward(desc, inp["x"], wstructs[i % n_copies], out, ws, stats=stats[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    kern_ms = sum(hev.elapsed_ms(ev_b[i], ev_e[i]) for i in range(steps)) / steps
+    ms_per_step = total_ms / steps
+    tokens_per_s = cfg.T * steps / (total_ms / 1e3)
+
+    bytes_total, flops, wbytes_used, _ = algorithmic_work(cfg, cnt, touched)
+    if decode:
+        # dominant kernel = fused decode FFN: streams the chosen experts' weights (+ x)
+        ae = 2
+        kbytes = wbytes_used + cfg.T * cfg.d * ae
+        achieved = kbytes / (kern_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "decode_ffn_kernel", "kernel_ms": round(kern_ms, 5), "alg_bytes": int(kbytes)}
+    else:
+        # dominant kernel = grouped gate/up GEMM + SwiGLU: 2/3 of the expert flops
+        rows = int(cnt.sum()) + (cfg.T if cfg.shared else 0)
+        kflops = 4 * rows * cfg.d * cfg.f
+        achieved = kflops / (kern_ms / 1e3) / 1e12
+        peak = FP32_PEAK_TFLOPS if cfg.act == "f32" else BF16_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": "gemm_mfma_kernel<gate/up>" if cfg.act != "f32" else "gemm_f32_kernel<gate/up>",
+                "kernel_ms": round(kern_ms, 5), "alg_flops": int(kflops)}
+
+    if args.copy_calibration:
+        n = 1 << 28
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, inp)
+
+    line = {
+        "metric": "MoE-layer tokens/s; decode HBM GB/s, prefill MFMA TFLOP/s vs peak",
+        "value": round(tokens_per_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "bf16 x fp8"}[cfg.wdt] if cfg.act == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "top_k": cfg.k, "f": cfg.f,
+                   "act": cfg.act, "weights": cfg.wdt, "shared_expert": cfg.shared,
+                   "capacity_factor": cfg.capacity_factor, "path": "fused_decode" if path == 2 else "grouped",
+                   "experts_touched": touched, "dropped_share": n_dropped / max(1, cfg.T * cfg.k),
+                   "weight_copies": n_copies},
+        "layer": {"alg_bytes": int(bytes_total), "alg_flops": int(flops),
+                  "hbm_GBps": round(bytes_total / (ms_per_step / 1e3) / 1e9, 1),
+                  "tflops": round(flops / (ms_per_step / 1e3) / 1e12, 3)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+/*
+ * moe.h -- C ABI of the routed Mixture-of-Experts SwiGLU feed-forward layer
+ * (forward pass) for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (page "MoE Model Architectures", Mixtral 8x7B sections "Sparse
+ * MoE Block" and "Expert FFN"; DeepSeek-V3 section "DeepSeekMoE
+ * Architecture"):
+ *     logits = x W_g (+ b)                      router gate
+ *     p      = softmax(logits)                  over the E experts
+ *     (idx, w) = top_k(p), w /= sum(w)          renormalisation optional
+ *     out[t] = sum_j w[t,j] * FFN_{idx[t,j]}(x[t])  (+ FFN_shared(x[t]))
+ *     FFN_e(v) = (silu(v W_gate[e]) * (v W_up[e])) W_down[e]
+ *
+ * Conventions shared by every entry point
+ *  - All data pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates device memory, never frees, and never synchronises the
+ *    host: every call only enqueues kernels on `stream` and returns.  Scratch
+ *    memory comes from the caller's workspace (`ws`, `ws_bytes`), sized by
+ *    moe_workspace_size().  All buffers sized by routing use their worst case
+ *    (T*k rows), so no count is ever read back to the host; calls can be
+ *    captured into a HIP graph.
+ *  - Arrays are dense and row-major.  x is [T, d]; W_g is [d, E]; expert
+ *    weights are input-major: W_gate, W_up are [E, d, f] and W_down is
+ *    [E, f, d] (the transpose of a torch nn.Linear weight).
+ *  - Arguments are validated on the host before any HIP call.  A failing
+ *    call returns a status code and enqueues nothing; moe_last_error()
+ *    describes the failure (thread-local text).
+ *  - T == 0 is valid and enqueues nothing.
+ *  - Results are bitwise deterministic run to run: no floating-point atomics.
+ *  - Calls on the same stream are ordered; calls that share a workspace must
+ *    not run concurrently on different streams.
+ *
+ * Conventions fixed here where the pages are silent (see the design notes):
+ *  - Router logits are rounded to fp32 once from an fp64 sum (+ bias), and
+ *    experts are selected on those fp32 logits, larger first, equal logits
+ *    ordered by the lower expert index.  Softmax weights are fp32.
+ *  - Capacity (capacity_factor > 0): C = max(1, ceil(cf * T * k / E)); an
+ *    assignment a = t*k + j is kept when fewer than C earlier assignments
+ *    (smaller a) went to the same expert.  Dropped assignments contribute
+ *    nothing and the kept weights are not renormalised again.
+ *    capacity_factor == 0 means uncapped (page "Faster writing: run only the
+ *    chosen experts; uncap the large profile", the profile change to 0).
+ *  - expert offsets have E + 1 entries with a leading 0 (the GPU-computed form
+ *    in "Current Bug: CuTeDSLMoERunner produces wrong output", root-cause
+ *    section); rows of one expert are kept in ascending assignment order.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size or flag   */
+  MOE_ERR_UNSUPPORTED = 2,   /* valid request this library does not handle */
+  MOE_ERR_WORKSPACE = 3,     /* ws too small (see moe_workspace_size)        */
+  MOE_ERR_HIP = 4            /* a kernel launch failed                      */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;  /* FP8 = OCP e4m3fn */
+
+typedef enum {
+  MOE_PATH_AUTO = 0,         /* fused decode for T <= 8, grouped otherwise        */
+  MOE_PATH_GROUPED = 1,      /* permute + grouped GEMMs + combine at any T        */
+  MOE_PATH_FUSED_DECODE = 2  /* T <= 8 only; larger T returns UNSUPPORTED         */
+} moe_path;
+
+#define MOE_FUSED_DECODE_MAX_T 8
+
+typedef struct {
+  int32_t T;                 /* tokens, >= 0                                     */
+  int32_t d;                 /* hidden size, multiple of 64                      */
+  int32_t E;                 /* routed experts, 1..1023                          */
+  int32_t top_k;             /* 1..min(E, 32)                                    */
+  int32_t f;                 /* expert intermediate size, multiple of 64         */
+  int32_t renormalize;       /* 0 | 1                                            */
+  float capacity_factor;     /* 0 => uncapped; else > 0 and finite               */
+  int32_t act_dtype;         /* x, W_g, out: MOE_F32 | MOE_BF16                  */
+  int32_t w_dtype;           /* experts: F32 (act F32) | BF16 or FP8_E4M3 (act BF16) */
+  int32_t has_shared;        /* 0 | 1: one always-on shared expert, weight 1     */
+  int32_t path;              /* moe_path                                         */
+} moe_desc;
+
+typedef struct {
+  const void* W_g;           /* [d, E] act dtype                                  */
+  const float* router_bias;  /* [E] fp32 or NULL; added to the logits           */
+  const void* W_gate;        /* [E, d, f] w dtype                                 */
+  const void* W_up;          /* [E, d, f]                                         */
+  const void* W_down;        /* [E, f, d]                                         */
+  const float* s_gate;       /* FP8 only: [E, f] per-output-channel scale, else NULL */
+  const float* s_up;         /* FP8 only: [E, f]                                  */
+  const float* s_down;       /* FP8 only: [E, d]                                  */
+  const void* Ws_gate;       /* shared expert [d, f] (has_shared) else NULL       */
+  const void* Ws_up;         /* [d, f]                                            */
+  const void* Ws_down;       /* [f, d]                                            */
+  const float* ss_gate;      /* FP8 shared scales [f], [f], [d] else NULL         */
+  const float* ss_up;
+  const float* ss_down;
+} moe_weights;
+
+typedef struct {
+  int32_t path_taken;        /* out: MOE_PATH_GROUPED or MOE_PATH_FUSED_DECODE    */
+  int32_t* d_n_dropped;      /* device [1] or NULL: dropped assignments           */
+  int32_t* d_counts;         /* device [E] or NULL: kept assignments per expert   */
+  hipEvent_t ev_begin;       /* NULL or an event recorded on `stream` just before */
+  hipEvent_t ev_end;         /* ... and just after the dominant expert-FFN kernel */
+} moe_stats;
+
+/* Bytes of workspace every entry point below needs for `desc` (the maximum
+ * over entry points).  Returns 0 when desc is invalid. */
+size_t moe_workspace_size(const moe_desc* desc);
+
+/* Per-expert capacity C for desc, or -1 when uncapped / desc invalid. */
+int32_t moe_capacity(const moe_desc* desc);
+
+/* Router: logits, softmax, top-k and (optional) renormalisation.
+ * Pages: "MoE Model Architectures", "Sparse MoE Block" (gate, softmax, topk,
+ * divide by the top-k sum), "Auxiliary-Loss-Free Load Balancing" (bias);
+ * "perf(moe): route granite-4.0-h single-token MoE through the fused kernel"
+ * (fp32 softmax scores already equal the renormalised top-k softmax).
+ *   x        [T, d] act dtype
+ *   topk_idx [T, k] int32 out: slot 0 holds the largest logit
+ *   topk_w   [T, k] fp32 out: softmax weights of the chosen experts
+ *   logits   [T, E] fp32 out, or NULL (then the workspace holds them) */
+moe_status moe_route(const moe_desc* desc, const void* x, const moe_weights* w,
+                     int32_t* topk_idx, float* topk_w, float* logits,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Token-to-expert permutation with capacity dropping.
+ * Pages: "Sparse MoE Block" (per-expert gather in token order, empty experts
+ * skipped); "Current Bug: CuTeDSLMoERunner produces wrong output" (expert
+ * offsets); "Top-1 Routing" (expert capacity, overflow dropped).
+ *   topk_idx      [T, k] int32 in, values in [0, E)
+ *   counts        [E]      kept assignments per expert
+ *   offsets       [E + 1]  exclusive prefix of counts, offsets[0] = 0
+ *   sorted_assign [T * k]  kept assignment ids a = t*k + j, expert-major,
+ *                          ascending a inside an expert; entries from
+ *                          offsets[E] on are set to -1
+ *   inv_perm      [T * k]  row of a in sorted_assign, or -1 if dropped
+ *   n_dropped     [1]      number of dropped assignments */
+moe_status moe_permute(const moe_desc* desc, const int32_t* topk_idx,
+                       int32_t* counts, int32_t* offsets, int32_t* sorted_assign,
+                       int32_t* inv_perm, int32_t* n_dropped,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Grouped SwiGLU expert FFN over the permuted rows; only experts with rows
+ * do work.  Pages: "Expert FFN" (w2(silu(w1 x) * w3 x)); "Faster writing: run
+ * only the chosen experts" (touch only chosen experts' weights).
+ *   sorted_assign, offsets  as produced by moe_permute (may come from elsewhere)
+ *   y_sorted  [T*k (+ T when has_shared), d] fp32 out: row r < offsets[E] is
+ *             FFN_e(x[sorted_assign[r] / k]) for the expert e owning row r;
+ *             rows T*k + t hold the shared expert's FFN(x[t]); other rows are
+ *             left untouched. */
+moe_status moe_grouped_ffn(const moe_desc* desc, const void* x, const moe_weights* w,
+                           const int32_t* sorted_assign, const int32_t* offsets,
+                           float* y_sorted, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Weighted combine: out[t] = sum_{j kept} topk_w[t,j] * y_sorted[inv_perm[t*k+j]]
+ * (+ y_sorted[T*k + t] with has_shared), summed in slot order in fp32 and
+ * rounded once to the act dtype.  Pages: "Sparse MoE Block" (weighted
+ * index_add), "Design Patterns" (shared + routed). */
+moe_status moe_combine(const moe_desc* desc, const float* y_sorted, const int32_t* inv_perm,
+                       const float* topk_w, void* out, hipStream_t stream);
+
+/* Whole layer: route -> (permute -> grouped FFN -> combine) or, for T <= 8,
+ * route -> fused decode (streams only the chosen experts' weights; page
+ * "perf(moe): route granite-4.0-h single-token MoE through the fused
+ * kernel").  out [T, d] act dtype.  stats may be NULL. */
+moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, void* out,
+                       moe_stats* stats, void* ws, size_t ws_bytes, hipStream_t stream);
+
+const char* moe_status_string(moe_status s);
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

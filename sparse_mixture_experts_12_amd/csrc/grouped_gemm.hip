@@ -1,0 +1,500 @@
+// Grouped SwiGLU expert FFN on gfx950.
+//
+// Pages: "MoE Model Architectures", Mixtral "Expert FFN" (w2(silu(w1 x) *
+// w3 x), no biases) and "Sparse MoE Block" (only experts that received
+// tokens run); DeepSeek-V3 "DeepSeekMoE Architecture" (an always-on shared
+// expert); "Faster writing: run only the chosen experts; uncap the large
+// profile" (read only the chosen experts' weights).
+//
+// Two kernels per call, both driven by a device-side tile schedule built from
+// the expert offsets (so no count is read back to the host):
+//   gate/up: H[r, n] = silu(A[r] . Wg[:, n]) * (A[r] . Wu[:, n]), A[r] the x
+//            row of the token owning permuted row r;  H is bf16 (fp32 for the
+//            fp32 layer)
+//   down:    Y[r, n] = H[r] . Wd[:, n]  (fp32)
+//
+// bf16 path: 256 threads (4 waves), v_mfma_f32_32x32x16_bf16, fp32
+// accumulation, K step 64, LDS double buffer.  The weights are stored
+// input-major ([K, N], N contiguous) while MFMA wants K-contiguous operands
+// per lane, so each thread loads an 8(k) x 8(n) block with coalesced row
+// reads, transposes it in registers and writes eight K-contiguous 16-byte
+// vectors to LDS.  fp8 e4m3fn weights are widened to bf16 (exact) in the same
+// step; their per-output-channel scales multiply the accumulators in the
+// epilogue.  LDS rows are 128 bytes (64 bf16 of K); the 16-byte chunk index
+// is XOR-swizzled with (row ^ row >> 3) & 7 so that both the transposing
+// stores and the MFMA operand reads spread over all banks.
+//
+// Work-group ids are remapped so that consecutive tiles (same weight column
+// tile, neighbouring row tiles of one expert) run on the same XCD and share
+// its L2.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kBK = 64;
+
+struct GemmParams {
+  const bf16_t* x;               // DUAL: activations [T, d]
+  const int32_t* sorted_assign;  // DUAL: permuted row -> assignment
+  const bf16_t* a_rows;          // !DUAL: H [rows, f]
+  const void* W0;                // DUAL: gate [E, K, N]; !DUAL: down [E, K, N]
+  const void* W1;                // DUAL: up
+  const void* Ws0;               // shared expert matrices
+  const void* Ws1;
+  const float* s0;               // fp8 scales [E, N] (gate or down)
+  const float* s1;               // fp8 scales up
+  const float* ss0;
+  const float* ss1;
+  const int32_t* sched;
+  int maxQ;
+  int T, k, E, K, N;
+  int shared_row0;               // T*k
+  bf16_t* h_out;                 // DUAL output [rows, N]
+  float* y_out;                  // !DUAL output [rows, N]
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row ^ (row >> 3)) & 7); }
+
+// Decode a logical tile id into (group, row0, rows, n-tile).
+__device__ __forceinline__ bool decode_tile(const int32_t* sched, int maxQ, int n_tiles, int* g, int* row0, int* rows,
+                                            int* nt) {
+  const int Q = sched[0];
+  const int total = Q * n_tiles;
+  const int per = (total + 7) >> 3;
+  const int bid = blockIdx.x;
+  const int slot = bid >> 3;
+  const int logical = (bid & 7) * per + slot;
+  if (slot >= per || logical >= total) return false;
+  const int q0 = logical / n_tiles;
+  const int grp = sched[1 + 4 * q0 + 0];
+  const int first = sched[1 + 4 * q0 + 3];
+  const int mg = sched[1 + 4 * maxQ + grp];
+  const int local = logical - first * n_tiles;
+  const int j = local / mg;
+  const int i = local - j * mg;
+  const int q = first + i;
+  *g = grp;
+  *row0 = sched[1 + 4 * q + 1];
+  *rows = sched[1 + 4 * q + 2];
+  *nt = j;
+  return true;
+}
+
+// 8 rows x 8 bf16 (row-major, 16 B per row) -> 8 vectors of 8 K-values.
+__device__ __forceinline__ void transpose8x8_bf16(const uint4 (&r)[8], uint4 (&o)[8]) {
+  const uint32_t* rw[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) rw[j] = reinterpret_cast<const uint32_t*>(&r[j]);
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    uint32_t d[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t a = rw[2 * p][n >> 1], b = rw[2 * p + 1][n >> 1];
+      d[p] = (n & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+    o[n] = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+}
+
+// fp8 e4m3fn (8 per row, 8 B) -> bf16 bits, then transpose.
+__device__ __forceinline__ void fp8_rows_to_bf16(const uint2 (&r8)[8], uint4 (&r)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float v[8];
+    fp8x4_to_f32(r8[j].x, v);
+    fp8x4_to_f32(r8[j].y, v + 4);
+    // values have at most 4 significant bits: the top 16 bits are exact bf16
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) w[p] = (__float_as_uint(v[2 * p]) >> 16) | (__float_as_uint(v[2 * p + 1]) & 0xffff0000u);
+    r[j] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+template <int WK, bool DUAL, int WM>
+__global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmParams p) {
+  constexpr int WN = 4 / WM;
+  constexpr int BM = 64 * WM;
+  constexpr int NMAT = DUAL ? 2 : 1;
+  constexpr int BN_MAT = DUAL ? 128 : 256;         // output columns per tile
+  constexpr int NI_MAT = BN_MAT / WN / 32;         // 32-wide MFMA column tiles per matrix per wave
+  constexpr int NI = NI_MAT * NMAT;
+  constexpr int MI = 2;                            // 64 rows per wave
+  constexpr int A_CHUNKS = BM * 8 / 256;           // 16-byte chunks per thread
+  constexpr int LDS_A = BM * kBK;                  // bf16 elements per stage
+  constexpr int LDS_B = 256 * kBK;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * (LDS_A + LDS_B)];
+
+  const int n_tiles = (p.N + BN_MAT - 1) / BN_MAT;
+  int g, row0, rows, nt;
+  if (!decode_tile(p.sched, p.maxQ, n_tiles, &g, &row0, &rows, &nt)) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const int n0 = nt * BN_MAT;
+  const bool shared = (g == p.E);
+
+  // ---- A row sources (fixed for the tile) ----
+  const bf16_t* arow[A_CHUNKS];
+  int akc[A_CHUNKS], ar[A_CHUNKS];
+#pragma unroll
+  for (int i = 0; i < A_CHUNKS; ++i) {
+    const int c = tid + 256 * i;
+    const int r = c >> 3;
+    ar[i] = r;
+    akc[i] = c & 7;
+    const int grow = row0 + r;
+    if (r < rows) {
+      if (DUAL) {
+        int tok = shared ? (grow - p.shared_row0) : (p.sorted_assign[grow] / p.k);
+        arow[i] = p.x + (size_t)tok * p.K;
+      } else {
+        arow[i] = p.a_rows + (size_t)grow * p.K;
+      }
+    } else {
+      arow[i] = nullptr;
+    }
+  }
+  // ---- B block (8 k x 8 n) of this thread ----
+  const int nb = tid & 31;
+  const int kb = tid >> 5;
+  int mat = 0, ncol;
+  if (DUAL) {
+    mat = nb >> 4;
+    ncol = n0 + (nb & 15) * 8;
+  } else {
+    ncol = n0 + nb * 8;
+  }
+  const bool b_ok = ncol < p.N;
+  const size_t wstride = (size_t)p.K * p.N;
+  const void* Wbase;
+  if (shared) Wbase = mat ? p.Ws1 : p.Ws0;
+  else Wbase = mat ? p.W1 : p.W0;
+  const size_t goff = shared ? 0 : (size_t)g * wstride;
+  // row n of this block in the LDS B tile
+  const int bn_row0 = DUAL ? (mat * 128 + (nb & 15) * 8) : nb * 8;
+
+  uint4 areg[A_CHUNKS];
+  uint4 breg[8];
+  uint2 breg8[8];
+
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i)
+      areg[i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0 + akc[i] * 8) : make_uint4(0, 0, 0, 0);
+    if (WK == W_FP8) {
+      const fp8_t* wb = (const fp8_t*)Wbase + goff + (size_t)(k0 + kb * 8) * p.N + ncol;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        breg8[j] = b_ok ? *reinterpret_cast<const uint2*>(wb + (size_t)j * p.N) : make_uint2(0, 0);
+    } else {
+      const bf16_t* wb = (const bf16_t*)Wbase + goff + (size_t)(k0 + kb * 8) * p.N + ncol;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        breg[j] = b_ok ? *reinterpret_cast<const uint4*>(wb + (size_t)j * p.N) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_tile = [&](int stage) {
+    bf16_t* As = lds + stage * (LDS_A + LDS_B);
+    bf16_t* Bs = As + LDS_A;
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i)
+      *reinterpret_cast<uint4*>(As + ar[i] * kBK + swz(ar[i], akc[i]) * 8) = areg[i];
+    if (WK == W_FP8) fp8_rows_to_bf16(breg8, breg);
+    uint4 o[8];
+    transpose8x8_bf16(breg, o);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int row = bn_row0 + n;
+      *reinterpret_cast<uint4*>(Bs + row * kBK + swz(row, kb) * 8) = o[n];
+    }
+  };
+
+  f32x16_t acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+
+  const int nK = p.K / kBK;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  const int l32 = lane & 31;
+  const int lhi = lane >> 5;
+  for (int kt = 0; kt < nK; ++kt) {
+    const int stage = kt & 1;
+    if (kt + 1 < nK) load_tile((kt + 1) * kBK);
+    const bf16_t* As = lds + stage * (LDS_A + LDS_B);
+    const bf16_t* Bs = As + LDS_A;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int chunk = ks * 2 + lhi;
+      bf16x8_t af[MI], bfr[NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int row = wm * 64 + mi * 32 + l32;
+        af[mi] = *reinterpret_cast<const bf16x8_t*>(As + row * kBK + swz(row, chunk) * 8);
+      }
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        int row;
+        if (DUAL) {
+          const int m_ = ni / NI_MAT, nl = ni % NI_MAT;
+          row = m_ * 128 + wn * (128 / WN) + nl * 32 + l32;
+        } else {
+          row = wn * (256 / WN) + ni * 32 + l32;
+        }
+        bfr[ni] = *reinterpret_cast<const bf16x8_t*>(Bs + row * kBK + swz(row, chunk) * 8);
+      }
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+    }
+    if (kt + 1 < nK) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue ----
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+    for (int nl = 0; nl < NI_MAT; ++nl) {
+      const int col = n0 + wn * (BN_MAT / WN) + nl * 32 + l32;
+      if (col >= p.N) continue;
+      float sc0 = 1.f, sc1 = 1.f;
+      if (WK == W_FP8) {
+        if (shared) {
+          sc0 = p.ss0[col];
+          if (DUAL) sc1 = p.ss1[col];
+        } else {
+          sc0 = p.s0[(size_t)g * p.N + col];
+          if (DUAL) sc1 = p.s1[(size_t)g * p.N + col];
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * 64 + mi * 32 + (v >> 2) * 8 + lhi * 4 + (v & 3);
+        if (r >= rows) continue;
+        const size_t orow = (size_t)(row0 + r) * p.N;
+        if (DUAL) {
+          const float gv = acc[mi][nl][v] * sc0;
+          const float uv = acc[mi][nl + NI_MAT][v] * sc1;
+          p.h_out[orow + col] = (bf16_t)f32_to_bf16(silu_f(gv) * uv);
+        } else {
+          p.y_out[orow + col] = acc[mi][nl][v] * sc0;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 layer: SIMT grouped GEMM, 64 rows x 64 columns per tile, fp32 FMA.
+// ---------------------------------------------------------------------------
+struct GemmParamsF32 {
+  const float* x;
+  const int32_t* sorted_assign;
+  const float* a_rows;
+  const float *W0, *W1, *Ws0, *Ws1;
+  const int32_t* sched;
+  int maxQ, T, k, E, K, N, shared_row0;
+  float* h_out;
+  float* y_out;
+};
+
+template <bool DUAL>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
+  constexpr int BM = 64, BN = 64, BK = 16;
+  __shared__ float As[BK][BM + 4];
+  __shared__ float Bs[DUAL ? 2 : 1][BK][BN + 4];
+  const int n_tiles = (p.N + BN - 1) / BN;
+  int g, row0, rows, nt;
+  if (!decode_tile(p.sched, p.maxQ, n_tiles, &g, &row0, &rows, &nt)) return;
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int n0 = nt * BN;
+  const bool shared = (g == p.E);
+  const size_t goff = shared ? 0 : (size_t)g * p.K * p.N;
+  const float* B0 = (shared ? p.Ws0 : p.W0 + goff);
+  const float* B1 = DUAL ? (shared ? p.Ws1 : p.W1 + goff) : nullptr;
+  // A rows loaded by this thread: 4 rows (r = tid / 16 + 16 * i), 1 k each
+  const float* arow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (tid >> 4) + 16 * i;
+    const int grow = row0 + r;
+    if (r < rows) {
+      if (DUAL) {
+        const int tok = shared ? (grow - p.shared_row0) : (p.sorted_assign[grow] / p.k);
+        arow[i] = p.x + (size_t)tok * p.K;
+      } else {
+        arow[i] = p.a_rows + (size_t)grow * p.K;
+      }
+    } else {
+      arow[i] = nullptr;
+    }
+  }
+  float acc0[4][4], acc1[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc0[i][j] = acc1[i][j] = 0.f;
+  for (int k0 = 0; k0 < p.K; k0 += BK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) As[tx][(tid >> 4) + 16 * i] = arow[i] ? arow[i][k0 + tx] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i;
+      const int kk = e >> 6, nn = e & 63;
+      const int col = n0 + nn;
+      Bs[0][kk][nn] = col < p.N ? B0[(size_t)(k0 + kk) * p.N + col] : 0.f;
+      if (DUAL) Bs[DUAL ? 1 : 0][kk][nn] = col < p.N ? B1[(size_t)(k0 + kk) * p.N + col] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float a[4], b0[4], b1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        b0[j] = Bs[0][kk][tx * 4 + j];
+        if (DUAL) b1[j] = Bs[DUAL ? 1 : 0][kk][tx * 4 + j];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc0[i][j] = __fmaf_rn(a[i], b0[j], acc0[i][j]);
+          if (DUAL) acc1[i][j] = __fmaf_rn(a[i], b1[j], acc1[i][j]);
+        }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = ty * 4 + i;
+    if (r >= rows) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + tx * 4 + j;
+      if (col >= p.N) continue;
+      const size_t o = (size_t)(row0 + r) * p.N + col;
+      if (DUAL) p.h_out[o] = silu_f(acc0[i][j]) * acc1[i][j];
+      else p.y_out[o] = acc0[i][j];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+static int pick_bm(const GroupedArgs& a) {
+  if (a.act_f32) return 64;
+  const int avg = (a.T * a.k) / (a.E > 0 ? a.E : 1);
+  return avg >= 96 ? 128 : 64;
+}
+
+static int max_row_tiles(int T, int k, int E, int has_shared, int BM) {
+  const int n = T * k;
+  int q = n / BM + (n < E ? n : E);
+  if (has_shared) q += (T + BM - 1) / BM;
+  return q;
+}
+
+size_t grouped_sched_ints(int T, int k, int E, int has_shared) {
+  // enough for the smallest tile height used (64 rows)
+  return 1 + 4 * (size_t)max_row_tiles(T, k, E, has_shared, 64) + (E + 1) + 16;
+}
+
+static inline int grid_for(int maxQ, int n_tiles) {
+  long total = (long)maxQ * n_tiles;
+  long per = (total + 7) / 8;
+  return (int)(8 * per);
+}
+
+hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
+  const int BM = pick_bm(a);
+  const int maxQ = max_row_tiles(a.T, a.k, a.E, a.has_shared, BM);
+  const int shared_rows = a.has_shared ? a.T : 0;
+  const int shared_row0 = a.T * a.k;
+  hipError_t err = launch_tile_schedule(a.offsets, a.E, BM, shared_rows, shared_row0, maxQ, a.sched, s);
+  if (err != hipSuccess) return err;
+
+  if (a.act_f32) {
+    GemmParamsF32 p{};
+    p.x = (const float*)a.x;
+    p.sorted_assign = a.sorted_assign;
+    p.sched = a.sched;
+    p.maxQ = maxQ;
+    p.T = a.T; p.k = a.k; p.E = a.E; p.shared_row0 = shared_row0;
+    // gate/up
+    p.W0 = (const float*)a.w.Wg; p.W1 = (const float*)a.w.Wu;
+    p.Ws0 = (const float*)a.w.Wsg; p.Ws1 = (const float*)a.w.Wsu;
+    p.K = a.d; p.N = a.f;
+    p.h_out = (float*)a.h;
+    if (a.ev_begin) hipEventRecord(a.ev_begin, s);
+    gemm_f32_kernel<true><<<grid_for(maxQ, (a.f + 63) / 64), 256, 0, s>>>(p);
+    if (a.ev_end) hipEventRecord(a.ev_end, s);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    // down
+    GemmParamsF32 q = p;
+    q.a_rows = (const float*)a.h;
+    q.W0 = (const float*)a.w.Wd; q.Ws0 = (const float*)a.w.Wsd;
+    q.W1 = nullptr; q.Ws1 = nullptr;
+    q.K = a.f; q.N = a.d;
+    q.y_out = a.y;
+    gemm_f32_kernel<false><<<grid_for(maxQ, (a.d + 63) / 64), 256, 0, s>>>(q);
+    return hipGetLastError();
+  }
+
+  GemmParams p{};
+  p.x = (const bf16_t*)a.x;
+  p.sorted_assign = a.sorted_assign;
+  p.sched = a.sched;
+  p.maxQ = maxQ;
+  p.T = a.T; p.k = a.k; p.E = a.E; p.shared_row0 = shared_row0;
+  p.W0 = a.w.Wg; p.W1 = a.w.Wu; p.Ws0 = a.w.Wsg; p.Ws1 = a.w.Wsu;
+  p.s0 = a.w.sg; p.s1 = a.w.su; p.ss0 = a.w.ssg; p.ss1 = a.w.ssu;
+  p.K = a.d; p.N = a.f;
+  p.h_out = (bf16_t*)a.h;
+  const int gu_grid = grid_for(maxQ, (a.f + 127) / 128);
+  if (a.ev_begin) hipEventRecord(a.ev_begin, s);
+  if (a.wkind == W_FP8) {
+    if (BM == 128) gemm_mfma_kernel<W_FP8, true, 2><<<gu_grid, 256, 0, s>>>(p);
+    else gemm_mfma_kernel<W_FP8, true, 1><<<gu_grid, 256, 0, s>>>(p);
+  } else {
+    if (BM == 128) gemm_mfma_kernel<W_BF16, true, 2><<<gu_grid, 256, 0, s>>>(p);
+    else gemm_mfma_kernel<W_BF16, true, 1><<<gu_grid, 256, 0, s>>>(p);
+  }
+  if (a.ev_end) hipEventRecord(a.ev_end, s);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  GemmParams q = p;
+  q.a_rows = (const bf16_t*)a.h;
+  q.W0 = a.w.Wd; q.W1 = nullptr; q.Ws0 = a.w.Wsd; q.Ws1 = nullptr;
+  q.s0 = a.w.sd; q.s1 = nullptr; q.ss0 = a.w.ssd; q.ss1 = nullptr;
+  q.K = a.f; q.N = a.d;
+  q.y_out = a.y;
+  const int dn_grid = grid_for(maxQ, (a.d + 255) / 256);
+  if (a.wkind == W_FP8) {
+    if (BM == 128) gemm_mfma_kernel<W_FP8, false, 2><<<dn_grid, 256, 0, s>>>(q);
+    else gemm_mfma_kernel<W_FP8, false, 1><<<dn_grid, 256, 0, s>>>(q);
+  } else {
+    if (BM == 128) gemm_mfma_kernel<W_BF16, false, 2><<<dn_grid, 256, 0, s>>>(q);
+    else gemm_mfma_kernel<W_BF16, false, 1><<<dn_grid, 256, 0, s>>>(q);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

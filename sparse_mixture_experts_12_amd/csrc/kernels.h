@@ -1,0 +1,88 @@
+// Internal launch interface between the C-ABI layer and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kDecodeMaxT = 8;
+
+struct RouteArgs {
+  const void* x;
+  const void* W_g;
+  const float* bias;
+  int T, d, E, k, renormalize;
+  int cap;          // -1: uncapped
+  bool act_f32;
+  float* logits;    // [T, E]; required when T > kDecodeMaxT
+  int32_t* idx;     // [T, k]
+  float* w;         // [T, k]
+  int32_t* plan;    // decode plan or nullptr (T <= kDecodeMaxT only)
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+struct PermuteArgs {
+  const int32_t* idx;
+  int n, E, cap;
+  int32_t *counts, *offsets, *sorted_assign, *inv_perm, *n_dropped, *rank_ws;
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+hipError_t launch_tile_schedule(const int32_t* offsets, int E, int BM, int shared_rows, int shared_row0, int maxQ,
+                                int32_t* sched, hipStream_t s);
+
+// Expert weights of one group set: routed experts [E,...] plus the optional
+// shared expert, addressed as group E.
+struct ExpertWeights {
+  const void *Wg, *Wu, *Wd;             // [E,d,f], [E,d,f], [E,f,d]
+  const float *sg, *su, *sd;            // fp8 scales or nullptr
+  const void *Wsg, *Wsu, *Wsd;          // shared expert or nullptr
+  const float *ssg, *ssu, *ssd;
+};
+
+enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
+
+struct GroupedArgs {
+  const void* x;                 // [T, d] act
+  const int32_t* sorted_assign;  // routed rows -> assignment id
+  const int32_t* offsets;        // [E + 1]
+  ExpertWeights w;
+  int T, d, E, k, f;
+  int has_shared;
+  int wkind;                     // WKind
+  bool act_f32;
+  float* y;                      // [T*k (+T), d] fp32
+  void* h;                       // [T*k (+T), f] bf16 (or fp32 for act f32)
+  int32_t* sched;                // schedule scratch
+  int32_t* sched2;               // second schedule (down GEMM uses its own BM)
+  hipEvent_t ev_begin, ev_end;
+};
+size_t grouped_sched_ints(int T, int k, int E, int has_shared);
+hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s);
+
+struct DecodeArgs {
+  const void* x;                 // [T, d] act
+  const int32_t* plan;           // from the small-T router
+  const float* topk_w;           // [T, k]
+  ExpertWeights w;
+  int T, d, E, k, f, has_shared, wkind;
+  bool act_f32;
+  float* partial;                // scratch
+  void* out;                     // [T, d] act
+  hipEvent_t ev_begin, ev_end;
+};
+size_t decode_partial_bytes(int T, int d, int E, int k, int f, int has_shared, int wkind);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+struct CombineArgs {
+  const float* y;
+  const int32_t* inv_perm;
+  const float* w;
+  int T, d, k, has_shared;
+  bool act_f32;
+  void* out;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,360 @@
+// C ABI of the MoE layer library (declared in include/moe.h): argument
+// validation, workspace layout and kernel sequencing.  No device memory is
+// allocated here and the host never waits on the device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+moe_status check_desc(const moe_desc* d) {
+  if (!d) return fail(MOE_ERR_INVALID_ARG, "desc is NULL");
+  if (d->T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%d < 0", d->T);
+  if (d->d < 64 || d->d % 64) return fail(MOE_ERR_INVALID_ARG, "d=%d must be a positive multiple of 64", d->d);
+  if (d->f < 64 || d->f % 64) return fail(MOE_ERR_INVALID_ARG, "f=%d must be a positive multiple of 64", d->f);
+  if (d->E < 1 || d->E > kMaxExperts - 1) return fail(MOE_ERR_INVALID_ARG, "E=%d outside 1..%d", d->E, kMaxExperts - 1);
+  const int kmax = d->E < kMaxTopK ? d->E : kMaxTopK;
+  if (d->top_k < 1 || d->top_k > kmax) return fail(MOE_ERR_INVALID_ARG, "top_k=%d outside 1..%d", d->top_k, kmax);
+  if (d->renormalize != 0 && d->renormalize != 1) return fail(MOE_ERR_INVALID_ARG, "renormalize must be 0 or 1");
+  if (d->has_shared != 0 && d->has_shared != 1) return fail(MOE_ERR_INVALID_ARG, "has_shared must be 0 or 1");
+  if (!(d->capacity_factor >= 0.f) || !isfinite(d->capacity_factor))
+    return fail(MOE_ERR_INVALID_ARG, "capacity_factor must be finite and >= 0");
+  if (d->path < MOE_PATH_AUTO || d->path > MOE_PATH_FUSED_DECODE) return fail(MOE_ERR_INVALID_ARG, "bad path");
+  if ((long long)d->T * d->top_k > (1LL << 24)) return fail(MOE_ERR_INVALID_ARG, "T*top_k too large");
+  const int a = d->act_dtype, w = d->w_dtype;
+  if (a != MOE_F32 && a != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "bad act_dtype %d", a);
+  if (w != MOE_F32 && w != MOE_BF16 && w != MOE_FP8_E4M3) return fail(MOE_ERR_INVALID_ARG, "bad w_dtype %d", w);
+  const bool ok = (a == MOE_F32 && w == MOE_F32) || (a == MOE_BF16 && (w == MOE_BF16 || w == MOE_FP8_E4M3));
+  if (!ok) return fail(MOE_ERR_UNSUPPORTED, "dtype pair act=%d w=%d not supported", a, w);
+  if (d->path == MOE_PATH_FUSED_DECODE) {
+    if (d->T > MOE_FUSED_DECODE_MAX_T)
+      return fail(MOE_ERR_UNSUPPORTED, "fused decode path takes T <= %d (T=%d)", MOE_FUSED_DECODE_MAX_T, d->T);
+    if (a != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "fused decode path takes bf16 activations");
+  }
+  return MOE_OK;
+}
+
+#define REQ(p, name)                                                                    \
+  do {                                                                                  \
+    if (!(p)) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", name);                     \
+    if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "%s not 16-byte aligned", name); \
+  } while (0)
+#define OPT(p, name)                                                                             \
+  do {                                                                                           \
+    if ((p) && !aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "%s not 16-byte aligned", name); \
+  } while (0)
+
+moe_status check_router_weights(const moe_weights* w) {
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  REQ(w->W_g, "W_g");
+  OPT(w->router_bias, "router_bias");
+  return MOE_OK;
+}
+
+moe_status check_expert_weights(const moe_desc* d, const moe_weights* w) {
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  REQ(w->W_gate, "W_gate");
+  REQ(w->W_up, "W_up");
+  REQ(w->W_down, "W_down");
+  const bool fp8 = d->w_dtype == MOE_FP8_E4M3;
+  if (fp8) {
+    REQ(w->s_gate, "s_gate");
+    REQ(w->s_up, "s_up");
+    REQ(w->s_down, "s_down");
+  }
+  if (d->has_shared) {
+    REQ(w->Ws_gate, "Ws_gate");
+    REQ(w->Ws_up, "Ws_up");
+    REQ(w->Ws_down, "Ws_down");
+    if (fp8) {
+      REQ(w->ss_gate, "ss_gate");
+      REQ(w->ss_up, "ss_up");
+      REQ(w->ss_down, "ss_down");
+    }
+  }
+  return MOE_OK;
+}
+
+int capacity_of(const moe_desc* d) {
+  if (!(d->capacity_factor > 0.f)) return -1;
+  const double c = ceil((double)d->capacity_factor * (double)d->T * (double)d->top_k / (double)d->E);
+  return c < 1.0 ? 1 : (int)c;
+}
+
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t logits, idx, w, plan, counts, offsets, sorted, inv, ndrop, rank, sched, h, y, partial, total;
+};
+
+bool decode_capable(const moe_desc* d) {
+  return d->T <= MOE_FUSED_DECODE_MAX_T && d->act_dtype == MOE_BF16 &&
+         (d->w_dtype == MOE_BF16 || d->w_dtype == MOE_FP8_E4M3);
+}
+
+Layout layout_of(const moe_desc* d) {
+  Layout L{};
+  const size_t T = d->T, k = d->top_k, E = d->E;
+  const size_t rows = T * k + (d->has_shared ? T : 0);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off += up256(bytes);
+    return at;
+  };
+  L.logits = take(T * E * 4);
+  L.idx = take(T * k * 4);
+  L.w = take(T * k * 4);
+  L.plan = take((1 + E + T * k) * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.sorted = take(T * k * 4);
+  L.inv = take(T * k * 4);
+  L.ndrop = take(4);
+  L.rank = take(T * k * 4);
+  L.sched = take(grouped_sched_ints(d->T, d->top_k, d->E, d->has_shared) * 4);
+  L.h = take(rows * d->f * (d->act_dtype == MOE_F32 ? 4 : 2));
+  L.y = take(rows * d->d * 4);
+  L.partial = decode_capable(d) ? take(decode_partial_bytes(d->T, d->d, d->E, d->top_k, d->f, d->has_shared,
+                                                           d->w_dtype == MOE_FP8_E4M3 ? W_FP8 : W_BF16))
+                                : take(0);
+  L.total = off;
+  return L;
+}
+
+moe_status check_ws(const moe_desc* d, void* ws, size_t ws_bytes) {
+  const size_t need = layout_of(d).total;
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if ((uintptr_t)ws & 255u) return fail(MOE_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+ExpertWeights expert_weights(const moe_weights* w) {
+  ExpertWeights x{};
+  x.Wg = w->W_gate; x.Wu = w->W_up; x.Wd = w->W_down;
+  x.sg = w->s_gate; x.su = w->s_up; x.sd = w->s_down;
+  x.Wsg = w->Ws_gate; x.Wsu = w->Ws_up; x.Wsd = w->Ws_down;
+  x.ssg = w->ss_gate; x.ssu = w->ss_up; x.ssd = w->ss_down;
+  return x;
+}
+
+int wkind_of(const moe_desc* d) {
+  return d->w_dtype == MOE_FP8_E4M3 ? W_FP8 : d->w_dtype == MOE_BF16 ? W_BF16 : W_F32;
+}
+
+moe_status do_route(const moe_desc* d, const void* x, const moe_weights* w, int32_t* idx, float* tw, float* logits,
+                    int32_t* plan, hipStream_t s) {
+  RouteArgs a{};
+  a.x = x; a.W_g = w->W_g; a.bias = w->router_bias;
+  a.T = d->T; a.d = d->d; a.E = d->E; a.k = d->top_k; a.renormalize = d->renormalize;
+  a.cap = capacity_of(d);
+  a.act_f32 = d->act_dtype == MOE_F32;
+  a.logits = logits; a.idx = idx; a.w = tw; a.plan = plan;
+  return hip_status(launch_route(a, s), "route");
+}
+
+moe_status do_permute(const moe_desc* d, const int32_t* idx, int32_t* counts, int32_t* offsets, int32_t* sorted,
+                      int32_t* inv, int32_t* ndrop, int32_t* rank, hipStream_t s) {
+  PermuteArgs a{};
+  a.idx = idx; a.n = d->T * d->top_k; a.E = d->E; a.cap = capacity_of(d);
+  a.counts = counts; a.offsets = offsets; a.sorted_assign = sorted; a.inv_perm = inv; a.n_dropped = ndrop;
+  a.rank_ws = rank;
+  return hip_status(launch_permute(a, s), "permute");
+}
+
+moe_status do_grouped(const moe_desc* d, const void* x, const moe_weights* w, const int32_t* sorted,
+                      const int32_t* offsets, float* y, char* ws, const Layout& L, hipEvent_t eb, hipEvent_t ee,
+                      hipStream_t s) {
+  GroupedArgs a{};
+  a.x = x; a.sorted_assign = sorted; a.offsets = offsets; a.w = expert_weights(w);
+  a.T = d->T; a.d = d->d; a.E = d->E; a.k = d->top_k; a.f = d->f; a.has_shared = d->has_shared;
+  a.wkind = wkind_of(d);
+  a.act_f32 = d->act_dtype == MOE_F32;
+  a.y = y;
+  a.h = ws + L.h;
+  a.sched = (int32_t*)(ws + L.sched);
+  a.ev_begin = eb; a.ev_end = ee;
+  return hip_status(launch_grouped_ffn(a, s), "grouped_ffn");
+}
+
+moe_status do_combine(const moe_desc* d, const float* y, const int32_t* inv, const float* tw, void* out,
+                      hipStream_t s) {
+  CombineArgs a{};
+  a.y = y; a.inv_perm = inv; a.w = tw; a.T = d->T; a.d = d->d; a.k = d->top_k; a.has_shared = d->has_shared;
+  a.act_f32 = d->act_dtype == MOE_F32;
+  a.out = out;
+  return hip_status(launch_combine(a, s), "combine");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_desc* desc) {
+  if (check_desc(desc) != MOE_OK) return 0;
+  return layout_of(desc).total;
+}
+
+int32_t moe_capacity(const moe_desc* desc) {
+  if (check_desc(desc) != MOE_OK) return -1;
+  return capacity_of(desc);
+}
+
+moe_status moe_route(const moe_desc* desc, const void* x, const moe_weights* w, int32_t* topk_idx, float* topk_w,
+                     float* logits, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (desc->T == 0) return MOE_OK;
+  REQ(x, "x");
+  REQ(topk_idx, "topk_idx");
+  REQ(topk_w, "topk_w");
+  OPT(logits, "logits");
+  if ((st = check_router_weights(w)) != MOE_OK) return st;
+  float* lg = logits;
+  if (!lg && desc->T > kDecodeMaxT) {
+    if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
+    lg = (float*)((char*)ws + layout_of(desc).logits);
+  }
+  return do_route(desc, x, w, topk_idx, topk_w, lg, nullptr, stream);
+}
+
+moe_status moe_permute(const moe_desc* desc, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                       int32_t* sorted_assign, int32_t* inv_perm, int32_t* n_dropped, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (desc->T == 0) return MOE_OK;
+  REQ(counts, "counts");
+  REQ(offsets, "offsets");
+  REQ(n_dropped, "n_dropped");
+  REQ(topk_idx, "topk_idx");
+  REQ(sorted_assign, "sorted_assign");
+  REQ(inv_perm, "inv_perm");
+  if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
+  const Layout L = layout_of(desc);
+  return do_permute(desc, topk_idx, counts, offsets, sorted_assign, inv_perm, n_dropped,
+                    (int32_t*)((char*)ws + L.rank), stream);
+}
+
+moe_status moe_grouped_ffn(const moe_desc* desc, const void* x, const moe_weights* w, const int32_t* sorted_assign,
+                           const int32_t* offsets, float* y_sorted, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (desc->T == 0) return MOE_OK;
+  REQ(x, "x");
+  REQ(sorted_assign, "sorted_assign");
+  REQ(offsets, "offsets");
+  REQ(y_sorted, "y_sorted");
+  if ((st = check_expert_weights(desc, w)) != MOE_OK) return st;
+  if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
+  return do_grouped(desc, x, w, sorted_assign, offsets, y_sorted, (char*)ws, layout_of(desc), nullptr, nullptr,
+                    stream);
+}
+
+moe_status moe_combine(const moe_desc* desc, const float* y_sorted, const int32_t* inv_perm, const float* topk_w,
+                       void* out, hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (desc->T == 0) return MOE_OK;
+  REQ(y_sorted, "y_sorted");
+  REQ(inv_perm, "inv_perm");
+  REQ(topk_w, "topk_w");
+  REQ(out, "out");
+  return do_combine(desc, y_sorted, inv_perm, topk_w, out, stream);
+}
+
+moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, void* out, moe_stats* stats,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const bool fused = desc->path == MOE_PATH_FUSED_DECODE || (desc->path == MOE_PATH_AUTO && decode_capable(desc));
+  if (stats) stats->path_taken = fused ? MOE_PATH_FUSED_DECODE : MOE_PATH_GROUPED;
+  if (desc->T == 0) return MOE_OK;
+  REQ(x, "x");
+  REQ(out, "out");
+  if ((st = check_router_weights(w)) != MOE_OK) return st;
+  if ((st = check_expert_weights(desc, w)) != MOE_OK) return st;
+  if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
+  if (stats) {
+    OPT(stats->d_n_dropped, "stats.d_n_dropped");
+    OPT(stats->d_counts, "stats.d_counts");
+  }
+  char* base = (char*)ws;
+  const Layout L = layout_of(desc);
+  int32_t* idx = (int32_t*)(base + L.idx);
+  float* tw = (float*)(base + L.w);
+  hipEvent_t eb = stats ? stats->ev_begin : nullptr;
+  hipEvent_t ee = stats ? stats->ev_end : nullptr;
+
+  if (fused) {
+    int32_t* plan = (int32_t*)(base + L.plan);
+    if ((st = do_route(desc, x, w, idx, tw, nullptr, plan, stream)) != MOE_OK) return st;
+    DecodeArgs a{};
+    a.x = x; a.plan = plan; a.topk_w = tw; a.w = expert_weights(w);
+    a.T = desc->T; a.d = desc->d; a.E = desc->E; a.k = desc->top_k; a.f = desc->f;
+    a.has_shared = desc->has_shared; a.wkind = wkind_of(desc); a.act_f32 = false;
+    a.partial = (float*)(base + L.partial);
+    a.out = out;
+    a.ev_begin = eb; a.ev_end = ee;
+    if ((st = hip_status(launch_decode(a, stream), "fused decode")) != MOE_OK) return st;
+    if (stats && (stats->d_n_dropped || stats->d_counts)) {
+      // the decode path does not build the permutation; derive the stats from it
+      int32_t* counts = stats->d_counts ? stats->d_counts : (int32_t*)(base + L.counts);
+      int32_t* nd = stats->d_n_dropped ? stats->d_n_dropped : (int32_t*)(base + L.ndrop);
+      return do_permute(desc, idx, counts, (int32_t*)(base + L.offsets), (int32_t*)(base + L.sorted),
+                        (int32_t*)(base + L.inv), nd, (int32_t*)(base + L.rank), stream);
+    }
+    return MOE_OK;
+  }
+  float* logits = (float*)(base + L.logits);
+  if ((st = do_route(desc, x, w, idx, tw, logits, nullptr, stream)) != MOE_OK) return st;
+  int32_t* counts = (stats && stats->d_counts) ? stats->d_counts : (int32_t*)(base + L.counts);
+  int32_t* nd = (stats && stats->d_n_dropped) ? stats->d_n_dropped : (int32_t*)(base + L.ndrop);
+  int32_t* offsets = (int32_t*)(base + L.offsets);
+  int32_t* sorted = (int32_t*)(base + L.sorted);
+  int32_t* inv = (int32_t*)(base + L.inv);
+  if ((st = do_permute(desc, idx, counts, offsets, sorted, inv, nd, (int32_t*)(base + L.rank), stream)) != MOE_OK)
+    return st;
+  float* y = (float*)(base + L.y);
+  if ((st = do_grouped(desc, x, w, sorted, offsets, y, base, L, eb, ee, stream)) != MOE_OK) return st;
+  return do_combine(desc, y, inv, tw, out, stream);
+}
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+}  // extern "C"

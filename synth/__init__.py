@@ -121,7 +121,7 @@ def router_bias(cfg: MoEConfig, device="cpu") -> Optional[torch.Tensor]:
     raise ValueError(cfg.bias)
 
 
-def make_inputs(cfg: MoEConfig, device="cpu") -> dict:
+def make_inputs(cfg: MoEConfig, device="cpu", router_only: bool = False) -> dict:
     """All tensors of one layer call, on `device` (contiguous, row-major).
 
     keys: x [T,d]; W_g [d,E]; bias [E] | None; W_gate, W_up [E,d,f];
@@ -134,6 +134,8 @@ def make_inputs(cfg: MoEConfig, device="cpu") -> dict:
     out["x"] = _store(_normal((cfg.T, cfg.d), cfg.x_std, tensor_seed(cfg.seed, "x"), dev), cfg.act)
     out["W_g"] = _store(_normal((cfg.d, cfg.E), cfg.w_std, tensor_seed(cfg.seed, "router"), dev), cfg.act)
     out["bias"] = router_bias(cfg, dev)
+    if router_only:
+        return out
 
     def alloc(shape):
         dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[cfg.wdt]

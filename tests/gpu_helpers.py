@@ -1,0 +1,75 @@
+"""Shared helpers of the GPU parity tests: seeded inputs on the device, the
+same tensors widened exactly for the CPU oracle, and tolerance checks."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+# max|gpu - oracle| / max|oracle| bounds per weight type (fp32, bf16, fp8)
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def codes(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.uint8).cpu().numpy()
+
+
+class OracleInputs:
+    """The device inputs of one layer call, seen by the oracle (exact fp64)."""
+
+    def __init__(self, inp: dict):
+        self.inp = inp
+        self.cfg = inp["cfg"]
+        self.x = to64(inp["x"])
+        self.W_g = to64(inp["W_g"])
+        self.bias = None if inp["bias"] is None else to64(inp["bias"])
+
+    def _triple(self, g, u, dn, sg, su, sd):
+        if self.cfg.wdt == "fp8":
+            return (oracle.dequantize(codes(g), sg.cpu().numpy(), 1),
+                    oracle.dequantize(codes(u), su.cpu().numpy(), 1),
+                    oracle.dequantize(codes(dn), sd.cpu().numpy(), 1))
+        return to64(g), to64(u), to64(dn)
+
+    def expert(self, e: int):
+        i = self.inp
+        if self.cfg.wdt == "fp8":
+            return self._triple(i["W_gate"][e], i["W_up"][e], i["W_down"][e],
+                                i["s_gate"][e], i["s_up"][e], i["s_down"][e])
+        return self._triple(i["W_gate"][e], i["W_up"][e], i["W_down"][e], None, None, None)
+
+    def shared(self):
+        i = self.inp
+        if not self.cfg.shared:
+            return None
+        return self._triple(i["Ws_gate"], i["Ws_up"], i["Ws_down"], i["ss_gate"], i["ss_up"], i["ss_down"])
+
+    def forward(self, tokens=None):
+        c = self.cfg
+        return oracle.forward(self.x, self.W_g, self.bias, c.k, c.renormalize, np.float32(c.capacity_factor),
+                              self.expert, c.E, shared=self.shared(), tokens=tokens)
+
+    def certificate(self):
+        return oracle.routing_certificate(self.x, self.W_g, self.bias, self.cfg.k)
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    den = float(np.abs(ref).max())
+    return float(np.abs(got - ref).max()) / (den if den > 0 else 1.0)
+
+
+def assert_close(got, ref, tol, what=""):
+    e = rel_err(np.asarray(got, np.float64), np.asarray(ref, np.float64))
+    assert e <= tol, f"{what}: max|gpu-oracle|/max|oracle| = {e:.3e} > {tol:.1e}"
+    return e
+
+
+def device_inputs(cfg: synth.MoEConfig, router_only=False) -> dict:
+    print(f"[inputs] {cfg}", flush=True)
+    return synth.make_inputs(cfg, "cuda", router_only=router_only)
