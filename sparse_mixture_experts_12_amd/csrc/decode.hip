@@ -19,6 +19,7 @@
 // of each used expert in a fixed order, applies the routing weights in slot
 // order (+ the shared expert with weight 1) and rounds once to bf16.
 // No atomics: results are bitwise reproducible.
+#include <hip/hip_ext.h>
 #include <stdlib.h>
 
 #include "common.h"
@@ -204,9 +205,10 @@ __global__ __launch_bounds__(256) void decode_ffn_kernel(DecodeParams p) {
   }
 }
 
-// Sum slices per used expert, weight by routing weights in slot order, add
-// the shared expert, round once to bf16.  Block: 64 columns of one token;
-// 16 slice groups x 16 column quads.
+// Sum the slice partials of the used experts for 64 columns of one token:
+// out = sum_j w[t,j] * partial[unit(t,j)][s] (+ shared partials), taken in a
+// fixed order (unit-major, then slices s = g, g + 16, ... per slice group g,
+// then the 16 group sums in order) and rounded once to bf16.
 __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restrict__ partial,
                                                             const int32_t* __restrict__ plan,
                                                             const float* __restrict__ topk_w, int T, int d, int E,
@@ -214,7 +216,8 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
                                                             bf16_t* __restrict__ out) {
   __shared__ float4 red[16][16];
   const int t = blockIdx.y;
-  const int col = blockIdx.x * 64 + (threadIdx.x & 15) * 4;
+  const int cq = threadIdx.x & 15;
+  const int col = blockIdx.x * 64 + cq * 4;
   const int sg = threadIdx.x >> 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   const int nunits = k + (has_shared ? 1 : 0);
@@ -224,53 +227,54 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
     if (j < k) {
       unit = plan[1 + E + t * k + j];
       wgt = topk_w[t * k + j];
-      if (unit < 0) continue;    // dropped: uniform across the block
+      if (unit < 0) continue;    // dropped by the capacity rule
     } else {
       unit = maxU;
       wgt = 1.f;
     }
-    float4 sacc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float* base = partial + ((size_t)unit * n_slices * T + t) * d + col;
+#pragma unroll 8
     for (int s = sg; s < n_slices; s += 16) {
-      const float4 v = *reinterpret_cast<const float4*>(partial + (((size_t)unit * n_slices + s) * T + t) * d + col);
-      sacc.x += v.x; sacc.y += v.y; sacc.z += v.z; sacc.w += v.w;
+      const float4 v = *reinterpret_cast<const float4*>(base + (size_t)s * T * d);
+      acc.x = __fmaf_rn(wgt, v.x, acc.x);
+      acc.y = __fmaf_rn(wgt, v.y, acc.y);
+      acc.z = __fmaf_rn(wgt, v.z, acc.z);
+      acc.w = __fmaf_rn(wgt, v.w, acc.w);
     }
-    red[sg][threadIdx.x & 15] = sacc;
-    __syncthreads();
-    if (sg == 0) {
-      float4 tot = red[0][threadIdx.x & 15];
-      for (int q = 1; q < 16; ++q) {
-        const float4 v = red[q][threadIdx.x & 15];
-        tot.x += v.x; tot.y += v.y; tot.z += v.z; tot.w += v.w;
-      }
-      acc.x = __fmaf_rn(wgt, tot.x, acc.x);
-      acc.y = __fmaf_rn(wgt, tot.y, acc.y);
-      acc.z = __fmaf_rn(wgt, tot.z, acc.z);
-      acc.w = __fmaf_rn(wgt, tot.w, acc.w);
-    }
-    __syncthreads();
   }
+  red[sg][cq] = acc;
+  __syncthreads();
   if (sg == 0) {
+    float4 tot = red[0][cq];
+    for (int q = 1; q < 16; ++q) {
+      const float4 v = red[q][cq];
+      tot.x += v.x; tot.y += v.y; tot.z += v.z; tot.w += v.w;
+    }
     uint2 o;
-    o.x = pack_bf16x2(acc.x, acc.y);
-    o.y = pack_bf16x2(acc.z, acc.w);
+    o.x = pack_bf16x2(tot.x, tot.y);
+    o.y = pack_bf16x2(tot.z, tot.w);
     *reinterpret_cast<uint2*>(out + (size_t)t * d + col) = o;
   }
 }
 
 static int pick_mt(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8; }
 
-static int pick_fs(int units, int f) {
+// Slice width: the widest slice (longest contiguous row segment of W_gate /
+// W_up, at most 512 bytes) that still gives every CU at least one work unit.
+static int pick_fs(int units, int f, int es) {
   static int forced = -1;
   if (forced < 0) {
     const char* e = getenv("MOE_DECODE_FS");
     forced = e ? atoi(e) : 0;
   }
-  if (forced == 32 || forced == 64 || forced == 128) {
-    if (f % forced == 0) return forced;
+  if ((forced == 64 || forced == 128 || forced == 256) && f % forced == 0) return forced;
+  const int cands[3] = {256, 128, 64};
+  for (int c : cands) {
+    if (f % c) continue;
+    if (c * es > 512) continue;
+    if (units * (f / c) >= 200) return c;
   }
-  if (f % 128 == 0 && units * (f / 128) >= 512) return 128;
-  if (units * (f / 64) >= 512) return 64;
-  return 32;
+  return 64;
 }
 
 static int decode_max_used(int T, int k, int E) { return (T * k < E) ? T * k : E; }
@@ -278,11 +282,12 @@ static int decode_max_used(int T, int k, int E) { return (T * k < E) ? T * k : E
 size_t decode_partial_bytes(int T, int d, int E, int k, int f, int has_shared, int wkind) {
   (void)wkind;
   const int units = decode_max_used(T, k, E) + (has_shared ? 1 : 0);
-  return (size_t)units * (size_t)(f / 32) * T * d * sizeof(float);
+  return (size_t)units * (size_t)(f / 64) * T * d * sizeof(float);
 }
 
 template <int WK, int MT, int FS>
-static hipError_t launch_decode_t(const DecodeParams& p, int units, hipStream_t s) {
+static hipError_t launch_decode_t(const DecodeParams& p, int units, hipStream_t s, hipEvent_t ev_begin,
+                                  hipEvent_t ev_end) {
   constexpr int ES = (WK == W_FP8) ? 1 : 2;
   constexpr int CH = FS / (16 / ES);
   constexpr int RG = 256 / (2 * CH);
@@ -295,24 +300,29 @@ static hipError_t launch_decode_t(const DecodeParams& p, int units, hipStream_t 
     if (e != hipSuccess) return e;
   }
   dim3 grid(p.f / FS, units);
-  decode_ffn_kernel<WK, MT, FS><<<grid, 256, lds, s>>>(p);
+  if (ev_begin || ev_end)
+    hipExtLaunchKernelGGL(decode_ffn_kernel<WK, MT, FS>, grid, dim3(256), (uint32_t)lds, s, ev_begin, ev_end, 0, p);
+  else
+    decode_ffn_kernel<WK, MT, FS><<<grid, 256, lds, s>>>(p);
   return hipGetLastError();
 }
 
 template <int WK, int MT>
-static hipError_t launch_decode_fs(const DecodeParams& p, int units, int fs, hipStream_t s) {
-  if (fs == 128) return launch_decode_t<WK, MT, 128>(p, units, s);
-  if (fs == 64) return launch_decode_t<WK, MT, 64>(p, units, s);
-  return launch_decode_t<WK, MT, 32>(p, units, s);
+static hipError_t launch_decode_fs(const DecodeParams& p, int units, int fs, hipStream_t s, hipEvent_t b,
+                                   hipEvent_t e) {
+  if (fs == 256) return launch_decode_t<WK, MT, 256>(p, units, s, b, e);
+  if (fs == 128) return launch_decode_t<WK, MT, 128>(p, units, s, b, e);
+  return launch_decode_t<WK, MT, 64>(p, units, s, b, e);
 }
 
 template <int WK>
-static hipError_t launch_decode_mt(const DecodeParams& p, int units, int fs, hipStream_t s) {
+static hipError_t launch_decode_mt(const DecodeParams& p, int units, int fs, hipStream_t s, hipEvent_t b,
+                                   hipEvent_t e) {
   switch (pick_mt(p.T)) {
-    case 1: return launch_decode_fs<WK, 1>(p, units, fs, s);
-    case 2: return launch_decode_fs<WK, 2>(p, units, fs, s);
-    case 4: return launch_decode_fs<WK, 4>(p, units, fs, s);
-    default: return launch_decode_fs<WK, 8>(p, units, fs, s);
+    case 1: return launch_decode_fs<WK, 1>(p, units, fs, s, b, e);
+    case 2: return launch_decode_fs<WK, 2>(p, units, fs, s, b, e);
+    case 4: return launch_decode_fs<WK, 4>(p, units, fs, s, b, e);
+    default: return launch_decode_fs<WK, 8>(p, units, fs, s, b, e);
   }
 }
 
@@ -326,11 +336,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   p.has_shared = a.has_shared;
   p.partial = a.partial;
   const int units = p.maxU + (a.has_shared ? 1 : 0);
-  const int fs = pick_fs(units, a.f);
-  if (a.ev_begin) hipEventRecord(a.ev_begin, s);
-  hipError_t err = (a.wkind == W_FP8) ? launch_decode_mt<W_FP8>(p, units, fs, s)
-                                      : launch_decode_mt<W_BF16>(p, units, fs, s);
-  if (a.ev_end) hipEventRecord(a.ev_end, s);
+  const int fs = pick_fs(units, a.f, a.wkind == W_FP8 ? 1 : 2);
+  hipError_t err = (a.wkind == W_FP8) ? launch_decode_mt<W_FP8>(p, units, fs, s, a.ev_begin, a.ev_end)
+                                      : launch_decode_mt<W_BF16>(p, units, fs, s, a.ev_begin, a.ev_end);
   if (err != hipSuccess) return err;
   dim3 g2(a.d / 64, a.T);
   decode_reduce_kernel<<<g2, 256, 0, s>>>(a.partial, a.plan, a.topk_w, a.T, a.d, a.E, a.k, a.f / fs, p.maxU,
