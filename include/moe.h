@@ -127,7 +127,9 @@ int32_t moe_capacity(const moe_desc* desc);
  *   x        [T, d] act dtype
  *   topk_idx [T, k] int32 out: slot 0 holds the largest logit
  *   topk_w   [T, k] fp32 out: softmax weights of the chosen experts
- *   logits   [T, E] fp32 out, or NULL (then the workspace holds them) */
+ *   logits   [T, E] fp32 out, or NULL
+ * For T > 8 the workspace (moe_workspace_size) must be passed; for T <= 8 it
+ * is not used and may be NULL. */
 moe_status moe_route(const moe_desc* desc, const void* x, const moe_weights* w,
                      int32_t* topk_idx, float* topk_w, float* logits,
                      void* ws, size_t ws_bytes, hipStream_t stream);

@@ -16,12 +16,14 @@ struct RouteArgs {
   int T, d, E, k, renormalize;
   int cap;          // -1: uncapped
   bool act_f32;
-  float* logits;    // [T, E]; required when T > kDecodeMaxT
+  float* logits;    // [T, E] or nullptr
+  double* part;     // fp64 partial logits (router_partial_bytes), T > kDecodeMaxT only
   int32_t* idx;     // [T, k]
   float* w;         // [T, k]
   int32_t* plan;    // decode plan or nullptr (T <= kDecodeMaxT only)
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+size_t router_partial_bytes(int T, int d, int E);
 
 struct PermuteArgs {
   const int32_t* idx;

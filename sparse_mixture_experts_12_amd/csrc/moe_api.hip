@@ -102,7 +102,7 @@ int capacity_of(const moe_desc* d) {
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t logits, idx, w, plan, counts, offsets, sorted, inv, ndrop, rank, sched, h, y, partial, total;
+  size_t part, idx, w, plan, counts, offsets, sorted, inv, ndrop, rank, sched, h, y, partial, total;
 };
 
 bool decode_capable(const moe_desc* d) {
@@ -120,7 +120,7 @@ Layout layout_of(const moe_desc* d) {
     off += up256(bytes);
     return at;
   };
-  L.logits = take(T * E * 4);
+  L.part = take(router_partial_bytes(d->T, d->d, d->E));
   L.idx = take(T * k * 4);
   L.w = take(T * k * 4);
   L.plan = take((1 + E + T * k) * 4);
@@ -167,13 +167,13 @@ int wkind_of(const moe_desc* d) {
 }
 
 moe_status do_route(const moe_desc* d, const void* x, const moe_weights* w, int32_t* idx, float* tw, float* logits,
-                    int32_t* plan, hipStream_t s) {
+                    double* part, int32_t* plan, hipStream_t s) {
   RouteArgs a{};
   a.x = x; a.W_g = w->W_g; a.bias = w->router_bias;
   a.T = d->T; a.d = d->d; a.E = d->E; a.k = d->top_k; a.renormalize = d->renormalize;
   a.cap = capacity_of(d);
   a.act_f32 = d->act_dtype == MOE_F32;
-  a.logits = logits; a.idx = idx; a.w = tw; a.plan = plan;
+  a.logits = logits; a.part = part; a.idx = idx; a.w = tw; a.plan = plan;
   return hip_status(launch_route(a, s), "route");
 }
 
@@ -234,12 +234,12 @@ moe_status moe_route(const moe_desc* desc, const void* x, const moe_weights* w, 
   REQ(topk_w, "topk_w");
   OPT(logits, "logits");
   if ((st = check_router_weights(w)) != MOE_OK) return st;
-  float* lg = logits;
-  if (!lg && desc->T > kDecodeMaxT) {
+  double* part = nullptr;
+  if (desc->T > kDecodeMaxT) {
     if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
-    lg = (float*)((char*)ws + layout_of(desc).logits);
+    part = (double*)((char*)ws + layout_of(desc).part);
   }
-  return do_route(desc, x, w, topk_idx, topk_w, lg, nullptr, stream);
+  return do_route(desc, x, w, topk_idx, topk_w, logits, part, nullptr, stream);
 }
 
 moe_status moe_permute(const moe_desc* desc, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
@@ -312,7 +312,7 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w
 
   if (fused) {
     int32_t* plan = (int32_t*)(base + L.plan);
-    if ((st = do_route(desc, x, w, idx, tw, nullptr, plan, stream)) != MOE_OK) return st;
+    if ((st = do_route(desc, x, w, idx, tw, nullptr, nullptr, plan, stream)) != MOE_OK) return st;
     DecodeArgs a{};
     a.x = x; a.plan = plan; a.topk_w = tw; a.w = expert_weights(w);
     a.T = desc->T; a.d = desc->d; a.E = desc->E; a.k = desc->top_k; a.f = desc->f;
@@ -330,8 +330,7 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w
     }
     return MOE_OK;
   }
-  float* logits = (float*)(base + L.logits);
-  if ((st = do_route(desc, x, w, idx, tw, logits, nullptr, stream)) != MOE_OK) return st;
+  if ((st = do_route(desc, x, w, idx, tw, nullptr, (double*)(base + L.part), nullptr, stream)) != MOE_OK) return st;
   int32_t* counts = (stats && stats->d_counts) ? stats->d_counts : (int32_t*)(base + L.counts);
   int32_t* nd = (stats && stats->d_n_dropped) ? stats->d_n_dropped : (int32_t*)(base + L.ndrop);
   int32_t* offsets = (int32_t*)(base + L.offsets);

@@ -16,65 +16,152 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Large-T logits: BT x BE tile per work-group, fp64 FMA, LDS staged.
-// 256 threads; each thread owns TM tokens x TN experts.
+// Large-T router logits as fp64 partial sums over slices of the hidden
+// dimension (split-K), finished by the top-k kernel, which adds the slices in
+// a fixed order.  Loads are branch-free (clamped addresses, zero
+// contributions) so each thread's loads are in flight together.
+//   part[z][t][e] = sum over rows r of slice z of x[t, r] * W_g[r, e]   (fp64)
 // ---------------------------------------------------------------------------
-template <typename TIn, int BT, int BE, int TM, int TN>
-__global__ __launch_bounds__(256) void router_logits_tiled(
-    const TIn* __restrict__ x, const TIn* __restrict__ W, const float* __restrict__ bias,
-    float* __restrict__ logits, int T, int d, int E) {
-  constexpr int BK = 16;
-  static_assert((BT / TM) * (BE / TN) == 256, "thread tile");
-  __shared__ double xs[BK][BT + 1];
-  __shared__ double ws[BK][BE + 1];
-  const int tid = threadIdx.x;
-  const int tx = tid % (BE / TN);   // expert group
-  const int ty = tid / (BE / TN);   // token group
-  const int t0 = blockIdx.x * BT;
-  const int e0 = blockIdx.y * BE;
-  double acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = 0.0;
+template <typename TIn>
+__device__ __forceinline__ double ld_or_zero(const TIn* __restrict__ p, size_t i, bool ok) {
+  const TIn v = p[ok ? i : 0];
+  return ok ? (double)ActTraits<TIn>::load(&v, 0) : 0.0;
+}
 
-  for (int k0 = 0; k0 < d; k0 += BK) {
-    for (int i = tid; i < BT * BK; i += 256) {
-      int tt = i / BK, kk = i % BK;
-      int t = t0 + tt;
-      xs[kk][tt] = (t < T) ? (double)ActTraits<TIn>::load(x, (size_t)t * d + k0 + kk) : 0.0;
-    }
-    for (int i = tid; i < BK * BE; i += 256) {
-      int kk = i / BE, ee = i % BE;
-      int e = e0 + ee;
-      ws[kk][ee] = (e < E) ? (double)ActTraits<TIn>::load(W, (size_t)(k0 + kk) * E + e) : 0.0;
-    }
-    __syncthreads();
+// Few experts (E <= EP <= 32): 16 tokens per work-group; the work-group's
+// W_g slice (dsplit rows x EP) is staged once in LDS as fp32 (exact for
+// bf16); the slice rows are split over 16 thread groups whose fp64 sums are
+// added in a fixed order.
+template <typename TIn, int EP>
+__global__ __launch_bounds__(256) void router_partial_small_e(const TIn* __restrict__ x, const TIn* __restrict__ W,
+                                                              double* __restrict__ part, int T, int d, int E,
+                                                              int dsplit) {
+  constexpr int BT = 16, DS = 16;
+  constexpr int MAXR = 8192 / EP;                       // staged rows (32 KB of fp32)
+  constexpr int RPT = MAXR / DS;                        // rows per thread
+  __shared__ float wch[MAXR][EP];
+  __shared__ double red[DS][BT][EP + 1];
+  const int tid = threadIdx.x;
+  const int tt = tid & (BT - 1), ds = tid >> 4;
+  const int t = blockIdx.x * BT + tt;
+  const int tc = min(t, T - 1);
+  const int z = blockIdx.y;
+  const int r_begin = z * dsplit;
+  const int rows = min(dsplit, d - r_begin);
+  for (int i = tid; i < MAXR * EP; i += 256) {
+    const int r = i / EP, e = i % EP;
+    const bool ok = (r < rows) && (e < E);
+    wch[r][e] = (float)ld_or_zero(W, (size_t)(r_begin + r) * E + e, ok);
+  }
+  // this thread's rows: RPT consecutive rows of token tc (branch-free loads)
+  float xv[RPT];
+  const int r0 = ds * RPT;
 #pragma unroll
-    for (int kk = 0; kk < BK; ++kk) {
-      double a[TM], b[TN];
+  for (int i = 0; i < RPT; ++i) {
+    const int r = r0 + i;
+    xv[i] = (float)ld_or_zero(x, (size_t)tc * d + r_begin + r, r < rows);
+  }
+  __syncthreads();
+  double acc[EP];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) a[i] = xs[kk][ty * TM + i];
+  for (int j = 0; j < EP; ++j) acc[j] = 0.0;
+#pragma unroll 4
+  for (int i = 0; i < RPT; ++i) {
+    const double xd = (double)xv[i];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) b[j] = ws[kk][tx * TN + j];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = __fma_rn(a[i], b[j], acc[i][j]);
-    }
-    __syncthreads();
+    for (int j = 0; j < EP; ++j) acc[j] = __fma_rn(xd, (double)wch[r0 + i][j], acc[j]);
   }
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    int t = t0 + ty * TM + i;
-    if (t >= T) continue;
+  for (int j = 0; j < EP; ++j) red[ds][tt][j] = acc[j];
+  __syncthreads();
+  for (int i = tid; i < BT * EP; i += 256) {
+    const int ti = i / EP, e = i % EP;
+    const int tok = blockIdx.x * BT + ti;
+    if (tok < T && e < E) {
+      double sum = 0.0;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      int e = e0 + tx * TN + j;
-      if (e >= E) continue;
-      double s = acc[i][j];
-      if (bias) s += (double)bias[e];
-      logits[(size_t)t * E + e] = (float)s;
+      for (int g = 0; g < DS; ++g) sum += red[g][ti][e];
+      part[((size_t)z * T + tok) * E + e] = sum;
+    }
+  }
+}
+
+// Many experts: 32 tokens x 64 experts per work-group, K step 32, LDS double
+// buffer with the next step's global loads issued before the current step's
+// FMAs.  Thread (ty, tx) owns tokens ty + 16 i (i < 2) and experts tx + 16 j
+// (j < 4), so LDS reads of one wave hit consecutive doubles.
+template <typename TIn>
+__global__ __launch_bounds__(256) void router_partial_tiled(const TIn* __restrict__ x, const TIn* __restrict__ W,
+                                                            double* __restrict__ part, int T, int d, int E,
+                                                            int dsplit) {
+  constexpr int BT = 32, BE = 64, BK = 32;
+  __shared__ double xs[2][BK][BT + 1];
+  __shared__ double ws[2][BK][BE + 1];
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int t0 = blockIdx.x * BT, e0 = blockIdx.y * BE;
+  const int z = blockIdx.z;
+  const int r_begin = z * dsplit;
+  const int r_end = min(d, r_begin + dsplit);
+  // staging roles: x tile 32 tokens x 32 k (4 per thread), W tile 32 k x 64 experts (8 per thread)
+  const int xr = tid >> 3, xk = (tid & 7) * 4;
+  const int wk = tid >> 3, we = (tid & 7) * 8;
+  const int xt = min(t0 + xr, T - 1);
+  const bool xt_ok = (t0 + xr) < T;
+  double xreg[4], wreg[8];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = k0 + xk + i;
+      xreg[i] = ld_or_zero(x, (size_t)xt * d + k, xt_ok && k < r_end);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = k0 + wk, e = e0 + we + j;
+      wreg[j] = ld_or_zero(W, (size_t)k * E + e, k < r_end && e < E);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xs[buf][xk + i][xr] = xreg[i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ws[buf][wk][we + j] = wreg[j];
+  };
+  double acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  load(r_begin);
+  store(0);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = r_begin; k0 < r_end; k0 += BK) {
+    const bool more = k0 + BK < r_end;
+    if (more) load(k0 + BK);
+#pragma unroll 8
+    for (int kk = 0; kk < BK; ++kk) {
+      double a[2], b[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = xs[buf][kk][ty + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = ws[buf][kk][tx + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __fma_rn(a[i], b[j], acc[i][j]);
+    }
+    if (more) store(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = t0 + ty + 16 * i;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + tx + 16 * j;
+      if (t < T && e < E) part[((size_t)z * T + t) * E + e] = acc[i][j];
     }
   }
 }
@@ -149,14 +236,6 @@ __device__ void wave_topk(const float* lg /* logits of the token, any memory */,
     out_idx[lane] = sel_idx;
     out_w[lane] = (float)(chosen_sum / den);
   }
-}
-
-__global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits, int T, int E,
-                                                           int k, int renormalize, int32_t* __restrict__ idx,
-                                                           float* __restrict__ w) {
-  int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  wave_topk(logits + (size_t)t * E, E, k, renormalize, idx + (size_t)t * k, w + (size_t)t * k);
 }
 
 // ---------------------------------------------------------------------------
@@ -402,23 +481,75 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
   if (tid < n) plan[1 + E + tid] = keep ? flag[sidx[tid]] : -1;
 }
 
+// One wave per token: add the S fp64 partial sums of each logit in slice
+// order, add the bias, round once to fp32, then top-k and weights.
+__global__ __launch_bounds__(256) void topk_finalize_kernel(const double* __restrict__ part, int S,
+                                                            const float* __restrict__ bias, int T, int E, int k,
+                                                            int renormalize, float* __restrict__ logits,
+                                                            int32_t* __restrict__ idx, float* __restrict__ w) {
+  __shared__ float lg[4][1024];
+  __shared__ int32_t sel[4][32];
+  __shared__ double ps[4][256];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wv;
+  if (t >= T) return;     // whole wave leaves together; no block barrier follows
+  for (int e = lane; e < E; e += 64) {
+    double s = 0.0;
+    for (int z = 0; z < S; ++z) s += part[((size_t)z * T + t) * E + e];
+    if (bias) s += (double)bias[e];
+    const float l = (float)s;
+    lg[wv][e] = l;
+    if (logits) logits[(size_t)t * E + e] = l;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0);
+  if (E <= 256)
+    wave_topk_rank(lg[wv], E, k, renormalize, sel[wv], ps[wv], idx + (size_t)t * k, w + (size_t)t * k);
+  else
+    wave_topk(lg[wv], E, k, renormalize, idx + (size_t)t * k, w + (size_t)t * k);
+}
+
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
+// Split of the hidden dimension for the large-T router: the few-expert kernel
+// stages at most 8192/EP rows of W_g per work-group; the many-expert kernel
+// splits until about 512 work-groups are in flight (at least 256 rows each).
+static void router_split(int T, int d, int E, int* S, int* dsplit) {
+  if (E <= 32) {
+    const int ep = E <= 8 ? 8 : E <= 16 ? 16 : 32;
+    *dsplit = 8192 / ep;
+  } else {
+    const long nblk = (long)((T + 31) / 32) * ((E + 63) / 64);
+    int s = (int)((512 + nblk - 1) / nblk);
+    const int smax = d / 256 > 0 ? d / 256 : 1;
+    s = s < 1 ? 1 : (s > smax ? smax : s);
+    int ds = (d + s - 1) / s;
+    *dsplit = (ds + 31) / 32 * 32;
+  }
+  *S = (d + *dsplit - 1) / *dsplit;
+}
+
+size_t router_partial_bytes(int T, int d, int E) {
+  if (T <= kDecodeMaxT) return 0;
+  int S, ds;
+  router_split(T, d, E, &S, &ds);
+  return (size_t)S * T * E * sizeof(double);
+}
+
 template <typename TIn>
-static hipError_t launch_logits(const void* x, const void* W, const float* bias, float* logits, int T, int d,
-                                int E, hipStream_t s) {
+static hipError_t launch_partials(const void* x, const void* W, double* part, int T, int d, int E, int S, int ds,
+                                  hipStream_t s) {
   const TIn* xp = (const TIn*)x;
   const TIn* wp = (const TIn*)W;
   if (E <= 8) {
-    dim3 g((T + 255) / 256, (E + 7) / 8);
-    router_logits_tiled<TIn, 256, 8, 4, 2><<<g, 256, 0, s>>>(xp, wp, bias, logits, T, d, E);
+    router_partial_small_e<TIn, 8><<<dim3((T + 15) / 16, S), 256, 0, s>>>(xp, wp, part, T, d, E, ds);
+  } else if (E <= 16) {
+    router_partial_small_e<TIn, 16><<<dim3((T + 15) / 16, S), 256, 0, s>>>(xp, wp, part, T, d, E, ds);
   } else if (E <= 32) {
-    dim3 g((T + 127) / 128, (E + 31) / 32);
-    router_logits_tiled<TIn, 128, 32, 4, 4><<<g, 256, 0, s>>>(xp, wp, bias, logits, T, d, E);
+    router_partial_small_e<TIn, 32><<<dim3((T + 15) / 16, S), 256, 0, s>>>(xp, wp, part, T, d, E, ds);
   } else {
-    dim3 g((T + 31) / 32, (E + 63) / 64);
-    router_logits_tiled<TIn, 32, 64, 2, 4><<<g, 256, 0, s>>>(xp, wp, bias, logits, T, d, E);
+    router_partial_tiled<TIn><<<dim3((T + 31) / 32, (E + 63) / 64, S), 256, 0, s>>>(xp, wp, part, T, d, E, ds);
   }
   return hipGetLastError();
 }
@@ -439,10 +570,13 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
 #undef MOE_ROUTE_SMALL
     return hipGetLastError();
   }
-  hipError_t err = a.act_f32 ? launch_logits<float>(a.x, a.W_g, a.bias, a.logits, a.T, a.d, a.E, s)
-                             : launch_logits<bf16_t>(a.x, a.W_g, a.bias, a.logits, a.T, a.d, a.E, s);
+  int S, ds;
+  router_split(a.T, a.d, a.E, &S, &ds);
+  hipError_t err = a.act_f32 ? launch_partials<float>(a.x, a.W_g, a.part, a.T, a.d, a.E, S, ds, s)
+                             : launch_partials<bf16_t>(a.x, a.W_g, a.part, a.T, a.d, a.E, S, ds, s);
   if (err != hipSuccess) return err;
-  topk_softmax_kernel<<<(a.T + 3) / 4, 256, 0, s>>>(a.logits, a.T, a.E, a.k, a.renormalize, a.idx, a.w);
+  topk_finalize_kernel<<<(a.T + 3) / 4, 256, 0, s>>>(a.part, S, a.bias, a.T, a.E, a.k, a.renormalize, a.logits,
+                                                     a.idx, a.w);
   return hipGetLastError();
 }
 
