@@ -29,6 +29,8 @@
 // its L2.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -84,47 +86,56 @@ __device__ __forceinline__ bool decode_tile(const int32_t* sched, int maxQ, int 
 }
 
 // 8 rows x 8 bf16 (row-major, 16 B per row) -> 8 vectors of 8 K-values.
-__device__ __forceinline__ void transpose8x8_bf16(const uint4 (&r)[8], uint4 (&o)[8]) {
-  const uint32_t* rw[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) rw[j] = reinterpret_cast<const uint32_t*>(&r[j]);
+// Native vector types only, so the staging arrays stay in registers.
+__device__ __forceinline__ void transpose8x8_bf16(const u32x4_t (&r)[8], u32x4_t (&o)[8]) {
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
-    uint32_t d[4];
+    u32x4_t d;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      uint32_t a = rw[2 * p][n >> 1], b = rw[2 * p + 1][n >> 1];
+      const uint32_t a = r[2 * p][n >> 1], b = r[2 * p + 1][n >> 1];
       d[p] = (n & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
     }
-    o[n] = make_uint4(d[0], d[1], d[2], d[3]);
+    o[n] = d;
   }
 }
 
-// fp8 e4m3fn (8 per row, 8 B) -> bf16 bits, then transpose.
-__device__ __forceinline__ void fp8_rows_to_bf16(const uint2 (&r8)[8], uint4 (&r)[8]) {
+// fp8 e4m3fn (8 per row, 8 B) -> bf16 bits (exact: at most 4 significant bits).
+__device__ __forceinline__ void fp8_rows_to_bf16(const u32x2_t (&r8)[8], u32x4_t (&r)[8]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     float v[8];
-    fp8x4_to_f32(r8[j].x, v);
-    fp8x4_to_f32(r8[j].y, v + 4);
-    // values have at most 4 significant bits: the top 16 bits are exact bf16
-    uint32_t w[4];
+    fp8x4_to_f32(r8[j][0], v);
+    fp8x4_to_f32(r8[j][1], v + 4);
+    u32x4_t w;
 #pragma unroll
     for (int p = 0; p < 4; ++p) w[p] = (__float_as_uint(v[2 * p]) >> 16) | (__float_as_uint(v[2 * p + 1]) & 0xffff0000u);
-    r[j] = make_uint4(w[0], w[1], w[2], w[3]);
+    r[j] = w;
   }
 }
 
-template <int WK, bool DUAL, int WM>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmParams p) {
-  constexpr int WN = 4 / WM;
-  constexpr int BM = 64 * WM;
+// Tile shapes (4 waves): BM = 256 -> waves 2x2, 128 rows x 128 B-rows each;
+// BM = 128 -> 2x2, 64 x 128; BM = 64 -> 1x4, 64 x 64.  The LDS B tile always
+// holds 256 "B rows" (output columns): 128 gate + 128 up columns for the
+// gate/up GEMM, 256 columns for the down GEMM.  PF = number of K steps whose
+// global loads are in flight ahead of the MFMAs (register stages).
+template <int BM> struct TileCfg {
+  static constexpr int WM = (BM >= 128) ? 2 : 1;
+  static constexpr int WN = 4 / WM;
+  static constexpr int PF = (BM == 128) ? 2 : 1;
+  static constexpr int OCC = (BM == 64) ? 2 : 1;    // work-groups per CU
+};
+
+template <int WK, bool DUAL, int BM>
+__global__ __launch_bounds__(256, TileCfg<BM>::OCC) void gemm_mfma_kernel(GemmParams p) {
+  constexpr int WM = TileCfg<BM>::WM, WN = TileCfg<BM>::WN, PF = TileCfg<BM>::PF;
   constexpr int NMAT = DUAL ? 2 : 1;
   constexpr int BN_MAT = DUAL ? 128 : 256;         // output columns per tile
   constexpr int NI_MAT = BN_MAT / WN / 32;         // 32-wide MFMA column tiles per matrix per wave
   constexpr int NI = NI_MAT * NMAT;
-  constexpr int MI = 2;                            // 64 rows per wave
-  constexpr int A_CHUNKS = BM * 8 / 256;           // 16-byte chunks per thread
+  constexpr int MI = BM / WM / 32;                 // 32-row MFMA tiles per wave
+  constexpr int WROWS = BM / WM;                   // rows per wave
+  constexpr int A_CHUNKS = BM * 8 / 256;           // 16-byte chunks of A per thread per K step
   constexpr int LDS_A = BM * kBK;                  // bf16 elements per stage
   constexpr int LDS_B = 256 * kBK;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * (LDS_A + LDS_B)];
@@ -141,7 +152,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmParams p) {
   const int n0 = nt * BN_MAT;
   const bool shared = (g == p.E);
 
-  // ---- A row sources (fixed for the tile) ----
+  // ---- A row sources: rows past the tile's valid rows read its first row;
+  // their results are never stored, so no masking is needed. ----
   const bf16_t* arow[A_CHUNKS];
   int akc[A_CHUNKS], ar[A_CHUNKS];
 #pragma unroll
@@ -150,70 +162,63 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmParams p) {
     const int r = c >> 3;
     ar[i] = r;
     akc[i] = c & 7;
-    const int grow = row0 + r;
-    if (r < rows) {
-      if (DUAL) {
-        int tok = shared ? (grow - p.shared_row0) : (p.sorted_assign[grow] / p.k);
-        arow[i] = p.x + (size_t)tok * p.K;
-      } else {
-        arow[i] = p.a_rows + (size_t)grow * p.K;
-      }
+    const int grow = row0 + (r < rows ? r : 0);
+    if (DUAL) {
+      const int tok = shared ? (grow - p.shared_row0) : (p.sorted_assign[grow] / p.k);
+      arow[i] = p.x + (size_t)tok * p.K + akc[i] * 8;
     } else {
-      arow[i] = nullptr;
+      arow[i] = p.a_rows + (size_t)grow * p.K + akc[i] * 8;
     }
   }
-  // ---- B block (8 k x 8 n) of this thread ----
+  // ---- B block (8 k x 8 n) of this thread; columns past N read the last
+  // valid block and are never stored. ----
   const int nb = tid & 31;
   const int kb = tid >> 5;
-  int mat = 0, ncol;
-  if (DUAL) {
-    mat = nb >> 4;
-    ncol = n0 + (nb & 15) * 8;
-  } else {
-    ncol = n0 + nb * 8;
-  }
-  const bool b_ok = ncol < p.N;
-  const size_t wstride = (size_t)p.K * p.N;
-  const void* Wbase;
-  if (shared) Wbase = mat ? p.Ws1 : p.Ws0;
-  else Wbase = mat ? p.W1 : p.W0;
-  const size_t goff = shared ? 0 : (size_t)g * wstride;
-  // row n of this block in the LDS B tile
+  const int mat = DUAL ? (nb >> 4) : 0;
+  int ncol = DUAL ? n0 + (nb & 15) * 8 : n0 + nb * 8;
+  if (ncol > p.N - 8) ncol = p.N - 8;
+  const size_t goff = shared ? 0 : (size_t)g * (size_t)p.K * p.N;
+  const void* Wbase = shared ? (mat ? p.Ws1 : p.Ws0) : (mat ? p.W1 : p.W0);
   const int bn_row0 = DUAL ? (mat * 128 + (nb & 15) * 8) : nb * 8;
+  constexpr int ES = (WK == W_FP8) ? 1 : 2;
+  const unsigned char* bptr = (const unsigned char*)Wbase + (goff + (size_t)(kb * 8) * p.N + ncol) * ES;
+  const size_t brow = (size_t)p.N * ES;
 
-  uint4 areg[A_CHUNKS];
-  uint4 breg[8];
-  uint2 breg8[8];
+  // register stages of prefetched global data (statically indexed)
+  u32x4_t sa[PF][A_CHUNKS];
+  u32x4_t sb[PF][WK == W_FP8 ? 1 : 8];
+  u32x2_t sb8[PF][WK == W_FP8 ? 8 : 1];
 
-  auto load_tile = [&](int k0) {
+  auto load_tile = [&](auto SI, int k0) {
+    constexpr int si = decltype(SI)::value;
 #pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i)
-      areg[i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0 + akc[i] * 8) : make_uint4(0, 0, 0, 0);
-    if (WK == W_FP8) {
-      const fp8_t* wb = (const fp8_t*)Wbase + goff + (size_t)(k0 + kb * 8) * p.N + ncol;
+    for (int i = 0; i < A_CHUNKS; ++i) sa[si][i] = *reinterpret_cast<const u32x4_t*>(arow[i] + k0);
+    const unsigned char* bp = bptr + (size_t)k0 * brow;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        breg8[j] = b_ok ? *reinterpret_cast<const uint2*>(wb + (size_t)j * p.N) : make_uint2(0, 0);
-    } else {
-      const bf16_t* wb = (const bf16_t*)Wbase + goff + (size_t)(k0 + kb * 8) * p.N + ncol;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        breg[j] = b_ok ? *reinterpret_cast<const uint4*>(wb + (size_t)j * p.N) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (WK == W_FP8) sb8[si][j] = *reinterpret_cast<const u32x2_t*>(bp + j * brow);
+      else sb[si][j] = *reinterpret_cast<const u32x4_t*>(bp + j * brow);
     }
   };
-  auto store_tile = [&](int stage) {
+  auto store_tile = [&](auto SI, int stage) {
+    constexpr int si = decltype(SI)::value;
     bf16_t* As = lds + stage * (LDS_A + LDS_B);
     bf16_t* Bs = As + LDS_A;
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i)
-      *reinterpret_cast<uint4*>(As + ar[i] * kBK + swz(ar[i], akc[i]) * 8) = areg[i];
-    if (WK == W_FP8) fp8_rows_to_bf16(breg8, breg);
-    uint4 o[8];
-    transpose8x8_bf16(breg, o);
+      *reinterpret_cast<u32x4_t*>(As + ar[i] * kBK + swz(ar[i], akc[i]) * 8) = sa[si][i];
+    u32x4_t o[8];
+    if constexpr (WK == W_FP8) {
+      u32x4_t rows8[8];
+      fp8_rows_to_bf16(sb8[si], rows8);
+      transpose8x8_bf16(rows8, o);
+    } else {
+      transpose8x8_bf16(sb[si], o);
+    }
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       const int row = bn_row0 + n;
-      *reinterpret_cast<uint4*>(Bs + row * kBK + swz(row, kb) * 8) = o[n];
+      *reinterpret_cast<u32x4_t*>(Bs + row * kBK + swz(row, kb) * 8) = o[n];
     }
   };
 
@@ -225,15 +230,9 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
-  const int nK = p.K / kBK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
   const int l32 = lane & 31;
   const int lhi = lane >> 5;
-  for (int kt = 0; kt < nK; ++kt) {
-    const int stage = kt & 1;
-    if (kt + 1 < nK) load_tile((kt + 1) * kBK);
+  auto compute = [&](int stage) {
     const bf16_t* As = lds + stage * (LDS_A + LDS_B);
     const bf16_t* Bs = As + LDS_A;
 #pragma unroll
@@ -242,7 +241,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmParams p) {
       bf16x8_t af[MI], bfr[NI];
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
-        const int row = wm * 64 + mi * 32 + l32;
+        const int row = wm * WROWS + mi * 32 + l32;
         af[mi] = *reinterpret_cast<const bf16x8_t*>(As + row * kBK + swz(row, chunk) * 8);
       }
 #pragma unroll
@@ -262,8 +261,38 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmParams p) {
         for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
     }
-    if (kt + 1 < nK) store_tile(stage ^ 1);
-    __syncthreads();
+  };
+
+  const int nK = p.K / kBK;
+  // prologue: K steps 0 .. PF-1 in flight, step 0 into LDS stage 0
+  load_tile(std::integral_constant<int, 0>{}, 0);
+  if constexpr (PF == 2) {
+    if (nK > 1) load_tile(std::integral_constant<int, 1>{}, kBK);
+  }
+  store_tile(std::integral_constant<int, 0>{}, 0);
+  __syncthreads();
+  // steady state: at step k, LDS stage k&1 holds step k and the register
+  // stages hold steps k+1 .. k+PF-1; step k+PF is issued before the MFMAs.
+  if constexpr (PF == 1) {
+    for (int k = 0; k < nK; ++k) {
+      if (k + 1 < nK) load_tile(std::integral_constant<int, 0>{}, (k + 1) * kBK);
+      compute(k & 1);
+      if (k + 1 < nK) store_tile(std::integral_constant<int, 0>{}, (k + 1) & 1);
+      __syncthreads();
+    }
+  } else {
+    for (int k = 0; k < nK; k += 2) {
+      if (k + 2 < nK) load_tile(std::integral_constant<int, 0>{}, (k + 2) * kBK);
+      compute(0);
+      if (k + 1 < nK) store_tile(std::integral_constant<int, 1>{}, 1);
+      __syncthreads();
+      if (k + 1 < nK) {
+        if (k + 3 < nK) load_tile(std::integral_constant<int, 1>{}, (k + 3) * kBK);
+        compute(1);
+        if (k + 2 < nK) store_tile(std::integral_constant<int, 0>{}, 0);
+        __syncthreads();
+      }
+    }
   }
 
   // ---- epilogue ----
@@ -285,7 +314,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmParams p) {
       }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = wm * 64 + mi * 32 + (v >> 2) * 8 + lhi * 4 + (v & 3);
+        const int r = wm * WROWS + mi * 32 + (v >> 2) * 8 + lhi * 4 + (v & 3);
         if (r >= rows) continue;
         const size_t orow = (size_t)(row0 + r) * p.N;
         if (DUAL) {
@@ -404,7 +433,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
 static int pick_bm(const GroupedArgs& a) {
   if (a.act_f32) return 64;
   const int avg = (a.T * a.k) / (a.E > 0 ? a.E : 1);
-  return avg >= 96 ? 128 : 64;
+  return avg >= 512 ? 256 : avg >= 96 ? 128 : 64;
 }
 
 static int max_row_tiles(int T, int k, int E, int has_shared, int BM) {
@@ -481,11 +510,13 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
       kern<<<gu_grid, 256, 0, s>>>(p);
   };
   if (a.wkind == W_FP8) {
-    if (BM == 128) launch_gu(gemm_mfma_kernel<W_FP8, true, 2>);
-    else launch_gu(gemm_mfma_kernel<W_FP8, true, 1>);
+    if (BM == 256) launch_gu(gemm_mfma_kernel<W_FP8, true, 256>);
+    else if (BM == 128) launch_gu(gemm_mfma_kernel<W_FP8, true, 128>);
+    else launch_gu(gemm_mfma_kernel<W_FP8, true, 64>);
   } else {
-    if (BM == 128) launch_gu(gemm_mfma_kernel<W_BF16, true, 2>);
-    else launch_gu(gemm_mfma_kernel<W_BF16, true, 1>);
+    if (BM == 256) launch_gu(gemm_mfma_kernel<W_BF16, true, 256>);
+    else if (BM == 128) launch_gu(gemm_mfma_kernel<W_BF16, true, 128>);
+    else launch_gu(gemm_mfma_kernel<W_BF16, true, 64>);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
@@ -497,11 +528,13 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   q.y_out = a.y;
   const int dn_grid = grid_for(maxQ, (a.d + 255) / 256);
   if (a.wkind == W_FP8) {
-    if (BM == 128) gemm_mfma_kernel<W_FP8, false, 2><<<dn_grid, 256, 0, s>>>(q);
-    else gemm_mfma_kernel<W_FP8, false, 1><<<dn_grid, 256, 0, s>>>(q);
+    if (BM == 256) gemm_mfma_kernel<W_FP8, false, 256><<<dn_grid, 256, 0, s>>>(q);
+    else if (BM == 128) gemm_mfma_kernel<W_FP8, false, 128><<<dn_grid, 256, 0, s>>>(q);
+    else gemm_mfma_kernel<W_FP8, false, 64><<<dn_grid, 256, 0, s>>>(q);
   } else {
-    if (BM == 128) gemm_mfma_kernel<W_BF16, false, 2><<<dn_grid, 256, 0, s>>>(q);
-    else gemm_mfma_kernel<W_BF16, false, 1><<<dn_grid, 256, 0, s>>>(q);
+    if (BM == 256) gemm_mfma_kernel<W_BF16, false, 256><<<dn_grid, 256, 0, s>>>(q);
+    else if (BM == 128) gemm_mfma_kernel<W_BF16, false, 128><<<dn_grid, 256, 0, s>>>(q);
+    else gemm_mfma_kernel<W_BF16, false, 64><<<dn_grid, 256, 0, s>>>(q);
   }
   return hipGetLastError();
 }
