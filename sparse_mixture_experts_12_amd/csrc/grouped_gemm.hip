@@ -122,7 +122,7 @@ __device__ __forceinline__ void fp8_rows_to_bf16(const u32x2_t (&r8)[8], u32x4_t
 template <int BM> struct TileCfg {
   static constexpr int WM = (BM >= 128) ? 2 : 1;
   static constexpr int WN = 4 / WM;
-  static constexpr int PF = (BM == 128) ? 2 : 1;
+  static constexpr int PF = (BM <= 128) ? 2 : 1;
   static constexpr int OCC = (BM == 64) ? 2 : 1;    // work-groups per CU
 };
 
@@ -264,34 +264,58 @@ __global__ __launch_bounds__(256, TileCfg<BM>::OCC) void gemm_mfma_kernel(GemmPa
   };
 
   const int nK = p.K / kBK;
-  // prologue: K steps 0 .. PF-1 in flight, step 0 into LDS stage 0
-  load_tile(std::integral_constant<int, 0>{}, 0);
-  if constexpr (PF == 2) {
-    if (nK > 1) load_tile(std::integral_constant<int, 1>{}, kBK);
-  }
-  store_tile(std::integral_constant<int, 0>{}, 0);
-  __syncthreads();
-  // steady state: at step k, LDS stage k&1 holds step k and the register
-  // stages hold steps k+1 .. k+PF-1; step k+PF is issued before the MFMAs.
+  // The steady-state loops issue and retire their loads unconditionally; the
+  // last steps are peeled, so no load is ever pending on a merge of control
+  // flow (which would make the compiler drain every load early).
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
   if constexpr (PF == 1) {
-    for (int k = 0; k < nK; ++k) {
-      if (k + 1 < nK) load_tile(std::integral_constant<int, 0>{}, (k + 1) * kBK);
+    // step k in LDS stage k&1; step k+1's loads are issued before step k's
+    // MFMAs and stored to the other stage after them
+    load_tile(I0{}, 0);
+    store_tile(I0{}, 0);
+    __syncthreads();
+    int k = 0;
+    for (; k + 1 < nK; ++k) {
+      load_tile(I0{}, (k + 1) * kBK);
+      __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the MFMAs
       compute(k & 1);
-      if (k + 1 < nK) store_tile(std::integral_constant<int, 0>{}, (k + 1) & 1);
+      store_tile(I0{}, (k + 1) & 1);
       __syncthreads();
     }
+    compute(k & 1);
   } else {
-    for (int k = 0; k < nK; k += 2) {
-      if (k + 2 < nK) load_tile(std::integral_constant<int, 0>{}, (k + 2) * kBK);
+    // pairs of steps: LDS stages 0/1 hold steps k, k+1; the loads of steps
+    // k+2, k+3 are issued first and stored after both steps' MFMAs
+    load_tile(I0{}, 0);
+    load_tile(I1{}, (nK > 1 ? 1 : 0) * kBK);
+    store_tile(I0{}, 0);
+    store_tile(I1{}, 1);
+    __syncthreads();
+    int k = 0;
+    for (; k + 3 < nK; k += 2) {
+      load_tile(I0{}, (k + 2) * kBK);
+      load_tile(I1{}, (k + 3) * kBK);
+      __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the MFMAs
       compute(0);
-      if (k + 1 < nK) store_tile(std::integral_constant<int, 1>{}, 1);
+      compute(1);
       __syncthreads();
-      if (k + 1 < nK) {
-        if (k + 3 < nK) load_tile(std::integral_constant<int, 1>{}, (k + 3) * kBK);
-        compute(1);
-        if (k + 2 < nK) store_tile(std::integral_constant<int, 0>{}, 0);
-        __syncthreads();
-      }
+      store_tile(I0{}, 0);
+      store_tile(I1{}, 1);
+      __syncthreads();
+    }
+    const int rem = nK - k;          // 1, 2 or 3 steps left; k and k+1 in LDS
+    if (rem == 3) {
+      load_tile(I0{}, (k + 2) * kBK);
+      compute(0);
+      compute(1);
+      __syncthreads();
+      store_tile(I0{}, 0);
+      __syncthreads();
+      compute(0);
+    } else {
+      compute(0);
+      if (rem == 2) compute(1);
     }
   }
 
@@ -433,7 +457,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
 static int pick_bm(const GroupedArgs& a) {
   if (a.act_f32) return 64;
   const int avg = (a.T * a.k) / (a.E > 0 ? a.E : 1);
-  return avg >= 512 ? 256 : avg >= 96 ? 128 : 64;
+  // measured on MI355X: 256-row tiles win for ~1000 rows per expert (Mixtral
+  // prefill), 64-row tiles for tens of rows per expert (fine-grained, fp8)
+  return avg >= 256 ? 256 : 64;
 }
 
 static int max_row_tiles(int T, int k, int E, int has_shared, int BM) {
@@ -511,11 +537,9 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   };
   if (a.wkind == W_FP8) {
     if (BM == 256) launch_gu(gemm_mfma_kernel<W_FP8, true, 256>);
-    else if (BM == 128) launch_gu(gemm_mfma_kernel<W_FP8, true, 128>);
     else launch_gu(gemm_mfma_kernel<W_FP8, true, 64>);
   } else {
     if (BM == 256) launch_gu(gemm_mfma_kernel<W_BF16, true, 256>);
-    else if (BM == 128) launch_gu(gemm_mfma_kernel<W_BF16, true, 128>);
     else launch_gu(gemm_mfma_kernel<W_BF16, true, 64>);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -529,11 +553,9 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   const int dn_grid = grid_for(maxQ, (a.d + 255) / 256);
   if (a.wkind == W_FP8) {
     if (BM == 256) gemm_mfma_kernel<W_FP8, false, 256><<<dn_grid, 256, 0, s>>>(q);
-    else if (BM == 128) gemm_mfma_kernel<W_FP8, false, 128><<<dn_grid, 256, 0, s>>>(q);
     else gemm_mfma_kernel<W_FP8, false, 64><<<dn_grid, 256, 0, s>>>(q);
   } else {
     if (BM == 256) gemm_mfma_kernel<W_BF16, false, 256><<<dn_grid, 256, 0, s>>>(q);
-    else if (BM == 128) gemm_mfma_kernel<W_BF16, false, 128><<<dn_grid, 256, 0, s>>>(q);
     else gemm_mfma_kernel<W_BF16, false, 64><<<dn_grid, 256, 0, s>>>(q);
   }
   return hipGetLastError();

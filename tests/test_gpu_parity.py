@@ -35,6 +35,9 @@ SMALL = {
     "bf16_k_equals_E": C["mixtral_prefill"].with_(T=40, d=256, f=256, E=4, k=4, seed=6),
     "bf16_one_expert": C["mixtral_prefill"].with_(T=50, d=256, f=256, E=1, k=1, seed=7),
     "bf16_top1_switch": C["mixtral_prefill"].with_(T=90, d=256, f=256, E=16, k=1, capacity_factor=1.0),
+    "bf16_big_tiles": C["mixtral_prefill"].with_(T=600, d=256, f=512, E=4, k=2, seed=8),
+    "fp8_big_tiles_shared": C["fp8_capacity"].with_(T=700, d=256, E=4, k=2, f=256, capacity_factor=0.0,
+                                                     shared=True, seed=9),
     "decode_T1": C["mixtral_decode"].with_(d=512, f=1024),
     "decode_T8": C["mixtral_decode_b8"].with_(d=512, f=1024),
     "decode_T5_shared_fp8": C["fp8_capacity_decode"].with_(T=5, d=256, E=16, f=256, shared=True),
@@ -175,7 +178,7 @@ def test_permute_all_to_one_expert_with_capacity():
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("name", ["tiny_f32", "tiny_f32_ragged", "bf16_prefill", "bf16_prefill_ragged",
                                   "bf16_finegrained_shared", "fp8_capacity", "fp8_capacity_tight",
-                                  "bf16_one_expert"])
+                                  "bf16_one_expert", "bf16_big_tiles", "fp8_big_tiles_shared"])
 def test_grouped_ffn_parity(name):
     cfg = SMALL[name]
     print(f"[grouped_ffn] {name}", flush=True)
