@@ -100,7 +100,7 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
-def cpu_baseline(cfg, inp, budget_s=12.0, max_calls=64):
+def cpu_baseline(cfg, inp, budget_s=12.0, max_calls=2000):
     """The CPU oracle, as it stands, on single-token (decode) or small-batch calls."""
     import numpy as np
     import oracle
