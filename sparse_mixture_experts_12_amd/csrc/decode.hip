@@ -205,20 +205,21 @@ __global__ __launch_bounds__(256) void decode_ffn_kernel(DecodeParams p) {
   }
 }
 
-// Sum the slice partials of the used experts for 64 columns of one token:
-// out = sum_j w[t,j] * partial[unit(t,j)][s] (+ shared partials), taken in a
-// fixed order (unit-major, then slices s = g, g + 16, ... per slice group g,
-// then the 16 group sums in order) and rounded once to bf16.
+// Sum the slice partials of the used experts for 16 columns of one token:
+// out = sum_j w[t,j] * partial[unit(t,j)][s] (+ shared partials).  Thread
+// (slice lane sl, column quad cq) accumulates s = sl, sl + 64, ... unit-major
+// in a fixed order; the 64 slice lanes are then added by a fixed LDS tree and
+// the result is rounded once to bf16.
 __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restrict__ partial,
                                                             const int32_t* __restrict__ plan,
                                                             const float* __restrict__ topk_w, int T, int d, int E,
                                                             int k, int n_slices, int maxU, int has_shared,
                                                             bf16_t* __restrict__ out) {
-  __shared__ float4 red[16][16];
+  __shared__ float4 red[64][4];
   const int t = blockIdx.y;
-  const int cq = threadIdx.x & 15;
-  const int col = blockIdx.x * 64 + cq * 4;
-  const int sg = threadIdx.x >> 4;
+  const int cq = threadIdx.x & 3;
+  const int sl = threadIdx.x >> 2;
+  const int col = blockIdx.x * 16 + cq * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   const int nunits = k + (has_shared ? 1 : 0);
   for (int j = 0; j < nunits; ++j) {
@@ -233,8 +234,8 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
       wgt = 1.f;
     }
     const float* base = partial + ((size_t)unit * n_slices * T + t) * d + col;
-#pragma unroll 8
-    for (int s = sg; s < n_slices; s += 16) {
+#pragma unroll 4
+    for (int s = sl; s < n_slices; s += 64) {
       const float4 v = *reinterpret_cast<const float4*>(base + (size_t)s * T * d);
       acc.x = __fmaf_rn(wgt, v.x, acc.x);
       acc.y = __fmaf_rn(wgt, v.y, acc.y);
@@ -242,14 +243,19 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
       acc.w = __fmaf_rn(wgt, v.w, acc.w);
     }
   }
-  red[sg][cq] = acc;
+  red[sl][cq] = acc;
   __syncthreads();
-  if (sg == 0) {
-    float4 tot = red[0][cq];
-    for (int q = 1; q < 16; ++q) {
-      const float4 v = red[q][cq];
-      tot.x += v.x; tot.y += v.y; tot.z += v.z; tot.w += v.w;
+  for (int half = 32; half >= 1; half >>= 1) {
+    if (sl < half) {
+      const float4 o = red[sl + half][cq];
+      float4 v = red[sl][cq];
+      v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+      red[sl][cq] = v;
     }
+    __syncthreads();
+  }
+  if (sl == 0) {
+    const float4 tot = red[0][cq];
     uint2 o;
     o.x = pack_bf16x2(tot.x, tot.y);
     o.y = pack_bf16x2(tot.z, tot.w);
@@ -340,7 +346,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   hipError_t err = (a.wkind == W_FP8) ? launch_decode_mt<W_FP8>(p, units, fs, s, a.ev_begin, a.ev_end)
                                       : launch_decode_mt<W_BF16>(p, units, fs, s, a.ev_begin, a.ev_end);
   if (err != hipSuccess) return err;
-  dim3 g2(a.d / 64, a.T);
+  dim3 g2(a.d / 16, a.T);
   decode_reduce_kernel<<<g2, 256, 0, s>>>(a.partial, a.plan, a.topk_w, a.T, a.d, a.E, a.k, a.f / fs, p.maxU,
                                           a.has_shared, (bf16_t*)a.out);
   return hipGetLastError();
