@@ -315,8 +315,7 @@ __device__ void wave_topk_rank(const float* lg, int E, int k, int renormalize, i
   if (lane < k) {
     const int e = sel[lane];
     out_idx[lane] = e;
-    const double pe = exp((double)lg[e] - (double)m);
-    out_w[lane] = (float)(pe / den);
+    out_w[lane] = (float)((renormalize ? ps[lane] : ps[e]) / den);
   }
 }
 
@@ -325,7 +324,7 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
     const TIn* __restrict__ x, const TIn* __restrict__ W, const float* __restrict__ bias, int T, int d,
     int E, int k, int renormalize, int cap, float* __restrict__ logits_out, int32_t* __restrict__ idx_out,
     float* __restrict__ w_out, int32_t* __restrict__ plan) {
-  __shared__ double wpart[kSmallWaves][64][8];
+  __shared__ double wpart[kSmallThreads][8];
   __shared__ float lg[MT * 1024];
   __shared__ int32_t sidx[MT * 32];
   __shared__ double ps[MT][256];
@@ -405,33 +404,35 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
         }
       }
     }
-    // butterfly over the lanes that share a chunk (fixed order)
-    for (int off = ecp; off < 64; off <<= 1) {
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[t][j] += __shfl_xor(acc[t][j], off);
-    }
+    // Reduction over the row groups, one token at a time: every thread stores
+    // its 8 sums in LDS; output (chunk c, column j) is then added by L lanes
+    // (each over a fixed stride of row groups) and a fixed butterfly across
+    // those L lanes of one wave.
+    const int nout = nchunk * 8;
+    int L = 1;
+    while (L * nout * 2 <= kSmallThreads && L < 64) L <<= 1;
+    const int o = tid / L, l = tid % L;
+    const int oc = o >> 3, oj = o & 7;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       if (t >= T) break;
-      if (lane < ecp) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) wpart[wave][lane][j] = acc[t][j];
-      }
+      for (int j = 0; j < 8; ++j) wpart[tid][j] = acc[t][j];
       __syncthreads();
-      if (tid < nchunk * 8) {
-        const int c = tid >> 3, j = tid & 7;
-        if (c * 8 + j < ne) {
-          double s = 0.0;
-#pragma unroll
-          for (int w = 0; w < kSmallWaves; ++w) s += wpart[w][c][j];
-          const int e = e0 + c * 8 + j;
-          if (bias) s += (double)bias[e];
-          const float l = (float)s;
-          lg[t * 1024 + e] = l;
-          if (logits_out) logits_out[(size_t)t * E + e] = l;
-        }
+      double sum = 0.0;
+      if (o < nout) {
+        // thread (rg, ec) stored its sums at index rg_wave * 64 + lane; row
+        // group r of chunk c lives at thread r * ecp + c (waves hold
+        // rows_per_wave row groups each)
+        for (int r = l; r < RG; r += L) sum += wpart[r * ecp + oc][oj];
+      }
+      for (int off = 1; off < L; off <<= 1) sum += __shfl_xor(sum, off);
+      if (o < nout && l == 0 && oc * 8 + oj < ne) {
+        const int e = e0 + oc * 8 + oj;
+        if (bias) sum += (double)bias[e];
+        const float lv = (float)sum;
+        lg[t * 1024 + e] = lv;
+        if (logits_out) logits_out[(size_t)t * E + e] = lv;
       }
       __syncthreads();
     }
