@@ -85,33 +85,39 @@ __device__ __forceinline__ bool decode_tile(const int32_t* sched, int maxQ, int 
   return true;
 }
 
-// 8 rows x 8 bf16 (row-major, 16 B per row) -> 8 vectors of 8 K-values.
-// Native vector types only, so the staging arrays stay in registers.
-__device__ __forceinline__ void transpose8x8_bf16(const u32x4_t (&r)[8], u32x4_t (&o)[8]) {
+// 8 fp8 e4m3fn codes -> 8 bf16 (exact: at most 4 significant bits).
+__device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(u32x2_t q) {
+  float v[8];
+  fp8x4_to_f32(q[0], v);
+  fp8x4_to_f32(q[1], v + 4);
+  u32x4_t w;
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    u32x4_t d;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t a = r[2 * p][n >> 1], b = r[2 * p + 1][n >> 1];
-      d[p] = (n & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-    o[n] = d;
-  }
+  for (int p = 0; p < 4; ++p) w[p] = (__float_as_uint(v[2 * p]) >> 16) | (__float_as_uint(v[2 * p + 1]) & 0xffff0000u);
+  return w;
 }
 
-// fp8 e4m3fn (8 per row, 8 B) -> bf16 bits (exact: at most 4 significant bits).
-__device__ __forceinline__ void fp8_rows_to_bf16(const u32x2_t (&r8)[8], u32x4_t (&r)[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float v[8];
-    fp8x4_to_f32(r8[j][0], v);
-    fp8x4_to_f32(r8[j][1], v + 4);
-    u32x4_t w;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) w[p] = (__float_as_uint(v[2 * p]) >> 16) | (__float_as_uint(v[2 * p + 1]) & 0xffff0000u);
-    r[j] = w;
-  }
+// LDS B tile: 64 K-rows x 256 output columns, N-contiguous as in global
+// memory; the column index is XOR-swizzled by (k & 3) << 4 so that the four
+// K-rows read together by a transposing LDS read fall in different banks.
+__device__ __forceinline__ int bswz(int k, int n) { return k * 256 + (n ^ ((k & 3) << 4)); }
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// MFMA B fragment (8 consecutive K of one output column per lane) from the
+// N-contiguous LDS tile with two gfx950 transposing reads.  Within each group
+// of 16 lanes, input lane x supplies a 4-element row R_x and output lane
+// 4a + b receives R_a[b], R_{a+4}[b], R_{a+8}[b], R_{a+12}[b].
+__device__ __forceinline__ bf16x8_t load_b_frag(const bf16_t* Bs, int kbase, int nbase, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int a = i & 3, j = i >> 2;
+  const int n = nbase + 16 * (g & 1) + 4 * a;
+  const int k0 = kbase + 8 * (g >> 1) + j;
+  typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(Bs + bswz(k0, n)));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(Bs + bswz(k0 + 4, n)));
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
 }
 
 // Tile shapes (4 waves): BM = 256 -> waves 2x2, 128 rows x 128 B-rows each;
@@ -170,18 +176,19 @@ __global__ __launch_bounds__(256, TileCfg<BM>::OCC) void gemm_mfma_kernel(GemmPa
       arow[i] = p.a_rows + (size_t)grow * p.K + akc[i] * 8;
     }
   }
-  // ---- B block (8 k x 8 n) of this thread; columns past N read the last
-  // valid block and are never stored. ----
-  const int nb = tid & 31;
-  const int kb = tid >> 5;
-  const int mat = DUAL ? (nb >> 4) : 0;
-  int ncol = DUAL ? n0 + (nb & 15) * 8 : n0 + nb * 8;
+  // ---- B: 8 chunks of 8 columns per thread, chunk c = tid + 256 i covers
+  // K-row (tid >> 5) + 8 i and tile columns 8 * (tid & 31) .. +7 (for the
+  // gate/up GEMM columns 0..127 come from W_gate, 128..255 from W_up).
+  // Columns past N read the last valid chunk and are never stored. ----
+  const int cc = tid & 31;
+  const int kr0 = tid >> 5;
+  const int mat = DUAL ? (cc >> 4) : 0;
+  int ncol = DUAL ? n0 + (cc & 15) * 8 : n0 + cc * 8;
   if (ncol > p.N - 8) ncol = p.N - 8;
   const size_t goff = shared ? 0 : (size_t)g * (size_t)p.K * p.N;
   const void* Wbase = shared ? (mat ? p.Ws1 : p.Ws0) : (mat ? p.W1 : p.W0);
-  const int bn_row0 = DUAL ? (mat * 128 + (nb & 15) * 8) : nb * 8;
   constexpr int ES = (WK == W_FP8) ? 1 : 2;
-  const unsigned char* bptr = (const unsigned char*)Wbase + (goff + (size_t)(kb * 8) * p.N + ncol) * ES;
+  const unsigned char* bptr = (const unsigned char*)Wbase + (goff + (size_t)kr0 * p.N + ncol) * ES;
   const size_t brow = (size_t)p.N * ES;
 
   // register stages of prefetched global data (statically indexed)
@@ -196,8 +203,8 @@ __global__ __launch_bounds__(256, TileCfg<BM>::OCC) void gemm_mfma_kernel(GemmPa
     const unsigned char* bp = bptr + (size_t)k0 * brow;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if constexpr (WK == W_FP8) sb8[si][j] = *reinterpret_cast<const u32x2_t*>(bp + j * brow);
-      else sb[si][j] = *reinterpret_cast<const u32x4_t*>(bp + j * brow);
+      if constexpr (WK == W_FP8) sb8[si][j] = *reinterpret_cast<const u32x2_t*>(bp + (size_t)(8 * j) * brow);
+      else sb[si][j] = *reinterpret_cast<const u32x4_t*>(bp + (size_t)(8 * j) * brow);
     }
   };
   auto store_tile = [&](auto SI, int stage) {
@@ -207,18 +214,12 @@ __global__ __launch_bounds__(256, TileCfg<BM>::OCC) void gemm_mfma_kernel(GemmPa
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i)
       *reinterpret_cast<u32x4_t*>(As + ar[i] * kBK + swz(ar[i], akc[i]) * 8) = sa[si][i];
-    u32x4_t o[8];
-    if constexpr (WK == W_FP8) {
-      u32x4_t rows8[8];
-      fp8_rows_to_bf16(sb8[si], rows8);
-      transpose8x8_bf16(rows8, o);
-    } else {
-      transpose8x8_bf16(sb[si], o);
-    }
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int row = bn_row0 + n;
-      *reinterpret_cast<u32x4_t*>(Bs + row * kBK + swz(row, kb) * 8) = o[n];
+    for (int j = 0; j < 8; ++j) {
+      u32x4_t v;
+      if constexpr (WK == W_FP8) v = fp8x8_to_bf16x8(sb8[si][j]);
+      else v = sb[si][j];
+      *reinterpret_cast<u32x4_t*>(Bs + bswz(kr0 + 8 * j, cc * 8)) = v;
     }
   };
 
@@ -246,14 +247,14 @@ __global__ __launch_bounds__(256, TileCfg<BM>::OCC) void gemm_mfma_kernel(GemmPa
       }
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
-        int row;
+        int nbase;
         if (DUAL) {
           const int m_ = ni / NI_MAT, nl = ni % NI_MAT;
-          row = m_ * 128 + wn * (128 / WN) + nl * 32 + l32;
+          nbase = m_ * 128 + wn * (128 / WN) + nl * 32;
         } else {
-          row = wn * (256 / WN) + ni * 32 + l32;
+          nbase = wn * (256 / WN) + ni * 32;
         }
-        bfr[ni] = *reinterpret_cast<const bf16x8_t*>(Bs + row * kBK + swz(row, chunk) * 8);
+        bfr[ni] = load_b_frag(Bs, ks * 16, nbase, lane);
       }
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
