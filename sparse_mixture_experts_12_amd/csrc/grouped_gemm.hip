@@ -355,6 +355,183 @@ __global__ __launch_bounds__(256, TileCfg<BM>::OCC) void gemm_mfma_kernel(GemmPa
 }
 
 // ---------------------------------------------------------------------------
+// bf16 weights: operands move from global memory straight into LDS
+// (global_load_lds, 16 bytes per lane), so no register staging and no LDS
+// store instructions.  One such load fills 1 KB of LDS in lane order; the LDS
+// swizzles are therefore applied on the source side: the lane that owns LDS
+// chunk c fetches the global chunk that the swizzle maps to c.
+// Two LDS stages: step k+1 streams into one stage while step k's MFMAs read
+// the other; a single barrier per step hands the stages over.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
+
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }   // vmcnt(0)
+
+template <bool DUAL, int BM>
+__global__ __launch_bounds__(256, TileCfg<BM>::OCC) void gemm_dl_kernel(GemmParams p) {
+  constexpr int WM = TileCfg<BM>::WM, WN = TileCfg<BM>::WN;
+  constexpr int NMAT = DUAL ? 2 : 1;
+  constexpr int BN_MAT = DUAL ? 128 : 256;
+  constexpr int NI_MAT = BN_MAT / WN / 32;
+  constexpr int NI = NI_MAT * NMAT;
+  constexpr int MI = BM / WM / 32;
+  constexpr int WROWS = BM / WM;
+  constexpr int A_LD = BM / 32;                    // 1 KB A blocks per wave per step (8 rows each)
+  constexpr int B_LD = 8;                          // 1 KB B blocks per wave per step (2 K-rows each)
+  constexpr int LDS_A = BM * kBK;
+  constexpr int LDS_B = 256 * kBK;
+  __shared__ __attribute__((aligned(1024))) bf16_t As0[LDS_A];
+  __shared__ __attribute__((aligned(1024))) bf16_t Bs0[LDS_B];
+  __shared__ __attribute__((aligned(1024))) bf16_t As1[LDS_A];
+  __shared__ __attribute__((aligned(1024))) bf16_t Bs1[LDS_B];
+
+  const int n_tiles = (p.N + BN_MAT - 1) / BN_MAT;
+  int g, row0, rows, nt;
+  if (!decode_tile(p.sched, p.maxQ, n_tiles, &g, &row0, &rows, &nt)) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const int n0 = nt * BN_MAT;
+  const bool shared = (g == p.E);
+
+  // ---- A sources: block b = wave + 4 i holds tile rows 8 b .. 8 b + 7; this
+  // lane fills row 8 b + lane / 8, LDS chunk lane % 8, i.e. global chunk
+  // (lane % 8) ^ key(row).  Rows past the tile's valid rows read its first
+  // row (never stored). ----
+  const bf16_t* asrc[A_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int r = 8 * (wave + 4 * i) + (lane >> 3);
+    const int gc = swz(r, lane & 7);
+    const int grow = row0 + (r < rows ? r : 0);
+    if (DUAL) {
+      const int tok = shared ? (grow - p.shared_row0) : (p.sorted_assign[grow] / p.k);
+      asrc[i] = p.x + (size_t)tok * p.K + gc * 8;
+    } else {
+      asrc[i] = p.a_rows + (size_t)grow * p.K + gc * 8;
+    }
+  }
+  // ---- B sources: block b = 8 wave + j holds K-rows 2 b, 2 b + 1; this lane
+  // fills K-row 2 b + lane / 32, LDS chunk lane % 32, i.e. tile column chunk
+  // (lane % 32) ^ 2 (krow & 3) (columns 0..127 gate, 128..255 up for the
+  // gate/up GEMM).  Columns past N read the last valid chunk (never stored).
+  const size_t goff = shared ? 0 : (size_t)g * (size_t)p.K * p.N;
+  const size_t brow = (size_t)p.N * 2;
+  const unsigned char* bsrc[2];                    // by parity of j
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int h = lane >> 5;
+    const int krow = 2 * (8 * wave + par) + h;     // K-row of block j = par (others add 2 j)
+    const int gc = (lane & 31) ^ (2 * (krow & 3));
+    const int mat = DUAL ? (gc >> 4) : 0;
+    int ncol = DUAL ? n0 + (gc & 15) * 8 : n0 + gc * 8;
+    if (ncol > p.N - 8) ncol = p.N - 8;
+    const void* Wbase = shared ? (mat ? p.Ws1 : p.Ws0) : (mat ? p.W1 : p.W0);
+    bsrc[par] = (const unsigned char*)Wbase + (goff + (size_t)krow * p.N + ncol) * 2;
+  }
+
+  auto issue = [&](bf16_t* As, bf16_t* Bs, int k0) {
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(asrc[i] + k0), (lds_ptr_t)(As + (wave + 4 * i) * 512), 16, 0, 0);
+    const size_t kb = (size_t)k0 * brow;
+#pragma unroll
+    for (int j = 0; j < B_LD; ++j)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(bsrc[j & 1] + kb + (size_t)(2 * (j & ~1)) * brow),
+                                       (lds_ptr_t)(Bs + (8 * wave + j) * 512), 16, 0, 0);
+  };
+
+  f32x16_t acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+
+  const int l32 = lane & 31;
+  const int lhi = lane >> 5;
+  auto frags = [&](const bf16_t* As, const bf16_t* Bs, int ks, bf16x8_t* af, bf16x8_t* bfr) {
+    const int chunk = ks * 2 + lhi;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int row = wm * WROWS + mi * 32 + l32;
+      af[mi] = *reinterpret_cast<const bf16x8_t*>(As + row * kBK + swz(row, chunk) * 8);
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      int nbase;
+      if (DUAL) {
+        const int m_ = ni / NI_MAT, nl = ni % NI_MAT;
+        nbase = m_ * 128 + wn * (128 / WN) + nl * 32;
+      } else {
+        nbase = wn * (256 / WN) + ni * 32;
+      }
+      bfr[ni] = load_b_frag(Bs, ks * 16, nbase, lane);
+    }
+  };
+  // fragments of sub-step ks + 1 are read while sub-step ks's MFMAs run
+  auto compute = [&](const bf16_t* As, const bf16_t* Bs) {
+    bf16x8_t af[2][MI], bfr[2][NI];
+    frags(As, Bs, 0, af[0], bfr[0]);
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      if (ks + 1 < kBK / 16) frags(As, Bs, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][mi], bfr[ks & 1][ni], acc[mi][ni], 0, 0, 0);
+    }
+  };
+
+  // Steps alternate between stage 0 (even) and stage 1 (odd).  Before a step
+  // computes, every wave waits for its own loads into that stage and meets the
+  // others at the barrier, which also certifies that the other stage is no
+  // longer read and may be refilled.
+  const int nK = p.K / kBK;
+  issue(As0, Bs0, 0);
+  int k = 0;
+  for (; k + 1 < nK; k += 2) {
+    wait_vmem_all();
+    __builtin_amdgcn_s_barrier();
+    issue(As1, Bs1, (k + 1) * kBK);
+    compute(As0, Bs0);
+    wait_vmem_all();
+    __builtin_amdgcn_s_barrier();
+    if (k + 2 < nK) issue(As0, Bs0, (k + 2) * kBK);
+    compute(As1, Bs1);
+  }
+  if (k < nK) {          // odd number of steps: the last one is in stage 0
+    wait_vmem_all();
+    __builtin_amdgcn_s_barrier();
+    compute(As0, Bs0);
+  }
+
+  // ---- epilogue ----
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+    for (int nl = 0; nl < NI_MAT; ++nl) {
+      const int col = n0 + wn * (BN_MAT / WN) + nl * 32 + l32;
+      if (col >= p.N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * WROWS + mi * 32 + (v >> 2) * 8 + lhi * 4 + (v & 3);
+        if (r >= rows) continue;
+        const size_t orow = (size_t)(row0 + r) * p.N;
+        if (DUAL) p.h_out[orow + col] = (bf16_t)f32_to_bf16(silu_f(acc[mi][nl][v]) * acc[mi][nl + NI_MAT][v]);
+        else p.y_out[orow + col] = acc[mi][nl][v];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 layer: SIMT grouped GEMM, 64 rows x 64 columns per tile, fp32 FMA.
 // ---------------------------------------------------------------------------
 struct GemmParamsF32 {
@@ -540,8 +717,8 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
     if (BM == 256) launch_gu(gemm_mfma_kernel<W_FP8, true, 256>);
     else launch_gu(gemm_mfma_kernel<W_FP8, true, 64>);
   } else {
-    if (BM == 256) launch_gu(gemm_mfma_kernel<W_BF16, true, 256>);
-    else launch_gu(gemm_mfma_kernel<W_BF16, true, 64>);
+    if (BM == 256) launch_gu(gemm_dl_kernel<true, 256>);
+    else launch_gu(gemm_dl_kernel<true, 64>);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
@@ -556,8 +733,8 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
     if (BM == 256) gemm_mfma_kernel<W_FP8, false, 256><<<dn_grid, 256, 0, s>>>(q);
     else gemm_mfma_kernel<W_FP8, false, 64><<<dn_grid, 256, 0, s>>>(q);
   } else {
-    if (BM == 256) gemm_mfma_kernel<W_BF16, false, 256><<<dn_grid, 256, 0, s>>>(q);
-    else gemm_mfma_kernel<W_BF16, false, 64><<<dn_grid, 256, 0, s>>>(q);
+    if (BM == 256) gemm_dl_kernel<false, 256><<<dn_grid, 256, 0, s>>>(q);
+    else gemm_dl_kernel<false, 64><<<dn_grid, 256, 0, s>>>(q);
   }
   return hipGetLastError();
 }
