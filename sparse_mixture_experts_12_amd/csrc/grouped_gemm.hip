@@ -367,6 +367,23 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
 
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }   // vmcnt(0)
+__device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0x0070); }    // vmcnt(0) lgkmcnt(0)
+
+// Scheduling hint for one K sub-step: each MFMA is followed by its share of
+// the LDS fragment reads (DS) and of the global->LDS loads (VM), so the
+// memory instructions issue while the matrix core is busy.
+template <int NMF, int NDS, int NVM, int I = 0>
+__device__ __forceinline__ void sched_interleave() {
+  if constexpr (I < NMF) {
+    constexpr int DPM = (NDS + NMF - 1) / NMF, VPM = (NVM + NMF - 1) / NMF;
+    constexpr int D = (NDS - I * DPM) < DPM ? (NDS - I * DPM) : DPM;
+    constexpr int V = (NVM - I * VPM) < VPM ? (NVM - I * VPM) : VPM;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (D > 0) __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
+    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x010, V, 0);
+    sched_interleave<NMF, NDS, NVM, I + 1>();
+  }
+}
 
 template <bool DUAL, int BM>
 __global__ __launch_bounds__(256, TileCfg<BM>::OCC) void gemm_dl_kernel(GemmParams p) {
@@ -474,43 +491,60 @@ __global__ __launch_bounds__(256, TileCfg<BM>::OCC) void gemm_dl_kernel(GemmPara
       bfr[ni] = load_b_frag(Bs, ks * 16, nbase, lane);
     }
   };
-  // fragments of sub-step ks + 1 are read while sub-step ks's MFMAs run
-  auto compute = [&](const bf16_t* As, const bf16_t* Bs) {
-    bf16x8_t af[2][MI], bfr[2][NI];
-    frags(As, Bs, 0, af[0], bfr[0]);
+  auto mfmas = [&](const bf16x8_t* af, const bf16x8_t* bfr) {
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      if (ks + 1 < kBK / 16) frags(As, Bs, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][mi], bfr[ks & 1][ni], acc[mi][ni], 0, 0, 0);
-    }
+      for (int ni = 0; ni < NI; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
   };
+  constexpr int NMF = MI * NI;           // MFMAs per 16-wide K sub-step
+  constexpr int NDS = MI + 2 * NI;       // LDS fragment reads per sub-step
+  constexpr int NVM = A_LD + B_LD;       // global->LDS loads per K step
 
-  // Steps alternate between stage 0 (even) and stage 1 (odd).  Before a step
-  // computes, every wave waits for its own loads into that stage and meets the
-  // others at the barrier, which also certifies that the other stage is no
-  // longer read and may be refilled.
+  // Software pipeline over 16-wide K sub-steps: the fragments of sub-step
+  // s + 1 are read while sub-step s's MFMAs run, across step boundaries too.
+  // A step's last sub-step runs after the barrier that publishes the next
+  // stage, so its MFMAs cover the first reads of the next step; that barrier
+  // also certifies that every wave has finished reading the step's stage,
+  // which is then refilled two steps ahead.  Near the end the refill repeats
+  // the last step (never read again), so every load is unconditional.
   const int nK = p.K / kBK;
+  bf16x8_t fa0[MI], fb0[NI], fa1[MI], fb1[NI];
   issue(As0, Bs0, 0);
+  wait_vmem_all();
+  __builtin_amdgcn_s_barrier();
+  issue(As1, Bs1, (nK > 1 ? 1 : 0) * kBK);
+  frags(As0, Bs0, 0, fa0, fb0);
+  auto step = [&](const bf16_t* As, const bf16_t* Bs, bf16_t* Aw, bf16_t* Bw, const bf16_t* An, const bf16_t* Bn,
+                  int k) {
+    frags(As, Bs, 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    sched_interleave<NMF, NDS, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    frags(As, Bs, 2, fa0, fb0);
+    mfmas(fa1, fb1);
+    sched_interleave<NMF, NDS, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    frags(As, Bs, 3, fa1, fb1);
+    mfmas(fa0, fb0);
+    sched_interleave<NMF, NDS, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    wait_all_mem();
+    __builtin_amdgcn_s_barrier();
+    issue(Aw, Bw, min(k + 2, nK - 1) * kBK);
+    frags(An, Bn, 0, fa0, fb0);
+    mfmas(fa1, fb1);
+    sched_interleave<NMF, NDS, NVM>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
   int k = 0;
   for (; k + 1 < nK; k += 2) {
-    wait_vmem_all();
-    __builtin_amdgcn_s_barrier();
-    issue(As1, Bs1, (k + 1) * kBK);
-    compute(As0, Bs0);
-    wait_vmem_all();
-    __builtin_amdgcn_s_barrier();
-    if (k + 2 < nK) issue(As0, Bs0, (k + 2) * kBK);
-    compute(As1, Bs1);
+    step(As0, Bs0, As0, Bs0, As1, Bs1, k);
+    step(As1, Bs1, As1, Bs1, As0, Bs0, k + 1);
   }
-  if (k < nK) {          // odd number of steps: the last one is in stage 0
-    wait_vmem_all();
-    __builtin_amdgcn_s_barrier();
-    compute(As0, Bs0);
-  }
+  if (k < nK) step(As0, Bs0, As0, Bs0, As1, Bs1, k);   // odd number of steps
+  wait_vmem_all();
 
   // ---- epilogue ----
 #pragma unroll
