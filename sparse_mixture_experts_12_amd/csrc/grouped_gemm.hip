@@ -65,28 +65,48 @@ struct GemmParams {
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row ^ (row >> 3)) & 7); }
 
-// Decode a logical tile id into (group, row0, rows, n-tile).
-__device__ __forceinline__ bool decode_tile(const int32_t* sched, int maxQ, int n_tiles, int* g, int* row0, int* rows,
-                                            int* nt) {
-  const int Q = sched[0];
-  const int total = Q * n_tiles;
-  const int per = (total + 7) >> 3;
+// Map this work-group to (group, row0, rows, n-tile).  The schedule holds a
+// heavy segment (row tiles of more than BM / 2 rows) and a light segment; each
+// is split into 8 contiguous ranges of equal tile count, range x running on
+// XCD x (work-groups are dealt to the XCDs round-robin by id), heavy tiles
+// first.  Within the heavy segment a group's tiles are ordered column-major,
+// so neighbouring row tiles of one weight column tile share an XCD's L2.
+// Work-groups past both ranges return false.
+__device__ __forceinline__ bool decode_tile(const int32_t* sched, int maxQ, int E, int n_tiles, int* g, int* row0,
+                                            int* rows, int* nt) {
+  const int QH = sched[0], QL = sched[1];
+  const int totH = QH * n_tiles, totL = QL * n_tiles;
+  const int perH = (totH + 7) >> 3, perL = (totL + 7) >> 3;
   const int bid = blockIdx.x;
+  const int xcd = bid & 7;
   const int slot = bid >> 3;
-  const int logical = (bid & 7) * per + slot;
-  if (slot >= per || logical >= total) return false;
-  const int q0 = logical / n_tiles;
-  const int grp = sched[1 + 4 * q0 + 0];
-  const int first = sched[1 + 4 * q0 + 3];
-  const int mg = sched[1 + 4 * maxQ + grp];
-  const int local = logical - first * n_tiles;
-  const int j = local / mg;
-  const int i = local - j * mg;
-  const int q = first + i;
-  *g = grp;
-  *row0 = sched[1 + 4 * q + 1];
-  *rows = sched[1 + 4 * q + 2];
-  *nt = j;
+  const int32_t* hs = sched + kSchedHead;
+  if (slot < perH) {
+    const int logical = xcd * perH + slot;
+    if (logical >= totH) return false;
+    const int q0 = logical / n_tiles;
+    const int grp = hs[4 * q0 + 0];
+    const int first = hs[4 * q0 + 3];
+    const int mg = hs[4 * maxQ + grp];
+    const int local = logical - first * n_tiles;
+    const int j = local / mg;
+    const int q = first + (local - j * mg);
+    *g = grp;
+    *row0 = hs[4 * q + 1];
+    *rows = hs[4 * q + 2];
+    *nt = j;
+    return true;
+  }
+  const int s = slot - perH;
+  if (s >= perL) return false;
+  const int logical = xcd * perL + s;
+  if (logical >= totL) return false;
+  const int pt = logical / n_tiles;
+  const int32_t* ls = hs + 4 * maxQ + (E + 1) + 3 * pt;
+  *g = ls[0];
+  *row0 = ls[1];
+  *rows = ls[2];
+  *nt = logical - pt * n_tiles;
   return true;
 }
 
@@ -128,15 +148,16 @@ __device__ __forceinline__ bf16x8_t load_b_frag(const bf16_t* Bs, int kbase, int
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// Tile shapes (4 waves): BM = 256 -> waves 2x2, 128 rows x 128 B-rows each;
-// BM = 128 -> 2x2, 64 x 128; BM = 64 -> 1x4, 64 x 64.  The LDS B tile always
-// holds 256 "B rows" (output columns): 128 gate + 128 up columns for the
-// gate/up GEMM, 256 columns for the down GEMM.  PF = number of K steps whose
-// global loads are in flight ahead of the MFMAs (register stages).
+// Register-staged (fp8) tile shapes, 4 waves: BM = 256 -> waves 2x2, 128 rows
+// x 128 B-columns each; BM = 64 -> 1x4, 64 x 64.  The LDS B tile always holds
+// 256 B-columns: 128 gate + 128 up columns for the gate/up GEMM, 256 columns
+// for the down GEMM.  PF = number of K steps whose global loads are in flight
+// ahead of the MFMAs (register stages); OCC = work-groups per CU (also used by
+// the direct-to-LDS kernels).
 template <int BM> struct TileCfg {
-  static constexpr int WM = (BM >= 128) ? 2 : 1;
+  static constexpr int WM = (BM >= 256) ? 2 : 1;
   static constexpr int WN = 4 / WM;
-  static constexpr int PF = (BM <= 128) ? 2 : 1;
+  static constexpr int PF = (BM < 256) ? 2 : 1;
   static constexpr int OCC = (BM == 64) ? 2 : 1;    // work-groups per CU
 };
 
@@ -156,7 +177,7 @@ __global__ __launch_bounds__(256, TileCfg<BM>::OCC) void gemm_mfma_kernel(GemmPa
 
   const int n_tiles = (p.N + BN_MAT - 1) / BN_MAT;
   int g, row0, rows, nt;
-  if (!decode_tile(p.sched, p.maxQ, n_tiles, &g, &row0, &rows, &nt)) return;
+  if (!decode_tile(p.sched, p.maxQ, p.E, n_tiles, &g, &row0, &rows, &nt)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -411,34 +432,31 @@ __device__ __forceinline__ void sched_interleave() {
   }
 }
 
-template <bool DUAL, int BM, int BK, int NST>
-__global__ __launch_bounds__(256, TileCfg<BM>::OCC) void gemm_dl_kernel(GemmParams p) {
-  constexpr int WM = TileCfg<BM>::WM, WN = TileCfg<BM>::WN;
+// One output tile of at most BMV rows: waves 2 x 2 (128 rows x 128 B-columns
+// each) for BMV = 256, 1 x 4 (BMV rows x 64 B-columns each) for 128 and 64.
+// The LDS stages are sized for BMMAX rows.
+template <bool DUAL, int BMV, int BMMAX, int BK, int NST>
+__device__ __forceinline__ void dl_tile(const GemmParams& p, int g, int row0, int rows, int nt, bf16_t* L0,
+                                        bf16_t* L1, bf16_t* L2, bf16_t* L3) {
+  constexpr int WM = (BMV >= 256) ? 2 : 1, WN = 4 / WM;
   constexpr int NMAT = DUAL ? 2 : 1;
   constexpr int BN_MAT = DUAL ? 128 : 256;
   constexpr int NI_MAT = BN_MAT / WN / 32;
   constexpr int NI = NI_MAT * NMAT;
-  constexpr int MI = BM / WM / 32;
-  constexpr int WROWS = BM / WM;
+  constexpr int MI = BMV / WM / 32;
+  constexpr int WROWS = BMV / WM;
   constexpr int CPR = BK / 8;                      // 16-byte chunks per A row
   constexpr int A_RPB = 64 / CPR;                  // A rows per 1 KB block
-  constexpr int A_LD = BM / A_RPB / 4;             // 1 KB A blocks per wave per step
+  constexpr int A_LD = BMV / A_RPB / 4;            // 1 KB A blocks per wave per step
   constexpr int B_LD = BK / 2 / 4;                 // 1 KB B blocks (2 K-rows each) per wave per step
   constexpr int SUB = BK / 16;                     // 16-wide MFMA sub-steps per step
-  constexpr int LDS_A = BM * BK, LDS_S = LDS_A + 256 * BK;
+  constexpr int LDS_A = BMMAX * BK;                // B tile offset inside a stage
   constexpr int NMF = MI * NI;                     // MFMAs per sub-step
   constexpr int NDS = MI + 2 * NI;                 // LDS fragment reads per sub-step
   constexpr int NVM = A_LD + B_LD;                 // global->LDS loads per step
-  static_assert(SUB % 2 == 0 && NST >= 2 && NST <= 4 && A_LD >= 1 && B_LD % 2 == 0, "tile configuration");
+  static_assert(SUB % 2 == 0 && NST >= 2 && NST <= 4 && A_LD >= 1 && B_LD % 2 == 0 && BMV <= BMMAX,
+                "tile configuration");
   static_assert((NST - 1) * NVM < 64, "outstanding loads exceed the vmcnt range");
-  __shared__ __attribute__((aligned(1024))) bf16_t L0[LDS_S];
-  __shared__ __attribute__((aligned(1024))) bf16_t L1[LDS_S];
-  __shared__ __attribute__((aligned(1024))) bf16_t L2[NST > 2 ? LDS_S : 8];
-  __shared__ __attribute__((aligned(1024))) bf16_t L3[NST > 3 ? LDS_S : 8];
-
-  const int n_tiles = (p.N + BN_MAT - 1) / BN_MAT;
-  int g, row0, rows, nt;
-  if (!decode_tile(p.sched, p.maxQ, n_tiles, &g, &row0, &rows, &nt)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -616,6 +634,29 @@ __global__ __launch_bounds__(256, TileCfg<BM>::OCC) void gemm_dl_kernel(GemmPara
   }
 }
 
+
+template <bool DUAL, int BMMAX, int BK, int NST>
+__global__ __launch_bounds__(256, TileCfg<BMMAX>::OCC) void gemm_dl_kernel(GemmParams p) {
+  constexpr int LDS_S = BMMAX * BK + 256 * BK;
+  __shared__ __attribute__((aligned(1024))) bf16_t L0[LDS_S];
+  __shared__ __attribute__((aligned(1024))) bf16_t L1[LDS_S];
+  __shared__ __attribute__((aligned(1024))) bf16_t L2[NST > 2 ? LDS_S : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t L3[NST > 3 ? LDS_S : 8];
+  constexpr int BN_MAT = DUAL ? 128 : 256;
+  const int n_tiles = (p.N + BN_MAT - 1) / BN_MAT;
+  int g, row0, rows, nt;
+  if (!decode_tile(p.sched, p.maxQ, p.E, n_tiles, &g, &row0, &rows, &nt)) return;
+  // An expert's last row tile is usually partial: run it with a body whose
+  // MFMA work matches its rows (<= 64, <= 128) instead of the full height.
+  if constexpr (BMMAX >= 256) {
+    if (rows > 128) dl_tile<DUAL, 256, BMMAX, BK, NST>(p, g, row0, rows, nt, L0, L1, L2, L3);
+    else if (rows > 64) dl_tile<DUAL, 128, BMMAX, BK, NST>(p, g, row0, rows, nt, L0, L1, L2, L3);
+    else dl_tile<DUAL, 64, BMMAX, BK, NST>(p, g, row0, rows, nt, L0, L1, L2, L3);
+  } else {
+    dl_tile<DUAL, BMMAX, BMMAX, BK, NST>(p, g, row0, rows, nt, L0, L1, L2, L3);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 layer: SIMT grouped GEMM, 64 rows x 64 columns per tile, fp32 FMA.
 // ---------------------------------------------------------------------------
@@ -637,7 +678,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
   __shared__ float Bs[DUAL ? 2 : 1][BK][BN + 4];
   const int n_tiles = (p.N + BN - 1) / BN;
   int g, row0, rows, nt;
-  if (!decode_tile(p.sched, p.maxQ, n_tiles, &g, &row0, &rows, &nt)) return;
+  if (!decode_tile(p.sched, p.maxQ, p.E, n_tiles, &g, &row0, &rows, &nt)) return;
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
   const int n0 = nt * BN;
@@ -740,12 +781,13 @@ static int max_row_tiles(int T, int k, int E, int has_shared, int BM) {
 
 size_t grouped_sched_ints(int T, int k, int E, int has_shared) {
   // enough for the smallest tile height used (64 rows)
-  return 1 + 4 * (size_t)max_row_tiles(T, k, E, has_shared, 64) + (E + 1) + 16;
+  return kSchedHead + 4 * (size_t)max_row_tiles(T, k, E, has_shared, 64) + 4 * (size_t)(E + 1) + 16;
 }
 
+// Work-groups: per XCD, enough slots for both schedule segments.  With
+// QH + QL <= maxQ row tiles, ceil(QH n / 8) + ceil(QL n / 8) <= ceil(maxQ n / 8) + 2.
 static inline int grid_for(int maxQ, int n_tiles) {
-  long total = (long)maxQ * n_tiles;
-  long per = (total + 7) / 8;
+  const long per = ((long)maxQ * n_tiles + 7) / 8 + 2;
   return (int)(8 * per);
 }
 

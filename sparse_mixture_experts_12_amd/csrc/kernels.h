@@ -31,6 +31,8 @@ struct PermuteArgs {
   int32_t *counts, *offsets, *sorted_assign, *inv_perm, *n_dropped, *rank_ws;
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+// Tile schedule header size (ints): [0] heavy row tiles, [1] light row tiles.
+constexpr int kSchedHead = 4;
 hipError_t launch_tile_schedule(const int32_t* offsets, int E, int BM, int shared_rows, int shared_row0, int maxQ,
                                 int32_t* sched, hipStream_t s);
 

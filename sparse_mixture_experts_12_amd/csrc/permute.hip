@@ -134,13 +134,24 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 //   sched[1 + 4q .. 4q + 4]     tile q: group, row0, rows, first tile of group
 //   group g's row-tile count is stored in sched[1 + 4*maxQ + g]
 // ---------------------------------------------------------------------------
+// Row tiles of every group (expert, or the shared expert as group E), in two
+// segments: "heavy" tiles with more than BM / 2 rows (all full tiles and a
+// large last tile) and "light" tiles with at most BM / 2 rows (a group's
+// small last tile).  The GEMMs run light tiles with a cheaper body and spread
+// each segment evenly over the XCDs.  Layout (ints):
+//   [0] QH, [1] QL,
+//   heavy tile q:  [kSchedHead + 4 q + {0: group, 1: row0, 2: rows, 3: first heavy tile of the group}]
+//   heavy count g: [kSchedHead + 4 maxQ + g]
+//   light tile p:  [kSchedHead + 4 maxQ + maxG + 3 p + {0: group, 1: row0, 2: rows}]
 __global__ __launch_bounds__(kPermThreads) void tile_schedule_kernel(const int32_t* __restrict__ offsets, int E,
                                                                      int BM, int shared_rows, int shared_row0,
                                                                      int maxQ, int32_t* __restrict__ sched) {
-  __shared__ int scan[kPermThreads];
-  __shared__ int s_total;
+  __shared__ int scan_h[kPermThreads];
+  __shared__ int scan_l[kPermThreads];
+  __shared__ int s_qh, s_ql;
   const int tid = threadIdx.x;
   const int G = E + (shared_rows > 0 ? 1 : 0);
+  const int maxG = E + 1;
   int rows = 0, row0 = 0;
   if (tid < E) {
     row0 = offsets[tid];
@@ -149,22 +160,36 @@ __global__ __launch_bounds__(kPermThreads) void tile_schedule_kernel(const int32
     row0 = shared_row0;
     rows = shared_rows;
   }
-  const int ntile = (rows + BM - 1) / BM;
-  scan[tid] = ntile;
+  const int full = rows / BM, rem = rows - full * BM;
+  const int nh = full + (rem > BM / 2 ? 1 : 0);
+  const int nl = (rem > 0 && rem <= BM / 2) ? 1 : 0;
+  scan_h[tid] = nh;
+  scan_l[tid] = nl;
   __syncthreads();
-  block_exclusive_scan_1024(scan, G, &s_total);
+  block_exclusive_scan_1024(scan_h, G, &s_qh);
+  block_exclusive_scan_1024(scan_l, G, &s_ql);
   if (tid < G) {
-    const int first = scan[tid];
-    sched[1 + 4 * maxQ + tid] = ntile;
-    for (int i = 0; i < ntile; ++i) {
-      int q = first + i;
-      sched[1 + 4 * q + 0] = tid;
-      sched[1 + 4 * q + 1] = row0 + i * BM;
-      sched[1 + 4 * q + 2] = min(BM, rows - i * BM);
-      sched[1 + 4 * q + 3] = first;
+    const int first = scan_h[tid];
+    int32_t* hs = sched + kSchedHead;
+    hs[4 * maxQ + tid] = nh;
+    for (int i = 0; i < nh; ++i) {
+      const int q = first + i;
+      hs[4 * q + 0] = tid;
+      hs[4 * q + 1] = row0 + i * BM;
+      hs[4 * q + 2] = min(BM, rows - i * BM);
+      hs[4 * q + 3] = first;
+    }
+    if (nl) {
+      int32_t* ls = hs + 4 * maxQ + maxG + 3 * scan_l[tid];
+      ls[0] = tid;
+      ls[1] = row0 + full * BM;
+      ls[2] = rem;
     }
   }
-  if (tid == 0) sched[0] = s_total;
+  if (tid == 0) {
+    sched[0] = s_qh;
+    sched[1] = s_ql;
+  }
 }
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {

@@ -36,6 +36,9 @@ SMALL = {
     "bf16_one_expert": C["mixtral_prefill"].with_(T=50, d=256, f=256, E=1, k=1, seed=7),
     "bf16_top1_switch": C["mixtral_prefill"].with_(T=90, d=256, f=256, E=16, k=1, capacity_factor=1.0),
     "bf16_big_tiles": C["mixtral_prefill"].with_(T=600, d=256, f=512, E=4, k=2, seed=8),
+    # 256-row tiles whose last tiles hold 108..139 rows: the 128- and 256-row bodies
+    "bf16_big_tiles_mid": C["mixtral_prefill"].with_(T=760, d=256, f=512, E=4, k=2, seed=3),
+    "bf16_big_tiles_shared": C["fine_grained"].with_(T=700, d=256, E=4, k=2, f=256, seed=10),
     "fp8_big_tiles_shared": C["fp8_capacity"].with_(T=700, d=256, E=4, k=2, f=256, capacity_factor=0.0,
                                                      shared=True, seed=9),
     "decode_T1": C["mixtral_decode"].with_(d=512, f=1024),
@@ -178,7 +181,8 @@ def test_permute_all_to_one_expert_with_capacity():
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("name", ["tiny_f32", "tiny_f32_ragged", "bf16_prefill", "bf16_prefill_ragged",
                                   "bf16_finegrained_shared", "fp8_capacity", "fp8_capacity_tight",
-                                  "bf16_one_expert", "bf16_big_tiles", "fp8_big_tiles_shared"])
+                                  "bf16_one_expert", "bf16_big_tiles", "bf16_big_tiles_mid",
+                                  "bf16_big_tiles_shared", "fp8_big_tiles_shared"])
 def test_grouped_ffn_parity(name):
     cfg = SMALL[name]
     print(f"[grouped_ffn] {name}", flush=True)
