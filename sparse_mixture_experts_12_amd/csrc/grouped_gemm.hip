@@ -766,9 +766,12 @@ constexpr int kDlNST = 2;
 
 static int pick_bm(const GroupedArgs& a) {
   if (a.act_f32) return 64;
+  // bf16 weights: 256-row tiles, whose small last tiles run 64/128-row bodies.
+  // Measured on MI355X, this also wins for skewed fine-grained loads (256
+  // experts of 0..1507 rows): fewer row tiles re-read each expert's weights.
+  if (a.wkind == W_BF16) return 256;
+  // fp8 weights (register-staged kernel): 64-row tiles unless experts are large
   const int avg = (a.T * a.k) / (a.E > 0 ? a.E : 1);
-  // measured on MI355X: 256-row tiles win for ~1000 rows per expert (Mixtral
-  // prefill), 64-row tiles for tens of rows per expert (fine-grained, fp8)
   return avg >= 256 ? 256 : 64;
 }
 
