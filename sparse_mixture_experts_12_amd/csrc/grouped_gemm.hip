@@ -457,6 +457,10 @@ __device__ __forceinline__ void dl_tile(const GemmParams& p, int g, int row0, in
   static_assert(SUB % 2 == 0 && NST >= 2 && NST <= 4 && A_LD >= 1 && B_LD % 2 == 0 && BMV <= BMMAX,
                 "tile configuration");
   static_assert((NST - 1) * NVM < 64, "outstanding loads exceed the vmcnt range");
+  // A light tile (<= 128 rows) is an expert's only row tile for its weight
+  // columns, so its weight loads are streamed with the non-temporal policy;
+  // full-height tiles keep the default so sibling row tiles hit in L2.
+  constexpr int kBPolicy = (BMV <= 128) ? 2 : 0;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -511,7 +515,7 @@ __device__ __forceinline__ void dl_tile(const GemmParams& p, int g, int row0, in
 #pragma unroll
     for (int j = 0; j < B_LD; ++j)
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(bsrc[j & 1] + kb + (size_t)(2 * (j & ~1)) * brow),
-                                       (lds_ptr_t)(L + LDS_A + (B_LD * wave + j) * 512), 16, 0, 0);
+                                       (lds_ptr_t)(L + LDS_A + (B_LD * wave + j) * 512), 16, 0, kBPolicy);
   };
 
   f32x16_t acc[MI][NI];
@@ -854,8 +858,7 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
     if (BM == 256) launch_gu(gemm_mfma_kernel<W_FP8, true, 256>);
     else launch_gu(gemm_mfma_kernel<W_FP8, true, 64>);
   } else {
-    if (BM == 256) launch_gu(gemm_dl_kernel<true, 256, kDlBK, kDlNST>);
-    else launch_gu(gemm_dl_kernel<true, 64, kDlBK, kDlNST>);
+    launch_gu(gemm_dl_kernel<true, 256, kDlBK, kDlNST>);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
@@ -870,8 +873,7 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
     if (BM == 256) gemm_mfma_kernel<W_FP8, false, 256><<<dn_grid, 256, 0, s>>>(q);
     else gemm_mfma_kernel<W_FP8, false, 64><<<dn_grid, 256, 0, s>>>(q);
   } else {
-    if (BM == 256) gemm_dl_kernel<false, 256, kDlBK, kDlNST><<<dn_grid, 256, 0, s>>>(q);
-    else gemm_dl_kernel<false, 64, kDlBK, kDlNST><<<dn_grid, 256, 0, s>>>(q);
+    gemm_dl_kernel<false, 256, kDlBK, kDlNST><<<dn_grid, 256, 0, s>>>(q);
   }
   return hipGetLastError();
 }
