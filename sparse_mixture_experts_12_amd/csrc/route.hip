@@ -18,152 +18,104 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // Large-T router logits as fp64 partial sums over slices of the hidden
 // dimension (split-K), finished by the top-k kernel, which adds the slices in
-// a fixed order.  Loads are branch-free (clamped addresses, zero
-// contributions) so each thread's loads are in flight together.
+// a fixed order:
 //   part[z][t][e] = sum over rows r of slice z of x[t, r] * W_g[r, e]   (fp64)
 // ---------------------------------------------------------------------------
-template <typename TIn>
-__device__ __forceinline__ double ld_or_zero(const TIn* __restrict__ p, size_t i, bool ok) {
-  const TIn v = p[ok ? i : 0];
-  return ok ? (double)ActTraits<TIn>::load(&v, 0) : 0.0;
-}
-
-// Few experts (E <= EP <= 32): 16 tokens per work-group; the work-group's
-// W_g slice (dsplit rows x EP) is staged once in LDS as fp32 (exact for
-// bf16); the slice rows are split over 16 thread groups whose fp64 sums are
-// added in a fixed order.
-template <typename TIn, int EP>
-__global__ __launch_bounds__(256) void router_partial_small_e(const TIn* __restrict__ x, const TIn* __restrict__ W,
-                                                              double* __restrict__ part, int T, int d, int E,
-                                                              int dsplit) {
-  constexpr int BT = 16, DS = 16;
-  constexpr int MAXR = 8192 / EP;                       // staged rows (32 KB of fp32)
-  constexpr int RPT = MAXR / DS;                        // rows per thread
-  __shared__ float wch[MAXR][EP];
-  __shared__ double red[DS][BT][EP + 1];
-  const int tid = threadIdx.x;
-  const int tt = tid & (BT - 1), ds = tid >> 4;
-  const int t = blockIdx.x * BT + tt;
-  const int tc = min(t, T - 1);
-  const int z = blockIdx.y;
+// ---------------------------------------------------------------------------
+// Partial logits on the fp64 matrix cores (v_mfma_f64_16x16x4f64).  The
+// products of bf16 or fp32 inputs are exact in fp64, so these partial sums
+// differ from a sequential fp64 sum only in the order of the additions.
+// Operand layout (checked on gfx950): A lane l = A[l % 16][l / 16],
+// B lane l = B[l / 16][l % 16], result lane l, register v = D[l / 16 + 4 v][l % 16].
+// Work-group tile BT tokens x BE experts (64 x 64, or 256 x 16 for few
+// experts), K step 16, operands staged in LDS as fp32 (exact) with padded
+// rows so that the 4 K-rows read by one fragment load fall in distinct banks.
+// ---------------------------------------------------------------------------
+template <typename TIn, int BE>
+__global__ __launch_bounds__(256) void router_partial_mfma(const TIn* __restrict__ x, const TIn* __restrict__ W,
+                                                           double* __restrict__ part, int T, int d, int E,
+                                                           int dsplit) {
+  typedef double f64x4_t __attribute__((ext_vector_type(4)));
+  constexpr int BT = (BE == 64) ? 64 : 256;
+  constexpr int WM = (BE == 64) ? 2 : 4, WN = 4 / WM;   // wave grid
+  constexpr int MT = BT / WM / 16, NT = BE / WN / 16;    // 16 x 16 MFMA tiles per wave
+  constexpr int BK = 16;
+  constexpr int XP = BT + 16, WP = BE + 16;
+  constexpr int XE = BT * BK / 256;                      // x elements per thread per step (4 or 16)
+  constexpr int TPT = BK / XE;                           // threads per token row
+  constexpr int WE = BE * BK / 256;                      // W elements per thread per step (4 or 1)
+  __shared__ float xs[2][BK][XP];
+  __shared__ float ws[2][BK][WP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int t0 = blockIdx.x * BT, e0 = blockIdx.y * BE, z = blockIdx.z;
   const int r_begin = z * dsplit;
-  const int rows = min(dsplit, d - r_begin);
-  for (int i = tid; i < MAXR * EP; i += 256) {
-    const int r = i / EP, e = i % EP;
-    const bool ok = (r < rows) && (e < E);
-    wch[r][e] = (float)ld_or_zero(W, (size_t)(r_begin + r) * E + e, ok);
-  }
-  // this thread's rows: RPT consecutive rows of token tc (branch-free loads)
-  float xv[RPT];
-  const int r0 = ds * RPT;
-#pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int r = r0 + i;
-    xv[i] = (float)ld_or_zero(x, (size_t)tc * d + r_begin + r, r < rows);
-  }
-  __syncthreads();
-  double acc[EP];
-#pragma unroll
-  for (int j = 0; j < EP; ++j) acc[j] = 0.0;
-#pragma unroll 4
-  for (int i = 0; i < RPT; ++i) {
-    const double xd = (double)xv[i];
-#pragma unroll
-    for (int j = 0; j < EP; ++j) acc[j] = __fma_rn(xd, (double)wch[r0 + i][j], acc[j]);
-  }
-#pragma unroll
-  for (int j = 0; j < EP; ++j) red[ds][tt][j] = acc[j];
-  __syncthreads();
-  for (int i = tid; i < BT * EP; i += 256) {
-    const int ti = i / EP, e = i % EP;
-    const int tok = blockIdx.x * BT + ti;
-    if (tok < T && e < E) {
-      double sum = 0.0;
-#pragma unroll
-      for (int g = 0; g < DS; ++g) sum += red[g][ti][e];
-      part[((size_t)z * T + tok) * E + e] = sum;
-    }
-  }
-}
-
-// Many experts: 32 tokens x 64 experts per work-group, K step 32, LDS double
-// buffer with the next step's global loads issued before the current step's
-// FMAs.  Thread (ty, tx) owns tokens ty + 16 i (i < 2) and experts tx + 16 j
-// (j < 4), so LDS reads of one wave hit consecutive doubles.
-template <typename TIn>
-__global__ __launch_bounds__(256) void router_partial_tiled(const TIn* __restrict__ x, const TIn* __restrict__ W,
-                                                            double* __restrict__ part, int T, int d, int E,
-                                                            int dsplit) {
-  constexpr int BT = 32, BE = 64, BK = 32;
-  __shared__ double xs[2][BK][BT + 1];
-  __shared__ double ws[2][BK][BE + 1];
-  const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
-  const int t0 = blockIdx.x * BT, e0 = blockIdx.y * BE;
-  const int z = blockIdx.z;
-  const int r_begin = z * dsplit;
-  const int r_end = min(d, r_begin + dsplit);
-  // staging roles: x tile 32 tokens x 32 k (4 per thread), W tile 32 k x 64 experts (8 per thread)
-  const int xr = tid >> 3, xk = (tid & 7) * 4;
-  const int wk = tid >> 3, we = (tid & 7) * 8;
-  const int xt = min(t0 + xr, T - 1);
-  const bool xt_ok = (t0 + xr) < T;
-  double xreg[4], wreg[8];
+  const int r_end = min(d, r_begin + dsplit);            // r_end - r_begin is a multiple of BK
+  const int xt_l = tid / TPT, xk_l = (tid % TPT) * XE;
+  const bool xt_ok = t0 + xt_l < T;
+  const TIn* xrow = x + (size_t)(xt_ok ? t0 + xt_l : T - 1) * d + xk_l;
+  const int wk_l = tid / (BE / WE), we_l = (tid % (BE / WE)) * WE;
+  float xr[XE], wr[WE];
+  // loads of the step at k0 (always a valid step; rows past T and experts past
+  // E read clamped addresses and are zeroed)
   auto load = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = k0 + xk + i;
-      xreg[i] = ld_or_zero(x, (size_t)xt * d + k, xt_ok && k < r_end);
+    for (int i = 0; i < XE; ++i) {
+      const float v = ActTraits<TIn>::load(xrow, k0 + i);
+      xr[i] = xt_ok ? v : 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int k = k0 + wk, e = e0 + we + j;
-      wreg[j] = ld_or_zero(W, (size_t)k * E + e, k < r_end && e < E);
+    for (int j = 0; j < WE; ++j) {
+      const int e = e0 + we_l + j;
+      const float v = ActTraits<TIn>::load(W, (size_t)(k0 + wk_l) * E + (e < E ? e : 0));
+      wr[j] = e < E ? v : 0.f;
     }
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xs[buf][xk + i][xr] = xreg[i];
+    for (int i = 0; i < XE; ++i) xs[buf][xk_l + i][xt_l] = xr[i];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ws[buf][wk][we + j] = wreg[j];
+    for (int j = 0; j < WE; ++j) ws[buf][wk_l][we_l + j] = wr[j];
   };
-  double acc[2][4];
+  f64x4_t acc[MT][NT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+    for (int j = 0; j < NT; ++j) acc[i][j] = (f64x4_t){0.0, 0.0, 0.0, 0.0};
+  const int fr = lane & 15, fk = lane >> 4;
   load(r_begin);
   store(0);
   __syncthreads();
   int buf = 0;
   for (int k0 = r_begin; k0 < r_end; k0 += BK) {
-    const bool more = k0 + BK < r_end;
-    if (more) load(k0 + BK);
-#pragma unroll 8
-    for (int kk = 0; kk < BK; ++kk) {
-      double a[2], b[4];
+    const int kn = (k0 + BK < r_end) ? k0 + BK : k0;      // last step reloads itself (unused)
+    load(kn);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = xs[buf][kk][ty + 16 * i];
+    for (int ks = 0; ks < BK / 4; ++ks) {
+      double a[MT], b[NT];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = ws[buf][kk][tx + 16 * j];
+      for (int i = 0; i < MT; ++i) a[i] = (double)xs[buf][ks * 4 + fk][wm * (BT / WM) + i * 16 + fr];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < NT; ++j) b[j] = (double)ws[buf][ks * 4 + fk][wn * (BE / WN) + j * 16 + fr];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __fma_rn(a[i], b[j], acc[i][j]);
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (more) store(buf ^ 1);
+    store(buf ^ 1);
     __syncthreads();
     buf ^= 1;
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int t = t0 + ty + 16 * i;
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx + 16 * j;
-      if (t < T && e < E) part[((size_t)z * T + t) * E + e] = acc[i][j];
-    }
-  }
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = t0 + wm * (BT / WM) + i * 16 + fk + 4 * v;
+        const int e = e0 + wn * (BE / WN) + j * 16 + fr;
+        if (t < T && e < E) part[((size_t)z * T + t) * E + e] = acc[i][j][v];
+      }
 }
 
 // ---------------------------------------------------------------------------
@@ -516,18 +468,16 @@ __global__ __launch_bounds__(256) void topk_finalize_kernel(const double* __rest
 // Split of the hidden dimension for the large-T router: the few-expert kernel
 // stages at most 8192/EP rows of W_g per work-group; the many-expert kernel
 // splits until about 512 work-groups are in flight (at least 256 rows each).
+// K split of the partial-logit kernel: enough work-groups (>= 512) to fill
+// the chip, each K range a multiple of 16 and at least 64 long.
 static void router_split(int T, int d, int E, int* S, int* dsplit) {
-  if (E <= 32) {
-    const int ep = E <= 8 ? 8 : E <= 16 ? 16 : 32;
-    *dsplit = 8192 / ep;
-  } else {
-    const long nblk = (long)((T + 31) / 32) * ((E + 63) / 64);
-    int s = (int)((512 + nblk - 1) / nblk);
-    const int smax = d / 256 > 0 ? d / 256 : 1;
-    s = s < 1 ? 1 : (s > smax ? smax : s);
-    int ds = (d + s - 1) / s;
-    *dsplit = (ds + 31) / 32 * 32;
-  }
+  const int bt = E <= 16 ? 256 : 64, be = E <= 16 ? 16 : 64;
+  const long nblk = (long)((T + bt - 1) / bt) * ((E + be - 1) / be);
+  long s = (512 + nblk - 1) / nblk;
+  const long smax = d / 64;
+  s = s < 1 ? 1 : (s > smax ? smax : s);
+  const int ds = (int)((d + s - 1) / s);
+  *dsplit = (ds + 15) / 16 * 16;
   *S = (d + *dsplit - 1) / *dsplit;
 }
 
@@ -543,15 +493,10 @@ static hipError_t launch_partials(const void* x, const void* W, double* part, in
                                   hipStream_t s) {
   const TIn* xp = (const TIn*)x;
   const TIn* wp = (const TIn*)W;
-  if (E <= 8) {
-    router_partial_small_e<TIn, 8><<<dim3((T + 15) / 16, S), 256, 0, s>>>(xp, wp, part, T, d, E, ds);
-  } else if (E <= 16) {
-    router_partial_small_e<TIn, 16><<<dim3((T + 15) / 16, S), 256, 0, s>>>(xp, wp, part, T, d, E, ds);
-  } else if (E <= 32) {
-    router_partial_small_e<TIn, 32><<<dim3((T + 15) / 16, S), 256, 0, s>>>(xp, wp, part, T, d, E, ds);
-  } else {
-    router_partial_tiled<TIn><<<dim3((T + 31) / 32, (E + 63) / 64, S), 256, 0, s>>>(xp, wp, part, T, d, E, ds);
-  }
+  if (E <= 16)
+    router_partial_mfma<TIn, 16><<<dim3((T + 255) / 256, (E + 15) / 16, S), 256, 0, s>>>(xp, wp, part, T, d, E, ds);
+  else
+    router_partial_mfma<TIn, 64><<<dim3((T + 63) / 64, (E + 63) / 64, S), 256, 0, s>>>(xp, wp, part, T, d, E, ds);
   return hipGetLastError();
 }
 
