@@ -158,7 +158,8 @@ def main():
     cfg = synth.CONFIGS[args.workload]
     decode = cfg.T <= 8 and cfg.act == "bf16"
     steps = args.steps if args.steps is not None else (200 if decode else 20)
-    warmup = args.warmup if args.warmup is not None else (10 if decode else 3)
+    # a few ms of warm-up lets the clocks settle before the timed region
+    warmup = args.warmup if args.warmup is not None else 10
     print(f"[bench] workload={cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} f={cfg.f} "
           f"act={cfg.act} w={cfg.wdt} steps={steps} warmup={warmup}", file=sys.stderr, flush=True)
 
@@ -234,16 +235,34 @@ def main():
                 "kernel": "decode_ffn_kernel", "kernel_ms": round(kern_ms, 5) if have_k else None,
                 "alg_bytes": int(kbytes)}
     else:
-        # dominant kernel = grouped gate/up GEMM + SwiGLU: 2/3 of the expert flops
+        # dominant kernel = grouped gate/up GEMM + SwiGLU: 2/3 of the expert flops.
+        # Its bound is whichever roofline its arithmetic intensity hits first:
+        # MFMA for Mixtral-sized experts, HBM for fine-grained and fp8 layers.
+        f32 = cfg.act == "f32"
         rows = int(cnt.sum()) + (cfg.T if cfg.shared else 0)
         kflops = 4 * rows * cfg.d * cfg.f
-        achieved = kflops / (kern_ms / 1e3) / 1e12 if have_k else None
-        peak = FP32_PEAK_TFLOPS if cfg.act == "f32" else BF16_PEAK_TFLOPS
-        roof = {"bound": "mfma", "achieved": round(achieved, 2) if have_k else None, "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4) if have_k else None,
+        n_exp = touched + (1 if cfg.shared else 0)
+        es = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.wdt]
+        scales = 2 * cfg.f * 4 if cfg.wdt == "fp8" else 0
+        ae = 4 if f32 else 2
+        kbytes = n_exp * (2 * cfg.d * cfg.f * es + scales) + cfg.T * cfg.d * ae + rows * cfg.f * ae
+        peak_f = FP32_PEAK_TFLOPS if f32 else BF16_PEAK_TFLOPS
+        ridge = peak_f * 1e12 / (HBM_PEAK_GBS * 1e9)
+        kname = "gemm_f32_kernel" if f32 else ("gemm_mfma_kernel" if cfg.wdt == "fp8" else "gemm_dl_kernel")
+        t = kern_ms / 1e3 if have_k else None
+        if kflops / kbytes >= ridge:
+            bound, peak, unit = "mfma", peak_f, "TFLOP/s"
+            achieved = kflops / t / 1e12 if have_k else None
+        else:
+            bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
+            achieved = kbytes / t / 1e9 if have_k else None
+        roof = {"bound": bound, "achieved": round(achieved, 2) if have_k else None, "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4) if have_k else None,
                 "traffic": measured_traffic("gemm_gateup", cfg.name),
-                "kernel": "gemm_mfma_kernel<gate/up>" if cfg.act != "f32" else "gemm_f32_kernel<gate/up>",
-                "kernel_ms": round(kern_ms, 5) if have_k else None, "alg_flops": int(kflops)}
+                "kernel": f"{kname}<gate/up>", "kernel_ms": round(kern_ms, 5) if have_k else None,
+                "alg_flops": int(kflops), "alg_bytes": int(kbytes),
+                "mfma_frac": round(kflops / t / 1e12 / peak_f, 4) if have_k else None,
+                "hbm_frac": round(kbytes / t / 1e9 / HBM_PEAK_GBS, 4) if have_k else None}
 
     if args.copy_calibration:
         # a plain elementwise kernel of known traffic (256 MiB read, 256 MiB
