@@ -5,6 +5,6 @@ package.  The product library never does.
 """
 from .moe_oracle import (  # noqa: F401
     capacity, dequantize, expert_ffn, forward, fp8_e4m3fn_decode, permute,
-    router_logits, routing_certificate, routing_weights, silu, softmax_rows,
-    topk_select,
+    router_logits, router_telemetry, routing_certificate, routing_weights, silu,
+    softmax_rows, topk_select,
 )

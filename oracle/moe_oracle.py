@@ -264,3 +264,35 @@ def routing_certificate(x, W_g, bias, k: int) -> dict:
             if not gap > need:
                 ok[t] = False
     return dict(ok=ok, margin=margin)
+
+
+# ----------------------------------------------------------------------------
+# Router telemetry: per-expert load and the Switch load-balancing loss
+# ([SWT] "Load Balancing Loss"; [DSK] "Auxiliary-Loss-Free Load Balancing").
+# ----------------------------------------------------------------------------
+def router_telemetry(logits32, idx, E: int) -> dict:
+    """Load statistics of one routing, from the fp32 logits and the chosen
+    experts (before any capacity limit).
+
+      routed[e]    number of (token, slot) assignments that chose expert e
+      prob_mean[e] mean over the tokens of expert e's full softmax probability
+      lb_loss      E * sum_e prob_mean[e] * routed[e] / T
+
+    [SWT] defines the loss as E times the sum over experts of the product of
+    the mean router probability and the fraction of tokens routed to the
+    expert, with the fraction taken as the token-mean of the one-hot of the
+    chosen index.  For k slots per token the same one-hot mean, summed over
+    the slots, is routed[e] / T, which is the reading used here.  [DSK] steers
+    load with a per-expert bias instead of a loss; the pages give no update
+    rule, so only its input, the per-expert load, is reported."""
+    probs = softmax_rows(logits32)
+    T = probs.shape[0]
+    routed = np.zeros(E, dtype=np.int64)
+    for t in range(T):
+        for e in idx[t]:
+            routed[int(e)] += 1
+    if T == 0:
+        return {"routed": routed, "prob_mean": np.zeros(E), "lb_loss": 0.0}
+    prob_mean = np.array([math.fsum(probs[:, e]) / T for e in range(E)])
+    lb_loss = E * math.fsum(prob_mean[e] * routed[e] / T for e in range(E))
+    return {"routed": routed, "prob_mean": prob_mean, "lb_loss": lb_loss}

@@ -359,3 +359,67 @@ def test_workload_shapes_match_pages(golden_dir):
         c = synth.CONFIGS[name]
         assert (c.d, c.f, c.E, c.k) == (rows["hidden_size"][0], rows["intermediate_size"][0],
                                         rows["num_local_experts"][0], rows["num_experts_per_tok"][0])
+
+
+# ----------------------------------------------------------------------------
+# Router telemetry ([SWT] "Load Balancing Loss")
+# ----------------------------------------------------------------------------
+def test_router_telemetry_closed_forms():
+    T, E, k = 12, 6, 2
+    # equal logits: every probability is 1/E and ties pick experts 0..k-1 for
+    # every token, so routed = [T, T, 0, ...] and the loss is E * k * (1/E) = k
+    l = np.zeros((T, E), dtype=np.float32)
+    idx = oracle.topk_select(oracle.softmax_rows(l), k)
+    r = oracle.router_telemetry(l, idx, E)
+    assert r["routed"].tolist() == [T, T, 0, 0, 0, 0]
+    np.testing.assert_allclose(r["prob_mean"], 1.0 / E, rtol=1e-15)
+    assert r["lb_loss"] == pytest.approx(k, rel=1e-14)
+    # balanced routing with uniform probabilities: loss = E * sum (1/E)(k/E) = k
+    bal = np.array([[(2 * t) % E, (2 * t + 1) % E] for t in range(T)], dtype=np.int32)
+    rb = oracle.router_telemetry(l, bal, E)
+    assert rb["routed"].tolist() == [T * k // E] * E
+    assert rb["lb_loss"] == pytest.approx(k, rel=1e-14)
+    # all probability on expert 0 and top-1 routing there: loss -> E
+    lc = np.full((T, E), -60.0, dtype=np.float32)
+    lc[:, 0] = 0.0
+    rc = oracle.router_telemetry(lc, np.zeros((T, 1), dtype=np.int32), E)
+    assert rc["routed"].tolist() == [T] + [0] * (E - 1)
+    assert rc["lb_loss"] == pytest.approx(E, rel=1e-20 + 1e-12)
+
+
+def test_router_telemetry_worked_example():
+    # two experts, logits 0 and ln 3: softmax [1/4, 3/4]
+    ln3 = np.float32(math.log(3.0))
+    # tokens with mirrored logits, top-1: P = [1/2, 1/2], one token each -> loss 2 (1/4 + 1/4) = 1
+    l = np.array([[0.0, ln3], [ln3, 0.0]], dtype=np.float32)
+    r = oracle.router_telemetry(l, np.array([[1], [0]], dtype=np.int32), 2)
+    np.testing.assert_allclose(r["prob_mean"], [0.5, 0.5], rtol=1e-7)
+    assert r["lb_loss"] == pytest.approx(1.0, rel=1e-7)
+    # both tokens [0, ln 3], both routed to expert 1: P = [1/4, 3/4], f = [0, 1] -> loss 2 * 3/4 = 1.5
+    # (the renormalised top-1 weight would give P = [0, 1] and loss 2)
+    l2 = np.array([[0.0, ln3], [0.0, ln3]], dtype=np.float32)
+    r2 = oracle.router_telemetry(l2, np.array([[1], [1]], dtype=np.int32), 2)
+    np.testing.assert_allclose(r2["prob_mean"], [0.25, 0.75], rtol=1e-7)
+    assert r2["routed"].tolist() == [0, 2]
+    assert r2["lb_loss"] == pytest.approx(1.5, rel=1e-7)
+
+
+def test_router_telemetry_invariants():
+    rng = np.random.default_rng(21)
+    T, E, k = 37, 9, 3
+    l = rng.normal(size=(T, E)).astype(np.float32)
+    idx = oracle.topk_select(oracle.softmax_rows(l), k)
+    r = oracle.router_telemetry(l, idx, E)
+    assert math.fsum(r["prob_mean"]) == pytest.approx(1.0, rel=1e-14)
+    assert r["routed"].sum() == T * k
+    np.testing.assert_array_equal(r["routed"], np.bincount(idx.ravel(), minlength=E))
+    # relabelling the experts permutes the per-expert outputs and keeps the loss
+    pi = rng.permutation(E)
+    inv = np.argsort(pi)
+    rp = oracle.router_telemetry(l[:, pi], inv[idx].astype(np.int32), E)
+    np.testing.assert_array_equal(rp["routed"], r["routed"][pi])
+    np.testing.assert_allclose(rp["prob_mean"], r["prob_mean"][pi], rtol=1e-14)
+    assert rp["lb_loss"] == pytest.approx(r["lb_loss"], rel=1e-14)
+    # empty batch
+    r0 = oracle.router_telemetry(np.zeros((0, E), dtype=np.float32), np.zeros((0, k), dtype=np.int32), E)
+    assert r0["routed"].sum() == 0 and r0["lb_loss"] == 0.0
