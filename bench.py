@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="skip the second timed region (per-launch events on the dominant kernel)")
+    ap.add_argument("--telemetry", action="store_true",
+                    help="also request the router telemetry outputs (routed load, mean probability, "
+                         "load-balancing loss) inside the timed region")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (for HBM counter scaling)")
     return ap.parse_args()
@@ -205,6 +208,12 @@ def main():
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     plain = ops.Stats()
+    if args.telemetry:
+        tel_routed = torch.zeros(cfg.E, dtype=torch.int32, device="cuda")
+        tel_pm = torch.zeros(cfg.E, dtype=torch.float32, device="cuda")
+        tel_loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+        plain = ops.Stats(d_routed=tel_routed.data_ptr(), d_prob_mean=tel_pm.data_ptr(),
+                          d_lb_loss=tel_loss.data_ptr())
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(steps):
@@ -214,6 +223,10 @@ def main():
     total_ms = t0.elapsed_time(t1)
     ms_per_step = total_ms / steps
     tokens_per_s = cfg.T * steps / (total_ms / 1e3)
+    if args.telemetry:
+        print(f"[bench] telemetry: load-balancing loss {float(tel_loss.cpu()[0]):.6f}, "
+              f"max routed load {int(tel_routed.max())}, idle experts {int((tel_routed == 0).sum())}",
+              file=sys.stderr, flush=True)
     kern_ms = float("nan")
     if not args.no_kernel_events:
         stats = [ops.Stats(ev_begin=ev_b[i].value, ev_end=ev_e[i].value) for i in range(steps)]
@@ -287,7 +300,7 @@ def main():
                    "act": cfg.act, "weights": cfg.wdt, "shared_expert": cfg.shared,
                    "capacity_factor": cfg.capacity_factor, "path": "fused_decode" if path == 2 else "grouped",
                    "experts_touched": touched, "dropped_share": n_dropped / max(1, cfg.T * cfg.k),
-                   "weight_copies": n_copies},
+                   "weight_copies": n_copies, "telemetry": bool(args.telemetry)},
         "layer": {"alg_bytes": int(bytes_total), "alg_flops": int(flops),
                   "hbm_GBps": round(bytes_total / (ms_per_step / 1e3) / 1e9, 1),
                   "tflops": round(flops / (ms_per_step / 1e3) / 1e12, 3)},

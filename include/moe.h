@@ -104,12 +104,28 @@ typedef struct {
   const float* ss_down;
 } moe_weights;
 
+/* Optional outputs of moe_forward.  The router telemetry fields follow
+ * "MoE Model Architectures", Switch Transformers "Load Balancing Loss" (E times
+ * the sum over experts of the mean router probability times the fraction of
+ * tokens routed there) and DeepSeek-V3 "Auxiliary-Loss-Free Load Balancing"
+ * (the per-expert load a router bias steers).  With k slots per token the
+ * fraction for expert e is d_routed[e] / T.  Requesting any telemetry field
+ * adds one small launch (T <= 64) or three; the router logits they read live
+ * in the workspace.  All fields are computed with fixed summation orders
+ * (bitwise reproducible).
+ * Nothing is written when T == 0. */
 typedef struct {
   int32_t path_taken;        /* out: MOE_PATH_GROUPED or MOE_PATH_FUSED_DECODE    */
   int32_t* d_n_dropped;      /* device [1] or NULL: dropped assignments           */
   int32_t* d_counts;         /* device [E] or NULL: kept assignments per expert   */
   hipEvent_t ev_begin;       /* NULL or an event recorded on `stream` just before */
   hipEvent_t ev_end;         /* ... and just after the dominant expert-FFN kernel */
+  int32_t* d_routed;         /* device [E] or NULL: assignments choosing each
+                                expert, before any capacity limit                 */
+  float* d_prob_mean;        /* device [E] or NULL: mean over tokens of the full
+                                softmax probability (fp64 sums, fp32 result)      */
+  float* d_lb_loss;          /* device [1] or NULL: E * sum_e prob_mean[e] *
+                                routed[e] / T                                     */
 } moe_stats;
 
 /* Bytes of workspace every entry point below needs for `desc` (the maximum

@@ -40,7 +40,8 @@ class Weights(ctypes.Structure):
 
 class Stats(ctypes.Structure):
     _fields_ = [("path_taken", ctypes.c_int32), ("d_n_dropped", ctypes.c_void_p),
-                ("d_counts", ctypes.c_void_p), ("ev_begin", ctypes.c_void_p), ("ev_end", ctypes.c_void_p)]
+                ("d_counts", ctypes.c_void_p), ("ev_begin", ctypes.c_void_p), ("ev_end", ctypes.c_void_p),
+                ("d_routed", ctypes.c_void_p), ("d_prob_mean", ctypes.c_void_p), ("d_lb_loss", ctypes.c_void_p)]
 
 
 class MoEError(RuntimeError):

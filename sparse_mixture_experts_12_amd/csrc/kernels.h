@@ -89,4 +89,17 @@ struct CombineArgs {
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
+// Router telemetry (optional side outputs of the layer call)
+struct TelemetryArgs {
+  const float* logits;           // [T, E] fp32 router logits
+  const int32_t* idx;            // [T, k] chosen experts (before capacity)
+  int T, E, k;
+  void* ws;                      // telemetry_ws_bytes(T, E)
+  int32_t* routed;               // [E] or nullptr
+  float* prob_mean;              // [E] or nullptr
+  float* lb_loss;                // [1] or nullptr
+};
+size_t telemetry_ws_bytes(int T, int E);
+hipError_t launch_telemetry(const TelemetryArgs& a, hipStream_t s);
+
 }  // namespace moe

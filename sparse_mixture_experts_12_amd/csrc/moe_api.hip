@@ -102,7 +102,7 @@ int capacity_of(const moe_desc* d) {
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t part, idx, w, plan, counts, offsets, sorted, inv, ndrop, rank, sched, h, y, partial, total;
+  size_t part, idx, w, plan, counts, offsets, sorted, inv, ndrop, rank, sched, h, y, partial, logits, tel, total;
 };
 
 bool decode_capable(const moe_desc* d) {
@@ -136,6 +136,8 @@ Layout layout_of(const moe_desc* d) {
   L.partial = decode_capable(d) ? take(decode_partial_bytes(d->T, d->d, d->E, d->top_k, d->f, d->has_shared,
                                                            d->w_dtype == MOE_FP8_E4M3 ? W_FP8 : W_BF16))
                                 : take(0);
+  L.logits = take(T * E * 4);                         // router logits, for the telemetry outputs
+  L.tel = take(telemetry_ws_bytes(d->T, d->E));
   L.total = off;
   return L;
 }
@@ -302,17 +304,31 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w
   if (stats) {
     OPT(stats->d_n_dropped, "stats.d_n_dropped");
     OPT(stats->d_counts, "stats.d_counts");
+    OPT(stats->d_routed, "stats.d_routed");
+    OPT(stats->d_prob_mean, "stats.d_prob_mean");
+    OPT(stats->d_lb_loss, "stats.d_lb_loss");
   }
   char* base = (char*)ws;
   const Layout L = layout_of(desc);
   int32_t* idx = (int32_t*)(base + L.idx);
   float* tw = (float*)(base + L.w);
+  const bool telemetry = stats && (stats->d_routed || stats->d_prob_mean || stats->d_lb_loss);
+  float* logits = telemetry ? (float*)(base + L.logits) : nullptr;
+  auto run_telemetry = [&]() -> moe_status {
+    if (!telemetry) return MOE_OK;
+    TelemetryArgs t{};
+    t.logits = logits; t.idx = idx; t.T = desc->T; t.E = desc->E; t.k = desc->top_k;
+    t.ws = base + L.tel;
+    t.routed = stats->d_routed; t.prob_mean = stats->d_prob_mean; t.lb_loss = stats->d_lb_loss;
+    return hip_status(launch_telemetry(t, stream), "telemetry");
+  };
   hipEvent_t eb = stats ? stats->ev_begin : nullptr;
   hipEvent_t ee = stats ? stats->ev_end : nullptr;
 
   if (fused) {
     int32_t* plan = (int32_t*)(base + L.plan);
-    if ((st = do_route(desc, x, w, idx, tw, nullptr, nullptr, plan, stream)) != MOE_OK) return st;
+    if ((st = do_route(desc, x, w, idx, tw, logits, nullptr, plan, stream)) != MOE_OK) return st;
+    if ((st = run_telemetry()) != MOE_OK) return st;
     DecodeArgs a{};
     a.x = x; a.plan = plan; a.topk_w = tw; a.w = expert_weights(w);
     a.T = desc->T; a.d = desc->d; a.E = desc->E; a.k = desc->top_k; a.f = desc->f;
@@ -330,7 +346,8 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w
     }
     return MOE_OK;
   }
-  if ((st = do_route(desc, x, w, idx, tw, nullptr, (double*)(base + L.part), nullptr, stream)) != MOE_OK) return st;
+  if ((st = do_route(desc, x, w, idx, tw, logits, (double*)(base + L.part), nullptr, stream)) != MOE_OK) return st;
+  if ((st = run_telemetry()) != MOE_OK) return st;
   int32_t* counts = (stats && stats->d_counts) ? stats->d_counts : (int32_t*)(base + L.counts);
   int32_t* nd = (stats && stats->d_n_dropped) ? stats->d_n_dropped : (int32_t*)(base + L.ndrop);
   int32_t* offsets = (int32_t*)(base + L.offsets);

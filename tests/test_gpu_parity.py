@@ -339,3 +339,44 @@ def test_forward_parity_full_size(name):
     assert int(dev_nd.cpu()[0]) == ref["n_dropped"]
     if name == "fine_grained":
         assert (ref["counts"] == 0).sum() >= 1, "the Zipf bias should leave some expert without tokens"
+
+
+# ---------------------------------------------------------------------------
+# Router telemetry side outputs of moe_forward, against the oracle
+# ---------------------------------------------------------------------------
+TEL_CASES = ["tiny_f32_ragged", "bf16_prefill_ragged", "bf16_finegrained_shared", "fp8_capacity_tight",
+             "bf16_top1_switch", "decode_T1", "decode_T8", "decode_T3_fp8_cap", "fine_grained", "mixtral_prefill"]
+
+
+@pytest.mark.parametrize("name", TEL_CASES)
+def test_router_telemetry_parity(name):
+    cfg = SMALL[name] if name in SMALL else C[name]
+    print(f"[telemetry] {name}", flush=True)
+    inp = device_inputs(cfg)
+    ov = OracleInputs(inp)
+    plain, _ = run_forward(inp)
+
+    def run():
+        routed = torch.full((cfg.E,), -7, dtype=torch.int32, device="cuda")
+        pm = torch.full((cfg.E,), float("nan"), dtype=torch.float32, device="cuda")
+        loss = torch.full((4,), float("nan"), dtype=torch.float32, device="cuda")
+        st = ops.Stats(d_routed=routed.data_ptr(), d_prob_mean=pm.data_ptr(), d_lb_loss=loss.data_ptr())
+        out, _ = run_forward(inp, stats=st)
+        return out, routed.cpu().numpy(), pm.cpu().numpy(), loss.cpu().numpy()
+
+    out, routed, pm, loss = run()
+    ref = ov.forward(tokens=np.arange(min(cfg.T, 2)))     # routing of every token; FFN of two
+    tel = oracle.router_telemetry(ref["logits"], ref["topk_idx"], cfg.E)
+    np.testing.assert_array_equal(routed, tel["routed"])
+    np.testing.assert_allclose(pm.astype(np.float64), tel["prob_mean"], rtol=1e-6, atol=1e-12)
+    assert loss[0] == pytest.approx(tel["lb_loss"], rel=1e-6)
+    assert np.isnan(loss[1:]).all()                       # nothing written past the loss
+    # the side outputs change nothing else and are bitwise reproducible
+    assert torch.equal(out, plain)
+    out2, routed2, pm2, loss2 = run()
+    assert torch.equal(out2, out)
+    np.testing.assert_array_equal(routed2, routed)
+    np.testing.assert_array_equal(pm2.view(np.int32), pm.view(np.int32))
+    np.testing.assert_array_equal(loss2[:1].view(np.int32), loss[:1].view(np.int32))
+    print(f"[telemetry] {name}: loss={loss[0]:.6f} oracle={tel['lb_loss']:.6f} "
+          f"max_load={routed.max()} idle_experts={(routed == 0).sum()}", flush=True)
