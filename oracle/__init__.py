@@ -4,7 +4,8 @@ Only tests, the smoke check and the bench's CPU-baseline leg may import this
 package.  The product library never does.
 """
 from .moe_oracle import (  # noqa: F401
-    capacity, dequantize, expert_ffn, forward, fp8_e4m3fn_decode, permute,
+    capacity, dequantize, expert_choice_capacity, expert_choice_forward, expert_choice_routing,
+    expert_ffn, forward, fp8_e4m3fn_decode, permute,
     router_logits, router_telemetry, routing_certificate, routing_weights, silu,
     softmax_rows, topk_select,
 )

@@ -296,3 +296,80 @@ def router_telemetry(logits32, idx, E: int) -> dict:
     prob_mean = np.array([math.fsum(probs[:, e]) / T for e in range(E)])
     lb_loss = E * math.fsum(prob_mean[e] * routed[e] / T for e in range(E))
     return {"routed": routed, "prob_mean": prob_mean, "lb_loss": lb_loss}
+
+
+# ----------------------------------------------------------------------------
+# Expert-choice routing ("MoE Model Architectures", Design Patterns, Pattern 3:
+# every expert selects its top tokens instead of tokens selecting experts).
+# ----------------------------------------------------------------------------
+def expert_choice_capacity(T: int, k: int, E: int, capacity_factor) -> int:
+    """Tokens each expert takes: C = ceil(cf * T * k / E) (cf = 0 -> 1, so the
+    number of (token, expert) pairs matches token choice), at least 1 and at
+    most T."""
+    cf = float(np.float32(capacity_factor))
+    c = math.ceil((cf if cf > 0 else 1.0) * T * k / E)
+    return max(1, min(T, c))
+
+
+def expert_choice_routing(logits32, k: int, capacity_factor, renormalize: bool) -> dict:
+    """Scores are the full softmax of the fp32 logits, rounded to fp32.  Expert
+    e takes the C tokens of largest score (equal scores -> lower token index);
+    its rows are those tokens in ascending order.  A token's weight for expert
+    e is its score (divided by the sum of its scores over the experts that
+    chose it when renormalising); tokens no expert chose get nothing.
+
+    Returns capacity, offsets[E+1], sorted_tokens[E*C] (row -> token),
+    pos[T, E] (row of (t, e) or -1) and weight[T, E] (0 where not chosen)."""
+    probs = softmax_rows(logits32)
+    s32 = probs.astype(np.float32)
+    T, E = probs.shape
+    C = expert_choice_capacity(T, k, E, capacity_factor) if T > 0 else 0
+    pos = np.full((T, E), -1, dtype=np.int64)
+    sorted_tokens = []
+    offsets = [0]
+    for e in range(E):
+        best = sorted(range(T), key=lambda t: (-float(s32[t, e]), t))[:C]
+        for t in sorted(best):
+            pos[t, e] = len(sorted_tokens)
+            sorted_tokens.append(t)
+        offsets.append(len(sorted_tokens))
+    weight = np.zeros((T, E), dtype=np.float64)
+    for t in range(T):
+        chosen = [e for e in range(E) if pos[t, e] >= 0]
+        den = math.fsum(float(s32[t, e]) for e in chosen) if (renormalize and chosen) else 1.0
+        for e in chosen:
+            weight[t, e] = float(s32[t, e]) / den
+    return dict(capacity=C, offsets=np.array(offsets, dtype=np.int64),
+                sorted_tokens=np.array(sorted_tokens, dtype=np.int64), pos=pos, weight=weight, scores=s32)
+
+
+def expert_choice_forward(x, W_g, bias, k: int, renormalize: bool, capacity_factor,
+                          expert: ExpertFn, E: int, shared: Optional[Sequence[np.ndarray]] = None,
+                          tokens: Optional[Sequence[int]] = None) -> dict:
+    """The layer with expert-choice routing: out[t] = sum over the experts that
+    chose t, in ascending expert order, of weight[t, e] * FFN_e(x[t]), plus the
+    shared expert.  Routing for every token; FFN and sum for `tokens`."""
+    x = _f64(x)
+    T = x.shape[0]
+    logits = router_logits(x, W_g, bias)
+    r = expert_choice_routing(logits, k, capacity_factor, renormalize)
+    toks = list(range(T)) if tokens is None else [int(t) for t in tokens]
+    want = set(toks)
+    y = {}
+    for e in range(E):
+        rows = [int(t) for t in r["sorted_tokens"][r["offsets"][e]:r["offsets"][e + 1]] if int(t) in want]
+        if not rows:
+            continue
+        Y = expert_ffn(x[rows], *expert(e))
+        for t, yy in zip(rows, Y):
+            y[(t, e)] = yy
+    out = np.zeros((len(toks), x.shape[1]), dtype=np.float64)
+    for i, t in enumerate(toks):
+        acc = np.zeros(x.shape[1], dtype=np.float64)
+        for e in range(E):
+            if r["pos"][t, e] >= 0:
+                acc = acc + r["weight"][t, e] * y[(t, e)]
+        out[i] = acc
+    if shared is not None:
+        out = out + expert_ffn(x[toks], *shared)
+    return dict(logits=logits, out=out, tokens=np.array(toks, dtype=np.int64), **r)

@@ -423,3 +423,83 @@ def test_router_telemetry_invariants():
     # empty batch
     r0 = oracle.router_telemetry(np.zeros((0, E), dtype=np.float32), np.zeros((0, k), dtype=np.int32), E)
     assert r0["routed"].sum() == 0 and r0["lb_loss"] == 0.0
+
+
+# ----------------------------------------------------------------------------
+# Expert-choice routing (Design Patterns, Pattern 3)
+# ----------------------------------------------------------------------------
+def test_expert_choice_capacity_closed_forms():
+    assert oracle.expert_choice_capacity(10, 2, 4, 0.0) == 5          # T k / E
+    assert oracle.expert_choice_capacity(10, 2, 4, 1.25) == 7         # ceil(6.25)
+    assert oracle.expert_choice_capacity(10, 2, 4, 0.01) == 1         # at least one token
+    assert oracle.expert_choice_capacity(10, 2, 4, 100.0) == 10       # at most T
+
+
+@pytest.mark.parametrize("seed,T,E,k,cf,renorm", [(1, 9, 4, 2, 0.0, True), (2, 13, 5, 1, 1.5, False),
+                                                  (3, 6, 3, 3, 0.0, True), (4, 17, 6, 2, 0.7, False)])
+def test_expert_choice_selection_property(seed, T, E, k, cf, renorm):
+    rng = np.random.default_rng(seed)
+    l = rng.normal(size=(T, E)).astype(np.float32)
+    l[2] = l[5 % T]                                    # a duplicated token row: equal scores
+    r = oracle.expert_choice_routing(l, k, cf, renorm)
+    C, s = r["capacity"], r["scores"]
+    assert C == oracle.expert_choice_capacity(T, k, E, cf)
+    assert r["offsets"].tolist() == [e * C for e in range(E + 1)]
+    for e in range(E):
+        chosen = [t for t in range(T) if r["pos"][t, e] >= 0]
+        assert len(chosen) == C
+        rows = r["sorted_tokens"][r["offsets"][e]:r["offsets"][e + 1]].tolist()
+        assert rows == sorted(chosen)                  # rows in ascending token order
+        assert all(r["pos"][t, e] == r["offsets"][e] + rows.index(t) for t in chosen)
+        for t in chosen:                               # every chosen token beats every other one
+            for u in range(T):
+                if r["pos"][u, e] < 0:
+                    assert s[t, e] > s[u, e] or (s[t, e] == s[u, e] and t < u)
+    times = (r["pos"] >= 0).sum(axis=1)
+    assert times.sum() == E * C
+    for t in range(T):
+        w = r["weight"][t]
+        if renorm and times[t] > 0:
+            assert math.fsum(w) == pytest.approx(1.0, rel=1e-15)
+        if not renorm:
+            np.testing.assert_array_equal(w[r["pos"][t] >= 0], s[t][r["pos"][t] >= 0].astype(np.float64))
+        assert np.all(w[r["pos"][t] < 0] == 0.0)
+
+
+def test_expert_choice_ties_go_to_lower_token():
+    l = np.zeros((7, 3), dtype=np.float32)             # every score 1/3
+    r = oracle.expert_choice_routing(l, 1, 0.0, False)
+    assert r["capacity"] == 3
+    assert r["sorted_tokens"].tolist() == [0, 1, 2] * 3
+
+
+def test_expert_choice_all_tokens_equals_token_choice_over_all_experts():
+    # C = T: every expert takes every token with weight = its full-softmax score,
+    # which is the token-choice layer with k = E and no renormalisation
+    T, d, E, f = 8, 16, 4, 24
+    x, Wg, ex, sh = _layer(T, d, E, E, f, shared=True, seed=3)
+    ec = oracle.expert_choice_forward(x, Wg, None, E, False, 0.0, lambda e: ex[e], E, shared=sh)
+    assert ec["capacity"] == T
+    tc = oracle.forward(x, Wg, None, E, False, 0.0, lambda e: ex[e], E, shared=sh)
+    np.testing.assert_allclose(ec["out"], tc["out"], rtol=2e-7, atol=1e-9)  # fp32-rounded scores
+
+
+def test_expert_choice_single_expert_is_dense_swiglu():
+    T, d, f = 11, 24, 40
+    x, Wg, ex, _ = _layer(T, d, 1, 1, f)
+    r = oracle.expert_choice_forward(x, Wg, None, 1, True, float(T), lambda e: ex[e], 1)
+    assert r["capacity"] == T and np.all(r["weight"] == 1.0)
+    np.testing.assert_allclose(r["out"], torch_dense_swiglu(x, *ex[0]).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_expert_choice_relabelling_invariance():
+    T, d, E, k, f = 10, 16, 5, 2, 20
+    x, Wg, ex, _ = _layer(T, d, E, k, f, seed=8)
+    r0 = oracle.expert_choice_forward(x, Wg, None, k, True, 0.0, lambda e: ex[e], E)
+    pi = np.random.default_rng(4).permutation(E)       # experts relabelled
+    r1 = oracle.expert_choice_forward(x, Wg[:, pi], None, k, True, 0.0, lambda e: ex[pi[e]], E)
+    np.testing.assert_array_equal(r1["pos"] >= 0, (r0["pos"] >= 0)[:, pi])
+    np.testing.assert_allclose(r1["out"], r0["out"], rtol=1e-13, atol=1e-13)
+    tp = np.random.default_rng(5).permutation(T)       # tokens relabelled (scores are distinct)
+    r2 = oracle.expert_choice_forward(x[tp], Wg, None, k, True, 0.0, lambda e: ex[e], E)
+    np.testing.assert_allclose(r2["out"], r0["out"][tp], rtol=1e-13, atol=1e-13)
