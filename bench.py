@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="skip the second timed region (per-launch events on the dominant kernel)")
+    ap.add_argument("--routing", choices=["token", "expert"], default="token",
+                    help="token choice (the pages' default) or expert choice (every expert takes its C best tokens)")
     ap.add_argument("--telemetry", action="store_true",
                     help="also request the router telemetry outputs (routed load, mean probability, "
                          "load-balancing loss) inside the timed region")
@@ -159,7 +161,7 @@ def main():
     from sparse_mixture_experts_12_amd import _lib as ops
 
     cfg = synth.CONFIGS[args.workload]
-    decode = cfg.T <= 8 and cfg.act == "bf16"
+    decode = cfg.T <= 8 and cfg.act == "bf16" and args.routing == "token"
     steps = args.steps if args.steps is not None else (200 if decode else 20)
     # a few ms of warm-up lets the clocks settle before the timed region
     warmup = args.warmup if args.warmup is not None else 10
@@ -179,7 +181,8 @@ def main():
                 c[key] = inp[key].clone()
         copies.append(c)
     wstructs = [ops.weights_struct(c) for c in copies]
-    desc = ops.desc_from_cfg(cfg)
+    routing = ops.ROUTING_EXPERT_CHOICE if args.routing == "expert" else ops.ROUTING_TOKEN_CHOICE
+    desc = ops.desc_from_cfg(cfg, routing=routing)
     ws = ops.alloc_workspace(desc)
     dt = torch.float32 if cfg.act == "f32" else torch.bfloat16
     out = torch.empty((cfg.T, cfg.d), dtype=dt, device="cuda")
@@ -300,7 +303,7 @@ def main():
                    "act": cfg.act, "weights": cfg.wdt, "shared_expert": cfg.shared,
                    "capacity_factor": cfg.capacity_factor, "path": "fused_decode" if path == 2 else "grouped",
                    "experts_touched": touched, "dropped_share": n_dropped / max(1, cfg.T * cfg.k),
-                   "weight_copies": n_copies, "telemetry": bool(args.telemetry)},
+                   "weight_copies": n_copies, "telemetry": bool(args.telemetry), "routing": args.routing},
         "layer": {"alg_bytes": int(bytes_total), "alg_flops": int(flops),
                   "hbm_GBps": round(bytes_total / (ms_per_step / 1e3) / 1e9, 1),
                   "tflops": round(flops / (ms_per_step / 1e3) / 1e12, 3)},

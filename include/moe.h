@@ -73,6 +73,21 @@ typedef enum {
 
 #define MOE_FUSED_DECODE_MAX_T 8
 
+/* Who chooses.  Token choice ("MoE Model Architectures", Mixtral "Sparse MoE
+ * Block"): every token takes its top_k experts.  Expert choice (same page,
+ * Design Patterns, Pattern 3 "Expert Choice Routing"): every expert takes the
+ * C tokens with the largest full-softmax score (fp32, ties -> lower token
+ * index), C = max(1, min(T, ceil(cf * T * top_k / E))) with cf =
+ * capacity_factor (1 when 0); a token's output is the sum over the experts
+ * that chose it, in ascending expert order, of its score (divided by the sum
+ * of those scores when renormalize = 1) times the expert output, plus the
+ * shared expert.  Expert choice runs through moe_forward only (grouped path,
+ * T <= MOE_EXPERT_CHOICE_MAX_T); the token-choice stage calls moe_route,
+ * moe_permute, moe_grouped_ffn and moe_combine return MOE_ERR_UNSUPPORTED for
+ * it. */
+typedef enum { MOE_ROUTING_TOKEN_CHOICE = 0, MOE_ROUTING_EXPERT_CHOICE = 1 } moe_routing;
+#define MOE_EXPERT_CHOICE_MAX_T 8192
+
 typedef struct {
   int32_t T;                 /* tokens, >= 0                                     */
   int32_t d;                 /* hidden size, multiple of 64                      */
@@ -85,6 +100,7 @@ typedef struct {
   int32_t w_dtype;           /* experts: F32 (act F32) | BF16 or FP8_E4M3 (act BF16) */
   int32_t has_shared;        /* 0 | 1: one always-on shared expert, weight 1     */
   int32_t path;              /* moe_path                                         */
+  int32_t routing;           /* moe_routing (0 = token choice, the default)      */
 } moe_desc;
 
 typedef struct {
@@ -132,7 +148,8 @@ typedef struct {
  * over entry points).  Returns 0 when desc is invalid. */
 size_t moe_workspace_size(const moe_desc* desc);
 
-/* Per-expert capacity C for desc, or -1 when uncapped / desc invalid. */
+/* Per-expert capacity C for desc, or -1 when uncapped / desc invalid.  With
+ * expert-choice routing, the number of tokens every expert takes. */
 int32_t moe_capacity(const moe_desc* desc);
 
 /* Router: logits, softmax, top-k and (optional) renormalisation.
@@ -189,7 +206,11 @@ moe_status moe_combine(const moe_desc* desc, const float* y_sorted, const int32_
 /* Whole layer: route -> (permute -> grouped FFN -> combine) or, for T <= 8,
  * route -> fused decode (streams only the chosen experts' weights; page
  * "perf(moe): route granite-4.0-h single-token MoE through the fused
- * kernel").  out [T, d] act dtype.  stats may be NULL. */
+ * kernel").  out [T, d] act dtype.  stats may be NULL.
+ * Expert-choice routing (desc->routing): route -> per-expert token selection
+ * -> grouped FFN -> combine; stats->d_counts receives C per expert,
+ * stats->d_n_dropped the number of tokens no expert chose; the telemetry
+ * fields are token-choice statistics and are declined (MOE_ERR_UNSUPPORTED). */
 moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, void* out,
                        moe_stats* stats, void* ws, size_t ws_bytes, hipStream_t stream);
 

@@ -18,6 +18,7 @@ LIB_PATH = os.environ.get("MOE_LIB", os.path.join(_PKG, "libmoe.so"))
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
 PATH_AUTO, PATH_GROUPED, PATH_FUSED_DECODE = range(3)
+ROUTING_TOKEN_CHOICE, ROUTING_EXPERT_CHOICE = range(2)
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 
 # Every symbol the header declares.
@@ -29,7 +30,8 @@ class Desc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("f", ctypes.c_int32), ("renormalize", ctypes.c_int32),
                 ("capacity_factor", ctypes.c_float), ("act_dtype", ctypes.c_int32),
-                ("w_dtype", ctypes.c_int32), ("has_shared", ctypes.c_int32), ("path", ctypes.c_int32)]
+                ("w_dtype", ctypes.c_int32), ("has_shared", ctypes.c_int32), ("path", ctypes.c_int32),
+                ("routing", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -96,9 +98,11 @@ def make_desc(T, d, E, top_k, f, act="bf16", wdt="bf16", renormalize=True, capac
                 int(bool(has_shared)), int(path))
 
 
-def desc_from_cfg(cfg, path=PATH_AUTO, T=None) -> Desc:
-    return make_desc(cfg.T if T is None else T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.act, cfg.wdt,
-                     cfg.renormalize, cfg.capacity_factor, cfg.shared, path)
+def desc_from_cfg(cfg, path=PATH_AUTO, T=None, routing=ROUTING_TOKEN_CHOICE) -> Desc:
+    d = make_desc(cfg.T if T is None else T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.act, cfg.wdt,
+                  cfg.renormalize, cfg.capacity_factor, cfg.shared, path)
+    d.routing = routing
+    return d
 
 
 def _ptr(t) -> int | None:

@@ -775,20 +775,19 @@ static int pick_bm(const GroupedArgs& a) {
   // experts of 0..1507 rows): fewer row tiles re-read each expert's weights.
   if (a.wkind == W_BF16) return 256;
   // fp8 weights (register-staged kernel): 64-row tiles unless experts are large
-  const int avg = (a.T * a.k) / (a.E > 0 ? a.E : 1);
+  const int avg = a.routed_rows / (a.E > 0 ? a.E : 1);
   return avg >= 256 ? 256 : 64;
 }
 
-static int max_row_tiles(int T, int k, int E, int has_shared, int BM) {
-  const int n = T * k;
-  int q = n / BM + (n < E ? n : E);
+static int max_row_tiles(int routed_rows, int T, int E, int has_shared, int BM) {
+  int q = routed_rows / BM + (routed_rows < E ? routed_rows : E);
   if (has_shared) q += (T + BM - 1) / BM;
   return q;
 }
 
-size_t grouped_sched_ints(int T, int k, int E, int has_shared) {
+size_t grouped_sched_ints(int routed_rows, int T, int E, int has_shared) {
   // enough for the smallest tile height used (64 rows)
-  return kSchedHead + 4 * (size_t)max_row_tiles(T, k, E, has_shared, 64) + 4 * (size_t)(E + 1) + 16;
+  return kSchedHead + 4 * (size_t)max_row_tiles(routed_rows, T, E, has_shared, 64) + 4 * (size_t)(E + 1) + 16;
 }
 
 // Work-groups: per XCD, enough slots for both schedule segments.  With
@@ -800,9 +799,9 @@ static inline int grid_for(int maxQ, int n_tiles) {
 
 hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   const int BM = pick_bm(a);
-  const int maxQ = max_row_tiles(a.T, a.k, a.E, a.has_shared, BM);
+  const int maxQ = max_row_tiles(a.routed_rows, a.T, a.E, a.has_shared, BM);
   const int shared_rows = a.has_shared ? a.T : 0;
-  const int shared_row0 = a.T * a.k;
+  const int shared_row0 = a.routed_rows;
   hipError_t err = launch_tile_schedule(a.offsets, a.E, BM, shared_rows, shared_row0, maxQ, a.sched, s);
   if (err != hipSuccess) return err;
 
@@ -812,7 +811,7 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
     p.sorted_assign = a.sorted_assign;
     p.sched = a.sched;
     p.maxQ = maxQ;
-    p.T = a.T; p.k = a.k; p.E = a.E; p.shared_row0 = shared_row0;
+    p.T = a.T; p.k = a.assign_div; p.E = a.E; p.shared_row0 = shared_row0;
     // gate/up
     p.W0 = (const float*)a.w.Wg; p.W1 = (const float*)a.w.Wu;
     p.Ws0 = (const float*)a.w.Wsg; p.Ws1 = (const float*)a.w.Wsu;
@@ -840,7 +839,7 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   p.sorted_assign = a.sorted_assign;
   p.sched = a.sched;
   p.maxQ = maxQ;
-  p.T = a.T; p.k = a.k; p.E = a.E; p.shared_row0 = shared_row0;
+  p.T = a.T; p.k = a.assign_div; p.E = a.E; p.shared_row0 = shared_row0;
   p.W0 = a.w.Wg; p.W1 = a.w.Wu; p.Ws0 = a.w.Wsg; p.Ws1 = a.w.Wsu;
   p.s0 = a.w.sg; p.s1 = a.w.su; p.ss0 = a.w.ssg; p.ss1 = a.w.ssu;
   p.K = a.d; p.N = a.f;

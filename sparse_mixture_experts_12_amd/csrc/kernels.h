@@ -53,16 +53,18 @@ struct GroupedArgs {
   const int32_t* offsets;        // [E + 1]
   ExpertWeights w;
   int T, d, E, k, f;
+  int routed_rows;               // rows before the shared expert's (T*k; E*C for expert choice)
+  int assign_div;                // token of permuted row r = sorted_assign[r] / assign_div (k; 1)
   int has_shared;
   int wkind;                     // WKind
   bool act_f32;
-  float* y;                      // [T*k (+T), d] fp32
-  void* h;                       // [T*k (+T), f] bf16 (or fp32 for act f32)
+  float* y;                      // [routed_rows (+T), d] fp32
+  void* h;                       // [routed_rows (+T), f] bf16 (or fp32 for act f32)
   int32_t* sched;                // schedule scratch
   int32_t* sched2;               // second schedule (down GEMM uses its own BM)
   hipEvent_t ev_begin, ev_end;
 };
-size_t grouped_sched_ints(int T, int k, int E, int has_shared);
+size_t grouped_sched_ints(int routed_rows, int T, int E, int has_shared);
 hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s);
 
 struct DecodeArgs {
@@ -101,5 +103,32 @@ struct TelemetryArgs {
 };
 size_t telemetry_ws_bytes(int T, int E);
 hipError_t launch_telemetry(const TelemetryArgs& a, hipStream_t s);
+
+// Expert-choice routing: every expert takes its C best tokens
+constexpr int kEcMaxT = 8192;
+struct ExpertChoiceArgs {
+  const float* logits;           // [T, E] fp32 router logits
+  int T, E, C, renormalize;
+  float* scores;                 // ws [E, T] fp32 full-softmax scores
+  int32_t* pos;                  // [T, E] row of (t, e) or -1
+  int32_t* crow;                 // [T, E] per token: rows of its experts, ascending expert order
+  float* w;                      // [T, E] per token: the matching combine weights
+  int32_t* ccount;               // [T] experts that took the token
+  int32_t* sorted_tokens;        // [E*C] permuted row -> token
+  int32_t* offsets;              // [E + 1] = e * C
+  int32_t* counts;               // [E] or nullptr: C per expert
+  int32_t* n_unchosen;           // [1] tokens no expert chose
+};
+hipError_t launch_expert_choice(const ExpertChoiceArgs& a, hipStream_t s);
+struct EcCombineArgs {
+  const float* y;                // [E*C (+T), d]
+  const int32_t* crow;
+  const float* w;
+  const int32_t* ccount;
+  int T, d, E, routed_rows, has_shared;
+  bool act_f32;
+  void* out;
+};
+hipError_t launch_ec_combine(const EcCombineArgs& a, hipStream_t s);
 
 }  // namespace moe

@@ -44,6 +44,14 @@ moe_status check_desc(const moe_desc* d) {
   if (w != MOE_F32 && w != MOE_BF16 && w != MOE_FP8_E4M3) return fail(MOE_ERR_INVALID_ARG, "bad w_dtype %d", w);
   const bool ok = (a == MOE_F32 && w == MOE_F32) || (a == MOE_BF16 && (w == MOE_BF16 || w == MOE_FP8_E4M3));
   if (!ok) return fail(MOE_ERR_UNSUPPORTED, "dtype pair act=%d w=%d not supported", a, w);
+  if (d->routing != MOE_ROUTING_TOKEN_CHOICE && d->routing != MOE_ROUTING_EXPERT_CHOICE)
+    return fail(MOE_ERR_INVALID_ARG, "bad routing %d", d->routing);
+  if (d->routing == MOE_ROUTING_EXPERT_CHOICE) {
+    if (d->path == MOE_PATH_FUSED_DECODE)
+      return fail(MOE_ERR_UNSUPPORTED, "expert-choice routing runs on the grouped path");
+    if (d->T > MOE_EXPERT_CHOICE_MAX_T)
+      return fail(MOE_ERR_UNSUPPORTED, "expert-choice routing takes T <= %d (T=%d)", MOE_EXPERT_CHOICE_MAX_T, d->T);
+  }
   if (d->path == MOE_PATH_FUSED_DECODE) {
     if (d->T > MOE_FUSED_DECODE_MAX_T)
       return fail(MOE_ERR_UNSUPPORTED, "fused decode path takes T <= %d (T=%d)", MOE_FUSED_DECODE_MAX_T, d->T);
@@ -93,7 +101,23 @@ moe_status check_expert_weights(const moe_desc* d, const moe_weights* w) {
   return MOE_OK;
 }
 
+bool expert_choice(const moe_desc* d) { return d->routing == MOE_ROUTING_EXPERT_CHOICE; }
+
+// Tokens every expert takes under expert-choice routing.
+int ec_capacity_of(const moe_desc* d) {
+  const double cf = d->capacity_factor > 0.f ? (double)d->capacity_factor : 1.0;
+  const double c = ceil(cf * (double)d->T * (double)d->top_k / (double)d->E);
+  const double cmax = d->T > 0 ? (double)d->T : 1.0;
+  return c < 1.0 ? 1 : (int)(c > cmax ? cmax : c);
+}
+
+// Routed rows of the grouped FFN (before the shared expert's T rows).
+size_t routed_rows_of(const moe_desc* d) {
+  return expert_choice(d) ? (size_t)d->E * ec_capacity_of(d) : (size_t)d->T * d->top_k;
+}
+
 int capacity_of(const moe_desc* d) {
+  if (expert_choice(d)) return ec_capacity_of(d);
   if (!(d->capacity_factor > 0.f)) return -1;
   const double c = ceil((double)d->capacity_factor * (double)d->T * (double)d->top_k / (double)d->E);
   return c < 1.0 ? 1 : (int)c;
@@ -102,7 +126,8 @@ int capacity_of(const moe_desc* d) {
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t part, idx, w, plan, counts, offsets, sorted, inv, ndrop, rank, sched, h, y, partial, logits, tel, total;
+  size_t part, idx, w, plan, counts, offsets, sorted, inv, ndrop, rank, sched, h, y, partial, logits, tel;
+  size_t ec_scores, ec_pos, ec_w, ec_crow, ec_count, ec_sorted, ec_offsets, total;
 };
 
 bool decode_capable(const moe_desc* d) {
@@ -113,7 +138,8 @@ bool decode_capable(const moe_desc* d) {
 Layout layout_of(const moe_desc* d) {
   Layout L{};
   const size_t T = d->T, k = d->top_k, E = d->E;
-  const size_t rows = T * k + (d->has_shared ? T : 0);
+  const size_t routed = routed_rows_of(d);
+  const size_t rows = routed + (d->has_shared ? T : 0);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
@@ -130,7 +156,7 @@ Layout layout_of(const moe_desc* d) {
   L.inv = take(T * k * 4);
   L.ndrop = take(4);
   L.rank = take(T * k * 4);
-  L.sched = take(grouped_sched_ints(d->T, d->top_k, d->E, d->has_shared) * 4);
+  L.sched = take(grouped_sched_ints((int)routed, d->T, d->E, d->has_shared) * 4);
   L.h = take(rows * d->f * (d->act_dtype == MOE_F32 ? 4 : 2));
   L.y = take(rows * d->d * 4);
   L.partial = decode_capable(d) ? take(decode_partial_bytes(d->T, d->d, d->E, d->top_k, d->f, d->has_shared,
@@ -138,6 +164,14 @@ Layout layout_of(const moe_desc* d) {
                                 : take(0);
   L.logits = take(T * E * 4);                         // router logits, for the telemetry outputs
   L.tel = take(telemetry_ws_bytes(d->T, d->E));
+  const bool ec = expert_choice(d);
+  L.ec_scores = take(ec ? E * T * 4 : 0);
+  L.ec_pos = take(ec ? T * E * 4 : 0);
+  L.ec_w = take(ec ? T * E * 4 : 0);
+  L.ec_crow = take(ec ? T * E * 4 : 0);
+  L.ec_count = take(ec ? T * 4 : 0);
+  L.ec_sorted = take(ec ? routed * 4 : 0);
+  L.ec_offsets = take(ec ? (E + 1) * 4 : 0);
   L.total = off;
   return L;
 }
@@ -168,12 +202,15 @@ int wkind_of(const moe_desc* d) {
   return d->w_dtype == MOE_FP8_E4M3 ? W_FP8 : d->w_dtype == MOE_BF16 ? W_BF16 : W_F32;
 }
 
+hipEvent_t eb_of(const moe_stats* st) { return st ? st->ev_begin : nullptr; }
+hipEvent_t ee_of(const moe_stats* st) { return st ? st->ev_end : nullptr; }
+
 moe_status do_route(const moe_desc* d, const void* x, const moe_weights* w, int32_t* idx, float* tw, float* logits,
                     double* part, int32_t* plan, hipStream_t s) {
   RouteArgs a{};
   a.x = x; a.W_g = w->W_g; a.bias = w->router_bias;
   a.T = d->T; a.d = d->d; a.E = d->E; a.k = d->top_k; a.renormalize = d->renormalize;
-  a.cap = capacity_of(d);
+  a.cap = expert_choice(d) ? -1 : capacity_of(d);     // token-choice capacity (decode plan)
   a.act_f32 = d->act_dtype == MOE_F32;
   a.logits = logits; a.part = part; a.idx = idx; a.w = tw; a.plan = plan;
   return hip_status(launch_route(a, s), "route");
@@ -194,6 +231,8 @@ moe_status do_grouped(const moe_desc* d, const void* x, const moe_weights* w, co
   GroupedArgs a{};
   a.x = x; a.sorted_assign = sorted; a.offsets = offsets; a.w = expert_weights(w);
   a.T = d->T; a.d = d->d; a.E = d->E; a.k = d->top_k; a.f = d->f; a.has_shared = d->has_shared;
+  a.routed_rows = (int)routed_rows_of(d);
+  a.assign_div = expert_choice(d) ? 1 : d->top_k;
   a.wkind = wkind_of(d);
   a.act_f32 = d->act_dtype == MOE_F32;
   a.y = y;
@@ -230,6 +269,8 @@ moe_status moe_route(const moe_desc* desc, const void* x, const moe_weights* w, 
                      float* logits, void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
+  if (expert_choice(desc))
+    return fail(MOE_ERR_UNSUPPORTED, "expert-choice routing runs through moe_forward only");
   if (desc->T == 0) return MOE_OK;
   REQ(x, "x");
   REQ(topk_idx, "topk_idx");
@@ -249,6 +290,8 @@ moe_status moe_permute(const moe_desc* desc, const int32_t* topk_idx, int32_t* c
                        hipStream_t stream) {
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
+  if (expert_choice(desc))
+    return fail(MOE_ERR_UNSUPPORTED, "expert-choice routing runs through moe_forward only");
   if (desc->T == 0) return MOE_OK;
   REQ(counts, "counts");
   REQ(offsets, "offsets");
@@ -266,6 +309,8 @@ moe_status moe_grouped_ffn(const moe_desc* desc, const void* x, const moe_weight
                            const int32_t* offsets, float* y_sorted, void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
+  if (expert_choice(desc))
+    return fail(MOE_ERR_UNSUPPORTED, "expert-choice routing runs through moe_forward only");
   if (desc->T == 0) return MOE_OK;
   REQ(x, "x");
   REQ(sorted_assign, "sorted_assign");
@@ -281,6 +326,8 @@ moe_status moe_combine(const moe_desc* desc, const float* y_sorted, const int32_
                        void* out, hipStream_t stream) {
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
+  if (expert_choice(desc))
+    return fail(MOE_ERR_UNSUPPORTED, "expert-choice routing runs through moe_forward only");
   if (desc->T == 0) return MOE_OK;
   REQ(y_sorted, "y_sorted");
   REQ(inv_perm, "inv_perm");
@@ -293,7 +340,8 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w
                        void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
-  const bool fused = desc->path == MOE_PATH_FUSED_DECODE || (desc->path == MOE_PATH_AUTO && decode_capable(desc));
+  const bool fused = !expert_choice(desc) && (desc->path == MOE_PATH_FUSED_DECODE ||
+                                              (desc->path == MOE_PATH_AUTO && decode_capable(desc)));
   if (stats) stats->path_taken = fused ? MOE_PATH_FUSED_DECODE : MOE_PATH_GROUPED;
   if (desc->T == 0) return MOE_OK;
   REQ(x, "x");
@@ -312,6 +360,33 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w
   const Layout L = layout_of(desc);
   int32_t* idx = (int32_t*)(base + L.idx);
   float* tw = (float*)(base + L.w);
+  if (expert_choice(desc)) {
+    if (stats && (stats->d_routed || stats->d_prob_mean || stats->d_lb_loss))
+      return fail(MOE_ERR_UNSUPPORTED, "router telemetry describes token-choice routing");
+    float* lg = (float*)(base + L.logits);
+    if ((st = do_route(desc, x, w, idx, tw, lg, (double*)(base + L.part), nullptr, stream)) != MOE_OK) return st;
+    ExpertChoiceArgs a{};
+    a.logits = lg; a.T = desc->T; a.E = desc->E; a.C = ec_capacity_of(desc); a.renormalize = desc->renormalize;
+    a.scores = (float*)(base + L.ec_scores);
+    a.pos = (int32_t*)(base + L.ec_pos);
+    a.w = (float*)(base + L.ec_w);
+    a.crow = (int32_t*)(base + L.ec_crow);
+    a.ccount = (int32_t*)(base + L.ec_count);
+    a.sorted_tokens = (int32_t*)(base + L.ec_sorted);
+    a.offsets = (int32_t*)(base + L.ec_offsets);
+    a.counts = stats ? stats->d_counts : nullptr;
+    a.n_unchosen = (stats && stats->d_n_dropped) ? stats->d_n_dropped : (int32_t*)(base + L.ndrop);
+    if ((st = hip_status(launch_expert_choice(a, stream), "expert choice")) != MOE_OK) return st;
+    float* y = (float*)(base + L.y);
+    if ((st = do_grouped(desc, x, w, a.sorted_tokens, a.offsets, y, base, L, eb_of(stats), ee_of(stats), stream)) !=
+        MOE_OK)
+      return st;
+    EcCombineArgs c{};
+    c.y = y; c.crow = a.crow; c.w = a.w; c.ccount = a.ccount; c.T = desc->T; c.d = desc->d; c.E = desc->E;
+    c.routed_rows = (int)routed_rows_of(desc); c.has_shared = desc->has_shared;
+    c.act_f32 = desc->act_dtype == MOE_F32; c.out = out;
+    return hip_status(launch_ec_combine(c, stream), "expert-choice combine");
+  }
   const bool telemetry = stats && (stats->d_routed || stats->d_prob_mean || stats->d_lb_loss);
   float* logits = telemetry ? (float*)(base + L.logits) : nullptr;
   auto run_telemetry = [&]() -> moe_status {

@@ -125,3 +125,35 @@ def test_oracle_and_library_are_independent():
             if fn.endswith((".py", ".hip", ".h", ".cpp")):
                 src = open(os.path.join(dirpath, fn)).read()
                 assert "import oracle" not in src and "from oracle" not in src, fn
+
+
+def test_expert_choice_validation(ops):
+    EC = ops.ROUTING_EXPERT_CHOICE
+    d = ops.make_desc(4, 64, 8, 2, 64)
+    d.routing = 2
+    assert ops.LIB.moe_forward(ctypes.byref(d), None, None, None, None, None, 0, None) == ops.MOE_ERR_INVALID_ARG
+    d = ops.make_desc(8193, 64, 8, 2, 64)
+    d.routing = EC
+    assert ops.LIB.moe_forward(ctypes.byref(d), None, None, None, None, None, 0, None) == ops.MOE_ERR_UNSUPPORTED
+    d = ops.make_desc(4, 64, 8, 2, 64, path=ops.PATH_FUSED_DECODE)
+    d.routing = EC
+    assert ops.LIB.moe_forward(ctypes.byref(d), None, None, None, None, None, 0, None) == ops.MOE_ERR_UNSUPPORTED
+    d = ops.make_desc(40, 64, 8, 2, 64)
+    d.routing = EC
+    for call in (lambda: ops.LIB.moe_route(ctypes.byref(d), None, None, None, None, None, None, 0, None),
+                 lambda: ops.LIB.moe_permute(ctypes.byref(d), None, None, None, None, None, None, None, 0, None),
+                 lambda: ops.LIB.moe_combine(ctypes.byref(d), None, None, None, None, None)):
+        assert call() == ops.MOE_ERR_UNSUPPORTED
+        assert "moe_forward" in ops.last_error()
+
+
+def test_expert_choice_capacity_and_workspace(ops):
+    import oracle
+    for T, k, E, cf in [(40, 2, 8, 0.0), (40, 2, 8, 1.25), (7, 1, 4, 0.01), (10, 2, 4, 100.0)]:
+        d = ops.make_desc(T, 64, E, k, 64, capacity_factor=cf)
+        d.routing = ops.ROUTING_EXPERT_CHOICE
+        assert ops.LIB.moe_capacity(ctypes.byref(d)) == oracle.expert_choice_capacity(T, k, E, cf)
+    tc = ops.make_desc(40, 64, 8, 2, 64, capacity_factor=4.0)
+    ec = ops.make_desc(40, 64, 8, 2, 64, capacity_factor=4.0)
+    ec.routing = ops.ROUTING_EXPERT_CHOICE                 # C = 40: every expert takes every token
+    assert ops.LIB.moe_workspace_size(ctypes.byref(ec)) > ops.LIB.moe_workspace_size(ctypes.byref(tc))

@@ -380,3 +380,80 @@ def test_router_telemetry_parity(name):
     np.testing.assert_array_equal(loss2[:1].view(np.int32), loss[:1].view(np.int32))
     print(f"[telemetry] {name}: loss={loss[0]:.6f} oracle={tel['lb_loss']:.6f} "
           f"max_load={routed.max()} idle_experts={(routed == 0).sum()}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Expert-choice routing (moe_desc.routing = expert choice), against the oracle
+# ---------------------------------------------------------------------------
+EC_CASES = {
+    "ec_bf16": C["mixtral_prefill"].with_(T=300, d=256, f=512, seed=12),
+    "ec_bf16_renorm_off_shared": C["fine_grained"].with_(T=96, d=512, E=32, f=256, renormalize=False, seed=13),
+    "ec_fp8_cf": C["fp8_capacity"].with_(T=200, d=256, E=16, f=128, seed=14),
+    "ec_f32": C["tiny_f32"].with_(T=77, seed=15),
+    "ec_all_tokens": C["mixtral_prefill"].with_(T=40, d=256, f=256, E=4, k=2, capacity_factor=2.0, seed=16),
+    "ec_small_batch": C["mixtral_prefill"].with_(T=5, d=256, f=256, E=8, k=2, seed=17),
+    "mixtral_prefill": C["mixtral_prefill"],
+    "fine_grained": C["fine_grained"],
+}
+EC_SAMPLE = {"mixtral_prefill": 8, "fine_grained": 3}
+
+
+def _ec_boundary_is_clear(ref, k, cf):
+    """The C-th and (C+1)-th scores of every expert are distinct fp32 values whose
+    fp64 sources are far (relatively 1e-12) from an fp32 rounding midpoint, so a
+    different fp64 summation order cannot change any selection."""
+    probs = oracle.softmax_rows(ref["logits"])
+    s32 = ref["scores"]
+    T, E = s32.shape
+    Cap = ref["capacity"]
+    if Cap >= T:
+        return True
+    for e in range(E):
+        order = sorted(range(T), key=lambda t: (-float(s32[t, e]), t))
+        for t in order[Cap - 1:Cap + 1]:
+            p = probs[t, e]
+            lo = np.float32(p)
+            nb = np.nextafter(lo, np.float32(np.inf if p > lo else -np.inf))
+            mid = (float(lo) + float(nb)) / 2.0
+            if abs(p - mid) <= 1e-12 * abs(p):
+                return False
+    return True
+
+
+@pytest.mark.parametrize("name", list(EC_CASES))
+def test_expert_choice_parity(name):
+    cfg = EC_CASES[name]
+    print(f"[expert-choice] {name}", flush=True)
+    inp = device_inputs(cfg)
+    ov = OracleInputs(inp)
+    desc = ops.desc_from_cfg(cfg, routing=ops.ROUTING_EXPERT_CHOICE)
+    ws = ops.alloc_workspace(desc)
+    dt = torch.float32 if cfg.act == "f32" else torch.bfloat16
+    counts = torch.full((cfg.E,), -1, dtype=torch.int32, device="cuda")
+    nd = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+
+    def run():
+        out = torch.empty((cfg.T, cfg.d), dtype=dt, device="cuda")
+        st = ops.Stats(d_n_dropped=nd.data_ptr(), d_counts=counts.data_ptr())
+        taken = ops.forward(desc, inp["x"], ops.weights_struct(inp), out, ws, stats=st)
+        torch.cuda.synchronize()
+        return out, taken
+
+    out, taken = run()
+    assert taken == ops.PATH_GROUPED
+    n = EC_SAMPLE.get(name)
+    toks = None if n is None else np.sort(np.random.default_rng(1).choice(cfg.T, size=n, replace=False))
+    ref = oracle.expert_choice_forward(ov.x, ov.W_g, ov.bias, cfg.k, cfg.renormalize,
+                                       np.float32(cfg.capacity_factor), ov.expert, cfg.E, shared=ov.shared(),
+                                       tokens=toks)
+    assert _ec_boundary_is_clear(ref, cfg.k, cfg.capacity_factor)
+    Cap = ref["capacity"]
+    assert ops.capacity(desc) == Cap
+    assert counts.cpu().numpy().tolist() == [Cap] * cfg.E
+    unchosen = int(((ref["pos"] >= 0).sum(axis=1) == 0).sum())
+    assert int(nd.cpu()[0]) == unchosen
+    got = to64(out) if toks is None else to64(out)[toks]
+    e = assert_close(got, ref["out"], TOL[cfg.wdt], name)
+    out2, _ = run()
+    assert torch.equal(out2, out)                       # bitwise reproducible
+    print(f"[expert-choice] {name}: C={Cap} unchosen_tokens={unchosen} rel_err={e:.3e}", flush=True)
