@@ -448,7 +448,15 @@ __global__ __launch_bounds__(256) void topk_finalize_kernel(const double* __rest
   if (t >= T) return;     // whole wave leaves together; no block barrier follows
   for (int e = lane; e < E; e += 64) {
     double s = 0.0;
-    for (int z = 0; z < S; ++z) s += part[((size_t)z * T + t) * E + e];
+    int z = 0;
+    for (; z + 8 <= S; z += 8) {               // eight independent loads in flight, added in slice order
+      double v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = part[((size_t)(z + i) * T + t) * E + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += v[i];
+    }
+    for (; z < S; ++z) s += part[((size_t)z * T + t) * E + e];
     if (bias) s += (double)bias[e];
     const float l = (float)s;
     lg[wv][e] = l;
