@@ -41,6 +41,12 @@ SMALL = {
     "bf16_big_tiles_shared": C["fine_grained"].with_(T=700, d=256, E=4, k=2, f=256, seed=10),
     "fp8_big_tiles_shared": C["fp8_capacity"].with_(T=700, d=256, E=4, k=2, f=256, capacity_factor=0.0,
                                                      shared=True, seed=9),
+    # range edges: many experts and top-32, d = f = 64, E = 1023 (+ shared), one token on the grouped path
+    "bf16_k32_E64": C["mixtral_prefill"].with_(T=50, d=128, f=128, E=64, k=32, seed=18),
+    "bf16_d64_f64": C["mixtral_prefill"].with_(T=90, d=64, f=64, seed=19),
+    "bf16_E1023_shared": C["fine_grained"].with_(T=40, d=64, f=64, E=1023, k=8, seed=20),
+    "f32_T1": C["tiny_f32"].with_(T=1, seed=21),
+    "decode_T2_E300_k16": C["mixtral_decode"].with_(T=2, d=128, f=128, E=300, k=16, seed=22),
     "decode_T1": C["mixtral_decode"].with_(d=512, f=1024),
     "decode_T8": C["mixtral_decode_b8"].with_(d=512, f=1024),
     "decode_T5_shared_fp8": C["fp8_capacity_decode"].with_(T=5, d=256, E=16, f=256, shared=True),
@@ -67,7 +73,10 @@ ROUTE_CASES = {**{k: v for k, v in C.items()},
                "fine_grained_T9": C["fine_grained"].with_(T=9),
                "fine_grained_T5": C["fine_grained"].with_(T=5),
                "k_equals_E": C["mixtral_prefill"].with_(T=33, E=4, k=4),
-               "E_1": C["mixtral_prefill"].with_(T=17, E=1, k=1)}
+               "E_1": C["mixtral_prefill"].with_(T=17, E=1, k=1),
+               # edges of the accepted ranges: E = 1023 with top-32, d = 64
+               "E_1023_k32": C["fine_grained"].with_(T=70, d=128, E=1023, k=32),
+               "d_64": C["mixtral_prefill"].with_(T=100, d=64, E=16, k=4, seed=3)}
 
 
 @pytest.mark.parametrize("name", list(ROUTE_CASES))
