@@ -5,7 +5,7 @@ package.  The product library never does.
 """
 from .moe_oracle import (  # noqa: F401
     capacity, dequantize, expert_choice_capacity, expert_choice_forward, expert_choice_routing,
-    expert_ffn, forward, fp8_e4m3fn_decode, permute,
+    e4m3_encode, expert_ffn, forward, fp8_e4m3fn_decode, mx_dequantize, mx_quantize, mx_roundtrip, permute,
     router_logits, router_telemetry, routing_certificate, routing_weights, silu,
     softmax_rows, topk_select,
 )

@@ -36,7 +36,12 @@ design notes of the repository):
   * capacity C = max(1, ceil(cf * T * k / E)) with cf the fp32 capacity
     factor; priority is assignment order a = t*k + j; dropped assignments add
     nothing and the remaining weights are not renormalised again;
-  * the shared expert has weight 1, is not counted in k and has no capacity.
+  * the shared expert has weight 1, is not counted in k and has no capacity;
+  * block-scaled (MXFP8) layers quantise the token rows entering the experts
+    and the activated rows before the down projection, 32 values per scale
+    along the reduction axis, with the OCP MX shared-exponent rule and
+    round-to-nearest-even, saturating E4M3 elements; the activated rows are
+    rounded to fp32 before that decision (the GPU produces them in fp32).
 """
 from __future__ import annotations
 
@@ -175,11 +180,15 @@ def silu(z) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
-def expert_ffn(X, W_gate, W_up, W_down) -> np.ndarray:
+def expert_ffn(X, W_gate, W_up, W_down, quant_h=None) -> np.ndarray:
+    """SwiGLU expert; quant_h (optional) maps the activated rows H to the
+    values the down projection sees (block-scaled layers quantise them)."""
     X = _f64(X)
     G = X @ _f64(W_gate)
     U = X @ _f64(W_up)
     H = silu(G) * U
+    if quant_h is not None:
+        H = quant_h(H)
     return H @ _f64(W_down)
 
 
@@ -191,7 +200,7 @@ ExpertFn = Callable[[int], Sequence[np.ndarray]]
 
 def forward(x, W_g, bias, k: int, renormalize: bool, capacity_factor,
             expert: ExpertFn, E: int, shared: Optional[Sequence[np.ndarray]] = None,
-            tokens: Optional[Sequence[int]] = None) -> dict:
+            tokens: Optional[Sequence[int]] = None, quant_x=None, quant_h=None) -> dict:
     """Routed MoE SwiGLU layer.
 
     expert(e) returns (W_gate[d,f], W_up[d,f], W_down[f,d]) of expert e as
@@ -200,6 +209,9 @@ def forward(x, W_g, bias, k: int, renormalize: bool, capacity_factor,
     Routing and permutation are computed for every token; the expert FFN and
     the weighted sum only for `tokens` (all when None), so large layers can be
     checked on a sample.  out rows follow the order of `tokens`.
+    quant_x / quant_h (optional) map the token rows entering the experts and
+    the activated intermediate rows to the values a block-scaled layer sees;
+    routing always uses the unquantised x.
     """
     x = _f64(x)
     T = x.shape[0]
@@ -218,7 +230,8 @@ def forward(x, W_g, bias, k: int, renormalize: bool, capacity_factor,
         rows = [int(a) for a in sa[offs[e]:offs[e + 1]] if int(a) // k in want]
         if not rows:                    # experts without tokens do no work ([MIX])
             continue
-        Y = expert_ffn(x[[a // k for a in rows]], *expert(e))
+        X = x[[a // k for a in rows]]
+        Y = expert_ffn(X if quant_x is None else quant_x(X), *expert(e), quant_h=quant_h)
         for a, y in zip(rows, Y):
             y_assign[a] = y
 
@@ -231,7 +244,8 @@ def forward(x, W_g, bias, k: int, renormalize: bool, capacity_factor,
                 acc = acc + w[t, j] * y_assign[a]
         out[r] = acc
     if shared is not None:              # [DSK]: shared output + routed output
-        out = out + expert_ffn(x[toks], *shared)
+        X = x[toks]
+        out = out + expert_ffn(X if quant_x is None else quant_x(X), *shared, quant_h=quant_h)
     return dict(logits=logits, probs=probs, topk_idx=idx, topk_w=w, capacity=cap,
                 out=out, tokens=np.array(toks, dtype=np.int64), **perm)
 
@@ -373,3 +387,70 @@ def expert_choice_forward(x, W_g, bias, k: int, renormalize: bool, capacity_fact
     if shared is not None:
         out = out + expert_ffn(x[toks], *shared)
     return dict(logits=logits, out=out, tokens=np.array(toks, dtype=np.int64), **r)
+
+
+
+# ----------------------------------------------------------------------------
+# MXFP8 block scaling (OCP Microscaling): E4M3 elements, one E8M0 power-of-two
+# scale per 32 consecutive elements along the reduction dimension.  Page:
+# "Current Bug: CuTeDSLMoERunner produces wrong output", "Root Cause: scale_a
+# layout doesn't match expert_offsets" (a grouped MoE whose activations carry
+# per-token block scale factors, found per expert through its row offsets; its
+# NVFP4 blocks are the same idea for another chip).  The block size, element
+# format and shared-exponent rule are the OCP MX ones, which the gfx950 scaled
+# matrix instructions consume.
+# ----------------------------------------------------------------------------
+MX_BLOCK = 32
+E4M3_MAX = 448.0
+E4M3_EMAX = 8               # exponent of the largest normal: 448 = 1.75 * 2^8
+
+_E4M3_POS_CODES = np.arange(0x7F, dtype=np.uint8)             # +0 .. +448, values rise with the code
+_E4M3_POS_VALS = fp8_e4m3fn_decode(_E4M3_POS_CODES)
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Round to the nearest E4M3 value, ties to the even code (RNE); magnitudes
+    beyond 448 saturate to 448; the sign bit is the input's (so a negative
+    value that rounds to zero gives -0, code 0x80)."""
+    v = _f64(v)
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    i = np.clip(np.searchsorted(_E4M3_POS_VALS, a, side="left"), 1, len(_E4M3_POS_VALS) - 1)
+    lo, hi = _E4M3_POS_VALS[i - 1], _E4M3_POS_VALS[i]
+    d_lo, d_hi = a - lo, hi - a
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (i % 2 == 0)), i, i - 1)   # code i is even <=> i % 2 == 0
+    code = np.where(a == 0.0, 0, code).astype(np.uint8)
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def mx_quantize(v, block: int = MX_BLOCK):
+    """Per block of `block` consecutive values along the last axis: shared
+    exponent s = floor(log2(max |v|)) - 8, clamped to [-127, 127] (an all-zero
+    block takes -127); elements = e4m3_encode(v / 2^s).  Returns (codes uint8,
+    scales uint8 with code s + 127)."""
+    v = _f64(v)
+    K = v.shape[-1]
+    assert K % block == 0
+    b = v.reshape(-1, K // block, block)
+    amax = np.abs(b).max(axis=2)
+    e = np.full(amax.shape, -127, dtype=np.int64)
+    nz = amax > 0
+    e[nz] = np.frexp(amax[nz])[1] - 1 - E4M3_EMAX          # frexp: amax = m 2^x, m in [0.5, 1)
+    e = np.clip(e, -127, 127)
+    codes = e4m3_encode(b / np.exp2(e.astype(np.float64))[:, :, None])
+    return codes.reshape(v.shape), (e + 127).astype(np.uint8).reshape(v.shape[:-1] + (K // block,))
+
+
+def mx_dequantize(codes, scales, block: int = MX_BLOCK) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.uint8)
+    s = np.asarray(scales, dtype=np.uint8).astype(np.float64)
+    f = np.exp2(s - 127.0)
+    return fp8_e4m3fn_decode(c) * np.repeat(f, block, axis=-1)
+
+
+def mx_roundtrip(v, as_fp32: bool = False) -> np.ndarray:
+    """The values a block-scaled operand carries: quantise and decode.  With
+    as_fp32 the input is rounded to fp32 first (an fp32 producer decides)."""
+    v = _f64(v)
+    if as_fp32:
+        v = v.astype(np.float32).astype(np.float64)
+    return mx_dequantize(*mx_quantize(v))

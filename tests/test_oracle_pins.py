@@ -503,3 +503,141 @@ def test_expert_choice_relabelling_invariance():
     tp = np.random.default_rng(5).permutation(T)       # tokens relabelled (scores are distinct)
     r2 = oracle.expert_choice_forward(x[tp], Wg, None, k, True, 0.0, lambda e: ex[e], E)
     np.testing.assert_allclose(r2["out"], r0["out"][tp], rtol=1e-13, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# MXFP8 block scaling (E4M3 elements, one power-of-two scale per 32 values)
+# --------------------------------------------------------------------------
+_POS = [(c, float(torch.tensor([c], dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)))
+        for c in range(0x7F)]                      # the 127 non-negative finite codes, from torch's decoder
+
+
+def _brute_e4m3(v):
+    """Nearest non-negative E4M3 value by exhaustive search in exact rationals,
+    ties to the even code; magnitude clamped to 448 first, sign carried."""
+    a = min(abs(Fraction(v)), Fraction(448))
+    best = min(_POS, key=lambda cv: (abs(a - Fraction(cv[1])), cv[0] & 1))
+    return best[0] | (0x80 if math.copysign(1.0, v) < 0 else 0)
+
+
+def test_e4m3_encode_roundtrips_every_finite_code():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3_encode(vals)
+    assert np.array_equal(got, codes)              # includes -0 -> 0x80
+
+
+def test_e4m3_encode_ties_saturation_and_subnormals():
+    cases = [(1.0625, 0x38), (1.1875, 0x3A),       # midpoints: 1|1.125 -> 1 (even), 1.125|1.25 -> 1.25
+             (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02),   # subnormal midpoints
+             (-(2.0 ** -10), 0x80), (5 * 2.0 ** -10, 0x02), (7 * 2.0 ** -10, 0x04),
+             (448.0, 0x7E), (464.0, 0x7E), (1e30, 0x7E), (-1e30, 0xFE), (0.0, 0x00), (-0.0, 0x80),
+             (240.0, 0x77), (248.0, 0x78), (232.0, 0x76)]   # 224 (0x76) | 240 (0x77) | 256 (0x78)
+    for v, c in cases:
+        assert oracle.e4m3_encode(np.array([v]))[0] == c, v
+        assert _brute_e4m3(v) == c, v
+
+
+def test_e4m3_encode_brute_force():
+    rng = np.random.default_rng(7)
+    v = np.concatenate([rng.normal(0, 1, 300) * np.exp2(rng.integers(-12, 10, 300)),
+                        (rng.integers(-1200, 1200, 200) / 4.0) * 2.0 ** -9])   # many exact ties
+    got = oracle.e4m3_encode(v)
+    ref = np.array([_brute_e4m3(float(t)) for t in v], dtype=np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def test_e4m3_encode_matches_torch_cast_in_range():
+    rng = np.random.default_rng(8)
+    v = np.clip(rng.normal(0, 1, 50000) * np.exp2(rng.integers(-12, 9, 50000)), -448, 448).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_encode(v.astype(np.float64)), ref)
+
+
+def test_mx_scale_rule_zero_block_and_powers_of_two():
+    codes, sc = oracle.mx_quantize(np.zeros((2, 64)))
+    assert np.all(codes == 0) and np.all(sc == 0)
+    for p in (-130, -100, -3, 0, 5, 100):
+        b = np.zeros(32)
+        b[7] = -(2.0 ** p)
+        codes, sc = oracle.mx_quantize(b[None, :])
+        e = max(p - 8, -127)
+        assert sc[0, 0] == e + 127
+        if p - 8 >= -127:
+            assert codes[0, 7] == 0xF8                 # -256 = -(2^8): exponent field 15, mantissa 0
+    # the scaled block maximum lies in [256, 512) whenever the exponent is not clamped
+    rng = np.random.default_rng(9)
+    v = rng.normal(0, 1, (40, 32)) * np.exp2(rng.integers(-60, 60, (40, 1)))
+    _, sc = oracle.mx_quantize(v)
+    r = np.abs(v).max(axis=1) / np.exp2(sc[:, 0].astype(np.float64) - 127)
+    assert np.all((r >= 256) & (r < 512))
+
+
+def test_mx_quantize_blocks_are_independent_and_along_last_axis():
+    rng = np.random.default_rng(10)
+    v = rng.normal(0, 1, (3, 96)) * np.array([1e-3, 1.0, 1e3])[None, :].repeat(32, axis=1)
+    codes, sc = oracle.mx_quantize(v)
+    assert codes.shape == (3, 96) and sc.shape == (3, 3)
+    for j in range(3):
+        cj, sj = oracle.mx_quantize(v[:, 32 * j:32 * j + 32])
+        assert np.array_equal(cj, codes[:, 32 * j:32 * j + 32]) and np.array_equal(sj[:, 0], sc[:, j])
+
+
+def test_mx_roundtrip_exact_for_representable_blocks_and_error_bound():
+    rng = np.random.default_rng(11)
+    # blocks built from E4M3 values with the maximum in [256, 448], times 2^s: exact round trip
+    pos = np.array([v for _, v in _POS])
+    el = rng.choice(pos, (16, 32)) * rng.choice([-1.0, 1.0], (16, 32))
+    el[:, 0] = rng.choice(pos[(pos >= 256)], 16)
+    s = rng.integers(-20, 20, (16, 1)).astype(np.float64)
+    v = el * np.exp2(s)
+    np.testing.assert_array_equal(oracle.mx_roundtrip(v), v)
+    # general blocks: half an E4M3 step relative (2^-4) or half the smallest
+    # subnormal step times the scale; clamped values lose less than 64 * scale
+    v = rng.normal(0, 1, (200, 32)) * np.exp2(rng.integers(-30, 30, (200, 1)))
+    q = oracle.mx_roundtrip(v)
+    _, sc = oracle.mx_quantize(v)
+    scale = np.exp2(sc.astype(np.float64) - 127).repeat(32, axis=1)
+    err = np.abs(q - v)
+    clamped = np.abs(v) > 448 * scale
+    assert np.all(err[~clamped] <= np.maximum(2.0 ** -4 * np.abs(v), 2.0 ** -10 * scale)[~clamped])
+    assert np.all(err[clamped] < 64 * scale[clamped])
+    assert np.all(np.abs(q[clamped]) == 448 * scale[clamped])
+
+
+def test_mx_dequantize_values():
+    codes = np.array([[0x38] + [0xB8] + [0x01] + [0] * 29])   # 1, -1, 2^-9
+    for s in (0, 120, 127, 130, 254):
+        got = oracle.mx_dequantize(codes, np.array([[s]], dtype=np.uint8))
+        f = 2.0 ** (s - 127)
+        assert got[0, 0] == f and got[0, 1] == -f and got[0, 2] == 2.0 ** -9 * f and np.all(got[0, 3:] == 0)
+
+
+def test_quant_hooks_are_on_expert_inputs_and_activations():
+    T, d, E, k, f = 11, 16, 4, 2, 24
+    x, Wg, ex, sh = _layer(T, d, E, k, f, shared=True, seed=3)
+    base = oracle.forward(x, Wg, None, k, True, 0.0, lambda e: ex[e], E, sh)
+    ident = oracle.forward(x, Wg, None, k, True, 0.0, lambda e: ex[e], E, sh,
+                           quant_x=lambda X: X, quant_h=lambda H: H)
+    np.testing.assert_array_equal(ident["out"], base["out"])
+    # quant_x: experts see |x| while routing still uses x
+    r = oracle.forward(x, Wg, None, k, True, 0.0, lambda e: ex[e], E, sh, quant_x=np.abs)
+    assert np.array_equal(r["topk_idx"], base["topk_idx"])
+    ref = torch_dense_swiglu(np.abs(x), *sh).numpy()
+    for t in range(T):
+        for j in range(k):
+            ref[t] += base["topk_w"][t, j] * torch_dense_swiglu(np.abs(x[t:t + 1]), *ex[base["topk_idx"][t, j]]).numpy()[0]
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
+    # quant_h acts on silu(x Wg) * (x Wu), before the down projection
+    relu = lambda H: np.maximum(H, 0.0)
+    r = oracle.forward(x, Wg, None, k, True, 0.0, lambda e: ex[e], E, sh, quant_h=relu)
+
+    def dense_relu(xx, wg, wu, wd):
+        X = torch.from_numpy(xx)
+        H = torch.nn.functional.silu(X @ torch.from_numpy(wg)) * (X @ torch.from_numpy(wu))
+        return torch.relu(H) @ torch.from_numpy(wd)
+    ref = dense_relu(x, *sh).numpy()
+    for t in range(T):
+        for j in range(k):
+            ref[t] += base["topk_w"][t, j] * dense_relu(x[t:t + 1], *ex[base["topk_idx"][t, j]]).numpy()[0]
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
