@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0        # dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3
+FP8_PEAK_TFLOPS = 5000.0         # dense fp8 MFMA (also the MXFP8 scaled MFMA)
 LLC_BYTES = 256 << 20
 
 
@@ -72,7 +73,7 @@ class HipEvents:
 def algorithmic_work(cfg, counts, touched):
     """Bytes and flops the layer must move/do for this routing (per call)."""
     import synth
-    es = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.wdt]
+    es = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp8": 1}[cfg.wdt]
     ae = 4 if cfg.act == "f32" else 2
     wexp = synth.weight_bytes_per_expert(cfg)
     n_exp = touched + (1 if cfg.shared else 0)
@@ -121,9 +122,18 @@ def cpu_baseline(cfg, inp, budget_s=12.0, max_calls=2000):
     bias = None if inp["bias"] is None else to64(inp["bias"])
     cache = {}
 
+    cd = lambda t: t.contiguous().view(torch.uint8).cpu().numpy()
+    mx = cfg.wdt == "mxfp8"
+
+    def mx_triple(g, u, dn, sg, su, sd):     # output-major codes + block scales -> [in, out] values
+        return tuple(oracle.mx_dequantize(cd(w), sc.cpu().numpy()).T for w, sc in ((g, sg), (u, su), (dn, sd)))
+
     def expert(e):
         if e not in cache:
-            if cfg.wdt == "fp8":
+            if mx:
+                cache[e] = mx_triple(inp["W_gate"][e], inp["W_up"][e], inp["W_down"][e],
+                                     inp["mx_gate"][e], inp["mx_up"][e], inp["mx_down"][e])
+            elif cfg.wdt == "fp8":
                 cd = lambda t: t.contiguous().view(torch.uint8).cpu().numpy()
                 cache[e] = (oracle.dequantize(cd(inp["W_gate"][e]), inp["s_gate"][e].cpu().numpy(), 1),
                             oracle.dequantize(cd(inp["W_up"][e]), inp["s_up"][e].cpu().numpy(), 1),
@@ -133,11 +143,21 @@ def cpu_baseline(cfg, inp, budget_s=12.0, max_calls=2000):
         return cache[e]
 
     shared = None
-    if cfg.shared:
+    if cfg.shared and mx:
+        shared = mx_triple(inp["Ws_gate"], inp["Ws_up"], inp["Ws_down"],
+                           inp["mxs_gate"], inp["mxs_up"], inp["mxs_down"])
+    elif cfg.shared and cfg.wdt == "fp8":
+        shared = (oracle.dequantize(cd(inp["Ws_gate"]), inp["ss_gate"].cpu().numpy(), 1),
+                  oracle.dequantize(cd(inp["Ws_up"]), inp["ss_up"].cpu().numpy(), 1),
+                  oracle.dequantize(cd(inp["Ws_down"]), inp["ss_down"].cpu().numpy(), 1))
+    elif cfg.shared:
         shared = (to64(inp["Ws_gate"]), to64(inp["Ws_up"]), to64(inp["Ws_down"]))
+    hooks = {}
+    if mx:
+        hooks = {"quant_x": oracle.mx_roundtrip, "quant_h": lambda H: oracle.mx_roundtrip(H, as_fp32=True)}
     tb = min(cfg.T, 8)             # tokens per oracle call
     call = lambda t0: oracle.forward(x[t0:t0 + tb], W_g, bias, cfg.k, cfg.renormalize,
-                                     np.float32(cfg.capacity_factor), expert, cfg.E, shared=shared)
+                                     np.float32(cfg.capacity_factor), expert, cfg.E, shared=shared, **hooks)
     call(0)                        # untimed: widen the touched experts' weights once
     n = 0
     t_start = time.perf_counter()
@@ -258,13 +278,18 @@ def main():
         rows = int(cnt.sum()) + (cfg.T if cfg.shared else 0)
         kflops = 4 * rows * cfg.d * cfg.f
         n_exp = touched + (1 if cfg.shared else 0)
-        es = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.wdt]
-        scales = 2 * cfg.f * 4 if cfg.wdt == "fp8" else 0
-        ae = 4 if f32 else 2
-        kbytes = n_exp * (2 * cfg.d * cfg.f * es + scales) + cfg.T * cfg.d * ae + rows * cfg.f * ae
-        peak_f = FP32_PEAK_TFLOPS if f32 else BF16_PEAK_TFLOPS
+        mx = cfg.wdt == "mxfp8"
+        es = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp8": 1}[cfg.wdt]
+        scales = 2 * cfg.f * 4 if cfg.wdt == "fp8" else (2 * cfg.f * cfg.d // 32 if mx else 0)
+        if mx:      # x and H travel as codes plus one scale byte per 32 values
+            kbytes = n_exp * (2 * cfg.d * cfg.f + scales) + (cfg.T * cfg.d + rows * cfg.f) * 33 // 32
+        else:
+            ae = 4 if f32 else 2
+            kbytes = n_exp * (2 * cfg.d * cfg.f * es + scales) + cfg.T * cfg.d * ae + rows * cfg.f * ae
+        peak_f = FP32_PEAK_TFLOPS if f32 else (FP8_PEAK_TFLOPS if mx else BF16_PEAK_TFLOPS)
         ridge = peak_f * 1e12 / (HBM_PEAK_GBS * 1e9)
-        kname = "gemm_f32_kernel" if f32 else ("gemm_mfma_kernel" if cfg.wdt == "fp8" else "gemm_dl_kernel")
+        kname = ("gemm_f32_kernel" if f32 else "gemm_mx_kernel" if mx else
+                 "gemm_mfma_kernel" if cfg.wdt == "fp8" else "gemm_dl_kernel")
         t = kern_ms / 1e3 if have_k else None
         if kflops / kbytes >= ridge:
             bound, peak, unit = "mfma", peak_f, "TFLOP/s"
@@ -297,7 +322,7 @@ def main():
         "metric": "MoE-layer tokens/s; decode HBM GB/s, prefill MFMA TFLOP/s vs peak",
         "value": round(tokens_per_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "bf16 x fp8"}[cfg.wdt] if cfg.act == "bf16" else "f32",
+        "vs_baseline": None, "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "bf16 x fp8", "mxfp8": "mxfp8"}[cfg.wdt] if cfg.act == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "top_k": cfg.k, "f": cfg.f,
                    "act": cfg.act, "weights": cfg.wdt, "shared_expert": cfg.shared,

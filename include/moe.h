@@ -63,7 +63,14 @@ typedef enum {
   MOE_ERR_HIP = 4            /* a kernel launch failed                      */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;  /* FP8 = OCP e4m3fn */
+/* FP8 = OCP e4m3fn codes with per-output-channel fp32 scales.  MXFP8 = OCP
+ * Microscaling: e4m3fn codes with one E8M0 scale byte (value 2^(byte - 127))
+ * per 32 consecutive values along the reduction axis; the layer quantises its
+ * activations to the same format on the fly (page "Current Bug:
+ * CuTeDSLMoERunner produces wrong output", "Root Cause: scale_a layout doesn't
+ * match expert_offsets": a grouped MoE on block-scaled activations and
+ * weights, NVFP4 there). */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP8 = 3 } moe_dtype;
 
 typedef enum {
   MOE_PATH_AUTO = 0,         /* fused decode for T <= 8, grouped otherwise        */
@@ -97,7 +104,9 @@ typedef struct {
   int32_t renormalize;       /* 0 | 1                                            */
   float capacity_factor;     /* 0 => uncapped; else > 0 and finite               */
   int32_t act_dtype;         /* x, W_g, out: MOE_F32 | MOE_BF16                  */
-  int32_t w_dtype;           /* experts: F32 (act F32) | BF16 or FP8_E4M3 (act BF16) */
+  int32_t w_dtype;           /* experts: F32 (act F32) | BF16, FP8_E4M3 or MXFP8
+                                (act BF16; MXFP8 needs d, f multiples of 128 and
+                                runs on the grouped path at every T)           */
   int32_t has_shared;        /* 0 | 1: one always-on shared expert, weight 1     */
   int32_t path;              /* moe_path                                         */
   int32_t routing;           /* moe_routing (0 = token choice, the default)      */
@@ -118,6 +127,16 @@ typedef struct {
   const float* ss_gate;      /* FP8 shared scales [f], [f], [d] else NULL         */
   const float* ss_up;
   const float* ss_down;
+  /* MXFP8 only (else NULL).  The codes in W_gate, W_up, W_down (and the
+   * shared Ws_*) are then OUTPUT-major, K contiguous: W_gate, W_up [E, f, d],
+   * W_down [E, d, f] (a torch nn.Linear weight's own layout); these are their
+   * E8M0 scales, one byte per 32 consecutive K values: */
+  const uint8_t* mx_gate;    /* [E, f, d/32]                                       */
+  const uint8_t* mx_up;      /* [E, f, d/32]                                       */
+  const uint8_t* mx_down;    /* [E, d, f/32]                                       */
+  const uint8_t* mxs_gate;   /* shared expert [f, d/32], [f, d/32], [d, f/32]      */
+  const uint8_t* mxs_up;
+  const uint8_t* mxs_down;
 } moe_weights;
 
 /* Optional outputs of moe_forward.  The router telemetry fields follow
@@ -213,6 +232,23 @@ moe_status moe_combine(const moe_desc* desc, const float* y_sorted, const int32_
  * fields are token-choice statistics and are declined (MOE_ERR_UNSUPPORTED). */
 moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, void* out,
                        moe_stats* stats, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* OCP MXFP8 quantisation of a row-major [rows, cols] matrix along its rows:
+ * for every 32 consecutive values of a row, with m their largest magnitude,
+ * the scale exponent is s = floor(log2 m) - 8 clamped to [-127, 127] (an
+ * all-zero block takes -127), scales[b] = s + 127, and each value v becomes
+ * the e4m3fn code nearest to v / 2^s (ties to the even code, magnitudes above
+ * 448 saturated to 448, the sign kept for values that round to zero).  The
+ * layer applies exactly this to x (and, inside its kernels, to the SwiGLU
+ * activations) when w_dtype is MOE_MXFP8; weights may be prepared with it.
+ *   in      [rows, cols] device, in_dtype MOE_F32 | MOE_BF16, 16-byte aligned
+ *   codes   [rows, cols] uint8 out;  scales [rows, cols/32] uint8 out
+ *   cols    multiple of 32; rows >= 0 (0 enqueues nothing)
+ * Page: "Current Bug: CuTeDSLMoERunner produces wrong output", "Root Cause:
+ * scale_a layout doesn't match expert_offsets" (per-token activation scale
+ * factors of a block-scaled grouped MoE). */
+moe_status moe_quantize_mxfp8(const void* in, int32_t in_dtype, int64_t rows, int32_t cols,
+                              uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
 const char* moe_status_string(moe_status s);
 const char* moe_last_error(void);

@@ -359,10 +359,12 @@ def expert_choice_routing(logits32, k: int, capacity_factor, renormalize: bool) 
 
 def expert_choice_forward(x, W_g, bias, k: int, renormalize: bool, capacity_factor,
                           expert: ExpertFn, E: int, shared: Optional[Sequence[np.ndarray]] = None,
-                          tokens: Optional[Sequence[int]] = None) -> dict:
+                          tokens: Optional[Sequence[int]] = None, quant_x=None, quant_h=None) -> dict:
     """The layer with expert-choice routing: out[t] = sum over the experts that
     chose t, in ascending expert order, of weight[t, e] * FFN_e(x[t]), plus the
-    shared expert.  Routing for every token; FFN and sum for `tokens`."""
+    shared expert.  Routing for every token; FFN and sum for `tokens`.
+    quant_x / quant_h as in forward()."""
+    qx = (lambda X: X) if quant_x is None else quant_x
     x = _f64(x)
     T = x.shape[0]
     logits = router_logits(x, W_g, bias)
@@ -374,7 +376,7 @@ def expert_choice_forward(x, W_g, bias, k: int, renormalize: bool, capacity_fact
         rows = [int(t) for t in r["sorted_tokens"][r["offsets"][e]:r["offsets"][e + 1]] if int(t) in want]
         if not rows:
             continue
-        Y = expert_ffn(x[rows], *expert(e))
+        Y = expert_ffn(qx(x[rows]), *expert(e), quant_h=quant_h)
         for t, yy in zip(rows, Y):
             y[(t, e)] = yy
     out = np.zeros((len(toks), x.shape[1]), dtype=np.float64)
@@ -385,7 +387,7 @@ def expert_choice_forward(x, W_g, bias, k: int, renormalize: bool, capacity_fact
                 acc = acc + r["weight"][t, e] * y[(t, e)]
         out[i] = acc
     if shared is not None:
-        out = out + expert_ffn(x[toks], *shared)
+        out = out + expert_ffn(qx(x[toks]), *shared, quant_h=quant_h)
     return dict(logits=logits, out=out, tokens=np.array(toks, dtype=np.int64), **r)
 
 

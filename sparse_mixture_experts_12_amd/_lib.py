@@ -16,14 +16,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_LIB", os.path.join(_PKG, "libmoe.so"))
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP8 = range(4)
 PATH_AUTO, PATH_GROUPED, PATH_FUSED_DECODE = range(3)
 ROUTING_TOKEN_CHOICE, ROUTING_EXPERT_CHOICE = range(2)
-_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "mxfp8": MOE_MXFP8}
 
 # Every symbol the header declares.
 EXPORTS = ("moe_workspace_size", "moe_capacity", "moe_route", "moe_permute", "moe_grouped_ffn",
-           "moe_combine", "moe_forward", "moe_status_string", "moe_last_error")
+           "moe_combine", "moe_forward", "moe_quantize_mxfp8", "moe_status_string", "moe_last_error")
 
 
 class Desc(ctypes.Structure):
@@ -37,7 +37,8 @@ class Desc(ctypes.Structure):
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "W_g", "router_bias", "W_gate", "W_up", "W_down", "s_gate", "s_up", "s_down",
-        "Ws_gate", "Ws_up", "Ws_down", "ss_gate", "ss_up", "ss_down")]
+        "Ws_gate", "Ws_up", "Ws_down", "ss_gate", "ss_up", "ss_down",
+        "mx_gate", "mx_up", "mx_down", "mxs_gate", "mxs_up", "mxs_down")]
 
 
 class Stats(ctypes.Structure):
@@ -67,6 +68,7 @@ def _load():
         "moe_grouped_ffn": (ctypes.c_int, [DP, P, WP, P, P, P, P, S, P]),
         "moe_combine": (ctypes.c_int, [DP, P, P, P, P, P]),
         "moe_forward": (ctypes.c_int, [DP, P, WP, P, SP, P, S, P]),
+        "moe_quantize_mxfp8": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, P, P, P]),
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_last_error": (ctypes.c_char_p, []),
     }
@@ -117,7 +119,8 @@ def weights_struct(inp: dict) -> Weights:
     """inp: a dict with the keys of synth.make_inputs (device tensors)."""
     return Weights(*[_ptr(inp.get(n)) for n in (
         "W_g", "bias", "W_gate", "W_up", "W_down", "s_gate", "s_up", "s_down",
-        "Ws_gate", "Ws_up", "Ws_down", "ss_gate", "ss_up", "ss_down")])
+        "Ws_gate", "Ws_up", "Ws_down", "ss_gate", "ss_up", "ss_down",
+        "mx_gate", "mx_up", "mx_down", "mxs_gate", "mxs_up", "mxs_down")])
 
 
 def _stream(stream=None) -> int:
@@ -171,3 +174,12 @@ def forward(desc, x, weights: Weights, out, ws, stats: Stats | None = None, stre
     _check(LIB.moe_forward(ctypes.byref(desc), _ptr(x), ctypes.byref(weights), _ptr(out), ctypes.byref(st),
                            _ptr(ws), ws.numel(), _stream(stream)), "moe_forward")
     return st.path_taken
+
+
+def quantize_mxfp8(x, codes, scales, stream=None):
+    """x: [rows, cols] f32 or bf16 device tensor -> codes [rows, cols] and
+    scales [rows, cols / 32] (uint8 device tensors)."""
+    dt = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}[x.dtype]
+    rows = x.numel() // x.shape[-1] if x.dim() else 0
+    _check(LIB.moe_quantize_mxfp8(_ptr(x), dt, rows, x.shape[-1], _ptr(codes), _ptr(scales), _stream(stream)),
+           "moe_quantize_mxfp8")

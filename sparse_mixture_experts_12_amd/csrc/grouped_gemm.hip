@@ -37,6 +37,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "gemm_common.h"
 #include "kernels.h"
 
 namespace moe {
@@ -64,51 +65,6 @@ struct GemmParams {
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row ^ (row >> 3)) & 7); }
-
-// Map this work-group to (group, row0, rows, n-tile).  The schedule holds a
-// heavy segment (row tiles of more than BM / 2 rows) and a light segment; each
-// is split into 8 contiguous ranges of equal tile count, range x running on
-// XCD x (work-groups are dealt to the XCDs round-robin by id), heavy tiles
-// first.  Within the heavy segment a group's tiles are ordered column-major,
-// so neighbouring row tiles of one weight column tile share an XCD's L2.
-// Work-groups past both ranges return false.
-__device__ __forceinline__ bool decode_tile(const int32_t* sched, int maxQ, int E, int n_tiles, int* g, int* row0,
-                                            int* rows, int* nt) {
-  const int QH = sched[0], QL = sched[1];
-  const int totH = QH * n_tiles, totL = QL * n_tiles;
-  const int perH = (totH + 7) >> 3, perL = (totL + 7) >> 3;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7;
-  const int slot = bid >> 3;
-  const int32_t* hs = sched + kSchedHead;
-  if (slot < perH) {
-    const int logical = xcd * perH + slot;
-    if (logical >= totH) return false;
-    const int q0 = logical / n_tiles;
-    const int grp = hs[4 * q0 + 0];
-    const int first = hs[4 * q0 + 3];
-    const int mg = hs[4 * maxQ + grp];
-    const int local = logical - first * n_tiles;
-    const int j = local / mg;
-    const int q = first + (local - j * mg);
-    *g = grp;
-    *row0 = hs[4 * q + 1];
-    *rows = hs[4 * q + 2];
-    *nt = j;
-    return true;
-  }
-  const int s = slot - perH;
-  if (s >= perL) return false;
-  const int logical = xcd * perL + s;
-  if (logical >= totL) return false;
-  const int pt = logical / n_tiles;
-  const int32_t* ls = hs + 4 * maxQ + (E + 1) + 3 * pt;
-  *g = ls[0];
-  *row0 = ls[1];
-  *rows = ls[2];
-  *nt = logical - pt * n_tiles;
-  return true;
-}
 
 // 8 fp8 e4m3fn codes -> 8 bf16 (exact: at most 4 significant bits).
 __device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(u32x2_t q) {
@@ -394,44 +350,6 @@ __global__ __launch_bounds__(256, TileCfg<BM>::OCC) void gemm_mfma_kernel(GemmPa
 // are issued as soon as every wave has finished reading step k's stage, so
 // NST - 1 steps of MFMA work cover each load's latency.
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
-
-// s_waitcnt: vmcnt(N) alone, or vmcnt(N) together with lgkmcnt(0)
-template <int N> __device__ __forceinline__ void wait_vmem_le() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
-}
-template <int N> __device__ __forceinline__ void wait_vmem_le_lds0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
-}
-
-// A tile rows hold BK bf16 = CPR 16-byte chunks; the chunk index is XOR-ed
-// with a function of the row so that each 16-lane pass of a ds_read_b128
-// (rows r .. r + 15, one chunk each) hits distinct banks.  Both keys were
-// checked against the LDS bank-conflict counter on gfx950.
-template <int CPR> __device__ __forceinline__ int aswz(int r, int c) {
-  if constexpr (CPR == 8) return c ^ ((r ^ (r >> 3)) & 7);
-  else return c ^ ((r >> 2) & 3);
-}
-
-// Scheduling hint for one K sub-step: each MFMA is followed by its share of
-// the LDS fragment reads (DS) and of the global->LDS loads (VM), so the
-// memory instructions issue while the matrix core is busy.
-template <int NMF, int NDS, int NVM, int I = 0>
-__device__ __forceinline__ void sched_interleave() {
-  if constexpr (I < NMF) {
-    constexpr int DPM = (NDS + NMF - 1) / NMF, VPM = (NVM + NMF - 1) / NMF;
-    constexpr int D = (NDS - I * DPM) < DPM ? (NDS - I * DPM) : DPM;
-    constexpr int V = (NVM - I * VPM) < VPM ? (NVM - I * VPM) : VPM;
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (D > 0) __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
-    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x010, V, 0);
-    sched_interleave<NMF, NDS, NVM, I + 1>();
-  }
-}
-
 // One output tile of at most BMV rows: waves 2 x 2 (128 rows x 128 B-columns
 // each) for BMV = 256, 1 x 4 (BMV rows x 64 B-columns each) for 128 and 64.
 // The LDS stages are sized for BMMAX rows.
@@ -779,7 +697,7 @@ static int pick_bm(const GroupedArgs& a) {
   return avg >= 256 ? 256 : 64;
 }
 
-static int max_row_tiles(int routed_rows, int T, int E, int has_shared, int BM) {
+int grouped_max_row_tiles(int routed_rows, int T, int E, int has_shared, int BM) {
   int q = routed_rows / BM + (routed_rows < E ? routed_rows : E);
   if (has_shared) q += (T + BM - 1) / BM;
   return q;
@@ -787,19 +705,20 @@ static int max_row_tiles(int routed_rows, int T, int E, int has_shared, int BM) 
 
 size_t grouped_sched_ints(int routed_rows, int T, int E, int has_shared) {
   // enough for the smallest tile height used (64 rows)
-  return kSchedHead + 4 * (size_t)max_row_tiles(routed_rows, T, E, has_shared, 64) + 4 * (size_t)(E + 1) + 16;
+  return kSchedHead + 4 * (size_t)grouped_max_row_tiles(routed_rows, T, E, has_shared, 64) + 4 * (size_t)(E + 1) + 16;
 }
 
 // Work-groups: per XCD, enough slots for both schedule segments.  With
 // QH + QL <= maxQ row tiles, ceil(QH n / 8) + ceil(QL n / 8) <= ceil(maxQ n / 8) + 2.
-static inline int grid_for(int maxQ, int n_tiles) {
+int grouped_grid(int maxQ, int n_tiles) {
   const long per = ((long)maxQ * n_tiles + 7) / 8 + 2;
   return (int)(8 * per);
 }
 
 hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
+  if (a.wkind == W_MX) return launch_grouped_ffn_mx(a, s);
   const int BM = pick_bm(a);
-  const int maxQ = max_row_tiles(a.routed_rows, a.T, a.E, a.has_shared, BM);
+  const int maxQ = grouped_max_row_tiles(a.routed_rows, a.T, a.E, a.has_shared, BM);
   const int shared_rows = a.has_shared ? a.T : 0;
   const int shared_row0 = a.routed_rows;
   hipError_t err = launch_tile_schedule(a.offsets, a.E, BM, shared_rows, shared_row0, maxQ, a.sched, s);
@@ -818,10 +737,10 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
     p.K = a.d; p.N = a.f;
     p.h_out = (float*)a.h;
     if (a.ev_begin || a.ev_end)
-      hipExtLaunchKernelGGL(gemm_f32_kernel<true>, dim3(grid_for(maxQ, (a.f + 63) / 64)), dim3(256), 0, s,
+      hipExtLaunchKernelGGL(gemm_f32_kernel<true>, dim3(grouped_grid(maxQ, (a.f + 63) / 64)), dim3(256), 0, s,
                             a.ev_begin, a.ev_end, 0, p);
     else
-      gemm_f32_kernel<true><<<grid_for(maxQ, (a.f + 63) / 64), 256, 0, s>>>(p);
+      gemm_f32_kernel<true><<<grouped_grid(maxQ, (a.f + 63) / 64), 256, 0, s>>>(p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // down
     GemmParamsF32 q = p;
@@ -830,7 +749,7 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
     q.W1 = nullptr; q.Ws1 = nullptr;
     q.K = a.f; q.N = a.d;
     q.y_out = a.y;
-    gemm_f32_kernel<false><<<grid_for(maxQ, (a.d + 63) / 64), 256, 0, s>>>(q);
+    gemm_f32_kernel<false><<<grouped_grid(maxQ, (a.d + 63) / 64), 256, 0, s>>>(q);
     return hipGetLastError();
   }
 
@@ -844,7 +763,7 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   p.s0 = a.w.sg; p.s1 = a.w.su; p.ss0 = a.w.ssg; p.ss1 = a.w.ssu;
   p.K = a.d; p.N = a.f;
   p.h_out = (bf16_t*)a.h;
-  const int gu_grid = grid_for(maxQ, (a.f + 127) / 128);
+  const int gu_grid = grouped_grid(maxQ, (a.f + 127) / 128);
   // the gate/up GEMM is the dominant kernel: optional events stamp its dispatch
   auto launch_gu = [&](auto kern) {
     if (a.ev_begin || a.ev_end)
@@ -867,7 +786,7 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   q.s0 = a.w.sd; q.s1 = nullptr; q.ss0 = a.w.ssd; q.ss1 = nullptr;
   q.K = a.f; q.N = a.d;
   q.y_out = a.y;
-  const int dn_grid = grid_for(maxQ, (a.d + 255) / 256);
+  const int dn_grid = grouped_grid(maxQ, (a.d + 255) / 256);
   if (a.wkind == W_FP8) {
     if (BM == 256) gemm_mfma_kernel<W_FP8, false, 256><<<dn_grid, 256, 0, s>>>(q);
     else gemm_mfma_kernel<W_FP8, false, 64><<<dn_grid, 256, 0, s>>>(q);

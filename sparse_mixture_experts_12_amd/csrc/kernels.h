@@ -43,9 +43,13 @@ struct ExpertWeights {
   const float *sg, *su, *sd;            // fp8 scales or nullptr
   const void *Wsg, *Wsu, *Wsd;          // shared expert or nullptr
   const float *ssg, *ssu, *ssd;
+  // MXFP8: codes are output-major ([E,f,d], [E,f,d], [E,d,f]) and these are
+  // their E8M0 block scales ([E,f,d/32], [E,f,d/32], [E,d,f/32]; shared [N, K/32])
+  const uint8_t *mxg, *mxu, *mxd;
+  const uint8_t *mxsg, *mxsu, *mxsd;
 };
 
-enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
+enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_MX = 3 };
 
 struct GroupedArgs {
   const void* x;                 // [T, d] act
@@ -61,11 +65,19 @@ struct GroupedArgs {
   float* y;                      // [routed_rows (+T), d] fp32
   void* h;                       // [routed_rows (+T), f] bf16 (or fp32 for act f32)
   int32_t* sched;                // schedule scratch
-  int32_t* sched2;               // second schedule (down GEMM uses its own BM)
+  uint8_t* mx_xq;                // W_MX: x codes [T, d] (scratch)
+  uint8_t* mx_xs;                // W_MX: x scales [T, d/32]
+  uint8_t* mx_hs;                // W_MX: H scales [rows, f/32]; h holds the H codes
   hipEvent_t ev_begin, ev_end;
 };
 size_t grouped_sched_ints(int routed_rows, int T, int E, int has_shared);
+int grouped_max_row_tiles(int routed_rows, int T, int E, int has_shared, int BM);
+int grouped_grid(int maxQ, int n_tiles);
 hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s);
+hipError_t launch_grouped_ffn_mx(const GroupedArgs& a, hipStream_t s);
+// OCP MXFP8 quantisation of rows x cols values (cols % 32 == 0) along rows
+hipError_t launch_mx_quantize(const void* in, bool in_f32, long rows, int cols, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s);
 
 struct DecodeArgs {
   const void* x;                 // [T, d] act

@@ -25,6 +25,8 @@ moe_status fail(moe_status s, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+size_t routed_rows_of(const moe_desc* d);
+
 moe_status check_desc(const moe_desc* d) {
   if (!d) return fail(MOE_ERR_INVALID_ARG, "desc is NULL");
   if (d->T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%d < 0", d->T);
@@ -41,9 +43,23 @@ moe_status check_desc(const moe_desc* d) {
   if ((long long)d->T * d->top_k > (1LL << 24)) return fail(MOE_ERR_INVALID_ARG, "T*top_k too large");
   const int a = d->act_dtype, w = d->w_dtype;
   if (a != MOE_F32 && a != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "bad act_dtype %d", a);
-  if (w != MOE_F32 && w != MOE_BF16 && w != MOE_FP8_E4M3) return fail(MOE_ERR_INVALID_ARG, "bad w_dtype %d", w);
-  const bool ok = (a == MOE_F32 && w == MOE_F32) || (a == MOE_BF16 && (w == MOE_BF16 || w == MOE_FP8_E4M3));
+  if (w != MOE_F32 && w != MOE_BF16 && w != MOE_FP8_E4M3 && w != MOE_MXFP8)
+    return fail(MOE_ERR_INVALID_ARG, "bad w_dtype %d", w);
+  const bool ok = (a == MOE_F32 && w == MOE_F32) ||
+                  (a == MOE_BF16 && (w == MOE_BF16 || w == MOE_FP8_E4M3 || w == MOE_MXFP8));
   if (!ok) return fail(MOE_ERR_UNSUPPORTED, "dtype pair act=%d w=%d not supported", a, w);
+  if (w == MOE_MXFP8) {
+    if (d->d % 128 || d->f % 128)
+      return fail(MOE_ERR_UNSUPPORTED, "MXFP8 layers take d and f multiples of 128 (d=%d f=%d)", d->d, d->f);
+    if (d->path == MOE_PATH_FUSED_DECODE) return fail(MOE_ERR_UNSUPPORTED, "MXFP8 layers run on the grouped path");
+  }
+  if (d->routing != MOE_ROUTING_TOKEN_CHOICE && d->routing != MOE_ROUTING_EXPERT_CHOICE)
+    return fail(MOE_ERR_INVALID_ARG, "bad routing %d", d->routing);
+  if (w == MOE_MXFP8) {   // the block-scaled kernels address code rows with 32-bit offsets
+    const double rows = (double)routed_rows_of(d) + (double)d->T;
+    if ((double)d->T * d->d >= 2147483648.0 || rows * d->f >= 2147483648.0)
+      return fail(MOE_ERR_UNSUPPORTED, "MXFP8 layer too large (T*d and rows*f must stay below 2^31)");
+  }
   if (d->routing != MOE_ROUTING_TOKEN_CHOICE && d->routing != MOE_ROUTING_EXPERT_CHOICE)
     return fail(MOE_ERR_INVALID_ARG, "bad routing %d", d->routing);
   if (d->routing == MOE_ROUTING_EXPERT_CHOICE) {
@@ -83,10 +99,16 @@ moe_status check_expert_weights(const moe_desc* d, const moe_weights* w) {
   REQ(w->W_up, "W_up");
   REQ(w->W_down, "W_down");
   const bool fp8 = d->w_dtype == MOE_FP8_E4M3;
+  const bool mx = d->w_dtype == MOE_MXFP8;
   if (fp8) {
     REQ(w->s_gate, "s_gate");
     REQ(w->s_up, "s_up");
     REQ(w->s_down, "s_down");
+  }
+  if (mx) {
+    REQ(w->mx_gate, "mx_gate");
+    REQ(w->mx_up, "mx_up");
+    REQ(w->mx_down, "mx_down");
   }
   if (d->has_shared) {
     REQ(w->Ws_gate, "Ws_gate");
@@ -96,6 +118,11 @@ moe_status check_expert_weights(const moe_desc* d, const moe_weights* w) {
       REQ(w->ss_gate, "ss_gate");
       REQ(w->ss_up, "ss_up");
       REQ(w->ss_down, "ss_down");
+    }
+    if (mx) {
+      REQ(w->mxs_gate, "mxs_gate");
+      REQ(w->mxs_up, "mxs_up");
+      REQ(w->mxs_down, "mxs_down");
     }
   }
   return MOE_OK;
@@ -126,7 +153,7 @@ int capacity_of(const moe_desc* d) {
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t part, idx, w, plan, counts, offsets, sorted, inv, ndrop, rank, sched, h, y, partial, logits, tel;
+  size_t part, idx, w, plan, counts, offsets, sorted, inv, ndrop, rank, sched, h, hs, xq, xs, y, partial, logits, tel;
   size_t ec_scores, ec_pos, ec_w, ec_crow, ec_count, ec_sorted, ec_offsets, total;
 };
 
@@ -157,7 +184,11 @@ Layout layout_of(const moe_desc* d) {
   L.ndrop = take(4);
   L.rank = take(T * k * 4);
   L.sched = take(grouped_sched_ints((int)routed, d->T, d->E, d->has_shared) * 4);
-  L.h = take(rows * d->f * (d->act_dtype == MOE_F32 ? 4 : 2));
+  const bool mx = d->w_dtype == MOE_MXFP8;
+  L.h = take(rows * d->f * (mx ? 1 : d->act_dtype == MOE_F32 ? 4 : 2));   // MXFP8: H codes
+  L.hs = take(mx ? rows * (d->f / 32) : 0);                                  // MXFP8: H scales
+  L.xq = take(mx ? T * d->d : 0);                                            // MXFP8: x codes
+  L.xs = take(mx ? T * (d->d / 32) : 0);                                     // MXFP8: x scales
   L.y = take(rows * d->d * 4);
   L.partial = decode_capable(d) ? take(decode_partial_bytes(d->T, d->d, d->E, d->top_k, d->f, d->has_shared,
                                                            d->w_dtype == MOE_FP8_E4M3 ? W_FP8 : W_BF16))
@@ -195,11 +226,13 @@ ExpertWeights expert_weights(const moe_weights* w) {
   x.sg = w->s_gate; x.su = w->s_up; x.sd = w->s_down;
   x.Wsg = w->Ws_gate; x.Wsu = w->Ws_up; x.Wsd = w->Ws_down;
   x.ssg = w->ss_gate; x.ssu = w->ss_up; x.ssd = w->ss_down;
+  x.mxg = w->mx_gate; x.mxu = w->mx_up; x.mxd = w->mx_down;
+  x.mxsg = w->mxs_gate; x.mxsu = w->mxs_up; x.mxsd = w->mxs_down;
   return x;
 }
 
 int wkind_of(const moe_desc* d) {
-  return d->w_dtype == MOE_FP8_E4M3 ? W_FP8 : d->w_dtype == MOE_BF16 ? W_BF16 : W_F32;
+  return d->w_dtype == MOE_MXFP8 ? W_MX : d->w_dtype == MOE_FP8_E4M3 ? W_FP8 : d->w_dtype == MOE_BF16 ? W_BF16 : W_F32;
 }
 
 hipEvent_t eb_of(const moe_stats* st) { return st ? st->ev_begin : nullptr; }
@@ -237,6 +270,9 @@ moe_status do_grouped(const moe_desc* d, const void* x, const moe_weights* w, co
   a.act_f32 = d->act_dtype == MOE_F32;
   a.y = y;
   a.h = ws + L.h;
+  a.mx_hs = (uint8_t*)(ws + L.hs);
+  a.mx_xq = (uint8_t*)(ws + L.xq);
+  a.mx_xs = (uint8_t*)(ws + L.xs);
   a.sched = (int32_t*)(ws + L.sched);
   a.ev_begin = eb; a.ev_end = ee;
   return hip_status(launch_grouped_ffn(a, s), "grouped_ffn");
@@ -433,6 +469,20 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w
   float* y = (float*)(base + L.y);
   if ((st = do_grouped(desc, x, w, sorted, offsets, y, base, L, eb, ee, stream)) != MOE_OK) return st;
   return do_combine(desc, y, inv, tw, out, stream);
+}
+
+moe_status moe_quantize_mxfp8(const void* in, int32_t in_dtype, int64_t rows, int32_t cols, uint8_t* codes,
+                              uint8_t* scales, hipStream_t stream) {
+  if (in_dtype != MOE_F32 && in_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "bad in_dtype %d", in_dtype);
+  if (rows < 0) return fail(MOE_ERR_INVALID_ARG, "rows=%lld < 0", (long long)rows);
+  if (cols < 32 || cols % 32) return fail(MOE_ERR_INVALID_ARG, "cols=%d must be a positive multiple of 32", cols);
+  if (rows > (1LL << 40) / cols) return fail(MOE_ERR_INVALID_ARG, "rows*cols too large");
+  if (rows == 0) return MOE_OK;
+  REQ(in, "in");
+  REQ(codes, "codes");
+  if (!scales) return fail(MOE_ERR_INVALID_ARG, "scales is NULL");
+  return hip_status(launch_mx_quantize(in, in_dtype == MOE_F32, (long)rows, cols, codes, scales, stream),
+                    "mx quantize");
 }
 
 const char* moe_status_string(moe_status s) {

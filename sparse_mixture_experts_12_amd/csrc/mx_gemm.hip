@@ -1,0 +1,455 @@
+// Block-scaled (MXFP8) grouped SwiGLU expert FFN on gfx950.
+//
+// Pages: "Current Bug: CuTeDSLMoERunner produces wrong output", "Root Cause:
+// scale_a layout doesn't match expert_offsets" (a grouped MoE whose
+// activations carry per-token block scale factors, addressed per expert
+// through its row offsets; NVFP4 on another chip); "MoE Model Architectures",
+// Mixtral "Expert FFN" (w2(silu(w1 x) * w3 x)) and "Sparse MoE Block" (only
+// experts with tokens run).
+//
+// Format (OCP Microscaling MXFP8): E4M3 codes, one E8M0 power-of-two scale
+// per 32 consecutive values along the reduction axis.  A block with largest
+// magnitude m gets the exponent s = floor(log2 m) - 8 (clamped to
+// [-127, 127], an all-zero block -127); its elements are v / 2^s rounded to
+// nearest even E4M3, magnitudes above 448 saturated.
+//
+//   quantise: x rows [T, d] (bf16 or fp32) -> codes [T, d], scales [T, d/32]
+//   gate/up:  H[r, n] = silu(A[r] . Wg[n]) * (A[r] . Wu[n]) in fp32, A[r] the
+//             quantised x row of the token owning permuted row r; H is then
+//             quantised per 32 columns in the epilogue -> codes + scales
+//   down:     Y[r, n] = H[r] . Wd[n]  (fp32)
+// Weights are stored output-major with K contiguous ([E, N, K] codes,
+// [E, N, K/32] scales), so both operands are K-contiguous rows: no
+// transposing reads.  The product runs on v_mfma_scale_f32_32x32x64_f8f6f4,
+// which applies both operands' block scales inside the matrix core.
+//
+// Tiles: BM (256, with 128- and 64-row bodies for an expert's short last
+// tile) permuted rows x 256 B-rows (the gate/up GEMM takes 128 gate and the
+// same 128 up columns), 4 waves, 128 K per LDS stage, two stages.  A and B
+// tiles move global -> LDS directly (16 bytes per lane) with the LDS swizzle
+// applied on the source side; the block scales (4 bytes per row per stage)
+// go to registers with plain loads issued beside them.
+//
+// MFMA operand layout (32x32x64, 8 bit): lane l = (i, h), i = l % 32 the row
+// (A) or column (B), h = l / 32; its 32 bytes hold K = 16 h .. 16 h + 15 and
+// 32 + 16 h .. 32 + 16 h + 15 of the 64; its scale byte (selected by the
+// instruction's op_sel from a 32-bit register) is that of K block h.
+#include <hip/hip_ext.h>
+
+#include <type_traits>
+
+#include "common.h"
+#include "gemm_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kMxBK = 128;    // K per LDS stage (bytes of codes)
+constexpr int kMxNST = 2;     // LDS stages
+
+struct MxParams {
+  const uint8_t* aq;             // DUAL: x codes [T, K]; !DUAL: H codes [rows, K]
+  const uint8_t* as;             // matching scales [., K / 32]
+  const int32_t* sorted_assign;  // DUAL: permuted row -> assignment
+  const uint8_t* W0;             // codes [E, N, K]: gate (DUAL) or down
+  const uint8_t* W1;             // up (DUAL)
+  const uint8_t* S0;             // scales [E, N, K / 32]
+  const uint8_t* S1;
+  const uint8_t* Ws0;            // shared expert [N, K], [N, K / 32]
+  const uint8_t* Ws1;
+  const uint8_t* Ss0;
+  const uint8_t* Ss1;
+  const int32_t* sched;
+  int maxQ;
+  int k, E, K, N;
+  int shared_row0;
+  uint8_t* hq_out;               // DUAL: H codes [rows, N]
+  uint8_t* hs_out;               // DUAL: H scales [rows, N / 32]
+  float* y_out;                  // !DUAL: [rows, N]
+};
+
+// Largest |v| over the 32 lanes of each half-wave (lanes 0..31, 32..63):
+// quad swap, quad pair swap, rotations by 4 and 8 inside each 16-lane row,
+// then the two rows of the half exchanged.
+__device__ __forceinline__ float half_wave_absmax(float v) {
+  float m = fabsf(v);
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x124, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x128, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x401F)));
+  return m;
+}
+
+// Biased E8M0 scale code of a block whose largest magnitude is m (fp32):
+// floor(log2 m) - 8 + 127 = exponent field - 8, at least 0 (zero and
+// subnormal blocks take -127).
+__device__ __forceinline__ int mx_scale_code(float m) { return max((int)((__float_as_uint(m) >> 23) & 0xff) - 8, 0); }
+
+// v / 2^(code - 127) rounded to E4M3 (RNE, saturated at 448).  The factor
+// 2^(127 - code) is a normal fp32 for every code this kernel produces
+// (code <= 246), so the scaling is exact.
+__device__ __forceinline__ float mx_scaled(float v, int code) {
+  const float f = __uint_as_float((uint32_t)(254 - code) << 23);
+  return fminf(fmaxf(v * f, -448.f), 448.f);
+}
+__device__ __forceinline__ uint32_t e4m3_byte(float q) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q, q, 0, false) & 0xffu;
+}
+
+// ---------------------------------------------------------------------------
+// Quantiser: 4 lanes per 32-value block, 8 values per lane.
+// ---------------------------------------------------------------------------
+template <typename TIn>
+__global__ __launch_bounds__(256) void mx_quantize_kernel(const TIn* __restrict__ in, long nblk,
+                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  const long blk = gid >> 2;
+  const bool ok = blk < nblk;
+  const long e0 = (ok ? gid : 0) * 8;
+  float v[8];
+  if constexpr (std::is_same<TIn, float>::value) {
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(in + e0);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(in + e0 + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      v[4 + i] = b[i];
+    }
+  } else {
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(in + e0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16lo(w[i]);
+      v[2 * i + 1] = bf16hi(w[i]);
+    }
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+  const int code = mx_scale_code(m);
+  u32x2_t o;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    int p = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(v[4 * w], code), mx_scaled(v[4 * w + 1], code), 0, false);
+    p = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(v[4 * w + 2], code), mx_scaled(v[4 * w + 3], code), p, true);
+    o[w] = (uint32_t)p;
+  }
+  if (ok) {
+    *reinterpret_cast<u32x2_t*>(codes + e0) = o;
+    if ((gid & 3) == 0) scales[blk] = (uint8_t)code;
+  }
+}
+
+hipError_t launch_mx_quantize(const void* in, bool in_f32, long rows, int cols, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s) {
+  const long nblk = rows * (long)(cols / 32);
+  if (nblk == 0) return hipSuccess;
+  const long threads = nblk * 4;
+  const unsigned grid = (unsigned)((threads + 255) / 256);
+  if (in_f32)
+    mx_quantize_kernel<float><<<grid, 256, 0, s>>>((const float*)in, nblk, codes, scales);
+  else
+    mx_quantize_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)in, nblk, codes, scales);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM tile
+// ---------------------------------------------------------------------------
+// One output tile of at most BMV rows: waves 2 x 2 (128 rows x 128 B-rows
+// each) for BMV = 256, 1 x 4 (BMV rows x 64 B-rows each) for 128 and 64.
+// LDS stage: 256 A rows then 256 B rows of 128 code bytes each (16-byte chunk
+// c of row r at chunk position aswz<8>(r, c): conflict-free 16-lane passes of
+// ds_read_b128 down a column of rows), then the stage's scale dwords (4 K
+// blocks) of the 256 A rows and of the 256 B rows.
+template <bool DUAL, int BMV>
+__device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int rows, int nt, uint8_t* L0,
+                                        uint8_t* L1) {
+  constexpr int BK = kMxBK;
+  constexpr int WM = (BMV >= 256) ? 2 : 1, WN = 4 / WM;
+  constexpr int NMAT = DUAL ? 2 : 1;
+  constexpr int BN_MAT = DUAL ? 128 : 256;
+  constexpr int NI_MAT = BN_MAT / WN / 32;
+  constexpr int NI = NI_MAT * NMAT;
+  constexpr int MI = BMV / WM / 32;
+  constexpr int WROWS = BMV / WM;
+  constexpr int A_LD = BMV / 8 / 4;                // 1 KB (8-row) A blocks per wave per stage
+  constexpr int B_LD = 256 / 8 / 4;                // 1 KB B blocks per wave per stage
+  constexpr int LDS_B = 256 * BK;                  // B codes
+  constexpr int LDS_SA = 512 * BK;                 // A scale dwords [256]
+  constexpr int LDS_SB = LDS_SA + 1024;            // B scale dwords [256]
+  constexpr int NMF = MI * NI;                      // MFMAs per 64-K sub-step
+  constexpr int NDS = 2 * (MI + NI) + MI + NI;      // LDS reads per sub-step (codes, scales)
+  constexpr int NVM = A_LD + B_LD + 2;              // global -> LDS loads per stage
+  static_assert(BK == 128 && kMxNST == 2 && A_LD >= 1, "tile configuration");
+  const int KS = p.K >> 5;                         // scale bytes per row
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const int l32 = lane & 31;
+  const int lhi = lane >> 5;
+  const int n0 = nt * BN_MAT;
+  const bool shared = (g == p.E);
+
+  // A row (x row of the owning token, or the H row) of tile row r; rows past
+  // the valid ones read the tile's first row (never stored).
+  auto a_row = [&](int r) -> uint32_t {
+    const int grow = row0 + (r < rows ? r : 0);
+    if (DUAL) return (uint32_t)(shared ? (grow - p.shared_row0) : (p.sorted_assign[grow] / p.k));
+    return (uint32_t)grow;
+  };
+  // B rows: wave w's 64 LDS B rows 64 w .. 64 w + 63 are one matrix's
+  // consecutive output columns from cb(w); a block past N (the down GEMM's
+  // last, half-used tile) re-reads the block 128 columns before (never stored).
+  const size_t gN = shared ? 0 : (size_t)g * p.N;
+  auto b_first = [&](int w, int* mat) -> int {
+    int c;
+    if (DUAL) {
+      *mat = w >> 1;
+      c = n0 + 64 * (w & 1);
+    } else {
+      *mat = 0;
+      c = n0 + 64 * w;
+    }
+    return c < p.N ? c : c - 128;
+  };
+  auto b_codes = [&](int mat) -> const uint8_t* { return shared ? (mat ? p.Ws1 : p.Ws0) : (mat ? p.W1 : p.W0); };
+  auto b_scales = [&](int mat) -> const uint8_t* { return shared ? (mat ? p.Ss1 : p.Ss0) : (mat ? p.S1 : p.S0); };
+
+  // ---- global -> LDS sources.  Code block b (A: b = wave + 4 i, B: b =
+  // B_LD wave + j) holds rows 8 b .. 8 b + 7; this lane fills row
+  // r = 8 b + lane / 8, LDS chunk lane % 8, i.e. global chunk
+  // aswz<8>(r, lane % 8) = (lane % 8) ^ (lane / 8) ^ (b % 8).
+  // Scales: this lane fills dword 64 wave + lane of each scale array. ----
+  // Every source is a wave-uniform base plus a 32-bit per-lane offset, so the
+  // loads take the scalar-base addressing form (one VGPR per address).
+  const int cx = (lane & 7) ^ (lane >> 3);
+  uint32_t aoff[A_LD];                              // byte offset of this lane's A chunk
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i)
+    aoff[i] = a_row(8 * (wave + 4 * i) + (lane >> 3)) * (uint32_t)p.K + ((cx ^ ((wave + 4 * i) & 7)) << 4);
+  int bmat;
+  const int bc = b_first(wave, &bmat);
+  const uint8_t* bbase = b_codes(bmat) + (gN + bc) * (size_t)p.K;
+  uint32_t boff[B_LD];
+#pragma unroll
+  for (int j = 0; j < B_LD; ++j)
+    boff[j] = (uint32_t)(8 * j + (lane >> 3)) * (uint32_t)p.K + ((cx ^ ((B_LD * wave + j) & 7)) << 4);
+  const uint32_t asoff = a_row(64 * wave + lane) * (uint32_t)KS;
+  const uint8_t* bsbase = b_scales(bmat) + (gN + bc) * (size_t)KS;
+  const uint32_t bsoff = (uint32_t)lane * (uint32_t)KS;
+
+  auto issue = [&](uint8_t* L, int k0) {
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(p.aq + (aoff[i] + (uint32_t)k0)),
+                                       (lds_ptr_t)(L + (wave + 4 * i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < B_LD; ++j)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(bbase + (boff[j] + (uint32_t)k0)),
+                                       (lds_ptr_t)(L + LDS_B + (B_LD * wave + j) * 1024), 16, 0,
+                                       (BMV <= 128) ? 2 : 0);   // light tiles stream their weights
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(p.as + (asoff + (uint32_t)(k0 >> 5))),
+                                     (lds_ptr_t)(L + LDS_SA + wave * 256), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(bsbase + (bsoff + (uint32_t)(k0 >> 5))),
+                                     (lds_ptr_t)(L + LDS_SB + wave * 256), 4, 0, 0);
+  };
+
+  f32x16_t acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+
+  // B row (LDS) of fragment ni for this lane
+  auto b_lrow = [&](int ni) -> int {
+    if (DUAL) return (ni / NI_MAT) * 128 + wn * (128 / WN) + (ni % NI_MAT) * 32 + l32;
+    return wn * (256 / WN) + ni * 32 + l32;
+  };
+  // Fragments of 64-K sub-step ks, plus the stage's scale dwords shifted so
+  // that byte 2 ks is this lane's K block (h) of the sub-step.
+  auto frags = [&](const uint8_t* L, int ks, i32x8_t* af, i32x8_t* bfr, uint32_t* sa, uint32_t* sb) {
+    const int c0 = 4 * ks + lhi, c1 = c0 + 2;
+    const int sh = 8 * lhi;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int row = wm * WROWS + mi * 32 + l32;
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(L + row * BK + aswz<8>(row, c0) * 16);
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(L + row * BK + aswz<8>(row, c1) * 16);
+      af[mi] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      sa[mi] = *reinterpret_cast<const uint32_t*>(L + LDS_SA + row * 4) >> sh;
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int j = b_lrow(ni);
+      const uint8_t* Lb = L + LDS_B + j * BK;
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(Lb + aswz<8>(j, c0) * 16);
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(Lb + aswz<8>(j, c1) * 16);
+      bfr[ni] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      sb[ni] = *reinterpret_cast<const uint32_t*>(L + LDS_SB + j * 4) >> sh;
+    }
+  };
+  auto mfmas = [&](const i32x8_t* af, const i32x8_t* bfr, const uint32_t* sa, const uint32_t* sb, auto KS_) {
+    constexpr int ops = 2 * decltype(KS_)::value;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bfr[ni], acc[mi][ni], 0, 0, ops,
+                                                                      (int)sa[mi], ops, (int)sb[ni]);
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  // Pipeline over the two 64-K sub-steps of each stage (as in the bf16
+  // kernel): sub-step 1's fragments are read while sub-step 0 multiplies; the
+  // stage's last MFMAs run after the barrier that publishes the next stage and
+  // cover the first fragment reads of the next stage.  The stage just read is
+  // then refilled two steps ahead (past the end: the last stage again, never
+  // read), so every wave issues the same loads per step and the vmcnt
+  // thresholds are exact.
+  const int nK = p.K / BK;
+  i32x8_t fa0[MI], fb0[NI], fa1[MI], fb1[NI];
+  uint32_t sa0[MI], sb0[NI], sa1[MI], sb1[NI];
+  issue(L0, 0);
+  issue(L1, min(1, nK - 1) * BK);
+  wait_vmem_le<NVM>();
+  __builtin_amdgcn_s_barrier();
+  frags(L0, 0, fa0, fb0, sa0, sb0);
+
+  auto step = [&](uint8_t* L, const uint8_t* Ln, int k) {
+    frags(L, 1, fa1, fb1, sa1, sb1);
+    mfmas(fa0, fb0, sa0, sb0, I0{});
+    sched_interleave<NMF, NDS, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmem_le_lds0<0>();
+    __builtin_amdgcn_s_barrier();
+    issue(L, min(k + 2, nK - 1) * BK);
+    frags(Ln, 0, fa0, fb0, sa0, sb0);
+    mfmas(fa1, fb1, sa1, sb1, I1{});
+    sched_interleave<NMF, NDS, NVM>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int k = 0;
+  for (; k + 2 <= nK; k += 2) {
+    step(L0, L1, k);
+    step(L1, L0, k + 1);
+  }
+  if (k < nK) step(L0, L1, k);
+  wait_vmem_le<0>();
+
+  // ---- epilogue ----
+  if constexpr (DUAL) {
+    // H = silu(gate) * up in fp32, quantised per row and 32 columns: a
+    // fragment's 32 columns of one row live in the 32 lanes of a half-wave.
+    const int KSo = p.N >> 5;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+      for (int nl = 0; nl < NI_MAT; ++nl) {
+        const int cb0 = n0 + wn * (BN_MAT / WN) + nl * 32;     // first H column of the fragment
+        uint32_t q[16];
+        int code[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float h = silu_f(acc[mi][nl][v]) * acc[mi][nl + NI_MAT][v];
+          code[v] = mx_scale_code(half_wave_absmax(h));
+          q[v] = e4m3_byte(mx_scaled(h, code[v]));
+        }
+        if (cb0 < p.N) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = wm * WROWS + mi * 32 + (v >> 2) * 8 + lhi * 4 + (v & 3);
+            if (r < rows) {
+              const size_t orow = (size_t)(row0 + r);
+              p.hq_out[orow * p.N + cb0 + l32] = (uint8_t)q[v];
+              if (l32 == 0) p.hs_out[orow * KSo + (cb0 >> 5)] = (uint8_t)code[v];
+            }
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int col = n0 + wn * (256 / WN) + ni * 32 + l32;
+        if (col >= p.N) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * WROWS + mi * 32 + (v >> 2) * 8 + lhi * 4 + (v & 3);
+          if (r < rows) p.y_out[(size_t)(row0 + r) * p.N + col] = acc[mi][ni][v];
+        }
+      }
+    }
+  }
+}
+
+template <bool DUAL>
+__global__ __launch_bounds__(256, 1) void gemm_mx_kernel(MxParams p) {
+  constexpr int LDS_S = 512 * kMxBK + 2048;
+  __shared__ __attribute__((aligned(1024))) uint8_t L0[LDS_S];
+  __shared__ __attribute__((aligned(1024))) uint8_t L1[LDS_S];
+  constexpr int BN_MAT = DUAL ? 128 : 256;
+  const int n_tiles = (p.N + BN_MAT - 1) / BN_MAT;
+  int g, row0, rows, nt;
+  if (!decode_tile(p.sched, p.maxQ, p.E, n_tiles, &g, &row0, &rows, &nt)) return;
+  if (rows > 128) mx_tile<DUAL, 256>(p, g, row0, rows, nt, L0, L1);
+  else if (rows > 64) mx_tile<DUAL, 128>(p, g, row0, rows, nt, L0, L1);
+  else mx_tile<DUAL, 64>(p, g, row0, rows, nt, L0, L1);
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+hipError_t launch_grouped_ffn_mx(const GroupedArgs& a, hipStream_t s) {
+  uint8_t* xq = a.mx_xq;
+  uint8_t* xs = a.mx_xs;
+  uint8_t* hq = (uint8_t*)a.h;
+  uint8_t* hs = a.mx_hs;
+  const int BM = 256;
+  const int maxQ = grouped_max_row_tiles(a.routed_rows, a.T, a.E, a.has_shared, BM);
+  hipError_t err = launch_tile_schedule(a.offsets, a.E, BM, a.has_shared ? a.T : 0, a.routed_rows, maxQ, a.sched, s);
+  if (err != hipSuccess) return err;
+  if ((err = launch_mx_quantize(a.x, a.act_f32, a.T, a.d, xq, xs, s)) != hipSuccess) return err;
+
+  MxParams p{};
+  p.aq = xq; p.as = xs;
+  p.sorted_assign = a.sorted_assign;
+  p.W0 = (const uint8_t*)a.w.Wg; p.W1 = (const uint8_t*)a.w.Wu;
+  p.S0 = a.w.mxg; p.S1 = a.w.mxu;
+  p.Ws0 = (const uint8_t*)a.w.Wsg; p.Ws1 = (const uint8_t*)a.w.Wsu;
+  p.Ss0 = a.w.mxsg; p.Ss1 = a.w.mxsu;
+  p.sched = a.sched; p.maxQ = maxQ;
+  p.k = a.assign_div; p.E = a.E; p.K = a.d; p.N = a.f; p.shared_row0 = a.routed_rows;
+  p.hq_out = hq; p.hs_out = hs;
+  const int gu_grid = grouped_grid(maxQ, a.f / 128);
+  if (a.ev_begin || a.ev_end)
+    hipExtLaunchKernelGGL(gemm_mx_kernel<true>, dim3(gu_grid), dim3(256), 0, s, a.ev_begin, a.ev_end, 0, p);
+  else
+    gemm_mx_kernel<true><<<gu_grid, 256, 0, s>>>(p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  MxParams q{};
+  q.aq = hq; q.as = hs;
+  q.W0 = (const uint8_t*)a.w.Wd; q.S0 = a.w.mxd;
+  q.Ws0 = (const uint8_t*)a.w.Wsd; q.Ss0 = a.w.mxsd;
+  q.sched = a.sched; q.maxQ = maxQ;
+  q.k = a.assign_div; q.E = a.E; q.K = a.f; q.N = a.d; q.shared_row0 = a.routed_rows;
+  q.y_out = a.y;
+  gemm_mx_kernel<false><<<grouped_grid(maxQ, (a.d + 255) / 256), 256, 0, s>>>(q);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -15,6 +15,12 @@ name and the expert id, so one expert can be regenerated on its own):
            weights in log space), fp32
   fp8      per output channel c: s[c] = max|w[:, c]| / 448, q = RNE(w / s)
            as float8_e4m3fn (the largest finite e4m3fn value is 448).
+  mxfp8    OCP Microscaling weights, stored output-major (W_gate, W_up
+           [E, f, d], W_down [E, d, f]) with one E8M0 scale byte per 32
+           consecutive input-dimension values (mx_gate, mx_up [E, f, d/32],
+           mx_down [E, d, f/32]): s = floor(log2 max|block|) - 8 clamped to
+           [-127, 127], q = RNE(w / 2^s) clamped to +-448 as float8_e4m3fn,
+           byte = s + 127.  The layer receives these codes as given.
 """
 from __future__ import annotations
 
@@ -37,7 +43,7 @@ class MoEConfig:
     k: int
     f: int
     act: str = "bf16"          # activation / router dtype: "f32" | "bf16"
-    wdt: str = "bf16"          # expert weight dtype: "f32" | "bf16" | "fp8"
+    wdt: str = "bf16"          # expert weight dtype: "f32" | "bf16" | "fp8" | "mxfp8"
     renormalize: bool = True
     capacity_factor: float = 0.0   # 0 => uncapped
     shared: bool = False       # one always-on shared expert (same f)
@@ -69,6 +75,11 @@ CONFIGS = {
                               wdt="fp8", capacity_factor=1.25),
     "fp8_capacity_decode": MoEConfig("fp8_capacity_decode", T=1, d=2048, E=128, k=8, f=768,
                                      wdt="fp8", capacity_factor=1.25),
+    # block-scaled (MXFP8) variants of the two prefill-shaped layers
+    "mixtral_prefill_mxfp8": MoEConfig("mixtral_prefill_mxfp8", T=4096, d=4096, E=8, k=2, f=14336,
+                                       wdt="mxfp8"),
+    "fine_grained_mxfp8": MoEConfig("fine_grained_mxfp8", T=2048, d=7168, E=256, k=8, f=2048,
+                                    wdt="mxfp8", shared=True, bias="zipf"),
 }
 
 
@@ -105,6 +116,18 @@ def quantize_fp8_per_channel(w32: torch.Tensor, channel_dim: int):
     return q, s.to(torch.float32)
 
 
+def quantize_mxfp8_rows(w32: torch.Tensor):
+    """w32 fp32 [..., K], K % 32 == 0 -> (codes float8_e4m3fn [..., K],
+    scales uint8 [..., K / 32]), blocks of 32 along the last axis."""
+    K = w32.shape[-1]
+    b = w32.reshape(*w32.shape[:-1], K // 32, 32)
+    amax = b.abs().amax(dim=-1)
+    _, ex = torch.frexp(amax)                       # amax = m 2^ex, m in [0.5, 1)
+    s = torch.where(amax > 0, ex - 9, torch.full_like(ex, -127)).clamp(-127, 127)
+    q = torch.clamp(torch.ldexp(b, (-s).unsqueeze(-1).to(b.dtype)), -FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
+    return q.reshape(w32.shape), (s + 127).to(torch.uint8)
+
+
 def _expert_mats(cfg: MoEConfig, tag: str, e: int, device):
     wg = _normal((cfg.d, cfg.f), cfg.w_std, tensor_seed(cfg.seed, tag + "gate", e), device)
     wu = _normal((cfg.d, cfg.f), cfg.w_std, tensor_seed(cfg.seed, tag + "up", e), device)
@@ -138,10 +161,13 @@ def make_inputs(cfg: MoEConfig, device="cpu", router_only: bool = False) -> dict
         return out
 
     def alloc(shape):
-        dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[cfg.wdt]
+        dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn,
+              "mxfp8": torch.float8_e4m3fn}[cfg.wdt]
         return torch.empty(shape, dtype=dt, device=dev)
 
     E, d, f = cfg.E, cfg.d, cfg.f
+    if cfg.wdt == "mxfp8":
+        return _make_mx_weights(cfg, dev, out)
     Wg, Wu, Wd = alloc((E, d, f)), alloc((E, d, f)), alloc((E, f, d))
     fp8 = cfg.wdt == "fp8"
     if fp8:
@@ -173,9 +199,35 @@ def make_inputs(cfg: MoEConfig, device="cpu", router_only: bool = False) -> dict
     return out
 
 
+def _make_mx_weights(cfg: MoEConfig, dev, out: dict) -> dict:
+    E, d, f = cfg.E, cfg.d, cfg.f
+    q8 = lambda *shape: torch.empty(shape, dtype=torch.float8_e4m3fn, device=dev)
+    u8 = lambda *shape: torch.empty(shape, dtype=torch.uint8, device=dev)
+    Wg, Wu, Wd = q8(E, f, d), q8(E, f, d), q8(E, d, f)
+    sg, su, sd = u8(E, f, d // 32), u8(E, f, d // 32), u8(E, d, f // 32)
+    for e in range(E):
+        wg, wu, wd = _expert_mats(cfg, "", e, dev)
+        Wg[e], sg[e] = quantize_mxfp8_rows(wg.t().contiguous())
+        Wu[e], su[e] = quantize_mxfp8_rows(wu.t().contiguous())
+        Wd[e], sd[e] = quantize_mxfp8_rows(wd.t().contiguous())
+        del wg, wu, wd
+    out.update(W_gate=Wg, W_up=Wu, W_down=Wd, mx_gate=sg, mx_up=su, mx_down=sd,
+               s_gate=None, s_up=None, s_down=None)
+    out.update(Ws_gate=None, Ws_up=None, Ws_down=None, ss_gate=None, ss_up=None, ss_down=None,
+               mxs_gate=None, mxs_up=None, mxs_down=None)
+    if cfg.shared:
+        wg, wu, wd = _expert_mats(cfg, "shared_", 0, dev)
+        out["Ws_gate"], out["mxs_gate"] = quantize_mxfp8_rows(wg.t().contiguous())
+        out["Ws_up"], out["mxs_up"] = quantize_mxfp8_rows(wu.t().contiguous())
+        out["Ws_down"], out["mxs_down"] = quantize_mxfp8_rows(wd.t().contiguous())
+    return out
+
+
 def weight_bytes_per_expert(cfg: MoEConfig) -> int:
-    es = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.wdt]
+    es = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp8": 1}[cfg.wdt]
     b = 3 * cfg.d * cfg.f * es
     if cfg.wdt == "fp8":
         b += (2 * cfg.f + cfg.d) * 4
+    if cfg.wdt == "mxfp8":
+        b += 3 * cfg.d * cfg.f // 32
     return b

@@ -9,7 +9,7 @@ import oracle
 import synth
 
 # max|gpu - oracle| / max|oracle| bounds per weight type (fp32, bf16, fp8)
-TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "mxfp8": 6e-2}
 
 
 def to64(t: torch.Tensor) -> np.ndarray:
@@ -31,6 +31,8 @@ class OracleInputs:
         self.bias = None if inp["bias"] is None else to64(inp["bias"])
 
     def _triple(self, g, u, dn, sg, su, sd):
+        if self.cfg.wdt == "mxfp8":         # output-major codes + block scales -> [in, out] values
+            return tuple(oracle.mx_dequantize(codes(w), sc.cpu().numpy()).T for w, sc in ((g, sg), (u, su), (dn, sd)))
         if self.cfg.wdt == "fp8":
             return (oracle.dequantize(codes(g), sg.cpu().numpy(), 1),
                     oracle.dequantize(codes(u), su.cpu().numpy(), 1),
@@ -39,6 +41,9 @@ class OracleInputs:
 
     def expert(self, e: int):
         i = self.inp
+        if self.cfg.wdt == "mxfp8":
+            return self._triple(i["W_gate"][e], i["W_up"][e], i["W_down"][e],
+                                i["mx_gate"][e], i["mx_up"][e], i["mx_down"][e])
         if self.cfg.wdt == "fp8":
             return self._triple(i["W_gate"][e], i["W_up"][e], i["W_down"][e],
                                 i["s_gate"][e], i["s_up"][e], i["s_down"][e])
@@ -48,12 +53,28 @@ class OracleInputs:
         i = self.inp
         if not self.cfg.shared:
             return None
+        if self.cfg.wdt == "mxfp8":
+            return self._triple(i["Ws_gate"], i["Ws_up"], i["Ws_down"], i["mxs_gate"], i["mxs_up"], i["mxs_down"])
         return self._triple(i["Ws_gate"], i["Ws_up"], i["Ws_down"], i["ss_gate"], i["ss_up"], i["ss_down"])
+
+    def quant_hooks(self) -> dict:
+        """Block-scaled layers: expert inputs and the fp32 SwiGLU activations
+        are MXFP8-quantised before their products."""
+        if self.cfg.wdt != "mxfp8":
+            return {}
+        return {"quant_x": oracle.mx_roundtrip, "quant_h": lambda H: oracle.mx_roundtrip(H, as_fp32=True)}
+
+    def ffn(self, X, e=None):
+        """One expert's (or, e None, the shared expert's) FFN of rows X."""
+        h = self.quant_hooks()
+        qx = h.get("quant_x")
+        return oracle.expert_ffn(X if qx is None else qx(X), *(self.shared() if e is None else self.expert(e)),
+                                 quant_h=h.get("quant_h"))
 
     def forward(self, tokens=None):
         c = self.cfg
         return oracle.forward(self.x, self.W_g, self.bias, c.k, c.renormalize, np.float32(c.capacity_factor),
-                              self.expert, c.E, shared=self.shared(), tokens=tokens)
+                              self.expert, c.E, shared=self.shared(), tokens=tokens, **self.quant_hooks())
 
     def certificate(self):
         return oracle.routing_certificate(self.x, self.W_g, self.bias, self.cfg.k)

@@ -21,7 +21,7 @@ def ops():
 def header_functions():
     src = open(os.path.join(ROOT, "include", "moe.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_header_symbol(ops):
@@ -157,3 +157,48 @@ def test_expert_choice_capacity_and_workspace(ops):
     ec = ops.make_desc(40, 64, 8, 2, 64, capacity_factor=4.0)
     ec.routing = ops.ROUTING_EXPERT_CHOICE                 # C = 40: every expert takes every token
     assert ops.LIB.moe_workspace_size(ctypes.byref(ec)) > ops.LIB.moe_workspace_size(ctypes.byref(tc))
+
+
+def test_mxfp8_validation(ops):
+    def fwd(d):
+        return ops.LIB.moe_forward(ctypes.byref(d), None, None, None, None, None, 0, None)
+    d = ops.make_desc(40, 192, 8, 2, 256, wdt="mxfp8")           # d % 128 != 0
+    assert fwd(d) == ops.MOE_ERR_UNSUPPORTED and "multiples of 128" in ops.last_error()
+    d = ops.make_desc(4, 256, 8, 2, 256, wdt="mxfp8", path=ops.PATH_FUSED_DECODE)
+    assert fwd(d) == ops.MOE_ERR_UNSUPPORTED and "grouped" in ops.last_error()
+    d = ops.make_desc(4, 256, 8, 2, 256, act="f32", wdt="mxfp8")
+    assert fwd(d) == ops.MOE_ERR_UNSUPPORTED
+    d = ops.make_desc(1 << 20, 4096, 8, 2, 14336, wdt="mxfp8")   # 32-bit row offsets would overflow
+    assert fwd(d) == ops.MOE_ERR_UNSUPPORTED and "2^31" in ops.last_error()
+    # a valid MXFP8 descriptor sizes a workspace holding x and H codes + scales
+    d = ops.make_desc(100, 256, 8, 2, 384, wdt="mxfp8")
+    b = ops.make_desc(100, 256, 8, 2, 384, wdt="bf16")
+    assert ops.workspace_size(d) > 0 and ops.workspace_size(b) > 0
+    # weights without their block scales are rejected before any HIP call
+    w = ops.Weights(W_g=16, W_gate=16, W_up=16, W_down=16)
+    r = ops.LIB.moe_forward(ctypes.byref(d), ctypes.c_void_p(16), ctypes.byref(w), ctypes.c_void_p(16), None,
+                            ctypes.c_void_p(256), 1 << 40, None)
+    assert r == ops.MOE_ERR_INVALID_ARG and "mx_gate" in ops.last_error()
+
+
+def test_mx_quantize_argument_checks(ops):
+    q = ctypes.c_void_p(16)
+    assert ops.LIB.moe_quantize_mxfp8(q, ops.MOE_BF16, 4, 48, q, q, None) == ops.MOE_ERR_INVALID_ARG
+    assert ops.LIB.moe_quantize_mxfp8(q, ops.MOE_FP8_E4M3, 4, 64, q, q, None) == ops.MOE_ERR_INVALID_ARG
+    assert ops.LIB.moe_quantize_mxfp8(q, ops.MOE_BF16, -1, 64, q, q, None) == ops.MOE_ERR_INVALID_ARG
+    assert ops.LIB.moe_quantize_mxfp8(None, ops.MOE_BF16, 0, 64, None, None, None) == ops.MOE_OK
+    assert ops.LIB.moe_quantize_mxfp8(None, ops.MOE_BF16, 3, 64, q, q, None) == ops.MOE_ERR_INVALID_ARG
+
+
+def test_synth_mx_weights_follow_the_oracle_quantiser():
+    """The input recipe's weight quantiser (torch) and the oracle's (numpy)
+    are separate implementations of the same OCP rule; they must agree."""
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(5)
+    w = (rng.normal(0, 0.02, (64, 256)) * np.exp2(rng.integers(-8, 8, (64, 1)))).astype(np.float32)
+    w[3, :32] = 0.0
+    q, s = synth.quantize_mxfp8_rows(torch.from_numpy(w))
+    rq, rs = oracle.mx_quantize(w.astype(np.float64))
+    np.testing.assert_array_equal(s.numpy(), rs)
+    np.testing.assert_array_equal(q.view(torch.uint8).numpy(), rq)

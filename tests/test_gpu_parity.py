@@ -51,6 +51,17 @@ SMALL = {
     "decode_T8": C["mixtral_decode_b8"].with_(d=512, f=1024),
     "decode_T5_shared_fp8": C["fp8_capacity_decode"].with_(T=5, d=256, E=16, f=256, shared=True),
     "decode_T3_fp8_cap": C["fp8_capacity_decode"].with_(T=3, d=256, E=8, f=128, k=4, capacity_factor=0.5),
+    # block-scaled (MXFP8) layers: 64/128/256-row tile bodies, ragged tails, the
+    # shared expert, capacity drops, a half-used last down-projection tile (d % 256 = 128)
+    "mx_prefill": C["mixtral_prefill_mxfp8"].with_(T=300, d=512, f=1024),
+    "mx_ragged": C["mixtral_prefill_mxfp8"].with_(T=133, d=256, f=768, seed=5),
+    "mx_big_tiles": C["mixtral_prefill_mxfp8"].with_(T=760, d=384, f=512, E=4, k=2, seed=3),
+    "mx_finegrained_shared": C["fine_grained_mxfp8"].with_(T=96, d=512, E=32, f=256),
+    "mx_big_tiles_shared": C["fine_grained_mxfp8"].with_(T=700, d=256, E=4, k=2, f=384, seed=10),
+    "mx_capacity": C["mixtral_prefill_mxfp8"].with_(T=200, d=256, E=16, k=8, f=128, capacity_factor=1.25,
+                                                     seed=23),
+    "mx_T1": C["mixtral_prefill_mxfp8"].with_(T=1, d=256, f=256, seed=24),
+    "mx_long_k": C["mixtral_prefill_mxfp8"].with_(T=70, d=2048, f=1280, E=4, k=1, seed=25),
 }
 
 
@@ -191,7 +202,8 @@ def test_permute_all_to_one_expert_with_capacity():
 @pytest.mark.parametrize("name", ["tiny_f32", "tiny_f32_ragged", "bf16_prefill", "bf16_prefill_ragged",
                                   "bf16_finegrained_shared", "fp8_capacity", "fp8_capacity_tight",
                                   "bf16_one_expert", "bf16_big_tiles", "bf16_big_tiles_mid",
-                                  "bf16_big_tiles_shared", "fp8_big_tiles_shared"])
+                                  "bf16_big_tiles_shared", "fp8_big_tiles_shared", "mx_prefill", "mx_big_tiles",
+                                  "mx_big_tiles_shared", "mx_capacity"])
 def test_grouped_ffn_parity(name):
     cfg = SMALL[name]
     print(f"[grouped_ffn] {name}", flush=True)
@@ -216,11 +228,11 @@ def test_grouped_ffn_parity(name):
         lo, hi = ref["offsets"][e], ref["offsets"][e + 1]
         if hi > lo:
             toks = ref["sorted_assign"][lo:hi] // k
-            yref[lo:hi] = oracle.expert_ffn(ov.x[toks], *ov.expert(e))
+            yref[lo:hi] = ov.ffn(ov.x[toks], e)
     assert_close(yg[:kept], yref, TOL[cfg.wdt], f"{name} routed rows")
     assert np.isnan(yg[kept:T * k]).all(), "rows past the kept ones must stay untouched"
     if cfg.shared:
-        assert_close(yg[T * k:], oracle.expert_ffn(ov.x, *ov.shared()), TOL[cfg.wdt], f"{name} shared rows")
+        assert_close(yg[T * k:], ov.ffn(ov.x), TOL[cfg.wdt], f"{name} shared rows")
 
 
 # ---------------------------------------------------------------------------
@@ -268,9 +280,11 @@ def test_forward_parity_small(name):
     st = ops.Stats(d_n_dropped=dev_nd.data_ptr(), d_counts=dev_counts.data_ptr())
     out, taken = run_forward(inp, stats=st)
     ref = ov.forward()
-    want_path = ops.PATH_FUSED_DECODE if (cfg.T <= 8 and cfg.act == "bf16") else ops.PATH_GROUPED
+    decode = cfg.T <= 8 and cfg.act == "bf16" and cfg.wdt != "mxfp8"
+    want_path = ops.PATH_FUSED_DECODE if decode else ops.PATH_GROUPED
     assert taken == want_path
-    assert_close(to64(out), ref["out"], TOL[cfg.wdt], name)
+    e = assert_close(to64(out), ref["out"], TOL[cfg.wdt], name)
+    print(f"[forward] {name}: rel_err={e:.3e}", flush=True)
     assert int(dev_nd.cpu()[0]) == ref["n_dropped"]
     np.testing.assert_array_equal(dev_counts.cpu().numpy(), ref["counts"])
 
@@ -322,8 +336,9 @@ def test_hip_graph_capture_replay(name):
 # token, outputs on a sample of tokens the oracle recomputes one by one.
 # ---------------------------------------------------------------------------
 FULL = ["tiny_f32", "mixtral_decode", "mixtral_decode_b8", "mixtral_prefill", "fine_grained",
-        "fp8_capacity", "fp8_capacity_decode"]
-SAMPLE = {"mixtral_prefill": 12, "fine_grained": 3, "fp8_capacity": 24}
+        "fp8_capacity", "fp8_capacity_decode", "mixtral_prefill_mxfp8", "fine_grained_mxfp8"]
+SAMPLE = {"mixtral_prefill": 12, "fine_grained": 3, "fp8_capacity": 24, "mixtral_prefill_mxfp8": 12,
+          "fine_grained_mxfp8": 3}
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -401,6 +416,7 @@ EC_CASES = {
     "ec_f32": C["tiny_f32"].with_(T=77, seed=15),
     "ec_all_tokens": C["mixtral_prefill"].with_(T=40, d=256, f=256, E=4, k=2, capacity_factor=2.0, seed=16),
     "ec_small_batch": C["mixtral_prefill"].with_(T=5, d=256, f=256, E=8, k=2, seed=17),
+    "ec_mx_shared": C["fine_grained_mxfp8"].with_(T=96, d=512, E=32, f=256, seed=26),
     "mixtral_prefill": C["mixtral_prefill"],
     "fine_grained": C["fine_grained"],
 }
@@ -454,7 +470,7 @@ def test_expert_choice_parity(name):
     toks = None if n is None else np.sort(np.random.default_rng(1).choice(cfg.T, size=n, replace=False))
     ref = oracle.expert_choice_forward(ov.x, ov.W_g, ov.bias, cfg.k, cfg.renormalize,
                                        np.float32(cfg.capacity_factor), ov.expert, cfg.E, shared=ov.shared(),
-                                       tokens=toks)
+                                       tokens=toks, **ov.quant_hooks())
     assert _ec_boundary_is_clear(ref, cfg.k, cfg.capacity_factor)
     Cap = ref["capacity"]
     assert ops.capacity(desc) == Cap
@@ -466,3 +482,49 @@ def test_expert_choice_parity(name):
     out2, _ = run()
     assert torch.equal(out2, out)                       # bitwise reproducible
     print(f"[expert-choice] {name}: C={Cap} unchosen_tokens={unchosen} rel_err={e:.3e}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 quantiser (moe_quantize_mxfp8): codes and scales bit-exact
+# ---------------------------------------------------------------------------
+def _mx_rows(rng, rows, cols):
+    v = rng.normal(0, 1, (rows, cols)) * np.exp2(rng.integers(-20, 20, (rows, 1)))
+    special = [np.zeros(32),                                         # all-zero block
+               -np.zeros(32),
+               rng.normal(0, 1, 32) * 1e-37,                         # scale exponent clamped at -127
+               np.array([448.0, 464.0, 480.0, 500.0, -511.0] + [1.0] * 27),   # saturation (block max 511)
+               2.0 ** np.arange(-10, 22),                            # powers of two across the E4M3 range
+               -(2.0 ** -20) * np.arange(32),                        # negatives that round to -0
+               (np.arange(32) + 0.5) * 2.0 ** -4]                    # ties
+    nb = cols // 32
+    for i, blk in enumerate(special):
+        r, b = divmod(i, nb)
+        if r < rows:
+            v[r, 32 * b:32 * b + 32] = blk
+    return v
+
+
+@pytest.mark.parametrize("dtype,rows,cols", [("bf16", 37, 256), ("f32", 37, 256), ("bf16", 4096, 4096),
+                                              ("f32", 5, 32), ("bf16", 300, 2048 + 96)])
+def test_mx_quantize_parity(dtype, rows, cols):
+    print(f"[mx_quantize] {dtype} {rows}x{cols}", flush=True)
+    rng = np.random.default_rng(rows * 31 + cols)
+    v = _mx_rows(rng, rows, cols)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    xt = torch.from_numpy(v.astype(np.float32)).to(tdt).cuda()
+    q = torch.full((rows, cols), 0x5A, dtype=torch.uint8, device="cuda")
+    s = torch.full((rows, cols // 32), 0x5A, dtype=torch.uint8, device="cuda")
+    ops.quantize_mxfp8(xt, q, s)
+    torch.cuda.synchronize()
+    rq, rs = oracle.mx_quantize(to64(xt))
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+
+
+def test_mx_quantize_empty_and_errors():
+    q = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    ops.quantize_mxfp8(x, q, q)                           # rows == 0 enqueues nothing
+    bad = torch.zeros((2, 48), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ops.MoEError):
+        ops.quantize_mxfp8(bad, q, q)
