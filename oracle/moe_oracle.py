@@ -84,12 +84,13 @@ def dequantize(codes, scale, channel_axis: int) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # Router  ([MIX] gate; [DSK] router bias)
 # ----------------------------------------------------------------------------
-def router_logits(x, W_g, bias=None) -> np.ndarray:
-    """logits[t, e] = fp32( sum_i x[t, i] * W_g[i, e] (+ bias[e]) ), fp64 sum."""
+def router_logits(x, W_g, bias=None, round32: bool = True) -> np.ndarray:
+    """logits[t, e] = fp32( sum_i x[t, i] * W_g[i, e] (+ bias[e]) ), fp64 sum.
+    round32=False keeps the fp64 sum (smooth in x and W_g, for derivative checks)."""
     s = _f64(x) @ _f64(W_g)
     if bias is not None:
         s = s + _f64(bias)[None, :]
-    return s.astype(np.float32)
+    return s.astype(np.float32) if round32 else s
 
 
 def softmax_rows(logits32) -> np.ndarray:
@@ -200,7 +201,8 @@ ExpertFn = Callable[[int], Sequence[np.ndarray]]
 
 def forward(x, W_g, bias, k: int, renormalize: bool, capacity_factor,
             expert: ExpertFn, E: int, shared: Optional[Sequence[np.ndarray]] = None,
-            tokens: Optional[Sequence[int]] = None, quant_x=None, quant_h=None) -> dict:
+            tokens: Optional[Sequence[int]] = None, quant_x=None, quant_h=None,
+            round_logits: bool = True) -> dict:
     """Routed MoE SwiGLU layer.
 
     expert(e) returns (W_gate[d,f], W_up[d,f], W_down[f,d]) of expert e as
@@ -211,11 +213,12 @@ def forward(x, W_g, bias, k: int, renormalize: bool, capacity_factor,
     checked on a sample.  out rows follow the order of `tokens`.
     quant_x / quant_h (optional) map the token rows entering the experts and
     the activated intermediate rows to the values a block-scaled layer sees;
-    routing always uses the unquantised x.
+    routing always uses the unquantised x.  round_logits=False skips the fp32
+    rounding of the router logits (derivative checks only).
     """
     x = _f64(x)
     T = x.shape[0]
-    logits = router_logits(x, W_g, bias)
+    logits = router_logits(x, W_g, bias, round_logits)
     probs = softmax_rows(logits)
     idx = topk_select(probs, k)
     w = routing_weights(probs, idx, renormalize)
@@ -390,6 +393,116 @@ def expert_choice_forward(x, W_g, bias, k: int, renormalize: bool, capacity_fact
         out = out + expert_ffn(qx(x[toks]), *shared, quant_h=quant_h)
     return dict(logits=logits, out=out, tokens=np.array(toks, dtype=np.int64), **r)
 
+
+
+# ----------------------------------------------------------------------------
+# Backward of the token-choice layer (gradients of a scalar loss L, given
+# dout = dL/dout).  Pages: "MoE Model Architectures", Mixtral "Sparse MoE
+# Block" / "Expert FFN" (the forward these are the derivatives of) and
+# DeepSeek-V3 "DeepSeekMoE Architecture" (shared expert, weight 1); "Testing
+# using claude to graft ETHOS onto modded-nanogpt base", "Key Implementation
+# Details" (a backward that recomputes the forward values and accumulates
+# every weight gradient over the tokens that chose the expert); "Faster
+# writing: run only the chosen experts; uncap the large profile", "Test plan"
+# (the chosen-experts dispatch must give the same slot gradients as running
+# every expert).
+#
+# The expert selection (top-k, capacity) is piecewise constant: gradients flow
+# through the routing weights and the expert FFNs with the selection held
+# fixed.  Readings where the pages are silent: the router logits' fp32
+# rounding is differentiated as the identity; dropped assignments carry no
+# gradient; the router bias gets the gradient of an additive logit term.
+# ----------------------------------------------------------------------------
+def dsilu(z) -> np.ndarray:
+    """d/dz of z * sigmoid(z) = sigmoid(z) * (1 + z * (1 - sigmoid(z)))."""
+    z = _f64(z)
+    s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def expert_ffn_backward(X, W_gate, W_up, W_down, dY) -> dict:
+    """Y = (silu(X Wg) * (X Wu)) Wd; given dY = dL/dY returns dX, dWg, dWu, dWd
+    and H (the activated rows)."""
+    X, dY = _f64(X), _f64(dY)
+    Wg, Wu, Wd = _f64(W_gate), _f64(W_up), _f64(W_down)
+    G = X @ Wg
+    U = X @ Wu
+    H = silu(G) * U
+    dH = dY @ Wd.T
+    dG = dH * U * dsilu(G)
+    dU = dH * silu(G)
+    return dict(dX=dG @ Wg.T + dU @ Wu.T, dW_gate=X.T @ dG, dW_up=X.T @ dU, dW_down=H.T @ dY, H=H)
+
+
+def routing_weights_backward(probs, idx, g, renormalize: bool) -> np.ndarray:
+    """dL/dlogits from g[t, j] = dL/dw[t, j].
+    renormalised: w_j = exp(l_ij) / sum over the chosen l, a softmax over the
+    chosen logits, so dl_(i_m) = w_m (g_m - sum_j g_j w_j), zero elsewhere;
+    not renormalised: w_j = p_(i_j) with p the softmax over all E logits, so
+    dl_e = p_e ([e chosen] g_(j(e)) - sum_j g_j p_(i_j))."""
+    p = _f64(probs)
+    T, k = idx.shape
+    dl = np.zeros_like(p)
+    for t in range(T):
+        sel = [int(e) for e in idx[t]]
+        if renormalize:
+            den = math.fsum(p[t, e] for e in sel)
+            w = [p[t, e] / den for e in sel]
+            s = math.fsum(g[t, j] * w[j] for j in range(k))
+            for j, e in enumerate(sel):
+                dl[t, e] = w[j] * (g[t, j] - s)
+        else:
+            s = math.fsum(g[t, j] * p[t, e] for j, e in enumerate(sel))
+            for e in range(p.shape[1]):
+                dl[t, e] = -p[t, e] * s
+            for j, e in enumerate(sel):
+                dl[t, e] += p[t, e] * g[t, j]
+    return dl
+
+
+def backward(x, W_g, bias, k: int, renormalize: bool, capacity_factor, expert: ExpertFn, E: int,
+             shared: Optional[Sequence[np.ndarray]], dout, round_logits: bool = True) -> dict:
+    """Gradients of the token-choice layer of forward() for dL/dout = dout:
+    dx [T,d], dW_g [d,E], d_bias [E], dW_gate/dW_up [E,d,f], dW_down [E,f,d],
+    the shared expert's dWs_* (or None), and the intermediates d_logits [T,E]
+    and g [T,k] = dL/dw (0 for dropped assignments)."""
+    x, W_g, dout = _f64(x), _f64(W_g), _f64(dout)
+    T, d = x.shape
+    logits = router_logits(x, W_g, bias, round_logits)
+    probs = softmax_rows(logits)
+    idx = topk_select(probs, k)
+    w = routing_weights(probs, idx, renormalize)
+    perm = permute(idx, E, capacity(T, k, E, capacity_factor))
+    f = _f64(expert(0)[0]).shape[1]
+    dx = np.zeros((T, d))
+    dWg_e = np.zeros((E, d, f))
+    dWu_e = np.zeros((E, d, f))
+    dWd_e = np.zeros((E, f, d))
+    g = np.zeros((T, k))
+    offs, sa = perm["offsets"], perm["sorted_assign"]
+    for e in range(E):
+        rows = [int(a) for a in sa[offs[e]:offs[e + 1]]]
+        if not rows:                                  # no tokens: zero gradient
+            continue
+        toks = [a // k for a in rows]
+        Wg, Wu, Wd = expert(e)
+        Y = expert_ffn(x[toks], Wg, Wu, Wd)           # the unweighted expert outputs
+        wt = np.array([w[a // k, a % k] for a in rows])
+        b = expert_ffn_backward(x[toks], Wg, Wu, Wd, wt[:, None] * dout[toks])
+        dWg_e[e], dWu_e[e], dWd_e[e] = b["dW_gate"], b["dW_up"], b["dW_down"]
+        for i, a in enumerate(rows):
+            t, j = a // k, a % k
+            dx[t] += b["dX"][i]
+            g[t, j] = float(np.dot(dout[t], Y[i]))    # dL/dw of a kept assignment
+    dl = routing_weights_backward(probs, idx, g, renormalize)
+    dx += dl @ W_g.T
+    out = dict(dx=dx, dW_g=x.T @ dl, d_bias=dl.sum(axis=0), dW_gate=dWg_e, dW_up=dWu_e, dW_down=dWd_e,
+               d_logits=dl, g=g, dWs_gate=None, dWs_up=None, dWs_down=None)
+    if shared is not None:
+        b = expert_ffn_backward(x, *shared, dout)
+        out["dx"] = dx + b["dX"]
+        out.update(dWs_gate=b["dW_gate"], dWs_up=b["dW_up"], dWs_down=b["dW_down"])
+    return out
 
 
 # ----------------------------------------------------------------------------

@@ -641,3 +641,158 @@ def test_quant_hooks_are_on_expert_inputs_and_activations():
         for j in range(k):
             ref[t] += base["topk_w"][t, j] * dense_relu(x[t:t + 1], *ex[base["topk_idx"][t, j]]).numpy()[0]
     np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Backward (gradients of L = sum(dout * out))
+# --------------------------------------------------------------------------
+def _fd(fun, v, h):
+    """Central differences of the scalar fun at every element of v."""
+    g = np.zeros_like(v)
+    it = np.nditer(v, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        old = v[i]
+        v[i] = old + h
+        fp = fun()
+        v[i] = old - h
+        fm = fun()
+        v[i] = old
+        g[i] = (fp - fm) / (2 * h)
+    return g
+
+
+def test_dsilu_against_torch_autograd_and_differences():
+    z = np.linspace(-30, 30, 601)
+    zt = torch.from_numpy(z.copy()).requires_grad_(True)
+    torch.nn.functional.silu(zt).sum().backward()
+    np.testing.assert_allclose(oracle.dsilu(z), zt.grad.numpy(), rtol=1e-13, atol=1e-15)
+    h = 1e-6
+    np.testing.assert_allclose(oracle.dsilu(z), (oracle.silu(z + h) - oracle.silu(z - h)) / (2 * h),
+                               rtol=1e-6, atol=1e-8)
+
+
+def test_expert_ffn_backward_against_torch_autograd():
+    rng = np.random.default_rng(21)
+    n, d, f = 7, 12, 20                                # d != f: a transposed operand fails
+    X, Wg, Wu, Wd = (rng.normal(0, s, sh) for s, sh in ((1, (n, d)), (0.3, (d, f)), (0.3, (d, f)), (0.3, (f, d))))
+    dY = rng.normal(0, 1, (n, d))
+    b = oracle.expert_ffn_backward(X, Wg, Wu, Wd, dY)
+    ts = [torch.from_numpy(a.copy()).requires_grad_(True) for a in (X, Wg, Wu, Wd)]
+    Y = (torch.nn.functional.silu(ts[0] @ ts[1]) * (ts[0] @ ts[2])) @ ts[3]
+    (Y * torch.from_numpy(dY)).sum().backward()
+    for key, t in zip(("dX", "dW_gate", "dW_up", "dW_down"), ts):
+        np.testing.assert_allclose(b[key], t.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+def test_routing_weights_backward_against_differences(renorm):
+    rng = np.random.default_rng(22)
+    T, E, k = 5, 7, 3
+    l = rng.normal(0, 1.5, (T, E))
+    idx = oracle.topk_select(oracle.softmax_rows(l), k)
+    g = rng.normal(0, 1, (T, k))
+    dl = oracle.routing_weights_backward(oracle.softmax_rows(l), idx, g, renorm)
+    fun = lambda: float((oracle.routing_weights(oracle.softmax_rows(l), idx, renorm) * g).sum())
+    np.testing.assert_allclose(dl, _fd(fun, l, 1e-6), rtol=1e-6, atol=1e-9)
+    if renorm:                                          # a softmax over the chosen logits: rows sum to 0
+        np.testing.assert_allclose(dl.sum(axis=1), 0.0, atol=1e-14)
+
+
+def _bwd_layer(T, d, E, k, f, shared, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0, 1, (T, d))
+    Wg = rng.normal(0, 0.6, (d, E))
+    bias = rng.normal(0, 0.3, E)
+    ex = [tuple(rng.normal(0, 0.3, sh) for sh in ((d, f), (d, f), (f, d))) for _ in range(E)]
+    sh = tuple(rng.normal(0, 0.3, s) for s in ((d, f), (d, f), (f, d))) if shared else None
+    dout = rng.normal(0, 1, (T, d))
+    return x, Wg, bias, ex, sh, dout
+
+
+@pytest.mark.parametrize("renorm,cf,shared", [(True, 0.0, False), (False, 0.0, True), (True, 0.7, True)])
+def test_layer_backward_against_central_differences(renorm, cf, shared):
+    """Every gradient of the whole layer (router included, with unrounded
+    logits) against central differences of L = sum(dout * out)."""
+    T, d, E, k, f = 6, 5, 4, 2, 3
+    x, Wg, bias, ex, sh, dout = _bwd_layer(T, d, E, k, f, shared, seed=23 + int(renorm) + int(10 * cf))
+    run = lambda: oracle.forward(x, Wg, bias, k, renorm, cf, lambda e: ex[e], E, sh, round_logits=False)
+    L = lambda: float((run()["out"] * dout).sum())
+    r0 = run()
+    b = oracle.backward(x, Wg, bias, k, renorm, cf, lambda e: ex[e], E, sh, dout, round_logits=False)
+    h, tol = 1e-5, dict(rtol=2e-5, atol=2e-7)
+    np.testing.assert_allclose(b["dx"], _fd(L, x, h), **tol)
+    np.testing.assert_allclose(b["dW_g"], _fd(L, Wg, h), **tol)
+    np.testing.assert_allclose(b["d_bias"], _fd(L, bias, h), **tol)
+    for e in range(E):
+        for key, m in (("dW_gate", 0), ("dW_up", 1), ("dW_down", 2)):
+            np.testing.assert_allclose(b[key][e], _fd(L, ex[e][m], h), **tol)
+    if shared:
+        for key, m in (("dWs_gate", 0), ("dWs_up", 1), ("dWs_down", 2)):
+            np.testing.assert_allclose(b[key], _fd(L, sh[m], h), **tol)
+    # the selection did not move under the perturbations, and capacity dropped something when asked to
+    assert np.array_equal(run()["topk_idx"], r0["topk_idx"])
+    if cf:
+        assert r0["n_dropped"] > 0
+        assert np.all(b["g"][r0["inv_perm"].reshape(T, k) < 0] == 0.0)
+
+
+def test_layer_backward_against_torch_autograd_gather_all_form():
+    """The chosen-experts backward equals torch autograd of the run-every-expert
+    form (zero weight for unchosen or dropped assignments), with rounded logits."""
+    T, d, E, k, f = 9, 6, 5, 2, 4
+    x, Wg, bias, ex, sh, dout = _bwd_layer(T, d, E, k, f, True, seed=31)
+    cf = 0.9
+    r = oracle.forward(x, Wg, bias, k, True, cf, lambda e: ex[e], E, sh)
+    b = oracle.backward(x, Wg, bias, k, True, cf, lambda e: ex[e], E, sh, dout)
+    keep = np.zeros((T, E))
+    for t in range(T):
+        for j in range(k):
+            if r["inv_perm"][t * k + j] >= 0:
+                keep[t, r["topk_idx"][t, j]] = 1.0
+    chosen = np.zeros((T, E))
+    for t in range(T):
+        chosen[t, r["topk_idx"][t]] = 1.0
+    tt = lambda a: torch.from_numpy(np.array(a, dtype=np.float64)).requires_grad_(True)
+    xt, Wgt, bt = tt(x), tt(Wg), tt(bias)
+    ext = [[tt(m) for m in trip] for trip in ex]
+    sht = [tt(m) for m in sh]
+    lg = xt @ Wgt + bt
+    p = torch.softmax(lg, dim=1) * torch.from_numpy(chosen)
+    w = p / p.sum(dim=1, keepdim=True)
+    ffn = lambda X, a, b_, c: (torch.nn.functional.silu(X @ a) * (X @ b_)) @ c
+    out = sum(w[:, e:e + 1] * torch.from_numpy(keep[:, e:e + 1]) * ffn(xt, *ext[e]) for e in range(E))
+    out = out + ffn(xt, *sht)
+    (out * torch.from_numpy(dout)).sum().backward()
+    np.testing.assert_allclose(out.detach().numpy(), r["out"], rtol=1e-6, atol=1e-6)   # fp32 logits vs fp64
+    tol = dict(rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(b["dx"], xt.grad.numpy(), **tol)
+    np.testing.assert_allclose(b["dW_g"], Wgt.grad.numpy(), **tol)
+    np.testing.assert_allclose(b["d_bias"], bt.grad.numpy(), **tol)
+    for e in range(E):
+        np.testing.assert_allclose(b["dW_gate"][e], ext[e][0].grad.numpy(), **tol)
+        np.testing.assert_allclose(b["dW_up"][e], ext[e][1].grad.numpy(), **tol)
+        np.testing.assert_allclose(b["dW_down"][e], ext[e][2].grad.numpy(), **tol)
+    for key, m in (("dWs_gate", 0), ("dWs_up", 1), ("dWs_down", 2)):
+        np.testing.assert_allclose(b[key], sht[m].grad.numpy(), **tol)
+
+
+def test_layer_backward_single_expert_is_dense_backward():
+    T, d, f = 8, 6, 10
+    x, Wg, bias, ex, _, dout = _bwd_layer(T, d, 1, 1, f, False, seed=33)
+    b = oracle.backward(x, Wg, bias, 1, True, 0.0, lambda e: ex[e], 1, None, dout)
+    dense = oracle.expert_ffn_backward(x, *ex[0], dout)
+    np.testing.assert_allclose(b["dx"], dense["dX"], rtol=1e-13, atol=1e-13)   # w = 1: no router gradient
+    assert np.all(b["d_logits"] == 0.0) and np.all(b["dW_g"] == 0.0)
+    np.testing.assert_allclose(b["dW_down"][0], dense["dW_down"], rtol=1e-13, atol=1e-13)
+
+
+def test_layer_backward_relabelling_permutes_expert_gradients():
+    T, d, E, k, f = 10, 6, 5, 2, 4
+    x, Wg, bias, ex, _, dout = _bwd_layer(T, d, E, k, f, False, seed=35)
+    perm = np.array([3, 0, 4, 1, 2])
+    b = oracle.backward(x, Wg, bias, k, True, 0.0, lambda e: ex[e], E, None, dout)
+    b2 = oracle.backward(x, Wg[:, perm], bias[perm], k, True, 0.0, lambda e: ex[perm[e]], E, None, dout)
+    np.testing.assert_allclose(b2["dx"], b["dx"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(b2["dW_g"], b["dW_g"][:, perm], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(b2["dW_down"], b["dW_down"][perm], rtol=1e-12, atol=1e-12)
