@@ -233,6 +233,49 @@ moe_status moe_combine(const moe_desc* desc, const float* y_sorted, const int32_
 moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, void* out,
                        moe_stats* stats, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Gradients produced by moe_backward (fp32, dense, row-major, caller-owned
+ * device memory).  Every field below is fully written by each call. */
+typedef struct {
+  float* dx;                 /* [T, d]                                            */
+  float* dW_g;               /* [d, E] router weight                              */
+  float* d_bias;             /* [E] router bias, or NULL (not computed)           */
+  float* dW_gate;            /* [E, d, f]                                         */
+  float* dW_up;              /* [E, d, f]                                         */
+  float* dW_down;            /* [E, f, d]                                         */
+  float* dWs_gate;           /* shared expert [d, f], [d, f], [f, d] (has_shared) */
+  float* dWs_up;
+  float* dWs_down;
+  hipEvent_t ev_begin;       /* NULL or recorded just before the dX GEMM         */
+  hipEvent_t ev_end;         /* ... and just after it                             */
+} moe_grads;
+
+/* Bytes of workspace moe_backward needs for desc (0 when desc is invalid or
+ * not supported by the backward). */
+size_t moe_backward_workspace_size(const moe_desc* desc);
+
+/* Backward of moe_forward for token-choice layers with bf16 activations and
+ * bf16 weights: given dout = dL/dout [T, d] (bf16), the gradients of L with
+ * respect to x, the router weight and bias, and every expert's (and the
+ * shared expert's) three matrices.  The expert selection (top-k, capacity)
+ * is held fixed: gradients flow through the routing weights (the softmax and
+ * its renormalisation over the chosen experts) and through the chosen
+ * experts' SwiGLU FFNs; dropped assignments carry no gradient; experts that
+ * received no token get zero gradients.  The routing and the expert
+ * activations are recomputed from x (nothing is kept from the forward).
+ * Weight gradients are summed over each expert's tokens in a fixed order
+ * without atomics: results are bitwise reproducible.  Pages: "Testing using
+ * claude to graft ETHOS onto modded-nanogpt base", "Key Implementation
+ * Details" (a backward that recomputes the forward values and accumulates each
+ * weight gradient over the tokens that chose the expert); "Faster writing:
+ * run only the chosen experts; uncap the large profile", "Test plan" (slot
+ * gradients of the chosen-experts dispatch).
+ *   x, dout  [T, d] bf16;  w as for moe_forward;  grads as documented above
+ *   ws       moe_backward_workspace_size(desc) bytes, 256-byte aligned
+ * Returns MOE_ERR_UNSUPPORTED for other dtypes or expert-choice routing.
+ * T == 0 writes zero weight gradients. */
+moe_status moe_backward(const moe_desc* desc, const void* x, const moe_weights* w, const void* dout,
+                        const moe_grads* grads, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* OCP MXFP8 quantisation of a row-major [rows, cols] matrix along its rows:
  * for every 32 consecutive values of a row, with m their largest magnitude,
  * the scale exponent is s = floor(log2 m) - 8 clamped to [-127, 127] (an

@@ -23,7 +23,8 @@ _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "mxfp8": MOE_MXFP8
 
 # Every symbol the header declares.
 EXPORTS = ("moe_workspace_size", "moe_capacity", "moe_route", "moe_permute", "moe_grouped_ffn",
-           "moe_combine", "moe_forward", "moe_quantize_mxfp8", "moe_status_string", "moe_last_error")
+           "moe_combine", "moe_forward", "moe_quantize_mxfp8", "moe_backward_workspace_size", "moe_backward",
+           "moe_status_string", "moe_last_error")
 
 
 class Desc(ctypes.Structure):
@@ -45,6 +46,12 @@ class Stats(ctypes.Structure):
     _fields_ = [("path_taken", ctypes.c_int32), ("d_n_dropped", ctypes.c_void_p),
                 ("d_counts", ctypes.c_void_p), ("ev_begin", ctypes.c_void_p), ("ev_end", ctypes.c_void_p),
                 ("d_routed", ctypes.c_void_p), ("d_prob_mean", ctypes.c_void_p), ("d_lb_loss", ctypes.c_void_p)]
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "dx", "dW_g", "d_bias", "dW_gate", "dW_up", "dW_down", "dWs_gate", "dWs_up", "dWs_down",
+        "ev_begin", "ev_end")]
 
 
 class MoEError(RuntimeError):
@@ -69,6 +76,8 @@ def _load():
         "moe_combine": (ctypes.c_int, [DP, P, P, P, P, P]),
         "moe_forward": (ctypes.c_int, [DP, P, WP, P, SP, P, S, P]),
         "moe_quantize_mxfp8": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, P, P, P]),
+        "moe_backward_workspace_size": (S, [DP]),
+        "moe_backward": (ctypes.c_int, [DP, P, WP, P, ctypes.POINTER(Grads), P, S, P]),
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_last_error": (ctypes.c_char_p, []),
     }
@@ -183,3 +192,25 @@ def quantize_mxfp8(x, codes, scales, stream=None):
     rows = x.numel() // x.shape[-1] if x.dim() else 0
     _check(LIB.moe_quantize_mxfp8(_ptr(x), dt, rows, x.shape[-1], _ptr(codes), _ptr(scales), _stream(stream)),
            "moe_quantize_mxfp8")
+
+
+def backward_workspace_size(desc: Desc) -> int:
+    return int(LIB.moe_backward_workspace_size(ctypes.byref(desc)))
+
+
+def alloc_backward_workspace(desc: Desc, device="cuda") -> torch.Tensor:
+    n = backward_workspace_size(desc)
+    if n == 0:
+        raise MoEError(MOE_ERR_UNSUPPORTED, "moe_backward_workspace_size", last_error())
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def grads_struct(g: dict, ev_begin=None, ev_end=None) -> Grads:
+    """g: dict with the keys of Grads (device fp32 tensors or None)."""
+    return Grads(*[_ptr(g.get(n)) for n in ("dx", "dW_g", "d_bias", "dW_gate", "dW_up", "dW_down",
+                                             "dWs_gate", "dWs_up", "dWs_down")], ev_begin, ev_end)
+
+
+def backward(desc, x, weights: Weights, dout, grads: Grads, ws, stream=None):
+    _check(LIB.moe_backward(ctypes.byref(desc), _ptr(x), ctypes.byref(weights), _ptr(dout), ctypes.byref(grads),
+                            _ptr(ws), ws.numel(), _stream(stream)), "moe_backward")

@@ -1,0 +1,359 @@
+// Grouped bf16 GEMMs of the layer's backward pass on gfx950.
+//
+// Pages: "Testing using claude to graft ETHOS onto modded-nanogpt base", "Key
+// Implementation Details" (a backward that recomputes the forward values and
+// accumulates each weight gradient over the tokens that chose the expert;
+// there with atomics, here as one deterministic reduction per output tile);
+// "MoE Model Architectures", Mixtral "Expert FFN" (the forward being
+// differentiated: w2(silu(w1 x) * w3 x)).
+//
+// Every backward GEMM runs over the padded permuted row space: the rows of
+// group g (expert g, or the shared expert as group E) sit at [poff[g],
+// poff[g + 1]), a multiple of 64 rows whose tail rows hold zeros.  One tile
+// routine covers the five products through the two layouts an operand can
+// have in memory:
+//   KC  K contiguous:   A(m, k) = A[m * lda + k]   (B(k, n) = B[n * ldb + k])
+//   MC  K selects rows: A(m, k) = A[k * lda + m]   (B(k, n) = B[k * ldb + n])
+//   MODE_GU  G, U = Xp W_gate, Xp W_up      A KC (padded rows), B MC (weights)
+//   MODE_NT  C = A B^T-style products       A KC (padded rows, K may be split
+//            over two (A, B) pairs), B KC (weights, output-major rows)
+//   MODE_TN  dW = A^T B over a group's rows A MC, B MC (activations), K = rows
+// KC tiles live in LDS as rows of 64 K values (128 bytes, 16-byte chunks
+// swizzled by aswz<8>) and reach the MFMA with ds_read_b128; MC tiles as 64
+// K-rows of 256 values (swizzled by bswz) read with the transposing
+// ds_read_b64_tr_b16 -- the two layouts of the forward kernel's A and B.
+// Tiles: up to 256 x 256, 4 waves (2 x 2 of 128 x 128, or 1 x 4 for the
+// 128- and 64-row bodies of a group's last row tile), v_mfma_f32_32x32x16_bf16,
+// 64 K per LDS stage, two stages filled by global_load_lds.
+#include <hip/hip_ext.h>
+
+#include <type_traits>
+
+#include "common.h"
+#include "gemm_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int MODE_GU = 0, MODE_NT = 1, MODE_TN = 2;
+constexpr int kBK = 64;
+
+__device__ __forceinline__ int bswz_key(int k) { return ((k & 3) << 4) | ((k & 1) << 6); }
+__device__ __forceinline__ int bswz(int k, int n) { return k * 256 + (n ^ bswz_key(k)); }
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// 8 consecutive K of one M (or N) index per lane from an MC tile (64 K-rows
+// x 256, swizzled by bswz) with two transposing reads: within each 16-lane
+// group, output lane 4a + b receives element b of the 4-element rows of
+// input lanes a, a + 4, a + 8, a + 12.
+__device__ __forceinline__ bf16x8_t mc_frag(const bf16_t* Ls, int kbase, int nbase, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int a = i & 3, j = i >> 2;
+  const int n = nbase + 16 * (g & 1) + 4 * a;
+  const int k0 = kbase + 8 * (g >> 1) + j;
+  typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(Ls + bswz(k0, n)));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(Ls + bswz(k0 + 4, n)));
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+}  // namespace
+
+// One output tile of at most BMV rows (see the file comment for the modes).
+template <int MODE, int BMV>
+__device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0, int rows, int n0, int kbeg,
+                                         int nK, bf16_t* L0, bf16_t* L1) {
+  constexpr bool A_KC = MODE != MODE_TN;
+  constexpr bool B_KC = MODE == MODE_NT;
+  constexpr bool DUAL = MODE == MODE_GU;
+  constexpr int WM = (BMV >= 256) ? 2 : 1, WN = 4 / WM;
+  constexpr int NMAT = DUAL ? 2 : 1;
+  constexpr int BN_MAT = DUAL ? 128 : 256;
+  constexpr int NI_MAT = BN_MAT / WN / 32;
+  constexpr int NI = NI_MAT * NMAT;
+  constexpr int MI = BMV / WM / 32;
+  constexpr int WROWS = BMV / WM;
+  constexpr int A_LD = A_KC ? BMV / 8 / 4 : 8;      // 1 KB blocks per wave per stage
+  constexpr int B_LD = 8;
+  constexpr int LDS_B = 256 * kBK;                 // B tile offset (elements) inside a stage
+  constexpr int NMF = MI * NI;
+  constexpr int NDS = (A_KC ? MI : 2 * MI) + (B_KC ? NI : 2 * NI);
+  constexpr int NVM = A_LD + B_LD;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const int l32 = lane & 31;
+  const int lhi = lane >> 5;
+  const bool shared = (g == p.E);
+
+  // ---- A sources ----
+  // KC: block b = wave + 4 i holds tile rows 8 b .. 8 b + 7; this lane fills
+  //     row r = 8 b + lane / 8, LDS chunk lane % 8 = global chunk
+  //     aswz<8>(r, lane % 8) (8 K values).  Rows past the valid ones read the
+  //     tile's first row (never stored).
+  // MC: block b = 8 wave + i holds K-rows 2 b, 2 b + 1; this lane fills K-row
+  //     2 b + lane / 32, LDS chunk lane % 32 = global chunk (lane % 32) ^
+  //     (bswz_key(krow) / 8) of the 256 M columns from row0 (clamped to M).
+  uint32_t aoff[A_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    if constexpr (A_KC) {
+      const int r = 8 * (wave + 4 * i) + (lane >> 3);
+      const int rr = row0 + (r < rows ? r : 0);
+      aoff[i] = (uint32_t)rr * (uint32_t)p.lda + aswz<8>(r, lane & 7) * 8;
+    } else {
+      const int krow = 2 * (8 * wave + i) + (lane >> 5);
+      int m = row0 + ((lane & 31) ^ (bswz_key(krow) >> 3)) * 8;
+      if (m > p.M - 8) m = p.M - 8;
+      aoff[i] = (uint32_t)krow * (uint32_t)p.lda + m;
+    }
+  }
+  // ---- B sources (same two layouts) ----
+  const bf16_t* bb0;
+  const bf16_t* bb1;
+  if constexpr (MODE == MODE_TN) {
+    bb0 = p.B0;
+    bb1 = p.B0;
+  } else {
+    const size_t gs = shared ? 0 : (size_t)g * (size_t)p.bgs;
+    bb0 = shared ? p.Bs0 : p.B0 + gs;
+    bb1 = shared ? p.Bs1 : (p.B1 ? p.B1 + gs : nullptr);
+  }
+  uint32_t boff[B_LD];
+#pragma unroll
+  for (int j = 0; j < B_LD; ++j) {
+    if constexpr (B_KC) {
+      const int r = 8 * (B_LD * wave + j) + (lane >> 3);
+      int c = n0 + r;
+      if (c > p.N - 1) c = p.N - 1;
+      boff[j] = (uint32_t)c * (uint32_t)p.ldb + aswz<8>(r, lane & 7) * 8;
+    } else {
+      const int krow = 2 * (B_LD * wave + j) + (lane >> 5);
+      const int gc = (lane & 31) ^ (bswz_key(krow) >> 3);
+      int c;
+      if (DUAL) c = n0 + (gc & 15) * 8;          // columns 0..127 gate, 128..255 up
+      else c = n0 + gc * 8;
+      if (c > p.N - 8) c = p.N - 8;
+      boff[j] = (uint32_t)krow * (uint32_t)p.ldb + c;
+    }
+  }
+
+  // Load K-step k0 (absolute K index kbeg + k0) into stage L.
+  auto issue = [&](bf16_t* L, int k0) {
+    const bf16_t* a_base;
+    const bf16_t* b_base;
+    const bf16_t* b_base_up = nullptr;
+    uint32_t ak, bk;
+    if constexpr (MODE == MODE_NT) {
+      const bool second = k0 >= p.K1;             // K split over two (A, B) pairs
+      const int kk = second ? k0 - p.K1 : k0;
+      a_base = second ? p.A1 : p.A0;
+      b_base = second ? bb1 : bb0;
+      ak = (uint32_t)kk;
+      bk = (uint32_t)kk;
+    } else if constexpr (MODE == MODE_GU) {
+      a_base = p.A0;
+      b_base = bb0;
+      b_base_up = bb1;
+      ak = (uint32_t)k0;
+      bk = (uint32_t)k0 * (uint32_t)p.ldb;
+    } else {
+      a_base = p.A0;
+      b_base = bb0;
+      ak = (uint32_t)(kbeg + k0) * (uint32_t)p.lda;
+      bk = (uint32_t)(kbeg + k0) * (uint32_t)p.ldb;
+    }
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+      const int blk = A_KC ? wave + 4 * i : 8 * wave + i;
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(a_base + (aoff[i] + ak)), (lds_ptr_t)(L + blk * 512), 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < B_LD; ++j) {
+      const bf16_t* bsrc = b_base;
+      if constexpr (DUAL) {
+        const int krow = 2 * (B_LD * wave + j) + (lane >> 5);
+        const int gc = (lane & 31) ^ (bswz_key(krow) >> 3);
+        bsrc = (gc >> 4) ? b_base_up : b_base;
+      }
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(bsrc + (boff[j] + bk)), (lds_ptr_t)(L + LDS_B + (B_LD * wave + j) * 512),
+                                       16, 0, 0);
+    }
+  };
+
+  f32x16_t acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+
+  auto b_col = [&](int ni) -> int {           // tile-local B index (N) of fragment ni
+    if (DUAL) return (ni / NI_MAT) * 128 + wn * (128 / WN) + (ni % NI_MAT) * 32;
+    return wn * (256 / WN) + ni * 32;
+  };
+  auto frags = [&](const bf16_t* L, int ks, bf16x8_t* af, bf16x8_t* bfr) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int mb = wm * WROWS + mi * 32;
+      if constexpr (A_KC) {
+        const int row = mb + l32;
+        af[mi] = *reinterpret_cast<const bf16x8_t*>(L + row * kBK + aswz<8>(row, ks * 2 + lhi) * 8);
+      } else {
+        af[mi] = mc_frag(L, ks * 16, mb, lane);
+      }
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int nb = b_col(ni);
+      if constexpr (B_KC) {
+        const int j = nb + l32;
+        bfr[ni] = *reinterpret_cast<const bf16x8_t*>(L + LDS_B + j * kBK + aswz<8>(j, ks * 2 + lhi) * 8);
+      } else {
+        bfr[ni] = mc_frag(L + LDS_B, ks * 16, nb, lane);
+      }
+    }
+  };
+  auto mfmas = [&](const bf16x8_t* af, const bf16x8_t* bfr) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+  };
+
+  // Two-stage pipeline over 16-wide K sub-steps (the forward kernel's): the
+  // next sub-step's fragments are read while the current one multiplies; the
+  // stage just read is refilled two steps ahead (past the end: the last step
+  // again, never read), so the vmcnt thresholds are exact.
+  if (nK > 0) {
+    bf16x8_t fa0[MI], fb0[NI], fa1[MI], fb1[NI];
+    issue(L0, 0);
+    issue(L1, min(1, nK - 1) * kBK);
+    wait_vmem_le<NVM>();
+    __builtin_amdgcn_s_barrier();
+    frags(L0, 0, fa0, fb0);
+    auto step = [&](bf16_t* L, const bf16_t* Ln, int k) {
+#pragma unroll
+      for (int sub = 0; sub < 3; ++sub) {
+        if (sub & 1) {
+          frags(L, sub + 1, fa0, fb0);
+          mfmas(fa1, fb1);
+        } else {
+          frags(L, sub + 1, fa1, fb1);
+          mfmas(fa0, fb0);
+        }
+        sched_interleave<NMF, NDS, 0>();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_vmem_le_lds0<0>();
+      __builtin_amdgcn_s_barrier();
+      issue(L, min(k + 2, nK - 1) * kBK);
+      frags(Ln, 0, fa0, fb0);
+      mfmas(fa1, fb1);
+      sched_interleave<NMF, NDS, NVM>();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int k = 0;
+    for (; k + 2 <= nK; k += 2) {
+      step(L0, L1, k);
+      step(L1, L0, k + 1);
+    }
+    if (k < nK) step(L0, L1, k);
+    wait_vmem_le<0>();
+  }
+
+  // ---- epilogue: fp32 stores ----
+  if constexpr (MODE == MODE_TN) {
+    float* C = shared ? p.Cs : p.C0 + (size_t)g * p.cstride;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int col = n0 + b_col(ni) + l32;
+        if (col >= p.N) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = row0 + wm * WROWS + mi * 32 + (v >> 2) * 8 + lhi * 4 + (v & 3);
+          if (r < p.M) C[(size_t)r * p.N + col] = acc[mi][ni][v];
+        }
+      }
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int nl = 0; nl < NI_MAT; ++nl) {
+        const int col = n0 + b_col(nl) + l32;
+        if (col >= p.N) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * WROWS + mi * 32 + (v >> 2) * 8 + lhi * 4 + (v & 3);
+          if (r >= rows) continue;
+          const size_t o = (size_t)(row0 + r) * p.N + col;
+          p.C0[o] = acc[mi][nl][v];
+          if constexpr (DUAL) p.C1[o] = acc[mi][nl + NI_MAT][v];
+        }
+      }
+  }
+}
+
+// GU / NT: row tiles of the padded groups from the device schedule.
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void bwd_rows_kernel(BwdGemmParams p) {
+  __shared__ __attribute__((aligned(1024))) bf16_t L0[512 * kBK];
+  __shared__ __attribute__((aligned(1024))) bf16_t L1[512 * kBK];
+  constexpr int BN_MAT = MODE == MODE_GU ? 128 : 256;
+  const int n_tiles = (p.N + BN_MAT - 1) / BN_MAT;
+  int g, row0, rows, nt;
+  // the schedule lists the G padded groups (the shared expert is group E)
+  if (!decode_tile(p.sched, p.maxQ, p.G, n_tiles, &g, &row0, &rows, &nt)) return;
+  const int nK = p.K / kBK;
+  if (rows > 128) bwd_tile<MODE, 256>(p, g, row0, rows, nt * BN_MAT, 0, nK, L0, L1);
+  else if (rows > 64) bwd_tile<MODE, 128>(p, g, row0, rows, nt * BN_MAT, 0, nK, L0, L1);
+  else bwd_tile<MODE, 64>(p, g, row0, rows, nt * BN_MAT, 0, nK, L0, L1);
+}
+
+// TN: one 256 x 256 tile of one group's weight gradient; work-groups are
+// dealt to the XCDs so that the tiles of one group share an XCD's L2.
+__global__ __launch_bounds__(256, 1) void bwd_wgrad_kernel(BwdGemmParams p, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) bf16_t L0[512 * kBK];
+  __shared__ __attribute__((aligned(1024))) bf16_t L1[512 * kBK];
+  const int per_g = tiles_m * tiles_n;
+  const int total = p.G * per_g;
+  const int per_x = (total + 7) >> 3;
+  const int logical = (blockIdx.x & 7) * per_x + (blockIdx.x >> 3);
+  if (logical >= total) return;
+  const int g = logical / per_g;
+  const int t = logical - g * per_g;
+  const int tm = t / tiles_n, tn = t - tm * tiles_n;
+  const int kbeg = p.poff[g];
+  const int nK = (p.poff[g + 1] - kbeg) / kBK;
+  bwd_tile<MODE_TN, 256>(p, g, tm * 256, 256, tn * 256, kbeg, nK, L0, L1);
+}
+
+hipError_t launch_bwd_rows(int mode, const BwdGemmParams& p, hipStream_t s) {
+  const int bn = mode == MODE_GU ? 128 : 256;
+  const int grid = grouped_grid(p.maxQ, (p.N + bn - 1) / bn);
+  if (mode == MODE_GU) bwd_rows_kernel<MODE_GU><<<grid, 256, 0, s>>>(p);
+  else bwd_rows_kernel<MODE_NT><<<grid, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_wgrad(const BwdGemmParams& p, hipStream_t s) {
+  const int tm = (p.M + 255) / 256, tn = (p.N + 255) / 256;
+  const int total = p.G * tm * tn;
+  const int grid = 8 * ((total + 7) / 8);
+  bwd_wgrad_kernel<<<grid, 256, 0, s>>>(p, tm, tn);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
+
 namespace moe {
 
 constexpr int kMaxExperts = 1024;
@@ -102,6 +104,64 @@ struct CombineArgs {
   void* out;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+// Backward pass (token choice, bf16 activations and weights)
+struct BwdGemmParams {          // grouped GEMMs of the backward
+  const bf16_t* A0;        // GU/NT: padded rows [P, lda]; TN: activations [P, lda]
+  const bf16_t* A1;        // NT: second K part (K >= K1), else nullptr
+  int lda;
+  const bf16_t* B0;        // GU: W_gate [E, K, N]; NT: weights [E, N, K]; TN: activations [P, ldb]
+  const bf16_t* B1;        // GU: W_up; NT: second K part's weights; TN: nullptr
+  const bf16_t* Bs0;       // shared expert's matrices (group E)
+  const bf16_t* Bs1;
+  int ldb;
+  long bgs;                // GU/NT: elements of one group's weight matrix
+  int K, K1;               // GU/NT: reduction length and the split point (K1 = K: no split)
+  int M, N;                // TN: output rows (M) and columns (N); GU/NT: N = output columns
+  const int32_t* sched;    // GU/NT row-tile schedule over the padded rows
+  int maxQ, E, G;
+  const int32_t* poff;     // [G + 1] padded group offsets
+  float* C0;               // GU: G rows [P, N]; NT: [P, N]; TN: dW [G][M][N] (group g at C0 + g * cstride)
+  float* C1;               // GU: U rows [P, N]
+  float* Cs;               // TN: the shared group's output (group E), or nullptr
+  long cstride;
+};
+hipError_t launch_bwd_rows(int mode, const BwdGemmParams& p, hipStream_t s);   // 0: G/U recompute, 1: NT
+hipError_t launch_bwd_wgrad(const BwdGemmParams& p, hipStream_t s);
+
+struct BackwardArgs {
+  const void* x;                 // [T, d] bf16
+  const void* dout;              // [T, d] bf16
+  const void* W_g;               // [d, E] bf16
+  ExpertWeights w;
+  int T, d, E, k, f, has_shared, renormalize;
+  // forward routing (recomputed by the caller)
+  const float* logits;           // [T, E]
+  const int32_t* topk_idx;       // [T, k]
+  const float* topk_w;           // [T, k]
+  const int32_t* offsets;        // [E + 1]
+  const int32_t* sorted_assign;  // [T k]
+  const int32_t* inv_perm;       // [T k]
+  // scratch (padded row space of backward_pad_rows rows)
+  int32_t* poff;                 // [G + 1]
+  int32_t* ptok;                 // [P]
+  float* pw;                     // [P]
+  int32_t* apos;                 // [T k]
+  float* gsc;                    // [P]
+  int32_t* sched;                // backward_sched_ints
+  bf16_t *Xp, *Dp;               // [P, d]
+  float *G, *U, *dH;             // [P, f]
+  bf16_t *dG, *dU, *Hw;          // [P, f]
+  float* dXp;                    // [P, d]
+  float* dl;                     // [T, E]
+  // outputs (fp32)
+  float *dx, *dW_g, *d_bias, *dW_gate, *dW_up, *dW_down, *dWs_gate, *dWs_up, *dWs_down;
+  hipEvent_t ev_begin, ev_end;
+};
+long backward_pad_rows(int T, int E, int k, int has_shared);
+size_t backward_sched_ints(int T, int E, int k, int has_shared);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
+hipError_t launch_zero(float* p, long n, hipStream_t s);
 
 // Router telemetry (optional side outputs of the layer call)
 struct TelemetryArgs {

@@ -471,6 +471,143 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w
   return do_combine(desc, y, inv, tw, out, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+moe_status check_backward_desc(const moe_desc* d) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->act_dtype != MOE_BF16 || d->w_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "the backward takes bf16 activations and bf16 weights");
+  if (expert_choice(d)) return fail(MOE_ERR_UNSUPPORTED, "the backward covers token-choice routing");
+  const double P = (double)backward_pad_rows(d->T, d->E, d->top_k, d->has_shared);
+  if (P * (d->f > d->d ? d->f : d->d) >= 2147483648.0)
+    return fail(MOE_ERR_UNSUPPORTED, "layer too large for the backward (padded rows * max(d, f) >= 2^31)");
+  return MOE_OK;
+}
+
+struct BwdLayout {
+  size_t part, idx, w, logits, counts, offsets, sorted, inv, ndrop, rank;
+  size_t poff, ptok, pw, apos, gsc, sched, Xp, Dp, G, U, dH, dG, dU, Hw, dXp, dl, total;
+};
+
+BwdLayout bwd_layout_of(const moe_desc* d) {
+  BwdLayout L{};
+  const size_t T = d->T, k = d->top_k, E = d->E, D = d->d, F = d->f;
+  const size_t P = (size_t)backward_pad_rows(d->T, d->E, d->top_k, d->has_shared);
+  const size_t Gn = E + (d->has_shared ? 1 : 0);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off += up256(bytes);
+    return at;
+  };
+  L.part = take(router_partial_bytes(d->T, d->d, d->E));
+  L.idx = take(T * k * 4);
+  L.w = take(T * k * 4);
+  L.logits = take(T * E * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.sorted = take(T * k * 4);
+  L.inv = take(T * k * 4);
+  L.ndrop = take(4);
+  L.rank = take(T * k * 4);
+  L.poff = take((Gn + 1) * 4);
+  L.ptok = take(P * 4);
+  L.pw = take(P * 4);
+  L.apos = take(T * k * 4);
+  L.gsc = take(P * 4);
+  L.sched = take(backward_sched_ints(d->T, d->E, d->top_k, d->has_shared) * 4);
+  L.Xp = take(P * D * 2);
+  L.Dp = take(P * D * 2);
+  L.G = take(P * F * 4);
+  L.U = take(P * F * 4);
+  L.dH = take(P * F * 4);
+  L.dG = take(P * F * 2);
+  L.dU = take(P * F * 2);
+  L.Hw = take(P * F * 2);
+  L.dXp = take(P * D * 4);
+  L.dl = take(T * E * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_backward_workspace_size(const moe_desc* desc) {
+  if (check_backward_desc(desc) != MOE_OK) return 0;
+  return bwd_layout_of(desc).total;
+}
+
+moe_status moe_backward(const moe_desc* desc, const void* x, const moe_weights* w, const void* dout,
+                        const moe_grads* g, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_backward_desc(desc);
+  if (st != MOE_OK) return st;
+  if (!g) return fail(MOE_ERR_INVALID_ARG, "grads is NULL");
+  REQ(g->dW_g, "grads.dW_g");
+  REQ(g->dW_gate, "grads.dW_gate");
+  REQ(g->dW_up, "grads.dW_up");
+  REQ(g->dW_down, "grads.dW_down");
+  OPT(g->d_bias, "grads.d_bias");
+  if (desc->has_shared) {
+    REQ(g->dWs_gate, "grads.dWs_gate");
+    REQ(g->dWs_up, "grads.dWs_up");
+    REQ(g->dWs_down, "grads.dWs_down");
+  }
+  if ((st = check_router_weights(w)) != MOE_OK) return st;
+  if ((st = check_expert_weights(desc, w)) != MOE_OK) return st;
+  const size_t E = desc->E, D = desc->d, F = desc->f;
+  if (desc->T == 0) {   // an empty batch: zero weight gradients
+    hipError_t e = launch_zero(g->dW_g, (long)(D * E), stream);
+    if (e == hipSuccess) e = launch_zero(g->d_bias, (long)E, stream);
+    if (e == hipSuccess) e = launch_zero(g->dW_gate, (long)(E * D * F), stream);
+    if (e == hipSuccess) e = launch_zero(g->dW_up, (long)(E * D * F), stream);
+    if (e == hipSuccess) e = launch_zero(g->dW_down, (long)(E * D * F), stream);
+    if (desc->has_shared) {
+      if (e == hipSuccess) e = launch_zero(g->dWs_gate, (long)(D * F), stream);
+      if (e == hipSuccess) e = launch_zero(g->dWs_up, (long)(D * F), stream);
+      if (e == hipSuccess) e = launch_zero(g->dWs_down, (long)(D * F), stream);
+    }
+    return hip_status(e, "zero gradients");
+  }
+  REQ(x, "x");
+  REQ(dout, "dout");
+  REQ(g->dx, "grads.dx");
+  const BwdLayout L = bwd_layout_of(desc);
+  if (ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if ((uintptr_t)ws & 255u) return fail(MOE_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  char* base = (char*)ws;
+  int32_t* idx = (int32_t*)(base + L.idx);
+  float* tw = (float*)(base + L.w);
+  float* logits = (float*)(base + L.logits);
+  if ((st = do_route(desc, x, w, idx, tw, logits, (double*)(base + L.part), nullptr, stream)) != MOE_OK) return st;
+  int32_t* offsets = (int32_t*)(base + L.offsets);
+  int32_t* sorted = (int32_t*)(base + L.sorted);
+  int32_t* inv = (int32_t*)(base + L.inv);
+  if ((st = do_permute(desc, idx, (int32_t*)(base + L.counts), offsets, sorted, inv, (int32_t*)(base + L.ndrop),
+                       (int32_t*)(base + L.rank), stream)) != MOE_OK)
+    return st;
+  BackwardArgs a{};
+  a.x = x; a.dout = dout; a.W_g = w->W_g; a.w = expert_weights(w);
+  a.T = desc->T; a.d = desc->d; a.E = desc->E; a.k = desc->top_k; a.f = desc->f;
+  a.has_shared = desc->has_shared; a.renormalize = desc->renormalize;
+  a.logits = logits; a.topk_idx = idx; a.topk_w = tw; a.offsets = offsets; a.sorted_assign = sorted; a.inv_perm = inv;
+  a.poff = (int32_t*)(base + L.poff); a.ptok = (int32_t*)(base + L.ptok); a.pw = (float*)(base + L.pw);
+  a.apos = (int32_t*)(base + L.apos); a.gsc = (float*)(base + L.gsc); a.sched = (int32_t*)(base + L.sched);
+  a.Xp = (bf16_t*)(base + L.Xp); a.Dp = (bf16_t*)(base + L.Dp);
+  a.G = (float*)(base + L.G); a.U = (float*)(base + L.U); a.dH = (float*)(base + L.dH);
+  a.dG = (bf16_t*)(base + L.dG); a.dU = (bf16_t*)(base + L.dU); a.Hw = (bf16_t*)(base + L.Hw);
+  a.dXp = (float*)(base + L.dXp); a.dl = (float*)(base + L.dl);
+  a.dx = g->dx; a.dW_g = g->dW_g; a.d_bias = g->d_bias; a.dW_gate = g->dW_gate; a.dW_up = g->dW_up;
+  a.dW_down = g->dW_down; a.dWs_gate = g->dWs_gate; a.dWs_up = g->dWs_up; a.dWs_down = g->dWs_down;
+  a.ev_begin = g->ev_begin; a.ev_end = g->ev_end;
+  return hip_status(launch_backward(a, stream), "backward");
+}
+
 moe_status moe_quantize_mxfp8(const void* in, int32_t in_dtype, int64_t rows, int32_t cols, uint8_t* codes,
                               uint8_t* scales, hipStream_t stream) {
   if (in_dtype != MOE_F32 && in_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "bad in_dtype %d", in_dtype);

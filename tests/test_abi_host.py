@@ -202,3 +202,26 @@ def test_synth_mx_weights_follow_the_oracle_quantiser():
     rq, rs = oracle.mx_quantize(w.astype(np.float64))
     np.testing.assert_array_equal(s.numpy(), rs)
     np.testing.assert_array_equal(q.view(torch.uint8).numpy(), rq)
+
+
+def test_backward_validation(ops):
+    def bwd(d, g=None):
+        gs = g if g is not None else ops.Grads()
+        return ops.LIB.moe_backward(ctypes.byref(d), None, None, None, ctypes.byref(gs), None, 0, None)
+    for wdt, act in (("fp8", "bf16"), ("mxfp8", "bf16"), ("f32", "f32")):
+        d = ops.make_desc(40, 256, 8, 2, 256, act=act, wdt=wdt)
+        assert bwd(d) == ops.MOE_ERR_UNSUPPORTED, wdt
+        assert ops.backward_workspace_size(d) == 0
+    d = ops.make_desc(40, 256, 8, 2, 256)
+    d.routing = ops.ROUTING_EXPERT_CHOICE
+    assert bwd(d) == ops.MOE_ERR_UNSUPPORTED and "token-choice" in ops.last_error()
+    d = ops.make_desc(40, 256, 8, 2, 256)
+    assert ops.backward_workspace_size(d) > ops.workspace_size(d)
+    assert bwd(d) == ops.MOE_ERR_INVALID_ARG and "dW_g" in ops.last_error()
+    r = ops.LIB.moe_backward(ctypes.byref(d), None, None, None, None, None, 0, None)
+    assert r == ops.MOE_ERR_INVALID_ARG and "grads" in ops.last_error()
+    g = ops.Grads(dW_g=16, dW_gate=16, dW_up=16, dW_down=16)
+    d = ops.make_desc(40, 256, 8, 2, 256, has_shared=True)
+    w = ops.Weights(W_g=16, W_gate=16, W_up=16, W_down=16)
+    r = ops.LIB.moe_backward(ctypes.byref(d), None, ctypes.byref(w), None, ctypes.byref(g), None, 0, None)
+    assert r == ops.MOE_ERR_INVALID_ARG and "dWs_gate" in ops.last_error()
