@@ -42,6 +42,9 @@ def parse():
                     help="skip the second timed region (per-launch events on the dominant kernel)")
     ap.add_argument("--routing", choices=["token", "expert"], default="token",
                     help="token choice (the pages' default) or expert choice (every expert takes its C best tokens)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time moe_backward (dL/dx and every weight gradient for a random dout) instead "
+                         "of the forward; bf16 token-choice layers")
     ap.add_argument("--telemetry", action="store_true",
                     help="also request the router telemetry outputs (routed load, mean probability, "
                          "load-balancing loss) inside the timed region")
@@ -170,6 +173,120 @@ def cpu_baseline(cfg, inp, budget_s=12.0, max_calls=2000):
                       f"(routing over all E experts, fp64 SwiGLU of the chosen experts), {dt:.1f} s"}
 
 
+def bench_backward(args, cfg):
+    """moe_backward on the workload: whole-call throughput (tokens/s), the dX
+    GEMM (the largest row-tile GEMM, 4 rows d f flops) against the bf16 MFMA
+    roofline, and the oracle's backward on a small token sample."""
+    import numpy as np
+    import torch
+    import synth
+    from sparse_mixture_experts_12_amd import _lib as ops
+    steps = args.steps if args.steps is not None else 10
+    warmup = args.warmup if args.warmup is not None else 3
+    print(f"[bench] backward workload={cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} f={cfg.f} "
+          f"steps={steps} warmup={warmup}", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(cfg, "cuda")
+    desc = ops.desc_from_cfg(cfg)
+    w = ops.weights_struct(inp)
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    dout = torch.randn((cfg.T, cfg.d), generator=gen).to(torch.bfloat16).cuda()
+    ws = ops.alloc_backward_workspace(desc)
+    z = lambda *sh: torch.empty(sh, dtype=torch.float32, device="cuda")
+    g = {"dx": z(cfg.T, cfg.d), "dW_g": z(cfg.d, cfg.E), "d_bias": z(cfg.E) if inp["bias"] is not None else None,
+         "dW_gate": z(cfg.E, cfg.d, cfg.f), "dW_up": z(cfg.E, cfg.d, cfg.f), "dW_down": z(cfg.E, cfg.f, cfg.d)}
+    if cfg.shared:
+        g.update(dWs_gate=z(cfg.d, cfg.f), dWs_up=z(cfg.d, cfg.f), dWs_down=z(cfg.f, cfg.d))
+    gs = ops.grads_struct(g)
+    # routing facts (kept rows) from one forward with stats
+    counts = torch.zeros(cfg.E, dtype=torch.int32, device="cuda")
+    out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
+    fws = ops.alloc_workspace(desc)
+    ops.forward(desc, inp["x"], w, out, fws, stats=ops.Stats(d_counts=counts.data_ptr()))
+    torch.cuda.synchronize()
+    rows = int(counts.sum()) + (cfg.T if cfg.shared else 0)
+    del fws
+    for _ in range(warmup):
+        ops.backward(desc, inp["x"], w, dout, gs, ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        ops.backward(desc, inp["x"], w, dout, gs, ws)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms = total_ms / steps
+    kern_ms = float("nan")
+    if not args.no_kernel_events:
+        hev = HipEvents()
+        eb = [hev.create() for _ in range(steps)]
+        ee = [hev.create() for _ in range(steps)]
+        for i in range(steps):
+            ops.backward(desc, inp["x"], w, dout, ops.grads_struct(g, eb[i].value, ee[i].value), ws)
+        torch.cuda.synchronize()
+        kern_ms = sum(hev.elapsed_ms(eb[i], ee[i]) for i in range(steps)) / steps
+    have_k = kern_ms == kern_ms
+    kflops = 4 * rows * cfg.d * cfg.f                   # dX = [dG | dU] [W_gate | W_up]^T
+    flops = 16 * rows * cfg.d * cfg.f + 4 * cfg.T * cfg.d * cfg.E
+    roof = {"bound": "mfma", "achieved": round(kflops / (kern_ms / 1e3) / 1e12, 2) if have_k else None,
+            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(kflops / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4) if have_k else None,
+            "traffic": measured_traffic("bwd_dx_gemm", cfg.name), "kernel": "bwd_rows_kernel<NT dX>",
+            "kernel_ms": round(kern_ms, 5) if have_k else None, "alg_flops": int(kflops)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle's backward", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_backward(cfg, inp, dout)
+    line = {
+        "metric": "MoE-layer backward tokens/s (dL/dx and all weight gradients)",
+        "value": round(cfg.T * steps / (total_ms / 1e3), 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) activations and dout, "
+        "N(0,0.02) weights)",
+        "config": {"workload": cfg.name, "pass": "backward", "T": cfg.T, "d": cfg.d, "E": cfg.E, "top_k": cfg.k,
+                   "f": cfg.f, "shared_expert": cfg.shared, "capacity_factor": cfg.capacity_factor},
+        "layer": {"alg_flops": int(flops), "tflops": round(flops / (ms / 1e3) / 1e12, 2)},
+        "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_backward(cfg, inp, dout, budget_s=12.0, max_calls=200):
+    """The oracle's backward, as it stands, on calls of a few tokens of the workload."""
+    import numpy as np
+    import oracle
+    import torch
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    to64 = lambda t: t.detach().to(torch.float64).cpu().numpy()
+    x, W_g, d64 = to64(inp["x"]), to64(inp["W_g"]), to64(dout)
+    bias = None if inp["bias"] is None else to64(inp["bias"])
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            cache[e] = (to64(inp["W_gate"][e]), to64(inp["W_up"][e]), to64(inp["W_down"][e]))
+        return cache[e]
+    shared = (to64(inp["Ws_gate"]), to64(inp["Ws_up"]), to64(inp["Ws_down"])) if cfg.shared else None
+    tb = min(cfg.T, 4)
+    call = lambda t0: oracle.backward(x[t0:t0 + tb], W_g, bias, cfg.k, cfg.renormalize,
+                                      np.float32(cfg.capacity_factor), expert, cfg.E, shared, d64[t0:t0 + tb])
+    call(0)
+    n = 0
+    t_start = time.perf_counter()
+    while n < max_calls and (time.perf_counter() - t_start) < budget_s:
+        call((n * tb) % max(1, cfg.T - tb + 1))
+        n += 1
+    dt = time.perf_counter() - t_start
+    return {"value": n * tb / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} oracle backward calls of {tb} tokens each of the {cfg.name} workload "
+                      f"(routing, fp64 expert and router gradients), {dt:.1f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -181,6 +298,8 @@ def main():
     from sparse_mixture_experts_12_amd import _lib as ops
 
     cfg = synth.CONFIGS[args.workload]
+    if args.backward:
+        return bench_backward(args, cfg)
     decode = cfg.T <= 8 and cfg.act == "bf16" and args.routing == "token"
     steps = args.steps if args.steps is not None else (200 if decode else 20)
     # a few ms of warm-up lets the clocks settle before the timed region

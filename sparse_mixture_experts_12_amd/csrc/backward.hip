@@ -248,37 +248,50 @@ __global__ __launch_bounds__(256) void dx_kernel(const float* __restrict__ dXp, 
   dx[(size_t)t * d + c] = acc + r;
 }
 
-// dW_g[c, e] = sum_t x[t, c] dl[t, e] (t ascending); 16 experts per thread.
-__global__ __launch_bounds__(256) void router_wgrad_kernel(const bf16_t* __restrict__ x, const float* __restrict__ dl,
-                                                           int T, int d, int E, float* __restrict__ dWg) {
-  constexpr int EB = 16;
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  const int e0 = blockIdx.y * EB;
-  const int ne = min(EB, E - e0);
-  float acc[EB];
+// dW_g[c, e] = sum_t x[t, c] dl[t, e] and d_bias[e] = sum_t dl[t, e] (row
+// c = d of the partials, x taken as 1): tokens in chunks of kRwChunk, each
+// (64 c x 16 e, chunk) work-group writes its partial sums; a second launch
+// adds the chunks in order.
+constexpr int kRwChunk = 256;
+
+__global__ __launch_bounds__(256) void router_wgrad_partial_kernel(const bf16_t* __restrict__ x,
+                                                                   const float* __restrict__ dl, int T, int d, int E,
+                                                                   float* __restrict__ part) {
+  const int c = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int e0 = blockIdx.y * 16 + (threadIdx.x >> 6) * 4;
+  const int t0 = blockIdx.z * kRwChunk;
+  const int t1 = min(T, t0 + kRwChunk);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const bool cok = c <= d;
+  for (int t = t0; t < t1; ++t) {
+    const float xv = c < d ? bf16_to_f32(x[(size_t)t * d + c]) : 1.f;
+    const float* r = dl + (size_t)t * E;
 #pragma unroll
-  for (int i = 0; i < EB; ++i) acc[i] = 0.f;
-  const bool ok = c < d;
-  for (int t = 0; t < T; ++t) {
-    const float xv = ok ? bf16_to_f32(x[(size_t)t * d + c]) : 0.f;
-    const float* r = dl + (size_t)t * E + e0;
-#pragma unroll
-    for (int i = 0; i < EB; ++i)
-      if (i < ne) acc[i] = __fmaf_rn(xv, r[i], acc[i]);
+    for (int i = 0; i < 4; ++i)
+      if (e0 + i < E) acc[i] = __fmaf_rn(xv, r[e0 + i], acc[i]);
   }
-  if (!ok) return;
+  if (!cok) return;
+  float* o = part + ((size_t)blockIdx.z * (d + 1) + c) * E;
 #pragma unroll
-  for (int i = 0; i < EB; ++i)
-    if (i < ne) dWg[(size_t)c * E + e0 + i] = acc[i];
+  for (int i = 0; i < 4; ++i)
+    if (e0 + i < E) o[e0 + i] = acc[i];
 }
 
-__global__ __launch_bounds__(256) void bias_grad_kernel(const float* __restrict__ dl, int T, int E,
-                                                        float* __restrict__ db) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= E) return;
+__global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* __restrict__ part, int nchunk, int d,
+                                                                  int E, float* __restrict__ dWg,
+                                                                  float* __restrict__ db) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const long n = (long)(d + 1) * E;
+  if (i >= n) return;
   float s = 0.f;
-  for (int t = 0; t < T; ++t) s += dl[(size_t)t * E + e];
-  db[e] = s;
+  for (int z = 0; z < nchunk; ++z) s += part[(size_t)z * n + i];
+  if (i < (long)d * E) dWg[i] = s;
+  else if (db) db[i - (long)d * E] = s;
+}
+
+size_t router_wgrad_ws_bytes(int T, int d, int E) {
+  const size_t nchunk = (T + kRwChunk - 1) / kRwChunk;
+  return nchunk * (size_t)(d + 1) * E * 4;
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, long n) {
@@ -388,9 +401,12 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
   else
     dx_kernel<false><<<gx, 256, 0, s>>>(a.dXp, a.apos, a.poff, a.dl, a.topk_idx, (const bf16_t*)a.W_g, a.T, a.d,
                                         a.E, a.k, a.has_shared, a.dx);
-  router_wgrad_kernel<<<dim3((a.d + 255) / 256, (a.E + 15) / 16), 256, 0, s>>>((const bf16_t*)a.x, a.dl, a.T, a.d,
-                                                                               a.E, a.dW_g);
-  if (a.d_bias) bias_grad_kernel<<<(a.E + 255) / 256, 256, 0, s>>>(a.dl, a.T, a.E, a.d_bias);
+  const int nchunk = (a.T + kRwChunk - 1) / kRwChunk;
+  router_wgrad_partial_kernel<<<dim3((a.d + 1 + 63) / 64, (a.E + 15) / 16, nchunk), 256, 0, s>>>(
+      (const bf16_t*)a.x, a.dl, a.T, a.d, a.E, a.rw_part);
+  const long nout = (long)(a.d + 1) * a.E;
+  router_wgrad_reduce_kernel<<<(unsigned)((nout + 255) / 256), 256, 0, s>>>(a.rw_part, nchunk, a.d, a.E, a.dW_g,
+                                                                           a.d_bias);
   return hipGetLastError();
 }
 

@@ -223,12 +223,19 @@ __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0
       }
     }
   };
+  // TN tiles multiply with the operands swapped, so the accumulators hold the
+  // transposed fragment: a lane then owns 4 consecutive output columns of one
+  // output row per register quad (16-byte stores in the epilogue).
   auto mfmas = [&](const bf16x8_t* af, const bf16x8_t* bfr) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+      for (int ni = 0; ni < NI; ++ni) {
+        if constexpr (MODE == MODE_TN)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+        else
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+      }
   };
 
   // Two-stage pipeline over 16-wide K sub-steps (the forward kernel's): the
@@ -274,19 +281,25 @@ __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0
 
   // ---- epilogue: fp32 stores ----
   if constexpr (MODE == MODE_TN) {
+    // acc[mi][ni][4 q + i] = C[row, col0 + i] with row = row0 + mb + l32 and
+    // col0 = n0 + nb + 8 q + 4 lhi (transposed fragment, see mfmas)
     float* C = shared ? p.Cs : p.C0 + (size_t)g * p.cstride;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < MI; ++mi) {
+      const int r = row0 + wm * WROWS + mi * 32 + l32;
+      if (r >= p.M) continue;
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
-        const int col = n0 + b_col(ni) + l32;
-        if (col >= p.N) continue;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = row0 + wm * WROWS + mi * 32 + (v >> 2) * 8 + lhi * 4 + (v & 3);
-          if (r < p.M) C[(size_t)r * p.N + col] = acc[mi][ni][v];
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + b_col(ni) + 8 * q + 4 * lhi;
+          if (col >= p.N) continue;
+          const f32x4_t v = {acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
+                             acc[mi][ni][4 * q + 3]};
+          *reinterpret_cast<f32x4_t*>(C + (size_t)r * p.N + col) = v;
         }
       }
+    }
   } else {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)

@@ -154,12 +154,14 @@ struct BackwardArgs {
   bf16_t *dG, *dU, *Hw;          // [P, f]
   float* dXp;                    // [P, d]
   float* dl;                     // [T, E]
+  float* rw_part;                // router_wgrad_ws_bytes
   // outputs (fp32)
   float *dx, *dW_g, *d_bias, *dW_gate, *dW_up, *dW_down, *dWs_gate, *dWs_up, *dWs_down;
   hipEvent_t ev_begin, ev_end;
 };
 long backward_pad_rows(int T, int E, int k, int has_shared);
 size_t backward_sched_ints(int T, int E, int k, int has_shared);
+size_t router_wgrad_ws_bytes(int T, int d, int E);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
 hipError_t launch_zero(float* p, long n, hipStream_t s);
 
