@@ -282,22 +282,43 @@ __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0
   // ---- epilogue: fp32 stores ----
   if constexpr (MODE == MODE_TN) {
     // acc[mi][ni][4 q + i] = C[row, col0 + i] with row = row0 + mb + l32 and
-    // col0 = n0 + nb + 8 q + 4 lhi (transposed fragment, see mfmas)
+    // col0 = n0 + nb + 8 q + 4 lhi (transposed fragment, see mfmas).  The
+    // 256 x 256 fp32 tile leaves through LDS in two halves of 128 rows, so the
+    // global stores are whole 1 KB rows (64 lanes x 16 bytes).  LDS row r
+    // (1 KB) holds 16-byte chunk c at position c ^ (r & 15): the 16-lane
+    // passes of both the fragment writes (16 rows, one chunk) and the row
+    // reads (one row, 16 chunks) hit distinct banks.
+    static_assert(BMV == 256 && WM == 2, "weight-gradient tiles are 256 x 256");
     float* C = shared ? p.Cs : p.C0 + (size_t)g * p.cstride;
+    auto lrow = [&](int r) -> float* { return reinterpret_cast<float*>(r < 64 ? L0 : L1) + (r & 63) * 256; };
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      const int r = row0 + wm * WROWS + mi * 32 + l32;
-      if (r >= p.M) continue;
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();                            // LDS free (K loop or previous half done)
+      if (wm == h) {
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
+        for (int mi = 0; mi < MI; ++mi) {
+          const int r = mi * 32 + l32;
+          float* Lr = lrow(r);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = n0 + b_col(ni) + 8 * q + 4 * lhi;
-          if (col >= p.N) continue;
-          const f32x4_t v = {acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
-                             acc[mi][ni][4 * q + 3]};
-          *reinterpret_cast<f32x4_t*>(C + (size_t)r * p.N + col) = v;
+          for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int chunk = (b_col(ni) + 8 * q + 4 * lhi) >> 2;
+              const f32x4_t v = {acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
+                                 acc[mi][ni][4 * q + 3]};
+              *reinterpret_cast<f32x4_t*>(Lr + ((chunk ^ (r & 15)) << 2)) = v;
+            }
         }
+      }
+      __syncthreads();
+      // 128 rows x 64 chunks; thread t takes chunk t % 64 of rows t / 64, + 4, ...
+      const int chunk = tid & 63;
+      const int col = n0 + chunk * 4;
+#pragma unroll 4
+      for (int r = tid >> 6; r < 128; r += 4) {
+        const int grow = row0 + 128 * h + r;
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(lrow(r) + ((chunk ^ (r & 15)) << 2));
+        if (grow < p.M && col < p.N) *reinterpret_cast<f32x4_t*>(C + (size_t)grow * p.N + col) = v;
       }
     }
   } else {
