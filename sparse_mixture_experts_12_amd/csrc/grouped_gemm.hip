@@ -538,19 +538,47 @@ __device__ __forceinline__ void dl_tile(const GemmParams& p, int g, int row0, in
   wait_vmem_le<0>();
 
   // ---- epilogue ----
+  if constexpr (DUAL) {
+    // H = bf16(silu(gate) * up).  Register v holds row 8 (v / 4) + 4 lhi + v % 4
+    // of column l32; neighbouring lanes (columns c, c + 1) swap halves so that
+    // the even lane stores (row v, columns c..c+1) and the odd lane (row v + 1,
+    // columns c - 1..c) as one dword each.
+    const bool odd = lane & 1;
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
+    for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-    for (int nl = 0; nl < NI_MAT; ++nl) {
-      const int col = n0 + wn * (BN_MAT / WN) + nl * 32 + l32;
-      if (col >= p.N) continue;
+      for (int nl = 0; nl < NI_MAT; ++nl) {
+        const int c2 = n0 + wn * (BN_MAT / WN) + nl * 32 + (l32 & ~1);
+        if (c2 >= p.N) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * WROWS + mi * 32 + (v >> 2) * 8 + lhi * 4 + (v & 3);
-        if (r >= rows) continue;
-        const size_t orow = (size_t)(row0 + r) * p.N;
-        if (DUAL) p.h_out[orow + col] = (bf16_t)f32_to_bf16(silu_f(acc[mi][nl][v]) * acc[mi][nl + NI_MAT][v]);
-        else p.y_out[orow + col] = acc[mi][nl][v];
+        for (int v = 0; v < 16; v += 2) {
+          float hv[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const float g = acc[mi][nl][v + i];
+            hv[i] = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * acc[mi][nl + NI_MAT][v + i];
+          }
+          const uint32_t own = pack_bf16x2(hv[0], hv[1]);
+          const uint32_t x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)own, 0xB1, 0xF, 0xF, false);
+          const uint32_t out = __builtin_amdgcn_perm(x, own, sel);
+          const int r = wm * WROWS + mi * 32 + (v >> 2) * 8 + lhi * 4 + (v & 3) + (odd ? 1 : 0);
+          if (r < rows) *reinterpret_cast<uint32_t*>(p.h_out + (size_t)(row0 + r) * p.N + c2) = out;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+      for (int nl = 0; nl < NI_MAT; ++nl) {
+        const int col = n0 + wn * (BN_MAT / WN) + nl * 32 + l32;
+        if (col >= p.N) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * WROWS + mi * 32 + (v >> 2) * 8 + lhi * 4 + (v & 3);
+          if (r < rows) p.y_out[(size_t)(row0 + r) * p.N + col] = acc[mi][nl][v];
+        }
       }
     }
   }

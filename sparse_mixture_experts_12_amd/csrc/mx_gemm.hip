@@ -70,17 +70,22 @@ struct MxParams {
   float* y_out;                  // !DUAL: [rows, N]
 };
 
-// Largest |v| over the 32 lanes of each half-wave (lanes 0..31, 32..63):
-// quad swap, quad pair swap, rotations by 4 and 8 inside each 16-lane row,
-// then the two rows of the half exchanged.
-__device__ __forceinline__ float half_wave_absmax(float v) {
-  float m = fabsf(v);
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x124, 0xF, 0xF, false)));
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x128, 0xF, 0xF, false)));
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x401F)));
-  return m;
+// Per 16-bit half, the largest value over the 32 lanes of each half-wave
+// (lanes 0..31, 32..63) as packed unsigned 16-bit integers: quad swap, quad
+// pair swap, rotations by 4 and 8 inside each 16-lane row, then the two rows
+// of the half exchanged.
+__device__ __forceinline__ uint32_t half_wave_max_u16x2(uint32_t v) {
+  typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+  auto mx = [](uint32_t a, uint32_t b) -> uint32_t {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a),
+                                                                  __builtin_bit_cast(u16x2_t, b)));
+  };
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
+  v = mx(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
+  return v;
 }
 
 // Biased E8M0 scale code of a block whose largest magnitude is m (fp32):
@@ -94,9 +99,6 @@ __device__ __forceinline__ int mx_scale_code(float m) { return max((int)((__floa
 __device__ __forceinline__ float mx_scaled(float v, int code) {
   const float f = __uint_as_float((uint32_t)(254 - code) << 23);
   return fminf(fmaxf(v * f, -448.f), 448.f);
-}
-__device__ __forceinline__ uint32_t e4m3_byte(float q) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q, q, 0, false) & 0xffu;
 }
 
 // ---------------------------------------------------------------------------
@@ -351,31 +353,60 @@ __device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int 
   // ---- epilogue ----
   if constexpr (DUAL) {
     // H = silu(gate) * up in fp32, quantised per row and 32 columns: a
-    // fragment's 32 columns of one row live in the 32 lanes of a half-wave.
+    // fragment's 32 columns of one row live in the 32 lanes of a half-wave
+    // (register v holds row 8 (v / 4) + 4 lhi + v % 4).  The block scale only
+    // needs the largest exponent field, reduced for two rows at a time as
+    // packed 16-bit integers.  The codes of 4 rows x 4 columns are transposed
+    // inside each lane quad so that every lane stores one dword (4 columns of
+    // one row); lane v of each half stores row v's scale byte.
     const int KSo = p.N >> 5;
+    const int j4 = lane & 3;
+    const uint32_t selA = (j4 & 1) ? 0x03070105u : 0x06020400u;
+    const uint32_t selB = (j4 & 2) ? 0x03020706u : 0x05040100u;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
       for (int nl = 0; nl < NI_MAT; ++nl) {
         const int cb0 = n0 + wn * (BN_MAT / WN) + nl * 32;     // first H column of the fragment
-        uint32_t q[16];
+        float h[16];
         int code[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float h = silu_f(acc[mi][nl][v]) * acc[mi][nl + NI_MAT][v];
-          code[v] = mx_scale_code(half_wave_absmax(h));
-          q[v] = e4m3_byte(mx_scaled(h, code[v]));
+          const float g = acc[mi][nl][v];
+          h[v] = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * acc[mi][nl + NI_MAT][v];
         }
-        if (cb0 < p.N) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int r = wm * WROWS + mi * 32 + (v >> 2) * 8 + lhi * 4 + (v & 3);
-            if (r < rows) {
-              const size_t orow = (size_t)(row0 + r);
-              p.hq_out[orow * p.N + cb0 + l32] = (uint8_t)q[v];
-              if (l32 == 0) p.hs_out[orow * KSo + (cb0 >> 5)] = (uint8_t)code[v];
-            }
-          }
+        for (int v = 0; v < 16; v += 2) {
+          uint32_t m = ((__float_as_uint(h[v]) >> 23) & 0xffu) | (((__float_as_uint(h[v + 1]) >> 23) & 0xffu) << 16);
+          m = half_wave_max_u16x2(m);
+          code[v] = max((int)(m & 0xffffu) - 8, 0);
+          code[v + 1] = max((int)(m >> 16) - 8, 0);
+        }
+        uint32_t rowq[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          int b = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(h[4 * g], code[4 * g]),
+                                                  mx_scaled(h[4 * g + 1], code[4 * g + 1]), 0, false);
+          b = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(h[4 * g + 2], code[4 * g + 2]),
+                                              mx_scaled(h[4 * g + 3], code[4 * g + 3]), b, true);
+          const uint32_t x = (uint32_t)__builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false);   // lane ^ 1
+          const uint32_t t = __builtin_amdgcn_perm(x, (uint32_t)b, selA);
+          const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)t, 0x4E, 0xF, 0xF, false);  // lane ^ 2
+          rowq[g] = __builtin_amdgcn_perm(y, t, selB);
+        }
+        int sc = code[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) sc = (l32 == v) ? code[v] : sc;
+        const int rbase = wm * WROWS + mi * 32 + lhi * 4;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int r = rbase + 8 * g + j4;
+          if (r < rows)
+            *reinterpret_cast<uint32_t*>(p.hq_out + (size_t)(row0 + r) * p.N + cb0 + (l32 & ~3)) = rowq[g];
+        }
+        if (l32 < 16) {
+          const int r = rbase + 8 * (l32 >> 2) + (l32 & 3);
+          if (r < rows) p.hs_out[(size_t)(row0 + r) * KSo + (cb0 >> 5)] = (uint8_t)sc;
         }
       }
     }
