@@ -233,8 +233,13 @@ def bench_backward(args, cfg):
     roof = {"bound": "mfma", "achieved": round(kflops / (kern_ms / 1e3) / 1e12, 2) if have_k else None,
             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(kflops / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4) if have_k else None,
-            "traffic": measured_traffic("bwd_dx_gemm", cfg.name), "kernel": "bwd_rows_kernel<NT dX>",
+            "traffic": measured_traffic("bwd_dx_gemm", cfg.name), "kernel": "bwd_rows_kernel<NTS> (dX)",
             "kernel_ms": round(kern_ms, 5) if have_k else None, "alg_flops": int(kflops)}
+    if args.copy_calibration:     # the plain copy kernel whose counters scale the GEMM's (see main)
+        a = torch.ones(1 << 27, dtype=torch.bfloat16, device="cuda")
+        b = torch.empty_like(a)
+        torch.neg(a, out=b)
+        torch.cuda.synchronize()
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle's backward", file=sys.stderr, flush=True)

@@ -373,7 +373,7 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
     q.K = 2 * a.f; q.K1 = a.f; q.N = a.d;
     q.C0 = a.dXp;
     if (a.ev_begin) hipEventRecord(a.ev_begin, s);
-    if ((err = launch_bwd_rows(1, q, s)) != hipSuccess) return err;
+    if ((err = launch_bwd_rows(2, q, s)) != hipSuccess) return err;
     if (a.ev_end) hipEventRecord(a.ev_end, s);
   }
   // 5. weight gradients: dW_gate = Xp^T dG, dW_up = Xp^T dU ([d, f] per group), dW_down = Hw^T Dp ([f, d])

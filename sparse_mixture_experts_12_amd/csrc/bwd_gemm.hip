@@ -15,8 +15,9 @@
 //   KC  K contiguous:   A(m, k) = A[m * lda + k]   (B(k, n) = B[n * ldb + k])
 //   MC  K selects rows: A(m, k) = A[k * lda + m]   (B(k, n) = B[k * ldb + n])
 //   MODE_GU  G, U = Xp W_gate, Xp W_up      A KC (padded rows), B MC (weights)
-//   MODE_NT  C = A B^T-style products       A KC (padded rows, K may be split
-//            over two (A, B) pairs), B KC (weights, output-major rows)
+//   MODE_NT  C = A B^T-style products       A KC (padded rows), B KC (weights,
+//            output-major rows); MODE_NTS the same with K split over two
+//            (A, B) pairs
 //   MODE_TN  dW = A^T B over a group's rows A MC, B MC (activations), K = rows
 // KC tiles live in LDS as rows of 64 K values (128 bytes, 16-byte chunks
 // swizzled by aswz<8>) and reach the MFMA with ds_read_b128; MC tiles as 64
@@ -37,7 +38,7 @@ namespace moe {
 
 namespace {
 
-constexpr int MODE_GU = 0, MODE_NT = 1, MODE_TN = 2;
+constexpr int MODE_GU = 0, MODE_NT = 1, MODE_NTS = 2, MODE_TN = 3;   // NTS: NT with K split over two pairs
 constexpr int kBK = 64;
 
 __device__ __forceinline__ int bswz_key(int k) { return ((k & 3) << 4) | ((k & 1) << 6); }
@@ -69,7 +70,7 @@ template <int MODE, int BMV>
 __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0, int rows, int n0, int kbeg,
                                          int nK, bf16_t* L0, bf16_t* L1) {
   constexpr bool A_KC = MODE != MODE_TN;
-  constexpr bool B_KC = MODE == MODE_NT;
+  constexpr bool B_KC = MODE == MODE_NT || MODE == MODE_NTS;
   constexpr bool DUAL = MODE == MODE_GU;
   constexpr int WM = (BMV >= 256) ? 2 : 1, WN = 4 / WM;
   constexpr int NMAT = DUAL ? 2 : 1;
@@ -152,13 +153,18 @@ __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0
     const bf16_t* b_base;
     const bf16_t* b_base_up = nullptr;
     uint32_t ak, bk;
-    if constexpr (MODE == MODE_NT) {
+    if constexpr (MODE == MODE_NTS) {
       const bool second = k0 >= p.K1;             // K split over two (A, B) pairs
       const int kk = second ? k0 - p.K1 : k0;
       a_base = second ? p.A1 : p.A0;
       b_base = second ? bb1 : bb0;
       ak = (uint32_t)kk;
       bk = (uint32_t)kk;
+    } else if constexpr (MODE == MODE_NT) {
+      a_base = p.A0;
+      b_base = bb0;
+      ak = (uint32_t)k0;
+      bk = (uint32_t)k0;
     } else if constexpr (MODE == MODE_GU) {
       a_base = p.A0;
       b_base = bb0;
@@ -378,6 +384,7 @@ hipError_t launch_bwd_rows(int mode, const BwdGemmParams& p, hipStream_t s) {
   const int bn = mode == MODE_GU ? 128 : 256;
   const int grid = grouped_grid(p.maxQ, (p.N + bn - 1) / bn);
   if (mode == MODE_GU) bwd_rows_kernel<MODE_GU><<<grid, 256, 0, s>>>(p);
+  else if (mode == MODE_NTS) bwd_rows_kernel<MODE_NTS><<<grid, 256, 0, s>>>(p);
   else bwd_rows_kernel<MODE_NT><<<grid, 256, 0, s>>>(p);
   return hipGetLastError();
 }

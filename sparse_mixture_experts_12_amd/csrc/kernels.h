@@ -126,7 +126,8 @@ struct BwdGemmParams {          // grouped GEMMs of the backward
   float* Cs;               // TN: the shared group's output (group E), or nullptr
   long cstride;
 };
-hipError_t launch_bwd_rows(int mode, const BwdGemmParams& p, hipStream_t s);   // 0: G/U recompute, 1: NT
+// mode 0: G/U recompute, 1: NT, 2: NT with K split over two (A, B) pairs
+hipError_t launch_bwd_rows(int mode, const BwdGemmParams& p, hipStream_t s);
 hipError_t launch_bwd_wgrad(const BwdGemmParams& p, hipStream_t s);
 
 struct BackwardArgs {
