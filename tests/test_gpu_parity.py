@@ -308,7 +308,7 @@ def test_bitwise_deterministic(name):
                        b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
 
 
-@pytest.mark.parametrize("name", ["bf16_prefill_ragged", "decode_T1"])
+@pytest.mark.parametrize("name", ["bf16_prefill_ragged", "decode_T1", "mx_ragged"])
 def test_hip_graph_capture_replay(name):
     cfg = SMALL[name]
     inp = device_inputs(cfg)
