@@ -15,9 +15,13 @@ namespace moe {
 // first.  Within the heavy segment a group's tiles are ordered column-major,
 // so neighbouring row tiles of one weight column tile share an XCD's L2.
 // Work-groups past both ranges return false.
+// SEG selects the segments one launch covers: 0 both (heavy first), 1 the
+// heavy segment only, 2 the light segment only (separate launches may use
+// kernels shaped for each segment).
+template <int SEG = 0>
 __device__ __forceinline__ bool decode_tile(const int32_t* sched, int maxQ, int E, int n_tiles, int* g, int* row0,
                                             int* rows, int* nt) {
-  const int QH = sched[0], QL = sched[1];
+  const int QH = SEG == 2 ? 0 : sched[0], QL = SEG == 1 ? 0 : sched[1];
   const int totH = QH * n_tiles, totL = QL * n_tiles;
   const int perH = (totH + 7) >> 3, perL = (totL + 7) >> 3;
   const int bid = blockIdx.x;

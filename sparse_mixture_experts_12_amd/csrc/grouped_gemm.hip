@@ -585,7 +585,13 @@ __device__ __forceinline__ void dl_tile(const GemmParams& p, int g, int row0, in
 }
 
 
-template <bool DUAL, int BMMAX, int BK, int NST>
+// SEG 0: every tile of the schedule (bodies of 256, 128 or 64 rows);
+// SEG 1: the heavy segment only (tiles of more than 128 rows, 256-row body);
+// SEG 2: the light segment only (an expert's last tile of at most 128 rows),
+//        with LDS stages sized for 128 rows so that three of them fit and two
+//        steps of loads are in flight: light tiles do little MFMA work per
+//        stage and are bound by load latency.
+template <bool DUAL, int BMMAX, int BK, int NST, int SEG = 0>
 __global__ __launch_bounds__(256, TileCfg<BMMAX>::OCC) void gemm_dl_kernel(GemmParams p) {
   constexpr int LDS_S = BMMAX * BK + 256 * BK;
   __shared__ __attribute__((aligned(1024))) bf16_t L0[LDS_S];
@@ -595,12 +601,17 @@ __global__ __launch_bounds__(256, TileCfg<BMMAX>::OCC) void gemm_dl_kernel(GemmP
   constexpr int BN_MAT = DUAL ? 128 : 256;
   const int n_tiles = (p.N + BN_MAT - 1) / BN_MAT;
   int g, row0, rows, nt;
-  if (!decode_tile(p.sched, p.maxQ, p.E, n_tiles, &g, &row0, &rows, &nt)) return;
+  if (!decode_tile<SEG>(p.sched, p.maxQ, p.E, n_tiles, &g, &row0, &rows, &nt)) return;
   // An expert's last row tile is usually partial: run it with a body whose
   // MFMA work matches its rows (<= 64, <= 128) instead of the full height.
-  if constexpr (BMMAX >= 256) {
+  if constexpr (SEG == 1) {
+    dl_tile<DUAL, 256, BMMAX, BK, NST>(p, g, row0, rows, nt, L0, L1, L2, L3);
+  } else if constexpr (BMMAX >= 256) {
     if (rows > 128) dl_tile<DUAL, 256, BMMAX, BK, NST>(p, g, row0, rows, nt, L0, L1, L2, L3);
     else if (rows > 64) dl_tile<DUAL, 128, BMMAX, BK, NST>(p, g, row0, rows, nt, L0, L1, L2, L3);
+    else dl_tile<DUAL, 64, BMMAX, BK, NST>(p, g, row0, rows, nt, L0, L1, L2, L3);
+  } else if constexpr (BMMAX >= 128) {
+    if (rows > 64) dl_tile<DUAL, 128, BMMAX, BK, NST>(p, g, row0, rows, nt, L0, L1, L2, L3);
     else dl_tile<DUAL, 64, BMMAX, BK, NST>(p, g, row0, rows, nt, L0, L1, L2, L3);
   } else {
     dl_tile<DUAL, BMMAX, BMMAX, BK, NST>(p, g, row0, rows, nt, L0, L1, L2, L3);
@@ -799,12 +810,27 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
     else
       kern<<<gu_grid, 256, 0, s>>>(p);
   };
+  // bf16: heavy tiles, then light tiles with their own kernel shape; the
+  // events (when requested) span both launches
+  const int groups = a.E + (a.has_shared ? 1 : 0);
+  auto launch_split = [&](auto heavy, auto light, const GemmParams& prm, int n_tiles, hipEvent_t eb, hipEvent_t ee) {
+    const int gh = grouped_grid(maxQ, n_tiles);
+    const int gl = grouped_grid(groups, n_tiles);
+    if (eb || ee) {
+      hipExtLaunchKernelGGL(heavy, dim3(gh), dim3(256), 0, s, eb, nullptr, 0, prm);
+      hipExtLaunchKernelGGL(light, dim3(gl), dim3(256), 0, s, nullptr, ee, 0, prm);
+    } else {
+      heavy<<<gh, 256, 0, s>>>(prm);
+      light<<<gl, 256, 0, s>>>(prm);
+    }
+  };
 
   if (a.wkind == W_FP8) {
     if (BM == 256) launch_gu(gemm_mfma_kernel<W_FP8, true, 256>);
     else launch_gu(gemm_mfma_kernel<W_FP8, true, 64>);
   } else {
-    launch_gu(gemm_dl_kernel<true, 256, kDlBK, kDlNST>);
+    launch_split(gemm_dl_kernel<true, 256, kDlBK, kDlNST, 1>, gemm_dl_kernel<true, 128, kDlBK, 3, 2>, p,
+                 (a.f + 127) / 128, a.ev_begin, a.ev_end);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
@@ -819,7 +845,8 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
     if (BM == 256) gemm_mfma_kernel<W_FP8, false, 256><<<dn_grid, 256, 0, s>>>(q);
     else gemm_mfma_kernel<W_FP8, false, 64><<<dn_grid, 256, 0, s>>>(q);
   } else {
-    gemm_dl_kernel<false, 256, kDlBK, kDlNST><<<dn_grid, 256, 0, s>>>(q);
+    launch_split(gemm_dl_kernel<false, 256, kDlBK, kDlNST, 1>, gemm_dl_kernel<false, 128, kDlBK, 3, 2>, q,
+                 (a.d + 255) / 256, nullptr, nullptr);
   }
   return hipGetLastError();
 }
