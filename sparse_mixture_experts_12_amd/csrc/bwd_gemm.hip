@@ -324,7 +324,9 @@ __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0
       for (int r = tid >> 6; r < 128; r += 4) {
         const int grow = row0 + 128 * h + r;
         const f32x4_t v = *reinterpret_cast<const f32x4_t*>(lrow(r) + ((chunk ^ (r & 15)) << 2));
-        if (grow < p.M && col < p.N) *reinterpret_cast<f32x4_t*>(C + (size_t)grow * p.N + col) = v;
+        // non-temporal: the gradients are not read again here, and the streaming
+        // writes would otherwise evict the group's rows that the next tiles reuse
+        if (grow < p.M && col < p.N) __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(C + (size_t)grow * p.N + col));
       }
     }
   } else {
