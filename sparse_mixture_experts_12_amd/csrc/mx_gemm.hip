@@ -47,7 +47,6 @@ namespace moe {
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kMxBK = 128;    // K per LDS stage (bytes of codes)
-constexpr int kMxNST = 2;     // LDS stages
 
 struct MxParams {
   const uint8_t* aq;             // DUAL: x codes [T, K]; !DUAL: H codes [rows, K]
@@ -169,9 +168,9 @@ hipError_t launch_mx_quantize(const void* in, bool in_f32, long rows, int cols, 
 // c of row r at chunk position aswz<8>(r, c): conflict-free 16-lane passes of
 // ds_read_b128 down a column of rows), then the stage's scale dwords (4 K
 // blocks) of the 256 A rows and of the 256 B rows.
-template <bool DUAL, int BMV>
+template <bool DUAL, int BMV, int BMMAX, int NST>
 __device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int rows, int nt, uint8_t* L0,
-                                        uint8_t* L1) {
+                                        uint8_t* L1, uint8_t* L2) {
   constexpr int BK = kMxBK;
   constexpr int WM = (BMV >= 256) ? 2 : 1, WN = 4 / WM;
   constexpr int NMAT = DUAL ? 2 : 1;
@@ -182,13 +181,14 @@ __device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int 
   constexpr int WROWS = BMV / WM;
   constexpr int A_LD = BMV / 8 / 4;                // 1 KB (8-row) A blocks per wave per stage
   constexpr int B_LD = 256 / 8 / 4;                // 1 KB B blocks per wave per stage
-  constexpr int LDS_B = 256 * BK;                  // B codes
-  constexpr int LDS_SA = 512 * BK;                 // A scale dwords [256]
+  constexpr int LDS_B = BMMAX * BK;                // B codes
+  constexpr int LDS_SA = (BMMAX + 256) * BK;       // A scale dwords [256]
   constexpr int LDS_SB = LDS_SA + 1024;            // B scale dwords [256]
   constexpr int NMF = MI * NI;                      // MFMAs per 64-K sub-step
   constexpr int NDS = 2 * (MI + NI) + MI + NI;      // LDS reads per sub-step (codes, scales)
   constexpr int NVM = A_LD + B_LD + 2;              // global -> LDS loads per stage
-  static_assert(BK == 128 && kMxNST == 2 && A_LD >= 1, "tile configuration");
+  static_assert(BK == 128 && (NST == 2 || NST == 3) && A_LD >= 1 && BMV <= BMMAX, "tile configuration");
+  static_assert((NST - 1) * NVM < 64, "outstanding loads exceed the vmcnt range");
   const int KS = p.K >> 5;                         // scale bytes per row
 
   const int tid = threadIdx.x;
@@ -320,12 +320,16 @@ __device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int 
   // then refilled two steps ahead (past the end: the last stage again, never
   // read), so every wave issues the same loads per step and the vmcnt
   // thresholds are exact.
+  // With three stages (light tiles) two steps of loads stay in flight: the
+  // wait after a stage's first sub-step only needs the next stage, and the
+  // stage just read is refilled NST steps ahead.
   const int nK = p.K / BK;
   i32x8_t fa0[MI], fb0[NI], fa1[MI], fb1[NI];
   uint32_t sa0[MI], sb0[NI], sa1[MI], sb1[NI];
   issue(L0, 0);
   issue(L1, min(1, nK - 1) * BK);
-  wait_vmem_le<NVM>();
+  if constexpr (NST > 2) issue(L2, min(2, nK - 1) * BK);
+  wait_vmem_le<(NST - 1) * NVM>();
   __builtin_amdgcn_s_barrier();
   frags(L0, 0, fa0, fb0, sa0, sb0);
 
@@ -334,20 +338,30 @@ __device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int 
     mfmas(fa0, fb0, sa0, sb0, I0{});
     sched_interleave<NMF, NDS, 0>();
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmem_le_lds0<0>();
+    wait_vmem_le_lds0<(NST - 2) * NVM>();
     __builtin_amdgcn_s_barrier();
-    issue(L, min(k + 2, nK - 1) * BK);
+    issue(L, min(k + NST, nK - 1) * BK);
     frags(Ln, 0, fa0, fb0, sa0, sb0);
     mfmas(fa1, fb1, sa1, sb1, I1{});
     sched_interleave<NMF, NDS, NVM>();
     __builtin_amdgcn_sched_barrier(0);
   };
   int k = 0;
-  for (; k + 2 <= nK; k += 2) {
-    step(L0, L1, k);
-    step(L1, L0, k + 1);
+  if constexpr (NST == 2) {
+    for (; k + 2 <= nK; k += 2) {
+      step(L0, L1, k);
+      step(L1, L0, k + 1);
+    }
+    if (k < nK) step(L0, L1, k);
+  } else {
+    for (; k + 3 <= nK; k += 3) {
+      step(L0, L1, k);
+      step(L1, L2, k + 1);
+      step(L2, L0, k + 2);
+    }
+    if (k < nK) step(L0, L1, k);
+    if (k + 1 < nK) step(L1, L2, k + 1);
   }
-  if (k < nK) step(L0, L1, k);
   wait_vmem_le<0>();
 
   // ---- epilogue ----
@@ -427,18 +441,28 @@ __device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int 
   }
 }
 
-template <bool DUAL>
+// SEG 1: heavy row tiles (more than 128 rows): 256-row LDS stages, two deep.
+// SEG 2: light row tiles (an expert's last tile, at most 128 rows): 128-row
+//        stages, three deep (two steps of loads in flight; these tiles do little
+//        MFMA work per stage and are bound by load latency).
+template <bool DUAL, int SEG>
 __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(MxParams p) {
-  constexpr int LDS_S = 512 * kMxBK + 2048;
+  constexpr int BMMAX = SEG == 1 ? 256 : 128;
+  constexpr int NST = SEG == 1 ? 2 : 3;
+  constexpr int LDS_S = (BMMAX + 256) * kMxBK + 2048;
   __shared__ __attribute__((aligned(1024))) uint8_t L0[LDS_S];
   __shared__ __attribute__((aligned(1024))) uint8_t L1[LDS_S];
+  __shared__ __attribute__((aligned(1024))) uint8_t L2[NST > 2 ? LDS_S : 16];
   constexpr int BN_MAT = DUAL ? 128 : 256;
   const int n_tiles = (p.N + BN_MAT - 1) / BN_MAT;
   int g, row0, rows, nt;
-  if (!decode_tile(p.sched, p.maxQ, p.E, n_tiles, &g, &row0, &rows, &nt)) return;
-  if (rows > 128) mx_tile<DUAL, 256>(p, g, row0, rows, nt, L0, L1);
-  else if (rows > 64) mx_tile<DUAL, 128>(p, g, row0, rows, nt, L0, L1);
-  else mx_tile<DUAL, 64>(p, g, row0, rows, nt, L0, L1);
+  if (!decode_tile<SEG>(p.sched, p.maxQ, p.E, n_tiles, &g, &row0, &rows, &nt)) return;
+  if constexpr (SEG == 1) {
+    mx_tile<DUAL, 256, BMMAX, NST>(p, g, row0, rows, nt, L0, L1, L2);
+  } else {
+    if (rows > 64) mx_tile<DUAL, 128, BMMAX, NST>(p, g, row0, rows, nt, L0, L1, L2);
+    else mx_tile<DUAL, 64, BMMAX, NST>(p, g, row0, rows, nt, L0, L1, L2);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -465,11 +489,20 @@ hipError_t launch_grouped_ffn_mx(const GroupedArgs& a, hipStream_t s) {
   p.sched = a.sched; p.maxQ = maxQ;
   p.k = a.assign_div; p.E = a.E; p.K = a.d; p.N = a.f; p.shared_row0 = a.routed_rows;
   p.hq_out = hq; p.hs_out = hs;
-  const int gu_grid = grouped_grid(maxQ, a.f / 128);
-  if (a.ev_begin || a.ev_end)
-    hipExtLaunchKernelGGL(gemm_mx_kernel<true>, dim3(gu_grid), dim3(256), 0, s, a.ev_begin, a.ev_end, 0, p);
-  else
-    gemm_mx_kernel<true><<<gu_grid, 256, 0, s>>>(p);
+  // heavy tiles, then light tiles; the events (when requested) span both
+  const int groups = a.E + (a.has_shared ? 1 : 0);
+  auto launch_split = [&](auto heavy, auto light, const MxParams& prm, int n_tiles, hipEvent_t eb, hipEvent_t ee) {
+    const int gh = grouped_grid(maxQ, n_tiles);
+    const int gl = grouped_grid(groups, n_tiles);
+    if (eb || ee) {
+      hipExtLaunchKernelGGL(heavy, dim3(gh), dim3(256), 0, s, eb, nullptr, 0, prm);
+      hipExtLaunchKernelGGL(light, dim3(gl), dim3(256), 0, s, nullptr, ee, 0, prm);
+    } else {
+      heavy<<<gh, 256, 0, s>>>(prm);
+      light<<<gl, 256, 0, s>>>(prm);
+    }
+  };
+  launch_split(gemm_mx_kernel<true, 1>, gemm_mx_kernel<true, 2>, p, a.f / 128, a.ev_begin, a.ev_end);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   MxParams q{};
@@ -479,7 +512,7 @@ hipError_t launch_grouped_ffn_mx(const GroupedArgs& a, hipStream_t s) {
   q.sched = a.sched; q.maxQ = maxQ;
   q.k = a.assign_div; q.E = a.E; q.K = a.f; q.N = a.d; q.shared_row0 = a.routed_rows;
   q.y_out = a.y;
-  gemm_mx_kernel<false><<<grouped_grid(maxQ, (a.d + 255) / 256), 256, 0, s>>>(q);
+  launch_split(gemm_mx_kernel<false, 1>, gemm_mx_kernel<false, 2>, q, (a.d + 255) / 256, nullptr, nullptr);
   return hipGetLastError();
 }
 
