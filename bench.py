@@ -413,7 +413,7 @@ def main():
         peak_f = FP32_PEAK_TFLOPS if f32 else (FP8_PEAK_TFLOPS if mx else BF16_PEAK_TFLOPS)
         ridge = peak_f * 1e12 / (HBM_PEAK_GBS * 1e9)
         kname = ("gemm_f32_kernel" if f32 else "gemm_mx_kernel" if mx else
-                 "gemm_mfma_kernel" if cfg.wdt == "fp8" else "gemm_dl_kernel")
+                 "gemm_dl_kernel")
         t = kern_ms / 1e3 if have_k else None
         if kflops / kbytes >= ridge:
             bound, peak, unit = "mfma", peak_f, "TFLOP/s"

@@ -13,7 +13,7 @@
 //            fp32 layer)
 //   down:    Y[r, n] = H[r] . Wd[:, n]  (fp32)
 //
-// Tiles are BM (256 or 64) permuted rows x 256 "B columns" (the gate/up GEMM
+// Tiles are up to 256 permuted rows x 256 "B columns" (the gate/up GEMM
 // takes 128 gate and the same 128 up columns), 256 threads (4 waves),
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  The weights stay in their
 // stored layout ([K, N], N contiguous) in LDS and reach the MFMA as
@@ -22,9 +22,10 @@
 //   bf16 weights (gemm_dl_kernel): A and B move global -> LDS directly
 //     (global_load_lds, 16 bytes per lane) into a ring of LDS stages, with
 //     the LDS swizzles applied on the source side.
-//   fp8 e4m3fn weights (gemm_mfma_kernel): loaded into registers, widened to
-//     bf16 (exact) and stored to LDS; the per-output-channel scales multiply
-//     the accumulators in the epilogue.
+//   fp8 e4m3fn weights (the same kernel, F8): the codes move global -> LDS
+//     the same way (half the bytes), ds_read_b64_tr_b8 gathers them
+//     K-contiguous and they widen to bf16 (exact) in registers; the
+//     per-output-channel scales multiply the accumulators in the epilogue.
 //   fp32 layer (gemm_f32_kernel): SIMT fp32 FMA.
 // Every LDS layout was checked against the bank-conflict counter on gfx950
 // (16-lane passes for 16-byte reads, 32-lane passes for 8-byte reads).
@@ -41,8 +42,6 @@
 #include "kernels.h"
 
 namespace moe {
-
-constexpr int kBK = 64;
 
 struct GemmParams {
   const bf16_t* x;               // DUAL: activations [T, d]
@@ -63,19 +62,6 @@ struct GemmParams {
   bf16_t* h_out;                 // DUAL output [rows, N]
   float* y_out;                  // !DUAL output [rows, N]
 };
-
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row ^ (row >> 3)) & 7); }
-
-// 8 fp8 e4m3fn codes -> 8 bf16 (exact: at most 4 significant bits).
-__device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(u32x2_t q) {
-  float v[8];
-  fp8x4_to_f32(q[0], v);
-  fp8x4_to_f32(q[1], v + 4);
-  u32x4_t w;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) w[p] = (__float_as_uint(v[2 * p]) >> 16) | (__float_as_uint(v[2 * p + 1]) & 0xffff0000u);
-  return w;
-}
 
 // LDS B tile: 64 K-rows x 256 output columns, N-contiguous as in global
 // memory.  A transposing LDS read touches four consecutive K-rows (512 bytes
@@ -104,240 +90,41 @@ __device__ __forceinline__ bf16x8_t load_b_frag(const bf16_t* Bs, int kbase, int
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// Register-staged (fp8) tile shapes, 4 waves: BM = 256 -> waves 2x2, 128 rows
-// x 128 B-columns each; BM = 64 -> 1x4, 64 x 64.  The LDS B tile always holds
-// 256 B-columns: 128 gate + 128 up columns for the gate/up GEMM, 256 columns
-// for the down GEMM.  PF = number of K steps whose global loads are in flight
-// ahead of the MFMAs (register stages); OCC = work-groups per CU (also used by
-// the direct-to-LDS kernels).
-template <int BM> struct TileCfg {
-  static constexpr int WM = (BM >= 256) ? 2 : 1;
-  static constexpr int WN = 4 / WM;
-  static constexpr int PF = (BM < 256) ? 2 : 1;
-  static constexpr int OCC = (BM == 64) ? 2 : 1;    // work-groups per CU
-};
+// fp8 LDS B tile: BK K-rows x 256 output columns of one byte, N-contiguous.
+// The 16-byte column chunk of K-row k sits at chunk ^ bkey8(k): the eight
+// K-rows one transposing read touches then fall on eight distinct chunks, and
+// the neighbouring 16-lane group (the next 16 columns, odd chunks) on the other
+// eight, so half a wave reads all 64 banks once.
+__device__ __forceinline__ int bkey8(int k) { return (k & 7) << 1; }
 
-template <int WK, bool DUAL, int BM>
-__global__ __launch_bounds__(256, TileCfg<BM>::OCC) void gemm_mfma_kernel(GemmParams p) {
-  constexpr int WM = TileCfg<BM>::WM, WN = TileCfg<BM>::WN, PF = TileCfg<BM>::PF;
-  constexpr int NMAT = DUAL ? 2 : 1;
-  constexpr int BN_MAT = DUAL ? 128 : 256;         // output columns per tile
-  constexpr int NI_MAT = BN_MAT / WN / 32;         // 32-wide MFMA column tiles per matrix per wave
-  constexpr int NI = NI_MAT * NMAT;
-  constexpr int MI = BM / WM / 32;                 // 32-row MFMA tiles per wave
-  constexpr int WROWS = BM / WM;                   // rows per wave
-  constexpr int A_CHUNKS = BM * 8 / 256;           // 16-byte chunks of A per thread per K step
-  constexpr int LDS_A = BM * kBK;                  // bf16 elements per stage
-  constexpr int LDS_B = 256 * kBK;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * (LDS_A + LDS_B)];
-
-  const int n_tiles = (p.N + BN_MAT - 1) / BN_MAT;
-  int g, row0, rows, nt;
-  if (!decode_tile(p.sched, p.maxQ, p.E, n_tiles, &g, &row0, &rows, &nt)) return;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WN;
-  const int wn = wave % WN;
-  const int n0 = nt * BN_MAT;
-  const bool shared = (g == p.E);
-
-  // ---- A row sources: rows past the tile's valid rows read its first row;
-  // their results are never stored, so no masking is needed. ----
-  const bf16_t* arow[A_CHUNKS];
-  int akc[A_CHUNKS], ar[A_CHUNKS];
-#pragma unroll
-  for (int i = 0; i < A_CHUNKS; ++i) {
-    const int c = tid + 256 * i;
-    const int r = c >> 3;
-    ar[i] = r;
-    akc[i] = c & 7;
-    const int grow = row0 + (r < rows ? r : 0);
-    if (DUAL) {
-      const int tok = shared ? (grow - p.shared_row0) : (p.sorted_assign[grow] / p.k);
-      arow[i] = p.x + (size_t)tok * p.K + akc[i] * 8;
-    } else {
-      arow[i] = p.a_rows + (size_t)grow * p.K + akc[i] * 8;
-    }
-  }
-  // ---- B: 8 chunks of 8 columns per thread, chunk c = tid + 256 i covers
-  // K-row (tid >> 5) + 8 i and tile columns 8 * (tid & 31) .. +7 (for the
-  // gate/up GEMM columns 0..127 come from W_gate, 128..255 from W_up).
-  // Columns past N read the last valid chunk and are never stored. ----
-  const int cc = tid & 31;
-  const int kr0 = tid >> 5;
-  const int mat = DUAL ? (cc >> 4) : 0;
-  int ncol = DUAL ? n0 + (cc & 15) * 8 : n0 + cc * 8;
-  if (ncol > p.N - 8) ncol = p.N - 8;
-  const size_t goff = shared ? 0 : (size_t)g * (size_t)p.K * p.N;
-  const void* Wbase = shared ? (mat ? p.Ws1 : p.Ws0) : (mat ? p.W1 : p.W0);
-  constexpr int ES = (WK == W_FP8) ? 1 : 2;
-  const unsigned char* bptr = (const unsigned char*)Wbase + (goff + (size_t)kr0 * p.N + ncol) * ES;
-  const size_t brow = (size_t)p.N * ES;
-
-  // register stages of prefetched global data (statically indexed)
-  u32x4_t sa[PF][A_CHUNKS];
-  u32x4_t sb[PF][WK == W_FP8 ? 1 : 8];
-  u32x2_t sb8[PF][WK == W_FP8 ? 8 : 1];
-
-  auto load_tile = [&](auto SI, int k0) {
-    constexpr int si = decltype(SI)::value;
-#pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) sa[si][i] = *reinterpret_cast<const u32x4_t*>(arow[i] + k0);
-    const unsigned char* bp = bptr + (size_t)k0 * brow;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if constexpr (WK == W_FP8) sb8[si][j] = *reinterpret_cast<const u32x2_t*>(bp + (size_t)(8 * j) * brow);
-      else sb[si][j] = *reinterpret_cast<const u32x4_t*>(bp + (size_t)(8 * j) * brow);
-    }
-  };
-  auto store_tile = [&](auto SI, int stage) {
-    constexpr int si = decltype(SI)::value;
-    bf16_t* As = lds + stage * (LDS_A + LDS_B);
-    bf16_t* Bs = As + LDS_A;
-#pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i)
-      *reinterpret_cast<u32x4_t*>(As + ar[i] * kBK + swz(ar[i], akc[i]) * 8) = sa[si][i];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      u32x4_t v;
-      if constexpr (WK == W_FP8) v = fp8x8_to_bf16x8(sb8[si][j]);
-      else v = sb[si][j];
-      *reinterpret_cast<u32x4_t*>(Bs + bswz(kr0 + 8 * j, cc * 8)) = v;
-    }
-  };
-
-  f32x16_t acc[MI][NI];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
-
-  const int l32 = lane & 31;
-  const int lhi = lane >> 5;
-  auto compute = [&](int stage) {
-    const bf16_t* As = lds + stage * (LDS_A + LDS_B);
-    const bf16_t* Bs = As + LDS_A;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int chunk = ks * 2 + lhi;
-      bf16x8_t af[MI], bfr[NI];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int row = wm * WROWS + mi * 32 + l32;
-        af[mi] = *reinterpret_cast<const bf16x8_t*>(As + row * kBK + swz(row, chunk) * 8);
-      }
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        int nbase;
-        if (DUAL) {
-          const int m_ = ni / NI_MAT, nl = ni % NI_MAT;
-          nbase = m_ * 128 + wn * (128 / WN) + nl * 32;
-        } else {
-          nbase = wn * (256 / WN) + ni * 32;
-        }
-        bfr[ni] = load_b_frag(Bs, ks * 16, nbase, lane);
-      }
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
-    }
-  };
-
-  const int nK = p.K / kBK;
-  // The steady-state loops issue and retire their loads unconditionally; the
-  // last steps are peeled, so no load is ever pending on a merge of control
-  // flow (which would make the compiler drain every load early).
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  if constexpr (PF == 1) {
-    // step k in LDS stage k&1; step k+1's loads are issued before step k's
-    // MFMAs and stored to the other stage after them
-    load_tile(I0{}, 0);
-    store_tile(I0{}, 0);
-    __syncthreads();
-    int k = 0;
-    for (; k + 1 < nK; ++k) {
-      load_tile(I0{}, (k + 1) * kBK);
-      __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the MFMAs
-      compute(k & 1);
-      store_tile(I0{}, (k + 1) & 1);
-      __syncthreads();
-    }
-    compute(k & 1);
-  } else {
-    // pairs of steps: LDS stages 0/1 hold steps k, k+1; the loads of steps
-    // k+2, k+3 are issued first and stored after both steps' MFMAs
-    load_tile(I0{}, 0);
-    load_tile(I1{}, (nK > 1 ? 1 : 0) * kBK);
-    store_tile(I0{}, 0);
-    store_tile(I1{}, 1);
-    __syncthreads();
-    int k = 0;
-    for (; k + 3 < nK; k += 2) {
-      load_tile(I0{}, (k + 2) * kBK);
-      load_tile(I1{}, (k + 3) * kBK);
-      __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the MFMAs
-      compute(0);
-      compute(1);
-      __syncthreads();
-      store_tile(I0{}, 0);
-      store_tile(I1{}, 1);
-      __syncthreads();
-    }
-    const int rem = nK - k;          // 1, 2 or 3 steps left; k and k+1 in LDS
-    if (rem == 3) {
-      load_tile(I0{}, (k + 2) * kBK);
-      compute(0);
-      compute(1);
-      __syncthreads();
-      store_tile(I0{}, 0);
-      __syncthreads();
-      compute(0);
-    } else {
-      compute(0);
-      if (rem == 2) compute(1);
-    }
-  }
-
-  // ---- epilogue ----
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
-#pragma unroll
-    for (int nl = 0; nl < NI_MAT; ++nl) {
-      const int col = n0 + wn * (BN_MAT / WN) + nl * 32 + l32;
-      if (col >= p.N) continue;
-      float sc0 = 1.f, sc1 = 1.f;
-      if (WK == W_FP8) {
-        if (shared) {
-          sc0 = p.ss0[col];
-          if (DUAL) sc1 = p.ss1[col];
-        } else {
-          sc0 = p.s0[(size_t)g * p.N + col];
-          if (DUAL) sc1 = p.s1[(size_t)g * p.N + col];
-        }
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * WROWS + mi * 32 + (v >> 2) * 8 + lhi * 4 + (v & 3);
-        if (r >= rows) continue;
-        const size_t orow = (size_t)(row0 + r) * p.N;
-        if (DUAL) {
-          const float gv = acc[mi][nl][v] * sc0;
-          const float uv = acc[mi][nl + NI_MAT][v] * sc1;
-          p.h_out[orow + col] = (bf16_t)f32_to_bf16(silu_f(gv) * uv);
-        } else {
-          p.y_out[orow + col] = acc[mi][nl][v] * sc0;
-        }
-      }
-    }
-  }
+// MFMA B fragment (8 consecutive K of one output column per lane, as bf16)
+// from the fp8 tile with one gfx950 byte-transposing read: within each group
+// of 16 lanes, input lane x supplies 8 bytes R_x and output lane 8a + b
+// receives R_a[b], R_{a+2}[b], ..., R_{a+14}[b].  Input lane x = a + 2j
+// therefore points at K-row kbase + j, columns c0 + 8a .. +7, and output lane
+// y holds column c0 + y, K-rows kbase .. +7.  e4m3 codes widen to bf16
+// exactly.
+__device__ __forceinline__ bf16x8_t load_b_frag8(const unsigned char* Bs, int kbase, int nbase, int lane) {
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) i32x2_t* lds_i32x2;
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const int g = lane >> 4, x = lane & 15;
+  const int n = nbase + 16 * (g & 1) + 8 * (x & 1);
+  const int k = kbase + 8 * (g >> 1) + (x >> 1);
+  const i32x2_t q = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (lds_i32x2)(Bs + k * 256 + ((((n >> 4) ^ bkey8(k)) << 4) | (n & 15))));
+  const bf16x2_t c0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)q[0], 1.f, false);
+  const bf16x2_t c1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)q[0], 1.f, true);
+  const bf16x2_t c2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)q[1], 1.f, false);
+  const bf16x2_t c3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)q[1], 1.f, true);
+  const bf16x8_t v = {c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
+  return v;
 }
+
+// Work-groups per CU for a kernel whose LDS stages hold BM rows.
+template <int BM> struct TileCfg {
+  static constexpr int OCC = (BM == 64) ? 2 : 1;
+};
 
 // ---------------------------------------------------------------------------
 // bf16 weights: operands move from global memory straight into LDS
@@ -352,8 +139,11 @@ __global__ __launch_bounds__(256, TileCfg<BM>::OCC) void gemm_mfma_kernel(GemmPa
 // ---------------------------------------------------------------------------
 // One output tile of at most BMV rows: waves 2 x 2 (128 rows x 128 B-columns
 // each) for BMV = 256, 1 x 4 (BMV rows x 64 B-columns each) for 128 and 64.
-// The LDS stages are sized for BMMAX rows.
-template <bool DUAL, int BMV, int BMMAX, int BK, int NST>
+// The LDS stages are sized for BMMAX rows.  F8: the weights are e4m3 codes with
+// per-output-column fp32 scales; their LDS tile holds the codes (half the
+// bytes of bf16), the fragment reads widen them to bf16 and the epilogue
+// applies the column scales.
+template <bool DUAL, int BMV, int BMMAX, int BK, int NST, bool F8 = false>
 __device__ __forceinline__ void dl_tile(const GemmParams& p, int g, int row0, int rows, int nt, bf16_t* L0,
                                         bf16_t* L1, bf16_t* L2, bf16_t* L3) {
   constexpr int WM = (BMV >= 256) ? 2 : 1, WN = 4 / WM;
@@ -366,11 +156,12 @@ __device__ __forceinline__ void dl_tile(const GemmParams& p, int g, int row0, in
   constexpr int CPR = BK / 8;                      // 16-byte chunks per A row
   constexpr int A_RPB = 64 / CPR;                  // A rows per 1 KB block
   constexpr int A_LD = BMV / A_RPB / 4;            // 1 KB A blocks per wave per step
-  constexpr int B_LD = BK / 2 / 4;                 // 1 KB B blocks (2 K-rows each) per wave per step
+  constexpr int B_RPB = F8 ? 4 : 2;                // K-rows per 1 KB B block
+  constexpr int B_LD = BK / B_RPB / 4;             // 1 KB B blocks per wave per step
   constexpr int SUB = BK / 16;                     // 16-wide MFMA sub-steps per step
   constexpr int LDS_A = BMMAX * BK;                // B tile offset inside a stage
   constexpr int NMF = MI * NI;                     // MFMAs per sub-step
-  constexpr int NDS = MI + 2 * NI;                 // LDS fragment reads per sub-step
+  constexpr int NDS = MI + (F8 ? 1 : 2) * NI;      // LDS fragment reads per sub-step
   constexpr int NVM = A_LD + B_LD;                 // global->LDS loads per step
   static_assert(SUB % 2 == 0 && NST >= 2 && NST <= 4 && A_LD >= 1 && B_LD % 2 == 0 && BMV <= BMMAX,
                 "tile configuration");
@@ -405,24 +196,35 @@ __device__ __forceinline__ void dl_tile(const GemmParams& p, int g, int row0, in
       asrc[i] = p.a_rows + (size_t)grow * p.K + gc * 8;
     }
   }
-  // ---- B sources: block b = B_LD wave + j holds K-rows 2 b, 2 b + 1; this
-  // lane fills K-row 2 b + lane / 32, LDS chunk lane % 32, i.e. tile column
-  // chunk (lane % 32) ^ (bswz_key(krow) / 8) (columns 0..127 gate, 128..255 up
-  // for the gate/up GEMM).  bswz_key depends on krow & 3 only, which is fixed
-  // by the parity of j.  Columns past N read the last valid chunk (never
-  // stored). ----
+  // ---- B sources: block b = B_LD wave + j holds K-rows B_RPB b .. +B_RPB-1.
+  // bf16: this lane fills K-row 2 b + lane / 32, LDS chunk lane % 32, i.e.
+  // tile column chunk (lane % 32) ^ (bswz_key(krow) / 8) of 8 columns; fp8:
+  // K-row 4 b + lane / 16, LDS chunk lane % 16, i.e. tile column chunk
+  // (lane % 16) ^ bkey8(krow) of 16 columns.  Tile columns 0..127 are gate,
+  // 128..255 up for the gate/up GEMM.  Both keys depend only on krow's bits
+  // that the parity of j fixes.  Columns past N read the last valid chunk
+  // (never stored). ----
+  constexpr int ES = F8 ? 1 : 2;                   // bytes per weight
+  constexpr int CW = 16 / ES;                      // columns per 16-byte chunk
   const size_t goff = shared ? 0 : (size_t)g * (size_t)p.K * p.N;
-  const size_t brow = (size_t)p.N * 2;
+  const size_t brow = (size_t)p.N * ES;
   const unsigned char* bsrc[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
-    const int krow = 2 * (B_LD * wave + par) + (lane >> 5);
-    const int gc = (lane & 31) ^ (bswz_key(krow) >> 3);
-    const int mat = DUAL ? (gc >> 4) : 0;
-    int ncol = DUAL ? n0 + (gc & 15) * 8 : n0 + gc * 8;
-    if (ncol > p.N - 8) ncol = p.N - 8;
+    int krow, gc;
+    if constexpr (F8) {
+      krow = 4 * (B_LD * wave + par) + (lane >> 4);
+      gc = (lane & 15) ^ bkey8(krow);
+    } else {
+      krow = 2 * (B_LD * wave + par) + (lane >> 5);
+      gc = (lane & 31) ^ (bswz_key(krow) >> 3);
+    }
+    constexpr int HALF = 128 / CW;                 // chunks per matrix in a gate/up tile
+    const int mat = DUAL ? (gc >= HALF) : 0;
+    int ncol = DUAL ? n0 + (gc % HALF) * CW : n0 + gc * CW;
+    if (ncol > p.N - CW) ncol = p.N - CW;
     const void* Wbase = shared ? (mat ? p.Ws1 : p.Ws0) : (mat ? p.W1 : p.W0);
-    bsrc[par] = (const unsigned char*)Wbase + (goff + (size_t)krow * p.N + ncol) * 2;
+    bsrc[par] = (const unsigned char*)Wbase + (goff + (size_t)krow * p.N + ncol) * ES;
   }
 
   auto issue = [&](bf16_t* L, int k0) {
@@ -432,7 +234,7 @@ __device__ __forceinline__ void dl_tile(const GemmParams& p, int g, int row0, in
     const size_t kb = (size_t)k0 * brow;
 #pragma unroll
     for (int j = 0; j < B_LD; ++j)
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(bsrc[j & 1] + kb + (size_t)(2 * (j & ~1)) * brow),
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(bsrc[j & 1] + kb + (size_t)(B_RPB * (j & ~1)) * brow),
                                        (lds_ptr_t)(L + LDS_A + (B_LD * wave + j) * 512), 16, 0, kBPolicy);
   };
 
@@ -462,7 +264,8 @@ __device__ __forceinline__ void dl_tile(const GemmParams& p, int g, int row0, in
       } else {
         nbase = wn * (256 / WN) + ni * 32;
       }
-      bfr[ni] = load_b_frag(L + LDS_A, ks * 16, nbase, lane);
+      if constexpr (F8) bfr[ni] = load_b_frag8(reinterpret_cast<const unsigned char*>(L + LDS_A), ks * 16, nbase, lane);
+      else bfr[ni] = load_b_frag(L + LDS_A, ks * 16, nbase, lane);
     }
   };
   auto mfmas = [&](const bf16x8_t* af, const bf16x8_t* bfr) {
@@ -551,13 +354,19 @@ __device__ __forceinline__ void dl_tile(const GemmParams& p, int g, int row0, in
       for (int nl = 0; nl < NI_MAT; ++nl) {
         const int c2 = n0 + wn * (BN_MAT / WN) + nl * 32 + (l32 & ~1);
         if (c2 >= p.N) continue;
+        float sc0 = 1.f, sc1 = 1.f;                // this lane's column scales (fp8)
+        if constexpr (F8) {
+          const size_t c = (shared ? 0 : (size_t)g * p.N) + c2 + (l32 & 1);
+          sc0 = (shared ? p.ss0 : p.s0)[c];
+          sc1 = (shared ? p.ss1 : p.s1)[c];
+        }
 #pragma unroll
         for (int v = 0; v < 16; v += 2) {
           float hv[2];
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
-            const float g = acc[mi][nl][v + i];
-            hv[i] = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * acc[mi][nl + NI_MAT][v + i];
+            const float g = acc[mi][nl][v + i] * sc0;
+            hv[i] = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * (acc[mi][nl + NI_MAT][v + i] * sc1);
           }
           const uint32_t own = pack_bf16x2(hv[0], hv[1]);
           const uint32_t x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)own, 0xB1, 0xF, 0xF, false);
@@ -574,10 +383,12 @@ __device__ __forceinline__ void dl_tile(const GemmParams& p, int g, int row0, in
       for (int nl = 0; nl < NI_MAT; ++nl) {
         const int col = n0 + wn * (BN_MAT / WN) + nl * 32 + l32;
         if (col >= p.N) continue;
+        float sc0 = 1.f;
+        if constexpr (F8) sc0 = shared ? p.ss0[col] : p.s0[(size_t)g * p.N + col];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = wm * WROWS + mi * 32 + (v >> 2) * 8 + lhi * 4 + (v & 3);
-          if (r < rows) p.y_out[(size_t)(row0 + r) * p.N + col] = acc[mi][nl][v];
+          if (r < rows) p.y_out[(size_t)(row0 + r) * p.N + col] = F8 ? acc[mi][nl][v] * sc0 : acc[mi][nl][v];
         }
       }
     }
@@ -591,9 +402,9 @@ __device__ __forceinline__ void dl_tile(const GemmParams& p, int g, int row0, in
 //        with LDS stages sized for 128 rows so that three of them fit and two
 //        steps of loads are in flight: light tiles do little MFMA work per
 //        stage and are bound by load latency.
-template <bool DUAL, int BMMAX, int BK, int NST, int SEG = 0>
+template <bool DUAL, int BMMAX, int BK, int NST, int SEG = 0, bool F8 = false>
 __global__ __launch_bounds__(256, TileCfg<BMMAX>::OCC) void gemm_dl_kernel(GemmParams p) {
-  constexpr int LDS_S = BMMAX * BK + 256 * BK;
+  constexpr int LDS_S = BMMAX * BK + (F8 ? 128 : 256) * BK;   // bf16 elements per stage
   __shared__ __attribute__((aligned(1024))) bf16_t L0[LDS_S];
   __shared__ __attribute__((aligned(1024))) bf16_t L1[LDS_S];
   __shared__ __attribute__((aligned(1024))) bf16_t L2[NST > 2 ? LDS_S : 8];
@@ -605,16 +416,16 @@ __global__ __launch_bounds__(256, TileCfg<BMMAX>::OCC) void gemm_dl_kernel(GemmP
   // An expert's last row tile is usually partial: run it with a body whose
   // MFMA work matches its rows (<= 64, <= 128) instead of the full height.
   if constexpr (SEG == 1) {
-    dl_tile<DUAL, 256, BMMAX, BK, NST>(p, g, row0, rows, nt, L0, L1, L2, L3);
+    dl_tile<DUAL, 256, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3);
   } else if constexpr (BMMAX >= 256) {
-    if (rows > 128) dl_tile<DUAL, 256, BMMAX, BK, NST>(p, g, row0, rows, nt, L0, L1, L2, L3);
-    else if (rows > 64) dl_tile<DUAL, 128, BMMAX, BK, NST>(p, g, row0, rows, nt, L0, L1, L2, L3);
-    else dl_tile<DUAL, 64, BMMAX, BK, NST>(p, g, row0, rows, nt, L0, L1, L2, L3);
+    if (rows > 128) dl_tile<DUAL, 256, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3);
+    else if (rows > 64) dl_tile<DUAL, 128, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3);
+    else dl_tile<DUAL, 64, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3);
   } else if constexpr (BMMAX >= 128) {
-    if (rows > 64) dl_tile<DUAL, 128, BMMAX, BK, NST>(p, g, row0, rows, nt, L0, L1, L2, L3);
-    else dl_tile<DUAL, 64, BMMAX, BK, NST>(p, g, row0, rows, nt, L0, L1, L2, L3);
+    if (rows > 64) dl_tile<DUAL, 128, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3);
+    else dl_tile<DUAL, 64, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3);
   } else {
-    dl_tile<DUAL, BMMAX, BMMAX, BK, NST>(p, g, row0, rows, nt, L0, L1, L2, L3);
+    dl_tile<DUAL, BMMAX, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3);
   }
 }
 
@@ -730,10 +541,7 @@ static int pick_bm(const GroupedArgs& a) {
   // bf16 weights: 256-row tiles, whose small last tiles run 64/128-row bodies.
   // Measured on MI355X, this also wins for skewed fine-grained loads (256
   // experts of 0..1507 rows): fewer row tiles re-read each expert's weights.
-  if (a.wkind == W_BF16) return 256;
-  // fp8 weights (register-staged kernel): 64-row tiles unless experts are large
-  const int avg = a.routed_rows / (a.E > 0 ? a.E : 1);
-  return avg >= 256 ? 256 : 64;
+  return 256;
 }
 
 int grouped_max_row_tiles(int routed_rows, int T, int E, int has_shared, int BM) {
@@ -802,16 +610,8 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   p.s0 = a.w.sg; p.s1 = a.w.su; p.ss0 = a.w.ssg; p.ss1 = a.w.ssu;
   p.K = a.d; p.N = a.f;
   p.h_out = (bf16_t*)a.h;
-  const int gu_grid = grouped_grid(maxQ, (a.f + 127) / 128);
-  // the gate/up GEMM is the dominant kernel: optional events stamp its dispatch
-  auto launch_gu = [&](auto kern) {
-    if (a.ev_begin || a.ev_end)
-      hipExtLaunchKernelGGL(kern, dim3(gu_grid), dim3(256), 0, s, a.ev_begin, a.ev_end, 0, p);
-    else
-      kern<<<gu_grid, 256, 0, s>>>(p);
-  };
-  // bf16: heavy tiles, then light tiles with their own kernel shape; the
-  // events (when requested) span both launches
+  // heavy tiles, then light tiles with their own kernel shape; the events
+  // (when requested) span both launches
   const int groups = a.E + (a.has_shared ? 1 : 0);
   auto launch_split = [&](auto heavy, auto light, const GemmParams& prm, int n_tiles, hipEvent_t eb, hipEvent_t ee) {
     const int gh = grouped_grid(maxQ, n_tiles);
@@ -826,8 +626,8 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   };
 
   if (a.wkind == W_FP8) {
-    if (BM == 256) launch_gu(gemm_mfma_kernel<W_FP8, true, 256>);
-    else launch_gu(gemm_mfma_kernel<W_FP8, true, 64>);
+    launch_split(gemm_dl_kernel<true, 256, kDlBK, kDlNST, 1, true>, gemm_dl_kernel<true, 128, kDlBK, 3, 2, true>, p,
+                 (a.f + 127) / 128, a.ev_begin, a.ev_end);
   } else {
     launch_split(gemm_dl_kernel<true, 256, kDlBK, kDlNST, 1>, gemm_dl_kernel<true, 128, kDlBK, 3, 2>, p,
                  (a.f + 127) / 128, a.ev_begin, a.ev_end);
@@ -840,10 +640,9 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   q.s0 = a.w.sd; q.s1 = nullptr; q.ss0 = a.w.ssd; q.ss1 = nullptr;
   q.K = a.f; q.N = a.d;
   q.y_out = a.y;
-  const int dn_grid = grouped_grid(maxQ, (a.d + 255) / 256);
   if (a.wkind == W_FP8) {
-    if (BM == 256) gemm_mfma_kernel<W_FP8, false, 256><<<dn_grid, 256, 0, s>>>(q);
-    else gemm_mfma_kernel<W_FP8, false, 64><<<dn_grid, 256, 0, s>>>(q);
+    launch_split(gemm_dl_kernel<false, 256, kDlBK, kDlNST, 1, true>, gemm_dl_kernel<false, 128, kDlBK, 3, 2, true>, q,
+                 (a.d + 255) / 256, nullptr, nullptr);
   } else {
     launch_split(gemm_dl_kernel<false, 256, kDlBK, kDlNST, 1>, gemm_dl_kernel<false, 128, kDlBK, 3, 2>, q,
                  (a.d + 255) / 256, nullptr, nullptr);
