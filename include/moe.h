@@ -180,8 +180,9 @@ int32_t moe_capacity(const moe_desc* desc);
  *   topk_idx [T, k] int32 out: slot 0 holds the largest logit
  *   topk_w   [T, k] fp32 out: softmax weights of the chosen experts
  *   logits   [T, E] fp32 out, or NULL
- * For T > 8 the workspace (moe_workspace_size) must be passed; for T <= 8 it
- * is not used and may be NULL. */
+ * For T > 8 the workspace (moe_workspace_size) must be passed.  For T <= 8 it
+ * may be NULL; when passed, routers with d * E > 65536 use it to spread the
+ * logit dot products over many work-groups (NULL: one work-group). */
 moe_status moe_route(const moe_desc* desc, const void* x, const moe_weights* w,
                      int32_t* topk_idx, float* topk_w, float* logits,
                      void* ws, size_t ws_bytes, hipStream_t stream);

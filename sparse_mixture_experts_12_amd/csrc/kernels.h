@@ -19,7 +19,7 @@ struct RouteArgs {
   int cap;          // -1: uncapped
   bool act_f32;
   float* logits;    // [T, E] or nullptr
-  double* part;     // fp64 partial logits (router_partial_bytes), T > kDecodeMaxT only
+  double* part;     // fp64 partial logits (router_partial_bytes); optional for T <= kDecodeMaxT
   int32_t* idx;     // [T, k]
   float* w;         // [T, k]
   int32_t* plan;    // decode plan or nullptr (T <= kDecodeMaxT only)

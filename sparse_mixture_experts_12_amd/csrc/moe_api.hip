@@ -317,6 +317,8 @@ moe_status moe_route(const moe_desc* desc, const void* x, const moe_weights* w, 
   if (desc->T > kDecodeMaxT) {
     if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
     part = (double*)((char*)ws + layout_of(desc).part);
+  } else if (ws && ws_bytes >= moe_workspace_size(desc)) {
+    part = (double*)((char*)ws + layout_of(desc).part);   // wide routers split their logits over d
   }
   return do_route(desc, x, w, topk_idx, topk_w, logits, part, nullptr, stream);
 }
@@ -438,7 +440,7 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w
 
   if (fused) {
     int32_t* plan = (int32_t*)(base + L.plan);
-    if ((st = do_route(desc, x, w, idx, tw, logits, nullptr, plan, stream)) != MOE_OK) return st;
+    if ((st = do_route(desc, x, w, idx, tw, logits, (double*)(base + L.part), plan, stream)) != MOE_OK) return st;
     if ((st = run_telemetry()) != MOE_OK) return st;
     DecodeArgs a{};
     a.x = x; a.plan = plan; a.topk_w = tw; a.w = expert_weights(w);

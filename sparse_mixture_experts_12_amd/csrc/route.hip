@@ -271,11 +271,13 @@ __device__ void wave_topk_rank(const float* lg, int E, int k, int renormalize, i
   }
 }
 
+constexpr int kSmallMaxS = 32;   // d slices of a split small-T router
+
 template <typename TIn, int MT>
 __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
     const TIn* __restrict__ x, const TIn* __restrict__ W, const float* __restrict__ bias, int T, int d,
     int E, int k, int renormalize, int cap, float* __restrict__ logits_out, int32_t* __restrict__ idx_out,
-    float* __restrict__ w_out, int32_t* __restrict__ plan) {
+    float* __restrict__ w_out, int32_t* __restrict__ plan, const double* __restrict__ part, int S) {
   __shared__ double wpart[kSmallThreads][8];
   __shared__ float lg[MT * 1024];
   __shared__ int32_t sidx[MT * 32];
@@ -284,7 +286,26 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const bool vec_ok = (E % 8) == 0;    // rows of W_g are 16-byte aligned only then
-  for (int e0 = 0; e0 < E; e0 += 512) {
+  if (part) {
+    // wide routers: the S fp64 partial sums over slices of d (split-K kernel)
+    // are added in slice order
+    for (int i = tid; i < T * E; i += kSmallThreads) {
+      const int t = i / E, e = i % E;
+      double v[kSmallMaxS];   // all loads in flight before the first add; past S: repeats, not added
+#pragma unroll
+      for (int z = 0; z < kSmallMaxS; ++z) v[z] = part[((size_t)min(z, S - 1) * T + t) * E + e];
+      double sum = 0.0;
+#pragma unroll
+      for (int z = 0; z < kSmallMaxS; ++z)
+        if (z < S) sum += v[z];
+      if (bias) sum += (double)bias[e];
+      const float lv = (float)sum;
+      lg[t * 1024 + e] = lv;
+      if (logits_out) logits_out[(size_t)t * E + e] = lv;
+    }
+    __syncthreads();
+  }
+  for (int e0 = 0; e0 < (part ? 0 : E); e0 += 512) {
     const int ne = min(E - e0, 512);
     const int nchunk = (ne + 7) / 8;
     int ecp = 1;
@@ -489,10 +510,24 @@ static void router_split(int T, int d, int E, int* S, int* dsplit) {
   *S = (d + *dsplit - 1) / *dsplit;
 }
 
+// Small T: one work-group reads all of W_g, which at d * E > 64 K weights
+// takes longer than spreading the dot products over split-K work-groups.
+static bool small_t_split(int d, int E) { return (long)d * E > 65536; }
+
+// Small T: at most kSmallMaxS slices (the top-k kernel adds them with all
+// loads in flight).
+static void router_split_any(int T, int d, int E, int* S, int* dsplit) {
+  router_split(T, d, E, S, dsplit);
+  if (T <= kDecodeMaxT && *S > kSmallMaxS) {
+    *dsplit = ((d + kSmallMaxS - 1) / kSmallMaxS + 15) / 16 * 16;
+    *S = (d + *dsplit - 1) / *dsplit;
+  }
+}
+
 size_t router_partial_bytes(int T, int d, int E) {
-  if (T <= kDecodeMaxT) return 0;
+  if (T <= kDecodeMaxT && !small_t_split(d, E)) return 0;
   int S, ds;
-  router_split(T, d, E, &S, &ds);
+  router_split_any(T, d, E, &S, &ds);
   return (size_t)S * T * E * sizeof(double);
 }
 
@@ -511,9 +546,17 @@ static hipError_t launch_partials(const void* x, const void* W, double* part, in
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.T <= kDecodeMaxT) {
     const int mt = a.T <= 1 ? 1 : a.T <= 2 ? 2 : a.T <= 4 ? 4 : 8;
+    int S = 0, ds = 0;
+    if (a.part && small_t_split(a.d, a.E)) {
+      router_split_any(a.T, a.d, a.E, &S, &ds);
+      hipError_t err = a.act_f32 ? launch_partials<float>(a.x, a.W_g, a.part, a.T, a.d, a.E, S, ds, s)
+                                 : launch_partials<bf16_t>(a.x, a.W_g, a.part, a.T, a.d, a.E, S, ds, s);
+      if (err != hipSuccess) return err;
+    }
+    const double* part = S ? a.part : nullptr;
 #define MOE_ROUTE_SMALL(TY, MTV)                                                                          \
   route_small_kernel<TY, MTV><<<1, kSmallThreads, 0, s>>>((const TY*)a.x, (const TY*)a.W_g, a.bias, a.T, a.d, a.E, a.k, \
-                                                a.renormalize, a.cap, a.logits, a.idx, a.w, a.plan)
+                                                a.renormalize, a.cap, a.logits, a.idx, a.w, a.plan, part, S)
     if (a.act_f32) {
       if (mt == 1) MOE_ROUTE_SMALL(float, 1); else if (mt == 2) MOE_ROUTE_SMALL(float, 2);
       else if (mt == 4) MOE_ROUTE_SMALL(float, 4); else MOE_ROUTE_SMALL(float, 8);

@@ -48,6 +48,9 @@ SMALL = {
     "f32_T1": C["tiny_f32"].with_(T=1, seed=21),
     "decode_T2_E300_k16": C["mixtral_decode"].with_(T=2, d=128, f=128, E=300, k=16, seed=22),
     "decode_T1": C["mixtral_decode"].with_(d=512, f=1024),
+    # enough work-groups (2 experts x 100 column slices) for the single fused
+    # decode kernel; the other small decode cases take the row-split kernels
+    "decode_T1_fused": C["mixtral_decode"].with_(d=256, f=6400, seed=26),
     "decode_T8": C["mixtral_decode_b8"].with_(d=512, f=1024),
     "decode_T5_shared_fp8": C["fp8_capacity_decode"].with_(T=5, d=256, E=16, f=256, shared=True),
     "decode_T3_fp8_cap": C["fp8_capacity_decode"].with_(T=3, d=256, E=8, f=128, k=4, capacity_factor=0.5),
@@ -119,6 +122,26 @@ def test_route_parity(name):
     np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=1e-6, atol=0)
     if cfg.renormalize:
         np.testing.assert_allclose(w.cpu().numpy().astype(np.float64).sum(1), 1.0, atol=1e-6)
+
+
+def test_small_t_route_without_workspace():
+    """A wide router (d * E > 65536) at T <= 8 splits its logits over d when
+    given the workspace and runs one work-group without it: same results."""
+    cfg = C["fine_grained"].with_(T=5)
+    inp = device_inputs(cfg, router_only=True)
+    desc = ops.desc_from_cfg(cfg)
+    outs = []
+    for ws in (ops.alloc_workspace(desc), None):
+        idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+        w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+        logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device="cuda")
+        ops.route(desc, inp["x"], ops.weights_struct(inp), idx, w, logits, ws)
+        torch.cuda.synchronize()
+        outs.append((idx.cpu(), w.cpu(), logits.cpu()))
+    np.testing.assert_array_equal(outs[0][0].numpy(), outs[1][0].numpy())
+    ulps = np.abs(outs[0][2].numpy().view(np.int32).astype(np.int64) - outs[1][2].numpy().view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1
+    np.testing.assert_allclose(outs[0][1].numpy(), outs[1][1].numpy(), rtol=1e-6, atol=0)
 
 
 def test_route_without_logits_output():
@@ -289,7 +312,8 @@ def test_forward_parity_small(name):
     np.testing.assert_array_equal(dev_counts.cpu().numpy(), ref["counts"])
 
 
-@pytest.mark.parametrize("name", ["decode_T1", "decode_T8", "decode_T5_shared_fp8", "decode_T3_fp8_cap"])
+@pytest.mark.parametrize("name", ["decode_T1", "decode_T1_fused", "decode_T8", "decode_T5_shared_fp8",
+                                  "decode_T3_fp8_cap"])
 def test_fused_decode_matches_grouped(name):
     cfg = SMALL[name]
     inp = device_inputs(cfg)
