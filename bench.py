@@ -86,6 +86,13 @@ def algorithmic_work(cfg, counts, touched):
     return bytes_total, flops, n_exp * wexp, es
 
 
+def split_decode(cfg) -> bool:
+    """Whether the decode path runs row-split (gate/up and down in two kernels):
+    the fused kernel would get fewer than 200 work-groups of 64 columns."""
+    units = min(cfg.T * cfg.k, cfg.E) + (1 if cfg.shared else 0)
+    return units * (cfg.f // 64) < 200
+
+
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if the
     kernel's sources are unchanged since the counters were taken."""
@@ -392,7 +399,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1) if have_k else None, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4) if have_k else None,
                 "traffic": measured_traffic("decode_ffn_kernel", cfg.name),
-                "kernel": "decode_ffn_kernel", "kernel_ms": round(kern_ms, 5) if have_k else None,
+                "kernel": "decode_ffn_kernel" + (" + decode_down_kernel" if split_decode(cfg) else ""), "kernel_ms": round(kern_ms, 5) if have_k else None,
                 "alg_bytes": int(kbytes)}
     else:
         # dominant kernel = grouped gate/up GEMM + SwiGLU: 2/3 of the expert flops.
@@ -423,7 +430,8 @@ def main():
             achieved = kbytes / t / 1e9 if have_k else None
         roof = {"bound": bound, "achieved": round(achieved, 2) if have_k else None, "peak": peak,
                 "unit": unit, "frac": round(achieved / peak, 4) if have_k else None,
-                "traffic": measured_traffic("gemm_gateup", cfg.name),
+                # the stored counters cover token-choice routing only
+                "traffic": measured_traffic("gemm_gateup", cfg.name) if args.routing == "token" else None,
                 "kernel": f"{kname}<gate/up>", "kernel_ms": round(kern_ms, 5) if have_k else None,
                 "alg_flops": int(kflops), "alg_bytes": int(kbytes),
                 "mfma_frac": round(kflops / t / 1e12 / peak_f, 4) if have_k else None,
