@@ -114,10 +114,35 @@ __global__ __launch_bounds__(256) void decode_ffn_kernel(DecodeParams p) {
   }
 
   // ---- stage x rows r_lo .. r_hi - 1 (bf16) as xs[r - r_lo][MT] ----
+  // 16-byte chunks c = (row block of 8, token), four per thread in flight;
+  // clamped indexes keep every load unconditional, tokens past T stage zeros
   bf16_t* xs = reinterpret_cast<bf16_t*>(smem);
-  for (int i = tid; i < (r_hi - r_lo) * MT; i += 256) {
-    const int r = r_lo + i / MT, t = i % MT;
-    xs[i] = (t < T) ? p.x[(size_t)t * d + r] : (bf16_t)0;
+  {
+    const int nchunk = (r_hi - r_lo) / 8 * MT;
+    for (int c0 = tid; c0 < nchunk; c0 += 4 * 256) {
+      u32x4_t v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = min(c0 + 256 * q, nchunk - 1);
+        const int t = c % MT, rb = c / MT;
+        v[q] = *reinterpret_cast<const u32x4_t*>(p.x + (size_t)min(t, T - 1) * d + r_lo + rb * 8);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = c0 + 256 * q;
+        if (c >= nchunk) break;
+        const int t = c % MT, rb = c / MT;
+        if (t >= T) v[q] = u32x4_t{0u, 0u, 0u, 0u};
+        if constexpr (MT == 1) {
+          *reinterpret_cast<u32x4_t*>(xs + rb * 8) = v[q];
+        } else {
+          const unsigned short* hv = reinterpret_cast<const unsigned short*>(&v[q]);
+          unsigned short* xw = reinterpret_cast<unsigned short*>(xs);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xw[(rb * 8 + j) * MT + t] = hv[j];
+        }
+      }
+    }
   }
   __syncthreads();
 
@@ -185,7 +210,7 @@ __global__ __launch_bounds__(256) void decode_ffn_kernel(DecodeParams p) {
     }
     return;
   }
-  float* hs = red + RG * 2 * MT * FS;                // [MT][FS]
+  float* hs = red + RG * 2 * MT * FS;                // [FS][MT]: a row's MT values are contiguous
   for (int i = tid; i < MT * FS; i += 256) {
     const int t = i / FS, col = i % FS;
     float g = 0.f, u = 0.f;
@@ -198,7 +223,7 @@ __global__ __launch_bounds__(256) void decode_ffn_kernel(DecodeParams p) {
       g *= shared ? p.w.ssg[fc] : p.w.sg[(size_t)e * p.f + fc];
       u *= shared ? p.w.ssu[fc] : p.w.su[(size_t)e * p.f + fc];
     }
-    hs[i] = silu_f(g) * u;
+    hs[col * MT + t] = silu_f(g) * u;
   }
   __syncthreads();
 
@@ -229,12 +254,13 @@ __global__ __launch_bounds__(256) void decode_ffn_kernel(DecodeParams p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) { wf[2 * q] = bf16lo(ww[q]); wf[2 * q + 1] = bf16hi(ww[q]); }
         }
+        float hv[MT];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const float hv = hs[t * FS + r0 + u];
+        for (int t = 0; t < MT; ++t) hv[t] = hs[(r0 + u) * MT + t];
 #pragma unroll
-          for (int j = 0; j < CPL; ++j) a2[t][j] = __fmaf_rn(hv, wf[j], a2[t][j]);
-        }
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) a2[t][j] = __fmaf_rn(hv[t], wf[j], a2[t][j]);
       }
     }
     const int col0 = ch * CPL;
@@ -272,7 +298,7 @@ __global__ __launch_bounds__(256) void decode_down_kernel(DecodeParams p, int DS
   constexpr int RG2 = 256 / CW;                // row groups
   constexpr int NR = FS2 / RG2;                // rows per thread (all loads in flight)
   static_assert(CW * RG2 == 256 && NR >= 1 && NR * RG2 == FS2, "down tile shape");
-  __shared__ float hs[MT][FS2];
+  __shared__ __attribute__((aligned(16))) float hs[FS2][MT];
   __shared__ float red[RG2][DW];
   const int s2 = blockIdx.x;
   const int unit = blockIdx.y;
@@ -330,7 +356,7 @@ __global__ __launch_bounds__(256) void decode_down_kernel(DecodeParams p, int DS
       }
       hv = silu_f(g) * u;
     }
-    hs[t][j] = hv;
+    hs[j][t] = hv;
   }
   __syncthreads();
   float a2[MT][CPL];
@@ -349,12 +375,13 @@ __global__ __launch_bounds__(256) void decode_down_kernel(DecodeParams p, int DS
 #pragma unroll
       for (int q = 0; q < 4; ++q) { wf[2 * q] = bf16lo(ww[q]); wf[2 * q + 1] = bf16hi(ww[q]); }
     }
+    float hv[MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const float hv = hs[t][rg + i * RG2];
+    for (int t = 0; t < MT; ++t) hv[t] = hs[rg + i * RG2][t];
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) a2[t][j] = __fmaf_rn(hv, wf[j], a2[t][j]);
-    }
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) a2[t][j] = __fmaf_rn(hv[t], wf[j], a2[t][j]);
   }
   const int n_slices = f / FS2;
 #pragma unroll
@@ -482,8 +509,8 @@ static DecodeSplit decode_split(int units, int d, int f, int es) {
   }
   const int groups = units * (f / sp.FS);
   sp.DS = 1;
-  while (sp.DS * 2 <= kMaxDS && sp.DS * 2 * groups <= 1024 && d % (sp.DS * 2) == 0 && d / (sp.DS * 2) >= 64)
-    sp.DS *= 2;
+  while (sp.DS * 2 <= kMaxDS && sp.DS * 2 * groups <= 1024 && d % (sp.DS * 16) == 0 && d / (sp.DS * 2) >= 64)
+    sp.DS *= 2;                                   // parts stay multiples of 8 rows
   sp.DW = 64;
   for (int c : {512, 256, 128}) {
     if (d % c == 0 && c * es <= 512) { sp.DW = c; break; }
