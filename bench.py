@@ -382,14 +382,29 @@ def main():
               f"max routed load {int(tel_routed.max())}, idle experts {int((tel_routed == 0).sum())}",
               file=sys.stderr, flush=True)
     kern_ms = float("nan")
+    step_pct = None
     if not args.no_kernel_events:
         stats = [ops.Stats(ev_begin=ev_b[i].value, ev_end=ev_e[i].value) for i in range(steps)]
         for i in range(steps):
             ops.forward(desc, inp["x"], wstructs[i % n_copies], out, ws, stats=stats[i])
         torch.cuda.synchronize()
         kern_ms = sum(hev.elapsed_ms(ev_b[i], ev_e[i]) for i in range(steps)) / steps
+        # Region 3: the same calls with an event between consecutive steps, for
+        # the per-step spread (each event adds a little to its step)
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        marks[0].record(stream)
+        for i in range(steps):
+            ops.forward(desc, inp["x"], wstructs[i % n_copies], out, ws, stats=plain)
+            marks[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+        q = lambda f: per_step[min(steps - 1, int(f * (steps - 1) + 0.5))]
+        step_pct = {"p10": round(q(0.1), 5), "p50": round(q(0.5), 5), "p90": round(q(0.9), 5)}
 
     bytes_total, flops, wbytes_used, _ = algorithmic_work(cfg, cnt, touched)
+    layer_peak = (FP32_PEAK_TFLOPS if cfg.act == "f32" else
+                  FP8_PEAK_TFLOPS if cfg.wdt == "mxfp8" else BF16_PEAK_TFLOPS)
+    t_star = max(bytes_total / (HBM_PEAK_GBS * 1e9), flops / (layer_peak * 1e12))
     have_k = kern_ms == kern_ms            # False when the second region was skipped
     if decode:
         # dominant kernel = fused decode FFN: streams the chosen experts' weights (+ x)
@@ -463,7 +478,12 @@ def main():
                    "weight_copies": n_copies, "telemetry": bool(args.telemetry), "routing": args.routing},
         "layer": {"alg_bytes": int(bytes_total), "alg_flops": int(flops),
                   "hbm_GBps": round(bytes_total / (ms_per_step / 1e3) / 1e9, 1),
-                  "tflops": round(flops / (ms_per_step / 1e3) / 1e12, 3)},
+                  "tflops": round(flops / (ms_per_step / 1e3) / 1e12, 3),
+                  # roofline time of the whole layer, max(bytes / HBM peak, flops / MFMA peak), against ms_per_step
+                  "t_star_ms": round(t_star * 1e3, 5), "t_star_frac": round(t_star * 1e3 / ms_per_step, 4),
+                  # per-step spread, from a third region with an event between steps
+                  "step_ms": step_pct,
+                  "experts_empty": int(cfg.E - touched)},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -625,7 +625,18 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
     }
   };
 
-  if (a.wkind == W_FP8) {
+  // fp8 layers whose groups all fit 64 rows (e.g. capped by the capacity):
+  // only light tiles exist, and 64-row stages (24 KB) let two work-groups
+  // share a CU, doubling the weight loads in flight
+  const bool small_f8 = a.wkind == W_FP8 && a.max_group_rows <= 64;
+  if (small_f8) {
+    const int gl = grouped_grid(groups, (a.f + 127) / 128);
+    if (a.ev_begin || a.ev_end)
+      hipExtLaunchKernelGGL(gemm_dl_kernel<true, 64, kDlBK, 3, 2, true>, dim3(gl), dim3(256), 0, s, a.ev_begin,
+                            a.ev_end, 0, p);
+    else
+      gemm_dl_kernel<true, 64, kDlBK, 3, 2, true><<<gl, 256, 0, s>>>(p);
+  } else if (a.wkind == W_FP8) {
     launch_split(gemm_dl_kernel<true, 256, kDlBK, kDlNST, 1, true>, gemm_dl_kernel<true, 128, kDlBK, 3, 2, true>, p,
                  (a.f + 127) / 128, a.ev_begin, a.ev_end);
   } else {
@@ -640,7 +651,9 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   q.s0 = a.w.sd; q.s1 = nullptr; q.ss0 = a.w.ssd; q.ss1 = nullptr;
   q.K = a.f; q.N = a.d;
   q.y_out = a.y;
-  if (a.wkind == W_FP8) {
+  if (small_f8) {
+    gemm_dl_kernel<false, 64, kDlBK, 3, 2, true><<<grouped_grid(groups, (a.d + 255) / 256), 256, 0, s>>>(q);
+  } else if (a.wkind == W_FP8) {
     launch_split(gemm_dl_kernel<false, 256, kDlBK, kDlNST, 1, true>, gemm_dl_kernel<false, 128, kDlBK, 3, 2, true>, q,
                  (a.d + 255) / 256, nullptr, nullptr);
   } else {

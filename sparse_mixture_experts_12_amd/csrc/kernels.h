@@ -62,6 +62,7 @@ struct GroupedArgs {
   int routed_rows;               // rows before the shared expert's (T*k; E*C for expert choice)
   int assign_div;                // token of permuted row r = sorted_assign[r] / assign_div (k; 1)
   int has_shared;
+  int max_group_rows;            // bound on any group's rows (capacity, T, the shared expert's T)
   int wkind;                     // WKind
   bool act_f32;
   float* y;                      // [routed_rows (+T), d] fp32

@@ -266,6 +266,12 @@ moe_status do_grouped(const moe_desc* d, const void* x, const moe_weights* w, co
   a.T = d->T; a.d = d->d; a.E = d->E; a.k = d->top_k; a.f = d->f; a.has_shared = d->has_shared;
   a.routed_rows = (int)routed_rows_of(d);
   a.assign_div = expert_choice(d) ? 1 : d->top_k;
+  {
+    // a token takes an expert at most once, so no group exceeds T rows; capacity caps routed groups
+    const int cap = capacity_of(d);
+    a.max_group_rows = cap > 0 && cap < d->T ? cap : d->T;
+    if (d->has_shared && d->T > a.max_group_rows) a.max_group_rows = d->T;
+  }
   a.wkind = wkind_of(d);
   a.act_f32 = d->act_dtype == MOE_F32;
   a.y = y;
