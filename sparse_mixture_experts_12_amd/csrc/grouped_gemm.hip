@@ -538,9 +538,9 @@ constexpr int kDlNST = 2;
 
 static int pick_bm(const GroupedArgs& a) {
   if (a.act_f32) return 64;
-  // bf16 weights: 256-row tiles, whose small last tiles run 64/128-row bodies.
-  // Measured on MI355X, this also wins for skewed fine-grained loads (256
-  // experts of 0..1507 rows): fewer row tiles re-read each expert's weights.
+  // bf16 and fp8 weights: 256-row tiles, whose small last tiles run 64/128-row
+  // bodies.  Measured on MI355X, this also wins for skewed fine-grained loads
+  // (256 experts of 0..1507 rows): fewer row tiles re-read each expert's weights.
   return 256;
 }
 
