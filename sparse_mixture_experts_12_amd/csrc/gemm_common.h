@@ -18,9 +18,10 @@ namespace moe {
 // SEG selects the segments one launch covers: 0 both (heavy first), 1 the
 // heavy segment only, 2 the light segment only (separate launches may use
 // kernels shaped for each segment).
+// lslot (optional): a light tile's index pt * n_tiles + nt in the light segment.
 template <int SEG = 0>
 __device__ __forceinline__ bool decode_tile(const int32_t* sched, int maxQ, int E, int n_tiles, int* g, int* row0,
-                                            int* rows, int* nt) {
+                                            int* rows, int* nt, int* lslot = nullptr) {
   const int QH = SEG == 2 ? 0 : sched[0], QL = SEG == 1 ? 0 : sched[1];
   const int totH = QH * n_tiles, totL = QL * n_tiles;
   const int perH = (totH + 7) >> 3, perL = (totL + 7) >> 3;
@@ -54,6 +55,7 @@ __device__ __forceinline__ bool decode_tile(const int32_t* sched, int maxQ, int 
   *row0 = ls[1];
   *rows = ls[2];
   *nt = logical - pt * n_tiles;
+  if (lslot) *lslot = logical;
   return true;
 }
 

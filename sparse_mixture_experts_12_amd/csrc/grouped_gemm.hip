@@ -61,6 +61,9 @@ struct GemmParams {
   int shared_row0;               // T*k
   bf16_t* h_out;                 // DUAL output [rows, N]
   float* y_out;                  // !DUAL output [rows, N]
+  float* y_part;                 // !DUAL light tiles split over K: parts 1.. [ksplit - 1][part_slots][128][256]
+  int ksplit;                    // K parts of the down GEMM's light tiles (1: none)
+  int part_slots;                // light-segment slots (groups x column tiles) covered by y_part
 };
 
 // LDS B tile: 64 K-rows x 256 output columns, N-contiguous as in global
@@ -143,9 +146,13 @@ template <int BM> struct TileCfg {
 // per-output-column fp32 scales; their LDS tile holds the codes (half the
 // bytes of bf16), the fragment reads widen them to bf16 and the epilogue
 // applies the column scales.
+//
+// K range: [k_lo, k_lo + nK BK).  A tile with kpart > 0 (light down tiles
+// split over K) writes its fp32 block to y_part slot `slot` instead of Y.
 template <bool DUAL, int BMV, int BMMAX, int BK, int NST, bool F8 = false>
 __device__ __forceinline__ void dl_tile(const GemmParams& p, int g, int row0, int rows, int nt, bf16_t* L0,
-                                        bf16_t* L1, bf16_t* L2, bf16_t* L3) {
+                                        bf16_t* L1, bf16_t* L2, bf16_t* L3, int k_lo, int nK, int kpart = 0,
+                                        int slot = 0) {
   constexpr int WM = (BMV >= 256) ? 2 : 1, WN = 4 / WM;
   constexpr int NMAT = DUAL ? 2 : 1;
   constexpr int BN_MAT = DUAL ? 128 : 256;
@@ -191,9 +198,9 @@ __device__ __forceinline__ void dl_tile(const GemmParams& p, int g, int row0, in
     const int grow = row0 + (r < rows ? r : 0);
     if (DUAL) {
       const int tok = shared ? (grow - p.shared_row0) : (p.sorted_assign[grow] / p.k);
-      asrc[i] = p.x + (size_t)tok * p.K + gc * 8;
+      asrc[i] = p.x + (size_t)tok * p.K + k_lo + gc * 8;
     } else {
-      asrc[i] = p.a_rows + (size_t)grow * p.K + gc * 8;
+      asrc[i] = p.a_rows + (size_t)grow * p.K + k_lo + gc * 8;
     }
   }
   // ---- B sources: block b = B_LD wave + j holds K-rows B_RPB b .. +B_RPB-1.
@@ -224,7 +231,7 @@ __device__ __forceinline__ void dl_tile(const GemmParams& p, int g, int row0, in
     int ncol = DUAL ? n0 + (gc % HALF) * CW : n0 + gc * CW;
     if (ncol > p.N - CW) ncol = p.N - CW;
     const void* Wbase = shared ? (mat ? p.Ws1 : p.Ws0) : (mat ? p.W1 : p.W0);
-    bsrc[par] = (const unsigned char*)Wbase + (goff + (size_t)krow * p.N + ncol) * ES;
+    bsrc[par] = (const unsigned char*)Wbase + (goff + (size_t)(k_lo + krow) * p.N + ncol) * ES;
   }
 
   auto issue = [&](bf16_t* L, int k0) {
@@ -284,7 +291,6 @@ __device__ __forceinline__ void dl_tile(const GemmParams& p, int g, int row0, in
   // then refilled NST steps ahead.  Past the end the refill repeats the last
   // step (never read again), so every wave issues the same number of loads per
   // step and the vmcnt thresholds below are exact.
-  const int nK = p.K / BK;
   bf16x8_t fa0[MI], fb0[NI], fa1[MI], fb1[NI];
   auto stage = [&](auto S) -> bf16_t* {
     constexpr int s = decltype(S)::value % NST;
@@ -385,10 +391,14 @@ __device__ __forceinline__ void dl_tile(const GemmParams& p, int g, int row0, in
         if (col >= p.N) continue;
         float sc0 = 1.f;
         if constexpr (F8) sc0 = shared ? p.ss0[col] : p.s0[(size_t)g * p.N + col];
+        // K part 0 (or no split): Y rows; parts 1..: this slot's 128 x 256 block
+        float* out = kpart == 0 ? p.y_out + (size_t)row0 * p.N + col
+                                : p.y_part + ((size_t)(kpart - 1) * p.part_slots + slot) * (128 * 256) + (col - n0);
+        const size_t ostride = kpart == 0 ? (size_t)p.N : 256;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = wm * WROWS + mi * 32 + (v >> 2) * 8 + lhi * 4 + (v & 3);
-          if (r < rows) p.y_out[(size_t)(row0 + r) * p.N + col] = F8 ? acc[mi][nl][v] * sc0 : acc[mi][nl][v];
+          if (r < rows) out[(size_t)r * ostride] = F8 ? acc[mi][nl][v] * sc0 : acc[mi][nl][v];
         }
       }
     }
@@ -411,21 +421,26 @@ __global__ __launch_bounds__(256, TileCfg<BMMAX>::OCC) void gemm_dl_kernel(GemmP
   __shared__ __attribute__((aligned(1024))) bf16_t L3[NST > 3 ? LDS_S : 8];
   constexpr int BN_MAT = DUAL ? 128 : 256;
   const int n_tiles = (p.N + BN_MAT - 1) / BN_MAT;
-  int g, row0, rows, nt;
-  if (!decode_tile<SEG>(p.sched, p.maxQ, p.E, n_tiles, &g, &row0, &rows, &nt)) return;
+  int g, row0, rows, nt, slot = 0;
+  if (!decode_tile<SEG>(p.sched, p.maxQ, p.E, n_tiles, &g, &row0, &rows, &nt, &slot)) return;
+  // light down tiles may be split over K (blockIdx.y = K part)
+  const int kparts = (!DUAL && SEG == 2) ? p.ksplit : 1;
+  const int kpart = (!DUAL && SEG == 2) ? (int)blockIdx.y : 0;
+  const int nK = p.K / BK / kparts;
+  const int k_lo = kpart * nK * BK;
   // An expert's last row tile is usually partial: run it with a body whose
   // MFMA work matches its rows (<= 64, <= 128) instead of the full height.
   if constexpr (SEG == 1) {
-    dl_tile<DUAL, 256, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3);
+    dl_tile<DUAL, 256, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
   } else if constexpr (BMMAX >= 256) {
-    if (rows > 128) dl_tile<DUAL, 256, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3);
-    else if (rows > 64) dl_tile<DUAL, 128, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3);
-    else dl_tile<DUAL, 64, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3);
+    if (rows > 128) dl_tile<DUAL, 256, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
+    else if (rows > 64) dl_tile<DUAL, 128, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
+    else dl_tile<DUAL, 64, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
   } else if constexpr (BMMAX >= 128) {
-    if (rows > 64) dl_tile<DUAL, 128, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3);
-    else dl_tile<DUAL, 64, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3);
+    if (rows > 64) dl_tile<DUAL, 128, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
+    else dl_tile<DUAL, 64, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
   } else {
-    dl_tile<DUAL, BMMAX, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3);
+    dl_tile<DUAL, BMMAX, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
   }
 }
 
@@ -536,6 +551,61 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
 constexpr int kDlBK = 64;
 constexpr int kDlNST = 2;
 
+// The down GEMM's light tiles (an expert's last <= 128 rows) run after all of
+// its heavy tiles.  When there are few of them (groups x column tiles <= 256,
+// e.g. 8 Mixtral experts x 16) that launch leaves most CUs idle for a whole
+// K loop, so each light tile is split into up to 4 K parts on as many
+// work-groups; part 0 writes Y, the others fp32 blocks that a small kernel
+// then adds to Y in part order (deterministic).
+int grouped_down_ksplit(int d, int f, int E, int has_shared, int wkind, int act_f32) {
+  if (act_f32 || wkind == W_MX) return 1;
+  const int slots = (E + (has_shared ? 1 : 0)) * ((d + 255) / 256);
+  if (slots > 256) return 1;
+  for (int ks : {4, 2})
+    if (f % (ks * kDlBK) == 0) return ks;
+  return 1;
+}
+
+size_t grouped_down_part_bytes(int d, int f, int E, int has_shared, int wkind, int act_f32) {
+  const int ks = grouped_down_ksplit(d, f, E, has_shared, wkind, act_f32);
+  const size_t slots = (size_t)(E + (has_shared ? 1 : 0)) * ((d + 255) / 256);
+  return (size_t)(ks - 1) * slots * 128 * 256 * sizeof(float);
+}
+
+// Y[rows of light slot, its 256 columns] += parts 1 .. ksplit - 1, in order.
+// Work-group (slot, 16-row block); each thread owns one column and issues the
+// loads of all its 16 rows (clamped, so none waits behind a branch) before
+// adding.
+constexpr int kReduceRows = 16;
+__global__ __launch_bounds__(256) void down_split_reduce_kernel(const int32_t* __restrict__ sched, int maxQ, int E,
+                                                                int n_tiles, int N, int ksplit, int part_slots,
+                                                                const float* __restrict__ part,
+                                                                float* __restrict__ y) {
+  const int slot = blockIdx.x;
+  if (slot >= sched[1] * n_tiles) return;
+  const int pt = slot / n_tiles, nt = slot - pt * n_tiles;
+  const int32_t* ls = sched + kSchedHead + 4 * maxQ + (E + 1) + 3 * pt;
+  const int row0 = ls[1], rows = ls[2];
+  const int rb = blockIdx.y * kReduceRows;
+  if (rb >= rows) return;
+  const int c = threadIdx.x, col = nt * 256 + c;
+  if (col >= N) return;
+  float v[kReduceRows];
+#pragma unroll
+  for (int i = 0; i < kReduceRows; ++i) v[i] = y[(size_t)(row0 + min(rb + i, rows - 1)) * N + col];
+  for (int kp = 1; kp < ksplit; ++kp) {
+    const float* pp = part + ((size_t)(kp - 1) * part_slots + slot) * (128 * 256) + c;
+    float w[kReduceRows];
+#pragma unroll
+    for (int i = 0; i < kReduceRows; ++i) w[i] = pp[min(rb + i, rows - 1) * 256];
+#pragma unroll
+    for (int i = 0; i < kReduceRows; ++i) v[i] += w[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kReduceRows; ++i)
+    if (rb + i < rows) y[(size_t)(row0 + rb + i) * N + col] = v[i];
+}
+
 static int pick_bm(const GroupedArgs& a) {
   if (a.act_f32) return 64;
   // bf16 and fp8 weights: 256-row tiles, whose small last tiles run 64/128-row
@@ -610,15 +680,17 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   p.s0 = a.w.sg; p.s1 = a.w.su; p.ss0 = a.w.ssg; p.ss1 = a.w.ssu;
   p.K = a.d; p.N = a.f;
   p.h_out = (bf16_t*)a.h;
+  p.ksplit = 1;
   // heavy tiles, then light tiles with their own kernel shape; the events
   // (when requested) span both launches
   const int groups = a.E + (a.has_shared ? 1 : 0);
-  auto launch_split = [&](auto heavy, auto light, const GemmParams& prm, int n_tiles, hipEvent_t eb, hipEvent_t ee) {
+  auto launch_split = [&](auto heavy, auto light, const GemmParams& prm, int n_tiles, hipEvent_t eb, hipEvent_t ee,
+                          int kparts = 1) {
     const int gh = grouped_grid(maxQ, n_tiles);
-    const int gl = grouped_grid(groups, n_tiles);
+    const dim3 gl(grouped_grid(groups, n_tiles), kparts);
     if (eb || ee) {
       hipExtLaunchKernelGGL(heavy, dim3(gh), dim3(256), 0, s, eb, nullptr, 0, prm);
-      hipExtLaunchKernelGGL(light, dim3(gl), dim3(256), 0, s, nullptr, ee, 0, prm);
+      hipExtLaunchKernelGGL(light, gl, dim3(256), 0, s, nullptr, ee, 0, prm);
     } else {
       heavy<<<gh, 256, 0, s>>>(prm);
       light<<<gl, 256, 0, s>>>(prm);
@@ -651,15 +723,23 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   q.s0 = a.w.sd; q.s1 = nullptr; q.ss0 = a.w.ssd; q.ss1 = nullptr;
   q.K = a.f; q.N = a.d;
   q.y_out = a.y;
+  const int dn_tiles = (a.d + 255) / 256;
+  q.ksplit = small_f8 ? 1 : grouped_down_ksplit(a.d, a.f, a.E, a.has_shared, a.wkind, a.act_f32);
+  q.part_slots = groups * dn_tiles;
+  q.y_part = a.y_part;
   if (small_f8) {
-    gemm_dl_kernel<false, 64, kDlBK, 3, 2, true><<<grouped_grid(groups, (a.d + 255) / 256), 256, 0, s>>>(q);
+    gemm_dl_kernel<false, 64, kDlBK, 3, 2, true><<<grouped_grid(groups, dn_tiles), 256, 0, s>>>(q);
   } else if (a.wkind == W_FP8) {
     launch_split(gemm_dl_kernel<false, 256, kDlBK, kDlNST, 1, true>, gemm_dl_kernel<false, 128, kDlBK, 3, 2, true>, q,
-                 (a.d + 255) / 256, nullptr, nullptr);
+                 dn_tiles, nullptr, nullptr, q.ksplit);
   } else {
     launch_split(gemm_dl_kernel<false, 256, kDlBK, kDlNST, 1>, gemm_dl_kernel<false, 128, kDlBK, 3, 2>, q,
-                 (a.d + 255) / 256, nullptr, nullptr);
+                 dn_tiles, nullptr, nullptr, q.ksplit);
   }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (q.ksplit > 1)
+    down_split_reduce_kernel<<<dim3(q.part_slots, 128 / kReduceRows), 256, 0, s>>>(
+        a.sched, maxQ, a.E, dn_tiles, a.d, q.ksplit, q.part_slots, a.y_part, a.y);
   return hipGetLastError();
 }
 

@@ -68,6 +68,7 @@ struct GroupedArgs {
   float* y;                      // [routed_rows (+T), d] fp32
   void* h;                       // [routed_rows (+T), f] bf16 (or fp32 for act f32)
   int32_t* sched;                // schedule scratch
+  float* y_part;                 // down light tiles' K parts 1.. (grouped_down_part_bytes)
   uint8_t* mx_xq;                // W_MX: x codes [T, d] (scratch)
   uint8_t* mx_xs;                // W_MX: x scales [T, d/32]
   uint8_t* mx_hs;                // W_MX: H scales [rows, f/32]; h holds the H codes
@@ -77,6 +78,8 @@ size_t grouped_sched_ints(int routed_rows, int T, int E, int has_shared);
 int grouped_max_row_tiles(int routed_rows, int T, int E, int has_shared, int BM);
 int grouped_grid(int maxQ, int n_tiles);
 hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s);
+int grouped_down_ksplit(int d, int f, int E, int has_shared, int wkind, int act_f32);
+size_t grouped_down_part_bytes(int d, int f, int E, int has_shared, int wkind, int act_f32);
 hipError_t launch_grouped_ffn_mx(const GroupedArgs& a, hipStream_t s);
 // OCP MXFP8 quantisation of rows x cols values (cols % 32 == 0) along rows
 hipError_t launch_mx_quantize(const void* in, bool in_f32, long rows, int cols, uint8_t* codes, uint8_t* scales,

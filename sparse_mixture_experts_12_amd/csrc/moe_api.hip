@@ -153,7 +153,8 @@ int capacity_of(const moe_desc* d) {
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t part, idx, w, plan, counts, offsets, sorted, inv, ndrop, rank, sched, h, hs, xq, xs, y, partial, logits, tel;
+  size_t part, idx, w, plan, counts, offsets, sorted, inv, ndrop, rank, sched, h, hs, xq, xs, y, ypart, partial, logits,
+      tel;
   size_t ec_scores, ec_pos, ec_w, ec_crow, ec_count, ec_sorted, ec_offsets, total;
 };
 
@@ -161,6 +162,8 @@ bool decode_capable(const moe_desc* d) {
   return d->T <= MOE_FUSED_DECODE_MAX_T && d->act_dtype == MOE_BF16 &&
          (d->w_dtype == MOE_BF16 || d->w_dtype == MOE_FP8_E4M3);
 }
+
+int wkind_of(const moe_desc* d);
 
 Layout layout_of(const moe_desc* d) {
   Layout L{};
@@ -190,6 +193,7 @@ Layout layout_of(const moe_desc* d) {
   L.xq = take(mx ? T * d->d : 0);                                            // MXFP8: x codes
   L.xs = take(mx ? T * (d->d / 32) : 0);                                     // MXFP8: x scales
   L.y = take(rows * d->d * 4);
+  L.ypart = take(grouped_down_part_bytes(d->d, d->f, d->E, d->has_shared, wkind_of(d), d->act_dtype == MOE_F32));
   L.partial = decode_capable(d) ? take(decode_partial_bytes(d->T, d->d, d->E, d->top_k, d->f, d->has_shared,
                                                            d->w_dtype == MOE_FP8_E4M3 ? W_FP8 : W_BF16))
                                 : take(0);
@@ -280,6 +284,7 @@ moe_status do_grouped(const moe_desc* d, const void* x, const moe_weights* w, co
   a.mx_xq = (uint8_t*)(ws + L.xq);
   a.mx_xs = (uint8_t*)(ws + L.xs);
   a.sched = (int32_t*)(ws + L.sched);
+  a.y_part = (float*)(ws + L.ypart);
   a.ev_begin = eb; a.ev_end = ee;
   return hip_status(launch_grouped_ffn(a, s), "grouped_ffn");
 }
