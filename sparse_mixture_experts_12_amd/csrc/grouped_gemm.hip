@@ -558,11 +558,12 @@ constexpr int kDlNST = 2;
 // work-groups; part 0 writes Y, the others fp32 blocks that a small kernel
 // then adds to Y in part order (deterministic).
 int grouped_down_ksplit(int d, int f, int E, int has_shared, int wkind, int act_f32) {
-  if (act_f32 || wkind == W_MX) return 1;
+  if (act_f32) return 1;
   const int slots = (E + (has_shared ? 1 : 0)) * ((d + 255) / 256);
   if (slots > 256) return 1;
+  const int bk = wkind == W_MX ? 128 : kDlBK;     // K per LDS stage of the light kernel
   for (int ks : {4, 2})
-    if (f % (ks * kDlBK) == 0) return ks;
+    if (f % (ks * bk) == 0) return ks;
   return 1;
 }
 
@@ -604,6 +605,13 @@ __global__ __launch_bounds__(256) void down_split_reduce_kernel(const int32_t* _
 #pragma unroll
   for (int i = 0; i < kReduceRows; ++i)
     if (rb + i < rows) y[(size_t)(row0 + rb + i) * N + col] = v[i];
+}
+
+hipError_t launch_down_split_reduce(const int32_t* sched, int maxQ, int E, int n_tiles, int N, int ksplit,
+                                    int part_slots, const float* part, float* y, hipStream_t s) {
+  down_split_reduce_kernel<<<dim3(part_slots, 128 / kReduceRows), 256, 0, s>>>(sched, maxQ, E, n_tiles, N, ksplit,
+                                                                               part_slots, part, y);
+  return hipGetLastError();
 }
 
 static int pick_bm(const GroupedArgs& a) {
@@ -738,8 +746,7 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (q.ksplit > 1)
-    down_split_reduce_kernel<<<dim3(q.part_slots, 128 / kReduceRows), 256, 0, s>>>(
-        a.sched, maxQ, a.E, dn_tiles, a.d, q.ksplit, q.part_slots, a.y_part, a.y);
+    return launch_down_split_reduce(a.sched, maxQ, a.E, dn_tiles, a.d, q.ksplit, q.part_slots, a.y_part, a.y, s);
   return hipGetLastError();
 }
 

@@ -80,6 +80,9 @@ int grouped_grid(int maxQ, int n_tiles);
 hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s);
 int grouped_down_ksplit(int d, int f, int E, int has_shared, int wkind, int act_f32);
 size_t grouped_down_part_bytes(int d, int f, int E, int has_shared, int wkind, int act_f32);
+// Y rows of the light down tiles += their K parts 1 .. ksplit - 1, in order
+hipError_t launch_down_split_reduce(const int32_t* sched, int maxQ, int E, int n_tiles, int N, int ksplit,
+                                    int part_slots, const float* part, float* y, hipStream_t s);
 hipError_t launch_grouped_ffn_mx(const GroupedArgs& a, hipStream_t s);
 // OCP MXFP8 quantisation of rows x cols values (cols % 32 == 0) along rows
 hipError_t launch_mx_quantize(const void* in, bool in_f32, long rows, int cols, uint8_t* codes, uint8_t* scales,

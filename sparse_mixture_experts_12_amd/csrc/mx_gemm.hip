@@ -67,6 +67,9 @@ struct MxParams {
   uint8_t* hq_out;               // DUAL: H codes [rows, N]
   uint8_t* hs_out;               // DUAL: H scales [rows, N / 32]
   float* y_out;                  // !DUAL: [rows, N]
+  float* y_part;                 // !DUAL light tiles split over K: parts 1.. [ksplit - 1][part_slots][128][256]
+  int ksplit;                    // K parts of the down GEMM's light tiles (1: none)
+  int part_slots;
 };
 
 // Per 16-bit half, the largest value over the 32 lanes of each half-wave
@@ -168,9 +171,11 @@ hipError_t launch_mx_quantize(const void* in, bool in_f32, long rows, int cols, 
 // c of row r at chunk position aswz<8>(r, c): conflict-free 16-lane passes of
 // ds_read_b128 down a column of rows), then the stage's scale dwords (4 K
 // blocks) of the 256 A rows and of the 256 B rows.
+// K range [k_lo, k_lo + nK BK); K part kpart > 0 writes its fp32 block to
+// y_part slot `slot` (light down tiles split over K).
 template <bool DUAL, int BMV, int BMMAX, int NST>
 __device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int rows, int nt, uint8_t* L0,
-                                        uint8_t* L1, uint8_t* L2) {
+                                        uint8_t* L1, uint8_t* L2, int k_lo, int nK, int kpart, int slot) {
   constexpr int BK = kMxBK;
   constexpr int WM = (BMV >= 256) ? 2 : 1, WN = 4 / WM;
   constexpr int NMAT = DUAL ? 2 : 1;
@@ -249,7 +254,8 @@ __device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int 
   const uint8_t* bsbase = b_scales(bmat) + (gN + bc) * (size_t)KS;
   const uint32_t bsoff = (uint32_t)lane * (uint32_t)KS;
 
-  auto issue = [&](uint8_t* L, int k0) {
+  auto issue = [&](uint8_t* L, int kr) {
+    const int k0 = k_lo + kr;
 #pragma unroll
     for (int i = 0; i < A_LD; ++i)
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(p.aq + (aoff[i] + (uint32_t)k0)),
@@ -323,7 +329,6 @@ __device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int 
   // With three stages (light tiles) two steps of loads stay in flight: the
   // wait after a stage's first sub-step only needs the next stage, and the
   // stage just read is refilled NST steps ahead.
-  const int nK = p.K / BK;
   i32x8_t fa0[MI], fb0[NI], fa1[MI], fb1[NI];
   uint32_t sa0[MI], sb0[NI], sa1[MI], sb1[NI];
   issue(L0, 0);
@@ -431,10 +436,14 @@ __device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int 
       for (int ni = 0; ni < NI; ++ni) {
         const int col = n0 + wn * (256 / WN) + ni * 32 + l32;
         if (col >= p.N) continue;
+        // K part 0 (or no split): Y rows; parts 1..: this slot's 128 x 256 block
+        float* out = kpart == 0 ? p.y_out + (size_t)row0 * p.N + col
+                                : p.y_part + ((size_t)(kpart - 1) * p.part_slots + slot) * (128 * 256) + (col - n0);
+        const size_t ostride = kpart == 0 ? (size_t)p.N : 256;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = wm * WROWS + mi * 32 + (v >> 2) * 8 + lhi * 4 + (v & 3);
-          if (r < rows) p.y_out[(size_t)(row0 + r) * p.N + col] = acc[mi][ni][v];
+          if (r < rows) out[(size_t)r * ostride] = acc[mi][ni][v];
         }
       }
     }
@@ -455,13 +464,18 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(MxParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t L2[NST > 2 ? LDS_S : 16];
   constexpr int BN_MAT = DUAL ? 128 : 256;
   const int n_tiles = (p.N + BN_MAT - 1) / BN_MAT;
-  int g, row0, rows, nt;
-  if (!decode_tile<SEG>(p.sched, p.maxQ, p.E, n_tiles, &g, &row0, &rows, &nt)) return;
+  int g, row0, rows, nt, slot = 0;
+  if (!decode_tile<SEG>(p.sched, p.maxQ, p.E, n_tiles, &g, &row0, &rows, &nt, &slot)) return;
+  // light down tiles may be split over K (blockIdx.y = K part)
+  const int kparts = (!DUAL && SEG == 2) ? p.ksplit : 1;
+  const int kpart = (!DUAL && SEG == 2) ? (int)blockIdx.y : 0;
+  const int nK = p.K / kMxBK / kparts;
+  const int k_lo = kpart * nK * kMxBK;
   if constexpr (SEG == 1) {
-    mx_tile<DUAL, 256, BMMAX, NST>(p, g, row0, rows, nt, L0, L1, L2);
+    mx_tile<DUAL, 256, BMMAX, NST>(p, g, row0, rows, nt, L0, L1, L2, k_lo, nK, kpart, slot);
   } else {
-    if (rows > 64) mx_tile<DUAL, 128, BMMAX, NST>(p, g, row0, rows, nt, L0, L1, L2);
-    else mx_tile<DUAL, 64, BMMAX, NST>(p, g, row0, rows, nt, L0, L1, L2);
+    if (rows > 64) mx_tile<DUAL, 128, BMMAX, NST>(p, g, row0, rows, nt, L0, L1, L2, k_lo, nK, kpart, slot);
+    else mx_tile<DUAL, 64, BMMAX, NST>(p, g, row0, rows, nt, L0, L1, L2, k_lo, nK, kpart, slot);
   }
 }
 
@@ -489,11 +503,13 @@ hipError_t launch_grouped_ffn_mx(const GroupedArgs& a, hipStream_t s) {
   p.sched = a.sched; p.maxQ = maxQ;
   p.k = a.assign_div; p.E = a.E; p.K = a.d; p.N = a.f; p.shared_row0 = a.routed_rows;
   p.hq_out = hq; p.hs_out = hs;
+  p.ksplit = 1;
   // heavy tiles, then light tiles; the events (when requested) span both
   const int groups = a.E + (a.has_shared ? 1 : 0);
-  auto launch_split = [&](auto heavy, auto light, const MxParams& prm, int n_tiles, hipEvent_t eb, hipEvent_t ee) {
+  auto launch_split = [&](auto heavy, auto light, const MxParams& prm, int n_tiles, hipEvent_t eb, hipEvent_t ee,
+                          int kparts = 1) {
     const int gh = grouped_grid(maxQ, n_tiles);
-    const int gl = grouped_grid(groups, n_tiles);
+    const dim3 gl(grouped_grid(groups, n_tiles), kparts);
     if (eb || ee) {
       hipExtLaunchKernelGGL(heavy, dim3(gh), dim3(256), 0, s, eb, nullptr, 0, prm);
       hipExtLaunchKernelGGL(light, dim3(gl), dim3(256), 0, s, nullptr, ee, 0, prm);
@@ -512,8 +528,15 @@ hipError_t launch_grouped_ffn_mx(const GroupedArgs& a, hipStream_t s) {
   q.sched = a.sched; q.maxQ = maxQ;
   q.k = a.assign_div; q.E = a.E; q.K = a.f; q.N = a.d; q.shared_row0 = a.routed_rows;
   q.y_out = a.y;
-  launch_split(gemm_mx_kernel<false, 1>, gemm_mx_kernel<false, 2>, q, (a.d + 255) / 256, nullptr, nullptr);
-  return hipGetLastError();
+  const int dn_tiles = (a.d + 255) / 256;
+  q.ksplit = grouped_down_ksplit(a.d, a.f, a.E, a.has_shared, a.wkind, a.act_f32);
+  q.part_slots = groups * dn_tiles;
+  q.y_part = a.y_part;
+  launch_split(gemm_mx_kernel<false, 1>, gemm_mx_kernel<false, 2>, q, dn_tiles, nullptr, nullptr, q.ksplit);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (q.ksplit > 1)
+    return launch_down_split_reduce(a.sched, maxQ, a.E, dn_tiles, a.d, q.ksplit, q.part_slots, a.y_part, a.y, s);
+  return hipSuccess;
 }
 
 }  // namespace moe
