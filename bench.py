@@ -302,8 +302,8 @@ def cpu_baseline_backward(cfg, inp, dout, budget_s=12.0, max_calls=200):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported on this build "
-              "(the layer shards by tokens or experts; see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer would shard by tokens or by experts across GPUs)", file=sys.stderr)
         sys.exit(2)
     import torch
     import synth

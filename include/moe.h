@@ -30,7 +30,7 @@
  *  - Calls on the same stream are ordered; calls that share a workspace must
  *    not run concurrently on different streams.
  *
- * Conventions fixed here where the pages are silent (see the design notes):
+ * Conventions fixed here where the pages are silent:
  *  - Router logits are rounded to fp32 once from an fp64 sum (+ bias), and
  *    experts are selected on those fp32 logits, larger first, equal logits
  *    ordered by the lower expert index.  Softmax weights are fp32.

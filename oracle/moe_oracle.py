@@ -28,8 +28,7 @@ Sources (page titles; sections named on each page):
          section: expert_offsets over the permuted rows, the inclusive form
          [4, 8, 8] and the leading-zero form [0, 4, 8, 8] for counts [4, 4, 0].
 
-Readings where the pages are silent (each is listed with its reason in the
-design notes of the repository):
+Readings where the pages are silent:
   * router logit = fp32 rounding (RNE) of the fp64 sum x.W_g (+ bias), so a
     GPU that accumulates in fp64 selects the same experts (certificate below);
   * equal probabilities are ordered by the lower expert index;
