@@ -248,7 +248,25 @@ __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0
   // next sub-step's fragments are read while the current one multiplies; the
   // stage just read is refilled two steps ahead (past the end: the last step
   // again, never read), so the vmcnt thresholds are exact.
-  if (nK > 0) {
+  if (MODE == MODE_TN && nK > 0 && nK <= 2) {
+    // weight-gradient tiles of small groups (one or two K steps): both stages
+    // are loaded once and used once, without the pipeline's refills of the
+    // last step (which would triple the loads of a one-step tile and add a
+    // round trip to wait for them)
+    bf16x8_t fa[MI], fb[NI];
+    issue(L0, 0);
+    if (nK == 2) issue(L1, kBK);
+    wait_vmem_le<0>();
+    __builtin_amdgcn_s_barrier();
+    for (int st = 0; st < nK; ++st) {
+      const bf16_t* L = st ? L1 : L0;
+#pragma unroll
+      for (int sub = 0; sub < kBK / 16; ++sub) {
+        frags(L, sub, fa, fb);
+        mfmas(fa, fb);
+      }
+    }
+  } else if (nK > 0) {
     bf16x8_t fa0[MI], fb0[NI], fa1[MI], fb1[NI];
     issue(L0, 0);
     issue(L1, min(1, nK - 1) * kBK);
@@ -364,22 +382,54 @@ __global__ __launch_bounds__(256, 1) void bwd_rows_kernel(BwdGemmParams p) {
   else bwd_tile<MODE, 64>(p, g, row0, rows, nt * BN_MAT, 0, nK, L0, L1);
 }
 
-// TN: one 256 x 256 tile of one group's weight gradient; work-groups are
-// dealt to the XCDs so that the tiles of one group share an XCD's L2.
+// TN: 256 x 256 tiles of the groups' weight gradients.  A tile's K loop runs
+// over its group's padded rows, so with skewed groups (a Zipf router bias)
+// equal tile counts per XCD would leave most of the work on one XCD.  Each
+// XCD instead takes the contiguous range of tiles (group-major, as before,
+// so a group's tiles share that XCD's L2) whose cost prefix falls in its
+// eighth of the total cost, a tile costing its group's rows plus a fixed
+// kWgTileCost for the prologue and the 256 KB of stores; the XCD's
+// work-groups stride through the range.
+constexpr long long kWgTileCost = 96;   // measured on fine_grained: 64-128 best (16: +16 %, 384: +18 %)
+
+// First tile (group-major index) whose cost prefix is >= w.
+__device__ long long wgrad_first_tile(const int32_t* __restrict__ poff, int G, int per_g, long long w) {
+  // cost prefix of group g's first tile: per_g * (poff[g] + g * kWgTileCost)
+  auto gstart = [&](int g) { return (long long)per_g * ((long long)poff[g] + g * kWgTileCost); };
+  int lo = 0, hi = G;                  // largest g in [0, G] with gstart(g) <= w
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (gstart(mid) <= w) lo = mid;
+    else hi = mid - 1;
+  }
+  const int g = lo;
+  if (g >= G) return (long long)G * per_g;
+  const long long cost = (long long)(poff[g + 1] - poff[g]) + kWgTileCost;
+  long long t = (w - gstart(g) + cost - 1) / cost;     // ceil
+  if (t > per_g) t = per_g;
+  return (long long)g * per_g + t;
+}
+
 __global__ __launch_bounds__(256, 1) void bwd_wgrad_kernel(BwdGemmParams p, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) bf16_t L0[512 * kBK];
   __shared__ __attribute__((aligned(1024))) bf16_t L1[512 * kBK];
   const int per_g = tiles_m * tiles_n;
-  const int total = p.G * per_g;
-  const int per_x = (total + 7) >> 3;
-  const int logical = (blockIdx.x & 7) * per_x + (blockIdx.x >> 3);
-  if (logical >= total) return;
-  const int g = logical / per_g;
-  const int t = logical - g * per_g;
-  const int tm = t / tiles_n, tn = t - tm * tiles_n;
-  const int kbeg = p.poff[g];
-  const int nK = (p.poff[g + 1] - kbeg) / kBK;
-  bwd_tile<MODE_TN, 256>(p, g, tm * 256, 256, tn * 256, kbeg, nK, L0, L1);
+  const int G = p.G;
+  const long long total = (long long)G * per_g;
+  const long long W = (long long)per_g * ((long long)p.poff[G] + G * kWgTileCost);
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
+  const long long t0 = xcd == 0 ? 0 : wgrad_first_tile(p.poff, G, per_g, W * xcd / 8);
+  const long long t1 = xcd == 7 ? total : wgrad_first_tile(p.poff, G, per_g, W * (xcd + 1) / 8);
+  for (long long t = t0 + slot; t < t1; t += nslots) {
+    const int g = (int)(t / per_g);
+    const int r = (int)(t - (long long)g * per_g);
+    const int tm = r / tiles_n, tn = r - tm * tiles_n;
+    const int kbeg = p.poff[g];
+    const int nK = (p.poff[g + 1] - kbeg) / kBK;
+    bwd_tile<MODE_TN, 256>(p, g, tm * 256, 256, tn * 256, kbeg, nK, L0, L1);
+    __syncthreads();                   // the next tile refills the LDS stages
+  }
 }
 
 hipError_t launch_bwd_rows(int mode, const BwdGemmParams& p, hipStream_t s) {
@@ -393,8 +443,12 @@ hipError_t launch_bwd_rows(int mode, const BwdGemmParams& p, hipStream_t s) {
 
 hipError_t launch_bwd_wgrad(const BwdGemmParams& p, hipStream_t s) {
   const int tm = (p.M + 255) / 256, tn = (p.N + 255) / 256;
-  const int total = p.G * tm * tn;
-  const int grid = 8 * ((total + 7) / 8);
+  // persistent: one work-group per CU (their LDS allows one), dealt round-robin to the 8 XCDs
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int grid = 8 * ((cus + 7) / 8);
   bwd_wgrad_kernel<<<grid, 256, 0, s>>>(p, tm, tn);
   return hipGetLastError();
 }
