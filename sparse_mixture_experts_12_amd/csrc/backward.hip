@@ -249,32 +249,60 @@ __global__ __launch_bounds__(256) void dx_kernel(const float* __restrict__ dXp, 
 }
 
 // dW_g[c, e] = sum_t x[t, c] dl[t, e] and d_bias[e] = sum_t dl[t, e] (row
-// c = d of the partials, x taken as 1): tokens in chunks of kRwChunk, each
-// (64 c x 16 e, chunk) work-group writes its partial sums; a second launch
-// adds the chunks in order.
+// c = d of the partials, x taken as 1): tokens in chunks of kRwChunk; a
+// work-group covers 256 c x 16 e of one chunk, a thread 4 consecutive c x 4
+// consecutive e, with the loads of 8 tokens in flight before their FMAs (each
+// sum still runs over the chunk's tokens in order); a second launch adds the
+// chunks in order.
 constexpr int kRwChunk = 256;
 
 __global__ __launch_bounds__(256) void router_wgrad_partial_kernel(const bf16_t* __restrict__ x,
                                                                    const float* __restrict__ dl, int T, int d, int E,
                                                                    float* __restrict__ part) {
-  const int c = blockIdx.x * 64 + (threadIdx.x & 63);
-  const int e0 = blockIdx.y * 16 + (threadIdx.x >> 6) * 4;
+  const int c = blockIdx.x * 256 + 4 * (threadIdx.x & 63);     // d % 4 == 0: a 4-block is all x or the bias row
+  const int e = blockIdx.y * 16 + 4 * (threadIdx.x >> 6);
+  if (c > d || e >= E) return;
   const int t0 = blockIdx.z * kRwChunk;
   const int t1 = min(T, t0 + kRwChunk);
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  const bool cok = c <= d;
-  for (int t = t0; t < t1; ++t) {
-    const float xv = c < d ? bf16_to_f32(x[(size_t)t * d + c]) : 1.f;
-    const float* r = dl + (size_t)t * E;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (e0 + i < E) acc[i] = __fmaf_rn(xv, r[e0 + i], acc[i]);
-  }
-  if (!cok) return;
-  float* o = part + ((size_t)blockIdx.z * (d + 1) + c) * E;
+  const bool bias_row = c == d;
+  const int ne = min(4, E - e);
+  const bool vec = ne == 4 && (E & 3) == 0;     // 16-byte aligned dl rows and partial rows
+  float acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    if (e0 + i < E) o[e0 + i] = acc[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  constexpr int U = 8;
+  for (int tb = t0; tb < t1; tb += U) {
+    uint2 xr[U];
+    float4 lr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {             // clamped tokens: every load unconditional
+      const int t = min(tb + u, t1 - 1);
+      xr[u] = bias_row ? make_uint2(0x3f80u, 0u) : *reinterpret_cast<const uint2*>(x + (size_t)t * d + c);
+      const float* r = dl + (size_t)t * E + e;
+      lr[u] = vec ? *reinterpret_cast<const float4*>(r)
+                  : make_float4(r[0], ne > 1 ? r[1] : 0.f, ne > 2 ? r[2] : 0.f, ne > 3 ? r[3] : 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (tb + u >= t1) break;
+      const float xv[4] = {bf16lo(xr[u].x), bf16hi(xr[u].x), bf16lo(xr[u].y), bf16hi(xr[u].y)};
+      const float lv[4] = {lr[u].x, lr[u].y, lr[u].z, lr[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __fmaf_rn(xv[i], lv[j], acc[i][j]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (c + i > d) break;
+    float* o = part + ((size_t)blockIdx.z * (d + 1) + c + i) * E + e;
+    if (vec) *reinterpret_cast<float4*>(o) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    else
+      for (int j = 0; j < ne; ++j) o[j] = acc[i][j];
+  }
 }
 
 __global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* __restrict__ part, int nchunk, int d,
@@ -402,7 +430,7 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
     dx_kernel<false><<<gx, 256, 0, s>>>(a.dXp, a.apos, a.poff, a.dl, a.topk_idx, (const bf16_t*)a.W_g, a.T, a.d,
                                         a.E, a.k, a.has_shared, a.dx);
   const int nchunk = (a.T + kRwChunk - 1) / kRwChunk;
-  router_wgrad_partial_kernel<<<dim3((a.d + 1 + 63) / 64, (a.E + 15) / 16, nchunk), 256, 0, s>>>(
+  router_wgrad_partial_kernel<<<dim3((a.d + 1 + 255) / 256, (a.E + 15) / 16, nchunk), 256, 0, s>>>(
       (const bf16_t*)a.x, a.dl, a.T, a.d, a.E, a.rw_part);
   const long nout = (long)(a.d + 1) * a.E;
   router_wgrad_reduce_kernel<<<(unsigned)((nout + 255) / 256), 256, 0, s>>>(a.rw_part, nchunk, a.d, a.E, a.dW_g,
