@@ -378,6 +378,13 @@ def test_forward_parity_full_size(name):
     out, taken = run_forward(inp, stats=st)
     n = SAMPLE.get(name)
     toks = None if n is None else np.sort(np.random.default_rng(0).choice(cfg.T, size=n, replace=False))
+    if toks is not None and cfg.E <= 16:
+        # also the token owning each expert's last permuted row, so every expert's
+        # last (partial, possibly K-split) row tile is checked
+        routing = ov.forward(tokens=np.arange(0))
+        offs, sa = routing["offsets"], routing["sorted_assign"]
+        tails = [int(sa[offs[e + 1] - 1]) // cfg.k for e in range(cfg.E) if offs[e + 1] > offs[e]]
+        toks = np.unique(np.concatenate([toks, np.array(tails, dtype=toks.dtype)]))
     ref = ov.forward(tokens=toks)
     got = to64(out) if toks is None else to64(out)[toks]
     e = assert_close(got, ref["out"], TOL[cfg.wdt], name)
