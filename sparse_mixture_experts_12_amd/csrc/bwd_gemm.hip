@@ -424,7 +424,14 @@ __global__ __launch_bounds__(256, 1) void bwd_wgrad_kernel(BwdGemmParams p, int 
   for (long long t = t0 + slot; t < t1; t += nslots) {
     const int g = (int)(t / per_g);
     const int r = (int)(t - (long long)g * per_g);
-    const int tm = r / tiles_n, tn = r - tm * tiles_n;
+    // inside a group: strips of 4 tile rows walked column by column, so the
+    // 32 tiles an XCD runs together are 4 row blocks x 8 column blocks and
+    // share 4 + 8 operand blocks from L2 (row-major order would share 1 + 32)
+    constexpr int GM = 4;
+    const int strip = r / (GM * tiles_n);
+    const int rs = r - strip * GM * tiles_n;
+    const int gm = min(GM, tiles_m - strip * GM);
+    const int tm = strip * GM + rs % gm, tn = rs / gm;
     const int kbeg = p.poff[g];
     const int nK = (p.poff[g + 1] - kbeg) / kBK;
     bwd_tile<MODE_TN, 256>(p, g, tm * 256, 256, tn * 256, kbeg, nK, L0, L1);
