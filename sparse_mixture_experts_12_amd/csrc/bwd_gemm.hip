@@ -66,9 +66,11 @@ __device__ __forceinline__ bf16x8_t mc_frag(const bf16_t* Ls, int kbase, int nba
 }  // namespace
 
 // One output tile of at most BMV rows (see the file comment for the modes).
-template <int MODE, int BMV>
+// LDS stages hold BMMAX A rows (KC) or 256 A columns (MC) plus the B tile;
+// NST stages form the ring (3: light row tiles, two steps of loads in flight).
+template <int MODE, int BMV, int BMMAX = 256, int NST = 2>
 __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0, int rows, int n0, int kbeg,
-                                         int nK, bf16_t* L0, bf16_t* L1) {
+                                         int nK, bf16_t* L0, bf16_t* L1, bf16_t* L2 = nullptr) {
   constexpr bool A_KC = MODE != MODE_TN;
   constexpr bool B_KC = MODE == MODE_NT || MODE == MODE_NTS;
   constexpr bool DUAL = MODE == MODE_GU;
@@ -81,7 +83,9 @@ __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0
   constexpr int WROWS = BMV / WM;
   constexpr int A_LD = A_KC ? BMV / 8 / 4 : 8;      // 1 KB blocks per wave per stage
   constexpr int B_LD = 8;
-  constexpr int LDS_B = 256 * kBK;                 // B tile offset (elements) inside a stage
+  constexpr int LDS_B = (MODE == MODE_TN ? 256 : BMMAX) * kBK;   // B tile offset (elements) inside a stage
+  static_assert(BMV <= BMMAX && (NST == 2 || NST == 3) && (MODE != MODE_TN || (BMMAX == 256 && NST == 2)),
+                "backward tile configuration");
   constexpr int NMF = MI * NI;
   constexpr int NDS = (A_KC ? MI : 2 * MI) + (B_KC ? NI : 2 * NI);
   constexpr int NVM = A_LD + B_LD;
@@ -270,7 +274,8 @@ __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0
     bf16x8_t fa0[MI], fb0[NI], fa1[MI], fb1[NI];
     issue(L0, 0);
     issue(L1, min(1, nK - 1) * kBK);
-    wait_vmem_le<NVM>();
+    if constexpr (NST > 2) issue(L2, min(2, nK - 1) * kBK);
+    wait_vmem_le<(NST - 1) * NVM>();
     __builtin_amdgcn_s_barrier();
     frags(L0, 0, fa0, fb0);
     auto step = [&](bf16_t* L, const bf16_t* Ln, int k) {
@@ -286,20 +291,30 @@ __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0
         sched_interleave<NMF, NDS, 0>();
         __builtin_amdgcn_sched_barrier(0);
       }
-      wait_vmem_le_lds0<0>();
+      wait_vmem_le_lds0<(NST - 2) * NVM>();
       __builtin_amdgcn_s_barrier();
-      issue(L, min(k + 2, nK - 1) * kBK);
+      issue(L, min(k + NST, nK - 1) * kBK);
       frags(Ln, 0, fa0, fb0);
       mfmas(fa1, fb1);
       sched_interleave<NMF, NDS, NVM>();
       __builtin_amdgcn_sched_barrier(0);
     };
     int k = 0;
-    for (; k + 2 <= nK; k += 2) {
-      step(L0, L1, k);
-      step(L1, L0, k + 1);
+    if constexpr (NST == 2) {
+      for (; k + 2 <= nK; k += 2) {
+        step(L0, L1, k);
+        step(L1, L0, k + 1);
+      }
+      if (k < nK) step(L0, L1, k);
+    } else {
+      for (; k + 3 <= nK; k += 3) {
+        step(L0, L1, k);
+        step(L1, L2, k + 1);
+        step(L2, L0, k + 2);
+      }
+      if (k < nK) step(L0, L1, k);
+      if (k + 1 < nK) step(L1, L2, k + 1);
     }
-    if (k < nK) step(L0, L1, k);
     wait_vmem_le<0>();
   }
 
@@ -367,19 +382,29 @@ __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0
 }
 
 // GU / NT: row tiles of the padded groups from the device schedule.
-template <int MODE>
+// SEG 1: heavy row tiles (> 128 rows), 256-row stages two deep; SEG 2: light
+// row tiles (a group's last <= 128 rows), 128-row stages three deep (two steps
+// of loads in flight: these tiles mostly stream weights).
+template <int MODE, int SEG>
 __global__ __launch_bounds__(256, 1) void bwd_rows_kernel(BwdGemmParams p) {
-  __shared__ __attribute__((aligned(1024))) bf16_t L0[512 * kBK];
-  __shared__ __attribute__((aligned(1024))) bf16_t L1[512 * kBK];
+  constexpr int BMMAX = SEG == 1 ? 256 : 128;
+  constexpr int NST = SEG == 1 ? 2 : 3;
+  constexpr int LDS_S = (BMMAX + 256) * kBK;
+  __shared__ __attribute__((aligned(1024))) bf16_t L0[LDS_S];
+  __shared__ __attribute__((aligned(1024))) bf16_t L1[LDS_S];
+  __shared__ __attribute__((aligned(1024))) bf16_t L2[NST > 2 ? LDS_S : 8];
   constexpr int BN_MAT = MODE == MODE_GU ? 128 : 256;
   const int n_tiles = (p.N + BN_MAT - 1) / BN_MAT;
   int g, row0, rows, nt;
   // the schedule lists the G padded groups (the shared expert is group E)
-  if (!decode_tile(p.sched, p.maxQ, p.G, n_tiles, &g, &row0, &rows, &nt)) return;
+  if (!decode_tile<SEG>(p.sched, p.maxQ, p.G, n_tiles, &g, &row0, &rows, &nt)) return;
   const int nK = p.K / kBK;
-  if (rows > 128) bwd_tile<MODE, 256>(p, g, row0, rows, nt * BN_MAT, 0, nK, L0, L1);
-  else if (rows > 64) bwd_tile<MODE, 128>(p, g, row0, rows, nt * BN_MAT, 0, nK, L0, L1);
-  else bwd_tile<MODE, 64>(p, g, row0, rows, nt * BN_MAT, 0, nK, L0, L1);
+  if constexpr (SEG == 1) {
+    bwd_tile<MODE, 256, BMMAX, NST>(p, g, row0, rows, nt * BN_MAT, 0, nK, L0, L1, L2);
+  } else {
+    if (rows > 64) bwd_tile<MODE, 128, BMMAX, NST>(p, g, row0, rows, nt * BN_MAT, 0, nK, L0, L1, L2);
+    else bwd_tile<MODE, 64, BMMAX, NST>(p, g, row0, rows, nt * BN_MAT, 0, nK, L0, L1, L2);
+  }
 }
 
 // TN: 256 x 256 tiles of the groups' weight gradients.  A tile's K loop runs
@@ -441,10 +466,19 @@ __global__ __launch_bounds__(256, 1) void bwd_wgrad_kernel(BwdGemmParams p, int 
 
 hipError_t launch_bwd_rows(int mode, const BwdGemmParams& p, hipStream_t s) {
   const int bn = mode == MODE_GU ? 128 : 256;
-  const int grid = grouped_grid(p.maxQ, (p.N + bn - 1) / bn);
-  if (mode == MODE_GU) bwd_rows_kernel<MODE_GU><<<grid, 256, 0, s>>>(p);
-  else if (mode == MODE_NTS) bwd_rows_kernel<MODE_NTS><<<grid, 256, 0, s>>>(p);
-  else bwd_rows_kernel<MODE_NT><<<grid, 256, 0, s>>>(p);
+  const int n_tiles = (p.N + bn - 1) / bn;
+  const int gh = grouped_grid(p.maxQ, n_tiles);   // heavy tiles, then light tiles
+  const int gl = grouped_grid(p.G, n_tiles);
+  if (mode == MODE_GU) {
+    bwd_rows_kernel<MODE_GU, 1><<<gh, 256, 0, s>>>(p);
+    bwd_rows_kernel<MODE_GU, 2><<<gl, 256, 0, s>>>(p);
+  } else if (mode == MODE_NTS) {
+    bwd_rows_kernel<MODE_NTS, 1><<<gh, 256, 0, s>>>(p);
+    bwd_rows_kernel<MODE_NTS, 2><<<gl, 256, 0, s>>>(p);
+  } else {
+    bwd_rows_kernel<MODE_NT, 1><<<gh, 256, 0, s>>>(p);
+    bwd_rows_kernel<MODE_NT, 2><<<gl, 256, 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 
