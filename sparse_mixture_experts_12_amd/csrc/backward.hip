@@ -330,6 +330,22 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, l
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
+// The dX GEMM's light row tiles (a group's last <= 128 padded rows) run after
+// its heavy ones; when they are few (groups x column tiles <= 256, e.g. 8
+// Mixtral experts x 16) each is split into up to 4 K parts, reduced in order.
+int backward_dx_ksplit(int d, int f, int G) {
+  const int slots = G * ((d + 255) / 256);
+  if (slots > 256) return 1;
+  for (int ks : {4, 2})
+    if ((2 * f) % (ks * 64) == 0) return ks;
+  return 1;
+}
+
+size_t backward_dx_part_bytes(int d, int f, int G) {
+  const int ks = backward_dx_ksplit(d, f, G);
+  return (size_t)(ks - 1) * (size_t)G * ((d + 255) / 256) * 128 * 256 * sizeof(float);
+}
+
 long backward_pad_rows(int T, int E, int k, int has_shared) {
   const long routed = (long)T * k + (long)(kPadRows - 1) * E;
   const long shared = has_shared ? ((long)T + kPadRows - 1) / kPadRows * kPadRows : 0;
@@ -400,6 +416,9 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
     q.ldb = a.f; q.bgs = (long)a.d * a.f;
     q.K = 2 * a.f; q.K1 = a.f; q.N = a.d;
     q.C0 = a.dXp;
+    q.ksplit = backward_dx_ksplit(a.d, a.f, G);
+    q.part_slots = G * ((a.d + 255) / 256);
+    q.part = a.dx_part;
     if (a.ev_begin) hipEventRecord(a.ev_begin, s);
     if ((err = launch_bwd_rows(2, q, s)) != hipSuccess) return err;
     if (a.ev_end) hipEventRecord(a.ev_end, s);

@@ -68,9 +68,12 @@ __device__ __forceinline__ bf16x8_t mc_frag(const bf16_t* Ls, int kbase, int nba
 // One output tile of at most BMV rows (see the file comment for the modes).
 // LDS stages hold BMMAX A rows (KC) or 256 A columns (MC) plus the B tile;
 // NST stages form the ring (3: light row tiles, two steps of loads in flight).
+// K runs over [kbeg, kbeg + nK kBK).  NT / NTS tiles with kpart > 0 (light
+// row tiles split over K) write their fp32 block to p.part slot `slot`.
 template <int MODE, int BMV, int BMMAX = 256, int NST = 2>
 __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0, int rows, int n0, int kbeg,
-                                         int nK, bf16_t* L0, bf16_t* L1, bf16_t* L2 = nullptr) {
+                                         int nK, bf16_t* L0, bf16_t* L1, bf16_t* L2 = nullptr, int kpart = 0,
+                                         int slot = 0) {
   constexpr bool A_KC = MODE != MODE_TN;
   constexpr bool B_KC = MODE == MODE_NT || MODE == MODE_NTS;
   constexpr bool DUAL = MODE == MODE_GU;
@@ -158,8 +161,9 @@ __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0
     const bf16_t* b_base_up = nullptr;
     uint32_t ak, bk;
     if constexpr (MODE == MODE_NTS) {
-      const bool second = k0 >= p.K1;             // K split over two (A, B) pairs
-      const int kk = second ? k0 - p.K1 : k0;
+      const int ka = kbeg + k0;
+      const bool second = ka >= p.K1;             // K split over two (A, B) pairs
+      const int kk = second ? ka - p.K1 : ka;
       a_base = second ? p.A1 : p.A0;
       b_base = second ? bb1 : bb0;
       ak = (uint32_t)kk;
@@ -167,14 +171,14 @@ __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0
     } else if constexpr (MODE == MODE_NT) {
       a_base = p.A0;
       b_base = bb0;
-      ak = (uint32_t)k0;
-      bk = (uint32_t)k0;
+      ak = (uint32_t)(kbeg + k0);
+      bk = (uint32_t)(kbeg + k0);
     } else if constexpr (MODE == MODE_GU) {
       a_base = p.A0;
       b_base = bb0;
       b_base_up = bb1;
-      ak = (uint32_t)k0;
-      bk = (uint32_t)k0 * (uint32_t)p.ldb;
+      ak = (uint32_t)(kbeg + k0);
+      bk = (uint32_t)(kbeg + k0) * (uint32_t)p.ldb;
     } else {
       a_base = p.A0;
       b_base = bb0;
@@ -369,13 +373,16 @@ __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0
       for (int nl = 0; nl < NI_MAT; ++nl) {
         const int col = n0 + b_col(nl) + l32;
         if (col >= p.N) continue;
+        // K part 0 (or no split): C0 rows; parts 1..: this slot's 128 x 256 block
+        float* out = kpart == 0 ? p.C0 + (size_t)row0 * p.N + col
+                                : p.part + ((size_t)(kpart - 1) * p.part_slots + slot) * (128 * 256) + (col - n0);
+        const size_t ostride = kpart == 0 ? (size_t)p.N : 256;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = wm * WROWS + mi * 32 + (v >> 2) * 8 + lhi * 4 + (v & 3);
           if (r >= rows) continue;
-          const size_t o = (size_t)(row0 + r) * p.N + col;
-          p.C0[o] = acc[mi][nl][v];
-          if constexpr (DUAL) p.C1[o] = acc[mi][nl + NI_MAT][v];
+          out[(size_t)r * ostride] = acc[mi][nl][v];
+          if constexpr (DUAL) p.C1[(size_t)(row0 + r) * p.N + col] = acc[mi][nl + NI_MAT][v];
         }
       }
   }
@@ -395,15 +402,20 @@ __global__ __launch_bounds__(256, 1) void bwd_rows_kernel(BwdGemmParams p) {
   __shared__ __attribute__((aligned(1024))) bf16_t L2[NST > 2 ? LDS_S : 8];
   constexpr int BN_MAT = MODE == MODE_GU ? 128 : 256;
   const int n_tiles = (p.N + BN_MAT - 1) / BN_MAT;
-  int g, row0, rows, nt;
+  int g, row0, rows, nt, slot = 0;
   // the schedule lists the G padded groups (the shared expert is group E)
-  if (!decode_tile<SEG>(p.sched, p.maxQ, p.G, n_tiles, &g, &row0, &rows, &nt)) return;
-  const int nK = p.K / kBK;
+  if (!decode_tile<SEG>(p.sched, p.maxQ, p.G, n_tiles, &g, &row0, &rows, &nt, &slot)) return;
+  // light NT / NTS tiles may be split over K (blockIdx.y = K part)
+  constexpr bool KSPLIT = SEG == 2 && MODE != MODE_GU;
+  const int kparts = KSPLIT && p.ksplit > 1 ? p.ksplit : 1;
+  const int kpart = KSPLIT ? (int)blockIdx.y : 0;
+  const int nK = p.K / kBK / kparts;
+  const int kbeg = kpart * nK * kBK;
   if constexpr (SEG == 1) {
-    bwd_tile<MODE, 256, BMMAX, NST>(p, g, row0, rows, nt * BN_MAT, 0, nK, L0, L1, L2);
+    bwd_tile<MODE, 256, BMMAX, NST>(p, g, row0, rows, nt * BN_MAT, kbeg, nK, L0, L1, L2);
   } else {
-    if (rows > 64) bwd_tile<MODE, 128, BMMAX, NST>(p, g, row0, rows, nt * BN_MAT, 0, nK, L0, L1, L2);
-    else bwd_tile<MODE, 64, BMMAX, NST>(p, g, row0, rows, nt * BN_MAT, 0, nK, L0, L1, L2);
+    if (rows > 64) bwd_tile<MODE, 128, BMMAX, NST>(p, g, row0, rows, nt * BN_MAT, kbeg, nK, L0, L1, L2, kpart, slot);
+    else bwd_tile<MODE, 64, BMMAX, NST>(p, g, row0, rows, nt * BN_MAT, kbeg, nK, L0, L1, L2, kpart, slot);
   }
 }
 
@@ -468,7 +480,8 @@ hipError_t launch_bwd_rows(int mode, const BwdGemmParams& p, hipStream_t s) {
   const int bn = mode == MODE_GU ? 128 : 256;
   const int n_tiles = (p.N + bn - 1) / bn;
   const int gh = grouped_grid(p.maxQ, n_tiles);   // heavy tiles, then light tiles
-  const int gl = grouped_grid(p.G, n_tiles);
+  const int ks = mode == MODE_GU ? 1 : (p.ksplit > 1 ? p.ksplit : 1);
+  const dim3 gl(grouped_grid(p.G, n_tiles), ks);
   if (mode == MODE_GU) {
     bwd_rows_kernel<MODE_GU, 1><<<gh, 256, 0, s>>>(p);
     bwd_rows_kernel<MODE_GU, 2><<<gl, 256, 0, s>>>(p);
@@ -479,7 +492,9 @@ hipError_t launch_bwd_rows(int mode, const BwdGemmParams& p, hipStream_t s) {
     bwd_rows_kernel<MODE_NT, 1><<<gh, 256, 0, s>>>(p);
     bwd_rows_kernel<MODE_NT, 2><<<gl, 256, 0, s>>>(p);
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ks == 1) return e;
+  return launch_down_split_reduce(p.sched, p.maxQ, p.G, n_tiles, p.N, ks, p.part_slots, p.part, p.C0, s);
 }
 
 hipError_t launch_bwd_wgrad(const BwdGemmParams& p, hipStream_t s) {

@@ -132,10 +132,16 @@ struct BwdGemmParams {          // grouped GEMMs of the backward
   float* C1;               // GU: U rows [P, N]
   float* Cs;               // TN: the shared group's output (group E), or nullptr
   long cstride;
+  float* part;             // NT/NTS light tiles split over K: parts 1.. [ksplit - 1][part_slots][128][256]
+  int ksplit;              // K parts of the light row tiles (0 or 1: none)
+  int part_slots;          // light-segment slots (groups x column tiles)
 };
 // mode 0: G/U recompute, 1: NT, 2: NT with K split over two (A, B) pairs
 hipError_t launch_bwd_rows(int mode, const BwdGemmParams& p, hipStream_t s);
 hipError_t launch_bwd_wgrad(const BwdGemmParams& p, hipStream_t s);
+// K parts of the dX GEMM's light row tiles, and the workspace their parts take
+int backward_dx_ksplit(int d, int f, int G);
+size_t backward_dx_part_bytes(int d, int f, int G);
 
 struct BackwardArgs {
   const void* x;                 // [T, d] bf16
@@ -163,6 +169,7 @@ struct BackwardArgs {
   float* dXp;                    // [P, d]
   float* dl;                     // [T, E]
   float* rw_part;                // router_wgrad_ws_bytes
+  float* dx_part;                // backward_dx_part_bytes
   // outputs (fp32)
   float *dx, *dW_g, *d_bias, *dW_gate, *dW_up, *dW_down, *dWs_gate, *dWs_up, *dWs_down;
   hipEvent_t ev_begin, ev_end;

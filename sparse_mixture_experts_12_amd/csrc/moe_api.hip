@@ -502,7 +502,7 @@ moe_status check_backward_desc(const moe_desc* d) {
 
 struct BwdLayout {
   size_t part, idx, w, logits, counts, offsets, sorted, inv, ndrop, rank;
-  size_t poff, ptok, pw, apos, gsc, sched, Xp, Dp, G, U, dH, dG, dU, Hw, dXp, dl, rw, total;
+  size_t poff, ptok, pw, apos, gsc, sched, Xp, Dp, G, U, dH, dG, dU, Hw, dXp, dl, rw, dxp, total;
 };
 
 BwdLayout bwd_layout_of(const moe_desc* d) {
@@ -543,6 +543,7 @@ BwdLayout bwd_layout_of(const moe_desc* d) {
   L.dXp = take(P * D * 4);
   L.dl = take(T * E * 4);
   L.rw = take(router_wgrad_ws_bytes(d->T, d->d, d->E));
+  L.dxp = take(backward_dx_part_bytes(d->d, d->f, (int)Gn));
   L.total = off;
   return L;
 }
@@ -616,6 +617,7 @@ moe_status moe_backward(const moe_desc* desc, const void* x, const moe_weights* 
   a.G = (float*)(base + L.G); a.U = (float*)(base + L.U); a.dH = (float*)(base + L.dH);
   a.dG = (bf16_t*)(base + L.dG); a.dU = (bf16_t*)(base + L.dU); a.Hw = (bf16_t*)(base + L.Hw);
   a.dXp = (float*)(base + L.dXp); a.dl = (float*)(base + L.dl); a.rw_part = (float*)(base + L.rw);
+  a.dx_part = (float*)(base + L.dxp);
   a.dx = g->dx; a.dW_g = g->dW_g; a.d_bias = g->d_bias; a.dW_gate = g->dW_gate; a.dW_up = g->dW_up;
   a.dW_down = g->dW_down; a.dWs_gate = g->dWs_gate; a.dWs_up = g->dWs_up; a.dWs_down = g->dWs_down;
   a.ev_begin = g->ev_begin; a.ev_end = g->ev_end;
