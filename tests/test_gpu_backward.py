@@ -154,6 +154,12 @@ def test_backward_parity_full_size(name, ntok, ncol):
     ref_fwd = ov.forward(tokens=np.arange(1))
     rng = np.random.default_rng(3)
     toks = np.sort(rng.choice(cfg.T, size=ntok, replace=False))
+    if cfg.E <= 16:
+        # also the token owning each expert's last row: its padded group's last
+        # (light, possibly K-split) row tile
+        offs, sa = ref_fwd["offsets"], ref_fwd["sorted_assign"]
+        tails = [int(sa[offs[e + 1] - 1]) // cfg.k for e in range(cfg.E) if offs[e + 1] > offs[e]]
+        toks = np.unique(np.concatenate([toks, np.array(tails, dtype=toks.dtype)]))
     got = to64(g["dx"][torch.from_numpy(toks).cuda()])
     want = np.stack([_token_dx(ov, cfg, ref_fwd, dout64, int(t)) for t in toks])
     e_dx = assert_close(got, want, TOL, f"{name} dx (sampled tokens)")
