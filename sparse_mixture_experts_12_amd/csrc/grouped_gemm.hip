@@ -460,7 +460,9 @@ struct GemmParamsF32 {
 
 template <bool DUAL>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
-  constexpr int BM = 64, BN = 64, BK = 16;
+  // BK = 64: four K steps cover the tiny layer's d = 256, each issuing all of
+  // its loads (16 A + 16 or 32 B per thread) before any is used
+  constexpr int BM = 64, BN = 64, BK = 64;
   __shared__ float As[BK][BM + 4];
   __shared__ float Bs[DUAL ? 2 : 1][BK][BN + 4];
   const int n_tiles = (p.N + BN - 1) / BN;
@@ -473,21 +475,20 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
   const size_t goff = shared ? 0 : (size_t)g * p.K * p.N;
   const float* B0 = (shared ? p.Ws0 : p.W0 + goff);
   const float* B1 = DUAL ? (shared ? p.Ws1 : p.W1 + goff) : nullptr;
-  // A rows loaded by this thread: 4 rows (r = tid / 16 + 16 * i), 1 k each
+  // A rows loaded by this thread: 4 rows (r = tid / 16 + 16 * i), 4 k each
+  // (tx + 16 j); rows past the tile's rows read its first row and stage zeros
   const float* arow[4];
+  bool alive[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (tid >> 4) + 16 * i;
-    const int grow = row0 + r;
-    if (r < rows) {
-      if (DUAL) {
-        const int tok = shared ? (grow - p.shared_row0) : (p.sorted_assign[grow] / p.k);
-        arow[i] = p.x + (size_t)tok * p.K;
-      } else {
-        arow[i] = p.a_rows + (size_t)grow * p.K;
-      }
+    alive[i] = r < rows;
+    const int grow = row0 + (alive[i] ? r : 0);
+    if (DUAL) {
+      const int tok = shared ? (grow - p.shared_row0) : (p.sorted_assign[grow] / p.k);
+      arow[i] = p.x + (size_t)tok * p.K;
     } else {
-      arow[i] = nullptr;
+      arow[i] = p.a_rows + (size_t)grow * p.K;
     }
   }
   float acc0[4][4], acc1[4][4];
@@ -495,16 +496,28 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc0[i][j] = acc1[i][j] = 0.f;
+  const int nn = tid & 63, kb = tid >> 6;          // B: column nn of K-rows kb + 4 i
+  const int colc = min(n0 + nn, p.N - 1);
+  const bool col_ok = n0 + nn < p.N;
   for (int k0 = 0; k0 < p.K; k0 += BK) {
+    float va[4][4], vb0[16], vb1[DUAL ? 16 : 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) As[tx][(tid >> 4) + 16 * i] = arow[i] ? arow[i][k0 + tx] : 0.f;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + 256 * i;
-      const int kk = e >> 6, nn = e & 63;
-      const int col = n0 + nn;
-      Bs[0][kk][nn] = col < p.N ? B0[(size_t)(k0 + kk) * p.N + col] : 0.f;
-      if (DUAL) Bs[DUAL ? 1 : 0][kk][nn] = col < p.N ? B1[(size_t)(k0 + kk) * p.N + col] : 0.f;
+      for (int j = 0; j < 4; ++j) va[i][j] = arow[i][k0 + tx + 16 * j];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      vb0[i] = B0[(size_t)(k0 + kb + 4 * i) * p.N + colc];
+      if (DUAL) vb1[DUAL ? i : 0] = B1[(size_t)(k0 + kb + 4 * i) * p.N + colc];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) As[tx + 16 * j][(tid >> 4) + 16 * i] = alive[i] ? va[i][j] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      Bs[0][kb + 4 * i][nn] = col_ok ? vb0[i] : 0.f;
+      if (DUAL) Bs[DUAL ? 1 : 0][kb + 4 * i][nn] = col_ok ? vb1[DUAL ? i : 0] : 0.f;
     }
     __syncthreads();
 #pragma unroll
