@@ -497,6 +497,28 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc0[i][j] = acc1[i][j] = 0.f;
   const int nn = tid & 63, kb = tid >> 6;          // B: column nn of K-rows kb + 4 i
+  const int rpt = rows <= 16 ? 1 : rows <= 32 ? 2 : 4;   // rows per thread
+  auto kloop = [&](auto RC) {
+    constexpr int R = decltype(RC)::value;
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float a[R], b0[4], b1[4];
+#pragma unroll
+      for (int i = 0; i < R; ++i) a[i] = As[kk][ty * R + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        b0[j] = Bs[0][kk][tx * 4 + j];
+        if (DUAL) b1[j] = Bs[DUAL ? 1 : 0][kk][tx * 4 + j];
+      }
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc0[i][j] = __fmaf_rn(a[i], b0[j], acc0[i][j]);
+          if (DUAL) acc1[i][j] = __fmaf_rn(a[i], b1[j], acc1[i][j]);
+        }
+    }
+  };
   const int colc = min(n0 + nn, p.N - 1);
   const bool col_ok = n0 + nn < p.N;
   for (int k0 = 0; k0 < p.K; k0 += BK) {
@@ -520,29 +542,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
       if (DUAL) Bs[DUAL ? 1 : 0][kb + 4 * i][nn] = col_ok ? vb1[DUAL ? i : 0] : 0.f;
     }
     __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < BK; ++kk) {
-      float a[4], b0[4], b1[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        b0[j] = Bs[0][kk][tx * 4 + j];
-        if (DUAL) b1[j] = Bs[DUAL ? 1 : 0][kk][tx * 4 + j];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc0[i][j] = __fmaf_rn(a[i], b0[j], acc0[i][j]);
-          if (DUAL) acc1[i][j] = __fmaf_rn(a[i], b1[j], acc1[i][j]);
-        }
-    }
+    // R rows x 4 columns per thread (rows ty R .. ty R + R - 1): R = 1 for
+    // tiles of at most 16 rows, 2 for at most 32, else 4, so all four waves
+    // do useful work
+    if (rpt == 1) kloop(std::integral_constant<int, 1>{});
+    else if (rpt == 2) kloop(std::integral_constant<int, 2>{});
+    else kloop(std::integral_constant<int, 4>{});
     __syncthreads();
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = ty * 4 + i;
+    const int r = i < rpt ? ty * rpt + i : rows;
     if (r >= rows) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
