@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--telemetry", action="store_true",
                     help="also request the router telemetry outputs (routed load, mean probability, "
                          "load-balancing loss) inside the timed region")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the region that replays the layer from a captured HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (for HBM counter scaling)")
     return ap.parse_args()
@@ -401,6 +403,31 @@ def main():
         q = lambda f: per_step[min(steps - 1, int(f * (steps - 1) + 0.5))]
         step_pct = {"p10": round(q(0.1), 5), "p50": round(q(0.5), 5), "p90": round(q(0.9), 5)}
 
+    # Region 4: the same layer calls captured once into a HIP graph (one call per
+    # weight copy) and replayed, as a serving loop would run them: the per-step
+    # cost without host-side launch work between the kernels.
+    graph_ms = None
+    if not args.no_graph:
+        gstream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gstream):
+            for c in range(n_copies):
+                ops.forward(desc, inp["x"], wstructs[c], out, ws)
+        reps = max(1, steps // n_copies)
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / (reps * n_copies)
+        del graph
+
     bytes_total, flops, wbytes_used, _ = algorithmic_work(cfg, cnt, touched)
     layer_peak = (FP32_PEAK_TFLOPS if cfg.act == "f32" else
                   FP8_PEAK_TFLOPS if cfg.wdt == "mxfp8" else BF16_PEAK_TFLOPS)
@@ -483,6 +510,9 @@ def main():
                   "t_star_ms": round(t_star * 1e3, 5), "t_star_frac": round(t_star * 1e3 / ms_per_step, 4),
                   # per-step spread, from a third region with an event between steps
                   "step_ms": step_pct,
+                  # the same steps replayed from a captured HIP graph
+                  "graph_ms_per_step": round(graph_ms, 5) if graph_ms else None,
+                  "graph_tokens_per_s": round(cfg.T / (graph_ms / 1e3), 2) if graph_ms else None,
                   "experts_empty": int(cfg.E - touched)},
         "roofline": roof,
         "cpu_baseline": cpu,
