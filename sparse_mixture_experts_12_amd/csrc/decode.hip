@@ -435,17 +435,32 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
   __syncthreads();
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   const int npairs = nunits * n_slices;
-#pragma unroll 4
-  for (int i = sl; i < npairs; i += 64) {
-    const int j = i / n_slices, s = i - j * n_slices;
-    const int unit = s_unit[j];
-    if (unit < 0) continue;
-    const float wgt = s_w[j];
-    const float4 v = *reinterpret_cast<const float4*>(partial + (((size_t)unit * n_slices + s) * T + t) * d + col);
-    acc.x = __fmaf_rn(wgt, v.x, acc.x);
-    acc.y = __fmaf_rn(wgt, v.y, acc.y);
-    acc.z = __fmaf_rn(wgt, v.z, acc.z);
-    acc.w = __fmaf_rn(wgt, v.w, acc.w);
+  // RB pairs per batch, all loads issued before the first add: pairs past
+  // the end and dropped slots load a valid partial (unit 0, or the last
+  // pair) and are not added, so no load waits behind a branch
+  constexpr int RB = 4;
+  for (int i0 = sl; i0 < npairs; i0 += 64 * RB) {
+    float4 v[RB];
+    float wgt[RB];
+    bool live[RB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      const int i = i0 + 64 * b;
+      const int ic = i < npairs ? i : npairs - 1;
+      const int j = ic / n_slices, s = ic - j * n_slices;
+      const int unit = s_unit[j];
+      live[b] = i < npairs && unit >= 0;
+      wgt[b] = s_w[j];
+      v[b] = *reinterpret_cast<const float4*>(partial + (((size_t)max(unit, 0) * n_slices + s) * T + t) * d + col);
+    }
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      if (!live[b]) continue;
+      acc.x = __fmaf_rn(wgt[b], v[b].x, acc.x);
+      acc.y = __fmaf_rn(wgt[b], v[b].y, acc.y);
+      acc.z = __fmaf_rn(wgt[b], v[b].z, acc.z);
+      acc.w = __fmaf_rn(wgt[b], v[b].w, acc.w);
+    }
   }
   red[sl][cq] = acc;
   __syncthreads();
