@@ -70,10 +70,30 @@ __device__ __forceinline__ bf16x8_t mc_frag(const bf16_t* Ls, int kbase, int nba
 // NST stages form the ring (3: light row tiles, two steps of loads in flight).
 // K runs over [kbeg, kbeg + nK kBK).  NT / NTS tiles with kpart > 0 (light
 // row tiles split over K) write their fp32 block to p.part slot `slot`.
+// Work-group barrier for LDS only: this wave's LDS operations complete, then
+// s_barrier.  Unlike __syncthreads() it does not wait for outstanding global
+// stores or direct-to-LDS loads, so the weight-gradient stores keep draining
+// across it (the empty asm statements keep the compiler from moving memory
+// operations across the barrier).
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("" ::: "memory");
+  wait_vmem_le_lds0<63>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// TN (weight-gradient) tiles of a persistent work-group also take:
+//   pre: this tile's only K step (nK == 1) was issued into L0 by the previous
+//        tile, before that tile's 64 stores per thread;
+//   nx:  issue the next tile's only K step (tile origin nx_m0, nx_n0, first
+//        padded row nx_k) into L1 here, after the K loop and before this
+//        tile's stores (this tile must lie wholly inside the output, so that
+//        every wave issues exactly 64 stores after those loads).
 template <int MODE, int BMV, int BMMAX = 256, int NST = 2>
 __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0, int rows, int n0, int kbeg,
                                          int nK, bf16_t* L0, bf16_t* L1, bf16_t* L2 = nullptr, int kpart = 0,
-                                         int slot = 0) {
+                                         int slot = 0, bool pre = false, bool nx = false, int nx_m0 = 0,
+                                         int nx_n0 = 0, int nx_k = 0) {
   constexpr bool A_KC = MODE != MODE_TN;
   constexpr bool B_KC = MODE == MODE_NT || MODE == MODE_NTS;
   constexpr bool DUAL = MODE == MODE_GU;
@@ -262,9 +282,16 @@ __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0
     // last step (which would triple the loads of a one-step tile and add a
     // round trip to wait for them)
     bf16x8_t fa[MI], fb[NI];
-    issue(L0, 0);
-    if (nK == 2) issue(L1, kBK);
-    wait_vmem_le<0>();
+    if (pre) {
+      // 16 loads, then exactly 64 stores per wave were issued: at most 63
+      // outstanding means the loads are done (vmcnt retires in issue order),
+      // while the stores keep draining under this tile's MFMAs
+      wait_vmem_le<63>();
+    } else {
+      issue(L0, 0);
+      if (nK == 2) issue(L1, kBK);
+      wait_vmem_le<0>();
+    }
     __builtin_amdgcn_s_barrier();
     for (int st = 0; st < nK; ++st) {
       const bf16_t* L = st ? L1 : L0;
@@ -326,22 +353,23 @@ __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0
   if constexpr (MODE == MODE_TN) {
     // acc[mi][ni][4 q + i] = C[row, col0 + i] with row = row0 + mb + l32 and
     // col0 = n0 + nb + 8 q + 4 lhi (transposed fragment, see mfmas).  The
-    // 256 x 256 fp32 tile leaves through LDS in two halves of 128 rows, so the
-    // global stores are whole 1 KB rows (64 lanes x 16 bytes).  LDS row r
+    // 256 x 256 fp32 tile leaves through L0 in four quarters of 64 rows, so
+    // the global stores are whole 1 KB rows (64 lanes x 16 bytes) and L1 is
+    // free for the next tile's loads.  LDS row r
     // (1 KB) holds 16-byte chunk c at position c ^ (r & 15): the 16-lane
     // passes of both the fragment writes (16 rows, one chunk) and the row
     // reads (one row, 16 chunks) hit distinct banks.
     static_assert(BMV == 256 && WM == 2, "weight-gradient tiles are 256 x 256");
     float* C = shared ? p.Cs : p.C0 + (size_t)g * p.cstride;
-    auto lrow = [&](int r) -> float* { return reinterpret_cast<float*>(r < 64 ? L0 : L1) + (r & 63) * 256; };
+    float* Lq = reinterpret_cast<float*>(L0);     // one 64-row quarter (64 KB) at a time
+    // quarter h of the accumulators -> Lq (the waves holding its 64 rows)
+    auto stage_quarter = [&](int h) {
+      if (wm == (h >> 1)) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      __syncthreads();                            // LDS free (K loop or previous half done)
-      if (wm == h) {
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-          const int r = mi * 32 + l32;
-          float* Lr = lrow(r);
+        for (int m2 = 0; m2 < 2; ++m2) {
+          const int mi = 2 * (h & 1) + m2;
+          const int r = m2 * 32 + l32;
+          float* Lr = Lq + r * 256;
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
@@ -353,17 +381,58 @@ __device__ __forceinline__ void bwd_tile(const BwdGemmParams& p, int g, int row0
             }
         }
       }
-      __syncthreads();
-      // 128 rows x 64 chunks; thread t takes chunk t % 64 of rows t / 64, + 4, ...
-      const int chunk = tid & 63;
-      const int col = n0 + chunk * 4;
+    };
+    // 64 rows x 64 chunks per quarter; thread t takes chunk t % 64 of rows
+    // t / 64, + 4, ...  Stores are non-temporal: the gradients are not read
+    // again here, and streaming writes would otherwise evict the group's rows
+    // that the next tiles reuse.
+    const int chunk = tid & 63;
+    const int col = n0 + chunk * 4;
+    if (row0 + 256 <= p.M && n0 + 256 <= p.N) {
+      // whole tile in range: 16 unconditional stores per thread and quarter,
+      // so every path the compiler sees from a prefetch passes 64 stores
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        lds_sync();                               // LDS free (K loop or previous quarter done)
+        if (h == 0 && nx) {
+          // the next tile's K step into L1 (the sources issue() computes)
+          const uint32_t ka = (uint32_t)nx_k * (uint32_t)p.lda, kb = (uint32_t)nx_k * (uint32_t)p.ldb;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int krow = 2 * (8 * wave + i) + (lane >> 5);
+            const int sw = (lane & 31) ^ (bswz_key(krow) >> 3);
+            int m = nx_m0 + sw * 8;
+            if (m > p.M - 8) m = p.M - 8;
+            int c = nx_n0 + sw * 8;
+            if (c > p.N - 8) c = p.N - 8;
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(p.A0 + ((uint32_t)krow * (uint32_t)p.lda + m + ka)),
+                                             (lds_ptr_t)(L1 + (8 * wave + i) * 512), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(p.B0 + ((uint32_t)krow * (uint32_t)p.ldb + c + kb)),
+                                             (lds_ptr_t)(L1 + LDS_B + (8 * wave + i) * 512), 16, 0, 0);
+          }
+        }
+        stage_quarter(h);
+        lds_sync();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = (tid >> 6) + 4 * i;
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(Lq + r * 256 + ((chunk ^ (r & 15)) << 2));
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(C + (size_t)(row0 + 64 * h + r) * p.N + col));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        lds_sync();
+        stage_quarter(h);
+        lds_sync();
 #pragma unroll 4
-      for (int r = tid >> 6; r < 128; r += 4) {
-        const int grow = row0 + 128 * h + r;
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(lrow(r) + ((chunk ^ (r & 15)) << 2));
-        // non-temporal: the gradients are not read again here, and the streaming
-        // writes would otherwise evict the group's rows that the next tiles reuse
-        if (grow < p.M && col < p.N) __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(C + (size_t)grow * p.N + col));
+        for (int r = tid >> 6; r < 64; r += 4) {
+          const int grow = row0 + 64 * h + r;
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(Lq + r * 256 + ((chunk ^ (r & 15)) << 2));
+          if (grow < p.M && col < p.N)
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(C + (size_t)grow * p.N + col));
+        }
       }
     }
   } else {
@@ -450,29 +519,69 @@ __device__ long long wgrad_first_tile(const int32_t* __restrict__ poff, int G, i
 __global__ __launch_bounds__(256, 1) void bwd_wgrad_kernel(BwdGemmParams p, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) bf16_t L0[512 * kBK];
   __shared__ __attribute__((aligned(1024))) bf16_t L1[512 * kBK];
+  __shared__ int32_t s_poff[kMaxExperts + 1];   // G + 1 <= kMaxExperts + 1 group offsets
   const int per_g = tiles_m * tiles_n;
   const int G = p.G;
+  // the group offsets live in LDS: reading them per tile then never waits on
+  // the vector-memory counter, which the previous tile's stores still hold
+  for (int i = threadIdx.x; i <= G; i += 256) s_poff[i] = p.poff[i];
+  __syncthreads();
   const long long total = (long long)G * per_g;
   const long long W = (long long)per_g * ((long long)p.poff[G] + G * kWgTileCost);
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
   const long long t0 = xcd == 0 ? 0 : wgrad_first_tile(p.poff, G, per_g, W * xcd / 8);
   const long long t1 = xcd == 7 ? total : wgrad_first_tile(p.poff, G, per_g, W * (xcd + 1) / 8);
-  for (long long t = t0 + slot; t < t1; t += nslots) {
-    const int g = (int)(t / per_g);
-    const int r = (int)(t - (long long)g * per_g);
-    // inside a group: strips of 4 tile rows walked column by column, so the
-    // 32 tiles an XCD runs together are 4 row blocks x 8 column blocks and
-    // share 4 + 8 operand blocks from L2 (row-major order would share 1 + 32)
+  // tile t -> group, tile row, tile column, first padded row, K steps.
+  // Inside a group: strips of 4 tile rows walked column by column, so the 32
+  // tiles an XCD runs together are 4 row blocks x 8 column blocks and share
+  // 4 + 8 operand blocks from L2 (row-major order would share 1 + 32).
+  // (all wave-uniform: the group index goes through readfirstlane so the
+  // offsets come in by scalar loads, which do not wait behind the stores)
+  auto tile_of = [&](long long t, int* g, int* tm, int* tn, int* kbeg, int* nK) {
+    *g = __builtin_amdgcn_readfirstlane((int)(t / per_g));
+    const int r = (int)(t - (long long)*g * per_g);
     constexpr int GM = 4;
     const int strip = r / (GM * tiles_n);
     const int rs = r - strip * GM * tiles_n;
     const int gm = min(GM, tiles_m - strip * GM);
-    const int tm = strip * GM + rs % gm, tn = rs / gm;
-    const int kbeg = p.poff[g];
-    const int nK = (p.poff[g + 1] - kbeg) / kBK;
-    bwd_tile<MODE_TN, 256>(p, g, tm * 256, 256, tn * 256, kbeg, nK, L0, L1);
-    __syncthreads();                   // the next tile refills the LDS stages
+    *tm = strip * GM + rs % gm;
+    *tn = rs / gm;
+    *kbeg = __builtin_amdgcn_readfirstlane(s_poff[*g]);
+    *nK = (__builtin_amdgcn_readfirstlane(s_poff[*g + 1]) - *kbeg) / kBK;
+  };
+  // Tiles of one K step (groups of <= 64 rows) are mostly store time (256 KB
+  // of fp32 each).  When the next tile has one K step, its loads go out into
+  // the other stage buffer before this tile's stores, so its MFMAs need not
+  // wait for those stores to drain; the two buffers then swap roles.
+  bf16_t* Lc = L0;
+  bf16_t* Ln = L1;
+  bool pre = false;
+  for (long long t = t0 + slot; t < t1; t += nslots) {
+    // retires a prefetch for this tile (issued before the previous tile's 64
+    // stores per thread) before any LDS access; otherwise it does not wait
+    wait_vmem_le<63>();
+    int g, tm, tn, kbeg, nK;
+    tile_of(t, &g, &tm, &tn, &kbeg, &nK);
+    int nx[3] = {0, 0, 0};
+    bool pf = false;
+    if (t + nslots < t1 && tm * 256 + 256 <= p.M && tn * 256 + 256 <= p.N) {
+      int g2, tm2, tn2, kbeg2, nK2;
+      tile_of(t + nslots, &g2, &tm2, &tn2, &kbeg2, &nK2);
+      if (nK2 == 1) {
+        pf = true;
+        nx[0] = tm2 * 256; nx[1] = tn2 * 256; nx[2] = kbeg2;
+      }
+    }
+    bwd_tile<MODE_TN, 256>(p, g, tm * 256, 256, tn * 256, kbeg, nK, Lc, Ln, nullptr, 0, 0, pre, pf, nx[0], nx[1],
+                           nx[2]);
+    if (pf) {
+      bf16_t* tmp = Lc;
+      Lc = Ln;
+      Ln = tmp;
+    }
+    pre = pf;
+    lds_sync();                        // the next tile reads or refills the LDS stages
   }
 }
 
