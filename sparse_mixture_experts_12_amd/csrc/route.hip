@@ -228,14 +228,17 @@ __device__ __forceinline__ void load8(const TIn* __restrict__ W, size_t off, int
 }
 
 // Rank-based top-k of one token (E <= 256) by one wave; lg in LDS.
-__device__ void wave_topk_rank(const float* lg, int E, int k, int renormalize, int32_t* sel /* LDS [k] */,
-                               double* ps /* LDS [max(E,k)] */, int32_t* out_idx, float* out_w) {
+// SL = logit slots per lane (E <= 64 * SL): the code a single call runs
+// shrinks with E, which matters for the one-work-group decode router.
+template <int SL>
+__device__ void wave_topk_rank_sl(const float* lg, int E, int k, int renormalize, int32_t* sel /* LDS [k] */,
+                                  double* ps /* LDS [max(E,k)] */, int32_t* out_idx, float* out_w) {
   const int lane = lane_id();
-  float v[4];
-  int rank[4];
+  float v[SL];
+  int rank[SL];
   float m = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < SL; ++i) {
     v[i] = (lane + 64 * i < E) ? lg[lane + 64 * i] : -INFINITY;
     rank[i] = 0;
   }
@@ -243,14 +246,14 @@ __device__ void wave_topk_rank(const float* lg, int E, int k, int renormalize, i
     const float u = lg[e2];
     m = fmaxf(m, u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < SL; ++i) {
       const int e = lane + 64 * i;
       rank[i] += (u > v[i] || (u == v[i] && e2 < e)) ? 1 : 0;
     }
   }
-  double p[4];
+  double p[SL];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < SL; ++i) {
     const int e = lane + 64 * i;
     p[i] = (e < E) ? exp((double)v[i] - (double)m) : 0.0;
     if (e < E && rank[i] < k) {
@@ -269,6 +272,13 @@ __device__ void wave_topk_rank(const float* lg, int E, int k, int renormalize, i
     out_idx[lane] = e;
     out_w[lane] = (float)((renormalize ? ps[lane] : ps[e]) / den);
   }
+}
+
+__device__ void wave_topk_rank(const float* lg, int E, int k, int renormalize, int32_t* sel, double* ps,
+                               int32_t* out_idx, float* out_w) {
+  if (E <= 64) wave_topk_rank_sl<1>(lg, E, k, renormalize, sel, ps, out_idx, out_w);
+  else if (E <= 128) wave_topk_rank_sl<2>(lg, E, k, renormalize, sel, ps, out_idx, out_w);
+  else wave_topk_rank_sl<4>(lg, E, k, renormalize, sel, ps, out_idx, out_w);
 }
 
 constexpr int kSmallMaxS = 32;   // d slices of a split small-T router
