@@ -32,6 +32,9 @@ CASES = {
     "T1": C["mixtral_prefill"].with_(T=1, d=256, f=256, seed=46),
     "d64_f64": C["mixtral_prefill"].with_(T=90, d=64, f=64, seed=47),
     "tight_capacity": C["mixtral_prefill"].with_(T=64, d=256, E=8, f=128, capacity_factor=0.5, seed=48),
+    # one-step weight-gradient tiles (<= 64 rows per group) whose 256 x 256 tiles alternate between whole
+    # and partial (f = 384: partial columns for dW_gate/dW_up, partial rows for dW_down), plus empty groups
+    "wgrad_mixed_tiles": C["fine_grained"].with_(T=128, d=512, E=16, k=2, f=384, seed=49),
 }
 
 
