@@ -31,7 +31,9 @@ Sources (page titles; sections named on each page):
 Readings where the pages are silent:
   * router logit = fp32 rounding (RNE) of the fp64 sum x.W_g (+ bias), so a
     GPU that accumulates in fp64 selects the same experts (certificate below);
-  * equal probabilities are ordered by the lower expert index;
+  * experts are selected on those fp32 logits, larger first, equal logits
+    ordered by the lower expert index (the same order as the probabilities,
+    which fp64 rounding or underflow could merge);
   * capacity C = max(1, ceil(cf * T * k / E)) with cf the fp32 capacity
     factor; priority is assignment order a = t*k + j; dropped assignments add
     nothing and the remaining weights are not renormalised again;
@@ -61,15 +63,23 @@ def _f64(a) -> np.ndarray:
 # 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no infinities,
 # exponent 1111 with mantissa 111 is NaN, exponent 0000 is subnormal).
 # ----------------------------------------------------------------------------
-def fp8_e4m3fn_decode(codes) -> np.ndarray:
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
-    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+def _e4m3fn_value(c: int) -> float:
+    sign = -1.0 if (c >> 7) & 1 else 1.0
     exp = (c >> 3) & 0xF
-    man = (c & 0x7).astype(np.float64)
-    normal = (1.0 + man / 8.0) * np.exp2(exp.astype(np.float64) - 7.0)
-    sub = (man / 8.0) * 2.0 ** -6
-    val = sign * np.where(exp == 0, sub, normal)
-    return np.where((exp == 15) & ((c & 7) == 7), np.nan, val)
+    man = c & 0x7
+    if exp == 15 and man == 7:
+        return math.nan
+    if exp == 0:                        # subnormal: 0.mmm x 2^-6
+        return sign * (man / 8.0) * 2.0 ** -6
+    return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+
+
+_E4M3FN_VALUES = np.array([_e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+
+
+def fp8_e4m3fn_decode(codes) -> np.ndarray:
+    """Value of every code: the 256 values above, looked up by code."""
+    return _E4M3FN_VALUES[np.asarray(codes, dtype=np.uint8)]
 
 
 def dequantize(codes, scale, channel_axis: int) -> np.ndarray:
@@ -103,20 +113,24 @@ def softmax_rows(logits32) -> np.ndarray:
     return p
 
 
-def topk_select(probs, k: int) -> np.ndarray:
-    """Per token, the k experts of largest probability, largest first; equal
-    probabilities ordered by the lower expert index ([MIX] topk)."""
-    T, E = probs.shape
+def topk_select(logits32, k: int) -> np.ndarray:
+    """Per token, the k experts of largest fp32 router logit, largest first;
+    equal logits ordered by the lower expert index ([MIX] topk of the softmax).
+    Softmax is strictly increasing in the logit, so these are the top-k
+    probabilities; ranking the fp32 logits themselves keeps apart experts whose
+    fp64 probabilities round (or underflow) to the same value."""
+    l = _f64(logits32)
+    T, E = l.shape
     idx = np.empty((T, k), dtype=np.int32)
     for t in range(T):
-        order = sorted(range(E), key=lambda e: (-probs[t, e], e))
+        order = sorted(range(E), key=lambda e: (-l[t, e], e))
         idx[t] = order[:k]
     return idx
 
 
 def routing_weights(probs, idx, renormalize: bool) -> np.ndarray:
-    """Top-k probabilities, divided by their sum when renormalising ([MIX]
-    'Normalize top-2 weights to sum to 1'; [DSK] same step)."""
+    """Top-k probabilities, divided by their sum when renormalising (the step
+    after the top-k in [MIX] "Sparse MoE Block"; [DSK] does the same)."""
     T, k = idx.shape
     w = np.empty((T, k), dtype=np.float64)
     for t in range(T):
@@ -219,7 +233,7 @@ def forward(x, W_g, bias, k: int, renormalize: bool, capacity_factor,
     T = x.shape[0]
     logits = router_logits(x, W_g, bias, round_logits)
     probs = softmax_rows(logits)
-    idx = topk_select(probs, k)
+    idx = topk_select(logits, k)
     w = routing_weights(probs, idx, renormalize)
     cap = capacity(T, k, E, capacity_factor)
     perm = permute(idx, E, cap)
@@ -257,17 +271,36 @@ def forward(x, W_g, bias, k: int, renormalize: bool, capacity_factor,
 # fp64 summation order when adjacent fp64 logit sums among the top k+1 are
 # separated by more than both sums' worst-case error plus two fp32 ulps.
 # ----------------------------------------------------------------------------
-def routing_certificate(x, W_g, bias, k: int) -> dict:
+def logit_error_bound(x, W_g, bias=None) -> np.ndarray:
+    """Worst-case distance between the exact router sum x.W_g (+ b) and its
+    value computed in fp64 with any order of the d (+1) additions: the
+    recursive-summation bound gamma_n * sum |terms| with gamma_n = n u /
+    (1 - n u), n = d + 1 and u = 2^-53 (products of bf16 or fp32 values are
+    exact in fp64, so only the additions round)."""
     x, W = _f64(x), _f64(W_g)
-    T, d = x.shape
-    E = W.shape[1]
-    s = x @ W
-    if bias is not None:
-        s = s + _f64(bias)[None, :]
+    d = x.shape[1]
     gamma = (d + 1) * U64 / (1.0 - (d + 1) * U64)
     bound = gamma * (np.abs(x) @ np.abs(W))
     if bias is not None:
         bound = bound + gamma * np.abs(_f64(bias))[None, :]
+    return bound
+
+
+def routing_certificate(x, W_g, bias, k: int) -> dict:
+    """ok[t]: token t's top-k (and slot order) on fp32-rounded logits is the
+    same for every fp64 summation order.  The fp64 sums s computed here and
+    any other order's sums are each within `bound` of the exact value, so two
+    experts keep their order (or tie) in every order when their computed gap
+    exceeds twice both bounds plus two fp32 ulps: the ulps cover two sums on
+    either side of one fp32 rounding boundary, which one order may round
+    apart and another together (a tie, broken by the expert index)."""
+    x, W = _f64(x), _f64(W_g)
+    T = x.shape[0]
+    E = W.shape[1]
+    s = x @ W
+    if bias is not None:
+        s = s + _f64(bias)[None, :]
+    bound = logit_error_bound(x, W, bias)
     ok = np.ones(T, dtype=bool)
     margin = np.full(T, np.inf)
     for t in range(T):
@@ -279,7 +312,7 @@ def routing_certificate(x, W_g, bias, k: int) -> dict:
             margin[t] = min(margin[t], gap - need)
             if not gap > need:
                 ok[t] = False
-    return dict(ok=ok, margin=margin)
+    return dict(ok=ok, margin=margin, bound=bound)
 
 
 # ----------------------------------------------------------------------------
@@ -469,7 +502,7 @@ def backward(x, W_g, bias, k: int, renormalize: bool, capacity_factor, expert: E
     T, d = x.shape
     logits = router_logits(x, W_g, bias, round_logits)
     probs = softmax_rows(logits)
-    idx = topk_select(probs, k)
+    idx = topk_select(logits, k)
     w = routing_weights(probs, idx, renormalize)
     perm = permute(idx, E, capacity(T, k, E, capacity_factor))
     f = _f64(expert(0)[0]).shape[1]

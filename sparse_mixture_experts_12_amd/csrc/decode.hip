@@ -27,7 +27,9 @@
 // DS parts in order, forms h and streams a block of FS2 rows x DW columns of
 // W_down per work-group; the same reduce kernel finishes.
 #include <hip/hip_ext.h>
-#include <stdlib.h>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -482,17 +484,29 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
   }
 }
 
+// Kernels whose dynamic LDS exceeds the default 64 KB limit need the limit
+// raised once per kernel and device; the largest size granted so far is
+// remembered, so steady-state calls make no runtime call for it.
+static hipError_t allow_dynamic_lds(const void* fn, size_t lds) {
+  if (lds <= 64 * 1024) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, size_t> granted;
+  std::lock_guard<std::mutex> lock(mu);
+  size_t& have = granted[{fn, dev}];
+  if (have >= lds) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess) have = lds;
+  return e;
+}
+
 static int pick_mt(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8; }
 
 // Slice width: the widest slice (longest contiguous row segment of W_gate /
 // W_up, at most 512 bytes) that still gives every CU at least one work unit.
 static int pick_fs(int units, int f, int es) {
-  static int forced = -1;
-  if (forced < 0) {
-    const char* e = getenv("MOE_DECODE_FS");
-    forced = e ? atoi(e) : 0;
-  }
-  if ((forced == 64 || forced == 128 || forced == 256) && f % forced == 0) return forced;
   const int cands[3] = {256, 128, 64};
   for (int c : cands) {
     if (f % c) continue;
@@ -550,10 +564,7 @@ static hipError_t launch_decode_split(const DecodeParams& p, int units, const De
     const size_t xs_bytes = (size_t)(p.d / sp.DS) * MT * sizeof(bf16_t);
     const size_t red_bytes = (size_t)(RG * 2 * MT * FS + MT * FS) * sizeof(float);
     const size_t lds = xs_bytes > red_bytes ? xs_bytes : red_bytes;
-    if (lds > 64 * 1024) {
-      hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-    }
+    if (hipError_t e = allow_dynamic_lds((const void*)kern, lds); e != hipSuccess) return e;
     const dim3 grid(p.f / FS, units, sp.DS);
     if (ev_begin)
       hipExtLaunchKernelGGL(kern, grid, dim3(256), (uint32_t)lds, s, ev_begin, nullptr, 0, p);
@@ -592,11 +603,7 @@ static hipError_t launch_decode_t(const DecodeParams& p, int units, hipStream_t 
   size_t xs_bytes = (size_t)p.d * MT * sizeof(bf16_t);
   size_t red_bytes = (size_t)(RG * 2 * MT * FS + MT * FS) * sizeof(float);
   size_t lds = xs_bytes > red_bytes ? xs_bytes : red_bytes;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_ffn_kernel<WK, MT, FS>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  if (hipError_t e = allow_dynamic_lds((const void*)decode_ffn_kernel<WK, MT, FS>, lds); e != hipSuccess) return e;
   dim3 grid(p.f / FS, units);
   if (ev_begin || ev_end)
     hipExtLaunchKernelGGL(decode_ffn_kernel<WK, MT, FS>, grid, dim3(256), (uint32_t)lds, s, ev_begin, ev_end, 0, p);

@@ -60,8 +60,6 @@ moe_status check_desc(const moe_desc* d) {
     if ((double)d->T * d->d >= 2147483648.0 || rows * d->f >= 2147483648.0)
       return fail(MOE_ERR_UNSUPPORTED, "MXFP8 layer too large (T*d and rows*f must stay below 2^31)");
   }
-  if (d->routing != MOE_ROUTING_TOKEN_CHOICE && d->routing != MOE_ROUTING_EXPERT_CHOICE)
-    return fail(MOE_ERR_INVALID_ARG, "bad routing %d", d->routing);
   if (d->routing == MOE_ROUTING_EXPERT_CHOICE) {
     if (d->path == MOE_PATH_FUSED_DECODE)
       return fail(MOE_ERR_UNSUPPORTED, "expert-choice routing runs on the grouped path");

@@ -35,7 +35,60 @@ CASES = {
     # one-step weight-gradient tiles (<= 64 rows per group) whose 256 x 256 tiles alternate between whole
     # and partial (f = 384: partial columns for dW_gate/dW_up, partial rows for dW_down), plus empty groups
     "wgrad_mixed_tiles": C["fine_grained"].with_(T=128, d=512, E=16, k=2, f=384, seed=49),
+    # 65 one-step groups x 15 tiles per weight-gradient launch (~122 tiles per XCD): every persistent
+    # work-group runs several one-step tiles in a row, whole tiles prefetching partial ones (f = 640)
+    "wgrad_prefetch_partial": C["fine_grained"].with_(T=64, d=1280, E=64, k=2, f=640, seed=50),
 }
+
+WG_TILE_COST = 96      # the weight-gradient kernel's per-tile cost term (rows + this)
+
+
+def _wgrad_prefetch_pairs(counts, T, has_shared, M, N, n_cu):
+    """Host replay of the persistent weight-gradient launch's tile split: the
+    pairs (t, t + nslots) one work-group runs back to back where tile t is
+    whole and the next tile has one K step (so its loads are issued before
+    tile t's stores), returned as (next tile is partial) flags."""
+    groups = [int(c) for c in counts] + ([T] if has_shared else [])
+    padded = [(r + 63) // 64 * 64 for r in groups]
+    poff = np.concatenate([[0], np.cumsum(padded)]).astype(np.int64)
+    G = len(groups)
+    tm_n, tn_n = (M + 255) // 256, (N + 255) // 256
+    per_g = tm_n * tn_n
+    total = G * per_g
+    W = per_g * (int(poff[G]) + G * WG_TILE_COST)
+
+    def gstart(g):
+        return per_g * (int(poff[g]) + g * WG_TILE_COST)
+
+    def first_tile(w):
+        g = max(i for i in range(G + 1) if gstart(i) <= w)
+        if g >= G:
+            return G * per_g
+        cost = int(poff[g + 1] - poff[g]) + WG_TILE_COST
+        return g * per_g + min(per_g, -(-(w - gstart(g)) // cost))
+
+    def tile_of(t):
+        g, r = divmod(t, per_g)
+        strip, rs = divmod(r, 4 * tn_n)
+        gm = min(4, tm_n - strip * 4)
+        return g, strip * 4 + rs % gm, rs // gm, int(poff[g + 1] - poff[g]) // 64
+
+    grid = 8 * ((n_cu + 7) // 8)
+    nslots = grid // 8
+    flags = []
+    for xcd in range(8):
+        t0 = 0 if xcd == 0 else first_tile(W * xcd // 8)
+        t1 = total if xcd == 7 else first_tile(W * (xcd + 1) // 8)
+        for t in range(t0, t1):
+            if t + nslots >= t1:
+                continue
+            _, tm, tn, _ = tile_of(t)
+            if tm * 256 + 256 > M or tn * 256 + 256 > N:
+                continue
+            _, tm2, tn2, nk2 = tile_of(t + nslots)
+            if nk2 == 1:
+                flags.append(tm2 * 256 + 256 > M or tn2 * 256 + 256 > N)
+    return flags
 
 
 def _dout(cfg, seed=7):
@@ -82,6 +135,15 @@ def test_backward_parity_small(name):
         for key in ("dWs_gate", "dWs_up", "dWs_down"):
             errs[key] = assert_close(to64(g[key]), ref[key], TOL, f"{name} {key}")
     r = ov.forward(tokens=np.arange(min(cfg.T, 1)))
+    if name == "wgrad_prefetch_partial":
+        # the case exists to run the prefetch of a partial one-step tile: check on the host that the
+        # launch's own tile split (dW_gate / dW_up: M = d, N = f; dW_down: M = f, N = d) contains it
+        n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+        flags = (_wgrad_prefetch_pairs(r["counts"], cfg.T, cfg.shared, cfg.d, cfg.f, n_cu) +
+                 _wgrad_prefetch_pairs(r["counts"], cfg.T, cfg.shared, cfg.f, cfg.d, n_cu))
+        assert any(flags) and not all(flags), f"prefetched tiles: {len(flags)}, partial: {sum(flags)}"
+        print(f"[backward] {name}: {len(flags)} prefetched one-step tiles, {sum(flags)} of them partial",
+              flush=True)
     empty = np.nonzero(r["counts"] == 0)[0]
     for e in empty:                                     # experts without tokens: exactly zero
         for key in ("dW_gate", "dW_up", "dW_down"):
@@ -157,12 +219,17 @@ def test_backward_parity_full_size(name, ntok, ncol):
     ref_fwd = ov.forward(tokens=np.arange(1))
     rng = np.random.default_rng(3)
     toks = np.sort(rng.choice(cfg.T, size=ntok, replace=False))
-    if cfg.E <= 16:
-        # also the token owning each expert's last row: its padded group's last
-        # (light, possibly K-split) row tile
-        offs, sa = ref_fwd["offsets"], ref_fwd["sorted_assign"]
-        tails = [int(sa[offs[e + 1] - 1]) // cfg.k for e in range(cfg.E) if offs[e + 1] > offs[e]]
-        toks = np.unique(np.concatenate([toks, np.array(tails, dtype=toks.dtype)]))
+    # also the token owning each expert's last row: its padded group's last
+    # (light, possibly K-split) row tile; with many experts, those of the
+    # heaviest, a median and the lightest non-empty expert
+    offs, sa = ref_fwd["offsets"], ref_fwd["sorted_assign"]
+    counts = ref_fwd["counts"]
+    nonempty = [e for e in range(cfg.E) if counts[e] > 0]
+    if cfg.E > 16:
+        by_load = sorted(nonempty, key=lambda e: (counts[e], e))
+        nonempty = sorted({by_load[-1], by_load[len(by_load) // 2], by_load[0]})
+    tails = [int(sa[offs[e + 1] - 1]) // cfg.k for e in nonempty]
+    toks = np.unique(np.concatenate([toks, np.array(tails, dtype=toks.dtype)]))
     got = to64(g["dx"][torch.from_numpy(toks).cuda()])
     want = np.stack([_token_dx(ov, cfg, ref_fwd, dout64, int(t)) for t in toks])
     e_dx = assert_close(got, want, TOL, f"{name} dx (sampled tokens)")
@@ -187,8 +254,8 @@ def test_backward_parity_full_size(name, ntok, ncol):
     for e in empty[:2]:
         for key in ("dW_gate", "dW_up", "dW_down"):
             assert torch.count_nonzero(g[key][int(e)]) == 0, (key, e)
-    print(f"[backward-full] {name}: dx rel_err={e_dx:.3e} dW rel_err max={max(errs):.3e} "
-          f"experts={experts} empty={len(empty)}", flush=True)
+    print(f"[backward-full] {name}: dx rel_err={e_dx:.3e} on {len(toks)} tokens (tails of experts {nonempty}) "
+          f"dW rel_err max={max(errs):.3e} experts={experts} empty={len(empty)}", flush=True)
 
 
 def test_backward_hip_graph_capture_replay():

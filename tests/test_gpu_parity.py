@@ -109,7 +109,7 @@ def test_route_parity(name):
     ov = OracleInputs(inp)
     ref_logits = oracle.router_logits(ov.x, ov.W_g, ov.bias)
     probs = oracle.softmax_rows(ref_logits)
-    ref_idx = oracle.topk_select(probs, k)
+    ref_idx = oracle.topk_select(ref_logits, k)
     ref_w = oracle.routing_weights(probs, ref_idx, cfg.renormalize)
     cert = ov.certificate()
     assert cert["ok"].all(), f"routing not certified for tokens {np.nonzero(~cert['ok'])[0][:10]}"
@@ -154,8 +154,8 @@ def test_route_without_logits_output():
     ops.route(desc, inp["x"], ops.weights_struct(inp), idx, w, None, ws)
     torch.cuda.synchronize()
     ov = OracleInputs(inp)
-    probs = oracle.softmax_rows(oracle.router_logits(ov.x, ov.W_g, ov.bias))
-    np.testing.assert_array_equal(idx.cpu().numpy(), oracle.topk_select(probs, cfg.k))
+    logits = oracle.router_logits(ov.x, ov.W_g, ov.bias)
+    np.testing.assert_array_equal(idx.cpu().numpy(), oracle.topk_select(logits, cfg.k))
 
 
 # ---------------------------------------------------------------------------
@@ -357,12 +357,33 @@ def test_hip_graph_capture_replay(name):
 
 # ---------------------------------------------------------------------------
 # Whole layer at the workloads' full sizes: routing and permutation on every
-# token, outputs on a sample of tokens the oracle recomputes one by one.
+# token; outputs on sampled tokens plus, for every non-empty expert, the tokens
+# owning its first and last permuted rows, and tokens on the shared expert's
+# row-tile boundaries, all recomputed by the oracle.
 # ---------------------------------------------------------------------------
 FULL = ["tiny_f32", "mixtral_decode", "mixtral_decode_b8", "mixtral_prefill", "fine_grained",
         "fp8_capacity", "fp8_capacity_decode", "mixtral_prefill_mxfp8", "fine_grained_mxfp8"]
 SAMPLE = {"mixtral_prefill": 12, "fine_grained": 3, "fp8_capacity": 24, "mixtral_prefill_mxfp8": 12,
           "fine_grained_mxfp8": 3}
+TILE = 64          # the smallest row-tile height any grouped GEMM body uses
+
+
+def _edge_tokens(offsets, sorted_assign, k, E):
+    """Tokens owning each non-empty expert's first and last permuted rows."""
+    out = []
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            out += [int(sorted_assign[lo]) // k, int(sorted_assign[hi - 1]) // k]
+    return out
+
+
+def _tile_edge_rows(lo, hi, tile=TILE):
+    """First and last row of every `tile`-row block of rows [lo, hi)."""
+    rows = set()
+    for r in range(lo, hi, tile):
+        rows.update((r, min(r + tile, hi) - 1))
+    return sorted(rows)
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -377,23 +398,81 @@ def test_forward_parity_full_size(name):
     st = ops.Stats(d_n_dropped=dev_nd.data_ptr(), d_counts=dev_counts.data_ptr())
     out, taken = run_forward(inp, stats=st)
     n = SAMPLE.get(name)
-    toks = None if n is None else np.sort(np.random.default_rng(0).choice(cfg.T, size=n, replace=False))
-    if toks is not None and cfg.E <= 16:
-        # also the token owning each expert's last permuted row, so every expert's
-        # last (partial, possibly K-split) row tile is checked
+    toks = None
+    if n is not None:
         routing = ov.forward(tokens=np.arange(0))
-        offs, sa = routing["offsets"], routing["sorted_assign"]
-        tails = [int(sa[offs[e + 1] - 1]) // cfg.k for e in range(cfg.E) if offs[e + 1] > offs[e]]
-        toks = np.unique(np.concatenate([toks, np.array(tails, dtype=toks.dtype)]))
+        picks = [np.random.default_rng(0).choice(cfg.T, size=n, replace=False),
+                 _edge_tokens(routing["offsets"], routing["sorted_assign"], cfg.k, cfg.E)]
+        if cfg.shared:
+            picks.append(_tile_edge_rows(0, cfg.T))
+        toks = np.unique(np.concatenate([np.asarray(p, dtype=np.int64) for p in picks]))
     ref = ov.forward(tokens=toks)
     got = to64(out) if toks is None else to64(out)[toks]
     e = assert_close(got, ref["out"], TOL[cfg.wdt], name)
-    print(f"[forward-full] {name}: path={taken} rel_err={e:.3e} dropped={ref['n_dropped']} "
+    covered = sum(1 for i in range(cfg.E) if ref["counts"][i] > 0)
+    print(f"[forward-full] {name}: path={taken} rel_err={e:.3e} tokens_checked={len(ref['out'])}/{cfg.T} "
+          f"experts_covered={covered}/{covered} dropped={ref['n_dropped']} "
           f"empty_experts={(ref['counts'] == 0).sum()}", flush=True)
     np.testing.assert_array_equal(dev_counts.cpu().numpy(), ref["counts"])
     assert int(dev_nd.cpu()[0]) == ref["n_dropped"]
     if name == "fine_grained":
         assert (ref["counts"] == 0).sum() >= 1, "the Zipf bias should leave some expert without tokens"
+
+
+# Grouped FFN at full size, expert by expert: the rows on every 64-row tile
+# boundary of every non-empty expert (so every row tile of every expert, heavy,
+# light or split over K, is compared on every output column) and of the shared
+# expert, against the oracle's FFN of that expert alone.  Expert-choice layers
+# feed the same kernels the oracle's expert-choice selection (E*C rows, token t
+# given as assignment t*k).
+GROUPED_FULL = ["mixtral_prefill", "fine_grained", "fp8_capacity", "mixtral_prefill_mxfp8",
+                "fine_grained_mxfp8", "fine_grained_expert_choice"]
+
+
+@pytest.mark.parametrize("name", GROUPED_FULL)
+def test_grouped_ffn_every_expert_full_size(name):
+    ec = name.endswith("_expert_choice")
+    cfg = C[name[:-len("_expert_choice")] if ec else name]
+    print(f"[grouped-full] {name}", flush=True)
+    inp = device_inputs(cfg)
+    ov = OracleInputs(inp)
+    T, k, d, E = cfg.T, cfg.k, cfg.d, cfg.E
+    if ec:
+        r = oracle.expert_choice_routing(oracle.router_logits(ov.x, ov.W_g, ov.bias), k,
+                                         np.float32(cfg.capacity_factor), cfg.renormalize)
+        offsets = r["offsets"].astype(np.int32)
+        assert offsets[-1] == T * k, "the expert-choice rows must fill the T*k routed rows"
+        sa = (r["sorted_tokens"] * k).astype(np.int32)
+    else:
+        r = ov.forward(tokens=np.arange(0))
+        offsets = r["offsets"]
+        sa = np.full(T * k, -1, dtype=np.int32)
+        sa[:len(r["sorted_assign"])] = r["sorted_assign"]
+    rows = T * k + (T if cfg.shared else 0)
+    y = torch.full((rows, d), float("nan"), dtype=torch.float32, device="cuda")
+    desc = ops.desc_from_cfg(cfg)
+    ws = ops.alloc_workspace(desc)
+    ops.grouped_ffn(desc, inp["x"], ops.weights_struct(inp), torch.from_numpy(sa).cuda(),
+                    torch.from_numpy(offsets).cuda(), y, ws)
+    torch.cuda.synchronize()
+    kept = int(offsets[-1])
+    assert bool(torch.isnan(y[kept:T * k]).all()), "rows past the kept ones must stay untouched"
+    worst, n_rows, covered = 0.0, 0, 0
+    nonempty = [e for e in range(E) if offsets[e + 1] > offsets[e]]
+    for e in nonempty:
+        rr = _tile_edge_rows(int(offsets[e]), int(offsets[e + 1]))
+        toks = sa[rr] // k
+        got = to64(y[torch.tensor(rr, device="cuda")])
+        worst = max(worst, assert_close(got, ov.ffn(ov.x[toks], e), TOL[cfg.wdt], f"{name} expert {e} rows {rr[:4]}"))
+        n_rows += len(rr)
+        covered += 1
+    if cfg.shared:
+        tt = _tile_edge_rows(0, T)
+        got = to64(y[torch.tensor([T * k + t for t in tt], device="cuda")])
+        worst = max(worst, assert_close(got, ov.ffn(ov.x[tt]), TOL[cfg.wdt], f"{name} shared rows"))
+        n_rows += len(tt)
+    print(f"[grouped-full] {name}: experts covered {covered}/{len(nonempty)} (+shared={cfg.shared}), "
+          f"rows checked {n_rows}/{kept + (T if cfg.shared else 0)}, worst rel_err={worst:.3e}", flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -498,7 +577,14 @@ def test_expert_choice_parity(name):
     out, taken = run()
     assert taken == ops.PATH_GROUPED
     n = EC_SAMPLE.get(name)
-    toks = None if n is None else np.sort(np.random.default_rng(1).choice(cfg.T, size=n, replace=False))
+    toks = None
+    if n is not None:
+        r = oracle.expert_choice_routing(oracle.router_logits(ov.x, ov.W_g, ov.bias), cfg.k,
+                                         np.float32(cfg.capacity_factor), cfg.renormalize)
+        edges = [int(r["sorted_tokens"][i]) for e in range(cfg.E)
+                 for i in (int(r["offsets"][e]), int(r["offsets"][e + 1]) - 1)]
+        toks = np.unique(np.concatenate([np.random.default_rng(1).choice(cfg.T, size=n, replace=False),
+                                         np.array(edges, dtype=np.int64)]))
     ref = oracle.expert_choice_forward(ov.x, ov.W_g, ov.bias, cfg.k, cfg.renormalize,
                                        np.float32(cfg.capacity_factor), ov.expert, cfg.E, shared=ov.shared(),
                                        tokens=toks, **ov.quant_hooks())
@@ -512,7 +598,8 @@ def test_expert_choice_parity(name):
     e = assert_close(got, ref["out"], TOL[cfg.wdt], name)
     out2, _ = run()
     assert torch.equal(out2, out)                       # bitwise reproducible
-    print(f"[expert-choice] {name}: C={Cap} unchosen_tokens={unchosen} rel_err={e:.3e}", flush=True)
+    print(f"[expert-choice] {name}: C={Cap} unchosen_tokens={unchosen} rel_err={e:.3e} "
+          f"tokens_checked={len(got)}/{cfg.T}", flush=True)
 
 
 # ---------------------------------------------------------------------------

@@ -130,7 +130,7 @@ def test_softmax_matches_scipy_and_topk_weights():
     p = oracle.softmax_rows(l)
     np.testing.assert_allclose(p, softmax(l.astype(np.float64), axis=1), rtol=1e-14, atol=0)
     for k in (1, 2, 6):
-        idx = oracle.topk_select(p, k)
+        idx = oracle.topk_select(l, k)
         w_on = oracle.routing_weights(p, idx, True)
         w_off = oracle.routing_weights(p, idx, False)
         np.testing.assert_allclose(w_on.sum(1), 1.0, rtol=0, atol=1e-15)
@@ -170,8 +170,7 @@ def test_topk_brute_force_with_ties(trial):
     k = int(rng.integers(1, E + 1))
     # few distinct values so ties are common
     l = np.float32(rng.integers(-3, 3, size=E) * 0.25 + (0 if trial % 2 else rng.normal(size=E)))
-    p = oracle.softmax_rows(l[None, :])
-    idx = oracle.topk_select(p, k)[0].tolist()
+    idx = oracle.topk_select(l[None, :], k)[0].tolist()
     assert set(idx) == _brute_topk(l, k)
     for a, b in zip(idx[:-1], idx[1:]):            # slots: larger first, ties lower index first
         assert l[a] > l[b] or (l[a] == l[b] and a < b)
@@ -353,6 +352,114 @@ def test_certificate_flags_near_ties():
     assert oracle.routing_certificate(x, W2, None, 2)["ok"][0]
 
 
+def _fp64_sum_in_order(terms, order):
+    acc = 0.0
+    for i in order:
+        acc = acc + float(terms[i])              # one IEEE fp64 addition per term
+    return acc
+
+
+def test_logit_error_bound_holds_for_every_summation_order():
+    """The certificate's bound against the exact sum (Fractions) of every
+    ordering of the additions.  Adding tiny terms one by one to 1 loses each
+    of them (ties to even), so some order misses the exact sum by (d - 1)
+    units of roundoff: more than half of the bound, which a halved bound
+    would no longer cover."""
+    u = 2.0 ** -53
+    d = 7
+    x = np.ones((1, d))
+    W = np.array([[1.0], *[[u]] * (d - 1)])
+    terms = (x[0] * W[:, 0]).tolist()
+    exact = sum(Fraction(t) for t in terms)
+    worst = max(abs(Fraction(_fp64_sum_in_order(terms, o)) - exact) for o in itertools.permutations(range(d)))
+    bound = float(oracle.logit_error_bound(x, W)[0, 0])
+    assert worst == Fraction(d - 1) * Fraction(u)
+    assert Fraction(bound) >= worst
+    assert worst > Fraction(bound) / 2
+    # with a bias term (d + 1 additions) and random mixed-sign terms
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        x = rng.normal(size=(1, 6)) * np.exp2(rng.integers(-30, 30, size=(1, 6)))
+        W = rng.normal(size=(6, 1))
+        b = rng.normal(size=1)
+        terms = (x[0] * W[:, 0]).tolist() + [float(b[0])]
+        if any(Fraction(t) != Fraction(x[0, i]) * Fraction(W[i, 0]) for i, t in enumerate(terms[:6])):
+            continue                              # keep only exact products
+        exact = sum(Fraction(t) for t in terms)
+        bound = Fraction(float(oracle.logit_error_bound(x, W, b)[0, 0]))
+        for o in itertools.permutations(range(7)):
+            assert abs(Fraction(_fp64_sum_in_order(terms, o)) - exact) <= bound
+
+
+def test_certificate_rejects_a_token_whose_selection_depends_on_the_order():
+    """Expert 1's sum lies a quarter fp64 ulp above the midpoint between the
+    fp32 values 1 and 1 + 2^-23.  Depending on the order of its additions it
+    rounds to either, so its fp32 logit either beats expert 0's (exactly 1)
+    or ties with it, and the tie goes to expert 0: the top-1 is not fixed.
+    The fp64 error bounds are ~1e-15 against a gap of 6e-8, so only the
+    certificate's fp32 ulp term can reject this token."""
+    m = 1.0 + 2.0 ** -24
+    e1, e2 = 0.75 * 2.0 ** -52, -0.5 * 2.0 ** -52
+    x = np.ones((1, 3))
+    W = np.array([[1.0, m], [0.0, e1], [0.0, e2]])
+    picks = set()
+    for o in itertools.permutations(range(3)):
+        l32 = np.array([[np.float32(_fp64_sum_in_order(W[:, e], o)) for e in range(2)]], dtype=np.float32)
+        picks.add(int(oracle.topk_select(l32, 1)[0, 0]))
+    assert picks == {0, 1}
+    c = oracle.routing_certificate(x, W, None, 1)
+    assert not c["ok"][0]
+    assert float(c["bound"].max()) < 1e-14
+    # well apart (expert 1 a few fp32 ulps above expert 0): certified, and every order agrees
+    W2 = W.copy()
+    W2[0, 1] = 1.0 + 2.0 ** -20
+    assert oracle.routing_certificate(x, W2, None, 1)["ok"][0]
+    assert {int(oracle.topk_select(np.array([[np.float32(_fp64_sum_in_order(W2[:, e], o)) for e in range(2)]],
+                                            dtype=np.float32), 1)[0, 0])
+            for o in itertools.permutations(range(3))} == {1}
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_certificate_is_sound_against_every_summation_order(seed):
+    """Tiny routers with planted near-ties: wherever the certificate accepts a
+    token, every ordering of every expert's additions (bias included) gives the
+    same fp32 top-k and slot order."""
+    rng = np.random.default_rng(seed)
+    T, d, E, k = 6, 4, 4, 2
+    x = np.float32(rng.normal(size=(T, d))).astype(np.float64)
+    W = np.float32(rng.normal(size=(d, E))).astype(np.float64)
+    W[:, 1] = W[:, 0] + np.float32(rng.normal(size=d) * 1e-7)   # experts 0 and 1 nearly tie
+    b = np.float32(rng.normal(size=E) * 0.1).astype(np.float64)
+    cert = oracle.routing_certificate(x, W, b, k)
+    orders = list(itertools.permutations(range(d + 1)))
+    for t in range(T):
+        seen = set()
+        for o in orders[::7]:
+            l32 = np.array([[np.float32(_fp64_sum_in_order(list(x[t] * W[:, e]) + [b[e]], o)) for e in range(E)]],
+                           dtype=np.float32)
+            seen.add(tuple(oracle.topk_select(l32, k)[0].tolist()))
+        if cert["ok"][t]:
+            assert len(seen) == 1, (t, seen)
+
+
+def test_selection_uses_fp32_logits_where_fp64_probabilities_merge():
+    """Logits more than ~745 below the maximum have fp64 probabilities that
+    underflow to 0, so ranking probabilities would tie experts 2 and 3 and
+    take the lower index.  The selection is made on the fp32 logits, which
+    stay distinct: expert 3 (-1000) comes before expert 2 (-1001).  The token
+    is certified: its logit gaps are exact and large."""
+    l = np.array([[0.0, 0.5, -1001.0, -1000.0]], dtype=np.float32)
+    p = oracle.softmax_rows(l)
+    assert p[0, 2] == p[0, 3] == 0.0
+    assert oracle.topk_select(l, 3)[0].tolist() == [1, 0, 3]
+    x = np.ones((1, 1))
+    assert oracle.routing_certificate(x, l.astype(np.float64), None, 3)["ok"][0]
+    w = oracle.routing_weights(p, oracle.topk_select(l, 3), True)
+    assert w[0, 2] == 0.0 and w[0].sum() == pytest.approx(1.0, rel=1e-15)
+    # an exact fp32 tie among the chosen experts is rejected (the tie order is a convention)
+    assert not oracle.routing_certificate(x, np.array([[0.0, 0.5, -1.0, -1.0]]), None, 3)["ok"][0]
+
+
 def test_workload_shapes_match_pages(golden_dir):
     rows = read_golden(golden_dir, "mixtral_shapes.txt")
     for name in ("mixtral_decode", "mixtral_decode_b8", "mixtral_prefill"):
@@ -369,7 +476,7 @@ def test_router_telemetry_closed_forms():
     # equal logits: every probability is 1/E and ties pick experts 0..k-1 for
     # every token, so routed = [T, T, 0, ...] and the loss is E * k * (1/E) = k
     l = np.zeros((T, E), dtype=np.float32)
-    idx = oracle.topk_select(oracle.softmax_rows(l), k)
+    idx = oracle.topk_select(l, k)
     r = oracle.router_telemetry(l, idx, E)
     assert r["routed"].tolist() == [T, T, 0, 0, 0, 0]
     np.testing.assert_allclose(r["prob_mean"], 1.0 / E, rtol=1e-15)
@@ -408,7 +515,7 @@ def test_router_telemetry_invariants():
     rng = np.random.default_rng(21)
     T, E, k = 37, 9, 3
     l = rng.normal(size=(T, E)).astype(np.float32)
-    idx = oracle.topk_select(oracle.softmax_rows(l), k)
+    idx = oracle.topk_select(l, k)
     r = oracle.router_telemetry(l, idx, E)
     assert math.fsum(r["prob_mean"]) == pytest.approx(1.0, rel=1e-14)
     assert r["routed"].sum() == T * k
@@ -690,7 +797,7 @@ def test_routing_weights_backward_against_differences(renorm):
     rng = np.random.default_rng(22)
     T, E, k = 5, 7, 3
     l = rng.normal(0, 1.5, (T, E))
-    idx = oracle.topk_select(oracle.softmax_rows(l), k)
+    idx = oracle.topk_select(l, k)
     g = rng.normal(0, 1, (T, k))
     dl = oracle.routing_weights_backward(oracle.softmax_rows(l), idx, g, renorm)
     fun = lambda: float((oracle.routing_weights(oracle.softmax_rows(l), idx, renorm) * g).sum())
