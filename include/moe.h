@@ -16,7 +16,8 @@
  *    never allocates device memory, never frees, and never synchronises the
  *    host: every call only enqueues kernels on `stream` and returns.  Scratch
  *    memory comes from the caller's workspace (`ws`, `ws_bytes`), sized by
- *    moe_workspace_size().  All buffers sized by routing use their worst case
+ *    moe_workspace_size() (moe_forward_noalloc uses a fixed per-GPU array of
+ *    the library instead).  All buffers sized by routing use their worst case
  *    (T*k rows), so no count is ever read back to the host; calls can be
  *    captured into a HIP graph.
  *  - Arrays are dense and row-major.  x is [T, d]; W_g is [d, E]; expert
@@ -233,6 +234,21 @@ moe_status moe_combine(const moe_desc* desc, const float* y_sorted, const int32_
  * fields are token-choice statistics and are declined (MOE_ERR_UNSUPPORTED). */
 moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, void* out,
                        moe_stats* stats, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, results and path choice as
+ * moe_forward; its scratch is a fixed array of MOE_NOALLOC_SCRATCH_BYTES
+ * inside the library, one copy per GPU, held until the process ends.  The
+ * first call on a device looks up that device's copy (with the device
+ * current).  Layers whose moe_workspace_size() exceeds the array return
+ * MOE_ERR_UNSUPPORTED and enqueue nothing.  Every call on one GPU uses the
+ * same array, which keeps the previous call's contents (none of which a call
+ * relies on): calls that overlap in time on one GPU, from different streams
+ * or threads, race and must be serialised by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+moe_status moe_forward_noalloc(const moe_desc* desc, const void* x, const moe_weights* w, void* out,
+                               moe_stats* stats, hipStream_t stream);
 
 /* Gradients produced by moe_backward (fp32, dense, row-major, caller-owned
  * device memory).  Every field below is fully written by each call. */

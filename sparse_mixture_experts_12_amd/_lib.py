@@ -23,7 +23,7 @@ _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "mxfp8": MOE_MXFP8
 
 # Every symbol the header declares.
 EXPORTS = ("moe_workspace_size", "moe_capacity", "moe_route", "moe_permute", "moe_grouped_ffn",
-           "moe_combine", "moe_forward", "moe_quantize_mxfp8", "moe_backward_workspace_size", "moe_backward",
+           "moe_combine", "moe_forward", "moe_forward_noalloc", "moe_quantize_mxfp8", "moe_backward_workspace_size", "moe_backward",
            "moe_status_string", "moe_last_error")
 
 
@@ -75,6 +75,7 @@ def _load():
         "moe_grouped_ffn": (ctypes.c_int, [DP, P, WP, P, P, P, P, S, P]),
         "moe_combine": (ctypes.c_int, [DP, P, P, P, P, P]),
         "moe_forward": (ctypes.c_int, [DP, P, WP, P, SP, P, S, P]),
+        "moe_forward_noalloc": (ctypes.c_int, [DP, P, WP, P, SP, P]),
         "moe_quantize_mxfp8": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, P, P, P]),
         "moe_backward_workspace_size": (S, [DP]),
         "moe_backward": (ctypes.c_int, [DP, P, WP, P, ctypes.POINTER(Grads), P, S, P]),
@@ -182,6 +183,17 @@ def forward(desc, x, weights: Weights, out, ws, stats: Stats | None = None, stre
     st = stats if stats is not None else Stats()
     _check(LIB.moe_forward(ctypes.byref(desc), _ptr(x), ctypes.byref(weights), _ptr(out), ctypes.byref(st),
                            _ptr(ws), ws.numel(), _stream(stream)), "moe_forward")
+    return st.path_taken
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20      # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def forward_noalloc(desc, x, weights: Weights, out, stats: Stats | None = None, stream=None) -> int:
+    """moe_forward_noalloc: the whole layer with the library's own per-GPU scratch."""
+    st = stats if stats is not None else Stats()
+    _check(LIB.moe_forward_noalloc(ctypes.byref(desc), _ptr(x), ctypes.byref(weights), _ptr(out),
+                                   ctypes.byref(st), _stream(stream)), "moe_forward_noalloc")
     return st.path_taken
 
 

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "kernels.h"
 
@@ -483,6 +485,52 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w
 }
 
 }  // extern "C"
+
+// Scratch of the allocation-free entry point: one copy per GPU, created with
+// the code object and held until the process ends.  Host code never passes
+// `scratch` itself to a kernel (in host code it names a host-side stand-in);
+// it uses the device address looked up per device below.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up on the first call made
+// with that device current.
+moe_status noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d outside 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    if (!ptr || ((uintptr_t)ptr & 255u)) return fail(MOE_ERR_HIP, "scratch address %p not 256-byte aligned", ptr);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" moe_status moe_forward_noalloc(const moe_desc* desc, const void* x, const moe_weights* w, void* out,
+                                          moe_stats* stats, hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const size_t need = layout_of(desc).total;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_UNSUPPORTED, "layer needs %zu bytes of scratch; the allocation-free entry point holds %zu",
+                need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(&ws)) != MOE_OK) return st;
+  return moe_forward(desc, x, w, out, stats, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
+}
 
 namespace {
 

@@ -225,3 +225,17 @@ def test_backward_validation(ops):
     w = ops.Weights(W_g=16, W_gate=16, W_up=16, W_down=16)
     r = ops.LIB.moe_backward(ctypes.byref(d), None, ctypes.byref(w), None, ctypes.byref(g), None, 0, None)
     assert r == ops.MOE_ERR_INVALID_ARG and "dWs_gate" in ops.last_error()
+
+
+def test_noalloc_declines_before_any_hip_call(ops):
+    """The allocation-free forward validates the descriptor and its scratch
+    need on the host first: a layer larger than the library's array is
+    declined with no device work (this runs without a GPU)."""
+    import ctypes
+    big = ops.make_desc(4096, 4096, 8, 2, 14336)
+    assert ops.workspace_size(big) > ops.NOALLOC_SCRATCH_BYTES
+    st = ops.LIB.moe_forward_noalloc(ctypes.byref(big), None, None, None, None, None)
+    assert st == ops.MOE_ERR_UNSUPPORTED
+    assert "scratch" in ops.last_error()
+    bad = ops.make_desc(4, 100, 8, 2, 64)                 # d not a multiple of 64
+    assert ops.LIB.moe_forward_noalloc(ctypes.byref(bad), None, None, None, None, None) == ops.MOE_ERR_INVALID_ARG
