@@ -50,6 +50,9 @@ def parse():
                          "load-balancing loss) inside the timed region")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the region that replays the layer from a captured HIP graph")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only --workload (a default run also times the other seeded workloads and reports "
+                         "them under the \"workloads\" key)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (for HBM counter scaling)")
     return ap.parse_args()
@@ -301,23 +304,16 @@ def cpu_baseline_backward(cfg, inp, dout, budget_s=12.0, max_calls=200):
                       f"(routing, fp64 expert and router gradients), {dt:.1f} s"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer would shard by tokens or by experts across GPUs)", file=sys.stderr)
-        sys.exit(2)
+def measure(args, cfg, steps=None, warmup=None, cpu=True, graph=True, copy_calibration=False):
+    """One workload: the timed regions below, returned as the JSON line's dict."""
     import torch
     import synth
     from sparse_mixture_experts_12_amd import _lib as ops
 
-    cfg = synth.CONFIGS[args.workload]
-    if args.backward:
-        return bench_backward(args, cfg)
     decode = cfg.T <= 8 and cfg.act == "bf16" and args.routing == "token"
-    steps = args.steps if args.steps is not None else (200 if decode else 20)
+    steps = steps if steps is not None else (200 if decode else 20)
     # a few ms of warm-up lets the clocks settle before the timed region
-    warmup = args.warmup if args.warmup is not None else 10
+    warmup = warmup if warmup is not None else 10
     print(f"[bench] workload={cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} f={cfg.f} "
           f"act={cfg.act} w={cfg.wdt} steps={steps} warmup={warmup}", file=sys.stderr, flush=True)
 
@@ -407,7 +403,7 @@ def main():
     # weight copy) and replayed, as a serving loop would run them: the per-step
     # cost without host-side launch work between the kernels.
     graph_ms = None
-    if not args.no_graph:
+    if graph:
         gstream = torch.cuda.Stream()
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
@@ -479,7 +475,7 @@ def main():
                 "mfma_frac": round(kflops / t / 1e12 / peak_f, 4) if have_k else None,
                 "hbm_frac": round(kbytes / t / 1e9 / HBM_PEAK_GBS, 4) if have_k else None}
 
-    if args.copy_calibration:
+    if copy_calibration:
         # a plain elementwise kernel of known traffic (256 MiB read, 256 MiB
         # written) whose HBM counters scale the layer kernels' counters
         a = torch.ones(1 << 27, dtype=torch.bfloat16, device="cuda")
@@ -487,10 +483,10 @@ def main():
         torch.neg(a, out=b)
         torch.cuda.synchronize()
 
-    cpu = None
-    if not args.no_cpu_baseline:
+    cpu_line = None
+    if cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg, inp)
+        cpu_line = cpu_baseline(cfg, inp)
 
     line = {
         "metric": "MoE-layer tokens/s; decode HBM GB/s, prefill MFMA TFLOP/s vs peak",
@@ -515,8 +511,52 @@ def main():
                   "graph_tokens_per_s": round(cfg.T / (graph_ms / 1e3), 2) if graph_ms else None,
                   "experts_empty": int(cfg.E - touched)},
         "roofline": roof,
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu_line,
     }
+    return line
+
+
+# Workloads timed after the headline in a default run, each with its own
+# warm-up and timed regions (no graph region, no CPU oracle): the prefill half
+# of the metric and the other seeded workloads.
+EXTRA_WORKLOADS = ("mixtral_prefill", "fine_grained", "fp8_capacity", "fp8_capacity_decode", "mixtral_decode_b8",
+                   "tiny_f32")
+
+
+def workload_row(line):
+    """The compact per-workload record carried under the headline line's "workloads" key."""
+    r, lay, c = line["roofline"], line["layer"], line["config"]
+    return {"T": c["T"], "ms_per_step": line["ms_per_step"], "tokens_per_s": line["value"],
+            "t_star_frac": lay["t_star_frac"], "path": c["path"], "experts_touched": c["experts_touched"],
+            "dropped_share": c["dropped_share"], "kernel": r["kernel"], "kernel_ms": r["kernel_ms"],
+            "bound": r["bound"], "achieved": r["achieved"], "unit": r["unit"], "frac": r["frac"],
+            "mfma_frac": r.get("mfma_frac"), "hbm_frac": r.get("hbm_frac"), "traffic": r["traffic"]}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer would shard by tokens or by experts across GPUs)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+
+    cfg = synth.CONFIGS[args.workload]
+    if args.backward:
+        return bench_backward(args, cfg)
+    line = measure(args, cfg, args.steps, args.warmup, cpu=not args.no_cpu_baseline, graph=not args.no_graph,
+                   copy_calibration=args.copy_calibration)
+    if not args.no_extra and args.routing == "token":
+        rows = {}
+        for name in EXTRA_WORKLOADS:
+            if name == args.workload:
+                continue
+            torch.cuda.empty_cache()
+            rows[name] = workload_row(measure(args, synth.CONFIGS[name], cpu=False, graph=False))
+            print(f"[bench] {name}: {rows[name]['ms_per_step']} ms/step, {rows[name]['kernel']} "
+                  f"{rows[name]['frac']} of its {rows[name]['bound']} roofline", file=sys.stderr, flush=True)
+        line["workloads"] = rows
     print(json.dumps(line), flush=True)
 
 
