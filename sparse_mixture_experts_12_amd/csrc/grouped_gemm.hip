@@ -663,14 +663,21 @@ int grouped_grid(int maxQ, int n_tiles) {
   return (int)(8 * per);
 }
 
+SchedSpec grouped_sched_spec(const GroupedArgs& a) {
+  const int BM = a.wkind == W_MX ? 256 : pick_bm(a);
+  return SchedSpec{a.sched, BM, a.has_shared ? a.T : 0, a.routed_rows,
+                   grouped_max_row_tiles(a.routed_rows, a.T, a.E, a.has_shared, BM)};
+}
+
 hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   if (a.wkind == W_MX) return launch_grouped_ffn_mx(a, s);
-  const int BM = pick_bm(a);
-  const int maxQ = grouped_max_row_tiles(a.routed_rows, a.T, a.E, a.has_shared, BM);
-  const int shared_rows = a.has_shared ? a.T : 0;
+  const SchedSpec sp = grouped_sched_spec(a);
+  const int maxQ = sp.maxQ;
   const int shared_row0 = a.routed_rows;
-  hipError_t err = launch_tile_schedule(a.offsets, a.E, BM, shared_rows, shared_row0, maxQ, a.sched, s);
-  if (err != hipSuccess) return err;
+  hipError_t err = hipSuccess;
+  if (!a.sched_ready &&
+      (err = launch_tile_schedule(a.offsets, a.E, sp.BM, sp.shared_rows, shared_row0, maxQ, a.sched, s)) != hipSuccess)
+    return err;
 
   if (a.act_f32) {
     GemmParamsF32 p{};

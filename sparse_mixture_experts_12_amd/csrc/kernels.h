@@ -27,12 +27,23 @@ struct RouteArgs {
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 size_t router_partial_bytes(int T, int d, int E);
 
+// Where and how to write the grouped GEMMs' tile schedule (see
+// tile_schedule_kernel); sched == nullptr: not requested.
+struct SchedSpec {
+  int32_t* sched;
+  int BM, shared_rows, shared_row0, maxQ;
+};
+
 struct PermuteArgs {
   const int32_t* idx;
   int n, E, cap;
-  int32_t *counts, *offsets, *sorted_assign, *inv_perm, *n_dropped, *rank_ws;
+  int32_t *counts, *offsets, *sorted_assign, *inv_perm, *n_dropped;
+  int32_t* rank_ws;                  // permute_ws_bytes(n, E) bytes of scratch
+  SchedSpec sched;                   // optional: also write the tile schedule
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+// rank_ws bytes launch_permute needs for n assignments over E experts
+size_t permute_ws_bytes(int n, int E);
 // Tile schedule header size (ints): [0] heavy row tiles, [1] light row tiles.
 constexpr int kSchedHead = 4;
 hipError_t launch_tile_schedule(const int32_t* offsets, int E, int BM, int shared_rows, int shared_row0, int maxQ,
@@ -68,6 +79,7 @@ struct GroupedArgs {
   float* y;                      // [routed_rows (+T), d] fp32
   void* h;                       // [routed_rows (+T), f] bf16 (or fp32 for act f32)
   int32_t* sched;                // schedule scratch
+  bool sched_ready;              // the schedule (grouped_sched_spec) was already written with the permutation
   float* y_part;                 // down light tiles' K parts 1.. (grouped_down_part_bytes)
   uint8_t* mx_xq;                // W_MX: x codes [T, d] (scratch)
   uint8_t* mx_xs;                // W_MX: x scales [T, d/32]
@@ -75,6 +87,8 @@ struct GroupedArgs {
   hipEvent_t ev_begin, ev_end;
 };
 size_t grouped_sched_ints(int routed_rows, int T, int E, int has_shared);
+// The schedule launch_grouped_ffn builds for a (its tile height and list size).
+SchedSpec grouped_sched_spec(const GroupedArgs& a);
 int grouped_max_row_tiles(int routed_rows, int T, int E, int has_shared, int BM);
 int grouped_grid(int maxQ, int n_tiles);
 hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s);

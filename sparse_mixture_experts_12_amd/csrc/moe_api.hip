@@ -185,7 +185,7 @@ Layout layout_of(const moe_desc* d) {
   L.sorted = take(T * k * 4);
   L.inv = take(T * k * 4);
   L.ndrop = take(4);
-  L.rank = take(T * k * 4);
+  L.rank = take(permute_ws_bytes(d->T * d->top_k, d->E));
   L.sched = take(grouped_sched_ints((int)routed, d->T, d->E, d->has_shared) * 4);
   const bool mx = d->w_dtype == MOE_MXFP8;
   L.h = take(rows * d->f * (mx ? 1 : d->act_dtype == MOE_F32 ? 4 : 2));   // MXFP8: H codes
@@ -254,17 +254,17 @@ moe_status do_route(const moe_desc* d, const void* x, const moe_weights* w, int3
 }
 
 moe_status do_permute(const moe_desc* d, const int32_t* idx, int32_t* counts, int32_t* offsets, int32_t* sorted,
-                      int32_t* inv, int32_t* ndrop, int32_t* rank, hipStream_t s) {
+                      int32_t* inv, int32_t* ndrop, int32_t* rank, hipStream_t s, SchedSpec sched = SchedSpec{}) {
   PermuteArgs a{};
   a.idx = idx; a.n = d->T * d->top_k; a.E = d->E; a.cap = capacity_of(d);
   a.counts = counts; a.offsets = offsets; a.sorted_assign = sorted; a.inv_perm = inv; a.n_dropped = ndrop;
   a.rank_ws = rank;
+  a.sched = sched;
   return hip_status(launch_permute(a, s), "permute");
 }
 
-moe_status do_grouped(const moe_desc* d, const void* x, const moe_weights* w, const int32_t* sorted,
-                      const int32_t* offsets, float* y, char* ws, const Layout& L, hipEvent_t eb, hipEvent_t ee,
-                      hipStream_t s) {
+GroupedArgs grouped_args(const moe_desc* d, const void* x, const moe_weights* w, const int32_t* sorted,
+                         const int32_t* offsets, float* y, char* ws, const Layout& L, hipEvent_t eb, hipEvent_t ee) {
   GroupedArgs a{};
   a.x = x; a.sorted_assign = sorted; a.offsets = offsets; a.w = expert_weights(w);
   a.T = d->T; a.d = d->d; a.E = d->E; a.k = d->top_k; a.f = d->f; a.has_shared = d->has_shared;
@@ -286,6 +286,14 @@ moe_status do_grouped(const moe_desc* d, const void* x, const moe_weights* w, co
   a.sched = (int32_t*)(ws + L.sched);
   a.y_part = (float*)(ws + L.ypart);
   a.ev_begin = eb; a.ev_end = ee;
+  return a;
+}
+
+moe_status do_grouped(const moe_desc* d, const void* x, const moe_weights* w, const int32_t* sorted,
+                      const int32_t* offsets, float* y, char* ws, const Layout& L, hipEvent_t eb, hipEvent_t ee,
+                      hipStream_t s, bool sched_ready = false) {
+  GroupedArgs a = grouped_args(d, x, w, sorted, offsets, y, ws, L, eb, ee);
+  a.sched_ready = sched_ready;
   return hip_status(launch_grouped_ffn(a, s), "grouped_ffn");
 }
 
@@ -477,10 +485,13 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w
   int32_t* offsets = (int32_t*)(base + L.offsets);
   int32_t* sorted = (int32_t*)(base + L.sorted);
   int32_t* inv = (int32_t*)(base + L.inv);
-  if ((st = do_permute(desc, idx, counts, offsets, sorted, inv, nd, (int32_t*)(base + L.rank), stream)) != MOE_OK)
-    return st;
   float* y = (float*)(base + L.y);
-  if ((st = do_grouped(desc, x, w, sorted, offsets, y, base, L, eb, ee, stream)) != MOE_OK) return st;
+  // the permutation also writes the grouped GEMMs' tile schedule (one launch fewer)
+  const SchedSpec sched = grouped_sched_spec(grouped_args(desc, x, w, sorted, offsets, y, base, L, eb, ee));
+  if ((st = do_permute(desc, idx, counts, offsets, sorted, inv, nd, (int32_t*)(base + L.rank), stream, sched)) !=
+      MOE_OK)
+    return st;
+  if ((st = do_grouped(desc, x, w, sorted, offsets, y, base, L, eb, ee, stream, true)) != MOE_OK) return st;
   return do_combine(desc, y, inv, tw, out, stream);
 }
 
@@ -571,7 +582,7 @@ BwdLayout bwd_layout_of(const moe_desc* d) {
   L.sorted = take(T * k * 4);
   L.inv = take(T * k * 4);
   L.ndrop = take(4);
-  L.rank = take(T * k * 4);
+  L.rank = take(permute_ws_bytes(d->T * d->top_k, d->E));
   L.poff = take((Gn + 1) * 4);
   L.ptok = take(P * 4);
   L.pw = take(P * 4);

@@ -487,10 +487,13 @@ hipError_t launch_grouped_ffn_mx(const GroupedArgs& a, hipStream_t s) {
   uint8_t* xs = a.mx_xs;
   uint8_t* hq = (uint8_t*)a.h;
   uint8_t* hs = a.mx_hs;
-  const int BM = 256;
-  const int maxQ = grouped_max_row_tiles(a.routed_rows, a.T, a.E, a.has_shared, BM);
-  hipError_t err = launch_tile_schedule(a.offsets, a.E, BM, a.has_shared ? a.T : 0, a.routed_rows, maxQ, a.sched, s);
-  if (err != hipSuccess) return err;
+  const SchedSpec sp = grouped_sched_spec(a);
+  const int BM = sp.BM;
+  const int maxQ = sp.maxQ;
+  hipError_t err = hipSuccess;
+  if (!a.sched_ready &&
+      (err = launch_tile_schedule(a.offsets, a.E, BM, sp.shared_rows, a.routed_rows, maxQ, a.sched, s)) != hipSuccess)
+    return err;
   if ((err = launch_mx_quantize(a.x, a.act_f32, a.T, a.d, xq, xs, s)) != hipSuccess) return err;
 
   MxParams p{};

@@ -477,21 +477,40 @@ __global__ __launch_bounds__(256) void topk_finalize_kernel(const double* __rest
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wv;
   if (t >= T) return;     // whole wave leaves together; no block barrier follows
-  for (int e = lane; e < E; e += 64) {
-    double s = 0.0;
-    int z = 0;
-    for (; z + 8 <= S; z += 8) {               // eight independent loads in flight, added in slice order
-      double v[8];
+  // the slices of up to two experts per lane are loaded together (one memory
+  // round trip for S <= 32, padding loads repeat a valid address) and added
+  // in slice order
+  constexpr int ZB = 32;
+  for (int e0 = lane; e0 < E; e0 += 128) {
+    const int e1 = e0 + 64;
+    const int e1c = e1 < E ? e1 : e0;
+    double s0 = 0.0, s1 = 0.0;
+    for (int z = 0; z < S; z += ZB) {
+      double v0[ZB], v1[ZB];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = part[((size_t)(z + i) * T + t) * E + e];
+      for (int i = 0; i < ZB; ++i) {
+        const size_t row = ((size_t)min(z + i, S - 1) * T + t) * E;
+        v0[i] = part[row + e0];
+        v1[i] = part[row + e1c];
+      }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s += v[i];
+      for (int i = 0; i < ZB; ++i)
+        if (z + i < S) {
+          s0 += v0[i];
+          s1 += v1[i];
+        }
     }
-    for (; z < S; ++z) s += part[((size_t)z * T + t) * E + e];
-    if (bias) s += (double)bias[e];
-    const float l = (float)s;
-    lg[wv][e] = l;
-    if (logits) logits[(size_t)t * E + e] = l;
+    if (bias) {
+      s0 += (double)bias[e0];
+      s1 += (double)bias[e1c];
+    }
+    const float l0 = (float)s0, l1 = (float)s1;
+    lg[wv][e0] = l0;
+    if (logits) logits[(size_t)t * E + e0] = l0;
+    if (e1 < E) {
+      lg[wv][e1] = l1;
+      if (logits) logits[(size_t)t * E + e1] = l1;
+    }
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_s_waitcnt(0);

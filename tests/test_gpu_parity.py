@@ -196,10 +196,18 @@ def test_permute_worked_example():
     assert r["offsets"].tolist() == [0, 4, 8, 8]
 
 
+# T*k up to 4096 runs the single-work-group permutation, beyond it the
+# multi-block one (4097, 16385: a one-assignment last block), which sums the
+# block counts inside its scatter launch up to 64 blocks (65536 assignments)
+# and in a launch of its own beyond; 2^21 x 8 = 2^24 is the largest T*k the
+# library accepts.
 @pytest.mark.parametrize("T,k,E,cf,skew", [
     (1, 2, 8, 0.0, 0), (64, 2, 8, 0.0, 0), (4096, 2, 8, 0.0, 0), (2048, 8, 256, 0.0, 1),
     (512, 8, 128, 1.25, 1), (1, 8, 128, 1.25, 0), (333, 3, 7, 1.0, 1), (1000, 1, 1, 0.0, 0),
-    (700, 4, 1023, 0.0, 0), (129, 2, 64, 0.3, 1), (2049, 8, 256, 1.0, 2)])
+    (700, 4, 1023, 0.0, 0), (129, 2, 64, 0.3, 1), (2049, 8, 256, 1.0, 2),
+    (4096, 1, 4, 0.0, 0), (4097, 1, 5, 0.0, 0), (16385, 1, 5, 0.0, 0), (5000, 4, 1023, 0.7, 1),
+    (32768, 2, 3, 0.8, 1), (32769, 2, 3, 0.8, 1),
+    (2 ** 21, 8, 256, 1.25, 1)])
 def test_permute_parity(T, k, E, cf, skew):
     print(f"[permute] T={T} k={k} E={E} cf={cf} skew={skew}", flush=True)
     rng = np.random.default_rng(T * 7 + E)
@@ -208,7 +216,10 @@ def test_permute_parity(T, k, E, cf, skew):
     else:
         p = 1.0 / np.arange(1, E + 1) ** (1.1 * skew)
         p /= p.sum()
-    idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    if T * k <= 100000:
+        idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    else:       # large: experts drawn independently per slot (repeats inside a token are fine here)
+        idx = rng.choice(E, size=(T, k), p=p).astype(np.int32)
     _check_perm(idx, E, cf)
 
 
