@@ -191,7 +191,7 @@ __device__ void wave_topk(const float* lg /* logits of the token, any memory */,
 }
 
 // ---------------------------------------------------------------------------
-// Small-T router (T <= 8) in one work-group of 1024 threads: logits for every
+// Small-T router (T <= 8) in one work-group of 512 threads: logits for every
 // token, top-k, and the decode plan used by the fused decode path:
 //   plan[0]            n_used: number of distinct experts with a kept assignment
 //   plan[1 .. E]       used expert ids, ascending (first n_used valid)
@@ -200,9 +200,11 @@ __device__ void wave_topk(const float* lg /* logits of the token, any memory */,
 // Each thread owns one chunk of 8 experts and a strided set of rows of W_g
 // (one 16-byte load per row for bf16), all issued before use; per-thread fp64
 // sums are combined by a fixed butterfly inside the wave and a fixed-order sum
-// over the 16 waves.  Top-k is rank based: every lane counts the logits that
-// precede its own (larger, or equal with a lower index), so no serial
-// cross-lane selection loop is needed.
+// over the waves.  When W_g is large, the same kernel first runs as S
+// work-groups that each write one slice of rows' fp64 partial logits, and the
+// one-work-group call adds the S slices in slice order.  Top-k is rank based:
+// every logit's rank is the count of logits that precede it (larger, or equal
+// with a lower index), so no serial cross-lane selection loop is needed.
 // ---------------------------------------------------------------------------
 constexpr int kSmallThreads = 512;
 constexpr int kSmallWaves = kSmallThreads / 64;
@@ -242,13 +244,24 @@ __device__ void wave_topk_rank_sl(const float* lg, int E, int k, int renormalize
     v[i] = (lane + 64 * i < E) ? lg[lane + 64 * i] : -INFINITY;
     rank[i] = 0;
   }
-  for (int e2 = 0; e2 < E; ++e2) {
-    const float u = lg[e2];
-    m = fmaxf(m, u);
+  // slots start at a valid expert (a NaN logit compares with nothing)
+  if (lane < k) sel[lane] = 0;
+  // every other logit comes from a register of the wave (readlane) rather
+  // than from LDS, which would cost one LDS round trip per compared logit.
+  // Padding slots hold -inf at indexes >= E and never precede a real expert.
 #pragma unroll
-    for (int i = 0; i < SL; ++i) {
-      const int e = lane + 64 * i;
-      rank[i] += (u > v[i] || (u == v[i] && e2 < e)) ? 1 : 0;
+  for (int i2 = 0; i2 < SL; ++i2) {
+    if (64 * i2 >= E) break;
+#pragma unroll
+    for (int l = 0; l < 64; ++l) {
+      const int e2 = 64 * i2 + l;
+      const float u = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i2]), l));
+      m = fmaxf(m, u);
+#pragma unroll
+      for (int i = 0; i < SL; ++i) {
+        const int e = lane + 64 * i;
+        rank[i] += (u > v[i] || (u == v[i] && e2 < e)) ? 1 : 0;
+      }
     }
   }
   double p[SL];
@@ -287,15 +300,24 @@ template <typename TIn, int MT>
 __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
     const TIn* __restrict__ x, const TIn* __restrict__ W, const float* __restrict__ bias, int T, int d,
     int E, int k, int renormalize, int cap, float* __restrict__ logits_out, int32_t* __restrict__ idx_out,
-    float* __restrict__ w_out, int32_t* __restrict__ plan, const double* __restrict__ part, int S) {
+    float* __restrict__ w_out, int32_t* __restrict__ plan, const double* __restrict__ part, int S,
+    double* __restrict__ part_out, int dsplit) {
   __shared__ double wpart[kSmallThreads][8];
   __shared__ float lg[MT * 1024];
   __shared__ int32_t sidx[MT * 32];
   __shared__ double ps[MT][256];
+  __shared__ double psel[MT][32];
   __shared__ int32_t flag[1024];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  // slots start at a valid expert, so a logit that compares with nothing
+  // (NaN) cannot leave an index for the plan to follow
+  for (int a = tid; a < T * k; a += kSmallThreads) sidx[a] = 0;
   const bool vec_ok = (E % 8) == 0;    // rows of W_g are 16-byte aligned only then
+  // split mode (part_out set): work-group z sums rows z * dsplit .. + dsplit - 1
+  // of x W_g in fp64 and writes them as slice z's partial logits, nothing else
+  const int r_lo = part_out ? (int)blockIdx.x * dsplit : 0;
+  const int r_hi = part_out ? min(d, r_lo + dsplit) : d;
   if (part) {
     // wide routers: the S fp64 partial sums over slices of d (split-K kernel)
     // are added in slice order
@@ -336,12 +358,12 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
       // and contribute zero, so all loads of a batch are in flight together.
       const int ecl = min(ec, nchunk - 1);
       const TIn* wbase = W + e0 + ecl * 8;
-      for (int r0 = rg; r0 < d; r0 += RB * RG) {
+      for (int r0 = r_lo + rg; r0 < r_hi; r0 += RB * RG) {
         uint4 raw[RB][sizeof(TIn) == 2 ? 1 : 2];
         TIn xr[RB][MT];
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
-          const int rc = min(r0 + b * RG, d - 1);
+          const int rc = min(r0 + b * RG, r_hi - 1);
           const uint4* src = reinterpret_cast<const uint4*>(wbase + (size_t)rc * E);
           raw[b][0] = src[0];
           if (sizeof(TIn) == 4) raw[b][sizeof(TIn) == 2 ? 0 : 1] = src[1];
@@ -350,7 +372,7 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
         }
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
-          const bool live = (r0 + b * RG) < d;
+          const bool live = (r0 + b * RG) < r_hi;
           double wv[8];
           if (sizeof(TIn) == 2) {
             const uint32_t q[4] = {raw[b][0].x, raw[b][0].y, raw[b][0].z, raw[b][0].w};
@@ -376,7 +398,7 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
       }
     } else if (nvalid > 0) {
       // E not a multiple of 8: element loads (rare shapes, not latency tuned)
-      for (int r = rg; r < d; r += RG) {
+      for (int r = r_lo + rg; r < r_hi; r += RG) {
         double wv[8];
         load8<TIn>(W, (size_t)r * E + e0 + ec * 8, nvalid, false, wv);
 #pragma unroll
@@ -410,7 +432,9 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
         for (int r = l; r < RG; r += L) sum += wpart[r * ecp + oc][oj];
       }
       for (int off = 1; off < L; off <<= 1) sum += __shfl_xor(sum, off);
-      if (o < nout && l == 0 && oc * 8 + oj < ne) {
+      if (o < nout && l == 0 && oc * 8 + oj < ne && part_out) {
+        part_out[((size_t)blockIdx.x * T + t) * E + e0 + oc * 8 + oj] = sum;
+      } else if (o < nout && l == 0 && oc * 8 + oj < ne) {
         const int e = e0 + oc * 8 + oj;
         if (bias) sum += (double)bias[e];
         const float lv = (float)sum;
@@ -420,13 +444,60 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
       __syncthreads();
     }
   }
-  // top-k: wave w handles token w
-  if (wave < T) {
-    if (E <= 256)
-      wave_topk_rank(lg + wave * 1024, E, k, renormalize, sidx + wave * k, ps[wave], idx_out + (size_t)wave * k,
-                     w_out + (size_t)wave * k);
-    else
-      wave_topk(lg + wave * 1024, E, k, renormalize, sidx + wave * k, w_out + (size_t)wave * k);
+  if (part_out) return;
+  if (E <= 256) {
+    // Rank-based top-k over the whole work-group: R adjacent lanes share one
+    // (token, expert) logit, each counts the logits that precede it (larger,
+    // or equal with a lower index) over a contiguous 1/R of the token's
+    // experts and takes their maximum; a butterfly over the R lanes adds the
+    // counts and the maxima.  One wave per token left the other waves idle
+    // and made this the router's longest step at T = 1, E = 128.
+    int R = 1;
+    while (R < 64 && 2 * R * T * E <= kSmallThreads && 16 * R <= E) R <<= 1;
+    const int chunk = (E + R - 1) / R;
+    for (int i0 = tid; i0 < T * E * R; i0 += kSmallThreads) {
+      const int item = i0 / R, q = i0 - item * R;
+      const int t = item / E, e = item - t * E;
+      const float* l = lg + t * 1024;
+      const float v = l[e];
+      const int lo = q * chunk, hi = min(E, lo + chunk);
+      int r = 0;
+      float m = -INFINITY;
+#pragma unroll 8
+      for (int e2 = lo; e2 < hi; ++e2) {
+        const float u = l[e2];
+        m = fmaxf(m, u);
+        r += (u > v || (u == v && e2 < e)) ? 1 : 0;
+      }
+      for (int off = 1; off < R; off <<= 1) {   // the R lanes of an item are active together
+        r += __shfl_xor(r, off);
+        m = fmaxf(m, __shfl_xor(m, off));
+      }
+      if (q == 0) {
+        const double pv = exp((double)v - (double)m);
+        if (r < k) {
+          sidx[t * k + r] = e;
+          psel[t][r] = pv;
+        }
+        if (!renormalize) ps[t][e] = pv;
+      }
+    }
+    __syncthreads();
+    // weights: the chosen experts (slot order) or all experts (index order)
+    // form the denominator
+    for (int a = tid; a < T * k; a += kSmallThreads) {
+      const int t = a / k, j = a - t * k;
+      double den = 0.0;
+      if (renormalize) {
+        for (int q = 0; q < k; ++q) den += psel[t][q];
+      } else {
+        for (int q = 0; q < E; ++q) den += ps[t][q];
+      }
+      idx_out[a] = sidx[a];
+      w_out[a] = (float)(psel[t][j] / den);
+    }
+  } else if (wave < T) {
+    wave_topk(lg + wave * 1024, E, k, renormalize, sidx + wave * k, w_out + (size_t)wave * k);
   }
   __syncthreads();
   const int n = T * k;
@@ -543,20 +614,25 @@ static void router_split(int T, int d, int E, int* S, int* dsplit) {
 // takes longer than spreading the dot products over split-K work-groups.
 static bool small_t_split(int d, int E) { return (long)d * E > 65536; }
 
-// Small T: at most kSmallMaxS slices (the top-k kernel adds them with all
-// loads in flight).
-static void router_split_any(int T, int d, int E, int* S, int* dsplit) {
-  router_split(T, d, E, S, dsplit);
-  if (T <= kDecodeMaxT && *S > kSmallMaxS) {
-    *dsplit = ((d + kSmallMaxS - 1) / kSmallMaxS + 15) / 16 * 16;
-    *S = (d + *dsplit - 1) / *dsplit;
-  }
+// Small T, split: slices of at least 64 rows and about 16 K weights of W_g
+// each (one batch of loads per thread of the 512-thread work-group), at most
+// kSmallMaxS slices (the top-k kernel adds them with all loads in flight).
+static void router_split_small(int d, int E, int* S, int* dsplit) {
+  int ds = 16384 / (E > 0 ? E : 1);
+  ds = ds < 64 ? 64 : ds;
+  if ((d + ds - 1) / ds > kSmallMaxS) ds = (d + kSmallMaxS - 1) / kSmallMaxS;
+  *dsplit = (ds + 15) / 16 * 16;
+  *S = (d + *dsplit - 1) / *dsplit;
 }
 
 size_t router_partial_bytes(int T, int d, int E) {
-  if (T <= kDecodeMaxT && !small_t_split(d, E)) return 0;
   int S, ds;
-  router_split_any(T, d, E, &S, &ds);
+  if (T <= kDecodeMaxT) {
+    if (!small_t_split(d, E)) return 0;
+    router_split_small(d, E, &S, &ds);
+  } else {
+    router_split(T, d, E, &S, &ds);
+  }
   return (size_t)S * T * E * sizeof(double);
 }
 
@@ -575,17 +651,21 @@ static hipError_t launch_partials(const void* x, const void* W, double* part, in
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.T <= kDecodeMaxT) {
     const int mt = a.T <= 1 ? 1 : a.T <= 2 ? 2 : a.T <= 4 ? 4 : 8;
+    // split: S work-groups write the slices' partial logits, then one
+    // work-group adds them and selects
     int S = 0, ds = 0;
-    if (a.part && small_t_split(a.d, a.E)) {
-      router_split_any(a.T, a.d, a.E, &S, &ds);
-      hipError_t err = a.act_f32 ? launch_partials<float>(a.x, a.W_g, a.part, a.T, a.d, a.E, S, ds, s)
-                                 : launch_partials<bf16_t>(a.x, a.W_g, a.part, a.T, a.d, a.E, S, ds, s);
-      if (err != hipSuccess) return err;
-    }
+    if (a.part && small_t_split(a.d, a.E)) router_split_small(a.d, a.E, &S, &ds);
     const double* part = S ? a.part : nullptr;
-#define MOE_ROUTE_SMALL(TY, MTV)                                                                          \
-  route_small_kernel<TY, MTV><<<1, kSmallThreads, 0, s>>>((const TY*)a.x, (const TY*)a.W_g, a.bias, a.T, a.d, a.E, a.k, \
-                                                a.renormalize, a.cap, a.logits, a.idx, a.w, a.plan, part, S)
+#define MOE_ROUTE_SMALL(TY, MTV)                                                                               \
+  do {                                                                                                         \
+    if (S)                                                                                                     \
+      route_small_kernel<TY, MTV><<<S, kSmallThreads, 0, s>>>((const TY*)a.x, (const TY*)a.W_g, nullptr, a.T,  \
+                                                              a.d, a.E, a.k, a.renormalize, a.cap, nullptr,    \
+                                                              nullptr, nullptr, nullptr, nullptr, 0, a.part, ds); \
+    route_small_kernel<TY, MTV><<<1, kSmallThreads, 0, s>>>((const TY*)a.x, (const TY*)a.W_g, a.bias, a.T, a.d,  \
+                                                            a.E, a.k, a.renormalize, a.cap, a.logits, a.idx, a.w,  \
+                                                            a.plan, part, S, nullptr, 0);                     \
+  } while (0)
     if (a.act_f32) {
       if (mt == 1) MOE_ROUTE_SMALL(float, 1); else if (mt == 2) MOE_ROUTE_SMALL(float, 2);
       else if (mt == 4) MOE_ROUTE_SMALL(float, 4); else MOE_ROUTE_SMALL(float, 8);
