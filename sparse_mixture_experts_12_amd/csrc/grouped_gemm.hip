@@ -33,6 +33,7 @@
 // Work-group ids are remapped so that consecutive tiles (same weight column
 // tile, neighbouring row tiles of one expert) run on the same XCD and share
 // its L2.
+#include <atomic>
 #include <hip/hip_ext.h>
 
 #include <type_traits>
@@ -574,6 +575,30 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
 constexpr int kDlBK = 64;
 constexpr int kDlNST = 2;
 
+static int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0, c = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if ((c = cached[dev].load(std::memory_order_relaxed)) > 0) return c;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) return 256;
+  cached[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
+// 64-row fp8 tiles: three LDS stages (72 KB) fit two work-groups per CU, two
+// stages (48 KB) fit three.  The tiles (at most one per group and column
+// tile) are equal, so the depth whose work-group slots they fill best (fewest
+// idle slots in the last round) is taken; three stages on a tie.
+static bool small_f8_two_stages(int n_wg) {
+  const long cus = device_cus();
+  auto fill = [&](int per_cu) {
+    const long slots = cus * per_cu;
+    const long rounds = (n_wg + slots - 1) / slots;
+    return (double)n_wg / (double)(rounds * slots);
+  };
+  return fill(3) > fill(2);
+}
+
 // The down GEMM's light tiles (an expert's last <= 128 rows) run after all of
 // its heavy tiles.  When there are few of them (groups x column tiles <= 256,
 // e.g. 8 Mixtral experts x 16) that launch leaves most CUs idle for a whole
@@ -741,11 +766,14 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   const bool small_f8 = a.wkind == W_FP8 && a.max_group_rows <= 64;
   if (small_f8) {
     const int gl = grouped_grid(groups, (a.f + 127) / 128);
-    if (a.ev_begin || a.ev_end)
-      hipExtLaunchKernelGGL(gemm_dl_kernel<true, 64, kDlBK, 3, 2, true>, dim3(gl), dim3(256), 0, s, a.ev_begin,
-                            a.ev_end, 0, p);
-    else
-      gemm_dl_kernel<true, 64, kDlBK, 3, 2, true><<<gl, 256, 0, s>>>(p);
+    auto gu = [&](auto kern) {
+      if (a.ev_begin || a.ev_end)
+        hipExtLaunchKernelGGL(kern, dim3(gl), dim3(256), 0, s, a.ev_begin, a.ev_end, 0, p);
+      else
+        kern<<<gl, 256, 0, s>>>(p);
+    };
+    if (small_f8_two_stages(groups * ((a.f + 127) / 128))) gu(gemm_dl_kernel<true, 64, kDlBK, 2, 2, true>);
+    else gu(gemm_dl_kernel<true, 64, kDlBK, 3, 2, true>);
   } else if (a.wkind == W_FP8) {
     launch_split(gemm_dl_kernel<true, 256, kDlBK, kDlNST, 1, true>, gemm_dl_kernel<true, 128, kDlBK, 3, 2, true>, p,
                  (a.f + 127) / 128, a.ev_begin, a.ev_end);
@@ -766,7 +794,9 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   q.part_slots = groups * dn_tiles;
   q.y_part = a.y_part;
   if (small_f8) {
-    gemm_dl_kernel<false, 64, kDlBK, 3, 2, true><<<grouped_grid(groups, dn_tiles), 256, 0, s>>>(q);
+    const int gd = grouped_grid(groups, dn_tiles);
+    if (small_f8_two_stages(groups * dn_tiles)) gemm_dl_kernel<false, 64, kDlBK, 2, 2, true><<<gd, 256, 0, s>>>(q);
+    else gemm_dl_kernel<false, 64, kDlBK, 3, 2, true><<<gd, 256, 0, s>>>(q);
   } else if (a.wkind == W_FP8) {
     launch_split(gemm_dl_kernel<false, 256, kDlBK, kDlNST, 1, true>, gemm_dl_kernel<false, 128, kDlBK, 3, 2, true>, q,
                  dn_tiles, nullptr, nullptr, q.ksplit);
