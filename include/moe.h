@@ -30,6 +30,12 @@
  *  - Results are bitwise deterministic run to run: no floating-point atomics.
  *  - Calls on the same stream are ordered; calls that share a workspace must
  *    not run concurrently on different streams.
+ *  - Layers of 64 or more expert groups (experts + shared) run part of the
+ *    grouped GEMMs on a second stream that the library creates once per host
+ *    thread and GPU (default priority, kept until the process ends); it
+ *    joins back into `stream` through events before the call's next kernel,
+ *    so ordering, graph capture and determinism are as for one stream.
+ *    moe_forward_noalloc keeps every launch on `stream`.
  *
  * Conventions fixed here where the pages are silent:
  *  - Router logits are rounded to fp32 once from an fp64 sum (+ bias), and

@@ -575,6 +575,35 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
 constexpr int kDlBK = 64;
 constexpr int kDlNST = 2;
 
+// Groups (experts + shared) from which the heavy and light launches of a
+// grouped GEMM run on two streams.
+constexpr int kConcurrentMinGroups = 64;
+
+// A second stream and its fork / join events, created at the first use by a
+// host thread on a device and kept until the process ends (default priority).
+// nullptr if they cannot be created: the launches then stay on one stream.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool bad = false;
+};
+static SideStream* side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  thread_local SideStream ss[64];
+  SideStream& r = ss[dev];
+  if (r.bad) return nullptr;
+  if (!r.s) {
+    if (hipStreamCreateWithFlags(&r.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&r.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&r.join, hipEventDisableTiming) != hipSuccess) {
+      r.bad = true;
+      return nullptr;
+    }
+  }
+  return &r;
+}
+
 static int device_cus() {
   static std::atomic<int> cached[64];
   int dev = 0, c = 0;
@@ -745,12 +774,33 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   p.h_out = (bf16_t*)a.h;
   p.ksplit = 1;
   // heavy tiles, then light tiles with their own kernel shape; the events
-  // (when requested) span both launches
+  // (when requested) span both launches.  Layers of many small experts run
+  // the two launches on two streams (fork / join through events): the light
+  // launch streams the small experts' weights while the heavy launch's last
+  // round of tiles would otherwise leave most CUs idle.  With few experts the
+  // light tiles re-read the heavy experts' weights and running them alongside
+  // slowed the heavy launch, so those stay in order on one stream.
   const int groups = a.E + (a.has_shared ? 1 : 0);
+  SideStream* side = (a.concurrent && groups >= kConcurrentMinGroups) ? side_stream() : nullptr;
+  hipError_t ferr = hipSuccess;
+  auto chk = [&](hipError_t e) { if (ferr == hipSuccess) ferr = e; };
   auto launch_split = [&](auto heavy, auto light, const GemmParams& prm, int n_tiles, hipEvent_t eb, hipEvent_t ee,
                           int kparts = 1) {
     const int gh = grouped_grid(maxQ, n_tiles);
     const dim3 gl(grouped_grid(groups, n_tiles), kparts);
+    if (side) {
+      chk(hipEventRecord(side->fork, s));
+      chk(hipStreamWaitEvent(side->s, side->fork, 0));
+      if (eb) hipExtLaunchKernelGGL(heavy, dim3(gh), dim3(256), 0, s, eb, nullptr, 0, prm);
+      else heavy<<<gh, 256, 0, s>>>(prm);
+      chk(hipGetLastError());
+      light<<<gl, 256, 0, side->s>>>(prm);
+      chk(hipGetLastError());
+      chk(hipEventRecord(side->join, side->s));
+      chk(hipStreamWaitEvent(s, side->join, 0));
+      if (ee) chk(hipEventRecord(ee, s));
+      return;
+    }
     if (eb || ee) {
       hipExtLaunchKernelGGL(heavy, dim3(gh), dim3(256), 0, s, eb, nullptr, 0, prm);
       hipExtLaunchKernelGGL(light, gl, dim3(256), 0, s, nullptr, ee, 0, prm);
@@ -782,6 +832,7 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
                  (a.f + 127) / 128, a.ev_begin, a.ev_end);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (ferr != hipSuccess) return ferr;
 
   GemmParams q = p;
   q.a_rows = (const bf16_t*)a.h;
@@ -805,6 +856,7 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
                  dn_tiles, nullptr, nullptr, q.ksplit);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (ferr != hipSuccess) return ferr;
   if (q.ksplit > 1)
     return launch_down_split_reduce(a.sched, maxQ, a.E, dn_tiles, a.d, q.ksplit, q.part_slots, a.y_part, a.y, s);
   return hipGetLastError();

@@ -85,6 +85,7 @@ struct GroupedArgs {
   uint8_t* mx_xs;                // W_MX: x scales [T, d/32]
   uint8_t* mx_hs;                // W_MX: H scales [rows, f/32]; h holds the H codes
   hipEvent_t ev_begin, ev_end;
+  bool concurrent;               // may run heavy and light launches on a second stream (fork / join)
 };
 size_t grouped_sched_ints(int routed_rows, int T, int E, int has_shared);
 // The schedule launch_grouped_ffn builds for a (its tile height and list size).

@@ -289,11 +289,16 @@ GroupedArgs grouped_args(const moe_desc* d, const void* x, const moe_weights* w,
   return a;
 }
 
+// Set while moe_forward_noalloc runs: every launch stays on the caller's
+// stream (no second stream or events are created on its behalf).
+thread_local bool t_one_stream = false;
+
 moe_status do_grouped(const moe_desc* d, const void* x, const moe_weights* w, const int32_t* sorted,
                       const int32_t* offsets, float* y, char* ws, const Layout& L, hipEvent_t eb, hipEvent_t ee,
                       hipStream_t s, bool sched_ready = false) {
   GroupedArgs a = grouped_args(d, x, w, sorted, offsets, y, ws, L, eb, ee);
   a.sched_ready = sched_ready;
+  a.concurrent = !t_one_stream;
   return hip_status(launch_grouped_ffn(a, s), "grouped_ffn");
 }
 
@@ -540,7 +545,10 @@ extern "C" moe_status moe_forward_noalloc(const moe_desc* desc, const void* x, c
                 need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
   void* ws = nullptr;
   if ((st = noalloc_scratch(&ws)) != MOE_OK) return st;
-  return moe_forward(desc, x, w, out, stats, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
+  t_one_stream = true;
+  st = moe_forward(desc, x, w, out, stats, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
+  t_one_stream = false;
+  return st;
 }
 
 namespace {
