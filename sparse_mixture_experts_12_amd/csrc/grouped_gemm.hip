@@ -575,19 +575,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
 constexpr int kDlBK = 64;
 constexpr int kDlNST = 2;
 
-// Groups (experts + shared) from which the heavy and light launches of a
-// grouped GEMM run on two streams.
-constexpr int kConcurrentMinGroups = 64;
-
-// A second stream and its fork / join events, created at the first use by a
-// host thread on a device and kept until the process ends (default priority).
-// nullptr if they cannot be created: the launches then stay on one stream.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool bad = false;
-};
-static SideStream* side_stream() {
+SideStream* side_stream() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
   thread_local SideStream ss[64];

@@ -87,6 +87,18 @@ struct GroupedArgs {
   hipEvent_t ev_begin, ev_end;
   bool concurrent;               // may run heavy and light launches on a second stream (fork / join)
 };
+// Groups (experts + shared) from which the heavy and light launches of a
+// grouped GEMM run on two streams.
+constexpr int kConcurrentMinGroups = 64;
+// A second stream and its fork / join events, created at the first use by a
+// host thread on a device and kept until the process ends (default priority).
+// nullptr if they cannot be created: the launches then stay on one stream.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool bad = false;
+};
+SideStream* side_stream();
 size_t grouped_sched_ints(int routed_rows, int T, int E, int has_shared);
 // The schedule launch_grouped_ffn builds for a (its tile height and list size).
 SchedSpec grouped_sched_spec(const GroupedArgs& a);

@@ -507,12 +507,30 @@ hipError_t launch_grouped_ffn_mx(const GroupedArgs& a, hipStream_t s) {
   p.k = a.assign_div; p.E = a.E; p.K = a.d; p.N = a.f; p.shared_row0 = a.routed_rows;
   p.hq_out = hq; p.hs_out = hs;
   p.ksplit = 1;
-  // heavy tiles, then light tiles; the events (when requested) span both
+  // heavy tiles, then light tiles; the events (when requested) span both.
+  // Layers of many small experts fork the light launch onto a second stream
+  // (as the bf16 / fp8 grouped GEMMs do).
   const int groups = a.E + (a.has_shared ? 1 : 0);
+  SideStream* side = (a.concurrent && groups >= kConcurrentMinGroups) ? side_stream() : nullptr;
+  hipError_t ferr = hipSuccess;
+  auto chk = [&](hipError_t e) { if (ferr == hipSuccess) ferr = e; };
   auto launch_split = [&](auto heavy, auto light, const MxParams& prm, int n_tiles, hipEvent_t eb, hipEvent_t ee,
                           int kparts = 1) {
     const int gh = grouped_grid(maxQ, n_tiles);
     const dim3 gl(grouped_grid(groups, n_tiles), kparts);
+    if (side) {
+      chk(hipEventRecord(side->fork, s));
+      chk(hipStreamWaitEvent(side->s, side->fork, 0));
+      if (eb) hipExtLaunchKernelGGL(heavy, dim3(gh), dim3(256), 0, s, eb, nullptr, 0, prm);
+      else heavy<<<gh, 256, 0, s>>>(prm);
+      chk(hipGetLastError());
+      light<<<gl, 256, 0, side->s>>>(prm);
+      chk(hipGetLastError());
+      chk(hipEventRecord(side->join, side->s));
+      chk(hipStreamWaitEvent(s, side->join, 0));
+      if (ee) chk(hipEventRecord(ee, s));
+      return;
+    }
     if (eb || ee) {
       hipExtLaunchKernelGGL(heavy, dim3(gh), dim3(256), 0, s, eb, nullptr, 0, prm);
       hipExtLaunchKernelGGL(light, dim3(gl), dim3(256), 0, s, nullptr, ee, 0, prm);
@@ -523,6 +541,7 @@ hipError_t launch_grouped_ffn_mx(const GroupedArgs& a, hipStream_t s) {
   };
   launch_split(gemm_mx_kernel<true, 1>, gemm_mx_kernel<true, 2>, p, a.f / 128, a.ev_begin, a.ev_end);
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (ferr != hipSuccess) return ferr;
 
   MxParams q{};
   q.aq = hq; q.as = hs;
@@ -537,6 +556,7 @@ hipError_t launch_grouped_ffn_mx(const GroupedArgs& a, hipStream_t s) {
   q.y_part = a.y_part;
   launch_split(gemm_mx_kernel<false, 1>, gemm_mx_kernel<false, 2>, q, dn_tiles, nullptr, nullptr, q.ksplit);
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (ferr != hipSuccess) return ferr;
   if (q.ksplit > 1)
     return launch_down_split_reduce(a.sched, maxQ, a.E, dn_tiles, a.d, q.ksplit, q.part_slots, a.y_part, a.y, s);
   return hipSuccess;

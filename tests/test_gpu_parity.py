@@ -65,6 +65,8 @@ SMALL = {
                                                      seed=23),
     "mx_T1": C["mixtral_prefill_mxfp8"].with_(T=1, d=256, f=256, seed=24),
     "mx_long_k": C["mixtral_prefill_mxfp8"].with_(T=70, d=2048, f=1280, E=4, k=1, seed=25),
+    # 97 expert groups: the light launches run on the library's second stream
+    "mx_many_experts": C["fine_grained_mxfp8"].with_(T=64, d=256, E=96, k=4, f=256, seed=27),
 }
 
 
@@ -343,9 +345,11 @@ def test_bitwise_deterministic(name):
                        b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
 
 
-# bf16_E1023_shared: 1024 expert groups, so the grouped GEMMs' light launches
-# run on the library's second stream (fork / join captured into the graph)
-@pytest.mark.parametrize("name", ["bf16_prefill_ragged", "decode_T1", "mx_ragged", "bf16_E1023_shared"])
+# bf16_E1023_shared, mx_many_experts: 64 or more expert groups, so the grouped
+# GEMMs' light launches run on the library's second stream (fork / join
+# captured into the graph)
+@pytest.mark.parametrize("name", ["bf16_prefill_ragged", "decode_T1", "mx_ragged", "bf16_E1023_shared",
+                                  "mx_many_experts"])
 def test_hip_graph_capture_replay(name):
     cfg = SMALL[name]
     inp = device_inputs(cfg)
