@@ -591,17 +591,29 @@ hipError_t launch_bwd_rows(int mode, const BwdGemmParams& p, hipStream_t s) {
   const int gh = grouped_grid(p.maxQ, n_tiles);   // heavy tiles, then light tiles
   const int ks = mode == MODE_GU ? 1 : (p.ksplit > 1 ? p.ksplit : 1);
   const dim3 gl(grouped_grid(p.G, n_tiles), ks);
+  // many expert groups: the light launch on the second stream, joined back
+  // before anything that reads its rows (as in the forward's grouped GEMMs)
+  SideStream* side = p.G >= kConcurrentMinGroups ? side_stream() : nullptr;
+  const hipStream_t sl = side ? side->s : s;
+  hipError_t e = hipSuccess;
+  if (side) {
+    if ((e = hipEventRecord(side->fork, s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(sl, side->fork, 0)) != hipSuccess) return e;
+  }
   if (mode == MODE_GU) {
     bwd_rows_kernel<MODE_GU, 1><<<gh, 256, 0, s>>>(p);
-    bwd_rows_kernel<MODE_GU, 2><<<gl, 256, 0, s>>>(p);
+    bwd_rows_kernel<MODE_GU, 2><<<gl, 256, 0, sl>>>(p);
   } else if (mode == MODE_NTS) {
     bwd_rows_kernel<MODE_NTS, 1><<<gh, 256, 0, s>>>(p);
-    bwd_rows_kernel<MODE_NTS, 2><<<gl, 256, 0, s>>>(p);
+    bwd_rows_kernel<MODE_NTS, 2><<<gl, 256, 0, sl>>>(p);
   } else {
     bwd_rows_kernel<MODE_NT, 1><<<gh, 256, 0, s>>>(p);
-    bwd_rows_kernel<MODE_NT, 2><<<gl, 256, 0, s>>>(p);
+    bwd_rows_kernel<MODE_NT, 2><<<gl, 256, 0, sl>>>(p);
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
+  if (side && e == hipSuccess) {
+    if ((e = hipEventRecord(side->join, sl)) == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
+  }
   if (e != hipSuccess || ks == 1) return e;
   return launch_down_split_reduce(p.sched, p.maxQ, p.G, n_tiles, p.N, ks, p.part_slots, p.part, p.C0, s);
 }
