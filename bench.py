@@ -187,8 +187,9 @@ def cpu_baseline(cfg, inp, budget_s=12.0, max_calls=2000):
 
 def bench_backward(args, cfg):
     """moe_backward on the workload: whole-call throughput (tokens/s), the dX
-    GEMM (the largest row-tile GEMM, 4 rows d f flops) against the bf16 MFMA
-    roofline, and the oracle's backward on a small token sample."""
+    GEMM (the largest row-tile GEMM, 4 rows d f flops) against the roofline its
+    arithmetic intensity reaches first (bf16 MFMA, or HBM for small experts),
+    and the oracle's backward on a small token sample."""
     import numpy as np
     import torch
     import synth
@@ -215,7 +216,9 @@ def bench_backward(args, cfg):
     fws = ops.alloc_workspace(desc)
     ops.forward(desc, inp["x"], w, out, fws, stats=ops.Stats(d_counts=counts.data_ptr()))
     torch.cuda.synchronize()
-    rows = int(counts.sum()) + (cfg.T if cfg.shared else 0)
+    cnt = counts.cpu().numpy()
+    rows = int(cnt.sum()) + (cfg.T if cfg.shared else 0)
+    n_exp = int((cnt > 0).sum()) + (1 if cfg.shared else 0)
     del fws
     for _ in range(warmup):
         ops.backward(desc, inp["x"], w, dout, gs, ws)
@@ -241,12 +244,24 @@ def bench_backward(args, cfg):
         kern_ms = sum(hev.elapsed_ms(eb[i], ee[i]) for i in range(steps)) / steps
     have_k = kern_ms == kern_ms
     kflops = 4 * rows * cfg.d * cfg.f                   # dX = [dG | dU] [W_gate | W_up]^T
+    # its bytes: the touched experts' W_gate and W_up (bf16), dG and dU (bf16),
+    # dX rows written in fp32; the bound is whichever roofline the arithmetic
+    # intensity reaches first, as for the forward's gate/up GEMM
+    kbytes = n_exp * 2 * cfg.d * cfg.f * 2 + rows * 2 * cfg.f * 2 + rows * cfg.d * 4
     flops = 16 * rows * cfg.d * cfg.f + 4 * cfg.T * cfg.d * cfg.E
-    roof = {"bound": "mfma", "achieved": round(kflops / (kern_ms / 1e3) / 1e12, 2) if have_k else None,
-            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(kflops / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4) if have_k else None,
+    t = kern_ms / 1e3 if have_k else None
+    if kflops / kbytes >= BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        bound, peak, unit = "mfma", BF16_PEAK_TFLOPS, "TFLOP/s"
+        achieved = kflops / t / 1e12 if have_k else None
+    else:
+        bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
+        achieved = kbytes / t / 1e9 if have_k else None
+    roof = {"bound": bound, "achieved": round(achieved, 2) if have_k else None, "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4) if have_k else None,
             "traffic": measured_traffic("bwd_dx_gemm", cfg.name), "kernel": "bwd_rows_kernel<NTS> (dX)",
-            "kernel_ms": round(kern_ms, 5) if have_k else None, "alg_flops": int(kflops)}
+            "kernel_ms": round(kern_ms, 5) if have_k else None, "alg_flops": int(kflops), "alg_bytes": int(kbytes),
+            "mfma_frac": round(kflops / t / 1e12 / BF16_PEAK_TFLOPS, 4) if have_k else None,
+            "hbm_frac": round(kbytes / t / 1e9 / HBM_PEAK_GBS, 4) if have_k else None}
     if args.copy_calibration:     # the plain copy kernel whose counters scale the GEMM's (see main)
         a = torch.ones(1 << 27, dtype=torch.bfloat16, device="cuda")
         b = torch.empty_like(a)
