@@ -436,12 +436,15 @@ __global__ __launch_bounds__(256, TileCfg<BMMAX>::OCC) void gemm_dl_kernel(GemmP
   } else if constexpr (BMMAX >= 256) {
     if (rows > 128) dl_tile<DUAL, 256, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
     else if (rows > 64) dl_tile<DUAL, 128, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
-    else dl_tile<DUAL, 64, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
+    else if (rows > 32) dl_tile<DUAL, 64, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
+    else dl_tile<DUAL, 32, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
   } else if constexpr (BMMAX >= 128) {
     if (rows > 64) dl_tile<DUAL, 128, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
-    else dl_tile<DUAL, 64, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
+    else if (rows > 32) dl_tile<DUAL, 64, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
+    else dl_tile<DUAL, 32, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
   } else {
-    dl_tile<DUAL, BMMAX, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
+    if (rows > 32) dl_tile<DUAL, BMMAX, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
+    else dl_tile<DUAL, 32, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
   }
 }
 
