@@ -126,6 +126,47 @@ def test_route_parity(name):
         np.testing.assert_allclose(w.cpu().numpy().astype(np.float64).sum(1), 1.0, atol=1e-6)
 
 
+# Exactly tied logits: odd expert columns of W_g copy the even ones, so every
+# expert ties with its neighbour (identical fp64 sums in every path).  The
+# selection must put the lower index first (the fixed tie rule), in each top-k
+# path: the small-T block ranks (whole W_g or split into slices), the wave
+# selection for E > 256, and the large-T wave ranks.
+TIE_CASES = {
+    "small_split_E128": C["fp8_capacity_decode"].with_(T=3),
+    "small_whole_E64": C["mixtral_decode"].with_(T=2, d=256, E=64, k=6, seed=31),
+    "small_split_E600": C["mixtral_decode"].with_(T=3, d=128, E=600, k=16, seed=32),
+    "large_E128": C["mixtral_prefill"].with_(T=40, d=256, E=128, k=8, seed=33),
+    "large_E600_renorm_off": C["mixtral_prefill"].with_(T=40, d=128, E=600, k=16, renormalize=False, seed=34),
+}
+
+
+@pytest.mark.parametrize("name", list(TIE_CASES))
+def test_route_exact_ties(name):
+    cfg = TIE_CASES[name]
+    print(f"[route-ties] {name}", flush=True)
+    inp = device_inputs(cfg, router_only=True)
+    inp["W_g"][:, 1::2] = inp["W_g"][:, 0::2]
+    desc = ops.desc_from_cfg(cfg)
+    T, k, E = cfg.T, cfg.k, cfg.E
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ops.route(desc, inp["x"], ops.weights_struct(inp), idx, w, logits, ops.alloc_workspace(desc))
+    torch.cuda.synchronize()
+    g_logits = logits.cpu().numpy()
+    assert np.array_equal(g_logits[:, 1::2], g_logits[:, 0::2]), "tied columns gave different logits"
+    ov = OracleInputs(inp)
+    ref_logits = oracle.router_logits(ov.x, ov.W_g, ov.bias)
+    ulps = np.abs(g_logits.view(np.int32).astype(np.int64) - ref_logits.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1
+    # the selection on the GPU's own logits: ties broken by the lower index
+    gi = idx.cpu().numpy()
+    np.testing.assert_array_equal(gi, oracle.topk_select(g_logits, k))
+    assert (gi[:, 0] % 2 == 0).all()                     # the first of a tied pair is the even expert
+    ref_w = oracle.routing_weights(oracle.softmax_rows(g_logits.astype(np.float64)), gi, cfg.renormalize)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=1e-6, atol=0)
+
+
 def test_small_t_route_without_workspace():
     """A wide router (d * E > 65536) at T <= 8 splits its logits over d when
     given the workspace and runs one work-group without it: same results."""
