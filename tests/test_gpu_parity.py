@@ -423,7 +423,7 @@ FULL = ["tiny_f32", "mixtral_decode", "mixtral_decode_b8", "mixtral_prefill", "f
         "fp8_capacity", "fp8_capacity_decode", "mixtral_prefill_mxfp8", "fine_grained_mxfp8"]
 SAMPLE = {"mixtral_prefill": 12, "fine_grained": 3, "fp8_capacity": 24, "mixtral_prefill_mxfp8": 12,
           "fine_grained_mxfp8": 3}
-TILE = 64          # the smallest row-tile height any grouped GEMM body uses
+TILE = 32          # the smallest row-tile height any grouped GEMM body uses
 
 
 def _edge_tokens(offsets, sorted_assign, k, E):
