@@ -32,7 +32,11 @@
 //
 // Work-group ids are remapped so that consecutive tiles (same weight column
 // tile, neighbouring row tiles of one expert) run on the same XCD and share
-// its L2.
+// its L2.  Each GEMM is two launches, full-height ("heavy") tiles and each
+// expert's small last ("light") tile, whose body matches its rows (256, 128,
+// 64 or 32); with 64 or more expert groups the light launch runs on a second
+// stream beside the heavy one.  fp8 layers whose groups all fit 64 rows run
+// one 64-row launch per GEMM.
 #include <atomic>
 #include <hip/hip_ext.h>
 
