@@ -55,6 +55,10 @@ def parse():
                          "them under the \"workloads\" key)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (for HBM counter scaling)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="instead of the layer, time torch.mm (hipBLASLt) on the workload's per-expert gate/up "
+                         "and down GEMM shapes with balanced routing: the vendor library's rate on this part, "
+                         "for the MFMA roofline's context")
     return ap.parse_args()
 
 
@@ -281,6 +285,56 @@ def bench_backward(args, cfg):
                    "f": cfg.f, "shared_expert": cfg.shared, "capacity_factor": cfg.capacity_factor},
         "layer": {"alg_flops": int(flops), "tflops": round(flops / (ms / 1e3) / 1e12, 2)},
         "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+
+
+def bench_library_gemm(args, cfg):
+    """torch.mm (hipBLASLt) on the layer's GEMM shapes: per expert M = T k / E
+    rows (balanced routing), gate/up as one [M, d] x [d, 2 f] product, down as
+    [M, f] x [f, d]; E products per step, bf16 in, bf16 out.  Context for the
+    grouped GEMMs' MFMA fraction, not a layer measurement."""
+    import torch
+    if cfg.wdt != "bf16" or cfg.act != "bf16":
+        print("--library-gemm takes bf16 layers", file=sys.stderr)
+        sys.exit(2)
+    steps = args.steps if args.steps is not None else 10
+    warmup = args.warmup if args.warmup is not None else 3
+    M = cfg.T * cfg.k // cfg.E
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    shapes = {"gate_up": (M, cfg.d, 2 * cfg.f), "down": (M, cfg.f, cfg.d)}
+    out = {}
+    for name, (m, kk, n) in shapes.items():
+        A = [torch.randn((m, kk), generator=gen, device="cuda").to(torch.bfloat16) for _ in range(cfg.E)]
+        B = [(torch.randn((kk, n), generator=gen, device="cuda") * 0.02).to(torch.bfloat16) for _ in range(cfg.E)]
+        C = [torch.empty((m, n), dtype=torch.bfloat16, device="cuda") for _ in range(cfg.E)]
+
+        def step():
+            for e in range(cfg.E):
+                torch.mm(A[e], B[e], out=C[e])
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            step()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        flops = 2.0 * cfg.E * m * kk * n
+        tf = flops / (ms / 1e3) / 1e12
+        out[name] = {"M": m, "K": kk, "N": n, "products": cfg.E, "ms": round(ms, 5), "tflops": round(tf, 1),
+                     "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+        print(f"[bench] library GEMM {name}: {cfg.E} x [{m}x{kk}] x [{kk}x{n}] {ms:.4f} ms, {tf:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        del A, B, C
+        torch.cuda.empty_cache()
+    line = {"metric": "library bf16 GEMM TFLOP/s (torch.mm on hipBLASLt) at the layer's per-expert GEMM shapes",
+            "value": out["gate_up"]["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "higher_is_better": True, "dtype": "bf16", "data": "synthetic (seeded N(0,1) rows, N(0,0.02) weights)",
+            "config": {"workload": cfg.name, "rows_per_expert": M, "experts": cfg.E}, "gemms": out,
+            "peak": BF16_PEAK_TFLOPS}
     print(json.dumps(line), flush=True)
 
 
@@ -558,6 +612,8 @@ def main():
     import synth
 
     cfg = synth.CONFIGS[args.workload]
+    if args.library_gemm:
+        return bench_library_gemm(args, cfg)
     if args.backward:
         return bench_backward(args, cfg)
     line = measure(args, cfg, args.steps, args.warmup, cpu=not args.no_cpu_baseline, graph=not args.no_graph,
