@@ -593,7 +593,7 @@ hipError_t launch_bwd_rows(int mode, const BwdGemmParams& p, hipStream_t s) {
   const dim3 gl(grouped_grid(p.G, n_tiles), ks);
   // many expert groups: the light launch on the second stream, joined back
   // before anything that reads its rows (as in the forward's grouped GEMMs)
-  SideStream* side = p.G >= kConcurrentMinGroups ? side_stream() : nullptr;
+  SideStream* side = p.G >= kConcurrentMinGroups ? side_stream(s) : nullptr;
   const hipStream_t sl = side ? side->s : s;
   hipError_t e = hipSuccess;
   if (side) {

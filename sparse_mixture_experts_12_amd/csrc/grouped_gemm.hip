@@ -582,13 +582,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
 constexpr int kDlBK = 64;
 constexpr int kDlNST = 2;
 
-SideStream* side_stream() {
+SideStream* side_stream(hipStream_t caller) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
   thread_local SideStream ss[64];
   SideStream& r = ss[dev];
   if (r.bad) return nullptr;
   if (!r.s) {
+    // creating a stream or an event while a graph is being captured is not
+    // allowed (and may end the capture): such a call stays on one stream
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(caller, &st) != hipSuccess || st != hipStreamCaptureStatusNone) return nullptr;
     if (hipStreamCreateWithFlags(&r.s, hipStreamNonBlocking) != hipSuccess ||
         hipEventCreateWithFlags(&r.fork, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&r.join, hipEventDisableTiming) != hipSuccess) {
@@ -776,7 +780,7 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   // light tiles re-read the heavy experts' weights and running them alongside
   // slowed the heavy launch, so those stay in order on one stream.
   const int groups = a.E + (a.has_shared ? 1 : 0);
-  SideStream* side = (a.concurrent && groups >= kConcurrentMinGroups) ? side_stream() : nullptr;
+  SideStream* side = (a.concurrent && groups >= kConcurrentMinGroups) ? side_stream(s) : nullptr;
   hipError_t ferr = hipSuccess;
   auto chk = [&](hipError_t e) { if (ferr == hipSuccess) ferr = e; };
   auto launch_split = [&](auto heavy, auto light, const GemmParams& prm, int n_tiles, hipEvent_t eb, hipEvent_t ee,

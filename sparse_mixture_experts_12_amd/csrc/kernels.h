@@ -92,13 +92,14 @@ struct GroupedArgs {
 constexpr int kConcurrentMinGroups = 64;
 // A second stream and its fork / join events, created at the first use by a
 // host thread on a device and kept until the process ends (default priority).
-// nullptr if they cannot be created: the launches then stay on one stream.
+// nullptr if they cannot be created, or if that first use comes while
+// `caller` is capturing a graph: the launches then stay on one stream.
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
   bool bad = false;
 };
-SideStream* side_stream();
+SideStream* side_stream(hipStream_t caller);
 size_t grouped_sched_ints(int routed_rows, int T, int E, int has_shared);
 // The schedule launch_grouped_ffn builds for a (its tile height and list size).
 SchedSpec grouped_sched_spec(const GroupedArgs& a);

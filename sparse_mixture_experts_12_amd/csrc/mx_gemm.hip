@@ -511,7 +511,7 @@ hipError_t launch_grouped_ffn_mx(const GroupedArgs& a, hipStream_t s) {
   // Layers of many small experts fork the light launch onto a second stream
   // (as the bf16 / fp8 grouped GEMMs do).
   const int groups = a.E + (a.has_shared ? 1 : 0);
-  SideStream* side = (a.concurrent && groups >= kConcurrentMinGroups) ? side_stream() : nullptr;
+  SideStream* side = (a.concurrent && groups >= kConcurrentMinGroups) ? side_stream(s) : nullptr;
   hipError_t ferr = hipSuccess;
   auto chk = [&](hipError_t e) { if (ferr == hipSuccess) ferr = e; };
   auto launch_split = [&](auto heavy, auto light, const MxParams& prm, int n_tiles, hipEvent_t eb, hipEvent_t ee,

@@ -413,6 +413,42 @@ def test_hip_graph_capture_replay(name):
         del junk
 
 
+def test_graph_capture_first_call_of_a_thread():
+    """A many-group layer whose first call in a host thread is made under graph
+    capture: the library creates no stream or event during the capture (it
+    keeps that call on the capturing stream) and the replays match eager."""
+    import threading
+    cfg = SMALL["bf16_E1023_shared"]
+    inp = device_inputs(cfg)
+    eager, _ = run_forward(inp)
+    desc = ops.desc_from_cfg(cfg)
+    ws = ops.alloc_workspace(desc)
+    out = torch.zeros_like(eager)
+    w = ops.weights_struct(inp)
+    box = {}
+
+    def capture():
+        try:
+            s = torch.cuda.Stream()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                ops.forward(desc, inp["x"], w, out, ws)
+            box["g"] = g
+        except Exception as e:                              # reported in the main thread
+            box["err"] = e
+
+    th = threading.Thread(target=capture)
+    th.start()
+    th.join()
+    assert "err" not in box, box.get("err")
+    for rep in range(3):
+        out.zero_()
+        box["g"].replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}"
+
+
 # ---------------------------------------------------------------------------
 # Whole layer at the workloads' full sizes: routing and permutation on every
 # token; outputs on sampled tokens plus, for every non-empty expert, the tokens
