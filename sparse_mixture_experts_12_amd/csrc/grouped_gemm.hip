@@ -787,9 +787,10 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
                           int kparts = 1) {
     const int gh = grouped_grid(maxQ, n_tiles);
     const dim3 gl(grouped_grid(groups, n_tiles), kparts);
-    if (side) {
-      chk(hipEventRecord(side->fork, s));
-      chk(hipStreamWaitEvent(side->s, side->fork, 0));
+    hipError_t fe = side ? hipEventRecord(side->fork, s) : hipErrorInvalidValue;
+    if (fe == hipSuccess) fe = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (side && fe != hipSuccess) chk(fe);      // no fork: both launches stay on `s`, in order
+    if (side && fe == hipSuccess) {
       if (eb) hipExtLaunchKernelGGL(heavy, dim3(gh), dim3(256), 0, s, eb, nullptr, 0, prm);
       else heavy<<<gh, 256, 0, s>>>(prm);
       chk(hipGetLastError());
