@@ -601,3 +601,70 @@ def mx_roundtrip(v, as_fp32: bool = False) -> np.ndarray:
     if as_fp32:
         v = v.astype(np.float32).astype(np.float64)
     return mx_dequantize(*mx_quantize(v))
+
+
+# ----------------------------------------------------------------------------
+# MXFP4 block scaling (OCP Microscaling): E2M1 elements -- a sign, two exponent
+# bits (bias 1) and one mantissa bit, i.e. 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
+# negatives -- with the same E8M0 scale per 32 values as MXFP8 and the same
+# rule for it: s = floor(log2 max|v|) - emax, emax = 2 for E2M1.  The pages
+# show the 4-bit block-scaled idea only as NVFP4 on another chip ("Current Bug:
+# CuTeDSLMoERunner produces wrong output", Root Cause); here it is the expert
+# weights' format, with the activations in MXFP8.
+# ----------------------------------------------------------------------------
+E2M1_MAX = 6.0
+E2M1_EMAX = 2               # 6 = 1.5 * 2^2
+
+
+def _e2m1_value(c: int) -> float:
+    sign = -1.0 if c & 8 else 1.0
+    e, m = (c >> 1) & 3, c & 1
+    mag = 0.5 * m if e == 0 else (1.0 + 0.5 * m) * 2.0 ** (e - 1)   # e = 0: subnormal, m / 2
+    return sign * mag
+
+
+_E2M1_VALUES = np.array([_e2m1_value(c) for c in range(16)], dtype=np.float64)
+_E2M1_POS_VALS = _E2M1_VALUES[:8]          # codes 0..7: +0 .. +6, rising with the code
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """Values of E2M1 codes (the low four bits of each byte)."""
+    return _E2M1_VALUES[np.asarray(codes, dtype=np.uint8) & 0x0F]
+
+
+def e2m1_encode(v) -> np.ndarray:
+    """Nearest E2M1 value, ties to the even code; magnitudes beyond 6 saturate
+    to 6; the sign bit is the input's (a negative value that rounds to zero
+    gives -0, code 8).  One code (0..15) per byte."""
+    v = _f64(v)
+    a = np.minimum(np.abs(v), E2M1_MAX)
+    i = np.clip(np.searchsorted(_E2M1_POS_VALS, a, side="left"), 1, len(_E2M1_POS_VALS) - 1)
+    lo, hi = _E2M1_POS_VALS[i - 1], _E2M1_POS_VALS[i]
+    d_lo, d_hi = a - lo, hi - a
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (i % 2 == 0)), i, i - 1)
+    code = np.where(a == 0.0, 0, code).astype(np.uint8)
+    return (code | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
+
+
+def mx4_quantize(v, block: int = MX_BLOCK):
+    """Per block of `block` consecutive values along the last axis: shared
+    exponent s = floor(log2(max |v|)) - 2, clamped to [-127, 127] (an all-zero
+    block takes -127); elements = e2m1_encode(v / 2^s).  Returns (codes uint8,
+    one E2M1 code per byte, scales uint8 with code s + 127)."""
+    v = _f64(v)
+    K = v.shape[-1]
+    assert K % block == 0
+    b = v.reshape(-1, K // block, block)
+    amax = np.abs(b).max(axis=2)
+    e = np.full(amax.shape, -127, dtype=np.int64)
+    nz = amax > 0
+    e[nz] = np.frexp(amax[nz])[1] - 1 - E2M1_EMAX
+    e = np.clip(e, -127, 127)
+    codes = e2m1_encode(b / np.exp2(e.astype(np.float64))[:, :, None])
+    return codes.reshape(v.shape), (e + 127).astype(np.uint8).reshape(v.shape[:-1] + (K // block,))
+
+
+def mx4_dequantize(codes, scales, block: int = MX_BLOCK) -> np.ndarray:
+    """codes: one E2M1 code per byte (as mx4_quantize returns them)."""
+    s = np.asarray(scales, dtype=np.uint8).astype(np.float64)
+    return e2m1_decode(codes) * np.repeat(np.exp2(s - 127.0), block, axis=-1)

@@ -720,6 +720,88 @@ def test_mx_dequantize_values():
         assert got[0, 0] == f and got[0, 1] == -f and got[0, 2] == 2.0 ** -9 * f and np.all(got[0, 3:] == 0)
 
 
+# --------------------------------------------------------------------------
+# MXFP4 block scaling (E2M1 elements, the same power-of-two scale per 32 values)
+# --------------------------------------------------------------------------
+# The OCP E2M1 element values written out (sign-magnitude, codes 0..7 and 8..15)
+_E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _brute_e2m1(v):
+    """Nearest E2M1 magnitude by exhaustive search in exact rationals, ties to
+    the even code; magnitude clamped to 6 first, sign carried as bit 3."""
+    a = min(abs(Fraction(v)), Fraction(6))
+    best = min(range(8), key=lambda c: (abs(a - Fraction(_E2M1_TABLE[c])), c & 1))
+    return best | (8 if math.copysign(1.0, v) < 0 else 0)
+
+
+def test_e2m1_decode_table():
+    got = oracle.e2m1_decode(np.arange(16, dtype=np.uint8))
+    want = np.array(_E2M1_TABLE + [-t for t in _E2M1_TABLE])
+    assert np.array_equal(got, want) and np.signbit(got[8])        # code 8 is -0
+    assert np.array_equal(oracle.e2m1_decode(np.array([0x17, 0xF2], dtype=np.uint8)), [6.0, 1.0])   # low nibble
+
+
+def test_e2m1_encode_roundtrip_ties_and_saturation():
+    codes = np.arange(16, dtype=np.uint8)
+    assert np.array_equal(oracle.e2m1_encode(oracle.e2m1_decode(codes)), codes)
+    # every midpoint goes to the even code: 0|0.5 -> 0, 0.5|1 -> 1, 1|1.5 -> 1, 1.5|2 -> 2, 2|3 -> 2, 3|4 -> 4, 4|6 -> 4
+    for v, c in [(0.25, 0), (0.75, 2), (1.25, 2), (1.75, 4), (2.5, 4), (3.5, 6), (5.0, 6),
+                 (6.0, 7), (7.99, 7), (1e30, 7), (-1e30, 15), (-0.1, 8), (-0.0, 8), (0.0, 0), (0.2500001, 1)]:
+        assert oracle.e2m1_encode(np.array([v]))[0] == c, v
+        assert _brute_e2m1(v) == c, v
+
+
+def test_e2m1_encode_brute_force():
+    rng = np.random.default_rng(17)
+    v = np.concatenate([rng.normal(0, 2, 400), rng.integers(-28, 28, 200) / 4.0])   # many exact ties
+    got = oracle.e2m1_encode(v)
+    ref = np.array([_brute_e2m1(float(t)) for t in v], dtype=np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def test_mx4_scale_rule_zero_block_and_block_maximum():
+    codes, sc = oracle.mx4_quantize(np.zeros((2, 64)))
+    assert np.all(codes == 0) and np.all(sc == 0)
+    for p in (-130, -100, -3, 0, 5, 100):
+        b = np.zeros(32)
+        b[3] = -(2.0 ** p)
+        codes, sc = oracle.mx4_quantize(b[None, :])
+        assert sc[0, 0] == max(p - 2, -127) + 127
+        if p - 2 >= -127:
+            assert codes[0, 3] == 8 | 6                 # -4 = -(2^2): the scaled maximum of a power of two
+    rng = np.random.default_rng(18)
+    v = rng.normal(0, 1, (40, 32)) * np.exp2(rng.integers(-60, 60, (40, 1)))
+    _, sc = oracle.mx4_quantize(v)
+    r = np.abs(v).max(axis=1) / np.exp2(sc[:, 0].astype(np.float64) - 127)
+    assert np.all((r >= 4) & (r < 8))                   # 2^emax <= scaled max < 2^(emax+1)
+
+
+def test_mx4_roundtrip_exact_for_representable_blocks_and_error_bound():
+    rng = np.random.default_rng(19)
+    pos = np.array(_E2M1_TABLE)
+    el = rng.choice(pos, (16, 32)) * rng.choice([-1.0, 1.0], (16, 32))
+    el[:, 0] = rng.choice([4.0, 6.0], 16)               # block maximum in [4, 8): scale 2^s exactly
+    s = rng.integers(-20, 20, (16, 1)).astype(np.float64)
+    v = el * np.exp2(s)
+    np.testing.assert_array_equal(oracle.mx4_dequantize(*oracle.mx4_quantize(v)), v)
+    # general blocks: half an element step, at most a quarter of the magnitude or
+    # of the scale; clamped values (|v| in (6, 8) x scale) lose less than 2 x scale
+    v = rng.normal(0, 1, (300, 32)) * np.exp2(rng.integers(-30, 30, (300, 1)))
+    c, sc = oracle.mx4_quantize(v)
+    q = oracle.mx4_dequantize(c, sc)
+    scale = np.exp2(sc.astype(np.float64) - 127).repeat(32, axis=1)
+    err = np.abs(q - v)
+    clamped = np.abs(v) > 6 * scale
+    assert np.all(err[~clamped] <= np.maximum(0.25 * np.abs(v), 0.25 * scale)[~clamped])
+    assert np.all(err[clamped] < 2 * scale[clamped]) and np.all(np.abs(q[clamped]) == 6 * scale[clamped])
+    # blocks are independent and run along the last axis
+    w = rng.normal(0, 1, (20, 64)) * np.array([1e-3, 1e3]).repeat(32)[None, :]
+    cj, sj = oracle.mx4_quantize(w[:, 32:64])
+    c2, s2 = oracle.mx4_quantize(w)
+    assert np.array_equal(cj, c2[:, 32:64]) and np.array_equal(sj[:, 0], s2[:, 1])
+
+
 def test_quant_hooks_are_on_expert_inputs_and_activations():
     T, d, E, k, f = 11, 16, 4, 2, 24
     x, Wg, ex, sh = _layer(T, d, E, k, f, shared=True, seed=3)
