@@ -85,7 +85,7 @@ class HipEvents:
 def algorithmic_work(cfg, counts, touched):
     """Bytes and flops the layer must move/do for this routing (per call)."""
     import synth
-    es = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp8": 1}[cfg.wdt]
+    es = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp8": 1, "mxfp4": 0.5}[cfg.wdt]
     ae = 4 if cfg.act == "f32" else 2
     wexp = synth.weight_bytes_per_expert(cfg)
     n_exp = touched + (1 if cfg.shared else 0)
@@ -142,10 +142,17 @@ def cpu_baseline(cfg, inp, budget_s=12.0, max_calls=2000):
     cache = {}
 
     cd = lambda t: t.contiguous().view(torch.uint8).cpu().numpy()
-    mx = cfg.wdt == "mxfp8"
+    mx = cfg.wdt in ("mxfp8", "mxfp4")
+
+    def mx_codes(w):                          # MXFP4: two E2M1 codes per byte, element 2j low
+        b = cd(w)
+        if cfg.wdt != "mxfp4":
+            return b
+        return np.stack([b & 0x0F, b >> 4], axis=-1).reshape(*b.shape[:-1], 2 * b.shape[-1])
 
     def mx_triple(g, u, dn, sg, su, sd):     # output-major codes + block scales -> [in, out] values
-        return tuple(oracle.mx_dequantize(cd(w), sc.cpu().numpy()).T for w, sc in ((g, sg), (u, su), (dn, sd)))
+        deq = oracle.mx4_dequantize if cfg.wdt == "mxfp4" else oracle.mx_dequantize
+        return tuple(deq(mx_codes(w), sc.cpu().numpy()).T for w, sc in ((g, sg), (u, su), (dn, sd)))
 
     def expert(e):
         if e not in cache:
@@ -495,7 +502,7 @@ def measure(args, cfg, steps=None, warmup=None, cpu=True, graph=True, copy_calib
 
     bytes_total, flops, wbytes_used, _ = algorithmic_work(cfg, cnt, touched)
     layer_peak = (FP32_PEAK_TFLOPS if cfg.act == "f32" else
-                  FP8_PEAK_TFLOPS if cfg.wdt == "mxfp8" else BF16_PEAK_TFLOPS)
+                  FP8_PEAK_TFLOPS if cfg.wdt in ("mxfp8", "mxfp4") else BF16_PEAK_TFLOPS)
     t_star = max(bytes_total / (HBM_PEAK_GBS * 1e9), flops / (layer_peak * 1e12))
     have_k = kern_ms == kern_ms            # False when the second region was skipped
     if decode:
@@ -516,11 +523,12 @@ def measure(args, cfg, steps=None, warmup=None, cpu=True, graph=True, copy_calib
         rows = int(cnt.sum()) + (cfg.T if cfg.shared else 0)
         kflops = 4 * rows * cfg.d * cfg.f
         n_exp = touched + (1 if cfg.shared else 0)
-        mx = cfg.wdt == "mxfp8"
-        es = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp8": 1}[cfg.wdt]
+        mx = cfg.wdt in ("mxfp8", "mxfp4")
+        es = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp8": 1, "mxfp4": 0.5}[cfg.wdt]
         scales = 2 * cfg.f * 4 if cfg.wdt == "fp8" else (2 * cfg.f * cfg.d // 32 if mx else 0)
         if mx:      # x and H travel as codes plus one scale byte per 32 values
-            kbytes = n_exp * (2 * cfg.d * cfg.f + scales) + (cfg.T * cfg.d + rows * cfg.f) * 33 // 32
+            kbytes = (n_exp * (int(2 * cfg.d * cfg.f * es) + scales)
+                      + (cfg.T * cfg.d + rows * cfg.f) * 33 // 32)
         else:
             ae = 4 if f32 else 2
             kbytes = n_exp * (2 * cfg.d * cfg.f * es + scales) + cfg.T * cfg.d * ae + rows * cfg.f * ae
@@ -561,7 +569,8 @@ def measure(args, cfg, steps=None, warmup=None, cpu=True, graph=True, copy_calib
         "metric": "MoE-layer tokens/s; decode HBM GB/s, prefill MFMA TFLOP/s vs peak",
         "value": round(tokens_per_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "bf16 x fp8", "mxfp8": "mxfp8"}[cfg.wdt] if cfg.act == "bf16" else "f32",
+        "vs_baseline": None, "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "bf16 x fp8", "mxfp8": "mxfp8",
+                                                                    "mxfp4": "mxfp8 x mxfp4"}[cfg.wdt] if cfg.act == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "top_k": cfg.k, "f": cfg.f,
                    "act": cfg.act, "weights": cfg.wdt, "shared_expert": cfg.shared,

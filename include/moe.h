@@ -76,8 +76,11 @@ typedef enum {
  * activations to the same format on the fly (page "Current Bug:
  * CuTeDSLMoERunner produces wrong output", "Root Cause: scale_a layout doesn't
  * match expert_offsets": a grouped MoE on block-scaled activations and
- * weights, NVFP4 there). */
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP8 = 3 } moe_dtype;
+ * weights, NVFP4 there).  MXFP4 = the same block scales with OCP E2M1 weight
+ * codes (0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives; scale exponent
+ * floor(log2 max|block|) - 2), two codes per byte, element 2j in the low
+ * nibble; the activations are MXFP8 as above. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP8 = 3, MOE_MXFP4 = 4 } moe_dtype;
 
 typedef enum {
   MOE_PATH_AUTO = 0,         /* fused decode for T <= 8, grouped otherwise        */
@@ -111,9 +114,10 @@ typedef struct {
   int32_t renormalize;       /* 0 | 1                                            */
   float capacity_factor;     /* 0 => uncapped; else > 0 and finite               */
   int32_t act_dtype;         /* x, W_g, out: MOE_F32 | MOE_BF16                  */
-  int32_t w_dtype;           /* experts: F32 (act F32) | BF16, FP8_E4M3 or MXFP8
-                                (act BF16; MXFP8 needs d, f multiples of 128 and
-                                runs on the grouped path at every T)           */
+  int32_t w_dtype;           /* experts: F32 (act F32) | BF16, FP8_E4M3, MXFP8 or
+                                MXFP4 (act BF16; MXFP8 and MXFP4 need d, f
+                                multiples of 128 and run on the grouped path at
+                                every T)                                       */
   int32_t has_shared;        /* 0 | 1: one always-on shared expert, weight 1     */
   int32_t path;              /* moe_path                                         */
   int32_t routing;           /* moe_routing (0 = token choice, the default)      */
@@ -134,10 +138,11 @@ typedef struct {
   const float* ss_gate;      /* FP8 shared scales [f], [f], [d] else NULL         */
   const float* ss_up;
   const float* ss_down;
-  /* MXFP8 only (else NULL).  The codes in W_gate, W_up, W_down (and the
-   * shared Ws_*) are then OUTPUT-major, K contiguous: W_gate, W_up [E, f, d],
-   * W_down [E, d, f] (a torch nn.Linear weight's own layout); these are their
-   * E8M0 scales, one byte per 32 consecutive K values: */
+  /* MXFP8 and MXFP4 only (else NULL).  The codes in W_gate, W_up, W_down (and
+   * the shared Ws_*) are then OUTPUT-major, K contiguous: W_gate, W_up
+   * [E, f, d], W_down [E, d, f] (a torch nn.Linear weight's own layout; for
+   * MXFP4 in bytes [E, f, d/2] and [E, d, f/2], two codes per byte); these are
+   * their E8M0 scales, one byte per 32 consecutive K values: */
   const uint8_t* mx_gate;    /* [E, f, d/32]                                       */
   const uint8_t* mx_up;      /* [E, f, d/32]                                       */
   const uint8_t* mx_down;    /* [E, d, f/32]                                       */

@@ -16,10 +16,10 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_LIB", os.path.join(_PKG, "libmoe.so"))
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP8 = range(4)
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP8, MOE_MXFP4 = range(5)
 PATH_AUTO, PATH_GROUPED, PATH_FUSED_DECODE = range(3)
 ROUTING_TOKEN_CHOICE, ROUTING_EXPERT_CHOICE = range(2)
-_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "mxfp8": MOE_MXFP8}
+_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "mxfp8": MOE_MXFP8, "mxfp4": MOE_MXFP4}
 
 # Every symbol the header declares.
 EXPORTS = ("moe_workspace_size", "moe_capacity", "moe_route", "moe_permute", "moe_grouped_ffn",

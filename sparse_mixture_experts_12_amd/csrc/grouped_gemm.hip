@@ -637,7 +637,7 @@ int grouped_down_ksplit(int d, int f, int E, int has_shared, int wkind, int act_
   if (act_f32) return 1;
   const int slots = (E + (has_shared ? 1 : 0)) * ((d + 255) / 256);
   if (slots > 256) return 1;
-  const int bk = wkind == W_MX ? 128 : kDlBK;     // K per LDS stage of the light kernel
+  const int bk = (wkind == W_MX || wkind == W_MX4) ? 128 : kDlBK;     // K per LDS stage of the light kernel
   for (int ks : {4, 2})
     if (f % (ks * bk) == 0) return ks;
   return 1;
@@ -717,13 +717,13 @@ int grouped_grid(int maxQ, int n_tiles) {
 }
 
 SchedSpec grouped_sched_spec(const GroupedArgs& a) {
-  const int BM = a.wkind == W_MX ? 256 : pick_bm(a);
+  const int BM = (a.wkind == W_MX || a.wkind == W_MX4) ? 256 : pick_bm(a);
   return SchedSpec{a.sched, BM, a.has_shared ? a.T : 0, a.routed_rows,
                    grouped_max_row_tiles(a.routed_rows, a.T, a.E, a.has_shared, BM)};
 }
 
 hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
-  if (a.wkind == W_MX) return launch_grouped_ffn_mx(a, s);
+  if (a.wkind == W_MX || a.wkind == W_MX4) return launch_grouped_ffn_mx(a, s);
   const SchedSpec sp = grouped_sched_spec(a);
   const int maxQ = sp.maxQ;
   const int shared_row0 = a.routed_rows;

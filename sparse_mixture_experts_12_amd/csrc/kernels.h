@@ -62,7 +62,7 @@ struct ExpertWeights {
   const uint8_t *mxsg, *mxsu, *mxsd;
 };
 
-enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_MX = 3 };
+enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_MX = 3, W_MX4 = 4 };   // W_MX4: E2M1 codes, two per byte
 
 struct GroupedArgs {
   const void* x;                 // [T, d] act

@@ -45,22 +45,22 @@ moe_status check_desc(const moe_desc* d) {
   if ((long long)d->T * d->top_k > (1LL << 24)) return fail(MOE_ERR_INVALID_ARG, "T*top_k too large");
   const int a = d->act_dtype, w = d->w_dtype;
   if (a != MOE_F32 && a != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "bad act_dtype %d", a);
-  if (w != MOE_F32 && w != MOE_BF16 && w != MOE_FP8_E4M3 && w != MOE_MXFP8)
+  if (w != MOE_F32 && w != MOE_BF16 && w != MOE_FP8_E4M3 && w != MOE_MXFP8 && w != MOE_MXFP4)
     return fail(MOE_ERR_INVALID_ARG, "bad w_dtype %d", w);
-  const bool ok = (a == MOE_F32 && w == MOE_F32) ||
-                  (a == MOE_BF16 && (w == MOE_BF16 || w == MOE_FP8_E4M3 || w == MOE_MXFP8));
+  const bool mx = w == MOE_MXFP8 || w == MOE_MXFP4;
+  const bool ok = (a == MOE_F32 && w == MOE_F32) || (a == MOE_BF16 && (w == MOE_BF16 || w == MOE_FP8_E4M3 || mx));
   if (!ok) return fail(MOE_ERR_UNSUPPORTED, "dtype pair act=%d w=%d not supported", a, w);
-  if (w == MOE_MXFP8) {
+  if (mx) {
     if (d->d % 128 || d->f % 128)
-      return fail(MOE_ERR_UNSUPPORTED, "MXFP8 layers take d and f multiples of 128 (d=%d f=%d)", d->d, d->f);
-    if (d->path == MOE_PATH_FUSED_DECODE) return fail(MOE_ERR_UNSUPPORTED, "MXFP8 layers run on the grouped path");
+      return fail(MOE_ERR_UNSUPPORTED, "MX layers take d and f multiples of 128 (d=%d f=%d)", d->d, d->f);
+    if (d->path == MOE_PATH_FUSED_DECODE) return fail(MOE_ERR_UNSUPPORTED, "MX layers run on the grouped path");
   }
   if (d->routing != MOE_ROUTING_TOKEN_CHOICE && d->routing != MOE_ROUTING_EXPERT_CHOICE)
     return fail(MOE_ERR_INVALID_ARG, "bad routing %d", d->routing);
-  if (w == MOE_MXFP8) {   // the block-scaled kernels address code rows with 32-bit offsets
+  if (mx) {   // the block-scaled kernels address code rows with 32-bit offsets
     const double rows = (double)routed_rows_of(d) + (double)d->T;
     if ((double)d->T * d->d >= 2147483648.0 || rows * d->f >= 2147483648.0)
-      return fail(MOE_ERR_UNSUPPORTED, "MXFP8 layer too large (T*d and rows*f must stay below 2^31)");
+      return fail(MOE_ERR_UNSUPPORTED, "MX layer too large (T*d and rows*f must stay below 2^31)");
   }
   if (d->routing == MOE_ROUTING_EXPERT_CHOICE) {
     if (d->path == MOE_PATH_FUSED_DECODE)
@@ -99,7 +99,7 @@ moe_status check_expert_weights(const moe_desc* d, const moe_weights* w) {
   REQ(w->W_up, "W_up");
   REQ(w->W_down, "W_down");
   const bool fp8 = d->w_dtype == MOE_FP8_E4M3;
-  const bool mx = d->w_dtype == MOE_MXFP8;
+  const bool mx = d->w_dtype == MOE_MXFP8 || d->w_dtype == MOE_MXFP4;
   if (fp8) {
     REQ(w->s_gate, "s_gate");
     REQ(w->s_up, "s_up");
@@ -187,7 +187,7 @@ Layout layout_of(const moe_desc* d) {
   L.ndrop = take(4);
   L.rank = take(permute_ws_bytes(d->T * d->top_k, d->E));
   L.sched = take(grouped_sched_ints((int)routed, d->T, d->E, d->has_shared) * 4);
-  const bool mx = d->w_dtype == MOE_MXFP8;
+  const bool mx = d->w_dtype == MOE_MXFP8 || d->w_dtype == MOE_MXFP4;
   L.h = take(rows * d->f * (mx ? 1 : d->act_dtype == MOE_F32 ? 4 : 2));   // MXFP8: H codes
   L.hs = take(mx ? rows * (d->f / 32) : 0);                                  // MXFP8: H scales
   L.xq = take(mx ? T * d->d : 0);                                            // MXFP8: x codes
@@ -236,7 +236,7 @@ ExpertWeights expert_weights(const moe_weights* w) {
 }
 
 int wkind_of(const moe_desc* d) {
-  return d->w_dtype == MOE_MXFP8 ? W_MX : d->w_dtype == MOE_FP8_E4M3 ? W_FP8 : d->w_dtype == MOE_BF16 ? W_BF16 : W_F32;
+  return d->w_dtype == MOE_MXFP4 ? W_MX4 : d->w_dtype == MOE_MXFP8 ? W_MX : d->w_dtype == MOE_FP8_E4M3 ? W_FP8 : d->w_dtype == MOE_BF16 ? W_BF16 : W_F32;
 }
 
 hipEvent_t eb_of(const moe_stats* st) { return st ? st->ev_begin : nullptr; }

@@ -34,6 +34,14 @@
 // (A) or column (B), h = l / 32; its 32 bytes hold K = 16 h .. 16 h + 15 and
 // 32 + 16 h .. 32 + 16 h + 15 of the 64; its scale byte (selected by the
 // instruction's op_sel from a 32-bit register) is that of K block h.
+//
+// MXFP4 weights (E2M1, two codes per byte, element 2j in the low nibble): the
+// B operand of the same instruction in its 4-bit format takes 16 bytes per
+// lane, lane (i, h) holding K = 32 h .. 32 h + 31 in order, low nibble first
+// (checked with an in-bounds probe of the instruction), so one 16-byte LDS
+// read per lane and sub-step; B rows of a stage are 64 bytes (128 K) with
+// the 4-chunk swizzle aswz<4>.  Scales, A (MXFP8 x or H) and the epilogues
+// are as for MXFP8 weights.
 #include <hip/hip_ext.h>
 
 #include <type_traits>
@@ -173,10 +181,11 @@ hipError_t launch_mx_quantize(const void* in, bool in_f32, long rows, int cols, 
 // blocks) of the 256 A rows and of the 256 B rows.
 // K range [k_lo, k_lo + nK BK); K part kpart > 0 writes its fp32 block to
 // y_part slot `slot` (light down tiles split over K).
-template <bool DUAL, int BMV, int BMMAX, int NST>
+template <bool DUAL, int BMV, int BMMAX, int NST, bool W4>
 __device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int rows, int nt, uint8_t* L0,
                                         uint8_t* L1, uint8_t* L2, int k_lo, int nK, int kpart, int slot) {
   constexpr int BK = kMxBK;
+  constexpr int BKB = W4 ? BK / 2 : BK;              // bytes of a B row per stage (E2M1: two per byte)
   constexpr int WM = (BMV >= 256) ? 2 : 1, WN = 4 / WM;
   constexpr int NMAT = DUAL ? 2 : 1;
   constexpr int BN_MAT = DUAL ? 128 : 256;
@@ -185,12 +194,13 @@ __device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int 
   constexpr int MI = BMV / WM / 32;
   constexpr int WROWS = BMV / WM;
   constexpr int A_LD = BMV / 8 / 4;                // 1 KB (8-row) A blocks per wave per stage
-  constexpr int B_LD = 256 / 8 / 4;                // 1 KB B blocks per wave per stage
+  constexpr int B_RPB = 1024 / BKB;                // B rows per 1 KB block
+  constexpr int B_LD = 256 / B_RPB / 4;            // 1 KB B blocks per wave per stage
   constexpr int LDS_B = BMMAX * BK;                // B codes
-  constexpr int LDS_SA = (BMMAX + 256) * BK;       // A scale dwords [256]
+  constexpr int LDS_SA = BMMAX * BK + 256 * BKB;   // A scale dwords [256]
   constexpr int LDS_SB = LDS_SA + 1024;            // B scale dwords [256]
   constexpr int NMF = MI * NI;                      // MFMAs per 64-K sub-step
-  constexpr int NDS = 2 * (MI + NI) + MI + NI;      // LDS reads per sub-step (codes, scales)
+  constexpr int NDS = 2 * MI + (W4 ? 1 : 2) * NI + MI + NI;   // LDS reads per sub-step (codes, scales)
   constexpr int NVM = A_LD + B_LD + 2;              // global -> LDS loads per stage
   static_assert(BK == 128 && (NST == 2 || NST == 3) && A_LD >= 1 && BMV <= BMMAX, "tile configuration");
   static_assert((NST - 1) * NVM < 64, "outstanding loads exceed the vmcnt range");
@@ -245,11 +255,16 @@ __device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int 
     aoff[i] = a_row(8 * (wave + 4 * i) + (lane >> 3)) * (uint32_t)p.K + ((cx ^ ((wave + 4 * i) & 7)) << 4);
   int bmat;
   const int bc = b_first(wave, &bmat);
-  const uint8_t* bbase = b_codes(bmat) + (gN + bc) * (size_t)p.K;
+  const uint32_t KB = W4 ? (uint32_t)p.K / 2 : (uint32_t)p.K;   // bytes of a weight row
+  const uint8_t* bbase = b_codes(bmat) + (gN + bc) * (size_t)KB;
   uint32_t boff[B_LD];
 #pragma unroll
-  for (int j = 0; j < B_LD; ++j)
-    boff[j] = (uint32_t)(8 * j + (lane >> 3)) * (uint32_t)p.K + ((cx ^ ((B_LD * wave + j) & 7)) << 4);
+  for (int j = 0; j < B_LD; ++j) {
+    if constexpr (W4)   // row 16 b + lane / 4, LDS chunk lane % 4 = aswz<4>(row, global chunk)
+      boff[j] = (uint32_t)(16 * j + (lane >> 2)) * KB + (uint32_t)(((lane & 3) ^ (lane >> 4)) << 4);
+    else
+      boff[j] = (uint32_t)(8 * j + (lane >> 3)) * KB + ((cx ^ ((B_LD * wave + j) & 7)) << 4);
+  }
   const uint32_t asoff = a_row(64 * wave + lane) * (uint32_t)KS;
   const uint8_t* bsbase = b_scales(bmat) + (gN + bc) * (size_t)KS;
   const uint32_t bsoff = (uint32_t)lane * (uint32_t)KS;
@@ -262,7 +277,7 @@ __device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int 
                                        (lds_ptr_t)(L + (wave + 4 * i) * 1024), 16, 0, 0);
 #pragma unroll
     for (int j = 0; j < B_LD; ++j)
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(bbase + (boff[j] + (uint32_t)k0)),
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(bbase + (boff[j] + (uint32_t)(W4 ? k0 / 2 : k0))),
                                        (lds_ptr_t)(L + LDS_B + (B_LD * wave + j) * 1024), 16, 0,
                                        (BMV <= 128) ? 2 : 0);   // light tiles stream their weights
     __builtin_amdgcn_global_load_lds((gbl_ptr_t)(p.as + (asoff + (uint32_t)(k0 >> 5))),
@@ -300,10 +315,15 @@ __device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int 
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       const int j = b_lrow(ni);
-      const uint8_t* Lb = L + LDS_B + j * BK;
-      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(Lb + aswz<8>(j, c0) * 16);
-      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(Lb + aswz<8>(j, c1) * 16);
-      bfr[ni] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      const uint8_t* Lb = L + LDS_B + j * BKB;
+      if constexpr (W4) {
+        const u32x4_t q = *reinterpret_cast<const u32x4_t*>(Lb + aswz<4>(j, 2 * ks + lhi) * 16);
+        bfr[ni] = i32x8_t{(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
+      } else {
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(Lb + aswz<8>(j, c0) * 16);
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(Lb + aswz<8>(j, c1) * 16);
+        bfr[ni] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
       sb[ni] = *reinterpret_cast<const uint32_t*>(L + LDS_SB + j * 4) >> sh;
     }
   };
@@ -313,8 +333,8 @@ __device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int 
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bfr[ni], acc[mi][ni], 0, 0, ops,
-                                                                      (int)sa[mi], ops, (int)sb[ni]);
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bfr[ni], acc[mi][ni], 0, W4 ? 4 : 0,
+                                                                      ops, (int)sa[mi], ops, (int)sb[ni]);
   };
 
   using I0 = std::integral_constant<int, 0>;
@@ -454,11 +474,11 @@ __device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int 
 // SEG 2: light row tiles (an expert's last tile, at most 128 rows): 128-row
 //        stages, three deep (two steps of loads in flight; these tiles do little
 //        MFMA work per stage and are bound by load latency).
-template <bool DUAL, int SEG>
+template <bool DUAL, int SEG, bool W4>
 __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(MxParams p) {
   constexpr int BMMAX = SEG == 1 ? 256 : 128;
   constexpr int NST = SEG == 1 ? 2 : 3;
-  constexpr int LDS_S = (BMMAX + 256) * kMxBK + 2048;
+  constexpr int LDS_S = BMMAX * kMxBK + 256 * (W4 ? kMxBK / 2 : kMxBK) + 2048;
   __shared__ __attribute__((aligned(1024))) uint8_t L0[LDS_S];
   __shared__ __attribute__((aligned(1024))) uint8_t L1[LDS_S];
   __shared__ __attribute__((aligned(1024))) uint8_t L2[NST > 2 ? LDS_S : 16];
@@ -472,17 +492,18 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(MxParams p) {
   const int nK = p.K / kMxBK / kparts;
   const int k_lo = kpart * nK * kMxBK;
   if constexpr (SEG == 1) {
-    mx_tile<DUAL, 256, BMMAX, NST>(p, g, row0, rows, nt, L0, L1, L2, k_lo, nK, kpart, slot);
+    mx_tile<DUAL, 256, BMMAX, NST, W4>(p, g, row0, rows, nt, L0, L1, L2, k_lo, nK, kpart, slot);
   } else {
-    if (rows > 64) mx_tile<DUAL, 128, BMMAX, NST>(p, g, row0, rows, nt, L0, L1, L2, k_lo, nK, kpart, slot);
-    else mx_tile<DUAL, 64, BMMAX, NST>(p, g, row0, rows, nt, L0, L1, L2, k_lo, nK, kpart, slot);
+    if (rows > 64) mx_tile<DUAL, 128, BMMAX, NST, W4>(p, g, row0, rows, nt, L0, L1, L2, k_lo, nK, kpart, slot);
+    else mx_tile<DUAL, 64, BMMAX, NST, W4>(p, g, row0, rows, nt, L0, L1, L2, k_lo, nK, kpart, slot);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-hipError_t launch_grouped_ffn_mx(const GroupedArgs& a, hipStream_t s) {
+template <bool W4>
+static hipError_t launch_grouped_ffn_mx_t(const GroupedArgs& a, hipStream_t s) {
   uint8_t* xq = a.mx_xq;
   uint8_t* xs = a.mx_xs;
   uint8_t* hq = (uint8_t*)a.h;
@@ -540,7 +561,7 @@ hipError_t launch_grouped_ffn_mx(const GroupedArgs& a, hipStream_t s) {
       light<<<gl, 256, 0, s>>>(prm);
     }
   };
-  launch_split(gemm_mx_kernel<true, 1>, gemm_mx_kernel<true, 2>, p, a.f / 128, a.ev_begin, a.ev_end);
+  launch_split(gemm_mx_kernel<true, 1, W4>, gemm_mx_kernel<true, 2, W4>, p, a.f / 128, a.ev_begin, a.ev_end);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (ferr != hipSuccess) return ferr;
 
@@ -555,12 +576,16 @@ hipError_t launch_grouped_ffn_mx(const GroupedArgs& a, hipStream_t s) {
   q.ksplit = grouped_down_ksplit(a.d, a.f, a.E, a.has_shared, a.wkind, a.act_f32);
   q.part_slots = groups * dn_tiles;
   q.y_part = a.y_part;
-  launch_split(gemm_mx_kernel<false, 1>, gemm_mx_kernel<false, 2>, q, dn_tiles, nullptr, nullptr, q.ksplit);
+  launch_split(gemm_mx_kernel<false, 1, W4>, gemm_mx_kernel<false, 2, W4>, q, dn_tiles, nullptr, nullptr, q.ksplit);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (ferr != hipSuccess) return ferr;
   if (q.ksplit > 1)
     return launch_down_split_reduce(a.sched, maxQ, a.E, dn_tiles, a.d, q.ksplit, q.part_slots, a.y_part, a.y, s);
   return hipSuccess;
+}
+
+hipError_t launch_grouped_ffn_mx(const GroupedArgs& a, hipStream_t s) {
+  return a.wkind == W_MX4 ? launch_grouped_ffn_mx_t<true>(a, s) : launch_grouped_ffn_mx_t<false>(a, s);
 }
 
 }  // namespace moe

@@ -21,6 +21,9 @@ name and the expert id, so one expert can be regenerated on its own):
            mx_down [E, d, f/32]): s = floor(log2 max|block|) - 8 clamped to
            [-127, 127], q = RNE(w / 2^s) clamped to +-448 as float8_e4m3fn,
            byte = s + 127.  The layer receives these codes as given.
+  mxfp4    the same layout and scale bytes with E2M1 elements, two per byte
+           (element 2j in the low nibble): s = floor(log2 max|block|) - 2,
+           q = RNE(w / 2^s) to {0, 0.5, 1, 1.5, 2, 3, 4, 6} with sign, |q| <= 6.
 """
 from __future__ import annotations
 
@@ -43,7 +46,7 @@ class MoEConfig:
     k: int
     f: int
     act: str = "bf16"          # activation / router dtype: "f32" | "bf16"
-    wdt: str = "bf16"          # expert weight dtype: "f32" | "bf16" | "fp8" | "mxfp8"
+    wdt: str = "bf16"          # expert weight dtype: "f32" | "bf16" | "fp8" | "mxfp8" | "mxfp4"
     renormalize: bool = True
     capacity_factor: float = 0.0   # 0 => uncapped
     shared: bool = False       # one always-on shared expert (same f)
@@ -80,6 +83,11 @@ CONFIGS = {
                                        wdt="mxfp8"),
     "fine_grained_mxfp8": MoEConfig("fine_grained_mxfp8", T=2048, d=7168, E=256, k=8, f=2048,
                                     wdt="mxfp8", shared=True, bias="zipf"),
+    # MXFP4 weights (E2M1 codes, two per byte) with MXFP8 activations
+    "mixtral_prefill_mxfp4": MoEConfig("mixtral_prefill_mxfp4", T=4096, d=4096, E=8, k=2, f=14336,
+                                       wdt="mxfp4"),
+    "fine_grained_mxfp4": MoEConfig("fine_grained_mxfp4", T=2048, d=7168, E=256, k=8, f=2048,
+                                    wdt="mxfp4", shared=True, bias="zipf"),
 }
 
 
@@ -128,6 +136,32 @@ def quantize_mxfp8_rows(w32: torch.Tensor):
     return q.reshape(w32.shape), (s + 127).to(torch.uint8)
 
 
+_E2M1_MIDS = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]   # midpoints of 0, .5, 1, 1.5, 2, 3, 4, 6
+
+
+def quantize_mxfp4_rows(w32: torch.Tensor):
+    """w32 fp32 [..., K], K % 32 == 0 -> (codes uint8 [..., K / 2], two E2M1
+    codes per byte, element 2 j in the low nibble and 2 j + 1 in the high
+    one; scales uint8 [..., K / 32]), blocks of 32 along the last axis:
+    s = floor(log2 max|block|) - 2, elements rounded to the nearest E2M1
+    value (ties to the even code, magnitudes above 6 saturated)."""
+    K = w32.shape[-1]
+    b = w32.reshape(*w32.shape[:-1], K // 32, 32)
+    amax = b.abs().amax(dim=-1)
+    _, ex = torch.frexp(amax)                       # amax = m 2^ex, m in [0.5, 1)
+    s = torch.where(amax > 0, ex - 3, torch.full_like(ex, -127)).clamp(-127, 127)
+    y = torch.ldexp(b, (-s).unsqueeze(-1).to(b.dtype))
+    a = y.abs().clamp(max=6.0)
+    mids = torch.tensor(_E2M1_MIDS, dtype=a.dtype, device=a.device)
+    code = torch.bucketize(a, mids)                 # mids[i - 1] < a <= mids[i] -> i
+    at_mid = (code < 7) & (a == mids[code.clamp(max=6)])
+    code = torch.where(at_mid & (code % 2 == 1), code + 1, code)   # a tie goes to the even code
+    code = code | torch.where(torch.signbit(y), 8, 0)
+    code = code.to(torch.uint8).reshape(*w32.shape[:-1], K)
+    packed = code[..., 0::2] | (code[..., 1::2] << 4)
+    return packed.contiguous(), (s + 127).to(torch.uint8)
+
+
 def _expert_mats(cfg: MoEConfig, tag: str, e: int, device):
     wg = _normal((cfg.d, cfg.f), cfg.w_std, tensor_seed(cfg.seed, tag + "gate", e), device)
     wu = _normal((cfg.d, cfg.f), cfg.w_std, tensor_seed(cfg.seed, tag + "up", e), device)
@@ -166,7 +200,7 @@ def make_inputs(cfg: MoEConfig, device="cpu", router_only: bool = False) -> dict
         return torch.empty(shape, dtype=dt, device=dev)
 
     E, d, f = cfg.E, cfg.d, cfg.f
-    if cfg.wdt == "mxfp8":
+    if cfg.wdt in ("mxfp8", "mxfp4"):
         return _make_mx_weights(cfg, dev, out)
     Wg, Wu, Wd = alloc((E, d, f)), alloc((E, d, f)), alloc((E, f, d))
     fp8 = cfg.wdt == "fp8"
@@ -200,16 +234,23 @@ def make_inputs(cfg: MoEConfig, device="cpu", router_only: bool = False) -> dict
 
 
 def _make_mx_weights(cfg: MoEConfig, dev, out: dict) -> dict:
+    """MXFP8 codes [E, N, K] (float8_e4m3fn) or MXFP4 codes [E, N, K / 2]
+    (uint8, two per byte), output-major, with scales [E, N, K / 32]."""
     E, d, f = cfg.E, cfg.d, cfg.f
-    q8 = lambda *shape: torch.empty(shape, dtype=torch.float8_e4m3fn, device=dev)
+    fp4 = cfg.wdt == "mxfp4"
+    quant = quantize_mxfp4_rows if fp4 else quantize_mxfp8_rows
+    if fp4:
+        q8 = lambda *shape: torch.empty(shape[:-1] + (shape[-1] // 2,), dtype=torch.uint8, device=dev)
+    else:
+        q8 = lambda *shape: torch.empty(shape, dtype=torch.float8_e4m3fn, device=dev)
     u8 = lambda *shape: torch.empty(shape, dtype=torch.uint8, device=dev)
     Wg, Wu, Wd = q8(E, f, d), q8(E, f, d), q8(E, d, f)
     sg, su, sd = u8(E, f, d // 32), u8(E, f, d // 32), u8(E, d, f // 32)
     for e in range(E):
         wg, wu, wd = _expert_mats(cfg, "", e, dev)
-        Wg[e], sg[e] = quantize_mxfp8_rows(wg.t().contiguous())
-        Wu[e], su[e] = quantize_mxfp8_rows(wu.t().contiguous())
-        Wd[e], sd[e] = quantize_mxfp8_rows(wd.t().contiguous())
+        Wg[e], sg[e] = quant(wg.t().contiguous())
+        Wu[e], su[e] = quant(wu.t().contiguous())
+        Wd[e], sd[e] = quant(wd.t().contiguous())
         del wg, wu, wd
     out.update(W_gate=Wg, W_up=Wu, W_down=Wd, mx_gate=sg, mx_up=su, mx_down=sd,
                s_gate=None, s_up=None, s_down=None)
@@ -217,13 +258,15 @@ def _make_mx_weights(cfg: MoEConfig, dev, out: dict) -> dict:
                mxs_gate=None, mxs_up=None, mxs_down=None)
     if cfg.shared:
         wg, wu, wd = _expert_mats(cfg, "shared_", 0, dev)
-        out["Ws_gate"], out["mxs_gate"] = quantize_mxfp8_rows(wg.t().contiguous())
-        out["Ws_up"], out["mxs_up"] = quantize_mxfp8_rows(wu.t().contiguous())
-        out["Ws_down"], out["mxs_down"] = quantize_mxfp8_rows(wd.t().contiguous())
+        out["Ws_gate"], out["mxs_gate"] = quant(wg.t().contiguous())
+        out["Ws_up"], out["mxs_up"] = quant(wu.t().contiguous())
+        out["Ws_down"], out["mxs_down"] = quant(wd.t().contiguous())
     return out
 
 
 def weight_bytes_per_expert(cfg: MoEConfig) -> int:
+    if cfg.wdt == "mxfp4":
+        return 3 * cfg.d * cfg.f // 2 + 3 * cfg.d * cfg.f // 32
     es = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp8": 1}[cfg.wdt]
     b = 3 * cfg.d * cfg.f * es
     if cfg.wdt == "fp8":

@@ -9,7 +9,7 @@ import oracle
 import synth
 
 # max|gpu - oracle| / max|oracle| bounds per weight type (fp32, bf16, fp8)
-TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "mxfp8": 6e-2}
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "mxfp8": 6e-2, "mxfp4": 6e-2}
 
 
 def to64(t: torch.Tensor) -> np.ndarray:
@@ -18,6 +18,12 @@ def to64(t: torch.Tensor) -> np.ndarray:
 
 def codes(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().view(torch.uint8).cpu().numpy()
+
+
+def unpack_e2m1(t: torch.Tensor) -> np.ndarray:
+    """Two E2M1 codes per byte (element 2j in the low nibble) -> one per byte."""
+    b = codes(t)
+    return np.stack([b & 0x0F, b >> 4], axis=-1).reshape(*b.shape[:-1], 2 * b.shape[-1])
 
 
 class OracleInputs:
@@ -33,6 +39,9 @@ class OracleInputs:
     def _triple(self, g, u, dn, sg, su, sd):
         if self.cfg.wdt == "mxfp8":         # output-major codes + block scales -> [in, out] values
             return tuple(oracle.mx_dequantize(codes(w), sc.cpu().numpy()).T for w, sc in ((g, sg), (u, su), (dn, sd)))
+        if self.cfg.wdt == "mxfp4":
+            return tuple(oracle.mx4_dequantize(unpack_e2m1(w), sc.cpu().numpy()).T
+                         for w, sc in ((g, sg), (u, su), (dn, sd)))
         if self.cfg.wdt == "fp8":
             return (oracle.dequantize(codes(g), sg.cpu().numpy(), 1),
                     oracle.dequantize(codes(u), su.cpu().numpy(), 1),
@@ -41,7 +50,7 @@ class OracleInputs:
 
     def expert(self, e: int):
         i = self.inp
-        if self.cfg.wdt == "mxfp8":
+        if self.cfg.wdt in ("mxfp8", "mxfp4"):
             return self._triple(i["W_gate"][e], i["W_up"][e], i["W_down"][e],
                                 i["mx_gate"][e], i["mx_up"][e], i["mx_down"][e])
         if self.cfg.wdt == "fp8":
@@ -53,14 +62,14 @@ class OracleInputs:
         i = self.inp
         if not self.cfg.shared:
             return None
-        if self.cfg.wdt == "mxfp8":
+        if self.cfg.wdt in ("mxfp8", "mxfp4"):
             return self._triple(i["Ws_gate"], i["Ws_up"], i["Ws_down"], i["mxs_gate"], i["mxs_up"], i["mxs_down"])
         return self._triple(i["Ws_gate"], i["Ws_up"], i["Ws_down"], i["ss_gate"], i["ss_up"], i["ss_down"])
 
     def quant_hooks(self) -> dict:
-        """Block-scaled layers: expert inputs and the fp32 SwiGLU activations
-        are MXFP8-quantised before their products."""
-        if self.cfg.wdt != "mxfp8":
+        """Block-scaled layers (MXFP8 or MXFP4 weights): expert inputs and the
+        fp32 SwiGLU activations are MXFP8-quantised before their products."""
+        if self.cfg.wdt not in ("mxfp8", "mxfp4"):
             return {}
         return {"quant_x": oracle.mx_roundtrip, "quant_h": lambda H: oracle.mx_roundtrip(H, as_fp32=True)}
 

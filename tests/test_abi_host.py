@@ -204,6 +204,24 @@ def test_synth_mx_weights_follow_the_oracle_quantiser():
     np.testing.assert_array_equal(q.view(torch.uint8).numpy(), rq)
 
 
+def test_synth_mxfp4_weights_follow_the_oracle_quantiser():
+    """MXFP4: the recipe's torch quantiser (packed two codes per byte, the
+    even element in the low nibble) against the oracle's numpy one."""
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(6)
+    w = (rng.normal(0, 0.02, (64, 256)) * np.exp2(rng.integers(-8, 8, (64, 1)))).astype(np.float32)
+    w[3, :32] = 0.0
+    w[5, :64] = (rng.integers(-28, 28, 64) / 4.0).astype(np.float32)   # exact midpoints
+    w[6, :32] = -1e-30                                                 # rounds to -0
+    q, s = synth.quantize_mxfp4_rows(torch.from_numpy(w))
+    rq, rs = oracle.mx4_quantize(w.astype(np.float64))
+    qn = q.numpy()
+    assert qn.shape == (64, 128) and s.shape == (64, 8)
+    np.testing.assert_array_equal(s.numpy(), rs)
+    np.testing.assert_array_equal(np.stack([qn & 15, qn >> 4], axis=-1).reshape(64, 256), rq)
+
+
 def test_backward_validation(ops):
     def bwd(d, g=None):
         gs = g if g is not None else ops.Grads()

@@ -67,6 +67,16 @@ SMALL = {
     "mx_long_k": C["mixtral_prefill_mxfp8"].with_(T=70, d=2048, f=1280, E=4, k=1, seed=25),
     # 97 expert groups: the light launches run on the library's second stream
     "mx_many_experts": C["fine_grained_mxfp8"].with_(T=64, d=256, E=96, k=4, f=256, seed=27),
+    # MXFP4 weights (E2M1, two per byte) with MXFP8 activations: 64/128/256-row
+    # bodies and ragged tails, the shared expert, capacity drops, a half-used
+    # last down tile (d % 256 = 128), many groups on the second stream
+    "mx4_prefill": C["mixtral_prefill_mxfp4"].with_(T=300, d=512, f=1024),
+    "mx4_big_tiles": C["mixtral_prefill_mxfp4"].with_(T=760, d=384, f=512, E=4, k=2, seed=3),
+    "mx4_finegrained_shared": C["fine_grained_mxfp4"].with_(T=96, d=512, E=32, f=256),
+    "mx4_capacity": C["mixtral_prefill_mxfp4"].with_(T=200, d=256, E=16, k=8, f=128, capacity_factor=1.25,
+                                                      seed=23),
+    "mx4_many_experts": C["fine_grained_mxfp4"].with_(T=64, d=256, E=96, k=4, f=256, seed=28),
+    "mx4_T1": C["mixtral_prefill_mxfp4"].with_(T=1, d=256, f=256, seed=29),
 }
 
 
@@ -280,7 +290,8 @@ def test_permute_all_to_one_expert_with_capacity():
                                   "bf16_finegrained_shared", "fp8_capacity", "fp8_capacity_tight",
                                   "bf16_one_expert", "bf16_big_tiles", "bf16_big_tiles_mid",
                                   "bf16_big_tiles_shared", "fp8_big_tiles_shared", "mx_prefill", "mx_big_tiles",
-                                  "mx_big_tiles_shared", "mx_capacity"])
+                                  "mx_big_tiles_shared", "mx_capacity", "mx4_prefill", "mx4_big_tiles",
+                                  "mx4_finegrained_shared", "mx4_capacity"])
 def test_grouped_ffn_parity(name):
     cfg = SMALL[name]
     print(f"[grouped_ffn] {name}", flush=True)
@@ -357,7 +368,7 @@ def test_forward_parity_small(name):
     st = ops.Stats(d_n_dropped=dev_nd.data_ptr(), d_counts=dev_counts.data_ptr())
     out, taken = run_forward(inp, stats=st)
     ref = ov.forward()
-    decode = cfg.T <= 8 and cfg.act == "bf16" and cfg.wdt != "mxfp8"
+    decode = cfg.T <= 8 and cfg.act == "bf16" and cfg.wdt not in ("mxfp8", "mxfp4")
     want_path = ops.PATH_FUSED_DECODE if decode else ops.PATH_GROUPED
     assert taken == want_path
     e = assert_close(to64(out), ref["out"], TOL[cfg.wdt], name)
@@ -456,9 +467,10 @@ def test_graph_capture_first_call_of_a_thread():
 # row-tile boundaries, all recomputed by the oracle.
 # ---------------------------------------------------------------------------
 FULL = ["tiny_f32", "mixtral_decode", "mixtral_decode_b8", "mixtral_prefill", "fine_grained",
-        "fp8_capacity", "fp8_capacity_decode", "mixtral_prefill_mxfp8", "fine_grained_mxfp8"]
+        "fp8_capacity", "fp8_capacity_decode", "mixtral_prefill_mxfp8", "fine_grained_mxfp8",
+        "mixtral_prefill_mxfp4", "fine_grained_mxfp4"]
 SAMPLE = {"mixtral_prefill": 12, "fine_grained": 3, "fp8_capacity": 24, "mixtral_prefill_mxfp8": 12,
-          "fine_grained_mxfp8": 3}
+          "fine_grained_mxfp8": 3, "mixtral_prefill_mxfp4": 12, "fine_grained_mxfp4": 3}
 TILE = 32          # the smallest row-tile height any grouped GEMM body uses
 
 
@@ -520,7 +532,7 @@ def test_forward_parity_full_size(name):
 # feed the same kernels the oracle's expert-choice selection (E*C rows, token t
 # given as assignment t*k).
 GROUPED_FULL = ["mixtral_prefill", "fine_grained", "fp8_capacity", "mixtral_prefill_mxfp8",
-                "fine_grained_mxfp8", "fine_grained_expert_choice"]
+                "fine_grained_mxfp8", "mixtral_prefill_mxfp4", "fine_grained_mxfp4", "fine_grained_expert_choice"]
 
 
 @pytest.mark.parametrize("name", GROUPED_FULL)
