@@ -159,19 +159,20 @@ def test_expert_choice_capacity_and_workspace(ops):
     assert ops.LIB.moe_workspace_size(ctypes.byref(ec)) > ops.LIB.moe_workspace_size(ctypes.byref(tc))
 
 
-def test_mxfp8_validation(ops):
+@pytest.mark.parametrize("wdt", ["mxfp8", "mxfp4"])
+def test_mx_validation(ops, wdt):
     def fwd(d):
         return ops.LIB.moe_forward(ctypes.byref(d), None, None, None, None, None, 0, None)
-    d = ops.make_desc(40, 192, 8, 2, 256, wdt="mxfp8")           # d % 128 != 0
+    d = ops.make_desc(40, 192, 8, 2, 256, wdt=wdt)           # d % 128 != 0
     assert fwd(d) == ops.MOE_ERR_UNSUPPORTED and "multiples of 128" in ops.last_error()
-    d = ops.make_desc(4, 256, 8, 2, 256, wdt="mxfp8", path=ops.PATH_FUSED_DECODE)
+    d = ops.make_desc(4, 256, 8, 2, 256, wdt=wdt, path=ops.PATH_FUSED_DECODE)
     assert fwd(d) == ops.MOE_ERR_UNSUPPORTED and "grouped" in ops.last_error()
-    d = ops.make_desc(4, 256, 8, 2, 256, act="f32", wdt="mxfp8")
+    d = ops.make_desc(4, 256, 8, 2, 256, act="f32", wdt=wdt)
     assert fwd(d) == ops.MOE_ERR_UNSUPPORTED
-    d = ops.make_desc(1 << 20, 4096, 8, 2, 14336, wdt="mxfp8")   # 32-bit row offsets would overflow
+    d = ops.make_desc(1 << 20, 4096, 8, 2, 14336, wdt=wdt)   # 32-bit row offsets would overflow
     assert fwd(d) == ops.MOE_ERR_UNSUPPORTED and "2^31" in ops.last_error()
-    # a valid MXFP8 descriptor sizes a workspace holding x and H codes + scales
-    d = ops.make_desc(100, 256, 8, 2, 384, wdt="mxfp8")
+    # a valid MX descriptor sizes a workspace holding x and H codes + scales
+    d = ops.make_desc(100, 256, 8, 2, 384, wdt=wdt)
     b = ops.make_desc(100, 256, 8, 2, 384, wdt="bf16")
     assert ops.workspace_size(d) > 0 and ops.workspace_size(b) > 0
     # weights without their block scales are rejected before any HIP call
@@ -226,7 +227,7 @@ def test_backward_validation(ops):
     def bwd(d, g=None):
         gs = g if g is not None else ops.Grads()
         return ops.LIB.moe_backward(ctypes.byref(d), None, None, None, ctypes.byref(gs), None, 0, None)
-    for wdt, act in (("fp8", "bf16"), ("mxfp8", "bf16"), ("f32", "f32")):
+    for wdt, act in (("fp8", "bf16"), ("mxfp8", "bf16"), ("mxfp4", "bf16"), ("f32", "f32")):
         d = ops.make_desc(40, 256, 8, 2, 256, act=act, wdt=wdt)
         assert bwd(d) == ops.MOE_ERR_UNSUPPORTED, wdt
         assert ops.backward_workspace_size(d) == 0
