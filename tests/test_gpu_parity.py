@@ -633,6 +633,7 @@ EC_CASES = {
     "ec_all_tokens": C["mixtral_prefill"].with_(T=40, d=256, f=256, E=4, k=2, capacity_factor=2.0, seed=16),
     "ec_small_batch": C["mixtral_prefill"].with_(T=5, d=256, f=256, E=8, k=2, seed=17),
     "ec_mx_shared": C["fine_grained_mxfp8"].with_(T=96, d=512, E=32, f=256, seed=26),
+    "ec_mx4_shared": C["fine_grained_mxfp4"].with_(T=96, d=512, E=32, f=256, seed=30),
     "mixtral_prefill": C["mixtral_prefill"],
     "fine_grained": C["fine_grained"],
 }
