@@ -470,14 +470,16 @@ __device__ __forceinline__ void mx_tile(const MxParams& p, int g, int row0, int 
   }
 }
 
-// SEG 1: heavy row tiles (more than 128 rows): 256-row LDS stages, two deep.
+// SEG 1: heavy row tiles (more than 128 rows): 256-row LDS stages, two deep
+//        with 8-bit weights; with 4-bit weights a stage is a quarter smaller,
+//        so three fit in LDS (150 KB) and keep two steps of loads in flight.
 // SEG 2: light row tiles (an expert's last tile, at most 128 rows): 128-row
 //        stages, three deep (two steps of loads in flight; these tiles do little
 //        MFMA work per stage and are bound by load latency).
 template <bool DUAL, int SEG, bool W4>
 __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(MxParams p) {
   constexpr int BMMAX = SEG == 1 ? 256 : 128;
-  constexpr int NST = SEG == 1 ? 2 : 3;
+  constexpr int NST = (SEG == 1 && !W4) ? 2 : 3;
   constexpr int LDS_S = BMMAX * kMxBK + 256 * (W4 ? kMxBK / 2 : kMxBK) + 2048;
   __shared__ __attribute__((aligned(1024))) uint8_t L0[LDS_S];
   __shared__ __attribute__((aligned(1024))) uint8_t L1[LDS_S];
