@@ -360,17 +360,18 @@ def expert_choice_capacity(T: int, k: int, E: int, capacity_factor) -> int:
     return max(1, min(T, c))
 
 
-def expert_choice_routing(logits32, k: int, capacity_factor, renormalize: bool) -> dict:
+def expert_choice_routing(logits32, k: int, capacity_factor, renormalize: bool, round_scores: bool = True) -> dict:
     """Scores are the full softmax of the fp32 logits, rounded to fp32.  Expert
     e takes the C tokens of largest score (equal scores -> lower token index);
     its rows are those tokens in ascending order.  A token's weight for expert
     e is its score (divided by the sum of its scores over the experts that
     chose it when renormalising); tokens no expert chose get nothing.
+    round_scores=False keeps the fp64 scores (for differentiating the layer).
 
     Returns capacity, offsets[E+1], sorted_tokens[E*C] (row -> token),
     pos[T, E] (row of (t, e) or -1) and weight[T, E] (0 where not chosen)."""
     probs = softmax_rows(logits32)
-    s32 = probs.astype(np.float32)
+    s32 = probs.astype(np.float32) if round_scores else probs
     T, E = probs.shape
     C = expert_choice_capacity(T, k, E, capacity_factor) if T > 0 else 0
     pos = np.full((T, E), -1, dtype=np.int64)
@@ -394,16 +395,18 @@ def expert_choice_routing(logits32, k: int, capacity_factor, renormalize: bool) 
 
 def expert_choice_forward(x, W_g, bias, k: int, renormalize: bool, capacity_factor,
                           expert: ExpertFn, E: int, shared: Optional[Sequence[np.ndarray]] = None,
-                          tokens: Optional[Sequence[int]] = None, quant_x=None, quant_h=None) -> dict:
+                          tokens: Optional[Sequence[int]] = None, quant_x=None, quant_h=None,
+                          round_logits: bool = True) -> dict:
     """The layer with expert-choice routing: out[t] = sum over the experts that
     chose t, in ascending expert order, of weight[t, e] * FFN_e(x[t]), plus the
     shared expert.  Routing for every token; FFN and sum for `tokens`.
-    quant_x / quant_h as in forward()."""
+    quant_x / quant_h as in forward(); round_logits=False keeps the fp64
+    logits and scores (for differentiating the layer)."""
     qx = (lambda X: X) if quant_x is None else quant_x
     x = _f64(x)
     T = x.shape[0]
-    logits = router_logits(x, W_g, bias)
-    r = expert_choice_routing(logits, k, capacity_factor, renormalize)
+    logits = router_logits(x, W_g, bias, round_logits)
+    r = expert_choice_routing(logits, k, capacity_factor, renormalize, round_logits)
     toks = list(range(T)) if tokens is None else [int(t) for t in tokens]
     want = set(toks)
     y = {}
@@ -530,6 +533,83 @@ def backward(x, W_g, bias, k: int, renormalize: bool, capacity_factor, expert: E
     dx += dl @ W_g.T
     out = dict(dx=dx, dW_g=x.T @ dl, d_bias=dl.sum(axis=0), dW_gate=dWg_e, dW_up=dWu_e, dW_down=dWd_e,
                d_logits=dl, g=g, dWs_gate=None, dWs_up=None, dWs_down=None)
+    if shared is not None:
+        b = expert_ffn_backward(x, *shared, dout)
+        out["dx"] = dx + b["dX"]
+        out.update(dWs_gate=b["dW_gate"], dWs_up=b["dW_up"], dWs_down=b["dW_down"])
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Backward of the expert-choice layer.  Pages: "MoE Model Architectures",
+# Design Patterns, Pattern 3 "Expert Choice Routing" (the forward: experts
+# take their best tokens; a token's output sums the experts that took it) and
+# Switch Transformers "Top-1 Routing" (scores are the router softmax); the
+# backward pages as for token choice above.  The selection (which tokens each
+# expert took) is held fixed, as the top-k is for token choice; the fp32
+# rounding of the scores is differentiated as the identity.
+# ----------------------------------------------------------------------------
+def expert_choice_weights_backward(probs, pos, g, renormalize: bool) -> np.ndarray:
+    """dL/dlogits from g[t, e] = dL/dweight[t, e] of the experts that took t
+    (pos[t, e] >= 0).  renormalised: the weights are a softmax over the
+    logits of the experts that took t, so dl_e = w_e (g_e - sum_i g_i w_i)
+    for those experts and zero elsewhere; not renormalised: weight = p_e,
+    the softmax over all E logits, so dl_e = p_e ([e took t] g_e - sum_i g_i p_i)
+    for every e.  A token no expert took gets zero."""
+    p = _f64(probs)
+    T, E = p.shape
+    dl = np.zeros_like(p)
+    for t in range(T):
+        chosen = [e for e in range(E) if pos[t, e] >= 0]
+        if not chosen:
+            continue
+        if renormalize:
+            den = math.fsum(p[t, e] for e in chosen)
+            w = {e: p[t, e] / den for e in chosen}
+            s = math.fsum(g[t, e] * w[e] for e in chosen)
+            for e in chosen:
+                dl[t, e] = w[e] * (g[t, e] - s)
+        else:
+            s = math.fsum(g[t, e] * p[t, e] for e in chosen)
+            for e in range(E):
+                dl[t, e] = -p[t, e] * s
+            for e in chosen:
+                dl[t, e] += p[t, e] * g[t, e]
+    return dl
+
+
+def expert_choice_backward(x, W_g, bias, k: int, renormalize: bool, capacity_factor, expert: ExpertFn, E: int,
+                           shared: Optional[Sequence[np.ndarray]], dout, round_logits: bool = True) -> dict:
+    """Gradients of expert_choice_forward() for dL/dout = dout, with the keys
+    of backward(); g is [T, E] (dL/dweight[t, e], zero where e did not take t)."""
+    x, W_g, dout = _f64(x), _f64(W_g), _f64(dout)
+    T, d = x.shape
+    logits = router_logits(x, W_g, bias, round_logits)
+    probs = softmax_rows(logits)
+    r = expert_choice_routing(logits, k, capacity_factor, renormalize, round_logits)
+    f = _f64(expert(0)[0]).shape[1]
+    dx = np.zeros((T, d))
+    dWg_e = np.zeros((E, d, f))
+    dWu_e = np.zeros((E, d, f))
+    dWd_e = np.zeros((E, f, d))
+    g = np.zeros((T, E))
+    offs, st = r["offsets"], r["sorted_tokens"]
+    for e in range(E):
+        toks = [int(t) for t in st[offs[e]:offs[e + 1]]]
+        if not toks:
+            continue
+        Wg, Wu, Wd = expert(e)
+        Y = expert_ffn(x[toks], Wg, Wu, Wd)           # the unweighted expert outputs
+        wt = np.array([r["weight"][t, e] for t in toks])
+        b = expert_ffn_backward(x[toks], Wg, Wu, Wd, wt[:, None] * dout[toks])
+        dWg_e[e], dWu_e[e], dWd_e[e] = b["dW_gate"], b["dW_up"], b["dW_down"]
+        for i, t in enumerate(toks):
+            dx[t] += b["dX"][i]
+            g[t, e] = float(np.dot(dout[t], Y[i]))
+    dl = expert_choice_weights_backward(probs, r["pos"], g, renormalize)
+    dx += dl @ W_g.T
+    out = dict(dx=dx, dW_g=x.T @ dl, d_bias=dl.sum(axis=0), dW_gate=dWg_e, dW_up=dWu_e, dW_down=dWd_e,
+               d_logits=dl, g=g, dWs_gate=None, dWs_up=None, dWs_down=None, capacity=r["capacity"], pos=r["pos"])
     if shared is not None:
         b = expert_ffn_backward(x, *shared, dout)
         out["dx"] = dx + b["dX"]

@@ -985,3 +985,79 @@ def test_layer_backward_relabelling_permutes_expert_gradients():
     np.testing.assert_allclose(b2["dx"], b["dx"], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(b2["dW_g"], b["dW_g"][:, perm], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(b2["dW_down"], b["dW_down"][perm], rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Backward of the expert-choice layer
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("renorm,cf,shared", [(True, 1.0, False), (False, 1.0, True), (True, 1.5, True)])
+def test_ec_layer_backward_against_central_differences(renorm, cf, shared):
+    """Every gradient of the expert-choice layer (unrounded logits and scores)
+    against central differences of L = sum(dout * out); the layer has tokens
+    that no expert took and tokens that several experts took."""
+    T, d, E, k, f = 8, 5, 4, 1, 3
+    x, Wg, bias, ex, sh, dout = _bwd_layer(T, d, E, k, f, shared, seed=61 + int(renorm) + int(10 * cf))
+    run = lambda: oracle.expert_choice_forward(x, Wg, bias, k, renorm, cf, lambda e: ex[e], E, sh,
+                                               round_logits=False)
+    L = lambda: float((run()["out"] * dout).sum())
+    r0 = run()
+    taken = (r0["pos"] >= 0).sum(axis=1)
+    assert (taken == 0).any() and (taken >= 2).any()
+    b = oracle.expert_choice_backward(x, Wg, bias, k, renorm, cf, lambda e: ex[e], E, sh, dout, round_logits=False)
+    h, tol = 1e-5, dict(rtol=2e-5, atol=2e-7)
+    np.testing.assert_allclose(b["dx"], _fd(L, x, h), **tol)
+    np.testing.assert_allclose(b["dW_g"], _fd(L, Wg, h), **tol)
+    np.testing.assert_allclose(b["d_bias"], _fd(L, bias, h), **tol)
+    for e in range(E):
+        for key, m in (("dW_gate", 0), ("dW_up", 1), ("dW_down", 2)):
+            np.testing.assert_allclose(b[key][e], _fd(L, ex[e][m], h), **tol)
+    if shared:
+        for key, m in (("dWs_gate", 0), ("dWs_up", 1), ("dWs_down", 2)):
+            np.testing.assert_allclose(b[key], _fd(L, sh[m], h), **tol)
+    assert np.array_equal(run()["pos"], r0["pos"])      # the selection did not move
+    assert np.all(b["g"][r0["pos"] < 0] == 0.0)
+    assert np.all(b["d_logits"][taken == 0] == 0.0)       # untaken tokens: no router gradient
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+def test_ec_backward_against_torch_autograd_gather_all_form(renorm):
+    """The expert-choice backward equals torch autograd of the run-every-expert
+    form (weight zero where the expert did not take the token), rounded logits."""
+    T, d, E, k, f = 11, 6, 5, 2, 4
+    x, Wg, bias, ex, sh, dout = _bwd_layer(T, d, E, k, f, True, seed=71 + int(renorm))
+    cf = 0.8
+    r = oracle.expert_choice_forward(x, Wg, bias, k, renorm, cf, lambda e: ex[e], E, sh)
+    b = oracle.expert_choice_backward(x, Wg, bias, k, renorm, cf, lambda e: ex[e], E, sh, dout)
+    mask = torch.from_numpy((r["pos"] >= 0).astype(np.float64))
+    tt = lambda a: torch.from_numpy(np.array(a, dtype=np.float64)).requires_grad_(True)
+    xt, Wgt, bt = tt(x), tt(Wg), tt(bias)
+    ext = [[tt(m) for m in trip] for trip in ex]
+    sht = [tt(m) for m in sh]
+    p = torch.softmax(xt @ Wgt + bt, dim=1) * mask
+    w = p / p.sum(dim=1, keepdim=True).clamp_min(1e-300) if renorm else p
+    ffn = lambda X, a, b_, c: (torch.nn.functional.silu(X @ a) * (X @ b_)) @ c
+    out = sum(w[:, e:e + 1] * ffn(xt, *ext[e]) for e in range(E)) + ffn(xt, *sht)
+    (out * torch.from_numpy(dout)).sum().backward()
+    np.testing.assert_allclose(out.detach().numpy(), r["out"], rtol=1e-6, atol=1e-6)   # fp32 scores vs fp64
+    tol = dict(rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(b["dx"], xt.grad.numpy(), **tol)
+    np.testing.assert_allclose(b["dW_g"], Wgt.grad.numpy(), **tol)
+    np.testing.assert_allclose(b["d_bias"], bt.grad.numpy(), **tol)
+    for e in range(E):
+        for key, m in (("dW_gate", 0), ("dW_up", 1), ("dW_down", 2)):
+            np.testing.assert_allclose(b[key][e], ext[e][m].grad.numpy(), **tol)
+    for key, m in (("dWs_gate", 0), ("dWs_up", 1), ("dWs_down", 2)):
+        np.testing.assert_allclose(b[key], sht[m].grad.numpy(), **tol)
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+def test_ec_backward_with_every_token_taken_is_the_token_choice_backward_with_k_equal_E(renorm):
+    """C = T: every expert takes every token, so the layer is the token-choice
+    layer with k = E (every expert chosen, no capacity) and both backwards agree."""
+    T, d, E, f = 6, 5, 3, 4
+    x, Wg, bias, ex, sh, dout = _bwd_layer(T, d, E, E, f, True, seed=81 + int(renorm))
+    ec = oracle.expert_choice_backward(x, Wg, bias, E, renorm, 1.0, lambda e: ex[e], E, sh, dout, round_logits=False)
+    assert ec["capacity"] == T and (ec["pos"] >= 0).all()
+    tc = oracle.backward(x, Wg, bias, E, renorm, 0.0, lambda e: ex[e], E, sh, dout, round_logits=False)
+    for key in ("dx", "dW_g", "d_bias", "dW_gate", "dW_up", "dW_down", "dWs_gate", "dWs_up", "dWs_down", "d_logits"):
+        np.testing.assert_allclose(ec[key], tc[key], rtol=1e-12, atol=1e-13, err_msg=key)
