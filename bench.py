@@ -208,9 +208,10 @@ def bench_backward(args, cfg):
     steps = args.steps if args.steps is not None else 10
     warmup = args.warmup if args.warmup is not None else 3
     print(f"[bench] backward workload={cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} f={cfg.f} "
-          f"steps={steps} warmup={warmup}", file=sys.stderr, flush=True)
+          f"routing={args.routing} steps={steps} warmup={warmup}", file=sys.stderr, flush=True)
     inp = synth.make_inputs(cfg, "cuda")
-    desc = ops.desc_from_cfg(cfg)
+    ec = args.routing == "expert"
+    desc = ops.desc_from_cfg(cfg, routing=ops.ROUTING_EXPERT_CHOICE if ec else ops.ROUTING_TOKEN_CHOICE)
     w = ops.weights_struct(inp)
     gen = torch.Generator(device="cpu").manual_seed(7)
     dout = torch.randn((cfg.T, cfg.d), generator=gen).to(torch.bfloat16).cuda()
@@ -269,7 +270,9 @@ def bench_backward(args, cfg):
         achieved = kbytes / t / 1e9 if have_k else None
     roof = {"bound": bound, "achieved": round(achieved, 2) if have_k else None, "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4) if have_k else None,
-            "traffic": measured_traffic("bwd_dx_gemm", cfg.name), "kernel": "bwd_rows_kernel<NTS> (dX)",
+            # the stored counters cover token-choice routing only
+            "traffic": None if ec else measured_traffic("bwd_dx_gemm", cfg.name),
+            "kernel": "bwd_rows_kernel<NTS> (dX)",
             "kernel_ms": round(kern_ms, 5) if have_k else None, "alg_flops": int(kflops), "alg_bytes": int(kbytes),
             "mfma_frac": round(kflops / t / 1e12 / BF16_PEAK_TFLOPS, 4) if have_k else None,
             "hbm_frac": round(kbytes / t / 1e9 / HBM_PEAK_GBS, 4) if have_k else None}
@@ -281,7 +284,7 @@ def bench_backward(args, cfg):
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle's backward", file=sys.stderr, flush=True)
-        cpu = cpu_baseline_backward(cfg, inp, dout)
+        cpu = cpu_baseline_backward(cfg, inp, dout, ec)
     line = {
         "metric": "MoE-layer backward tokens/s (dL/dx and all weight gradients)",
         "value": round(cfg.T * steps / (total_ms / 1e3), 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
@@ -289,7 +292,8 @@ def bench_backward(args, cfg):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) activations and dout, "
         "N(0,0.02) weights)",
         "config": {"workload": cfg.name, "pass": "backward", "T": cfg.T, "d": cfg.d, "E": cfg.E, "top_k": cfg.k,
-                   "f": cfg.f, "shared_expert": cfg.shared, "capacity_factor": cfg.capacity_factor},
+                   "f": cfg.f, "shared_expert": cfg.shared, "capacity_factor": cfg.capacity_factor,
+                   "routing": args.routing},
         "layer": {"alg_flops": int(flops), "tflops": round(flops / (ms / 1e3) / 1e12, 2)},
         "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
@@ -345,8 +349,9 @@ def bench_library_gemm(args, cfg):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline_backward(cfg, inp, dout, budget_s=12.0, max_calls=200):
-    """The oracle's backward, as it stands, on calls of a few tokens of the workload."""
+def cpu_baseline_backward(cfg, inp, dout, ec=False, budget_s=12.0, max_calls=200):
+    """The oracle's backward, as it stands, on calls of a few tokens of the
+    workload (expert choice: the selection among those tokens)."""
     import numpy as np
     import oracle
     import torch
@@ -366,8 +371,9 @@ def cpu_baseline_backward(cfg, inp, dout, budget_s=12.0, max_calls=200):
         return cache[e]
     shared = (to64(inp["Ws_gate"]), to64(inp["Ws_up"]), to64(inp["Ws_down"])) if cfg.shared else None
     tb = min(cfg.T, 4)
-    call = lambda t0: oracle.backward(x[t0:t0 + tb], W_g, bias, cfg.k, cfg.renormalize,
-                                      np.float32(cfg.capacity_factor), expert, cfg.E, shared, d64[t0:t0 + tb])
+    fn = oracle.expert_choice_backward if ec else oracle.backward
+    call = lambda t0: fn(x[t0:t0 + tb], W_g, bias, cfg.k, cfg.renormalize, np.float32(cfg.capacity_factor), expert,
+                         cfg.E, shared, d64[t0:t0 + tb])
     call(0)
     n = 0
     t_start = time.perf_counter()
@@ -376,8 +382,8 @@ def cpu_baseline_backward(cfg, inp, dout, budget_s=12.0, max_calls=200):
         n += 1
     dt = time.perf_counter() - t_start
     return {"value": n * tb / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} oracle backward calls of {tb} tokens each of the {cfg.name} workload "
-                      f"(routing, fp64 expert and router gradients), {dt:.1f} s"}
+            "sample": f"{n} oracle {'expert-choice ' if ec else ''}backward calls of {tb} tokens each of the "
+                      f"{cfg.name} workload (routing, fp64 expert and router gradients), {dt:.1f} s"}
 
 
 def measure(args, cfg, steps=None, warmup=None, cpu=True, graph=True, copy_calibration=False):

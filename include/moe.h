@@ -281,17 +281,21 @@ typedef struct {
  * not supported by the backward). */
 size_t moe_backward_workspace_size(const moe_desc* desc);
 
-/* Backward of moe_forward for token-choice layers with bf16 activations and
- * bf16 weights: given dout = dL/dout [T, d] (bf16), the gradients of L with
- * respect to x, the router weight and bias, and every expert's (and the
- * shared expert's) three matrices.  The expert selection (top-k, capacity)
- * is held fixed: gradients flow through the routing weights (the softmax and
- * its renormalisation over the chosen experts) and through the chosen
- * experts' SwiGLU FFNs; dropped assignments carry no gradient; experts that
- * received no token get zero gradients.  The routing and the expert
- * activations are recomputed from x (nothing is kept from the forward).
- * Weight gradients are summed over each expert's tokens in a fixed order
- * without atomics: results are bitwise reproducible.  Pages: "Testing using
+/* Backward of moe_forward for layers with bf16 activations and bf16 weights,
+ * token-choice or expert-choice routing: given dout = dL/dout [T, d] (bf16),
+ * the gradients of L with respect to x, the router weight and bias, and every
+ * expert's (and the shared expert's) three matrices.  The expert selection
+ * (top-k, capacity) is held fixed: gradients flow through the routing weights
+ * (the softmax and its renormalisation over the chosen experts) and through
+ * the chosen experts' SwiGLU FFNs; dropped assignments carry no gradient;
+ * experts that received no token get zero gradients.  Expert choice ("MoE
+ * Model Architectures", Design Patterns, Pattern 3): the tokens each expert
+ * took are held fixed; a token's routing gradient runs over the experts that
+ * took it (the full softmax, or its renormalisation over those experts), and
+ * a token no expert took gets only the shared expert's gradient.  The routing
+ * and the expert activations are recomputed from x (nothing is kept from the
+ * forward).  Weight gradients are summed over each expert's tokens in a fixed
+ * order without atomics: results are bitwise reproducible.  Pages: "Testing using
  * claude to graft ETHOS onto modded-nanogpt base", "Key Implementation
  * Details" (a backward that recomputes the forward values and accumulates each
  * weight gradient over the tokens that chose the expert); "Faster writing:
@@ -299,7 +303,7 @@ size_t moe_backward_workspace_size(const moe_desc* desc);
  * gradients of the chosen-experts dispatch).
  *   x, dout  [T, d] bf16;  w as for moe_forward;  grads as documented above
  *   ws       moe_backward_workspace_size(desc) bytes, 256-byte aligned
- * Returns MOE_ERR_UNSUPPORTED for other dtypes or expert-choice routing.
+ * Returns MOE_ERR_UNSUPPORTED for other dtypes.
  * T == 0 writes zero weight gradients. */
 moe_status moe_backward(const moe_desc* desc, const void* x, const moe_weights* w, const void* dout,
                         const moe_grads* grads, void* ws, size_t ws_bytes, hipStream_t stream);

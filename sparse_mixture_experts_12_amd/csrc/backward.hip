@@ -20,6 +20,12 @@
 //                  else         -> dl_e = p_e ([e chosen] g(e) - sum_j g_j p_(e_j))
 //   dx_t = sum_j [kept] (dG_r W_gate^T + dU_r W_up^T) + (shared expert's) + dl_t W_g^T
 //   dW_g = x^T dl, d_bias = sum_t dl_t
+// Expert-choice layers ("MoE Model Architectures", Design Patterns, Pattern 3)
+// differ only in where the rows come from: expert e's C rows are the tokens it
+// took, a token's slots are the experts that took it (0 to E of them, listed
+// in ascending expert order), and the same two router formulas apply over
+// that list (renormalised: a softmax over the experts that took the token;
+// else the full softmax).
 // Every sum runs in a fixed order: the result is bitwise reproducible.
 #include "common.h"
 #include "kernels.h"
@@ -83,6 +89,58 @@ __global__ __launch_bounds__(256) void pad_rows_kernel(const int32_t* __restrict
         const int a = sorted_assign[offsets[lo] + local];
         tok = a / k;
         wt = topk_w[a];
+      }
+    } else if (local < T) {
+      tok = local;
+      wt = 1.f;
+    }
+  }
+  ptok[p] = tok;
+  pw[p] = wt;
+}
+
+// Expert choice: per padded row its token (the expert's row r holds token
+// sorted_tokens[r]) and the token's combine weight for that expert (its list
+// entry for row r); per token list entry i < ccount[t] (rows crow[t E + i],
+// expert crow / C) its padded row, -1 past the list.
+__global__ __launch_bounds__(256) void pad_rows_ec_kernel(const int32_t* __restrict__ poff,
+                                                          const int32_t* __restrict__ offsets,
+                                                          const int32_t* __restrict__ sorted_tokens,
+                                                          const int32_t* __restrict__ crow,
+                                                          const float* __restrict__ cw,
+                                                          const int32_t* __restrict__ ccount, int C, int E, int G,
+                                                          int T, int pmax, int32_t* __restrict__ ptok,
+                                                          float* __restrict__ pw, int32_t* __restrict__ apos) {
+  const long p = (long)blockIdx.x * 256 + threadIdx.x;
+  if (p < (long)T * E) {
+    const int t = (int)(p / E), i = (int)(p - (long)t * E);
+    int v = -1;
+    if (i < ccount[t]) {
+      const int r = crow[p];
+      const int e = r / C;
+      v = poff[e] + (r - e * C);
+    }
+    apos[p] = v;
+  }
+  if (p >= pmax) return;
+  int tok = -1;
+  float wt = 0.f;
+  if (p < poff[G]) {
+    int lo = 0, hi = G;                             // largest g with poff[g] <= p
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (poff[mid] <= p) lo = mid;
+      else hi = mid;
+    }
+    const int local = (int)p - poff[lo];
+    if (lo < E) {
+      if (local < offsets[lo + 1] - offsets[lo]) {
+        const int r = offsets[lo] + local;
+        tok = sorted_tokens[r];
+        const int n = ccount[tok];
+        const size_t b = (size_t)tok * E;
+        for (int i = 0; i < n; ++i)
+          if (crow[b + i] == r) wt = cw[b + i];
       }
     } else if (local < T) {
       tok = local;
@@ -220,6 +278,78 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
   }
 }
 
+// Expert choice, one wave per token: s = sum over the token's list (ascending
+// experts) of g w, then for every expert e
+//   renormalised: dl_e = w_e (g_e - s) if e took the token, else 0
+//   otherwise:    dl_e = p_e (g_e - s) with g_e = 0 if e did not take it
+// (w_e, the forward's combine weight, is the padded row's pw; p_e the score).
+__global__ __launch_bounds__(256) void router_bwd_ec_kernel(const float* __restrict__ scores,
+                                                            const int32_t* __restrict__ pos,
+                                                            const int32_t* __restrict__ crow,
+                                                            const int32_t* __restrict__ ccount,
+                                                            const int32_t* __restrict__ poff,
+                                                            const float* __restrict__ gsc,
+                                                            const float* __restrict__ pw, int T, int E, int C,
+                                                            int renorm, float* __restrict__ dl) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const size_t b = (size_t)t * E;
+  const int n = ccount[t];
+  float s = 0.f;
+  for (int i = lane; i < n; i += 64) {
+    const int r = crow[b + i];
+    const int e = r / C;
+    const int pp = poff[e] + (r - e * C);
+    s += gsc[pp] * pw[pp];
+  }
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  s = __shfl(s, 0);
+  for (int e = lane; e < E; e += 64) {
+    const int r = pos[b + e];
+    float g = 0.f, w = 0.f;
+    if (r >= 0) {
+      const int pp = poff[e] + (r - e * C);
+      g = gsc[pp];
+      w = pw[pp];
+    }
+    float v;
+    if (renorm) v = r >= 0 ? w * (g - s) : 0.f;
+    else v = scores[(size_t)e * T + t] * (g - s);
+    dl[b + e] = v;
+  }
+}
+
+// Expert choice: dx[t, c] = sum over the token's list of dXp[its padded row, c]
+//   + dXp[shared row of t, c] + sum_e dl[t, e] W_g[c, e]   (fp32, in this order;
+// renormalised: dl is zero off the token's list, so only the list is summed)
+template <bool SPARSE>
+__global__ __launch_bounds__(256) void dx_ec_kernel(const float* __restrict__ dXp, const int32_t* __restrict__ apos,
+                                                    const int32_t* __restrict__ poff, const float* __restrict__ dl,
+                                                    const int32_t* __restrict__ crow,
+                                                    const int32_t* __restrict__ ccount, int C,
+                                                    const bf16_t* __restrict__ Wg, int T, int d, int E,
+                                                    int has_shared, float* __restrict__ dx) {
+  const int t = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= d) return;
+  const size_t b = (size_t)t * E;
+  const int n = ccount[t];
+  float acc = 0.f;
+  for (int i = 0; i < n; ++i) acc += dXp[(size_t)apos[b + i] * d + c];
+  if (has_shared) acc += dXp[(size_t)(poff[E] + t) * d + c];
+  float r = 0.f;
+  if (SPARSE) {
+    for (int i = 0; i < n; ++i) {
+      const int e = crow[b + i] / C;
+      r = __fmaf_rn(dl[b + e], bf16_to_f32(Wg[(size_t)c * E + e]), r);
+    }
+  } else {
+    for (int e = 0; e < E; ++e) r = __fmaf_rn(dl[b + e], bf16_to_f32(Wg[(size_t)c * E + e]), r);
+  }
+  dx[(size_t)t * d + c] = acc + r;
+}
+
 // dx[t, c] = sum_j [kept] dXp[apos[t k + j], c] + dXp[shared row of t, c]
 //            + sum_e dl[t, e] W_g[c, e]       (fp32, in this order)
 template <bool SPARSE>
@@ -346,15 +476,15 @@ size_t backward_dx_part_bytes(int d, int f, int G) {
   return (size_t)(ks - 1) * (size_t)G * ((d + 255) / 256) * 128 * 256 * sizeof(float);
 }
 
-long backward_pad_rows(int T, int E, int k, int has_shared) {
-  const long routed = (long)T * k + (long)(kPadRows - 1) * E;
+long backward_pad_rows(long routed, int T, int E, int has_shared) {
+  const long padded = routed + (long)(kPadRows - 1) * E;
   const long shared = has_shared ? ((long)T + kPadRows - 1) / kPadRows * kPadRows : 0;
-  return (routed + shared + 63) / 64 * 64;
+  return (padded + shared + 63) / 64 * 64;
 }
 
-size_t backward_sched_ints(int T, int E, int k, int has_shared) {
+size_t backward_sched_ints(long routed, int T, int E, int has_shared) {
   const int G = E + (has_shared ? 1 : 0);
-  const long pmax = backward_pad_rows(T, E, k, has_shared);
+  const long pmax = backward_pad_rows(routed, T, E, has_shared);
   return kSchedHead + 4 * (size_t)grouped_max_row_tiles((int)pmax, 0, G, 0, 64) + 4 * (size_t)(G + 1) + 16;
 }
 
@@ -367,12 +497,19 @@ hipError_t launch_zero(float* p, long n, hipStream_t s) {
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
   hipError_t err;
   const int G = a.E + (a.has_shared ? 1 : 0);
-  const long pmax = backward_pad_rows(a.T, a.E, a.k, a.has_shared);
+  const bool ec = a.ec_C > 0;
+  const long pmax = backward_pad_rows(a.routed, a.T, a.E, a.has_shared);
   pad_offsets_kernel<<<1, 1024, 0, s>>>(a.offsets, a.E, a.has_shared ? a.T : 0, a.poff);
-  const long npr = pmax > (long)a.T * a.k ? pmax : (long)a.T * a.k;
-  pad_rows_kernel<<<(unsigned)((npr + 255) / 256), 256, 0, s>>>(a.poff, a.offsets, a.sorted_assign, a.inv_perm,
-                                                                 a.topk_idx, a.topk_w, a.E, G, a.k, a.T, (int)pmax,
-                                                                 a.ptok, a.pw, a.apos);
+  const long nslot = ec ? (long)a.T * a.E : (long)a.T * a.k;
+  const long npr = pmax > nslot ? pmax : nslot;
+  if (ec)
+    pad_rows_ec_kernel<<<(unsigned)((npr + 255) / 256), 256, 0, s>>>(a.poff, a.offsets, a.sorted_assign, a.ec_crow,
+                                                                      a.ec_w, a.ec_count, a.ec_C, a.E, G, a.T,
+                                                                      (int)pmax, a.ptok, a.pw, a.apos);
+  else
+    pad_rows_kernel<<<(unsigned)((npr + 255) / 256), 256, 0, s>>>(a.poff, a.offsets, a.sorted_assign, a.inv_perm,
+                                                                   a.topk_idx, a.topk_w, a.E, G, a.k, a.T, (int)pmax,
+                                                                   a.ptok, a.pw, a.apos);
   gather_rows_kernel<<<(unsigned)((pmax * (a.d / 8) + 255) / 256), 256, 0, s>>>(
       (const bf16_t*)a.x, (const bf16_t*)a.dout, a.ptok, (int)pmax, a.d, a.Xp, a.Dp);
   if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -439,15 +576,26 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
     if ((err = launch_bwd_wgrad(r, s)) != hipSuccess) return err;
   }
   // 6. router: dL/dlogits, then dx, dW_g, d_bias
-  router_bwd_kernel<<<(a.T + 3) / 4, 256, 0, s>>>(a.logits, a.topk_idx, a.topk_w, a.apos, a.gsc, a.T, a.E, a.k,
-                                                  a.renormalize, a.dl);
   const dim3 gx((a.d + 255) / 256, a.T);
-  if (a.renormalize)
-    dx_kernel<true><<<gx, 256, 0, s>>>(a.dXp, a.apos, a.poff, a.dl, a.topk_idx, (const bf16_t*)a.W_g, a.T, a.d, a.E,
-                                       a.k, a.has_shared, a.dx);
-  else
-    dx_kernel<false><<<gx, 256, 0, s>>>(a.dXp, a.apos, a.poff, a.dl, a.topk_idx, (const bf16_t*)a.W_g, a.T, a.d,
-                                        a.E, a.k, a.has_shared, a.dx);
+  if (ec) {
+    router_bwd_ec_kernel<<<(a.T + 3) / 4, 256, 0, s>>>(a.ec_scores, a.ec_pos, a.ec_crow, a.ec_count, a.poff, a.gsc,
+                                                       a.pw, a.T, a.E, a.ec_C, a.renormalize, a.dl);
+    if (a.renormalize)
+      dx_ec_kernel<true><<<gx, 256, 0, s>>>(a.dXp, a.apos, a.poff, a.dl, a.ec_crow, a.ec_count, a.ec_C,
+                                            (const bf16_t*)a.W_g, a.T, a.d, a.E, a.has_shared, a.dx);
+    else
+      dx_ec_kernel<false><<<gx, 256, 0, s>>>(a.dXp, a.apos, a.poff, a.dl, a.ec_crow, a.ec_count, a.ec_C,
+                                             (const bf16_t*)a.W_g, a.T, a.d, a.E, a.has_shared, a.dx);
+  } else {
+    router_bwd_kernel<<<(a.T + 3) / 4, 256, 0, s>>>(a.logits, a.topk_idx, a.topk_w, a.apos, a.gsc, a.T, a.E, a.k,
+                                                    a.renormalize, a.dl);
+    if (a.renormalize)
+      dx_kernel<true><<<gx, 256, 0, s>>>(a.dXp, a.apos, a.poff, a.dl, a.topk_idx, (const bf16_t*)a.W_g, a.T, a.d,
+                                         a.E, a.k, a.has_shared, a.dx);
+    else
+      dx_kernel<false><<<gx, 256, 0, s>>>(a.dXp, a.apos, a.poff, a.dl, a.topk_idx, (const bf16_t*)a.W_g, a.T, a.d,
+                                          a.E, a.k, a.has_shared, a.dx);
+  }
   const int nchunk = (a.T + kRwChunk - 1) / kRwChunk;
   router_wgrad_partial_kernel<<<dim3((a.d + 1 + 255) / 256, (a.E + 15) / 16, nchunk), 256, 0, s>>>(
       (const bf16_t*)a.x, a.dl, a.T, a.d, a.E, a.rw_part);

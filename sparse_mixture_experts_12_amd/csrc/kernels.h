@@ -177,18 +177,26 @@ struct BackwardArgs {
   const void* W_g;               // [d, E] bf16
   ExpertWeights w;
   int T, d, E, k, f, has_shared, renormalize;
+  long routed;                   // routed rows: T k (token choice) or E C (expert choice)
   // forward routing (recomputed by the caller)
   const float* logits;           // [T, E]
-  const int32_t* topk_idx;       // [T, k]
-  const float* topk_w;           // [T, k]
+  const int32_t* topk_idx;       // [T, k]   (token choice)
+  const float* topk_w;           // [T, k]   (token choice)
   const int32_t* offsets;        // [E + 1]
-  const int32_t* sorted_assign;  // [T k]
-  const int32_t* inv_perm;       // [T k]
+  const int32_t* sorted_assign;  // [T k] assignment per row; expert choice: [E C] token per row
+  const int32_t* inv_perm;       // [T k]   (token choice)
+  // expert choice (ec_C > 0): the selection of launch_expert_choice
+  int ec_C;
+  const float* ec_scores;        // [E, T] full-softmax scores
+  const int32_t* ec_pos;         // [T, E] row of (t, e) or -1
+  const int32_t* ec_crow;        // [T, E] per token: rows of its experts, ascending expert order
+  const float* ec_w;             // [T, E] the matching combine weights
+  const int32_t* ec_count;       // [T] experts that took the token
   // scratch (padded row space of backward_pad_rows rows)
   int32_t* poff;                 // [G + 1]
   int32_t* ptok;                 // [P]
   float* pw;                     // [P]
-  int32_t* apos;                 // [T k]
+  int32_t* apos;                 // [T k]; expert choice: [T, E] per token list entry
   float* gsc;                    // [P]
   int32_t* sched;                // backward_sched_ints
   bf16_t *Xp, *Dp;               // [P, d]
@@ -202,8 +210,8 @@ struct BackwardArgs {
   float *dx, *dW_g, *d_bias, *dW_gate, *dW_up, *dW_down, *dWs_gate, *dWs_up, *dWs_down;
   hipEvent_t ev_begin, ev_end;
 };
-long backward_pad_rows(int T, int E, int k, int has_shared);
-size_t backward_sched_ints(int T, int E, int k, int has_shared);
+long backward_pad_rows(long routed, int T, int E, int has_shared);
+size_t backward_sched_ints(long routed, int T, int E, int has_shared);
 size_t router_wgrad_ws_bytes(int T, int d, int E);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
 hipError_t launch_zero(float* p, long n, hipStream_t s);

@@ -558,8 +558,7 @@ moe_status check_backward_desc(const moe_desc* d) {
   if (st != MOE_OK) return st;
   if (d->act_dtype != MOE_BF16 || d->w_dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "the backward takes bf16 activations and bf16 weights");
-  if (expert_choice(d)) return fail(MOE_ERR_UNSUPPORTED, "the backward covers token-choice routing");
-  const double P = (double)backward_pad_rows(d->T, d->E, d->top_k, d->has_shared);
+  const double P = (double)backward_pad_rows((long)routed_rows_of(d), d->T, d->E, d->has_shared);
   if (P * (d->f > d->d ? d->f : d->d) >= 2147483648.0)
     return fail(MOE_ERR_UNSUPPORTED, "layer too large for the backward (padded rows * max(d, f) >= 2^31)");
   return MOE_OK;
@@ -567,13 +566,16 @@ moe_status check_backward_desc(const moe_desc* d) {
 
 struct BwdLayout {
   size_t part, idx, w, logits, counts, offsets, sorted, inv, ndrop, rank;
+  size_t ec_scores, ec_pos, ec_w, ec_crow, ec_count;
   size_t poff, ptok, pw, apos, gsc, sched, Xp, Dp, G, U, dH, dG, dU, Hw, dXp, dl, rw, dxp, total;
 };
 
 BwdLayout bwd_layout_of(const moe_desc* d) {
   BwdLayout L{};
   const size_t T = d->T, k = d->top_k, E = d->E, D = d->d, F = d->f;
-  const size_t P = (size_t)backward_pad_rows(d->T, d->E, d->top_k, d->has_shared);
+  const bool ec = expert_choice(d);
+  const size_t routed = routed_rows_of(d);
+  const size_t P = (size_t)backward_pad_rows((long)routed, d->T, d->E, d->has_shared);
   const size_t Gn = E + (d->has_shared ? 1 : 0);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -587,16 +589,21 @@ BwdLayout bwd_layout_of(const moe_desc* d) {
   L.logits = take(T * E * 4);
   L.counts = take(E * 4);
   L.offsets = take((E + 1) * 4);
-  L.sorted = take(T * k * 4);
-  L.inv = take(T * k * 4);
+  L.sorted = take(routed * 4);                      // expert choice: the token of every row
+  L.inv = take(ec ? 0 : T * k * 4);
   L.ndrop = take(4);
-  L.rank = take(permute_ws_bytes(d->T * d->top_k, d->E));
+  L.rank = take(ec ? 0 : permute_ws_bytes(d->T * d->top_k, d->E));
+  L.ec_scores = take(ec ? E * T * 4 : 0);
+  L.ec_pos = take(ec ? T * E * 4 : 0);
+  L.ec_w = take(ec ? T * E * 4 : 0);
+  L.ec_crow = take(ec ? T * E * 4 : 0);
+  L.ec_count = take(ec ? T * 4 : 0);
   L.poff = take((Gn + 1) * 4);
   L.ptok = take(P * 4);
   L.pw = take(P * 4);
-  L.apos = take(T * k * 4);
+  L.apos = take((ec ? T * E : T * k) * 4);
   L.gsc = take(P * 4);
-  L.sched = take(backward_sched_ints(d->T, d->E, d->top_k, d->has_shared) * 4);
+  L.sched = take(backward_sched_ints((long)routed, d->T, d->E, d->has_shared) * 4);
   L.Xp = take(P * D * 2);
   L.Dp = take(P * D * 2);
   L.G = take(P * F * 4);
@@ -668,13 +675,29 @@ moe_status moe_backward(const moe_desc* desc, const void* x, const moe_weights* 
   int32_t* offsets = (int32_t*)(base + L.offsets);
   int32_t* sorted = (int32_t*)(base + L.sorted);
   int32_t* inv = (int32_t*)(base + L.inv);
-  if ((st = do_permute(desc, idx, (int32_t*)(base + L.counts), offsets, sorted, inv, (int32_t*)(base + L.ndrop),
-                       (int32_t*)(base + L.rank), stream)) != MOE_OK)
-    return st;
   BackwardArgs a{};
+  if (expert_choice(desc)) {                      // the forward's selection, recomputed
+    ExpertChoiceArgs e{};
+    e.logits = logits; e.T = desc->T; e.E = desc->E; e.C = ec_capacity_of(desc); e.renormalize = desc->renormalize;
+    e.scores = (float*)(base + L.ec_scores);
+    e.pos = (int32_t*)(base + L.ec_pos);
+    e.w = (float*)(base + L.ec_w);
+    e.crow = (int32_t*)(base + L.ec_crow);
+    e.ccount = (int32_t*)(base + L.ec_count);
+    e.sorted_tokens = sorted;
+    e.offsets = offsets;
+    e.counts = nullptr;
+    e.n_unchosen = (int32_t*)(base + L.ndrop);
+    if ((st = hip_status(launch_expert_choice(e, stream), "expert choice")) != MOE_OK) return st;
+    a.ec_C = e.C; a.ec_scores = e.scores; a.ec_pos = e.pos; a.ec_crow = e.crow; a.ec_w = e.w; a.ec_count = e.ccount;
+  } else if ((st = do_permute(desc, idx, (int32_t*)(base + L.counts), offsets, sorted, inv,
+                              (int32_t*)(base + L.ndrop), (int32_t*)(base + L.rank), stream)) != MOE_OK) {
+    return st;
+  }
   a.x = x; a.dout = dout; a.W_g = w->W_g; a.w = expert_weights(w);
   a.T = desc->T; a.d = desc->d; a.E = desc->E; a.k = desc->top_k; a.f = desc->f;
   a.has_shared = desc->has_shared; a.renormalize = desc->renormalize;
+  a.routed = (long)routed_rows_of(desc);
   a.logits = logits; a.topk_idx = idx; a.topk_w = tw; a.offsets = offsets; a.sorted_assign = sorted; a.inv_perm = inv;
   a.poff = (int32_t*)(base + L.poff); a.ptok = (int32_t*)(base + L.ptok); a.pw = (float*)(base + L.pw);
   a.apos = (int32_t*)(base + L.apos); a.gsc = (float*)(base + L.gsc); a.sched = (int32_t*)(base + L.sched);

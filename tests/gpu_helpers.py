@@ -103,3 +103,25 @@ def assert_close(got, ref, tol, what=""):
 def device_inputs(cfg: synth.MoEConfig, router_only=False) -> dict:
     print(f"[inputs] {cfg}", flush=True)
     return synth.make_inputs(cfg, "cuda", router_only=router_only)
+
+
+def ec_boundary_is_clear(ref):
+    """The C-th and (C+1)-th scores of every expert are distinct fp32 values whose
+    fp64 sources are far (relatively 1e-12) from an fp32 rounding midpoint, so a
+    different fp64 summation order cannot change any selection."""
+    probs = oracle.softmax_rows(ref["logits"])
+    s32 = ref["scores"]
+    T, E = s32.shape
+    Cap = ref["capacity"]
+    if Cap >= T:
+        return True
+    for e in range(E):
+        order = sorted(range(T), key=lambda t: (-float(s32[t, e]), t))
+        for t in order[Cap - 1:Cap + 1]:
+            p = probs[t, e]
+            lo = np.float32(p)
+            nb = np.nextafter(lo, np.float32(np.inf if p > lo else -np.inf))
+            mid = (float(lo) + float(nb)) / 2.0
+            if abs(p - mid) <= 1e-12 * abs(p):
+                return False
+    return True

@@ -231,9 +231,17 @@ def test_backward_validation(ops):
         d = ops.make_desc(40, 256, 8, 2, 256, act=act, wdt=wdt)
         assert bwd(d) == ops.MOE_ERR_UNSUPPORTED, wdt
         assert ops.backward_workspace_size(d) == 0
+    # expert choice: bf16 layers are taken; the padded row space holds E C rows
     d = ops.make_desc(40, 256, 8, 2, 256)
     d.routing = ops.ROUTING_EXPERT_CHOICE
-    assert bwd(d) == ops.MOE_ERR_UNSUPPORTED and "token-choice" in ops.last_error()
+    assert bwd(d) == ops.MOE_ERR_INVALID_ARG and "dW_g" in ops.last_error()
+    tc = ops.make_desc(40, 256, 8, 2, 256, capacity_factor=4.0)
+    ec = ops.make_desc(40, 256, 8, 2, 256, capacity_factor=4.0)       # C = T = 40: 320 rows, T k = 80
+    ec.routing = ops.ROUTING_EXPERT_CHOICE
+    assert ops.backward_workspace_size(ec) > ops.backward_workspace_size(tc) > 0
+    ec8 = ops.make_desc(40, 256, 8, 2, 256, wdt="fp8")
+    ec8.routing = ops.ROUTING_EXPERT_CHOICE
+    assert bwd(ec8) == ops.MOE_ERR_UNSUPPORTED and ops.backward_workspace_size(ec8) == 0
     d = ops.make_desc(40, 256, 8, 2, 256)
     assert ops.backward_workspace_size(d) > ops.workspace_size(d)
     assert bwd(d) == ops.MOE_ERR_INVALID_ARG and "dW_g" in ops.last_error()

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import OracleInputs, assert_close, device_inputs, to64
+from gpu_helpers import OracleInputs, assert_close, device_inputs, ec_boundary_is_clear, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -105,9 +105,9 @@ def _alloc_grads(cfg):
     return g
 
 
-def run_backward(inp, dout):
+def run_backward(inp, dout, routing=None):
     cfg = inp["cfg"]
-    desc = ops.desc_from_cfg(cfg)
+    desc = ops.desc_from_cfg(cfg, routing=ops.ROUTING_TOKEN_CHOICE if routing is None else routing)
     ws = ops.alloc_backward_workspace(desc)
     g = _alloc_grads(cfg)
     ops.backward(desc, inp["x"], ops.weights_struct(inp), dout, ops.grads_struct(g), ws)
@@ -284,3 +284,115 @@ def test_backward_hip_graph_capture_replay():
         for key in g:
             assert torch.equal(g[key], eager[key]), (rep, key)
         del junk
+
+
+# ---------------------------------------------------------------------------
+# Expert-choice layers (moe_desc.routing = expert choice): every expert takes
+# its C best tokens, a token's slots are the 0..E experts that took it
+# ---------------------------------------------------------------------------
+EC_CASES = {
+    "ec_prefill": C["mixtral_prefill"].with_(T=300, d=256, f=512, seed=51),
+    "ec_renorm_off_shared": C["fine_grained"].with_(T=96, d=512, E=32, f=256, renormalize=False, seed=52),
+    # C = ceil(0.5 T k / E): about half the tokens are taken by no expert
+    "ec_low_capacity_shared": C["fine_grained"].with_(T=120, d=256, E=16, k=2, f=256, capacity_factor=0.5,
+                                                      seed=53),
+    "ec_every_token": C["mixtral_prefill"].with_(T=40, d=256, f=256, E=4, k=2, capacity_factor=2.0, seed=54),
+    # C = T: every token is in all 96 experts' lists (longer than a wave)
+    "ec_long_lists": C["fine_grained"].with_(T=40, d=256, E=96, k=8, f=128, capacity_factor=12.0, seed=55),
+    "ec_small_batch": C["mixtral_prefill"].with_(T=5, d=256, f=256, E=8, k=2, seed=56),
+}
+
+
+def _ec_routing(ov, cfg):
+    logits = oracle.router_logits(ov.x, ov.W_g, ov.bias)
+    r = oracle.expert_choice_routing(logits, cfg.k, np.float32(cfg.capacity_factor), cfg.renormalize)
+    r["logits"] = logits
+    assert ec_boundary_is_clear(r)
+    return r
+
+
+@pytest.mark.parametrize("name", list(EC_CASES))
+def test_backward_expert_choice_parity(name):
+    cfg = EC_CASES[name]
+    print(f"[backward-ec] {name}", flush=True)
+    inp = device_inputs(cfg)
+    ov = OracleInputs(inp)
+    r = _ec_routing(ov, cfg)
+    dout = _dout(cfg)
+    g = run_backward(inp, dout, ops.ROUTING_EXPERT_CHOICE)
+    ref = oracle.expert_choice_backward(ov.x, ov.W_g, ov.bias, cfg.k, cfg.renormalize,
+                                        np.float32(cfg.capacity_factor), ov.expert, cfg.E, ov.shared(), to64(dout))
+    assert np.array_equal(ref["pos"], r["pos"])
+    errs = {}
+    for key in ("dx", "dW_g", "dW_gate", "dW_up", "dW_down"):
+        errs[key] = assert_close(to64(g[key]), ref[key], TOL, f"{name} {key}")
+    if inp["bias"] is not None:
+        errs["d_bias"] = assert_close(to64(g["d_bias"]), ref["d_bias"], TOL, f"{name} d_bias")
+    if cfg.shared:
+        for key in ("dWs_gate", "dWs_up", "dWs_down"):
+            errs[key] = assert_close(to64(g[key]), ref[key], TOL, f"{name} {key}")
+    taken = (r["pos"] >= 0).sum(axis=1)
+    untaken = np.nonzero(taken == 0)[0]
+    if len(untaken):                                    # tokens no expert took: only the shared expert's dx
+        want = (oracle.expert_ffn_backward(ov.x[untaken], *ov.shared(), to64(dout)[untaken])["dX"] if cfg.shared
+                else np.zeros((len(untaken), cfg.d)))
+        assert_close(to64(g["dx"])[untaken], want, TOL, f"{name} dx of untaken tokens")
+    g2 = run_backward(inp, dout, ops.ROUTING_EXPERT_CHOICE)
+    for key in g:
+        assert torch.equal(g[key], g2[key]), key        # bitwise reproducible
+    print(f"[backward-ec] {name}: C={r['capacity']} untaken_tokens={len(untaken)} max_list={taken.max()} " +
+          " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+
+
+def _token_dx_ec(ov, cfg, r, probs, dout64, t):
+    x_t = ov.x[t:t + 1]
+    gt = np.zeros((1, cfg.E))
+    dx = np.zeros(cfg.d)
+    for e in np.nonzero(r["pos"][t] >= 0)[0]:
+        W = ov.expert(int(e))
+        gt[0, e] = float(np.dot(dout64[t], oracle.expert_ffn(x_t, *W)[0]))
+        dx += oracle.expert_ffn_backward(x_t, *W, r["weight"][t, e] * dout64[t:t + 1])["dX"][0]
+    dl = oracle.expert_choice_weights_backward(probs[t:t + 1], r["pos"][t:t + 1], gt, cfg.renormalize)
+    dx += (dl @ ov.W_g.T)[0]
+    if cfg.shared:
+        dx += oracle.expert_ffn_backward(x_t, *ov.shared(), dout64[t:t + 1])["dX"][0]
+    return dx
+
+
+@pytest.mark.parametrize("name,ntok,ncol", [("mixtral_prefill", 4, 4), ("fine_grained", 3, 3)])
+def test_backward_expert_choice_full_size(name, ntok, ncol):
+    """Full-size expert-choice layers: dx of sampled tokens (plus the tokens in
+    the first and last rows of the first, a middle and the last expert) and
+    weight-gradient columns of two experts, each from the oracle's functions."""
+    cfg = C[name]
+    print(f"[backward-ec-full] {name}", flush=True)
+    inp = device_inputs(cfg)
+    ov = OracleInputs(inp)
+    cache = {}
+    expert = ov.expert
+    ov.expert = lambda e: cache[e] if e in cache else cache.setdefault(e, expert(e))
+    r = _ec_routing(ov, cfg)
+    probs = oracle.softmax_rows(r["logits"])
+    dout = _dout(cfg)
+    dout64 = to64(dout)
+    g = run_backward(inp, dout, ops.ROUTING_EXPERT_CHOICE)
+    rng = np.random.default_rng(5)
+    offs, st = r["offsets"], r["sorted_tokens"]
+    edges = [int(st[i]) for e in (0, cfg.E // 2, cfg.E - 1) for i in (int(offs[e]), int(offs[e + 1]) - 1)]
+    toks = np.unique(np.concatenate([rng.choice(cfg.T, size=ntok, replace=False), np.array(edges)]))
+    got = to64(g["dx"][torch.from_numpy(toks).cuda()])
+    want = np.stack([_token_dx_ec(ov, cfg, r, probs, dout64, int(t)) for t in toks])
+    e_dx = assert_close(got, want, TOL, f"{name} expert-choice dx (sampled tokens)")
+    cols = np.sort(rng.choice(cfg.f, size=ncol, replace=False))
+    ci = torch.from_numpy(cols).cuda()
+    errs = []
+    for e in (0, cfg.E - 1):
+        rows = st[offs[e]:offs[e + 1]]
+        wt = np.array([r["weight"][t, e] for t in rows])
+        Wg, Wu, Wd = ov.expert(e)
+        b = oracle.expert_ffn_backward(ov.x[rows], Wg[:, cols], Wu[:, cols], Wd[cols, :], wt[:, None] * dout64[rows])
+        errs.append(assert_close(to64(g["dW_gate"][e][:, ci]), b["dW_gate"], TOL, f"{name} dW_gate[{e}]"))
+        errs.append(assert_close(to64(g["dW_up"][e][:, ci]), b["dW_up"], TOL, f"{name} dW_up[{e}]"))
+        errs.append(assert_close(to64(g["dW_down"][e][ci, :]), b["dW_down"], TOL, f"{name} dW_down[{e}]"))
+    print(f"[backward-ec-full] {name}: C={r['capacity']} dx rel_err={e_dx:.3e} on {len(toks)} tokens, "
+          f"dW rel_err max={max(errs):.3e}", flush=True)

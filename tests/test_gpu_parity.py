@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import TOL, OracleInputs, assert_close, device_inputs, rel_err, to64
+from gpu_helpers import TOL, OracleInputs, assert_close, device_inputs, ec_boundary_is_clear, rel_err, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -640,28 +640,6 @@ EC_CASES = {
 EC_SAMPLE = {"mixtral_prefill": 8, "fine_grained": 3}
 
 
-def _ec_boundary_is_clear(ref, k, cf):
-    """The C-th and (C+1)-th scores of every expert are distinct fp32 values whose
-    fp64 sources are far (relatively 1e-12) from an fp32 rounding midpoint, so a
-    different fp64 summation order cannot change any selection."""
-    probs = oracle.softmax_rows(ref["logits"])
-    s32 = ref["scores"]
-    T, E = s32.shape
-    Cap = ref["capacity"]
-    if Cap >= T:
-        return True
-    for e in range(E):
-        order = sorted(range(T), key=lambda t: (-float(s32[t, e]), t))
-        for t in order[Cap - 1:Cap + 1]:
-            p = probs[t, e]
-            lo = np.float32(p)
-            nb = np.nextafter(lo, np.float32(np.inf if p > lo else -np.inf))
-            mid = (float(lo) + float(nb)) / 2.0
-            if abs(p - mid) <= 1e-12 * abs(p):
-                return False
-    return True
-
-
 @pytest.mark.parametrize("name", list(EC_CASES))
 def test_expert_choice_parity(name):
     cfg = EC_CASES[name]
@@ -695,7 +673,7 @@ def test_expert_choice_parity(name):
     ref = oracle.expert_choice_forward(ov.x, ov.W_g, ov.bias, cfg.k, cfg.renormalize,
                                        np.float32(cfg.capacity_factor), ov.expert, cfg.E, shared=ov.shared(),
                                        tokens=toks, **ov.quant_hooks())
-    assert _ec_boundary_is_clear(ref, cfg.k, cfg.capacity_factor)
+    assert ec_boundary_is_clear(ref)
     Cap = ref["capacity"]
     assert ops.capacity(desc) == Cap
     assert counts.cpu().numpy().tolist() == [Cap] * cfg.E
