@@ -1,4 +1,4 @@
-"""CPU oracle for the routed Mixture-of-Experts SwiGLU feed-forward layer (forward pass).
+"""CPU oracle for the routed Mixture-of-Experts SwiGLU feed-forward layer (forward and backward).
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's CPU
 baseline may import this module.  It shares no code with the HIP library and
