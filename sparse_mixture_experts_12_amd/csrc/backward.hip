@@ -556,9 +556,9 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
     q.ksplit = backward_dx_ksplit(a.d, a.f, G);
     q.part_slots = G * ((a.d + 255) / 256);
     q.part = a.dx_part;
-    if (a.ev_begin) hipEventRecord(a.ev_begin, s);
+    if (a.ev_begin && (err = hipEventRecord(a.ev_begin, s)) != hipSuccess) return err;
     if ((err = launch_bwd_rows(2, q, s)) != hipSuccess) return err;
-    if (a.ev_end) hipEventRecord(a.ev_end, s);
+    if (a.ev_end && (err = hipEventRecord(a.ev_end, s)) != hipSuccess) return err;
   }
   // 5. weight gradients: dW_gate = Xp^T dG, dW_up = Xp^T dU ([d, f] per group), dW_down = Hw^T Dp ([f, d])
   {
