@@ -293,7 +293,7 @@ def bench_backward(args, cfg):
         "N(0,0.02) weights)",
         "config": {"workload": cfg.name, "pass": "backward", "T": cfg.T, "d": cfg.d, "E": cfg.E, "top_k": cfg.k,
                    "f": cfg.f, "shared_expert": cfg.shared, "capacity_factor": cfg.capacity_factor,
-                   "routing": args.routing},
+                   "routing": args.routing, "weights": cfg.wdt},
         "layer": {"alg_flops": int(flops), "tflops": round(flops / (ms / 1e3) / 1e12, 2)},
         "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)

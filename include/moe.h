@@ -281,9 +281,9 @@ typedef struct {
  * not supported by the backward). */
 size_t moe_backward_workspace_size(const moe_desc* desc);
 
-/* Backward of moe_forward for layers with bf16 activations and bf16 weights,
- * token-choice or expert-choice routing: given dout = dL/dout [T, d] (bf16),
- * the gradients of L with respect to x, the router weight and bias, and every
+/* Backward of moe_forward for layers with bf16 activations and bf16 or fp8
+ * weights, token-choice or expert-choice routing: given dout = dL/dout [T, d]
+ * (bf16), the gradients of L with respect to x, the router weight and bias, and every
  * expert's (and the shared expert's) three matrices.  The expert selection
  * (top-k, capacity) is held fixed: gradients flow through the routing weights
  * (the softmax and its renormalisation over the chosen experts) and through
@@ -294,8 +294,11 @@ size_t moe_backward_workspace_size(const moe_desc* desc);
  * took it (the full softmax, or its renormalisation over those experts), and
  * a token no expert took gets only the shared expert's gradient.  The routing
  * and the expert activations are recomputed from x (nothing is kept from the
- * forward).  Weight gradients are summed over each expert's tokens in a fixed
- * order without atomics: results are bitwise reproducible.  Pages: "Testing using
+ * forward).  fp8 weights: the gradients are with respect to the weights'
+ * values (e4m3 code x channel scale; the scales get none), and the GEMMs run
+ * on those values rounded once to bf16, kept in the workspace.  Weight
+ * gradients are summed over each expert's tokens in a fixed order without
+ * atomics: results are bitwise reproducible.  Pages: "Testing using
  * claude to graft ETHOS onto modded-nanogpt base", "Key Implementation
  * Details" (a backward that recomputes the forward values and accumulates each
  * weight gradient over the tokens that chose the expert); "Faster writing:
@@ -303,7 +306,7 @@ size_t moe_backward_workspace_size(const moe_desc* desc);
  * gradients of the chosen-experts dispatch).
  *   x, dout  [T, d] bf16;  w as for moe_forward;  grads as documented above
  *   ws       moe_backward_workspace_size(desc) bytes, 256-byte aligned
- * Returns MOE_ERR_UNSUPPORTED for other dtypes.
+ * Returns MOE_ERR_UNSUPPORTED for other dtypes (fp32, MXFP8, MXFP4).
  * T == 0 writes zero weight gradients. */
 moe_status moe_backward(const moe_desc* desc, const void* x, const moe_weights* w, const void* dout,
                         const moe_grads* grads, void* ws, size_t ws_bytes, hipStream_t stream);

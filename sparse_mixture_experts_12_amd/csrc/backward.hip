@@ -452,6 +452,37 @@ size_t router_wgrad_ws_bytes(int T, int d, int E) {
   return nchunk * (size_t)(d + 1) * E * 4;
 }
 
+// fp8 layers: out[m, r, c] = bf16(e4m3(codes[m, r, c]) * scale[m, c]) for
+// n_mats matrices of R x C (the scale is per output channel, the column), so
+// the bf16 GEMMs below run on the weights' values; 8 codes per thread.
+__global__ __launch_bounds__(256) void dequant_fp8_kernel(const uint8_t* __restrict__ codes,
+                                                          const float* __restrict__ scale, long n8, int R, int C,
+                                                          bf16_t* __restrict__ out) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const long e0 = i * 8;
+  const long per_mat = (long)R * C;
+  const long m = e0 / per_mat;
+  const int c = (int)(e0 % C);
+  const uint2 w = *reinterpret_cast<const uint2*>(codes + e0);
+  const float* s = scale + m * C + c;
+  float v[8];
+  fp8x4_to_f32(w.x, v);
+  fp8x4_to_f32(w.y, v + 4);
+  u32x4_t o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(v[2 * j] * s[2 * j], v[2 * j + 1] * s[2 * j + 1]);
+  *reinterpret_cast<u32x4_t*>(out + e0) = o;
+}
+
+hipError_t launch_dequant_fp8(const void* codes, const float* scale, long n_mats, int R, int C, bf16_t* out,
+                              hipStream_t s) {
+  const long n8 = n_mats * R * (long)C / 8;
+  if (n8 <= 0) return hipSuccess;
+  dequant_fp8_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>((const uint8_t*)codes, scale, n8, R, C, out);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, long n) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0.f;

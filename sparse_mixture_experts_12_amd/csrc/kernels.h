@@ -214,6 +214,9 @@ long backward_pad_rows(long routed, int T, int E, int has_shared);
 size_t backward_sched_ints(long routed, int T, int E, int has_shared);
 size_t router_wgrad_ws_bytes(int T, int d, int E);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
+// fp8 weights -> bf16 values (code * per-column scale) for the backward's GEMMs
+hipError_t launch_dequant_fp8(const void* codes, const float* scale, long n_mats, int R, int C, bf16_t* out,
+                              hipStream_t s);
 hipError_t launch_zero(float* p, long n, hipStream_t s);
 
 // Router telemetry (optional side outputs of the layer call)

@@ -556,8 +556,8 @@ namespace {
 moe_status check_backward_desc(const moe_desc* d) {
   moe_status st = check_desc(d);
   if (st != MOE_OK) return st;
-  if (d->act_dtype != MOE_BF16 || d->w_dtype != MOE_BF16)
-    return fail(MOE_ERR_UNSUPPORTED, "the backward takes bf16 activations and bf16 weights");
+  if (d->act_dtype != MOE_BF16 || (d->w_dtype != MOE_BF16 && d->w_dtype != MOE_FP8_E4M3))
+    return fail(MOE_ERR_UNSUPPORTED, "the backward takes bf16 activations and bf16 or fp8 weights");
   const double P = (double)backward_pad_rows((long)routed_rows_of(d), d->T, d->E, d->has_shared);
   if (P * (d->f > d->d ? d->f : d->d) >= 2147483648.0)
     return fail(MOE_ERR_UNSUPPORTED, "layer too large for the backward (padded rows * max(d, f) >= 2^31)");
@@ -567,6 +567,7 @@ moe_status check_backward_desc(const moe_desc* d) {
 struct BwdLayout {
   size_t part, idx, w, logits, counts, offsets, sorted, inv, ndrop, rank;
   size_t ec_scores, ec_pos, ec_w, ec_crow, ec_count;
+  size_t wq_gate, wq_up, wq_down, wqs_gate, wqs_up, wqs_down;   // fp8 layers: bf16 weight values
   size_t poff, ptok, pw, apos, gsc, sched, Xp, Dp, G, U, dH, dG, dU, Hw, dXp, dl, rw, dxp, total;
 };
 
@@ -598,6 +599,14 @@ BwdLayout bwd_layout_of(const moe_desc* d) {
   L.ec_w = take(ec ? T * E * 4 : 0);
   L.ec_crow = take(ec ? T * E * 4 : 0);
   L.ec_count = take(ec ? T * 4 : 0);
+  const bool f8 = d->w_dtype == MOE_FP8_E4M3;
+  const bool f8s = f8 && d->has_shared;
+  L.wq_gate = take(f8 ? E * D * F * 2 : 0);
+  L.wq_up = take(f8 ? E * D * F * 2 : 0);
+  L.wq_down = take(f8 ? E * D * F * 2 : 0);
+  L.wqs_gate = take(f8s ? D * F * 2 : 0);
+  L.wqs_up = take(f8s ? D * F * 2 : 0);
+  L.wqs_down = take(f8s ? D * F * 2 : 0);
   L.poff = take((Gn + 1) * 4);
   L.ptok = take(P * 4);
   L.pw = take(P * 4);
@@ -695,6 +704,21 @@ moe_status moe_backward(const moe_desc* desc, const void* x, const moe_weights* 
     return st;
   }
   a.x = x; a.dout = dout; a.W_g = w->W_g; a.w = expert_weights(w);
+  if (desc->w_dtype == MOE_FP8_E4M3) {            // the GEMMs run on the weights' values in bf16
+    ExpertWeights v{};
+    v.Wg = base + L.wq_gate; v.Wu = base + L.wq_up; v.Wd = base + L.wq_down;
+    hipError_t e = launch_dequant_fp8(w->W_gate, w->s_gate, (long)E, (int)D, (int)F, (bf16_t*)v.Wg, stream);
+    if (e == hipSuccess) e = launch_dequant_fp8(w->W_up, w->s_up, (long)E, (int)D, (int)F, (bf16_t*)v.Wu, stream);
+    if (e == hipSuccess) e = launch_dequant_fp8(w->W_down, w->s_down, (long)E, (int)F, (int)D, (bf16_t*)v.Wd, stream);
+    if (desc->has_shared) {
+      v.Wsg = base + L.wqs_gate; v.Wsu = base + L.wqs_up; v.Wsd = base + L.wqs_down;
+      if (e == hipSuccess) e = launch_dequant_fp8(w->Ws_gate, w->ss_gate, 1, (int)D, (int)F, (bf16_t*)v.Wsg, stream);
+      if (e == hipSuccess) e = launch_dequant_fp8(w->Ws_up, w->ss_up, 1, (int)D, (int)F, (bf16_t*)v.Wsu, stream);
+      if (e == hipSuccess) e = launch_dequant_fp8(w->Ws_down, w->ss_down, 1, (int)F, (int)D, (bf16_t*)v.Wsd, stream);
+    }
+    if ((st = hip_status(e, "fp8 weight values")) != MOE_OK) return st;
+    a.w = v;
+  }
   a.T = desc->T; a.d = desc->d; a.E = desc->E; a.k = desc->top_k; a.f = desc->f;
   a.has_shared = desc->has_shared; a.renormalize = desc->renormalize;
   a.routed = (long)routed_rows_of(desc);

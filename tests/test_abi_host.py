@@ -227,10 +227,15 @@ def test_backward_validation(ops):
     def bwd(d, g=None):
         gs = g if g is not None else ops.Grads()
         return ops.LIB.moe_backward(ctypes.byref(d), None, None, None, ctypes.byref(gs), None, 0, None)
-    for wdt, act in (("fp8", "bf16"), ("mxfp8", "bf16"), ("mxfp4", "bf16"), ("f32", "f32")):
+    for wdt, act in (("mxfp8", "bf16"), ("mxfp4", "bf16"), ("f32", "f32")):
         d = ops.make_desc(40, 256, 8, 2, 256, act=act, wdt=wdt)
         assert bwd(d) == ops.MOE_ERR_UNSUPPORTED, wdt
         assert ops.backward_workspace_size(d) == 0
+    # fp8 weights: taken; the workspace adds the bf16 weight values (3 E d f + 3 d f with the shared expert)
+    d8 = ops.make_desc(40, 256, 8, 2, 256, wdt="fp8", has_shared=True)
+    db = ops.make_desc(40, 256, 8, 2, 256, has_shared=True)
+    assert bwd(d8) == ops.MOE_ERR_INVALID_ARG and "dW_g" in ops.last_error()
+    assert ops.backward_workspace_size(d8) >= ops.backward_workspace_size(db) + 2 * (3 * 8 + 3) * 256 * 256
     # expert choice: bf16 layers are taken; the padded row space holds E C rows
     d = ops.make_desc(40, 256, 8, 2, 256)
     d.routing = ops.ROUTING_EXPERT_CHOICE
@@ -239,9 +244,9 @@ def test_backward_validation(ops):
     ec = ops.make_desc(40, 256, 8, 2, 256, capacity_factor=4.0)       # C = T = 40: 320 rows, T k = 80
     ec.routing = ops.ROUTING_EXPERT_CHOICE
     assert ops.backward_workspace_size(ec) > ops.backward_workspace_size(tc) > 0
-    ec8 = ops.make_desc(40, 256, 8, 2, 256, wdt="fp8")
-    ec8.routing = ops.ROUTING_EXPERT_CHOICE
-    assert bwd(ec8) == ops.MOE_ERR_UNSUPPORTED and ops.backward_workspace_size(ec8) == 0
+    ecm = ops.make_desc(40, 256, 8, 2, 256, wdt="mxfp8")
+    ecm.routing = ops.ROUTING_EXPERT_CHOICE
+    assert bwd(ecm) == ops.MOE_ERR_UNSUPPORTED and ops.backward_workspace_size(ecm) == 0
     d = ops.make_desc(40, 256, 8, 2, 256)
     assert ops.backward_workspace_size(d) > ops.workspace_size(d)
     assert bwd(d) == ops.MOE_ERR_INVALID_ARG and "dW_g" in ops.last_error()

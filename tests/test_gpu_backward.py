@@ -38,6 +38,9 @@ CASES = {
     # 65 one-step groups x 15 tiles per weight-gradient launch (~122 tiles per XCD): every persistent
     # work-group runs several one-step tiles in a row, whole tiles prefetching partial ones (f = 640)
     "wgrad_prefetch_partial": C["fine_grained"].with_(T=64, d=1280, E=64, k=2, f=640, seed=50),
+    # fp8 e4m3 weights with per-output-channel scales (capacity drops, shared expert)
+    "fp8_capacity_shared": C["fp8_capacity"].with_(T=160, d=256, E=16, k=4, f=256, shared=True, seed=57),
+    "fp8_uncapped": C["fp8_capacity"].with_(T=96, d=512, E=8, k=2, f=192, capacity_factor=0.0, seed=58),
 }
 
 WG_TILE_COST = 96      # the weight-gradient kernel's per-tile cost term (rows + this)
@@ -300,6 +303,7 @@ EC_CASES = {
     # C = T: every token is in all 96 experts' lists (longer than a wave)
     "ec_long_lists": C["fine_grained"].with_(T=40, d=256, E=96, k=8, f=128, capacity_factor=12.0, seed=55),
     "ec_small_batch": C["mixtral_prefill"].with_(T=5, d=256, f=256, E=8, k=2, seed=56),
+    "ec_fp8_shared": C["fp8_capacity"].with_(T=128, d=256, E=16, k=4, f=256, shared=True, seed=59),
 }
 
 
@@ -396,3 +400,23 @@ def test_backward_expert_choice_full_size(name, ntok, ncol):
         errs.append(assert_close(to64(g["dW_down"][e][ci, :]), b["dW_down"], TOL, f"{name} dW_down[{e}]"))
     print(f"[backward-ec-full] {name}: C={r['capacity']} dx rel_err={e_dx:.3e} on {len(toks)} tokens, "
           f"dW rel_err max={max(errs):.3e}", flush=True)
+
+
+def test_backward_fp8_full_size_every_element():
+    """The full fp8_capacity layer (T = 512, 128 experts of d = 2048, f = 768,
+    capacity 1.25): every gradient element against the oracle's backward on the
+    weights' values (code x channel scale)."""
+    cfg = C["fp8_capacity"]
+    print("[backward-full] fp8_capacity", flush=True)
+    inp = device_inputs(cfg)
+    ov = OracleInputs(inp)
+    assert ov.certificate()["ok"].all()
+    dout = _dout(cfg)
+    g = run_backward(inp, dout)
+    ref = oracle.backward(ov.x, ov.W_g, ov.bias, cfg.k, cfg.renormalize, np.float32(cfg.capacity_factor),
+                          ov.expert, cfg.E, ov.shared(), to64(dout))
+    errs = {key: assert_close(to64(g[key]), ref[key], TOL, f"fp8_capacity {key}")
+            for key in ("dx", "dW_g", "dW_gate", "dW_up", "dW_down")}
+    if inp["bias"] is not None:
+        errs["d_bias"] = assert_close(to64(g["d_bias"]), ref["d_bias"], TOL, "fp8_capacity d_bias")
+    print("[backward-full] fp8_capacity: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
