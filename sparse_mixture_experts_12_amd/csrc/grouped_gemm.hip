@@ -468,11 +468,13 @@ struct GemmParamsF32 {
 
 template <bool DUAL>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
-  // BK = 64: four K steps cover the tiny layer's d = 256, each issuing all of
-  // its loads (16 A + 16 or 32 B per thread) before any is used
+  // 64-wide K steps, 16-byte loads (4 A and 4 B vectors per matrix per
+  // thread), and the next step's loads issued into registers before the
+  // current step's FMAs, so each step's memory latency hides behind the
+  // previous step's arithmetic.  K and N are multiples of 64.
   constexpr int BM = 64, BN = 64, BK = 64;
   __shared__ float As[BK][BM + 4];
-  __shared__ float Bs[DUAL ? 2 : 1][BK][BN + 4];
+  __shared__ __attribute__((aligned(16))) float Bs[DUAL ? 2 : 1][BK][BN + 4];
   const int n_tiles = (p.N + BN - 1) / BN;
   int g, row0, rows, nt;
   if (!decode_tile(p.sched, p.maxQ, p.E, n_tiles, &g, &row0, &rows, &nt)) return;
@@ -483,28 +485,30 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
   const size_t goff = shared ? 0 : (size_t)g * p.K * p.N;
   const float* B0 = (shared ? p.Ws0 : p.W0 + goff);
   const float* B1 = DUAL ? (shared ? p.Ws1 : p.W1 + goff) : nullptr;
-  // A rows loaded by this thread: 4 rows (r = tid / 16 + 16 * i), 4 k each
-  // (tx + 16 j); rows past the tile's rows read its first row and stage zeros
+  // A: tile rows ty + 16 i, K columns 4 tx .. 4 tx + 3 of each step; rows
+  // past the tile's rows read its first row and stage zeros.  B: K-rows
+  // ty + 16 i of the step, columns n0 + 4 tx .. + 3.
   const float* arow[4];
   bool alive[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 4) + 16 * i;
+    const int r = ty + 16 * i;
     alive[i] = r < rows;
     const int grow = row0 + (alive[i] ? r : 0);
     if (DUAL) {
       const int tok = shared ? (grow - p.shared_row0) : (p.sorted_assign[grow] / p.k);
-      arow[i] = p.x + (size_t)tok * p.K;
+      arow[i] = p.x + (size_t)tok * p.K + 4 * tx;
     } else {
-      arow[i] = p.a_rows + (size_t)grow * p.K;
+      arow[i] = p.a_rows + (size_t)grow * p.K + 4 * tx;
     }
   }
+  const float* b0p = B0 + (size_t)ty * p.N + n0 + 4 * tx;
+  const float* b1p = DUAL ? B1 + (size_t)ty * p.N + n0 + 4 * tx : nullptr;
   float acc0[4][4], acc1[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc0[i][j] = acc1[i][j] = 0.f;
-  const int nn = tid & 63, kb = tid >> 6;          // B: column nn of K-rows kb + 4 i
   const int rpt = rows <= 16 ? 1 : rows <= 32 ? 2 : 4;   // rows per thread
   auto kloop = [&](auto RC) {
     constexpr int R = decltype(RC)::value;
@@ -527,29 +531,30 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
         }
     }
   };
-  const int colc = min(n0 + nn, p.N - 1);
-  const bool col_ok = n0 + nn < p.N;
-  for (int k0 = 0; k0 < p.K; k0 += BK) {
-    float va[4][4], vb0[16], vb1[DUAL ? 16 : 1];
+  f32x4_t va[4], vb0[4], vb1[DUAL ? 4 : 1];
+  auto load = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) va[i] = *reinterpret_cast<const f32x4_t*>(arow[i] + k0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) va[i][j] = arow[i][k0 + tx + 16 * j];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      vb0[i] = B0[(size_t)(k0 + kb + 4 * i) * p.N + colc];
-      if (DUAL) vb1[DUAL ? i : 0] = B1[(size_t)(k0 + kb + 4 * i) * p.N + colc];
+    for (int i = 0; i < 4; ++i) {
+      const size_t o = (size_t)(k0 + 16 * i) * p.N;
+      vb0[i] = *reinterpret_cast<const f32x4_t*>(b0p + o);
+      if (DUAL) vb1[DUAL ? i : 0] = *reinterpret_cast<const f32x4_t*>(b1p + o);
     }
+  };
+  load(0);
+  for (int k0 = 0; k0 < p.K; k0 += BK) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) As[tx + 16 * j][(tid >> 4) + 16 * i] = alive[i] ? va[i][j] : 0.f;
+      for (int j = 0; j < 4; ++j) As[4 * tx + j][ty + 16 * i] = alive[i] ? va[i][j] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      Bs[0][kb + 4 * i][nn] = col_ok ? vb0[i] : 0.f;
-      if (DUAL) Bs[DUAL ? 1 : 0][kb + 4 * i][nn] = col_ok ? vb1[DUAL ? i : 0] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<f32x4_t*>(&Bs[0][ty + 16 * i][4 * tx]) = vb0[i];
+      if (DUAL) *reinterpret_cast<f32x4_t*>(&Bs[DUAL ? 1 : 0][ty + 16 * i][4 * tx]) = vb1[DUAL ? i : 0];
     }
     __syncthreads();
+    if (k0 + BK < p.K) load(k0 + BK);                 // next step's loads fly during this step's FMAs
     // R rows x 4 columns per thread (rows ty R .. ty R + R - 1): R = 1 for
     // tiles of at most 16 rows, 2 for at most 32, else 4, so all four waves
     // do useful work
@@ -565,7 +570,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int col = n0 + tx * 4 + j;
-      if (col >= p.N) continue;
       const size_t o = (size_t)(row0 + r) * p.N + col;
       if (DUAL) p.h_out[o] = silu_f(acc0[i][j]) * acc1[i][j];
       else p.y_out[o] = acc0[i][j];
