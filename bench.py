@@ -214,7 +214,8 @@ def bench_backward(args, cfg):
     desc = ops.desc_from_cfg(cfg, routing=ops.ROUTING_EXPERT_CHOICE if ec else ops.ROUTING_TOKEN_CHOICE)
     w = ops.weights_struct(inp)
     gen = torch.Generator(device="cpu").manual_seed(7)
-    dout = torch.randn((cfg.T, cfg.d), generator=gen).to(torch.bfloat16).cuda()
+    adt = torch.float32 if cfg.act == "f32" else torch.bfloat16
+    dout = torch.randn((cfg.T, cfg.d), generator=gen).to(adt).cuda()
     ws = ops.alloc_backward_workspace(desc)
     z = lambda *sh: torch.empty(sh, dtype=torch.float32, device="cuda")
     g = {"dx": z(cfg.T, cfg.d), "dW_g": z(cfg.d, cfg.E), "d_bias": z(cfg.E) if inp["bias"] is not None else None,
@@ -224,7 +225,7 @@ def bench_backward(args, cfg):
     gs = ops.grads_struct(g)
     # routing facts (kept rows) from one forward with stats
     counts = torch.zeros(cfg.E, dtype=torch.int32, device="cuda")
-    out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((cfg.T, cfg.d), dtype=adt, device="cuda")
     fws = ops.alloc_workspace(desc)
     ops.forward(desc, inp["x"], w, out, fws, stats=ops.Stats(d_counts=counts.data_ptr()))
     torch.cuda.synchronize()
@@ -259,11 +260,15 @@ def bench_backward(args, cfg):
     # its bytes: the touched experts' W_gate and W_up (bf16), dG and dU (bf16),
     # dX rows written in fp32; the bound is whichever roofline the arithmetic
     # intensity reaches first, as for the forward's gate/up GEMM
-    kbytes = n_exp * 2 * cfg.d * cfg.f * 2 + rows * 2 * cfg.f * 2 + rows * cfg.d * 4
+    # (fp32 layers: fp32 weights and rows, and the fp32 vector peak for the SIMT GEMM)
+    f32 = cfg.act == "f32"
+    es = 4 if f32 else 2
+    kbytes = n_exp * 2 * cfg.d * cfg.f * es + rows * 2 * cfg.f * es + rows * cfg.d * 4
     flops = 16 * rows * cfg.d * cfg.f + 4 * cfg.T * cfg.d * cfg.E
     t = kern_ms / 1e3 if have_k else None
-    if kflops / kbytes >= BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
-        bound, peak, unit = "mfma", BF16_PEAK_TFLOPS, "TFLOP/s"
+    cpeak = FP32_PEAK_TFLOPS if f32 else BF16_PEAK_TFLOPS
+    if kflops / kbytes >= cpeak * 1e12 / (HBM_PEAK_GBS * 1e9):
+        bound, peak, unit = ("alu" if f32 else "mfma"), cpeak, "TFLOP/s"
         achieved = kflops / t / 1e12 if have_k else None
     else:
         bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
@@ -272,9 +277,9 @@ def bench_backward(args, cfg):
             "frac": round(achieved / peak, 4) if have_k else None,
             # the stored counters cover token-choice routing only
             "traffic": None if ec else measured_traffic("bwd_dx_gemm", cfg.name),
-            "kernel": "bwd_rows_kernel<NTS> (dX)",
+            "kernel": "bwd_rows_f32_kernel (dX)" if f32 else "bwd_rows_kernel<NTS> (dX)",
             "kernel_ms": round(kern_ms, 5) if have_k else None, "alg_flops": int(kflops), "alg_bytes": int(kbytes),
-            "mfma_frac": round(kflops / t / 1e12 / BF16_PEAK_TFLOPS, 4) if have_k else None,
+            "mfma_frac": round(kflops / t / 1e12 / BF16_PEAK_TFLOPS, 4) if have_k and not f32 else None,
             "hbm_frac": round(kbytes / t / 1e9 / HBM_PEAK_GBS, 4) if have_k else None}
     if args.copy_calibration:     # the plain copy kernel whose counters scale the GEMM's (see main)
         a = torch.ones(1 << 27, dtype=torch.bfloat16, device="cuda")
@@ -289,7 +294,7 @@ def bench_backward(args, cfg):
         "metric": "MoE-layer backward tokens/s (dL/dx and all weight gradients)",
         "value": round(cfg.T * steps / (total_ms / 1e3), 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) activations and dout, "
+        "vs_baseline": None, "dtype": "f32" if f32 else "bf16", "data": "synthetic (seeded N(0,1) activations and dout, "
         "N(0,0.02) weights)",
         "config": {"workload": cfg.name, "pass": "backward", "T": cfg.T, "d": cfg.d, "E": cfg.E, "top_k": cfg.k,
                    "f": cfg.f, "shared_expert": cfg.shared, "capacity_factor": cfg.capacity_factor,

@@ -282,8 +282,9 @@ typedef struct {
 size_t moe_backward_workspace_size(const moe_desc* desc);
 
 /* Backward of moe_forward for layers with bf16 activations and bf16 or fp8
- * weights, token-choice or expert-choice routing: given dout = dL/dout [T, d]
- * (bf16), the gradients of L with respect to x, the router weight and bias, and every
+ * weights, and for fp32 layers, token-choice or expert-choice routing: given
+ * dout = dL/dout [T, d] (act dtype), the gradients of L with respect to x, the
+ * router weight and bias, and every
  * expert's (and the shared expert's) three matrices.  The expert selection
  * (top-k, capacity) is held fixed: gradients flow through the routing weights
  * (the softmax and its renormalisation over the chosen experts) and through
@@ -296,7 +297,8 @@ size_t moe_backward_workspace_size(const moe_desc* desc);
  * and the expert activations are recomputed from x (nothing is kept from the
  * forward).  fp8 weights: the gradients are with respect to the weights'
  * values (e4m3 code x channel scale; the scales get none), and the GEMMs run
- * on those values rounded once to bf16, kept in the workspace.  Weight
+ * on those values rounded once to bf16, kept in the workspace.  fp32 layers
+ * compute every intermediate in fp32 (SIMT FMA; no bf16 rounding).  Weight
  * gradients are summed over each expert's tokens in a fixed order without
  * atomics: results are bitwise reproducible.  Pages: "Testing using
  * claude to graft ETHOS onto modded-nanogpt base", "Key Implementation
@@ -304,9 +306,9 @@ size_t moe_backward_workspace_size(const moe_desc* desc);
  * weight gradient over the tokens that chose the expert); "Faster writing:
  * run only the chosen experts; uncap the large profile", "Test plan" (slot
  * gradients of the chosen-experts dispatch).
- *   x, dout  [T, d] bf16;  w as for moe_forward;  grads as documented above
+ *   x, dout  [T, d] act dtype;  w as for moe_forward;  grads as documented above
  *   ws       moe_backward_workspace_size(desc) bytes, 256-byte aligned
- * Returns MOE_ERR_UNSUPPORTED for other dtypes (fp32, MXFP8, MXFP4).
+ * Returns MOE_ERR_UNSUPPORTED for other dtypes (MXFP8, MXFP4 weights).
  * T == 0 writes zero weight gradients. */
 moe_status moe_backward(const moe_desc* desc, const void* x, const moe_weights* w, const void* dout,
                         const moe_grads* grads, void* ws, size_t ws_bytes, hipStream_t stream);

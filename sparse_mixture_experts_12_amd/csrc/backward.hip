@@ -27,6 +27,8 @@
 // that list (renormalised: a softmax over the experts that took the token;
 // else the full softmax).
 // Every sum runs in a fixed order: the result is bitwise reproducible.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -151,34 +153,37 @@ __global__ __launch_bounds__(256) void pad_rows_ec_kernel(const int32_t* __restr
   pw[p] = wt;
 }
 
-// Xp[p] = x[ptok[p]], Dp[p] = dout[ptok[p]] (zero rows for padding); 8 bf16 per thread.
-__global__ __launch_bounds__(256) void gather_rows_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ dout,
-                                                          const int32_t* __restrict__ ptok, int pmax, int d,
-                                                          bf16_t* __restrict__ Xp, bf16_t* __restrict__ Dp) {
+// Xp[p] = x[ptok[p]], Dp[p] = dout[ptok[p]] (zero rows for padding); one
+// 16-byte chunk per thread (8 bf16 or 4 fp32 values); row_bytes = d * element size.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ x, const uint8_t* __restrict__ dout,
+                                                          const int32_t* __restrict__ ptok, int pmax, int row_bytes,
+                                                          uint8_t* __restrict__ Xp, uint8_t* __restrict__ Dp) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  const int per_row = d / 8;
+  const int per_row = row_bytes / 16;
   const long p = i / per_row;
   if (p >= pmax) return;
-  const int c = (int)(i - p * per_row) * 8;
+  const int c = (int)(i - p * per_row) * 16;
   const int t = ptok[p];
   u32x4_t vx = {0u, 0u, 0u, 0u}, vd = {0u, 0u, 0u, 0u};
   if (t >= 0) {
-    vx = *reinterpret_cast<const u32x4_t*>(x + (size_t)t * d + c);
-    vd = *reinterpret_cast<const u32x4_t*>(dout + (size_t)t * d + c);
+    vx = *reinterpret_cast<const u32x4_t*>(x + (size_t)t * row_bytes + c);
+    vd = *reinterpret_cast<const u32x4_t*>(dout + (size_t)t * row_bytes + c);
   }
-  *reinterpret_cast<u32x4_t*>(Xp + (size_t)p * d + c) = vx;
-  *reinterpret_cast<u32x4_t*>(Dp + (size_t)p * d + c) = vd;
+  *reinterpret_cast<u32x4_t*>(Xp + (size_t)p * row_bytes + c) = vx;
+  *reinterpret_cast<u32x4_t*>(Dp + (size_t)p * row_bytes + c) = vd;
 }
 
 // One work-group per padded row: SwiGLU backward and the row's slot gradient
-//   H = bf16(silu(G) U) (the forward's rounding), gsc = dH' . H,
-//   dG = w dH' U silu'(G), dU = w dH' silu(G), Hw = bf16(w H)   (bf16 out)
+//   H = silu(G) U (rounded to bf16 as the bf16 forward rounds it), gsc = dH' . H,
+//   dG = w dH' U silu'(G), dU = w dH' silu(G), Hw = w H   (TO: bf16 or fp32 out)
 // The dot product: each thread sums its columns in order, then a fixed tree.
+template <typename TO>
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict__ G, const float* __restrict__ U,
                                                          const float* __restrict__ dH, const float* __restrict__ pw,
                                                          const int32_t* __restrict__ pend, int f,
-                                                         bf16_t* __restrict__ dG, bf16_t* __restrict__ dU,
-                                                         bf16_t* __restrict__ Hw, float* __restrict__ gsc) {
+                                                         TO* __restrict__ dG, TO* __restrict__ dU,
+                                                         TO* __restrict__ Hw, float* __restrict__ gsc) {
+  constexpr bool BF = !std::is_same<TO, float>::value;
   __shared__ float red[256];
   const size_t p = blockIdx.x;
   if ((int)p >= *pend) return;                    // past the last group: never read
@@ -195,19 +200,25 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict
       const float g = g4[i], u = u4[i], dh = d4[i];
       const float s = 1.f / (1.f + __expf(-g));
       const float si = g * s;
-      const float h = bf16_to_f32(f32_to_bf16(si * u));
+      const float h = BF ? bf16_to_f32(f32_to_bf16(si * u)) : si * u;
       part = __fmaf_rn(dh, h, part);
       og[i] = w * dh * u * (s * (1.f + g * (1.f - s)));
       ou[i] = w * dh * si;
       oh[i] = w * h;
     }
-    uint2 vg, vu, vh;
-    vg.x = pack_bf16x2(og[0], og[1]); vg.y = pack_bf16x2(og[2], og[3]);
-    vu.x = pack_bf16x2(ou[0], ou[1]); vu.y = pack_bf16x2(ou[2], ou[3]);
-    vh.x = pack_bf16x2(oh[0], oh[1]); vh.y = pack_bf16x2(oh[2], oh[3]);
-    *reinterpret_cast<uint2*>(dG + base + c) = vg;
-    *reinterpret_cast<uint2*>(dU + base + c) = vu;
-    *reinterpret_cast<uint2*>(Hw + base + c) = vh;
+    if constexpr (BF) {
+      uint2 vg, vu, vh;
+      vg.x = pack_bf16x2(og[0], og[1]); vg.y = pack_bf16x2(og[2], og[3]);
+      vu.x = pack_bf16x2(ou[0], ou[1]); vu.y = pack_bf16x2(ou[2], ou[3]);
+      vh.x = pack_bf16x2(oh[0], oh[1]); vh.y = pack_bf16x2(oh[2], oh[3]);
+      *reinterpret_cast<uint2*>(dG + base + c) = vg;
+      *reinterpret_cast<uint2*>(dU + base + c) = vu;
+      *reinterpret_cast<uint2*>(Hw + base + c) = vh;
+    } else {
+      *reinterpret_cast<f32x4_t*>(dG + base + c) = f32x4_t{og[0], og[1], og[2], og[3]};
+      *reinterpret_cast<f32x4_t*>(dU + base + c) = f32x4_t{ou[0], ou[1], ou[2], ou[3]};
+      *reinterpret_cast<f32x4_t*>(Hw + base + c) = f32x4_t{oh[0], oh[1], oh[2], oh[3]};
+    }
   }
   red[threadIdx.x] = part;
   __syncthreads();
@@ -323,12 +334,12 @@ __global__ __launch_bounds__(256) void router_bwd_ec_kernel(const float* __restr
 // Expert choice: dx[t, c] = sum over the token's list of dXp[its padded row, c]
 //   + dXp[shared row of t, c] + sum_e dl[t, e] W_g[c, e]   (fp32, in this order;
 // renormalised: dl is zero off the token's list, so only the list is summed)
-template <bool SPARSE>
+template <bool SPARSE, typename TW>
 __global__ __launch_bounds__(256) void dx_ec_kernel(const float* __restrict__ dXp, const int32_t* __restrict__ apos,
                                                     const int32_t* __restrict__ poff, const float* __restrict__ dl,
                                                     const int32_t* __restrict__ crow,
                                                     const int32_t* __restrict__ ccount, int C,
-                                                    const bf16_t* __restrict__ Wg, int T, int d, int E,
+                                                    const TW* __restrict__ Wg, int T, int d, int E,
                                                     int has_shared, float* __restrict__ dx) {
   const int t = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
@@ -342,20 +353,20 @@ __global__ __launch_bounds__(256) void dx_ec_kernel(const float* __restrict__ dX
   if (SPARSE) {
     for (int i = 0; i < n; ++i) {
       const int e = crow[b + i] / C;
-      r = __fmaf_rn(dl[b + e], bf16_to_f32(Wg[(size_t)c * E + e]), r);
+      r = __fmaf_rn(dl[b + e], ActTraits<TW>::load(Wg, (size_t)c * E + e), r);
     }
   } else {
-    for (int e = 0; e < E; ++e) r = __fmaf_rn(dl[b + e], bf16_to_f32(Wg[(size_t)c * E + e]), r);
+    for (int e = 0; e < E; ++e) r = __fmaf_rn(dl[b + e], ActTraits<TW>::load(Wg, (size_t)c * E + e), r);
   }
   dx[(size_t)t * d + c] = acc + r;
 }
 
 // dx[t, c] = sum_j [kept] dXp[apos[t k + j], c] + dXp[shared row of t, c]
 //            + sum_e dl[t, e] W_g[c, e]       (fp32, in this order)
-template <bool SPARSE>
+template <bool SPARSE, typename TW>
 __global__ __launch_bounds__(256) void dx_kernel(const float* __restrict__ dXp, const int32_t* __restrict__ apos,
                                                  const int32_t* __restrict__ poff, const float* __restrict__ dl,
-                                                 const int32_t* __restrict__ topk_idx, const bf16_t* __restrict__ Wg,
+                                                 const int32_t* __restrict__ topk_idx, const TW* __restrict__ Wg,
                                                  int T, int d, int E, int k, int has_shared, float* __restrict__ dx) {
   const int t = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
@@ -370,10 +381,10 @@ __global__ __launch_bounds__(256) void dx_kernel(const float* __restrict__ dXp, 
   if (SPARSE) {                                   // renormalised: dl is zero off the chosen experts
     for (int j = 0; j < k; ++j) {
       const int e = topk_idx[t * k + j];
-      r = __fmaf_rn(dl[(size_t)t * E + e], bf16_to_f32(Wg[(size_t)c * E + e]), r);
+      r = __fmaf_rn(dl[(size_t)t * E + e], ActTraits<TW>::load(Wg, (size_t)c * E + e), r);
     }
   } else {
-    for (int e = 0; e < E; ++e) r = __fmaf_rn(dl[(size_t)t * E + e], bf16_to_f32(Wg[(size_t)c * E + e]), r);
+    for (int e = 0; e < E; ++e) r = __fmaf_rn(dl[(size_t)t * E + e], ActTraits<TW>::load(Wg, (size_t)c * E + e), r);
   }
   dx[(size_t)t * d + c] = acc + r;
 }
@@ -386,7 +397,8 @@ __global__ __launch_bounds__(256) void dx_kernel(const float* __restrict__ dXp, 
 // chunks in order.
 constexpr int kRwChunk = 256;
 
-__global__ __launch_bounds__(256) void router_wgrad_partial_kernel(const bf16_t* __restrict__ x,
+template <typename TX>
+__global__ __launch_bounds__(256) void router_wgrad_partial_kernel(const TX* __restrict__ x,
                                                                    const float* __restrict__ dl, int T, int d, int E,
                                                                    float* __restrict__ part) {
   const int c = blockIdx.x * 256 + 4 * (threadIdx.x & 63);     // d % 4 == 0: a 4-block is all x or the bias row
@@ -404,12 +416,19 @@ __global__ __launch_bounds__(256) void router_wgrad_partial_kernel(const bf16_t*
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
   constexpr int U = 8;
   for (int tb = t0; tb < t1; tb += U) {
-    uint2 xr[U];
+    f32x4_t xr[U];
     float4 lr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {             // clamped tokens: every load unconditional
       const int t = min(tb + u, t1 - 1);
-      xr[u] = bias_row ? make_uint2(0x3f80u, 0u) : *reinterpret_cast<const uint2*>(x + (size_t)t * d + c);
+      if (bias_row) {
+        xr[u] = f32x4_t{1.f, 0.f, 0.f, 0.f};
+      } else if constexpr (std::is_same<TX, float>::value) {
+        xr[u] = *reinterpret_cast<const f32x4_t*>(x + (size_t)t * d + c);
+      } else {
+        const uint2 q = *reinterpret_cast<const uint2*>(x + (size_t)t * d + c);
+        xr[u] = f32x4_t{bf16lo(q.x), bf16hi(q.x), bf16lo(q.y), bf16hi(q.y)};
+      }
       const float* r = dl + (size_t)t * E + e;
       lr[u] = vec ? *reinterpret_cast<const float4*>(r)
                   : make_float4(r[0], ne > 1 ? r[1] : 0.f, ne > 2 ? r[2] : 0.f, ne > 3 ? r[3] : 0.f);
@@ -417,7 +436,7 @@ __global__ __launch_bounds__(256) void router_wgrad_partial_kernel(const bf16_t*
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (tb + u >= t1) break;
-      const float xv[4] = {bf16lo(xr[u].x), bf16hi(xr[u].x), bf16lo(xr[u].y), bf16hi(xr[u].y)};
+      const float xv[4] = {xr[u][0], xr[u][1], xr[u][2], xr[u][3]};
       const float lv[4] = {lr[u].x, lr[u].y, lr[u].z, lr[u].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -525,6 +544,14 @@ hipError_t launch_zero(float* p, long n, hipStream_t s) {
   return hipGetLastError();
 }
 
+static hipError_t backward_gemms_bf16(const BackwardArgs& a, long pmax, int G, hipStream_t s);
+static hipError_t backward_gemms_f32(const BackwardArgs& a, long pmax, int G, hipStream_t s);
+template <typename TA>
+static hipError_t backward_router_t(const BackwardArgs& a, hipStream_t s);
+static hipError_t backward_router(const BackwardArgs& a, hipStream_t s) {
+  return a.f32 ? backward_router_t<float>(a, s) : backward_router_t<bf16_t>(a, s);
+}
+
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
   hipError_t err;
   const int G = a.E + (a.has_shared ? 1 : 0);
@@ -541,9 +568,22 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
     pad_rows_kernel<<<(unsigned)((npr + 255) / 256), 256, 0, s>>>(a.poff, a.offsets, a.sorted_assign, a.inv_perm,
                                                                    a.topk_idx, a.topk_w, a.E, G, a.k, a.T, (int)pmax,
                                                                    a.ptok, a.pw, a.apos);
-  gather_rows_kernel<<<(unsigned)((pmax * (a.d / 8) + 255) / 256), 256, 0, s>>>(
-      (const bf16_t*)a.x, (const bf16_t*)a.dout, a.ptok, (int)pmax, a.d, a.Xp, a.Dp);
+  const int row_bytes = a.d * (a.f32 ? 4 : 2);
+  gather_rows_kernel<<<(unsigned)((pmax * (row_bytes / 16) + 255) / 256), 256, 0, s>>>(
+      (const uint8_t*)a.x, (const uint8_t*)a.dout, a.ptok, (int)pmax, row_bytes, (uint8_t*)a.Xp, (uint8_t*)a.Dp);
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (a.f32) {
+    if ((err = backward_gemms_f32(a, pmax, G, s)) != hipSuccess) return err;
+  } else if ((err = backward_gemms_bf16(a, pmax, G, s)) != hipSuccess) {
+    return err;
+  }
+  return backward_router(a, s);
+}
+
+// Steps 1-5 for bf16 layers (fp8 layers arrive here with their weights'
+// values already in bf16): the MFMA row-tile and weight-gradient GEMMs.
+static hipError_t backward_gemms_bf16(const BackwardArgs& a, long pmax, int G, hipStream_t s) {
+  hipError_t err;
 
   // row tiles of the G padded groups (the shared expert is group E, read from poff like the others)
   const int maxQ = grouped_max_row_tiles((int)pmax, 0, G, 0, 256);
@@ -573,7 +613,8 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
     if ((err = launch_bwd_rows(1, q, s)) != hipSuccess) return err;
   }
   // 3. SwiGLU backward per padded row
-  swiglu_bwd_kernel<<<(unsigned)pmax, 256, 0, s>>>(a.G, a.U, a.dH, a.pw, a.poff + G, a.f, a.dG, a.dU, a.Hw, a.gsc);
+  swiglu_bwd_kernel<bf16_t><<<(unsigned)pmax, 256, 0, s>>>(a.G, a.U, a.dH, a.pw, a.poff + G, a.f, a.dG, a.dU, a.Hw,
+                                                           a.gsc);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   // 4. dXp = dG W_gate^T + dU W_up^T (fp32)
   {
@@ -606,30 +647,97 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
     r.C0 = a.dW_down; r.Cs = a.dWs_down;
     if ((err = launch_bwd_wgrad(r, s)) != hipSuccess) return err;
   }
-  // 6. router: dL/dlogits, then dx, dW_g, d_bias
+  return hipSuccess;
+}
+
+// Steps 1-5 for fp32 layers: the same products with the SIMT fp32 GEMMs, and
+// the SwiGLU backward keeping fp32 (no bf16 rounding of H, dG, dU, w H).
+static hipError_t backward_gemms_f32(const BackwardArgs& a, long pmax, int G, hipStream_t s) {
+  hipError_t err;
+  const float* Xp = (const float*)a.Xp;
+  const float* Dp = (const float*)a.Dp;
+  float* dG = (float*)a.dG;
+  float* dU = (float*)a.dU;
+  float* Hw = (float*)a.Hw;
+  BwdF32Params p{};
+  p.poff = a.poff; p.G = G; p.E = a.E;
+  // 1. G = Xp W_gate, U = Xp W_up
+  {
+    BwdF32Params q = p;
+    q.A0 = Xp; q.lda = a.d; q.ldb = a.f; q.bgs = (long)a.d * a.f; q.b_kc = false;
+    q.K = a.d; q.N = a.f;
+    q.B0 = (const float*)a.w.Wg; q.Bs0 = (const float*)a.w.Wsg; q.C = a.G;
+    if ((err = launch_bwd_rows_f32(q, pmax, s)) != hipSuccess) return err;
+    q.B0 = (const float*)a.w.Wu; q.Bs0 = (const float*)a.w.Wsu; q.C = a.U;
+    if ((err = launch_bwd_rows_f32(q, pmax, s)) != hipSuccess) return err;
+  }
+  // 2. dH' = Dp W_down^T
+  {
+    BwdF32Params q = p;
+    q.A0 = Dp; q.lda = a.d; q.ldb = a.d; q.bgs = (long)a.f * a.d; q.b_kc = true;
+    q.K = a.d; q.N = a.f;
+    q.B0 = (const float*)a.w.Wd; q.Bs0 = (const float*)a.w.Wsd; q.C = a.dH;
+    if ((err = launch_bwd_rows_f32(q, pmax, s)) != hipSuccess) return err;
+  }
+  // 3. SwiGLU backward per padded row
+  swiglu_bwd_kernel<float><<<(unsigned)pmax, 256, 0, s>>>(a.G, a.U, a.dH, a.pw, a.poff + G, a.f, dG, dU, Hw, a.gsc);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  // 4. dXp = dG W_gate^T + dU W_up^T
+  {
+    BwdF32Params q = p;
+    q.A0 = dG; q.A1 = dU; q.lda = a.f; q.ldb = a.f; q.bgs = (long)a.d * a.f; q.b_kc = true;
+    q.K = 2 * a.f; q.K1 = a.f; q.N = a.d;
+    q.B0 = (const float*)a.w.Wg; q.B1 = (const float*)a.w.Wu;
+    q.Bs0 = (const float*)a.w.Wsg; q.Bs1 = (const float*)a.w.Wsu;
+    q.C = a.dXp;
+    if (a.ev_begin && (err = hipEventRecord(a.ev_begin, s)) != hipSuccess) return err;
+    if ((err = launch_bwd_rows_f32(q, pmax, s)) != hipSuccess) return err;
+    if (a.ev_end && (err = hipEventRecord(a.ev_end, s)) != hipSuccess) return err;
+  }
+  // 5. weight gradients
+  {
+    BwdF32Params q = p;
+    q.A0 = Xp; q.lda = a.d; q.M = a.d; q.ldb = a.f; q.N = a.f; q.cstride = (long)a.d * a.f;
+    q.B0 = dG; q.C = a.dW_gate; q.Cs = a.dWs_gate;
+    if ((err = launch_bwd_wgrad_f32(q, s)) != hipSuccess) return err;
+    q.B0 = dU; q.C = a.dW_up; q.Cs = a.dWs_up;
+    if ((err = launch_bwd_wgrad_f32(q, s)) != hipSuccess) return err;
+    BwdF32Params r = p;
+    r.A0 = Hw; r.lda = a.f; r.M = a.f; r.B0 = Dp; r.ldb = a.d; r.N = a.d; r.cstride = (long)a.f * a.d;
+    r.C = a.dW_down; r.Cs = a.dWs_down;
+    if ((err = launch_bwd_wgrad_f32(r, s)) != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+// Step 6: dL/dlogits, then dx, dW_g and d_bias (TA: the activation type).
+template <typename TA>
+static hipError_t backward_router_t(const BackwardArgs& a, hipStream_t s) {
+  const bool ec = a.ec_C > 0;
+  const TA* Wg = (const TA*)a.W_g;
   const dim3 gx((a.d + 255) / 256, a.T);
   if (ec) {
     router_bwd_ec_kernel<<<(a.T + 3) / 4, 256, 0, s>>>(a.ec_scores, a.ec_pos, a.ec_crow, a.ec_count, a.poff, a.gsc,
                                                        a.pw, a.T, a.E, a.ec_C, a.renormalize, a.dl);
     if (a.renormalize)
-      dx_ec_kernel<true><<<gx, 256, 0, s>>>(a.dXp, a.apos, a.poff, a.dl, a.ec_crow, a.ec_count, a.ec_C,
-                                            (const bf16_t*)a.W_g, a.T, a.d, a.E, a.has_shared, a.dx);
+      dx_ec_kernel<true, TA><<<gx, 256, 0, s>>>(a.dXp, a.apos, a.poff, a.dl, a.ec_crow, a.ec_count, a.ec_C, Wg, a.T,
+                                                a.d, a.E, a.has_shared, a.dx);
     else
-      dx_ec_kernel<false><<<gx, 256, 0, s>>>(a.dXp, a.apos, a.poff, a.dl, a.ec_crow, a.ec_count, a.ec_C,
-                                             (const bf16_t*)a.W_g, a.T, a.d, a.E, a.has_shared, a.dx);
+      dx_ec_kernel<false, TA><<<gx, 256, 0, s>>>(a.dXp, a.apos, a.poff, a.dl, a.ec_crow, a.ec_count, a.ec_C, Wg, a.T,
+                                                 a.d, a.E, a.has_shared, a.dx);
   } else {
     router_bwd_kernel<<<(a.T + 3) / 4, 256, 0, s>>>(a.logits, a.topk_idx, a.topk_w, a.apos, a.gsc, a.T, a.E, a.k,
                                                     a.renormalize, a.dl);
     if (a.renormalize)
-      dx_kernel<true><<<gx, 256, 0, s>>>(a.dXp, a.apos, a.poff, a.dl, a.topk_idx, (const bf16_t*)a.W_g, a.T, a.d,
-                                         a.E, a.k, a.has_shared, a.dx);
+      dx_kernel<true, TA><<<gx, 256, 0, s>>>(a.dXp, a.apos, a.poff, a.dl, a.topk_idx, Wg, a.T, a.d, a.E, a.k,
+                                             a.has_shared, a.dx);
     else
-      dx_kernel<false><<<gx, 256, 0, s>>>(a.dXp, a.apos, a.poff, a.dl, a.topk_idx, (const bf16_t*)a.W_g, a.T, a.d,
-                                          a.E, a.k, a.has_shared, a.dx);
+      dx_kernel<false, TA><<<gx, 256, 0, s>>>(a.dXp, a.apos, a.poff, a.dl, a.topk_idx, Wg, a.T, a.d, a.E, a.k,
+                                              a.has_shared, a.dx);
   }
   const int nchunk = (a.T + kRwChunk - 1) / kRwChunk;
-  router_wgrad_partial_kernel<<<dim3((a.d + 1 + 255) / 256, (a.E + 15) / 16, nchunk), 256, 0, s>>>(
-      (const bf16_t*)a.x, a.dl, a.T, a.d, a.E, a.rw_part);
+  router_wgrad_partial_kernel<TA><<<dim3((a.d + 1 + 255) / 256, (a.E + 15) / 16, nchunk), 256, 0, s>>>(
+      (const TA*)a.x, a.dl, a.T, a.d, a.E, a.rw_part);
   const long nout = (long)(a.d + 1) * a.E;
   router_wgrad_reduce_kernel<<<(unsigned)((nout + 255) / 256), 256, 0, s>>>(a.rw_part, nchunk, a.d, a.E, a.dW_g,
                                                                            a.d_bias);

@@ -630,4 +630,112 @@ hipError_t launch_bwd_wgrad(const BwdGemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// fp32 layers: the same products in fp32 with SIMT FMA (64 x 64 output tiles,
+// 256 threads of 4 x 4 outputs, 16-wide K steps staged in LDS; each output one
+// FMA chain in K order).  Groups are padded to 64 rows, so a 64-row tile of the
+// padded row space lies inside one group.
+// ---------------------------------------------------------------------------
+namespace {
+
+__device__ __forceinline__ void f32_tile_fma(const float (*As)[68], const float (*Bs)[68], int tx, int ty,
+                                             float (*acc)[4]) {
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) {
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&As[kk][4 * ty]);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(&Bs[kk][4 * tx]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __fmaf_rn(a[i], b[j], acc[i][j]);
+  }
+}
+
+// Row products: C[p, n] = sum_k A(p, k) B_g(k, n) over the padded rows p of
+// group g, A rows K-contiguous; B_g(k, n) = B[k ldb + n] (b_kc false) or
+// B[n ldb + k] (b_kc true), the shared expert's matrix for g = E; with A1 the
+// K range splits at K1 into (A0, B0) and (A1, B1).
+__global__ __launch_bounds__(256) void bwd_rows_f32_kernel(BwdF32Params p) {
+  __shared__ __attribute__((aligned(16))) float As[16][68];
+  __shared__ __attribute__((aligned(16))) float Bs[16][68];
+  const int row0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  if (row0 >= p.poff[p.G]) return;
+  int lo = 0, hi = p.G;                             // the group holding row0
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.poff[mid] <= row0) lo = mid;
+    else hi = mid;
+  }
+  const bool shared = lo == p.E;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  float acc[4][4] = {};
+  for (int part = 0; part < (p.A1 ? 2 : 1); ++part) {
+    const float* A = part ? p.A1 : p.A0;
+    const float* B = part ? (shared ? p.Bs1 : p.B1 + (size_t)lo * p.bgs) : (shared ? p.Bs0 : p.B0 + (size_t)lo * p.bgs);
+    const int K = p.A1 ? (part ? p.K - p.K1 : p.K1) : p.K;
+    for (int k0 = 0; k0 < K; k0 += 16) {
+      {                                             // A: row tid / 4, K columns 4 (tid % 4) .. + 3
+        const int r = tid >> 2, c = 4 * (tid & 3);
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(A + (size_t)(row0 + r) * p.lda + k0 + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) As[c + j][r] = v[j];
+      }
+      if (p.b_kc) {                                 // B: column tid / 4, K rows 4 (tid % 4) .. + 3
+        const int n = tid >> 2, c = 4 * (tid & 3);
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(B + (size_t)(n0 + n) * p.ldb + k0 + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Bs[c + j][n] = v[j];
+      } else {                                      // B: K row tid / 16, columns 4 (tid % 16) .. + 3
+        const int kk = tid >> 4, n = 4 * (tid & 15);
+        *reinterpret_cast<f32x4_t*>(&Bs[kk][n]) = *reinterpret_cast<const f32x4_t*>(B + (size_t)(k0 + kk) * p.ldb + n0 + n);
+      }
+      __syncthreads();
+      f32_tile_fma(As, Bs, tx, ty, acc);
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<f32x4_t*>(p.C + (size_t)(row0 + 4 * ty + i) * p.N + n0 + 4 * tx) =
+        f32x4_t{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+}
+
+// Weight gradients: C_g[m, n] = sum over group g's padded rows r of
+// A[r lda + m] B[r ldb + n] (group E: the shared expert's Cs); an empty group
+// writes zeros.
+__global__ __launch_bounds__(256) void bwd_wgrad_f32_kernel(BwdF32Params p) {
+  __shared__ __attribute__((aligned(16))) float As[16][68];
+  __shared__ __attribute__((aligned(16))) float Bs[16][68];
+  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64, g = blockIdx.z;
+  const int r0 = p.poff[g], r1 = p.poff[g + 1];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int kk = tid >> 4, c4 = 4 * (tid & 15);
+  float acc[4][4] = {};
+  for (int k0 = r0; k0 < r1; k0 += 16) {
+    *reinterpret_cast<f32x4_t*>(&As[kk][c4]) = *reinterpret_cast<const f32x4_t*>(p.A0 + (size_t)(k0 + kk) * p.lda + m0 + c4);
+    *reinterpret_cast<f32x4_t*>(&Bs[kk][c4]) = *reinterpret_cast<const f32x4_t*>(p.B0 + (size_t)(k0 + kk) * p.ldb + n0 + c4);
+    __syncthreads();
+    f32_tile_fma(As, Bs, tx, ty, acc);
+    __syncthreads();
+  }
+  float* C = g == p.E ? p.Cs : p.C + (size_t)g * p.cstride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<f32x4_t*>(C + (size_t)(m0 + 4 * ty + i) * p.N + n0 + 4 * tx) =
+        f32x4_t{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+}
+
+}  // namespace
+
+hipError_t launch_bwd_rows_f32(const BwdF32Params& p, long pmax, hipStream_t s) {
+  if (pmax <= 0) return hipSuccess;
+  bwd_rows_f32_kernel<<<dim3(p.N / 64, (unsigned)(pmax / 64)), 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_wgrad_f32(const BwdF32Params& p, hipStream_t s) {
+  bwd_wgrad_f32_kernel<<<dim3(p.N / 64, p.M / 64, p.G), 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
 }  // namespace moe

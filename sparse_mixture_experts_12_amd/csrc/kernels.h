@@ -167,6 +167,24 @@ struct BwdGemmParams {          // grouped GEMMs of the backward
 // mode 0: G/U recompute, 1: NT, 2: NT with K split over two (A, B) pairs
 hipError_t launch_bwd_rows(int mode, const BwdGemmParams& p, hipStream_t s);
 hipError_t launch_bwd_wgrad(const BwdGemmParams& p, hipStream_t s);
+struct BwdF32Params {           // backward GEMMs of fp32 layers (padded rows as above)
+  const float* A0;               // rows: [P, lda] K-contiguous; wgrad: [P, lda], m contiguous
+  const float* A1;               // rows: second K part (K >= K1), else nullptr
+  int lda;
+  const float *B0, *B1;          // rows: expert weights (group stride bgs); wgrad: [P, ldb]
+  const float *Bs0, *Bs1;        // rows: shared expert's weights
+  int ldb;
+  long bgs;
+  bool b_kc;                     // rows: B(k, n) = B[n ldb + k] (else B[k ldb + n])
+  int K, K1, N, M;               // K: rows products' reduction; N: output columns; M: wgrad output rows
+  const int32_t* poff;           // [G + 1] padded group offsets
+  int G, E;
+  float* C;                      // rows: [P, N]; wgrad: group g at C + g cstride ([M, N])
+  float* Cs;                     // wgrad: the shared expert's [M, N]
+  long cstride;
+};
+hipError_t launch_bwd_rows_f32(const BwdF32Params& p, long pmax, hipStream_t s);
+hipError_t launch_bwd_wgrad_f32(const BwdF32Params& p, hipStream_t s);
 // K parts of the dX GEMM's light row tiles, and the workspace their parts take
 int backward_dx_ksplit(int d, int f, int G);
 size_t backward_dx_part_bytes(int d, int f, int G);
@@ -199,9 +217,10 @@ struct BackwardArgs {
   int32_t* apos;                 // [T k]; expert choice: [T, E] per token list entry
   float* gsc;                    // [P]
   int32_t* sched;                // backward_sched_ints
-  bf16_t *Xp, *Dp;               // [P, d]
+  bf16_t *Xp, *Dp;               // [P, d] (fp32 layers: float)
   float *G, *U, *dH;             // [P, f]
-  bf16_t *dG, *dU, *Hw;          // [P, f]
+  bf16_t *dG, *dU, *Hw;          // [P, f] (fp32 layers: float)
+  bool f32;                      // fp32 activations and weights
   float* dXp;                    // [P, d]
   float* dl;                     // [T, E]
   float* rw_part;                // router_wgrad_ws_bytes

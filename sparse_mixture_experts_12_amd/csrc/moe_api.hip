@@ -556,8 +556,10 @@ namespace {
 moe_status check_backward_desc(const moe_desc* d) {
   moe_status st = check_desc(d);
   if (st != MOE_OK) return st;
-  if (d->act_dtype != MOE_BF16 || (d->w_dtype != MOE_BF16 && d->w_dtype != MOE_FP8_E4M3))
-    return fail(MOE_ERR_UNSUPPORTED, "the backward takes bf16 activations and bf16 or fp8 weights");
+  const bool bf = d->act_dtype == MOE_BF16 && (d->w_dtype == MOE_BF16 || d->w_dtype == MOE_FP8_E4M3);
+  const bool f32 = d->act_dtype == MOE_F32 && d->w_dtype == MOE_F32;
+  if (!bf && !f32)
+    return fail(MOE_ERR_UNSUPPORTED, "the backward takes bf16 activations with bf16 or fp8 weights, or fp32 layers");
   const double P = (double)backward_pad_rows((long)routed_rows_of(d), d->T, d->E, d->has_shared);
   if (P * (d->f > d->d ? d->f : d->d) >= 2147483648.0)
     return fail(MOE_ERR_UNSUPPORTED, "layer too large for the backward (padded rows * max(d, f) >= 2^31)");
@@ -613,14 +615,15 @@ BwdLayout bwd_layout_of(const moe_desc* d) {
   L.apos = take((ec ? T * E : T * k) * 4);
   L.gsc = take(P * 4);
   L.sched = take(backward_sched_ints((long)routed, d->T, d->E, d->has_shared) * 4);
-  L.Xp = take(P * D * 2);
-  L.Dp = take(P * D * 2);
+  const size_t ea = d->act_dtype == MOE_F32 ? 4 : 2;    // gathered rows and the SwiGLU backward's outputs
+  L.Xp = take(P * D * ea);
+  L.Dp = take(P * D * ea);
   L.G = take(P * F * 4);
   L.U = take(P * F * 4);
   L.dH = take(P * F * 4);
-  L.dG = take(P * F * 2);
-  L.dU = take(P * F * 2);
-  L.Hw = take(P * F * 2);
+  L.dG = take(P * F * ea);
+  L.dU = take(P * F * ea);
+  L.Hw = take(P * F * ea);
   L.dXp = take(P * D * 4);
   L.dl = take(T * E * 4);
   L.rw = take(router_wgrad_ws_bytes(d->T, d->d, d->E));
@@ -722,6 +725,7 @@ moe_status moe_backward(const moe_desc* desc, const void* x, const moe_weights* 
   a.T = desc->T; a.d = desc->d; a.E = desc->E; a.k = desc->top_k; a.f = desc->f;
   a.has_shared = desc->has_shared; a.renormalize = desc->renormalize;
   a.routed = (long)routed_rows_of(desc);
+  a.f32 = desc->act_dtype == MOE_F32;
   a.logits = logits; a.topk_idx = idx; a.topk_w = tw; a.offsets = offsets; a.sorted_assign = sorted; a.inv_perm = inv;
   a.poff = (int32_t*)(base + L.poff); a.ptok = (int32_t*)(base + L.ptok); a.pw = (float*)(base + L.pw);
   a.apos = (int32_t*)(base + L.apos); a.gsc = (float*)(base + L.gsc); a.sched = (int32_t*)(base + L.sched);

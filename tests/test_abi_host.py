@@ -227,10 +227,14 @@ def test_backward_validation(ops):
     def bwd(d, g=None):
         gs = g if g is not None else ops.Grads()
         return ops.LIB.moe_backward(ctypes.byref(d), None, None, None, ctypes.byref(gs), None, 0, None)
-    for wdt, act in (("mxfp8", "bf16"), ("mxfp4", "bf16"), ("f32", "f32")):
+    for wdt, act in (("mxfp8", "bf16"), ("mxfp4", "bf16"), ("f32", "bf16")):
         d = ops.make_desc(40, 256, 8, 2, 256, act=act, wdt=wdt)
         assert bwd(d) == ops.MOE_ERR_UNSUPPORTED, wdt
         assert ops.backward_workspace_size(d) == 0
+    # fp32 layers: taken; gathered rows and SwiGLU-backward outputs are fp32
+    d32 = ops.make_desc(40, 256, 8, 2, 256, act="f32", wdt="f32")
+    assert bwd(d32) == ops.MOE_ERR_INVALID_ARG and "dW_g" in ops.last_error()
+    assert ops.backward_workspace_size(d32) > ops.backward_workspace_size(ops.make_desc(40, 256, 8, 2, 256))
     # fp8 weights: taken; the workspace adds the bf16 weight values (3 E d f + 3 d f with the shared expert)
     d8 = ops.make_desc(40, 256, 8, 2, 256, wdt="fp8", has_shared=True)
     db = ops.make_desc(40, 256, 8, 2, 256, has_shared=True)
