@@ -284,8 +284,8 @@ size_t moe_backward_workspace_size(const moe_desc* desc);
 /* Backward of moe_forward for layers with bf16 activations and bf16 or fp8
  * weights, and for fp32 layers, token-choice or expert-choice routing: given
  * dout = dL/dout [T, d] (act dtype), the gradients of L with respect to x, the
- * router weight and bias, and every
- * expert's (and the shared expert's) three matrices.  The expert selection
+ * router weight and bias, and every expert's (and the shared expert's) three
+ * matrices.  The expert selection
  * (top-k, capacity) is held fixed: gradients flow through the routing weights
  * (the softmax and its renormalisation over the chosen experts) and through
  * the chosen experts' SwiGLU FFNs; dropped assignments carry no gradient;
