@@ -455,14 +455,18 @@ def dsilu(z) -> np.ndarray:
     return s * (1.0 + z * (1.0 - s))
 
 
-def expert_ffn_backward(X, W_gate, W_up, W_down, dY) -> dict:
+def expert_ffn_backward(X, W_gate, W_up, W_down, dY, quant_h=None) -> dict:
     """Y = (silu(X Wg) * (X Wu)) Wd; given dY = dL/dY returns dX, dWg, dWu, dWd
-    and H (the activated rows)."""
+    and H (the activated rows).  quant_h (block-scaled layers): the down
+    projection sees quant_h(H), differentiated as the identity (straight
+    through), so dW_down uses the quantised rows and dH passes unchanged."""
     X, dY = _f64(X), _f64(dY)
     Wg, Wu, Wd = _f64(W_gate), _f64(W_up), _f64(W_down)
     G = X @ Wg
     U = X @ Wu
     H = silu(G) * U
+    if quant_h is not None:
+        H = quant_h(H)
     dH = dY @ Wd.T
     dG = dH * U * dsilu(G)
     dU = dH * silu(G)
@@ -496,11 +500,14 @@ def routing_weights_backward(probs, idx, g, renormalize: bool) -> np.ndarray:
 
 
 def backward(x, W_g, bias, k: int, renormalize: bool, capacity_factor, expert: ExpertFn, E: int,
-             shared: Optional[Sequence[np.ndarray]], dout, round_logits: bool = True) -> dict:
+             shared: Optional[Sequence[np.ndarray]], dout, round_logits: bool = True,
+             quant_x=None, quant_h=None) -> dict:
     """Gradients of the token-choice layer of forward() for dL/dout = dout:
     dx [T,d], dW_g [d,E], d_bias [E], dW_gate/dW_up [E,d,f], dW_down [E,f,d],
     the shared expert's dWs_* (or None), and the intermediates d_logits [T,E]
-    and g [T,k] = dL/dw (0 for dropped assignments)."""
+    and g [T,k] = dL/dw (0 for dropped assignments).  quant_x / quant_h as in
+    forward(), each differentiated as the identity (straight through)."""
+    qx = (lambda X: X) if quant_x is None else quant_x
     x, W_g, dout = _f64(x), _f64(W_g), _f64(dout)
     T, d = x.shape
     logits = router_logits(x, W_g, bias, round_logits)
@@ -521,9 +528,10 @@ def backward(x, W_g, bias, k: int, renormalize: bool, capacity_factor, expert: E
             continue
         toks = [a // k for a in rows]
         Wg, Wu, Wd = expert(e)
-        Y = expert_ffn(x[toks], Wg, Wu, Wd)           # the unweighted expert outputs
+        X = qx(x[toks])
+        Y = expert_ffn(X, Wg, Wu, Wd, quant_h=quant_h)   # the unweighted expert outputs
         wt = np.array([w[a // k, a % k] for a in rows])
-        b = expert_ffn_backward(x[toks], Wg, Wu, Wd, wt[:, None] * dout[toks])
+        b = expert_ffn_backward(X, Wg, Wu, Wd, wt[:, None] * dout[toks], quant_h=quant_h)
         dWg_e[e], dWu_e[e], dWd_e[e] = b["dW_gate"], b["dW_up"], b["dW_down"]
         for i, a in enumerate(rows):
             t, j = a // k, a % k
@@ -534,7 +542,7 @@ def backward(x, W_g, bias, k: int, renormalize: bool, capacity_factor, expert: E
     out = dict(dx=dx, dW_g=x.T @ dl, d_bias=dl.sum(axis=0), dW_gate=dWg_e, dW_up=dWu_e, dW_down=dWd_e,
                d_logits=dl, g=g, dWs_gate=None, dWs_up=None, dWs_down=None)
     if shared is not None:
-        b = expert_ffn_backward(x, *shared, dout)
+        b = expert_ffn_backward(qx(x), *shared, dout, quant_h=quant_h)
         out["dx"] = dx + b["dX"]
         out.update(dWs_gate=b["dW_gate"], dWs_up=b["dW_up"], dWs_down=b["dW_down"])
     return out
@@ -579,9 +587,12 @@ def expert_choice_weights_backward(probs, pos, g, renormalize: bool) -> np.ndarr
 
 
 def expert_choice_backward(x, W_g, bias, k: int, renormalize: bool, capacity_factor, expert: ExpertFn, E: int,
-                           shared: Optional[Sequence[np.ndarray]], dout, round_logits: bool = True) -> dict:
+                           shared: Optional[Sequence[np.ndarray]], dout, round_logits: bool = True,
+                           quant_x=None, quant_h=None) -> dict:
     """Gradients of expert_choice_forward() for dL/dout = dout, with the keys
-    of backward(); g is [T, E] (dL/dweight[t, e], zero where e did not take t)."""
+    of backward(); g is [T, E] (dL/dweight[t, e], zero where e did not take t).
+    quant_x / quant_h as in backward()."""
+    qx = (lambda X: X) if quant_x is None else quant_x
     x, W_g, dout = _f64(x), _f64(W_g), _f64(dout)
     T, d = x.shape
     logits = router_logits(x, W_g, bias, round_logits)
@@ -599,9 +610,10 @@ def expert_choice_backward(x, W_g, bias, k: int, renormalize: bool, capacity_fac
         if not toks:
             continue
         Wg, Wu, Wd = expert(e)
-        Y = expert_ffn(x[toks], Wg, Wu, Wd)           # the unweighted expert outputs
+        X = qx(x[toks])
+        Y = expert_ffn(X, Wg, Wu, Wd, quant_h=quant_h)   # the unweighted expert outputs
         wt = np.array([r["weight"][t, e] for t in toks])
-        b = expert_ffn_backward(x[toks], Wg, Wu, Wd, wt[:, None] * dout[toks])
+        b = expert_ffn_backward(X, Wg, Wu, Wd, wt[:, None] * dout[toks], quant_h=quant_h)
         dWg_e[e], dWu_e[e], dWd_e[e] = b["dW_gate"], b["dW_up"], b["dW_down"]
         for i, t in enumerate(toks):
             dx[t] += b["dX"][i]
@@ -611,7 +623,7 @@ def expert_choice_backward(x, W_g, bias, k: int, renormalize: bool, capacity_fac
     out = dict(dx=dx, dW_g=x.T @ dl, d_bias=dl.sum(axis=0), dW_gate=dWg_e, dW_up=dWu_e, dW_down=dWd_e,
                d_logits=dl, g=g, dWs_gate=None, dWs_up=None, dWs_down=None, capacity=r["capacity"], pos=r["pos"])
     if shared is not None:
-        b = expert_ffn_backward(x, *shared, dout)
+        b = expert_ffn_backward(qx(x), *shared, dout, quant_h=quant_h)
         out["dx"] = dx + b["dX"]
         out.update(dWs_gate=b["dW_gate"], dWs_up=b["dW_up"], dWs_down=b["dW_down"])
     return out

@@ -1061,3 +1061,80 @@ def test_ec_backward_with_every_token_taken_is_the_token_choice_backward_with_k_
     tc = oracle.backward(x, Wg, bias, E, renorm, 0.0, lambda e: ex[e], E, sh, dout, round_logits=False)
     for key in ("dx", "dW_g", "d_bias", "dW_gate", "dW_up", "dW_down", "dWs_gate", "dWs_up", "dWs_down", "d_logits"):
         np.testing.assert_allclose(ec[key], tc[key], rtol=1e-12, atol=1e-13, err_msg=key)
+
+
+# --------------------------------------------------------------------------
+# Backward of block-scaled layers: the forward's quantisation of the expert
+# inputs and of the activated rows, differentiated as the identity
+# --------------------------------------------------------------------------
+def _qh(H):
+    return oracle.mx_roundtrip(H, as_fp32=True)
+
+
+@pytest.mark.parametrize("ec", [False, True])
+def test_backward_with_identity_hooks_is_the_plain_backward(ec):
+    T, d, E, k, f = 9, 64, 4, 2, 64
+    x, Wg, bias, ex, sh, dout = _bwd_layer(T, d, E, k, f, True, seed=91 + int(ec))
+    fn = oracle.expert_choice_backward if ec else oracle.backward
+    a = fn(x, Wg, bias, k, True, 0.9, lambda e: ex[e], E, sh, dout)
+    b = fn(x, Wg, bias, k, True, 0.9, lambda e: ex[e], E, sh, dout, quant_x=lambda v: v, quant_h=lambda v: v)
+    for key in ("dx", "dW_g", "d_bias", "dW_gate", "dW_up", "dW_down", "dWs_gate", "dWs_up", "dWs_down"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("ec,renorm", [(False, True), (False, False), (True, True)])
+def test_block_scaled_backward_against_torch_autograd_straight_through(ec, renorm):
+    """torch autograd of the run-every-expert form in which each quantiser is
+    q(v) = v + (Q(v) - v).detach() (Q: the oracle's MX round trip, applied to
+    the expert inputs and to the activated rows)."""
+    T, d, E, k, f = 10, 64, 4, 2, 64
+    x, Wg, bias, ex, sh, dout = _bwd_layer(T, d, E, k, f, True, seed=95 + int(ec) + 2 * int(renorm))
+    cf = 0.9
+    hooks = dict(quant_x=oracle.mx_roundtrip, quant_h=_qh)
+    if ec:
+        r = oracle.expert_choice_forward(x, Wg, bias, k, renorm, cf, lambda e: ex[e], E, sh, **hooks)
+        b = oracle.expert_choice_backward(x, Wg, bias, k, renorm, cf, lambda e: ex[e], E, sh, dout, **hooks)
+        mask = (r["pos"] >= 0).astype(np.float64)
+    else:
+        r = oracle.forward(x, Wg, bias, k, renorm, cf, lambda e: ex[e], E, sh, **hooks)
+        b = oracle.backward(x, Wg, bias, k, renorm, cf, lambda e: ex[e], E, sh, dout, **hooks)
+        mask = np.zeros((T, E))
+        for t in range(T):
+            for j in range(k):
+                if r["inv_perm"][t * k + j] >= 0:
+                    mask[t, r["topk_idx"][t, j]] = 1.0
+        chosen = np.zeros((T, E))
+        for t in range(T):
+            chosen[t, r["topk_idx"][t]] = 1.0
+    tt = lambda a: torch.from_numpy(np.array(a, dtype=np.float64)).requires_grad_(True)
+    ste = lambda v, Q: v + (torch.from_numpy(Q(v.detach().numpy())) - v).detach()
+    xt, Wgt, bt = tt(x), tt(Wg), tt(bias)
+    ext = [[tt(m) for m in trip] for trip in ex]
+    sht = [tt(m) for m in sh]
+    p = torch.softmax(xt @ Wgt + bt, dim=1)
+    if ec:
+        w = p * torch.from_numpy(mask)
+        if renorm:
+            w = w / w.sum(dim=1, keepdim=True).clamp_min(1e-300)
+    else:
+        pc = p * torch.from_numpy(chosen)
+        w = (pc / pc.sum(dim=1, keepdim=True) if renorm else pc) * torch.from_numpy(mask)
+    xq = ste(xt, oracle.mx_roundtrip)
+
+    def ffn(a, b_, c):
+        H = torch.nn.functional.silu(xq @ a) * (xq @ b_)
+        return ste(H, _qh) @ c
+    out = sum(w[:, e:e + 1] * ffn(*ext[e]) for e in range(E)) + ffn(*sht)
+    (out * torch.from_numpy(dout)).sum().backward()
+    np.testing.assert_allclose(out.detach().numpy(), r["out"], rtol=1e-6, atol=1e-6)   # fp32 logits vs fp64
+    tol = dict(rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(b["dx"], xt.grad.numpy(), **tol)
+    np.testing.assert_allclose(b["dW_g"], Wgt.grad.numpy(), **tol)
+    np.testing.assert_allclose(b["d_bias"], bt.grad.numpy(), **tol)
+    for e in range(E):
+        for key, m in (("dW_gate", 0), ("dW_up", 1), ("dW_down", 2)):
+            np.testing.assert_allclose(b[key][e], ext[e][m].grad.numpy(), **tol)
+    for key, m in (("dWs_gate", 0), ("dWs_up", 1), ("dWs_down", 2)):
+        np.testing.assert_allclose(b[key], sht[m].grad.numpy(), **tol)
+    # the quantisation is not the identity on these inputs
+    assert np.abs(oracle.mx_roundtrip(x) - x).max() > 1e-3
