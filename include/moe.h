@@ -281,8 +281,9 @@ typedef struct {
  * not supported by the backward). */
 size_t moe_backward_workspace_size(const moe_desc* desc);
 
-/* Backward of moe_forward for layers with bf16 activations and bf16 or fp8
- * weights, and for fp32 layers, token-choice or expert-choice routing: given
+/* Backward of moe_forward for layers with bf16 activations and bf16, fp8,
+ * MXFP8 or MXFP4 weights, and for fp32 layers, token-choice or expert-choice
+ * routing: given
  * dout = dL/dout [T, d] (act dtype), the gradients of L with respect to x, the
  * router weight and bias, and every expert's (and the shared expert's) three
  * matrices.  The expert selection
@@ -297,7 +298,10 @@ size_t moe_backward_workspace_size(const moe_desc* desc);
  * and the expert activations are recomputed from x (nothing is kept from the
  * forward).  fp8 weights: the gradients are with respect to the weights'
  * values (e4m3 code x channel scale; the scales get none), and the GEMMs run
- * on those values rounded once to bf16, kept in the workspace.  fp32 layers
+ * on those values rounded once to bf16, kept in the workspace.  MXFP8 / MXFP4
+ * weights: the same, with the values exact in bf16; the forward's MXFP8
+ * quantisation of the expert inputs and of the activated rows is recomputed
+ * and differentiated as the identity (straight through).  fp32 layers
  * compute every intermediate in fp32 (SIMT FMA; no bf16 rounding).  Weight
  * gradients are summed over each expert's tokens in a fixed order without
  * atomics: results are bitwise reproducible.  Pages: "Testing using
@@ -308,7 +312,7 @@ size_t moe_backward_workspace_size(const moe_desc* desc);
  * gradients of the chosen-experts dispatch).
  *   x, dout  [T, d] act dtype;  w as for moe_forward;  grads as documented above
  *   ws       moe_backward_workspace_size(desc) bytes, 256-byte aligned
- * Returns MOE_ERR_UNSUPPORTED for other dtypes (MXFP8, MXFP4 weights).
+ * Returns MOE_ERR_UNSUPPORTED for dtype pairs the forward declines.
  * T == 0 writes zero weight gradients. */
 moe_status moe_backward(const moe_desc* desc, const void* x, const moe_weights* w, const void* dout,
                         const moe_grads* grads, void* ws, size_t ws_bytes, hipStream_t stream);

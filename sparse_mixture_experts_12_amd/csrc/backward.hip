@@ -177,12 +177,17 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restr
 //   H = silu(G) U (rounded to bf16 as the bf16 forward rounds it), gsc = dH' . H,
 //   dG = w dH' U silu'(G), dU = w dH' silu(G), Hw = w H   (TO: bf16 or fp32 out)
 // The dot product: each thread sums its columns in order, then a fixed tree.
+// Block-scaled layers (hq set): the down projection saw H quantised to MXFP8
+// (codes hq [P, f], scales hs [P, f / 32]), so gsc and Hw take those values;
+// dG and dU pass through the quantisation unchanged (straight through).
 template <typename TO>
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict__ G, const float* __restrict__ U,
                                                          const float* __restrict__ dH, const float* __restrict__ pw,
                                                          const int32_t* __restrict__ pend, int f,
                                                          TO* __restrict__ dG, TO* __restrict__ dU,
-                                                         TO* __restrict__ Hw, float* __restrict__ gsc) {
+                                                         TO* __restrict__ Hw, float* __restrict__ gsc,
+                                                         const uint8_t* __restrict__ hq = nullptr,
+                                                         const uint8_t* __restrict__ hs = nullptr) {
   constexpr bool BF = !std::is_same<TO, float>::value;
   __shared__ float red[256];
   const size_t p = blockIdx.x;
@@ -194,13 +199,20 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict
     const f32x4_t g4 = *reinterpret_cast<const f32x4_t*>(G + base + c);
     const f32x4_t u4 = *reinterpret_cast<const f32x4_t*>(U + base + c);
     const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(dH + base + c);
+    float hqv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (hq) {                                     // 4 codes of one 32-column block
+      fp8x4_to_f32(*reinterpret_cast<const uint32_t*>(hq + base + c), hqv);
+      const int e = (int)hs[p * (size_t)(f >> 5) + (c >> 5)] - 127;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hqv[i] = ldexpf(hqv[i], e);
+    }
     float og[4], ou[4], oh[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float g = g4[i], u = u4[i], dh = d4[i];
       const float s = 1.f / (1.f + __expf(-g));
       const float si = g * s;
-      const float h = BF ? bf16_to_f32(f32_to_bf16(si * u)) : si * u;
+      const float h = hq ? hqv[i] : BF ? bf16_to_f32(f32_to_bf16(si * u)) : si * u;
       part = __fmaf_rn(dh, h, part);
       og[i] = w * dh * u * (s * (1.f + g * (1.f - s)));
       ou[i] = w * dh * si;
@@ -502,6 +514,108 @@ hipError_t launch_dequant_fp8(const void* codes, const float* scale, long n_mats
   return hipGetLastError();
 }
 
+// Block-scaled layers: H = silu(G) U in fp32 (as the forward's gate/up
+// epilogue forms it before quantising), 4 values per thread.
+__global__ __launch_bounds__(256) void swiglu_h_kernel(const float* __restrict__ G, const float* __restrict__ U,
+                                                       long n4, float* __restrict__ H) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4_t g = reinterpret_cast<const f32x4_t*>(G)[i];
+  const f32x4_t u = reinterpret_cast<const f32x4_t*>(U)[i];
+  f32x4_t h;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) h[j] = g[j] / (1.f + __expf(-g[j])) * u[j];
+  reinterpret_cast<f32x4_t*>(H)[i] = h;
+}
+
+// MXFP8 rows -> bf16 values (code x 2^(scale - 127)), same layout; 8 per thread.
+__global__ __launch_bounds__(256) void dequant_mx_rows_kernel(const uint8_t* __restrict__ codes,
+                                                              const uint8_t* __restrict__ scales, long n8,
+                                                              bf16_t* __restrict__ out) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const uint2 w = reinterpret_cast<const uint2*>(codes)[i];
+  const int e = (int)scales[i >> 2] - 127;        // 8 values = a quarter of a 32-value block
+  float v[8];
+  fp8x4_to_f32(w.x, v);
+  fp8x4_to_f32(w.y, v + 4);
+  u32x4_t o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(ldexpf(v[2 * j], e), ldexpf(v[2 * j + 1], e));
+  reinterpret_cast<u32x4_t*>(out)[i] = o;
+}
+
+// E2M1 code (sign, 2 exponent bits with bias 1, 1 mantissa bit) -> value.
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t m = c & 7u;
+  const float mag = m < 2 ? 0.5f * (float)m : ldexpf(1.f + 0.5f * (float)(m & 1u), (int)(m >> 1) - 1);
+  return (c & 8u) ? -mag : mag;
+}
+
+// Block-scaled weights -> the bf16 backward's input-major layout: codes
+// [mats, N, K] (K contiguous; E2M1: two per byte, element 2j in the low
+// nibble) with E8M0 scales [mats, N, K / 32] become out[m, k, n] = value.
+// One 64 (N) x 64 (K) tile per work-group, transposed through LDS.
+template <bool W4>
+__global__ __launch_bounds__(256) void dequant_mx_transpose_kernel(const uint8_t* __restrict__ codes,
+                                                                   const uint8_t* __restrict__ scales, int N, int K,
+                                                                   bf16_t* __restrict__ out) {
+  __shared__ float tile[64][65];
+  const int k0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
+  const size_t m = blockIdx.z;
+  const int tid = threadIdx.x;
+  {                                               // row n0 + tid / 4, K values k0 + 16 (tid % 4) .. + 15
+    const int n = tid >> 2, kc = 16 * (tid & 3);
+    const size_t row = m * N + n0 + n;
+    const int e = (int)scales[row * (size_t)(K >> 5) + ((k0 + kc) >> 5)] - 127;
+    float v[16];
+    if constexpr (W4) {
+      const uint2 w = *reinterpret_cast<const uint2*>(codes + row * (size_t)(K >> 1) + ((k0 + kc) >> 1));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t b = ((j < 4 ? w.x : w.y) >> (8 * (j & 3))) & 0xffu;
+        v[2 * j] = e2m1_value(b & 15u);
+        v[2 * j + 1] = e2m1_value(b >> 4);
+      }
+    } else {
+      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(codes + row * (size_t)K + k0 + kc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fp8x4_to_f32(w[j], v + 4 * j);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) tile[kc + j][n] = ldexpf(v[j], e);
+  }
+  __syncthreads();
+  {                                               // K row k0 + tid / 4, columns n0 + 16 (tid % 4) .. + 15
+    const int k = tid >> 2, nc = 16 * (tid & 3);
+    u32x4_t o0, o1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o0[j] = pack_bf16x2(tile[k][nc + 2 * j], tile[k][nc + 2 * j + 1]);
+      o1[j] = pack_bf16x2(tile[k][nc + 8 + 2 * j], tile[k][nc + 8 + 2 * j + 1]);
+    }
+    bf16_t* dst = out + (m * K + k0 + k) * (size_t)N + n0 + nc;
+    *reinterpret_cast<u32x4_t*>(dst) = o0;
+    *reinterpret_cast<u32x4_t*>(dst + 8) = o1;
+  }
+}
+
+hipError_t launch_dequant_mx_rows(const uint8_t* codes, const uint8_t* scales, long n, bf16_t* out, hipStream_t s) {
+  const long n8 = n / 8;
+  if (n8 <= 0) return hipSuccess;
+  dequant_mx_rows_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(codes, scales, n8, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_mx_transpose(const void* codes, const uint8_t* scales, bool w4, int mats, int N, int K,
+                                       bf16_t* out, hipStream_t s) {
+  if (mats <= 0) return hipSuccess;
+  const dim3 grid(K / 64, N / 64, mats);
+  if (w4) dequant_mx_transpose_kernel<true><<<grid, 256, 0, s>>>((const uint8_t*)codes, scales, N, K, out);
+  else dequant_mx_transpose_kernel<false><<<grid, 256, 0, s>>>((const uint8_t*)codes, scales, N, K, out);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, long n) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0.f;
@@ -570,7 +684,8 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
                                                                    a.ptok, a.pw, a.apos);
   const int row_bytes = a.d * (a.f32 ? 4 : 2);
   gather_rows_kernel<<<(unsigned)((pmax * (row_bytes / 16) + 255) / 256), 256, 0, s>>>(
-      (const uint8_t*)a.x, (const uint8_t*)a.dout, a.ptok, (int)pmax, row_bytes, (uint8_t*)a.Xp, (uint8_t*)a.Dp);
+      (const uint8_t*)(a.x_rows ? a.x_rows : a.x), (const uint8_t*)a.dout, a.ptok, (int)pmax, row_bytes,
+      (uint8_t*)a.Xp, (uint8_t*)a.Dp);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (a.f32) {
     if ((err = backward_gemms_f32(a, pmax, G, s)) != hipSuccess) return err;
@@ -612,9 +727,16 @@ static hipError_t backward_gemms_bf16(const BackwardArgs& a, long pmax, int G, h
     q.C0 = a.dH;
     if ((err = launch_bwd_rows(1, q, s)) != hipSuccess) return err;
   }
-  // 3. SwiGLU backward per padded row
+  // 3. SwiGLU backward per padded row (block-scaled layers: H as the forward
+  //    quantised it, MXFP8 per 32 columns of a row)
+  if (a.hq) {
+    const long n4 = pmax * (long)a.f / 4;
+    swiglu_h_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(a.G, a.U, n4, a.Hf);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = launch_mx_quantize(a.Hf, true, pmax, a.f, a.hq, a.hs, s)) != hipSuccess) return err;
+  }
   swiglu_bwd_kernel<bf16_t><<<(unsigned)pmax, 256, 0, s>>>(a.G, a.U, a.dH, a.pw, a.poff + G, a.f, a.dG, a.dU, a.Hw,
-                                                           a.gsc);
+                                                           a.gsc, a.hq, a.hs);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   // 4. dXp = dG W_gate^T + dU W_up^T (fp32)
   {

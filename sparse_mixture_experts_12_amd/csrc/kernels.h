@@ -221,6 +221,12 @@ struct BackwardArgs {
   float *G, *U, *dH;             // [P, f]
   bf16_t *dG, *dU, *Hw;          // [P, f] (fp32 layers: float)
   bool f32;                      // fp32 activations and weights
+  // block-scaled layers: the expert inputs as the forward quantised them
+  // (bf16 values, [T, d]; nullptr: x itself), and the activated rows' fp32
+  // values Hf [P, f] with their MXFP8 codes hq [P, f] and scales hs [P, f / 32]
+  const void* x_rows;
+  float* Hf;
+  uint8_t *hq, *hs;
   float* dXp;                    // [P, d]
   float* dl;                     // [T, E]
   float* rw_part;                // router_wgrad_ws_bytes
@@ -233,6 +239,11 @@ long backward_pad_rows(long routed, int T, int E, int has_shared);
 size_t backward_sched_ints(long routed, int T, int E, int has_shared);
 size_t router_wgrad_ws_bytes(int T, int d, int E);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
+// block-scaled layers: MXFP8 rows -> bf16 values (same layout), and MXFP8 /
+// MXFP4 weights [mats, N, K] -> bf16 values [mats, K, N]
+hipError_t launch_dequant_mx_rows(const uint8_t* codes, const uint8_t* scales, long n, bf16_t* out, hipStream_t s);
+hipError_t launch_dequant_mx_transpose(const void* codes, const uint8_t* scales, bool w4, int mats, int N, int K,
+                                       bf16_t* out, hipStream_t s);
 // fp8 weights -> bf16 values (code * per-column scale) for the backward's GEMMs
 hipError_t launch_dequant_fp8(const void* codes, const float* scale, long n_mats, int R, int C, bf16_t* out,
                               hipStream_t s);

@@ -556,10 +556,12 @@ namespace {
 moe_status check_backward_desc(const moe_desc* d) {
   moe_status st = check_desc(d);
   if (st != MOE_OK) return st;
-  const bool bf = d->act_dtype == MOE_BF16 && (d->w_dtype == MOE_BF16 || d->w_dtype == MOE_FP8_E4M3);
+  const bool bf = d->act_dtype == MOE_BF16 && (d->w_dtype == MOE_BF16 || d->w_dtype == MOE_FP8_E4M3 ||
+                                               d->w_dtype == MOE_MXFP8 || d->w_dtype == MOE_MXFP4);
   const bool f32 = d->act_dtype == MOE_F32 && d->w_dtype == MOE_F32;
   if (!bf && !f32)
-    return fail(MOE_ERR_UNSUPPORTED, "the backward takes bf16 activations with bf16 or fp8 weights, or fp32 layers");
+    return fail(MOE_ERR_UNSUPPORTED, "the backward takes bf16 activations with bf16, fp8, MXFP8 or MXFP4 weights, "
+                "or fp32 layers");
   const double P = (double)backward_pad_rows((long)routed_rows_of(d), d->T, d->E, d->has_shared);
   if (P * (d->f > d->d ? d->f : d->d) >= 2147483648.0)
     return fail(MOE_ERR_UNSUPPORTED, "layer too large for the backward (padded rows * max(d, f) >= 2^31)");
@@ -569,7 +571,8 @@ moe_status check_backward_desc(const moe_desc* d) {
 struct BwdLayout {
   size_t part, idx, w, logits, counts, offsets, sorted, inv, ndrop, rank;
   size_t ec_scores, ec_pos, ec_w, ec_crow, ec_count;
-  size_t wq_gate, wq_up, wq_down, wqs_gate, wqs_up, wqs_down;   // fp8 layers: bf16 weight values
+  size_t wq_gate, wq_up, wq_down, wqs_gate, wqs_up, wqs_down;   // fp8 / MX layers: bf16 weight values
+  size_t mx_xq, mx_xs, mx_xv, mx_hf, mx_hq, mx_hs;              // MX layers: quantised x and H
   size_t poff, ptok, pw, apos, gsc, sched, Xp, Dp, G, U, dH, dG, dU, Hw, dXp, dl, rw, dxp, total;
 };
 
@@ -601,7 +604,8 @@ BwdLayout bwd_layout_of(const moe_desc* d) {
   L.ec_w = take(ec ? T * E * 4 : 0);
   L.ec_crow = take(ec ? T * E * 4 : 0);
   L.ec_count = take(ec ? T * 4 : 0);
-  const bool f8 = d->w_dtype == MOE_FP8_E4M3;
+  const bool mxl = d->w_dtype == MOE_MXFP8 || d->w_dtype == MOE_MXFP4;
+  const bool f8 = d->w_dtype == MOE_FP8_E4M3 || mxl;
   const bool f8s = f8 && d->has_shared;
   L.wq_gate = take(f8 ? E * D * F * 2 : 0);
   L.wq_up = take(f8 ? E * D * F * 2 : 0);
@@ -609,6 +613,12 @@ BwdLayout bwd_layout_of(const moe_desc* d) {
   L.wqs_gate = take(f8s ? D * F * 2 : 0);
   L.wqs_up = take(f8s ? D * F * 2 : 0);
   L.wqs_down = take(f8s ? D * F * 2 : 0);
+  L.mx_xq = take(mxl ? T * D : 0);
+  L.mx_xs = take(mxl ? T * D / 32 : 0);
+  L.mx_xv = take(mxl ? T * D * 2 : 0);
+  L.mx_hf = take(mxl ? P * F * 4 : 0);
+  L.mx_hq = take(mxl ? P * F : 0);
+  L.mx_hs = take(mxl ? P * F / 32 : 0);
   L.poff = take((Gn + 1) * 4);
   L.ptok = take(P * 4);
   L.pw = take(P * 4);
@@ -721,6 +731,37 @@ moe_status moe_backward(const moe_desc* desc, const void* x, const moe_weights* 
     }
     if ((st = hip_status(e, "fp8 weight values")) != MOE_OK) return st;
     a.w = v;
+  } else if (desc->w_dtype == MOE_MXFP8 || desc->w_dtype == MOE_MXFP4) {
+    // the GEMMs run on the weights' values in bf16 (exact: at most 4 significant
+    // bits times a power of two), laid out input-major as for bf16 layers; the
+    // expert inputs and the activated rows are quantised as the forward did
+    const bool w4 = desc->w_dtype == MOE_MXFP4;
+    ExpertWeights v{};
+    v.Wg = base + L.wq_gate; v.Wu = base + L.wq_up; v.Wd = base + L.wq_down;
+    hipError_t e = launch_dequant_mx_transpose(w->W_gate, w->mx_gate, w4, (int)E, (int)F, (int)D, (bf16_t*)v.Wg, stream);
+    if (e == hipSuccess)
+      e = launch_dequant_mx_transpose(w->W_up, w->mx_up, w4, (int)E, (int)F, (int)D, (bf16_t*)v.Wu, stream);
+    if (e == hipSuccess)
+      e = launch_dequant_mx_transpose(w->W_down, w->mx_down, w4, (int)E, (int)D, (int)F, (bf16_t*)v.Wd, stream);
+    if (desc->has_shared) {
+      v.Wsg = base + L.wqs_gate; v.Wsu = base + L.wqs_up; v.Wsd = base + L.wqs_down;
+      if (e == hipSuccess)
+        e = launch_dequant_mx_transpose(w->Ws_gate, w->mxs_gate, w4, 1, (int)F, (int)D, (bf16_t*)v.Wsg, stream);
+      if (e == hipSuccess)
+        e = launch_dequant_mx_transpose(w->Ws_up, w->mxs_up, w4, 1, (int)F, (int)D, (bf16_t*)v.Wsu, stream);
+      if (e == hipSuccess)
+        e = launch_dequant_mx_transpose(w->Ws_down, w->mxs_down, w4, 1, (int)D, (int)F, (bf16_t*)v.Wsd, stream);
+    }
+    uint8_t* xq = (uint8_t*)(base + L.mx_xq);
+    uint8_t* xs = (uint8_t*)(base + L.mx_xs);
+    if (e == hipSuccess) e = launch_mx_quantize(x, false, desc->T, desc->d, xq, xs, stream);
+    if (e == hipSuccess) e = launch_dequant_mx_rows(xq, xs, (long)desc->T * desc->d, (bf16_t*)(base + L.mx_xv), stream);
+    if ((st = hip_status(e, "block-scaled weight and input values")) != MOE_OK) return st;
+    a.w = v;
+    a.x_rows = base + L.mx_xv;
+    a.Hf = (float*)(base + L.mx_hf);
+    a.hq = (uint8_t*)(base + L.mx_hq);
+    a.hs = (uint8_t*)(base + L.mx_hs);
   }
   a.T = desc->T; a.d = desc->d; a.E = desc->E; a.k = desc->top_k; a.f = desc->f;
   a.has_shared = desc->has_shared; a.renormalize = desc->renormalize;

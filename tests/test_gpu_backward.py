@@ -21,10 +21,11 @@ else:  # collected on CPU hosts but never run there (marker)
 C = synth.CONFIGS
 TOL = 2e-2          # bf16 (and fp8-weight) layers
 TOL_F32 = 1e-5      # fp32 layers
+TOL_MX = 6e-2       # block-scaled layers (the forward's MXFP8 bar: H is requantised)
 
 
 def _tol(cfg):
-    return TOL_F32 if cfg.act == "f32" else TOL
+    return TOL_F32 if cfg.act == "f32" else TOL_MX if cfg.wdt in ("mxfp8", "mxfp4") else TOL
 
 CASES = {
     "prefill": C["mixtral_prefill"].with_(T=300, d=256, f=512, seed=40),
@@ -50,6 +51,11 @@ CASES = {
     "f32_tiny": C["tiny_f32"],
     "f32_shared_cap_renorm_off": C["tiny_f32"].with_(T=96, E=16, k=4, f=256, shared=True, renormalize=False,
                                                      capacity_factor=1.0, seed=60),
+    # block-scaled weights (MXFP8 x and H, MXFP8 or MXFP4 weights), straight-through quantisation
+    "mx8_finegrained_shared": C["fine_grained_mxfp8"].with_(T=96, d=512, E=32, f=256, seed=62),
+    "mx4_prefill": C["mixtral_prefill_mxfp4"].with_(T=300, d=256, f=512, seed=63),
+    "mx8_capacity_renorm_off": C["mixtral_prefill_mxfp8"].with_(T=120, d=256, E=8, f=256, capacity_factor=0.8,
+                                                                renormalize=False, seed=64),
 }
 
 WG_TILE_COST = 96      # the weight-gradient kernel's per-tile cost term (rows + this)
@@ -138,7 +144,7 @@ def test_backward_parity_small(name):
     dout = _dout(cfg)
     g = run_backward(inp, dout)
     ref = oracle.backward(ov.x, ov.W_g, ov.bias, cfg.k, cfg.renormalize, np.float32(cfg.capacity_factor),
-                          ov.expert, cfg.E, ov.shared(), to64(dout))
+                          ov.expert, cfg.E, ov.shared(), to64(dout), **ov.quant_hooks())
     errs = {}
     tol = _tol(cfg)
     for key in ("dx", "dW_g", "dW_gate", "dW_up", "dW_down"):
@@ -316,6 +322,7 @@ EC_CASES = {
     "ec_small_batch": C["mixtral_prefill"].with_(T=5, d=256, f=256, E=8, k=2, seed=56),
     "ec_fp8_shared": C["fp8_capacity"].with_(T=128, d=256, E=16, k=4, f=256, shared=True, seed=59),
     "ec_f32_shared": C["tiny_f32"].with_(T=80, E=16, k=4, f=256, shared=True, seed=61),
+    "ec_mx4_shared": C["fine_grained_mxfp4"].with_(T=96, d=512, E=32, f=256, seed=65),
 }
 
 
@@ -337,7 +344,8 @@ def test_backward_expert_choice_parity(name):
     dout = _dout(cfg)
     g = run_backward(inp, dout, ops.ROUTING_EXPERT_CHOICE)
     ref = oracle.expert_choice_backward(ov.x, ov.W_g, ov.bias, cfg.k, cfg.renormalize,
-                                        np.float32(cfg.capacity_factor), ov.expert, cfg.E, ov.shared(), to64(dout))
+                                        np.float32(cfg.capacity_factor), ov.expert, cfg.E, ov.shared(), to64(dout),
+                                        **ov.quant_hooks())
     assert np.array_equal(ref["pos"], r["pos"])
     errs = {}
     tol = _tol(cfg)
@@ -351,8 +359,10 @@ def test_backward_expert_choice_parity(name):
     taken = (r["pos"] >= 0).sum(axis=1)
     untaken = np.nonzero(taken == 0)[0]
     if len(untaken):                                    # tokens no expert took: only the shared expert's dx
-        want = (oracle.expert_ffn_backward(ov.x[untaken], *ov.shared(), to64(dout)[untaken])["dX"] if cfg.shared
-                else np.zeros((len(untaken), cfg.d)))
+        hk = ov.quant_hooks()
+        xu = hk["quant_x"](ov.x[untaken]) if hk else ov.x[untaken]
+        want = (oracle.expert_ffn_backward(xu, *ov.shared(), to64(dout)[untaken], quant_h=hk.get("quant_h"))["dX"]
+                if cfg.shared else np.zeros((len(untaken), cfg.d)))
         assert_close(to64(g["dx"])[untaken], want, tol, f"{name} dx of untaken tokens")
     g2 = run_backward(inp, dout, ops.ROUTING_EXPERT_CHOICE)
     for key in g:
