@@ -283,33 +283,31 @@ size_t moe_backward_workspace_size(const moe_desc* desc);
 
 /* Backward of moe_forward for layers with bf16 activations and bf16, fp8,
  * MXFP8 or MXFP4 weights, and for fp32 layers, token-choice or expert-choice
- * routing: given
- * dout = dL/dout [T, d] (act dtype), the gradients of L with respect to x, the
- * router weight and bias, and every expert's (and the shared expert's) three
- * matrices.  The expert selection
- * (top-k, capacity) is held fixed: gradients flow through the routing weights
- * (the softmax and its renormalisation over the chosen experts) and through
- * the chosen experts' SwiGLU FFNs; dropped assignments carry no gradient;
- * experts that received no token get zero gradients.  Expert choice ("MoE
- * Model Architectures", Design Patterns, Pattern 3): the tokens each expert
- * took are held fixed; a token's routing gradient runs over the experts that
- * took it (the full softmax, or its renormalisation over those experts), and
- * a token no expert took gets only the shared expert's gradient.  The routing
- * and the expert activations are recomputed from x (nothing is kept from the
- * forward).  fp8 weights: the gradients are with respect to the weights'
- * values (e4m3 code x channel scale; the scales get none), and the GEMMs run
- * on those values rounded once to bf16, kept in the workspace.  MXFP8 / MXFP4
- * weights: the same, with the values exact in bf16; the forward's MXFP8
- * quantisation of the expert inputs and of the activated rows is recomputed
- * and differentiated as the identity (straight through).  fp32 layers
- * compute every intermediate in fp32 (SIMT FMA; no bf16 rounding).  Weight
- * gradients are summed over each expert's tokens in a fixed order without
- * atomics: results are bitwise reproducible.  Pages: "Testing using
- * claude to graft ETHOS onto modded-nanogpt base", "Key Implementation
- * Details" (a backward that recomputes the forward values and accumulates each
- * weight gradient over the tokens that chose the expert); "Faster writing:
- * run only the chosen experts; uncap the large profile", "Test plan" (slot
- * gradients of the chosen-experts dispatch).
+ * routing: given dout = dL/dout [T, d] (act dtype), the gradients of L with
+ * respect to x, the router weight and bias, and every expert's (and the shared
+ * expert's) three matrices.  The expert selection (top-k, capacity) is held
+ * fixed: gradients flow through the routing weights (the softmax and its
+ * renormalisation over the chosen experts) and through the chosen experts'
+ * SwiGLU FFNs; dropped assignments carry no gradient; experts that received no
+ * token get zero gradients.  Expert choice ("MoE Model Architectures", Design
+ * Patterns, Pattern 3): the tokens each expert took are held fixed; a token's
+ * routing gradient runs over the experts that took it (the full softmax, or
+ * its renormalisation over those experts), and a token no expert took gets
+ * only the shared expert's gradient.  The routing and the expert activations
+ * are recomputed from x (nothing is kept from the forward).  fp8 weights: the
+ * gradients are with respect to the weights' values (e4m3 code x channel
+ * scale; the scales get none), and the GEMMs run on those values rounded once
+ * to bf16, kept in the workspace.  MXFP8 / MXFP4 weights: the same, with the
+ * values exact in bf16; the forward's MXFP8 quantisation of the expert inputs
+ * and of the activated rows is recomputed and differentiated as the identity
+ * (straight through).  fp32 layers compute every intermediate in fp32 (SIMT
+ * FMA; no bf16 rounding).  Weight gradients are summed over each expert's
+ * tokens in a fixed order without atomics: results are bitwise reproducible.
+ * Pages: "Testing using claude to graft ETHOS onto modded-nanogpt base", "Key
+ * Implementation Details" (a backward that recomputes the forward values and
+ * accumulates each weight gradient over the tokens that chose the expert);
+ * "Faster writing: run only the chosen experts; uncap the large profile",
+ * "Test plan" (slot gradients of the chosen-experts dispatch).
  *   x, dout  [T, d] act dtype;  w as for moe_forward;  grads as documented above
  *   ws       moe_backward_workspace_size(desc) bytes, 256-byte aligned
  * Returns MOE_ERR_UNSUPPORTED for dtype pairs the forward declines.
