@@ -44,7 +44,7 @@ def parse():
                     help="token choice (the pages' default) or expert choice (every expert takes its C best tokens)")
     ap.add_argument("--backward", action="store_true",
                     help="time moe_backward (dL/dx and every weight gradient for a random dout) instead "
-                         "of the forward; bf16 or fp8-weight layers, either routing")
+                         "of the forward; every layer dtype, either routing")
     ap.add_argument("--telemetry", action="store_true",
                     help="also request the router telemetry outputs (routed load, mean probability, "
                          "load-balancing loss) inside the timed region")
