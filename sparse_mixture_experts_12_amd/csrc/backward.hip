@@ -1,5 +1,6 @@
-// Backward of the token-choice layer on gfx950: everything around the grouped
-// GEMMs of bwd_gemm.hip.
+// Backward of the layer on gfx950: everything around the grouped GEMMs of
+// bwd_gemm.hip, for token-choice and expert-choice routing and every layer
+// dtype the forward takes.
 //
 // Pages: "MoE Model Architectures", Mixtral "Sparse MoE Block" (softmax, top-k,
 // divide by the top-k sum, weighted sum of the chosen experts: the forward
@@ -26,6 +27,11 @@
 // in ascending expert order), and the same two router formulas apply over
 // that list (renormalised: a softmax over the experts that took the token;
 // else the full softmax).
+// Weight dtypes: fp8 layers differentiate with respect to the weights' values
+// (code x channel scale), MXFP8 / MXFP4 layers likewise, with the forward's
+// MXFP8 quantisation of x and H recomputed and passed straight through; both
+// run the bf16 GEMMs on a bf16 copy of the values written first.  fp32 layers
+// keep every intermediate in fp32 and use the SIMT fp32 GEMMs.
 // Every sum runs in a fixed order: the result is bitwise reproducible.
 #include <type_traits>
 
