@@ -172,7 +172,8 @@ def test_backward_parity_small(name):
           f" empty_experts={len(empty)}", flush=True)
 
 
-@pytest.mark.parametrize("name", ["prefill", "renorm_off_shared_cap"])
+@pytest.mark.parametrize("name", ["prefill", "renorm_off_shared_cap", "fp8_capacity_shared", "f32_tiny",
+                                  "mx8_finegrained_shared", "mx4_prefill"])
 def test_backward_bitwise_deterministic(name):
     inp = device_inputs(CASES[name])
     dout = _dout(CASES[name])
