@@ -578,6 +578,137 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
 }
 
 // ---------------------------------------------------------------------------
+// fp32 layer, few tiles: 64-row x 16-column tiles whose K range is split over
+// the 256 threads as 16 columns x 16 K parts.  Small fp32 layers (a few rows
+// per expert) give the 64 x 64 kernel fewer work-groups than CUs, each with a
+// long dependent K loop in which every B value read from LDS feeds only a
+// handful of rows; here four times as many work-groups each run a quarter of
+// the columns, a thread reads its own column of B straight from memory
+// (16 lanes -> 64 contiguous bytes) and the tile's A rows come from LDS as
+// broadcasts.  K moves in steps of 128 (8 per part; a last step of 64 gives 4),
+// the next step's loads in flight during the current step's FMAs.  The 16 part
+// sums of each output are added in part order through LDS (deterministic);
+// the gate/up GEMM applies SwiGLU to the two finished sums.
+// ---------------------------------------------------------------------------
+template <bool DUAL, int R>
+__device__ __forceinline__ void f32_narrow_tile(const GemmParamsF32& p, int g, int row0, int rows, int nt,
+                                                float* As /* LDS [64][132] */) {
+  constexpr int NMAT = DUAL ? 2 : 1;
+  constexpr int KS = 128, LDA = KS + 4;
+  constexpr int NA = R / 8;                        // A float4 loads per thread per step
+  const int tid = threadIdx.x;
+  const int c = tid & 15, part = tid >> 4;
+  const int n0 = nt * 16;
+  const bool shared = (g == p.E);
+  const size_t goff = shared ? 0 : (size_t)g * p.K * p.N;
+  const float* Bm[NMAT];
+  Bm[0] = (shared ? p.Ws0 : p.W0 + goff) + n0 + c;
+  if (DUAL) Bm[DUAL ? 1 : 0] = (shared ? p.Ws1 : p.W1 + goff) + n0 + c;
+  // A: load i of this thread covers tile row tid / 32 + 8 i, float4 tid % 32
+  // of the step; rows past the tile's rows read its first row (never stored)
+  const float* arow[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int r = tid / 32 + 8 * i;
+    const int grow = row0 + (r < rows ? r : 0);
+    if (DUAL) {
+      const int tok = shared ? (grow - p.shared_row0) : (p.sorted_assign[grow] / p.k);
+      arow[i] = p.x + (size_t)tok * p.K + 4 * (tid % 32);
+    } else {
+      arow[i] = p.a_rows + (size_t)grow * p.K + 4 * (tid % 32);
+    }
+  }
+  f32x4_t va[NA];
+  float vb[NMAT][8];
+  // loads of the step at k0 (kp = 8 values per part, 4 on a last step of 64)
+  auto load = [&](int k0, int kp) {
+    const bool full = kp == 8;
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      va[i] = (full || (tid % 32) < 16) ? *reinterpret_cast<const f32x4_t*>(arow[i] + k0) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        vb[m][j] = (j < kp) ? Bm[m][(size_t)(k0 + part * kp + j) * p.N] : 0.f;
+  };
+  float acc[NMAT][R];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[m][r] = 0.f;
+  int kp = p.K >= KS ? 8 : 4;
+  load(0, kp);
+  for (int k0 = 0; k0 < p.K; k0 += KS) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      *reinterpret_cast<f32x4_t*>(As + (tid / 32 + 8 * i) * LDA + 4 * (tid % 32)) = va[i];
+    float b[NMAT][8];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b[m][j] = vb[m][j];
+    const int kcur = kp;
+    __syncthreads();
+    const int kn = k0 + KS;
+    if (kn < p.K) {
+      kp = p.K - kn >= KS ? 8 : 4;
+      load(kn, kp);                                // next step's loads fly during this step's FMAs
+    }
+    // this part's K values of the step: LDS columns part * kcur .. + kcur - 1
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h == 1 && kcur == 4) break;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const f32x4_t a4 = *reinterpret_cast<const f32x4_t*>(As + r * LDA + part * kcur + 4 * h);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) acc[m][r] = __fmaf_rn(a4[j], b[m][4 * h + j], acc[m][r]);
+      }
+    }
+    __syncthreads();
+  }
+  // part sums through LDS, 16 rows at a time: red[part][m][row][col]
+  float* red = As;
+#pragma unroll
+  for (int r0 = 0; r0 < R; r0 += 16) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[((part * NMAT + m) * 16 + r) * 16 + c] = acc[m][r0 + r];
+    __syncthreads();
+    const int rr = tid >> 4;                       // output row r0 + rr, column c
+    float sum[NMAT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      sum[m] = 0.f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) sum[m] += red[((q * NMAT + m) * 16 + rr) * 16 + c];
+    }
+    const int r = r0 + rr;
+    if (r < rows) {
+      const size_t o = (size_t)(row0 + r) * p.N + n0 + c;
+      if (DUAL) p.h_out[o] = silu_f(sum[0]) * sum[DUAL ? 1 : 0];
+      else p.y_out[o] = sum[0];
+    }
+    __syncthreads();
+  }
+}
+
+template <bool DUAL>
+__global__ __launch_bounds__(256) void gemm_f32_narrow_kernel(GemmParamsF32 p) {
+  __shared__ __attribute__((aligned(16))) float As[64 * 132];
+  const int n_tiles = p.N / 16;
+  int g, row0, rows, nt;
+  if (!decode_tile(p.sched, p.maxQ, p.E, n_tiles, &g, &row0, &rows, &nt)) return;
+  if (rows <= 16) f32_narrow_tile<DUAL, 16>(p, g, row0, rows, nt, As);
+  else if (rows <= 32) f32_narrow_tile<DUAL, 32>(p, g, row0, rows, nt, As);
+  else f32_narrow_tile<DUAL, 64>(p, g, row0, rows, nt, As);
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 // direct-to-LDS bf16 kernels: K columns per step and LDS ring depth.
@@ -743,16 +874,24 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
     p.sched = a.sched;
     p.maxQ = maxQ;
     p.T = a.T; p.k = a.assign_div; p.E = a.E; p.shared_row0 = shared_row0;
+    // a GEMM whose 64 x 64 tiles (at most maxQ x N / 64) would not give every
+    // CU a work-group runs the 16-column kernel with its K split over threads
+    const auto narrow = [&](int N) { return (long)maxQ * (N / 64) < device_cus(); };
     // gate/up
     p.W0 = (const float*)a.w.Wg; p.W1 = (const float*)a.w.Wu;
     p.Ws0 = (const float*)a.w.Wsg; p.Ws1 = (const float*)a.w.Wsu;
     p.K = a.d; p.N = a.f;
     p.h_out = (float*)a.h;
-    if (a.ev_begin || a.ev_end)
-      hipExtLaunchKernelGGL(gemm_f32_kernel<true>, dim3(grouped_grid(maxQ, (a.f + 63) / 64)), dim3(256), 0, s,
-                            a.ev_begin, a.ev_end, 0, p);
-    else
-      gemm_f32_kernel<true><<<grouped_grid(maxQ, (a.f + 63) / 64), 256, 0, s>>>(p);
+    const bool ng = narrow(a.f);
+    const dim3 gg(grouped_grid(maxQ, ng ? a.f / 16 : (a.f + 63) / 64));
+    const void* kg = ng ? (const void*)gemm_f32_narrow_kernel<true> : (const void*)gemm_f32_kernel<true>;
+    if (a.ev_begin || a.ev_end) {
+      if (ng) hipExtLaunchKernelGGL(gemm_f32_narrow_kernel<true>, gg, dim3(256), 0, s, a.ev_begin, a.ev_end, 0, p);
+      else hipExtLaunchKernelGGL(gemm_f32_kernel<true>, gg, dim3(256), 0, s, a.ev_begin, a.ev_end, 0, p);
+    } else {
+      void* args[] = {&p};
+      if ((err = hipLaunchKernel(kg, gg, dim3(256), args, 0, s)) != hipSuccess) return err;
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // down
     GemmParamsF32 q = p;
@@ -761,7 +900,8 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
     q.W1 = nullptr; q.Ws1 = nullptr;
     q.K = a.f; q.N = a.d;
     q.y_out = a.y;
-    gemm_f32_kernel<false><<<grouped_grid(maxQ, (a.d + 63) / 64), 256, 0, s>>>(q);
+    if (narrow(a.d)) gemm_f32_narrow_kernel<false><<<grouped_grid(maxQ, a.d / 16), 256, 0, s>>>(q);
+    else gemm_f32_kernel<false><<<grouped_grid(maxQ, (a.d + 63) / 64), 256, 0, s>>>(q);
     return hipGetLastError();
   }
 

@@ -16,23 +16,24 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Large-T router logits as fp64 partial sums over slices of the hidden
+// Router logits for T > 8 as fp64 partial sums over slices of the hidden
 // dimension (split-K), finished by the top-k kernel, which adds the slices in
 // a fixed order:
 //   part[z][t][e] = sum over rows r of slice z of x[t, r] * W_g[r, e]   (fp64)
-// ---------------------------------------------------------------------------
-// ---------------------------------------------------------------------------
+//
 // Partial logits on the fp64 matrix cores (v_mfma_f64_16x16x4f64).  The
 // products of bf16 or fp32 inputs are exact in fp64, so these partial sums
 // differ from a sequential fp64 sum only in the order of the additions.
 // Operand layout (checked on gfx950): A lane l = A[l % 16][l / 16],
 // B lane l = B[l / 16][l % 16], result lane l, register v = D[l / 16 + 4 v][l % 16].
-// Work-group tile BT tokens x BE experts (64 x 64, or 256 x 16 for few
-// experts), K step 16, operands staged in LDS as fp32 (exact) with padded
-// rows so that the 4 K-rows read by one fragment load fall in distinct banks.
+// Large layers (router_partial_lds): work-group tile BT tokens x BE experts
+// (64 x 64, or 256 x 16 for few experts), K step 16, operands staged in LDS as
+// fp32 (exact) with padded rows so that the 4 K-rows read by one fragment load
+// fall in distinct banks; each operand value is read from L2 by E / BE or
+// T / BT work-groups.
 // ---------------------------------------------------------------------------
 template <typename TIn, int BE>
-__global__ __launch_bounds__(256) void router_partial_mfma(const TIn* __restrict__ x, const TIn* __restrict__ W,
+__global__ __launch_bounds__(256) void router_partial_lds(const TIn* __restrict__ x, const TIn* __restrict__ W,
                                                            double* __restrict__ part, int T, int d, int E,
                                                            int dsplit) {
   typedef double f64x4_t __attribute__((ext_vector_type(4)));
@@ -116,6 +117,92 @@ __global__ __launch_bounds__(256) void router_partial_mfma(const TIn* __restrict
         const int e = e0 + wn * (BE / WN) + j * 16 + fr;
         if (t < T && e < E) part[((size_t)z * T + t) * E + e] = acc[i][j][v];
       }
+}
+
+// ---------------------------------------------------------------------------
+// Small layers (router_partial_tile, fewer than 128 tiles of 16 x 16):
+// one work-group computes 16 tokens x 16 experts over its K slice; the slice
+// is dealt to the four waves in 32-wide chunks (chunk c to wave c mod 4) and
+// the waves' sums are added in wave order through LDS.  In MFMA step s of the
+// chunk at k0, lane l supplies A = x[t0 + l % 16][k0 + 8 (l / 16) + s] and
+// B = W_g[k0 + 8 (l / 16) + s][e0 + l % 16]; both operands index K the same
+// way, so the eight steps add the chunk's 32 products of every (token,
+// expert) pair.  A lane's eight x values are one contiguous 16-byte (bf16) or
+// 32-byte (fp32) load; the next chunk's loads are in flight during the
+// current chunk's MFMAs.  No LDS staging and four waves per 256 outputs: more
+// work-groups than the 64 x 64 tiles give when T x E is small, at the price
+// of 4x (16 / 64) more L2 reads per operand, which is why large layers keep
+// the LDS-staged tiles (measured on MI355X: Mixtral prefill 20 us LDS-staged
+// vs 36 us with 16 x 16 tiles; the tiny fp32 layer 6.5 vs 4.9 us).
+// ---------------------------------------------------------------------------
+template <typename TIn>
+__device__ __forceinline__ void load_x8(const TIn* p, float* v) {
+  if constexpr (sizeof(TIn) == 2) {
+    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16lo(w[i]);
+      v[2 * i + 1] = bf16hi(w[i]);
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(256) void router_partial_tile(const TIn* __restrict__ x, const TIn* __restrict__ W,
+                                                           double* __restrict__ part, int T, int d, int E,
+                                                           int dsplit) {
+  typedef double f64x4_t __attribute__((ext_vector_type(4)));
+  __shared__ double red[3][4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16, z = blockIdx.z;
+  const int r_begin = z * dsplit;
+  const int r_end = min(d, r_begin + dsplit);            // r_end - r_begin is a multiple of 32
+  const int m = lane & 15, kg = lane >> 4;
+  // rows past T and experts past E read clamped addresses; they only reach
+  // output rows / columns that are never stored
+  const TIn* xrow = x + (size_t)min(t0 + m, T - 1) * d + 8 * kg;
+  const TIn* wcol = W + min(e0 + m, E - 1) + (size_t)(8 * kg) * E;
+  auto load = [&](int k0, float* xv, float* wv) {
+    load_x8<TIn>(xrow + k0, xv);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) wv[s] = ActTraits<TIn>::load(wcol, (size_t)(k0 + s) * E);
+  };
+  f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+  float xc[8], wc[8], xn[8], wn[8];
+  int k0 = r_begin + 32 * wave;
+  if (k0 < r_end) load(k0, xc, wc);
+  for (; k0 < r_end; k0 += 128) {
+    const bool more = k0 + 128 < r_end;
+    if (more) load(k0 + 128, xn, wn);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xc[s], (double)wc[s], acc, 0, 0, 0);
+    if (more) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        xc[s] = xn[s];
+        wc[s] = wn[s];
+      }
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave - 1][v][lane] = acc[v];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const double sum = ((acc[v] + red[0][v][lane]) + red[1][v][lane]) + red[2][v][lane];
+      const int t = t0 + kg + 4 * v;
+      const int e = e0 + m;
+      if (t < T && e < E) part[((size_t)z * T + t) * E + e] = sum;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -538,6 +625,8 @@ __global__ __launch_bounds__(kSmallThreads) void route_small_kernel(
 
 // One wave per token: add the S fp64 partial sums of each logit in slice
 // order, add the bias, round once to fp32, then top-k and weights.
+// ZB slices' loads are in flight together (4 for S <= 4, else 32).
+template <int ZB>
 __global__ __launch_bounds__(256) void topk_finalize_kernel(const double* __restrict__ part, int S,
                                                             const float* __restrict__ bias, int T, int E, int k,
                                                             int renormalize, float* __restrict__ logits,
@@ -549,9 +638,8 @@ __global__ __launch_bounds__(256) void topk_finalize_kernel(const double* __rest
   const int t = blockIdx.x * 4 + wv;
   if (t >= T) return;     // whole wave leaves together; no block barrier follows
   // the slices of up to two experts per lane are loaded together (one memory
-  // round trip for S <= 32, padding loads repeat a valid address) and added
+  // round trip for S <= ZB, padding loads repeat a valid address) and added
   // in slice order
-  constexpr int ZB = 32;
   for (int e0 = lane; e0 < E; e0 += 128) {
     const int e1 = e0 + 64;
     const int e1c = e1 < E ? e1 : e0;
@@ -594,19 +682,25 @@ __global__ __launch_bounds__(256) void topk_finalize_kernel(const double* __rest
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-// Split of the hidden dimension for the large-T router: the few-expert kernel
-// stages at most 8192/EP rows of W_g per work-group; the many-expert kernel
-// splits until about 512 work-groups are in flight (at least 256 rows each).
-// K split of the partial-logit kernel: enough work-groups (>= 512) to fill
-// the chip, each K range a multiple of 16 and at least 64 long.
+// Tiles of 16 x 16 below which the small-layer partial kernel runs.
+constexpr long kTileRouterMaxTiles = 128;
+
+static bool tile_router(int T, int E) { return (long)((T + 15) / 16) * ((E + 15) / 16) < kTileRouterMaxTiles; }
+
+// K split of the partial-logit kernels.  LDS-staged tiles: enough work-groups
+// (>= 512) to fill the chip, each K range a multiple of 16 and at least 64
+// long.  16 x 16 tiles: about 256 work-groups (one wave per SIMD), each slice
+// at least 128 long (one 32-wide chunk per wave) and a multiple of 32.
 static void router_split(int T, int d, int E, int* S, int* dsplit) {
-  const int bt = E <= 16 ? 256 : 64, be = E <= 16 ? 16 : 64;
+  const bool tile = tile_router(T, E);
+  const int bt = tile ? 16 : (E <= 16 ? 256 : 64), be = tile ? 16 : (E <= 16 ? 16 : 64);
+  const long target = tile ? 256 : 512, minlen = tile ? 128 : 64, align = tile ? 32 : 16;
   const long nblk = (long)((T + bt - 1) / bt) * ((E + be - 1) / be);
-  long s = (512 + nblk - 1) / nblk;
-  const long smax = d / 64;
+  long s = (target + nblk - 1) / nblk;
+  const long smax = d / minlen > 0 ? d / minlen : 1;
   s = s < 1 ? 1 : (s > smax ? smax : s);
   const int ds = (int)((d + s - 1) / s);
-  *dsplit = (ds + 15) / 16 * 16;
+  *dsplit = (int)((ds + align - 1) / align * align);
   *S = (d + *dsplit - 1) / *dsplit;
 }
 
@@ -641,10 +735,12 @@ static hipError_t launch_partials(const void* x, const void* W, double* part, in
                                   hipStream_t s) {
   const TIn* xp = (const TIn*)x;
   const TIn* wp = (const TIn*)W;
-  if (E <= 16)
-    router_partial_mfma<TIn, 16><<<dim3((T + 255) / 256, (E + 15) / 16, S), 256, 0, s>>>(xp, wp, part, T, d, E, ds);
+  if (tile_router(T, E))
+    router_partial_tile<TIn><<<dim3((T + 15) / 16, (E + 15) / 16, S), 256, 0, s>>>(xp, wp, part, T, d, E, ds);
+  else if (E <= 16)
+    router_partial_lds<TIn, 16><<<dim3((T + 255) / 256, (E + 15) / 16, S), 256, 0, s>>>(xp, wp, part, T, d, E, ds);
   else
-    router_partial_mfma<TIn, 64><<<dim3((T + 63) / 64, (E + 63) / 64, S), 256, 0, s>>>(xp, wp, part, T, d, E, ds);
+    router_partial_lds<TIn, 64><<<dim3((T + 63) / 64, (E + 63) / 64, S), 256, 0, s>>>(xp, wp, part, T, d, E, ds);
   return hipGetLastError();
 }
 
@@ -681,8 +777,12 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   hipError_t err = a.act_f32 ? launch_partials<float>(a.x, a.W_g, a.part, a.T, a.d, a.E, S, ds, s)
                              : launch_partials<bf16_t>(a.x, a.W_g, a.part, a.T, a.d, a.E, S, ds, s);
   if (err != hipSuccess) return err;
-  topk_finalize_kernel<<<(a.T + 3) / 4, 256, 0, s>>>(a.part, S, a.bias, a.T, a.E, a.k, a.renormalize, a.logits,
-                                                     a.idx, a.w);
+  if (S <= 4)
+    topk_finalize_kernel<4><<<(a.T + 3) / 4, 256, 0, s>>>(a.part, S, a.bias, a.T, a.E, a.k, a.renormalize, a.logits,
+                                                          a.idx, a.w);
+  else
+    topk_finalize_kernel<32><<<(a.T + 3) / 4, 256, 0, s>>>(a.part, S, a.bias, a.T, a.E, a.k, a.renormalize,
+                                                           a.logits, a.idx, a.w);
   return hipGetLastError();
 }
 

@@ -26,6 +26,11 @@ C = synth.CONFIGS
 SMALL = {
     "tiny_f32": C["tiny_f32"],
     "tiny_f32_ragged": C["tiny_f32"].with_(T=77, seed=3),
+    # fp32: the shared expert's 64- and 32-row tiles with capacity drops (16-column
+    # kernel), and a layer whose gate/up GEMM has enough 64 x 64 tiles for the
+    # 64-column kernel while its down GEMM takes the 16-column one with K = 1024
+    "f32_shared_cap": C["tiny_f32"].with_(T=96, E=16, k=4, f=256, shared=True, capacity_factor=1.25, seed=30),
+    "f32_wide": C["tiny_f32"].with_(T=512, d=512, f=1024, seed=31),
     "bf16_prefill": C["mixtral_prefill"].with_(T=300, d=512, f=1024),
     "bf16_prefill_ragged": C["mixtral_prefill"].with_(T=133, d=256, f=768, seed=5),
     "bf16_finegrained_shared": C["fine_grained"].with_(T=96, d=512, E=32, f=256),
@@ -286,7 +291,7 @@ def test_permute_all_to_one_expert_with_capacity():
 # ---------------------------------------------------------------------------
 # Grouped FFN, given the oracle's permutation
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["tiny_f32", "tiny_f32_ragged", "bf16_prefill", "bf16_prefill_ragged",
+@pytest.mark.parametrize("name", ["tiny_f32", "tiny_f32_ragged", "f32_shared_cap", "f32_wide", "bf16_prefill", "bf16_prefill_ragged",
                                   "bf16_finegrained_shared", "fp8_capacity", "fp8_capacity_tight",
                                   "bf16_one_expert", "bf16_big_tiles", "bf16_big_tiles_mid",
                                   "bf16_big_tiles_shared", "fp8_big_tiles_shared", "mx_prefill", "mx_big_tiles",
