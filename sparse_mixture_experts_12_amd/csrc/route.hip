@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void router_partial_lds(const TIn* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Small layers (router_partial_tile, fewer than 128 tiles of 16 x 16):
+// Small layers (router_partial_tile, at most 256 tiles of 16 x 16):
 // one work-group computes 16 tokens x 16 experts over its K slice; the slice
 // is dealt to the four waves in 32-wide chunks (chunk c to wave c mod 4) and
 // the waves' sums are added in wave order through LDS.  In MFMA step s of the
@@ -128,12 +128,14 @@ __global__ __launch_bounds__(256) void router_partial_lds(const TIn* __restrict_
 // B = W_g[k0 + 8 (l / 16) + s][e0 + l % 16]; both operands index K the same
 // way, so the eight steps add the chunk's 32 products of every (token,
 // expert) pair.  A lane's eight x values are one contiguous 16-byte (bf16) or
-// 32-byte (fp32) load; the next chunk's loads are in flight during the
-// current chunk's MFMAs.  No LDS staging and four waves per 256 outputs: more
+// 32-byte (fp32) load; the next two chunks' loads are in flight during a
+// chunk's MFMAs.  No LDS staging and four waves per 256 outputs: more
 // work-groups than the 64 x 64 tiles give when T x E is small, at the price
 // of 4x (16 / 64) more L2 reads per operand, which is why large layers keep
-// the LDS-staged tiles (measured on MI355X: Mixtral prefill 20 us LDS-staged
-// vs 36 us with 16 x 16 tiles; the tiny fp32 layer 6.5 vs 4.9 us).
+// the LDS-staged tiles.  Measured on MI355X, partial + top-k kernels: tiny
+// fp32 layer (T 64, E 8) 15.0 -> 8.6 us, fp8 layer (T 512, E 128) 23.9 ->
+// 19.7 us, Mixtral prefill (T 4096, E 8) 36.3 -> 30.6 us; the fine-grained
+// layer (T 2048, E 256, 2048 tiles) was slower with these tiles (190 -> 210 us).
 // ---------------------------------------------------------------------------
 template <typename TIn>
 __device__ __forceinline__ void load_x8(const TIn* p, float* v) {
@@ -173,20 +175,24 @@ __global__ __launch_bounds__(256) void router_partial_tile(const TIn* __restrict
     for (int s = 0; s < 8; ++s) wv[s] = ActTraits<TIn>::load(wcol, (size_t)(k0 + s) * E);
   };
   f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
-  float xc[8], wc[8], xn[8], wn[8];
-  int k0 = r_begin + 32 * wave;
-  if (k0 < r_end) load(k0, xc, wc);
-  for (; k0 < r_end; k0 += 128) {
-    const bool more = k0 + 128 < r_end;
-    if (more) load(k0 + 128, xn, wn);
+  auto mfmas = [&](const float* xv, const float* wv) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xc[s], (double)wc[s], acc, 0, 0, 0);
-    if (more) {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        xc[s] = xn[s];
-        wc[s] = wn[s];
-      }
+    for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[s], (double)wv[s], acc, 0, 0, 0);
+  };
+  // this wave's chunks start at k_i = r_begin + 32 wave + 128 i; two buffers,
+  // each refilled right after its MFMAs, so two chunks' loads are in flight
+  // while a chunk's MFMAs run
+  const int kw = r_begin + 32 * wave;
+  const int n = kw < r_end ? (r_end - kw + 127) / 128 : 0;
+  float x0[8], w0[8], x1[8], w1[8];
+  if (n > 0) load(kw, x0, w0);
+  if (n > 1) load(kw + 128, x1, w1);
+  for (int i = 0; i < n; i += 2) {
+    mfmas(x0, w0);
+    if (i + 2 < n) load(kw + 128 * (i + 2), x0, w0);
+    if (i + 1 < n) {
+      mfmas(x1, w1);
+      if (i + 3 < n) load(kw + 128 * (i + 3), x1, w1);
     }
   }
   if (wave > 0) {
@@ -682,19 +688,19 @@ __global__ __launch_bounds__(256) void topk_finalize_kernel(const double* __rest
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-// Tiles of 16 x 16 below which the small-layer partial kernel runs.
-constexpr long kTileRouterMaxTiles = 128;
+// Layers of at most this many 16 x 16 tiles run the small-layer partial kernel.
+constexpr long kTileRouterMaxTiles = 256;
 
-static bool tile_router(int T, int E) { return (long)((T + 15) / 16) * ((E + 15) / 16) < kTileRouterMaxTiles; }
+static bool tile_router(int T, int E) { return (long)((T + 15) / 16) * ((E + 15) / 16) <= kTileRouterMaxTiles; }
 
 // K split of the partial-logit kernels.  LDS-staged tiles: enough work-groups
 // (>= 512) to fill the chip, each K range a multiple of 16 and at least 64
-// long.  16 x 16 tiles: about 256 work-groups (one wave per SIMD), each slice
-// at least 128 long (one 32-wide chunk per wave) and a multiple of 32.
+// long.  16 x 16 tiles: about 1024 work-groups (four waves per SIMD), each
+// slice at least 256 long (two 32-wide chunks per wave) and a multiple of 32.
 static void router_split(int T, int d, int E, int* S, int* dsplit) {
   const bool tile = tile_router(T, E);
   const int bt = tile ? 16 : (E <= 16 ? 256 : 64), be = tile ? 16 : (E <= 16 ? 16 : 64);
-  const long target = tile ? 256 : 512, minlen = tile ? 128 : 64, align = tile ? 32 : 16;
+  const long target = tile ? 1024 : 512, minlen = tile ? 256 : 64, align = tile ? 32 : 16;
   const long nblk = (long)((T + bt - 1) / bt) * ((E + be - 1) / be);
   long s = (target + nblk - 1) / nblk;
   const long smax = d / minlen > 0 ? d / minlen : 1;
