@@ -55,6 +55,10 @@ def parse():
                          "them under the \"workloads\" key)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (for HBM counter scaling)")
+    ap.add_argument("--probe", action="store_true",
+                    help="instead of the layer, time the roofline probes (libmoe_probe.so): a pure HBM read stream "
+                         "and back-to-back bf16 MFMAs on register operands (random and zero data), the ceilings "
+                         "this part sustains")
     ap.add_argument("--library-gemm", action="store_true",
                     help="instead of the layer, time torch.mm (hipBLASLt) on the workload's per-expert gate/up "
                          "and down GEMM shapes with balanced routing: the vendor library's rate on this part, "
@@ -622,6 +626,58 @@ def workload_row(line):
             "mfma_frac": r.get("mfma_frac"), "hbm_frac": r.get("hbm_frac"), "traffic": r["traffic"]}
 
 
+def bench_probe(args):
+    """Roofline probes: HBM read rate of a 4 GiB stream, and the bf16 MFMA rate on
+    register operands (no memory traffic) with random and with zero data."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_mixture_experts_12_amd", "libmoe_probe.so"))
+    lib.probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    steps = args.steps or 10
+    warmup = args.warmup if args.warmup is not None else 3
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(steps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    out = {"probe": "roofline", "steps": steps, "warmup": warmup}
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.view(torch.int32).random_()
+    rd = {}
+    for grid in (2048, 8192, 32768, 131072):
+        sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+        ms = timed(lambda: lib.probe_hbm_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, sp))
+        rd[grid] = nbytes / (ms * 1e-3) / 1e9
+    best = max(rd, key=rd.get)
+    out["hbm_read"] = {"bytes": nbytes, "GBps_by_grid": {str(g): round(v, 1) for g, v in rd.items()},
+                       "best_GBps": round(rd[best], 1), "frac_of_8TBps": round(rd[best] / HBM_PEAK_GBS, 4)}
+    del buf
+    grid, iters = 2048, 4096
+    flops = grid * 4 * iters * 8 * 32768
+    res = {}
+    for kind in ("random", "zero"):
+        src = torch.randn(grid * 256 * 64, device="cuda").to(torch.bfloat16)
+        if kind == "zero":
+            src.zero_()
+        o = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+        ms = timed(lambda: lib.probe_mfma_bf16(src.data_ptr(), grid, iters, o.data_ptr(), sp))
+        tf = flops / (ms * 1e-3) / 1e12
+        res[kind] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1), "frac_of_2500": round(tf / BF16_PEAK_TFLOPS, 4)}
+    out["mfma_bf16_register_only"] = {"grid": grid, "iters": iters, "flops": flops, **res}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -631,6 +687,8 @@ def main():
     import torch
     import synth
 
+    if args.probe:
+        return bench_probe(args)
     cfg = synth.CONFIGS[args.workload]
     if args.library_gemm:
         return bench_library_gemm(args, cfg)

@@ -1,4 +1,6 @@
-"""Build libmoe.so (the gfx950 HIP kernels + C ABI) in-tree with hipcc.
+"""Build libmoe.so (the gfx950 HIP kernels + C ABI) in-tree with hipcc, and
+libmoe_probe.so (the roofline probes bench.py --probe times; not part of the
+layer).
 
 Every source compiles to its own object in parallel (each carries its own
 gfx950 code object), then hipcc links the shared library."""
@@ -13,6 +15,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmoe.so")
+PROBE_LIB = os.path.join(PKG, "libmoe_probe.so")
+PROBE_SRC = os.path.join(PKG, "csrc", "probe", "roofline_probe.hip")
 OBJ_DIR = os.path.join(ROOT, "_build")
 
 HIPCC_FLAGS = [
@@ -55,5 +59,14 @@ def build(verbose: bool = False, out: str = LIB, extra=(), jobs: int = 0) -> str
     return out
 
 
+def build_probe(verbose: bool = False, out: str = PROBE_LIB) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = out + ".tmp"
+    _run([hipcc, *HIPCC_FLAGS, "-shared", PROBE_SRC, "-o", tmp], verbose)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probe(verbose=True))

@@ -31,6 +31,26 @@ def test_library_exports_every_header_symbol(ops):
         assert hasattr(ops.LIB, n), n
 
 
+def test_probe_library_exports_its_header_symbols():
+    """libmoe_probe.so (the roofline probes bench.py --probe times) exports
+    what include/moe_probe.h declares and rejects bad arguments before any
+    launch."""
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "moe_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(probe_[a-z0-9_]+)\s*\(", src)))
+    assert names == ["probe_hbm_read", "probe_mfma_bf16"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_mixture_experts_12_amd", "libmoe_probe.so"))
+    for n in names:
+        assert hasattr(lib, n), n
+    lib.probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    invalid = 1   # hipErrorInvalidValue
+    assert lib.probe_hbm_read(None, 1 << 20, None, 8, None) == invalid
+    assert lib.probe_hbm_read(16, 100, 16, 8, None) == invalid          # not a multiple of 32 KB
+    assert lib.probe_hbm_read(16, 1 << 20, 16, 0, None) == invalid
+    assert lib.probe_mfma_bf16(16, 8, 3, 16, None) == invalid           # odd iteration count
+    assert lib.probe_mfma_bf16(None, 8, 4, 16, None) == invalid
+
+
 def test_capacity_matches_oracle(ops):
     for (T, k, E, cf) in [(512, 8, 128, 1.25), (1, 8, 128, 1.25), (64, 2, 8, 0.0), (10, 1, 4, 1.0),
                           (7, 3, 5, 0.01), (4096, 2, 8, 1.1)]:
