@@ -107,7 +107,9 @@ ROUTE_CASES = {**{k: v for k, v in C.items()},
                "E_1": C["mixtral_prefill"].with_(T=17, E=1, k=1),
                # edges of the accepted ranges: E = 1023 with top-32, d = 64
                "E_1023_k32": C["fine_grained"].with_(T=70, d=128, E=1023, k=32),
-               "d_64": C["mixtral_prefill"].with_(T=100, d=64, E=16, k=4, seed=3)}
+               "d_64": C["mixtral_prefill"].with_(T=100, d=64, E=16, k=4, seed=3),
+               # more than 256 tiles of 16 x 16 with E <= 16: the LDS-staged 256 x 16 partial tiles
+               "lds_few_experts": C["mixtral_prefill"].with_(T=4200, d=512, E=16, k=4, seed=11)}
 
 
 @pytest.mark.parametrize("name", list(ROUTE_CASES))
