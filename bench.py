@@ -549,7 +549,7 @@ def measure(args, cfg, steps=None, warmup=None, cpu=True, graph=True, copy_calib
             kbytes = n_exp * (2 * cfg.d * cfg.f * es + scales) + cfg.T * cfg.d * ae + rows * cfg.f * ae
         peak_f = FP32_PEAK_TFLOPS if f32 else (FP8_PEAK_TFLOPS if mx else BF16_PEAK_TFLOPS)
         ridge = peak_f * 1e12 / (HBM_PEAK_GBS * 1e9)
-        kname = ("gemm_f32_kernel" if f32 else "gemm_mx_kernel" if mx else
+        kname = ("gemm_f32_*kernel" if f32 else "gemm_mx_kernel" if mx else
                  "gemm_dl_kernel")
         t = kern_ms / 1e3 if have_k else None
         if kflops / kbytes >= ridge:
