@@ -655,11 +655,13 @@ def bench_probe(args):
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     buf.view(torch.int32).random_()
     rd = {}
-    for grid in (2048, 8192, 32768, 131072):
+    for grid in (64, 128, 256, 512, 1024, 2048, 8192, 32768, 131072):
         sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
         ms = timed(lambda: lib.probe_hbm_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, sp))
         rd[grid] = nbytes / (ms * 1e-3) / 1e9
     best = max(rd, key=rd.get)
+    # grids of at most 256 work-groups put one on each of that many CUs: the per-CU streaming rate
+    out["hbm_read_per_cu_GBps"] = {str(g): round(v / g, 2) for g, v in rd.items() if g <= 256}
     out["hbm_read"] = {"bytes": nbytes, "GBps_by_grid": {str(g): round(v, 1) for g, v in rd.items()},
                        "best_GBps": round(rd[best], 1), "frac_of_8TBps": round(rd[best] / HBM_PEAK_GBS, 4)}
     del buf
