@@ -31,6 +31,8 @@ SMALL = {
     # 64-column kernel while its down GEMM takes the 16-column one with K = 1024
     "f32_shared_cap": C["tiny_f32"].with_(T=96, E=16, k=4, f=256, shared=True, capacity_factor=1.25, seed=30),
     "f32_wide": C["tiny_f32"].with_(T=512, d=512, f=1024, seed=31),
+    # fp32, K not a multiple of 128: a last K step of 64 in both GEMMs (gate/up K = 192, down K = 320)
+    "f32_k192": C["tiny_f32"].with_(T=40, d=192, f=320, E=4, k=2, seed=32),
     "bf16_prefill": C["mixtral_prefill"].with_(T=300, d=512, f=1024),
     "bf16_prefill_ragged": C["mixtral_prefill"].with_(T=133, d=256, f=768, seed=5),
     "bf16_finegrained_shared": C["fine_grained"].with_(T=96, d=512, E=32, f=256),
@@ -109,7 +111,11 @@ ROUTE_CASES = {**{k: v for k, v in C.items()},
                "E_1023_k32": C["fine_grained"].with_(T=70, d=128, E=1023, k=32),
                "d_64": C["mixtral_prefill"].with_(T=100, d=64, E=16, k=4, seed=3),
                # more than 256 tiles of 16 x 16 with E <= 16: the LDS-staged 256 x 16 partial tiles
-               "lds_few_experts": C["mixtral_prefill"].with_(T=4200, d=512, E=16, k=4, seed=11)}
+               "lds_few_experts": C["mixtral_prefill"].with_(T=4200, d=512, E=16, k=4, seed=11),
+               # 16 x 16 partial tiles with ragged token and expert tiles and a K slice of 320
+               # (waves take 3, 3, 2 and 2 chunks of 32), in bf16 and fp32
+               "tile_ragged": C["mixtral_prefill"].with_(T=50, d=320, E=100, k=6, seed=12),
+               "tile_ragged_f32": C["tiny_f32"].with_(T=45, d=192, E=12, k=3, seed=13)}
 
 
 @pytest.mark.parametrize("name", list(ROUTE_CASES))
@@ -293,7 +299,8 @@ def test_permute_all_to_one_expert_with_capacity():
 # ---------------------------------------------------------------------------
 # Grouped FFN, given the oracle's permutation
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["tiny_f32", "tiny_f32_ragged", "f32_shared_cap", "f32_wide", "bf16_prefill", "bf16_prefill_ragged",
+@pytest.mark.parametrize("name", ["tiny_f32", "tiny_f32_ragged", "f32_shared_cap", "f32_wide", "f32_k192",
+                                  "bf16_prefill", "bf16_prefill_ragged",
                                   "bf16_finegrained_shared", "fp8_capacity", "fp8_capacity_tight",
                                   "bf16_one_expert", "bf16_big_tiles", "bf16_big_tiles_mid",
                                   "bf16_big_tiles_shared", "fp8_big_tiles_shared", "mx_prefill", "mx_big_tiles",
