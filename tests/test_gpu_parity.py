@@ -153,13 +153,14 @@ def test_route_parity(name):
 # expert ties with its neighbour (identical fp64 sums in every path).  The
 # selection must put the lower index first (the fixed tie rule), in each top-k
 # path: the small-T block ranks (whole W_g or split into slices), the wave
-# selection for E > 256, and the large-T wave ranks.
+# argmax rounds (E > 128, or 1024 tokens and more), and the wave ranks.
 TIE_CASES = {
     "small_split_E128": C["fp8_capacity_decode"].with_(T=3),
     "small_whole_E64": C["mixtral_decode"].with_(T=2, d=256, E=64, k=6, seed=31),
     "small_split_E600": C["mixtral_decode"].with_(T=3, d=128, E=600, k=16, seed=32),
     "large_E128": C["mixtral_prefill"].with_(T=40, d=256, E=128, k=8, seed=33),
     "large_E600_renorm_off": C["mixtral_prefill"].with_(T=40, d=128, E=600, k=16, renormalize=False, seed=34),
+    "large_T1100_E8": C["mixtral_prefill"].with_(T=1100, d=128, E=8, k=2, seed=35),
 }
 
 
