@@ -29,8 +29,8 @@ namespace moe {
 // Large layers (router_partial_lds): work-group tile BT tokens x BE experts
 // (64 x 64, or 256 x 16 for few experts), K step 16, operands staged in LDS as
 // fp32 (exact) with padded rows so that the 4 K-rows read by one fragment load
-// fall in distinct banks; each operand value is read from L2 by E / BE or
-// T / BT work-groups.
+// fall in distinct banks, each step's loads issued two steps ahead; each
+// operand value is read from L2 by E / BE or T / BT work-groups.
 // ---------------------------------------------------------------------------
 template <typename TIn, int BE>
 __global__ __launch_bounds__(256) void router_partial_lds(const TIn* __restrict__ x, const TIn* __restrict__ W,
@@ -56,27 +56,31 @@ __global__ __launch_bounds__(256) void router_partial_lds(const TIn* __restrict_
   const bool xt_ok = t0 + xt_l < T;
   const TIn* xrow = x + (size_t)(xt_ok ? t0 + xt_l : T - 1) * d + xk_l;
   const int wk_l = tid / (BE / WE), we_l = (tid % (BE / WE)) * WE;
-  float xr[XE], wr[WE];
+  // two register sets: the loads of step j go to set j % 2, two steps ahead of
+  // the MFMAs that use them (stored to LDS at the end of step j - 1)
+  float xr[2][XE], wr[2][WE];
   // loads of the step at k0 (always a valid step; rows past T and experts past
   // E read clamped addresses and are zeroed)
-  auto load = [&](int k0) {
+  auto load = [&](int k0, auto SET) {
+    constexpr int q = decltype(SET)::value;
 #pragma unroll
     for (int i = 0; i < XE; ++i) {
       const float v = ActTraits<TIn>::load(xrow, k0 + i);
-      xr[i] = xt_ok ? v : 0.f;
+      xr[q][i] = xt_ok ? v : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < WE; ++j) {
       const int e = e0 + we_l + j;
       const float v = ActTraits<TIn>::load(W, (size_t)(k0 + wk_l) * E + (e < E ? e : 0));
-      wr[j] = e < E ? v : 0.f;
+      wr[q][j] = e < E ? v : 0.f;
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, auto SET) {
+    constexpr int q = decltype(SET)::value;
 #pragma unroll
-    for (int i = 0; i < XE; ++i) xs[buf][xk_l + i][xt_l] = xr[i];
+    for (int i = 0; i < XE; ++i) xs[buf][xk_l + i][xt_l] = xr[q][i];
 #pragma unroll
-    for (int j = 0; j < WE; ++j) ws[buf][wk_l][we_l + j] = wr[j];
+    for (int j = 0; j < WE; ++j) ws[buf][wk_l][we_l + j] = wr[q][j];
   };
   f64x4_t acc[MT][NT];
 #pragma unroll
@@ -84,13 +88,7 @@ __global__ __launch_bounds__(256) void router_partial_lds(const TIn* __restrict_
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = (f64x4_t){0.0, 0.0, 0.0, 0.0};
   const int fr = lane & 15, fk = lane >> 4;
-  load(r_begin);
-  store(0);
-  __syncthreads();
-  int buf = 0;
-  for (int k0 = r_begin; k0 < r_end; k0 += BK) {
-    const int kn = (k0 + BK < r_end) ? k0 + BK : k0;      // last step reloads itself (unused)
-    load(kn);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < BK / 4; ++ks) {
       double a[MT], b[NT];
@@ -103,9 +101,29 @@ __global__ __launch_bounds__(256) void router_partial_lds(const TIn* __restrict_
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    store(buf ^ 1);
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  const int nk = (r_end - r_begin) / BK;                 // >= 1
+  // clamped step index: steps past the end reload the last step (unused)
+  const auto kof = [&](int j) { return r_begin + min(j, nk - 1) * BK; };
+  load(kof(0), S0{});
+  load(kof(1), S1{});
+  store(0, S0{});
+  __syncthreads();
+  // step j: issue step j + 2's loads into set j % 2, compute from LDS buffer
+  // j % 2, then store step j + 1 (set (j + 1) % 2) into the other buffer
+  for (int j = 0; j < nk; j += 2) {
+    load(kof(j + 2), S0{});
+    compute(0);
+    store(1, S1{});
     __syncthreads();
-    buf ^= 1;
+    if (j + 1 < nk) {
+      load(kof(j + 3), S1{});
+      compute(1);
+      store(0, S0{});
+      __syncthreads();
+    }
   }
 #pragma unroll
   for (int i = 0; i < MT; ++i)
