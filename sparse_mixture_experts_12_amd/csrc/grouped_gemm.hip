@@ -26,7 +26,9 @@
 //     the same way (half the bytes), ds_read_b64_tr_b8 gathers them
 //     K-contiguous and they widen to bf16 (exact) in registers; the
 //     per-output-channel scales multiply the accumulators in the epilogue.
-//   fp32 layer (gemm_f32_kernel): SIMT fp32 FMA.
+//   fp32 layer: SIMT fp32 FMA, 64 x 64 tiles (gemm_f32_kernel), or 64 x 16 tiles
+//     with K split over the threads when the layer has few tiles
+//     (gemm_f32_narrow_kernel).
 // Every LDS layout was checked against the bank-conflict counter on gfx950
 // (16-lane passes for 16-byte reads, 32-lane passes for 8-byte reads).
 //
