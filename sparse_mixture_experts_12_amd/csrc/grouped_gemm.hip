@@ -37,8 +37,10 @@
 // its L2.  Each GEMM is two launches, full-height ("heavy") tiles and each
 // expert's small last ("light") tile, whose body matches its rows (256, 128,
 // 64 or 32); with 64 or more expert groups the light launch runs on a second
-// stream beside the heavy one.  fp8 layers whose groups all fit 64 rows run
-// one 64-row launch per GEMM.
+// stream beside the heavy one.  With bf16 weights a last tile is light only
+// at <= 64 rows (64-row stages two deep, two work-groups per CU); last tiles
+// of 65..128 rows run in the heavy launch with the 128-row body.  fp8 layers
+// whose groups all fit 64 rows run one 64-row launch per GEMM.
 #include <atomic>
 #include <hip/hip_ext.h>
 
@@ -438,7 +440,10 @@ __global__ __launch_bounds__(256, TileCfg<BMMAX>::OCC) void gemm_dl_kernel(GemmP
   // An expert's last row tile is usually partial: run it with a body whose
   // MFMA work matches its rows (<= 64, <= 128) instead of the full height.
   if constexpr (SEG == 1) {
-    dl_tile<DUAL, 256, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
+    // heavy tiles: full ones, and last tiles above the light bound (65..128
+    // rows for bf16 weights take the 128-row body)
+    if (F8 || rows > 128) dl_tile<DUAL, 256, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
+    else dl_tile<DUAL, 128, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
   } else if constexpr (BMMAX >= 256) {
     if (rows > 128) dl_tile<DUAL, 256, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
     else if (rows > 64) dl_tile<DUAL, 128, BMMAX, BK, NST, F8>(p, g, row0, rows, nt, L0, L1, L2, L3, k_lo, nK, kpart, slot);
@@ -853,10 +858,16 @@ int grouped_grid(int maxQ, int n_tiles) {
   return (int)(8 * per);
 }
 
+// bf16 weights: a group's last tile is light only at <= 64 rows (run by the
+// 64-row light kernel, two work-groups per CU); last tiles of 65..128 rows
+// join the heavy launch with its 128-row body.
+constexpr int kBf16LightMax = 64;
+
 SchedSpec grouped_sched_spec(const GroupedArgs& a) {
   const int BM = (a.wkind == W_MX || a.wkind == W_MX4) ? 256 : pick_bm(a);
+  const int lm = (a.wkind == W_BF16 && !a.act_f32) ? kBf16LightMax : 0;
   return SchedSpec{a.sched, BM, a.has_shared ? a.T : 0, a.routed_rows,
-                   grouped_max_row_tiles(a.routed_rows, a.T, a.E, a.has_shared, BM)};
+                   grouped_max_row_tiles(a.routed_rows, a.T, a.E, a.has_shared, BM), lm};
 }
 
 hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
@@ -866,7 +877,8 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   const int shared_row0 = a.routed_rows;
   hipError_t err = hipSuccess;
   if (!a.sched_ready &&
-      (err = launch_tile_schedule(a.offsets, a.E, sp.BM, sp.shared_rows, shared_row0, maxQ, a.sched, s)) != hipSuccess)
+      (err = launch_tile_schedule(a.offsets, a.E, sp.BM, sp.shared_rows, shared_row0, maxQ, a.sched, s,
+                                  sp.light_max)) != hipSuccess)
     return err;
 
   if (a.act_f32) {
@@ -974,7 +986,7 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
     launch_split(gemm_dl_kernel<true, 256, kDlBK, kDlNST, 1, true>, gemm_dl_kernel<true, 128, kDlBK, 3, 2, true>, p,
                  (a.f + 127) / 128, a.ev_begin, a.ev_end);
   } else {
-    launch_split(gemm_dl_kernel<true, 256, kDlBK, kDlNST, 1>, gemm_dl_kernel<true, 128, kDlBK, 3, 2>, p,
+    launch_split(gemm_dl_kernel<true, 256, kDlBK, kDlNST, 1>, gemm_dl_kernel<true, kBf16LightMax, kDlBK, 2, 2>, p,
                  (a.f + 127) / 128, a.ev_begin, a.ev_end);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -997,8 +1009,14 @@ hipError_t launch_grouped_ffn(const GroupedArgs& a, hipStream_t s) {
   } else if (a.wkind == W_FP8) {
     launch_split(gemm_dl_kernel<false, 256, kDlBK, kDlNST, 1, true>, gemm_dl_kernel<false, 128, kDlBK, 3, 2, true>, q,
                  dn_tiles, nullptr, nullptr, q.ksplit);
-  } else {
+  } else if (q.ksplit > 1) {
+    // few light tiles, each split over K parts: the 128-row stages three deep
+    // keep more of each part's weight stream in flight (Mixtral prefill light
+    // down 81 us against 104 us with the 64-row two-stage kernel)
     launch_split(gemm_dl_kernel<false, 256, kDlBK, kDlNST, 1>, gemm_dl_kernel<false, 128, kDlBK, 3, 2>, q,
+                 dn_tiles, nullptr, nullptr, q.ksplit);
+  } else {
+    launch_split(gemm_dl_kernel<false, 256, kDlBK, kDlNST, 1>, gemm_dl_kernel<false, kBf16LightMax, kDlBK, 2, 2>, q,
                  dn_tiles, nullptr, nullptr, q.ksplit);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;

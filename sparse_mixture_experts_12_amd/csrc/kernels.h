@@ -32,6 +32,7 @@ size_t router_partial_bytes(int T, int d, int E);
 struct SchedSpec {
   int32_t* sched;
   int BM, shared_rows, shared_row0, maxQ;
+  int light_max = 0;                 // a group's last tile is light at <= light_max rows (0: BM / 2)
 };
 
 struct PermuteArgs {
@@ -47,7 +48,7 @@ size_t permute_ws_bytes(int n, int E);
 // Tile schedule header size (ints): [0] heavy row tiles, [1] light row tiles.
 constexpr int kSchedHead = 4;
 hipError_t launch_tile_schedule(const int32_t* offsets, int E, int BM, int shared_rows, int shared_row0, int maxQ,
-                                int32_t* sched, hipStream_t s);
+                                int32_t* sched, hipStream_t s, int light_max = 0);
 
 // Expert weights of one group set: routed experts [E,...] plus the optional
 // shared expert, addressed as group E.

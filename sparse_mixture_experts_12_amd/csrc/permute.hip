@@ -316,9 +316,9 @@ __global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(
 //   group g's row-tile count is stored in sched[1 + 4*maxQ + g]
 // ---------------------------------------------------------------------------
 // Row tiles of every group (expert, or the shared expert as group E), in two
-// segments: "heavy" tiles with more than BM / 2 rows (all full tiles and a
-// large last tile) and "light" tiles with at most BM / 2 rows (a group's
-// small last tile).  The GEMMs run light tiles with a cheaper body and spread
+// segments: "heavy" tiles with more than light_max rows (all full tiles and a
+// large last tile) and "light" tiles with at most light_max rows (a group's
+// small last tile; light_max is BM / 2 unless the caller sets it).  The GEMMs run light tiles with a cheaper body and spread
 // each segment evenly over the XCDs.  Layout (ints):
 //   [0] QH, [1] QL,
 //   heavy tile q:  [kSchedHead + 4 q + {0: group, 1: row0, 2: rows, 3: first heavy tile of the group}]
@@ -330,10 +330,11 @@ __global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(
 __device__ void write_tile_schedule(int row0, int rows, int E, int G, const SchedSpec& sp, int* s_wave) {
   const int tid = threadIdx.x;
   const int BM = sp.BM, maxQ = sp.maxQ, maxG = E + 1;
+  const int LM = sp.light_max > 0 ? sp.light_max : BM / 2;
   if (tid >= G) rows = 0;
   const int full = rows / BM, rem = rows - full * BM;
-  const int nh = full + (rem > BM / 2 ? 1 : 0);
-  const int nl = (rem > 0 && rem <= BM / 2) ? 1 : 0;
+  const int nh = full + (rem > LM ? 1 : 0);
+  const int nl = (rem > 0 && rem <= LM) ? 1 : 0;
   int qh = 0, ql = 0;
   const int first = block_exclusive_scan<kPermThreads>(nh, s_wave, &qh);
   const int lfirst = block_exclusive_scan<kPermThreads>(nl, s_wave, &ql);
@@ -402,8 +403,8 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_tile_schedule(const int32_t* offsets, int E, int BM, int shared_rows, int shared_row0, int maxQ,
-                                int32_t* sched, hipStream_t s) {
-  SchedSpec sp{sched, BM, shared_rows, shared_row0, maxQ};
+                                int32_t* sched, hipStream_t s, int light_max) {
+  SchedSpec sp{sched, BM, shared_rows, shared_row0, maxQ, light_max};
   tile_schedule_kernel<<<1, kPermThreads, 0, s>>>(offsets, E, sp);
   return hipGetLastError();
 }
