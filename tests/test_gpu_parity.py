@@ -46,6 +46,12 @@ SMALL = {
     # 256-row tiles whose last tiles hold 108..139 rows: the 128- and 256-row bodies
     "bf16_big_tiles_mid": C["mixtral_prefill"].with_(T=760, d=256, f=512, E=4, k=2, seed=3),
     "bf16_big_tiles_shared": C["fine_grained"].with_(T=700, d=256, E=4, k=2, f=256, seed=10),
+    # last tiles at the bf16 light bound: 64 rows (light, full 64-row body), 65 rows (heavy launch,
+    # 128-row body), 128 rows (128-row body full) and 129 rows (256-row body)
+    "bf16_last_64": C["mixtral_prefill"].with_(T=311, d=128, f=256, seed=45),
+    "bf16_last_65": C["mixtral_prefill"].with_(T=311, d=128, f=256, seed=42),
+    "bf16_last_128": C["mixtral_prefill"].with_(T=476, d=128, f=256, seed=42),
+    "bf16_last_129": C["mixtral_prefill"].with_(T=443, d=128, f=256, seed=40),
     "fp8_big_tiles_shared": C["fp8_capacity"].with_(T=700, d=256, E=4, k=2, f=256, capacity_factor=0.0,
                                                      shared=True, seed=9),
     # range edges: many experts and top-32, d = f = 64, E = 1023 (+ shared), one token on the grouped path
@@ -304,7 +310,8 @@ def test_permute_all_to_one_expert_with_capacity():
                                   "bf16_prefill", "bf16_prefill_ragged",
                                   "bf16_finegrained_shared", "fp8_capacity", "fp8_capacity_tight",
                                   "bf16_one_expert", "bf16_big_tiles", "bf16_big_tiles_mid",
-                                  "bf16_big_tiles_shared", "fp8_big_tiles_shared", "mx_prefill", "mx_big_tiles",
+                                  "bf16_big_tiles_shared", "bf16_last_64", "bf16_last_65", "bf16_last_128",
+                                  "bf16_last_129", "fp8_big_tiles_shared", "mx_prefill", "mx_big_tiles",
                                   "mx_big_tiles_shared", "mx_capacity", "mx4_prefill", "mx4_big_tiles",
                                   "mx4_finegrained_shared", "mx4_capacity"])
 def test_grouped_ffn_parity(name):
